@@ -1,0 +1,214 @@
+/*
+ * moe.h - C ABI of a deterministic MoE layer (forward and backward) for one AMD MI355X (gfx950).
+ *
+ * The layer is the mixture-of-experts step that the pages on Mixture-of-Kittens (MoK) describe.
+ * Those pages are the MarkTechPost article "Cursor Open-Sources Mixture-of-Kittens (MoK): A
+ * Deterministic MoE Training Megakernel for GB300 NVL72 Racks", the toknow.ai post
+ * "Mixture-of-Kittens: Cursor's Open-Source Kernel Trains AI Up to 2.37x Faster" and the aiweekly.co
+ * alert "Cursor open-sources MoE megakernel for GB300 NVL72 racks". This library takes one GPU's
+ * share of it.
+ *
+ * Forward: the router, then an expert-grouped permute into a ring slot, then per-expert SwiGLU
+ * MLPs, then a weighted combine. Backward: dgrad and wgrad of every GEMM, plus the router-weight
+ * gradient, which is computed inside the SwiGLU backward (MarkTechPost, closing paragraph of
+ * "Three design decisions that matter").
+ *
+ * Conventions for every entry point:
+ *  - Every pointer argument is DEVICE memory of the current HIP device, owned by the caller. The
+ *    library never allocates, frees or synchronises. Each call only enqueues kernels on `stream`
+ *    (a hipStream_t; NULL means the null stream) and returns.
+ *  - Row-major layouts throughout. bf16 is IEEE bfloat16 stored as uint16. Weights follow the
+ *    [out, in] convention: W1 is [E, 2I, d] (rows 0..I-1 gate, I..2I-1 up), W2 is [E, d, I], and
+ *    the router weight Wr is [E, d].
+ *  - Return value: MOE_OK (0), or a negative moe_status. Arguments are checked on the host before
+ *    anything is enqueued. A failed check enqueues nothing. Nothing prints and nothing throws.
+ *  - Determinism: every result is a function of the inputs alone. No float atomics are used,
+ *    and every reduction runs in a fixed order, so two runs are bitwise identical.
+ *  - No host synchronisation: per-expert counts never leave the device. Buffers are sized for
+ *    the worst case, so no token is ever dropped, whatever the expert imbalance (MarkTechPost,
+ *    "Three design decisions that matter": ring token buffer; "Key Takeaways").
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* moe_stream_t; /* hipStream_t */
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,     /* null pointer, bad shape, misaligned pointer */
+    MOE_ERR_RING_TOO_SMALL = -2,  /* ring_bytes < (slot + 1) * ring slot bytes */
+    MOE_ERR_UNSUPPORTED = -3,     /* a mode this build does not provide */
+    MOE_ERR_HIP = -4,             /* a HIP runtime error while enqueuing */
+    MOE_ERR_WORKSPACE_TOO_SMALL = -5
+} moe_status;
+
+enum { MOE_PREC_BF16 = 0, MOE_PREC_MXFP8 = 1 };
+
+/* cfg.flags bits */
+enum {
+    MOE_FLAG_PERSISTENT = 1 /* grouped GEMMs as persistent grids walking the schedule table */
+};
+
+/* Device status word (first 4 bytes of the workspace). moe_permute clears it and ORs bits into
+ * it; the caller may read it after its own synchronisation. */
+enum { MOE_DEVICE_BAD_EXPERT_INDEX = 1 /* a topk_idx entry outside [0, E): that row is skipped */ };
+
+/* Layer shape and mode. Constraints checked on the host: T >= 1; 1 <= k <= E <= 1024;
+ * d % 256 == 0; I % 128 == 0; T * k < 2^31; precision MOE_PREC_BF16. */
+typedef struct moe_cfg {
+    int32_t T;         /* tokens entering the layer */
+    int32_t d;         /* hidden size */
+    int32_t E;         /* experts on this GPU */
+    int32_t k;         /* experts per token (top-k) */
+    int32_t I;         /* SwiGLU intermediate size */
+    int32_t precision; /* MOE_PREC_* */
+    int32_t flags;     /* MOE_FLAG_* */
+} moe_cfg;
+
+/* Byte sizes of the caller-owned buffers, and the offsets of the intermediates inside them. */
+typedef struct moe_sizes {
+    size_t ring_slot;      /* one ring slot: the permuted tokens Xp, bf16 [T*k, d] */
+    size_t saved;          /* forward activations kept for backward */
+    size_t saved_H;        /* offset of H = [g | u], bf16 [T*k, 2I], rows in position order */
+    size_t saved_A;        /* offset of A = silu(g) * u, bf16 [T*k, I] */
+    size_t workspace;      /* scratch for route/permute/forward/backward (one buffer serves all) */
+    size_t ws_O;           /* offset of the expert outputs O, bf16 [T*k, d], valid after forward */
+    size_t ws_dH;          /* offset of dH, bf16 [T*k, 2I], valid after backward */
+    size_t ws_dXp;         /* offset of dXp, bf16 [T*k, d], valid after backward */
+} moe_sizes;
+
+/* Sizes of every caller buffer for `cfg`. Host only; enqueues nothing. */
+int moe_query(const moe_cfg* cfg, moe_sizes* out);
+
+/*
+ * moe_route - router logits, top-k selection and renormalised softmax weights.
+ *
+ * The toknow.ai summary describes an MoE as sending each input to a few experts. The gate used
+ * here is the plain top-k softmax:
+ *   logits[t,e] = sum_i x[t,i] * w_router[e,i], in fp32. For each (t,e) one accumulator starts
+ *       at +0 and gains the exact bf16 x bf16 products for i = 0,1,..,d-1 in ascending order,
+ *       rounding after each addition.
+ *   topk_idx[t,:] holds the k largest logits in descending order; equal logits go to the lower
+ *       expert index. Selection compares logits numerically (-0 == +0; NaN unsupported).
+ *   topk_w[t,j] = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0), in fp32 (l_0 = the largest),
+ *       which equals softmax over all E followed by renormalisation over the k selected.
+ *
+ *   x        bf16 [T, d]    in
+ *   w_router bf16 [E, d]    in
+ *   logits   fp32 [T, E]    out
+ *   topk_idx int32 [T, k]   out
+ *   topk_w   fp32 [T, k]    out
+ */
+int moe_route(const moe_cfg* cfg, const void* x, const void* w_router, float* logits,
+              int32_t* topk_idx, float* topk_w, moe_stream_t stream);
+
+/*
+ * moe_permute - expert histogram, exclusive scan, and a stable grouping of the T*k rows by
+ * expert into ring slot `slot`.
+ *
+ * The gather half of the pages' dispatch is the part that stays on one GPU (MarkTechPost, "Three
+ * design decisions that matter": pull-based dispatch and the ring token buffer). Row r = t*k + j
+ * goes to position pos = offsets[e] + (number of rows r' < r with the same expert e), so inside
+ * an expert segment rows ascend by r.
+ *
+ *   topk_idx int32 [T, k]          in   (from moe_route, or given by the caller)
+ *   x        bf16 [T, d]           in
+ *   ring     bytes [ring_bytes]    out: slot `slot` (at slot * ring_slot bytes) receives
+ *                                       Xp[pos] = x[row_src[pos] / k], bf16 [T*k, d]
+ *   counts   int32 [E]             out: rows per expert
+ *   offsets  int32 [E+1]           out: exclusive scan of counts, offsets[E] = T*k
+ *   row_src  int32 [T*k]           out: pos -> r
+ *   tk_row   int32 [T*k]           out: r -> pos (-1 for a skipped bad-index row)
+ *   workspace bytes [ws_bytes]     scratch; also holds the device status word
+ * Errors: MOE_ERR_RING_TOO_SMALL when (slot + 1) * ring_slot > ring_bytes or slot < 0.
+ */
+int moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, void* ring,
+                size_t ring_bytes, int32_t slot, int32_t* counts, int32_t* offsets,
+                int32_t* row_src, int32_t* tk_row, void* workspace, size_t ws_bytes,
+                moe_stream_t stream);
+
+/*
+ * moe_forward - grouped SwiGLU expert MLPs over the ring slot, then the weighted combine.
+ *
+ * The expert-grouped GEMMs are in MarkTechPost, "Three design decisions that matter". For each
+ * expert e and each of its positions:
+ *   [g | u] = Xp[pos] W1[e]^T   (fp32 accumulate; stored bf16 as H)
+ *   A       = silu(g) * u        (from the fp32 g, u; stored bf16)
+ *   O[pos]  = A W2[e]^T          (fp32 accumulate; stored bf16 in the workspace)
+ * Combine, which is atomic-free and fixed-order:
+ *   y[t] = bf16( sum_{j=0..k-1} topk_w[t,j] * O[tk_row[t*k+j]] ), fp32 FMA with j ascending.
+ *
+ *   ring, ring_bytes, slot   in: the slot written by moe_permute
+ *   offsets, tk_row          in: from moe_permute
+ *   topk_w   fp32 [T, k]     in
+ *   w1       bf16 [E, 2I, d] in
+ *   w2       bf16 [E, d, I]  in
+ *   wq                       in: MXFP8 weights (NULL in BF16 mode)
+ *   y        bf16 [T, d]     out
+ *   saved    bytes [saved_bytes]   out: H and A at the offsets moe_query reports
+ *   workspace bytes [ws_bytes]     scratch
+ */
+int moe_forward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t slot,
+                const int32_t* offsets, const int32_t* tk_row, const float* topk_w,
+                const void* w1, const void* w2, const void* wq, void* y, void* saved,
+                size_t saved_bytes, void* workspace, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_backward - gradients of L = <y, dy> with respect to x, the router weight, w1, w2 and the
+ * routing weights.
+ *
+ * Per position pos (token t, slot j, expert e, weight w):
+ *   dA'      = dy[t] W2[e]                           (fp32, never stored)
+ *   dw       = <dA', A[pos]>, which equals <dy[t], A[pos] W2[e]^T>. This is the router-weight
+ *              gradient, fused into the SwiGLU backward (MarkTechPost, closing paragraph of
+ *              "Three design decisions that matter"). Per-tile partials are summed in
+ *              ascending tile order.
+ *   dA       = w * dA'
+ *   dg, du   = dA * u * s * (1 + g (1 - s)),  dA * silu(g)   (s = sigmoid(g); g, u from H)
+ *   dH[pos]  = bf16([dg | du]);  dXp[pos] = bf16(dH[pos] W1[e])
+ *   dW2[e]   = sum over pos in e, ascending, of bf16(w dy[t]) (x) A[pos]       (fp32)
+ *   dW1[e]   = sum over pos in e, ascending, of dH[pos] (x) Xp[pos]           (fp32)
+ * Per token: d_topk_w[t,j] = dw of its row. When w_router is given (the layer routed itself):
+ *   dlogit_j = w_j (dw_j - sum_i w_i dw_i), and 0 off the selected set;
+ *   dx[t]    = bf16( sum_j dXp[tk_row[t*k+j]] + sum_j dlogit_j Wr[e_j] ), j ascending, fp32;
+ *   dWr[e]   = sum over pos in e, ascending, of dlogit(pos) * Xp[pos]          (fp32).
+ * When w_router is NULL (routing given), dx[t] = bf16(sum_j dXp[tk_row[t*k+j]]), and dwr is not
+ * touched. Experts with no rows get zero dW1/dW2 blocks. With accumulate != 0, dw1, dw2 and dwr
+ * are added to (fp32 read-modify-write) instead of overwritten.
+ *
+ *   ring, ring_bytes, slot        in: the slot holding this batch's Xp (written by moe_permute)
+ *   offsets, row_src, tk_row      in: from moe_permute
+ *   topk_idx int32 [T, k], topk_w fp32 [T, k]   in
+ *   w_router bf16 [E, d] or NULL  in
+ *   w1, w2, wq                    in (as in moe_forward)
+ *   saved                         in: from moe_forward of the same batch
+ *   dy       bf16 [T, d]          in
+ *   dx       bf16 [T, d]          out
+ *   dw1      fp32 [E, 2I, d]      out (or accumulated)
+ *   dw2      fp32 [E, d, I]       out (or accumulated)
+ *   dwr      fp32 [E, d]          out (or accumulated); ignored when w_router is NULL
+ *   d_topk_w fp32 [T, k]          out
+ *   workspace bytes [ws_bytes]    scratch (dH and dXp at the offsets moe_query reports)
+ */
+int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t slot,
+                 const int32_t* offsets, const int32_t* row_src, const int32_t* tk_row,
+                 const int32_t* topk_idx, const float* topk_w, const void* w_router,
+                 const void* w1, const void* w2, const void* wq, const void* saved,
+                 size_t saved_bytes, const void* dy, void* dx, float* dw1, float* dw2,
+                 float* dwr, float* d_topk_w, int32_t accumulate, void* workspace,
+                 size_t ws_bytes, moe_stream_t stream);
+
+/* A static string for a moe_status value. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

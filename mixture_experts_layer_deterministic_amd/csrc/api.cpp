@@ -1,0 +1,265 @@
+// C ABI of the MoE layer: argument checks, buffer layout and launch sequences.
+// Every call checks its arguments on the host, then enqueues its kernels on the caller's
+// stream. It never allocates, synchronises or prints.
+#include <hip/hip_runtime.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  // workspace
+  size_t status, sched, blk_cnt, blk_flag, rank, O, dH, dXp, dwpart, dl_pos, total;
+  // saved
+  size_t H, A, saved_total;
+  size_t slot;
+  int nb, nIt, max_mtiles;
+};
+
+bool cfg_ok(const moe_cfg* c) {
+  if (!c) return false;
+  if (c->T < 1 || c->d < 256 || c->d % 256 != 0 || c->I < 128 || c->I % 128 != 0) return false;
+  if (c->E < 1 || c->E > 1024 || c->k < 1 || c->k > c->E || c->k > kMaxTopK) return false;
+  const long long Tk = (long long)c->T * c->k;
+  if (Tk >= (1LL << 31) || (long long)c->T * c->E >= (1LL << 31)) return false;
+  return true;
+}
+
+Layout layout(const moe_cfg* c) {
+  Layout L{};
+  const size_t Tk = (size_t)c->T * c->k, d = c->d, I = c->I, E = c->E;
+  L.nb = (int)((Tk + kPermRows - 1) / kPermRows);
+  L.nIt = c->I / kDgradBN;
+  L.max_mtiles = sched_max_mtiles((int)Tk, c->E);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.status = take(16);
+  L.sched = take(sizeof(int2) * (1 + (size_t)L.max_mtiles));
+  L.blk_cnt = take(sizeof(int32_t) * (size_t)L.nb * E);
+  L.blk_flag = take(sizeof(int32_t) * (size_t)L.nb);
+  L.rank = take(sizeof(int32_t) * Tk);
+  L.O = take(2 * Tk * d);
+  L.dH = take(2 * Tk * 2 * I);
+  L.dXp = take(2 * Tk * d);
+  L.dwpart = take(sizeof(float) * Tk * L.nIt);
+  L.dl_pos = take(sizeof(float) * Tk);
+  L.total = o;
+  o = 0;
+  L.H = take(2 * Tk * 2 * I);
+  L.A = take(2 * Tk * I);
+  L.saved_total = o;
+  L.slot = 2 * Tk * d;
+  return L;
+}
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) % 16) == 0; }
+bool aligned4(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) % 4) == 0; }
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+template <class T>
+const T* at(const void* base, size_t off) {
+  return reinterpret_cast<const T*>(static_cast<const char*>(base) + off);
+}
+
+// First error wins; later launches are skipped once one fails.
+struct Launches {
+  hipError_t err = hipSuccess;
+  void operator()(hipError_t e) {
+    if (err == hipSuccess) err = e;
+  }
+  int status() const { return err == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+};
+
+int check_mode(const moe_cfg* c) {
+  if (!cfg_ok(c)) return MOE_ERR_INVALID_ARG;
+  if (c->precision != MOE_PREC_BF16) return MOE_ERR_UNSUPPORTED;
+  if (c->flags & ~MOE_FLAG_PERSISTENT) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int check_ring(const Layout& L, const void* ring, size_t ring_bytes, int32_t slot) {
+  if (!aligned16(ring)) return MOE_ERR_INVALID_ARG;
+  if (slot < 0 || (size_t)(slot + 1) * L.slot > ring_bytes) return MOE_ERR_RING_TOO_SMALL;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_query(const moe_cfg* cfg, moe_sizes* out) {
+  if (!out || !cfg_ok(cfg)) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(cfg);
+  out->ring_slot = L.slot;
+  out->saved = L.saved_total;
+  out->saved_H = L.H;
+  out->saved_A = L.A;
+  out->workspace = L.total;
+  out->ws_O = L.O;
+  out->ws_dH = L.dH;
+  out->ws_dXp = L.dXp;
+  return MOE_OK;
+}
+
+int moe_route(const moe_cfg* cfg, const void* x, const void* w_router, float* logits,
+              int32_t* topk_idx, float* topk_w, moe_stream_t stream) {
+  int st = check_mode(cfg);
+  if (st) return st;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned4(logits) || !aligned4(topk_idx) ||
+      !aligned4(topk_w))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Launches L;
+  L(launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
+                         logits, cfg->T, cfg->d, cfg->E, s));
+  if (L.err == hipSuccess)
+    L(launch_router_topk(logits, cfg->T, cfg->E, cfg->k, topk_idx, topk_w, s));
+  return L.status();
+}
+
+int moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, void* ring,
+                size_t ring_bytes, int32_t slot, int32_t* counts, int32_t* offsets,
+                int32_t* row_src, int32_t* tk_row, void* workspace, size_t ws_bytes,
+                moe_stream_t stream) {
+  int st = check_mode(cfg);
+  if (st) return st;
+  const Layout Y = layout(cfg);
+  if (!aligned4(topk_idx) || !aligned16(x) || !aligned4(counts) || !aligned4(offsets) ||
+      !aligned4(row_src) || !aligned4(tk_row) || !aligned16(workspace))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ring(Y, ring, ring_bytes, slot))) return st;
+  if (ws_bytes < Y.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int Tk = cfg->T * cfg->k;
+  int32_t* blk = at<int32_t>(workspace, Y.blk_cnt);
+  int32_t* flag = at<int32_t>(workspace, Y.blk_flag);
+  int32_t* rank = at<int32_t>(workspace, Y.rank);
+  uint16_t* xp = at<uint16_t>(ring, (size_t)slot * Y.slot);
+  Launches L;
+  L(launch_perm_hist(topk_idx, Tk, cfg->E, blk, rank, flag, s));
+  if (!L.err)
+    L(launch_perm_scan(blk, Y.nb, cfg->E, flag, counts, offsets, at<int32_t>(workspace, Y.status),
+                       s));
+  if (!L.err)
+    L(launch_perm_place(topk_idx, rank, blk, Tk, cfg->E, cfg->k, row_src, tk_row,
+                        static_cast<const uint16_t*>(x), xp, cfg->d, s));
+  return L.status();
+}
+
+int moe_forward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t slot,
+                const int32_t* offsets, const int32_t* tk_row, const float* topk_w,
+                const void* w1, const void* w2, const void* wq, void* y, void* saved,
+                size_t saved_bytes, void* workspace, size_t ws_bytes, moe_stream_t stream) {
+  (void)wq;
+  int st = check_mode(cfg);
+  if (st) return st;
+  const Layout Y = layout(cfg);
+  if (!aligned4(offsets) || !aligned4(tk_row) || !aligned4(topk_w) || !aligned16(w1) ||
+      !aligned16(w2) || !aligned16(y) || !aligned16(saved) || !aligned16(workspace))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ring(Y, ring, ring_bytes, slot))) return st;
+  if (saved_bytes < Y.saved_total || ws_bytes < Y.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool pers = cfg->flags & MOE_FLAG_PERSISTENT;
+  const int Tk = cfg->T * cfg->k;
+  const uint16_t* xp = at<uint16_t>(ring, (size_t)slot * Y.slot);
+  int2* sched = at<int2>(workspace, Y.sched);
+  uint16_t* H = at<uint16_t>(saved, Y.H);
+  uint16_t* A = at<uint16_t>(saved, Y.A);
+  uint16_t* O = at<uint16_t>(workspace, Y.O);
+  Launches L;
+  L(launch_sched_build(offsets, cfg->E, sched, s));
+  if (!L.err)
+    L(launch_fwd_gateup({xp, static_cast<const uint16_t*>(w1), H, A, offsets, sched, cfg->d,
+                         cfg->I, Tk, cfg->E},
+                        pers, s));
+  if (!L.err)
+    L(launch_fwd_down({A, static_cast<const uint16_t*>(w2), O, offsets, sched, cfg->d, cfg->I, Tk,
+                       cfg->E},
+                      pers, s));
+  if (!L.err)
+    L(launch_combine(O, tk_row, topk_w, cfg->T, cfg->k, cfg->d, static_cast<uint16_t*>(y), s));
+  return L.status();
+}
+
+int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t slot,
+                 const int32_t* offsets, const int32_t* row_src, const int32_t* tk_row,
+                 const int32_t* topk_idx, const float* topk_w, const void* w_router,
+                 const void* w1, const void* w2, const void* wq, const void* saved,
+                 size_t saved_bytes, const void* dy, void* dx, float* dw1, float* dw2,
+                 float* dwr, float* d_topk_w, int32_t accumulate, void* workspace,
+                 size_t ws_bytes, moe_stream_t stream) {
+  (void)wq;
+  int st = check_mode(cfg);
+  if (st) return st;
+  const Layout Y = layout(cfg);
+  const bool routed = w_router != nullptr;
+  if (!aligned4(offsets) || !aligned4(row_src) || !aligned4(tk_row) || !aligned4(topk_idx) ||
+      !aligned4(topk_w) || !aligned16(w1) || !aligned16(w2) || !aligned16(saved) ||
+      !aligned16(dy) || !aligned16(dx) || !aligned16(dw1) || !aligned16(dw2) ||
+      !aligned4(d_topk_w) || !aligned16(workspace))
+    return MOE_ERR_INVALID_ARG;
+  if (routed && (!aligned16(w_router) || !aligned16(dwr))) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ring(Y, ring, ring_bytes, slot))) return st;
+  if (saved_bytes < Y.saved_total || ws_bytes < Y.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool pers = cfg->flags & MOE_FLAG_PERSISTENT;
+  const int Tk = cfg->T * cfg->k, d = cfg->d, I = cfg->I, E = cfg->E, k = cfg->k;
+  const uint16_t* xp = at<uint16_t>(ring, (size_t)slot * Y.slot);
+  const uint16_t* H = at<uint16_t>(saved, Y.H);
+  const uint16_t* A = at<uint16_t>(saved, Y.A);
+  int2* sched = at<int2>(workspace, Y.sched);
+  uint16_t* dH = at<uint16_t>(workspace, Y.dH);
+  uint16_t* dXp = at<uint16_t>(workspace, Y.dXp);
+  float* dwpart = at<float>(workspace, Y.dwpart);
+  float* dl_pos = at<float>(workspace, Y.dl_pos);
+  const uint16_t* dyp = static_cast<const uint16_t*>(dy);
+  const uint16_t* w1p = static_cast<const uint16_t*>(w1);
+  const uint16_t* w2p = static_cast<const uint16_t*>(w2);
+  Launches L;
+  L(launch_sched_build(offsets, E, sched, s));
+  if (!L.err)
+    L(launch_bwd_down_dgrad({dyp, row_src, topk_w, w2p, H, A, dH, dwpart, offsets, sched, d, I, k,
+                             Tk, E},
+                            pers, s));
+  if (!L.err)
+    L(launch_dw_router(dwpart, Y.nIt, tk_row, topk_w, cfg->T, k, d_topk_w, dl_pos, routed, s));
+  if (!L.err)
+    L(launch_bwd_down_wgrad({dyp, row_src, topk_w, A, dw2, offsets, d, I, k, E, accumulate}, pers,
+                            s));
+  if (!L.err) L(launch_bwd_gate_dgrad({dH, w1p, dXp, offsets, sched, d, I, Tk, E}, pers, s));
+  if (!L.err) L(launch_bwd_gate_wgrad({dH, xp, dw1, offsets, d, I, E, accumulate}, pers, s));
+  if (!L.err)
+    L(launch_uncombine(dXp, tk_row, topk_idx, dl_pos,
+                       routed ? static_cast<const uint16_t*>(w_router) : nullptr, cfg->T, k, d,
+                       static_cast<uint16_t*>(dx), s));
+  if (!L.err && routed) L(launch_dwr(dl_pos, xp, offsets, E, d, dwr, accumulate, s));
+  return L.status();
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_RING_TOO_SMALL: return "ring buffer too small for the requested slot";
+    case MOE_ERR_UNSUPPORTED: return "unsupported mode";
+    case MOE_ERR_HIP: return "HIP runtime error while enqueuing";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace or saved buffer too small";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,192 @@
+// Gather-form combine and its backward companions. Every output is written by exactly one
+// thread, which sums in a fixed order: atomic-free and bitwise reproducible.
+//
+// The combine is the local half of the pages' forward combine; the backward un-permute is the
+// local half of their reverse dispatch (MarkTechPost, "Three design decisions that matter").
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+static int rows_per_block(int d) {
+  int rpb = 2048 / (d / 8);
+  return rpb < 1 ? 1 : (rpb > 256 ? 256 : rpb);
+}
+
+// y[t] = bf16( sum_{j=0..k-1} w[t,j] * O[tk_row[t*k+j]] ), fp32 fma with j ascending.
+__global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict__ O,
+                                                      const int32_t* __restrict__ tk_row,
+                                                      const float* __restrict__ topk_w, int T,
+                                                      int k, int d, uint16_t* __restrict__ y,
+                                                      int tpb) {
+  const int vpr = d / 8;
+  const int t0 = blockIdx.x * tpb;
+  for (int i = threadIdx.x; i < tpb * vpr; i += 256) {
+    const int t = t0 + i / vpr, v = i % vpr;
+    if (t >= T) continue;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int pos = tk_row[(size_t)t * k + j];
+      if (pos < 0) continue;
+      const float wj = topk_w[(size_t)t * k + j];
+      const uint4 o = *reinterpret_cast<const uint4*>(O + (size_t)pos * d + v * 8);
+      const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = __builtin_fmaf(wj, bf2f_lo(ow[q]), acc[2 * q]);
+        acc[2 * q + 1] = __builtin_fmaf(wj, bf2f_hi(ow[q]), acc[2 * q + 1]);
+      }
+    }
+    uint4 out;
+    out.x = pack_bf2(acc[0], acc[1]);
+    out.y = pack_bf2(acc[2], acc[3]);
+    out.z = pack_bf2(acc[4], acc[5]);
+    out.w = pack_bf2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(y + (size_t)t * d + v * 8) = out;
+  }
+}
+
+// One thread per token: dw of each of its rows (the down-dgrad epilogue's per-tile partials,
+// summed in ascending tile order) -> d_topk_w; and, when the layer routed itself, the top-k
+// softmax backward dl_j = w_j (dw_j - sum_i w_i dw_i) stored per position.
+__global__ void __launch_bounds__(256) dw_router_kernel(const float* __restrict__ dwpart, int nIt,
+                                                        const int32_t* __restrict__ tk_row,
+                                                        const float* __restrict__ topk_w, int T,
+                                                        int k, float* __restrict__ d_topk_w,
+                                                        float* __restrict__ dl_pos, int routed) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  float s = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const size_t r = (size_t)t * k + j;
+    const int pos = tk_row[r];
+    float dw = 0.f;
+    if (pos >= 0)
+      for (int it = 0; it < nIt; ++it) dw += dwpart[(size_t)pos * nIt + it];
+    d_topk_w[r] = dw;
+    s = __builtin_fmaf(topk_w[r], dw, s);
+  }
+  if (!routed) return;
+  for (int j = 0; j < k; ++j) {
+    const size_t r = (size_t)t * k + j;
+    const int pos = tk_row[r];
+    if (pos >= 0) {
+      const float w = topk_w[r];
+      dl_pos[pos] = w * (d_topk_w[r] - s);
+    }
+  }
+}
+
+// dx[t] = bf16( sum_j dXp[tk_row[t*k+j]] + sum_j dl_j * Wr[e_j] ), j ascending, fp32; the
+// router term only when wr is given.
+__global__ void __launch_bounds__(256) uncombine_kernel(
+    const uint16_t* __restrict__ dXp, const int32_t* __restrict__ tk_row,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ dl_pos,
+    const uint16_t* __restrict__ wr, int T, int k, int d, uint16_t* __restrict__ dx, int tpb) {
+  const int vpr = d / 8;
+  const int t0 = blockIdx.x * tpb;
+  for (int i = threadIdx.x; i < tpb * vpr; i += 256) {
+    const int t = t0 + i / vpr, v = i % vpr;
+    if (t >= T) continue;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int pos = tk_row[(size_t)t * k + j];
+      if (pos < 0) continue;
+      const uint4 g = *reinterpret_cast<const uint4*>(dXp + (size_t)pos * d + v * 8);
+      const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf2f_lo(gw[q]);
+        acc[2 * q + 1] += bf2f_hi(gw[q]);
+      }
+    }
+    if (wr) {
+      for (int j = 0; j < k; ++j) {
+        const int pos = tk_row[(size_t)t * k + j];
+        if (pos < 0) continue;
+        const float dl = dl_pos[pos];
+        const int e = topk_idx[(size_t)t * k + j];
+        const uint4 g = *reinterpret_cast<const uint4*>(wr + (size_t)e * d + v * 8);
+        const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = __builtin_fmaf(dl, bf2f_lo(gw[q]), acc[2 * q]);
+          acc[2 * q + 1] = __builtin_fmaf(dl, bf2f_hi(gw[q]), acc[2 * q + 1]);
+        }
+      }
+    }
+    uint4 out;
+    out.x = pack_bf2(acc[0], acc[1]);
+    out.y = pack_bf2(acc[2], acc[3]);
+    out.z = pack_bf2(acc[4], acc[5]);
+    out.w = pack_bf2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(dx + (size_t)t * d + v * 8) = out;
+  }
+}
+
+// dWr[e, c] = sum over positions p of expert e, ascending, of dl_pos[p] * Xp[p, c] (fp32).
+// Block (cx, e) covers columns [512 cx, 512 cx + 512); each thread owns 8 columns.
+__global__ void __launch_bounds__(64) dwr_kernel(const float* __restrict__ dl_pos,
+                                                 const uint16_t* __restrict__ xp,
+                                                 const int32_t* __restrict__ offsets, int d,
+                                                 float* __restrict__ dwr, int accumulate) {
+  const int e = blockIdx.y;
+  const int c0 = (blockIdx.x * 64 + threadIdx.x) * 8;
+  if (c0 >= d) return;
+  const int p0 = offsets[e], p1 = offsets[e + 1];
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int p = p0; p < p1; ++p) {
+    const float dl = dl_pos[p];
+    const uint4 g = *reinterpret_cast<const uint4*>(xp + (size_t)p * d + c0);
+    const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] = __builtin_fmaf(dl, bf2f_lo(gw[q]), acc[2 * q]);
+      acc[2 * q + 1] = __builtin_fmaf(dl, bf2f_hi(gw[q]), acc[2 * q + 1]);
+    }
+  }
+  float4* dst = reinterpret_cast<float4*>(dwr + (size_t)e * d + c0);
+  float4 a = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  float4 b = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  if (accumulate) {
+    const float4 oa = dst[0], ob = dst[1];
+    a.x += oa.x; a.y += oa.y; a.z += oa.z; a.w += oa.w;
+    b.x += ob.x; b.y += ob.y; b.z += ob.z; b.w += ob.w;
+  }
+  dst[0] = a;
+  dst[1] = b;
+}
+
+hipError_t launch_combine(const uint16_t* O, const int32_t* tk_row, const float* topk_w, int T,
+                          int k, int d, uint16_t* y, hipStream_t s) {
+  const int tpb = rows_per_block(d);
+  hipLaunchKernelGGL(combine_kernel, dim3((T + tpb - 1) / tpb), dim3(256), 0, s, O, tk_row, topk_w,
+                     T, k, d, y, tpb);
+  return hipGetLastError();
+}
+
+hipError_t launch_dw_router(const float* dwpart, int nIt, const int32_t* tk_row,
+                            const float* topk_w, int T, int k, float* d_topk_w, float* dl_pos,
+                            int routed, hipStream_t s) {
+  hipLaunchKernelGGL(dw_router_kernel, dim3((T + 255) / 256), dim3(256), 0, s, dwpart, nIt, tk_row,
+                     topk_w, T, k, d_topk_w, dl_pos, routed);
+  return hipGetLastError();
+}
+
+hipError_t launch_uncombine(const uint16_t* dXp, const int32_t* tk_row, const int32_t* topk_idx,
+                            const float* dl_pos, const uint16_t* wr, int T, int k, int d,
+                            uint16_t* dx, hipStream_t s) {
+  const int tpb = rows_per_block(d);
+  hipLaunchKernelGGL(uncombine_kernel, dim3((T + tpb - 1) / tpb), dim3(256), 0, s, dXp, tk_row,
+                     topk_idx, dl_pos, wr, T, k, d, dx, tpb);
+  return hipGetLastError();
+}
+
+hipError_t launch_dwr(const float* dl_pos, const uint16_t* xp, const int32_t* offsets, int E,
+                      int d, float* dwr, int accumulate, hipStream_t s) {
+  hipLaunchKernelGGL(dwr_kernel, dim3((d + 511) / 512, E), dim3(64), 0, s, dl_pos, xp, offsets, d,
+                     dwr, accumulate);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,827 @@
+// Expert-grouped GEMMs of the MoE layer on gfx950 MFMA (bf16 in, fp32 accumulate).
+//
+// The expert-grouped GEMMs are named in the MarkTechPost page on Mixture-of-Kittens (MoK),
+// section "Three design decisions that matter". There are six products:
+//   fwd  gate/up : [g|u][pos]   = Xp[pos]  . W1[e]^T      SwiGLU in the epilogue
+//   fwd  down    : O[pos]       = A[pos]   . W2[e]^T
+//   bwd  down dg : dA'[pos]     = dY[t]    . W2[e]        SwiGLU backward + router-weight grad
+//   bwd  gate dg : dXp[pos]     = dH[pos]  . W1[e]
+//   bwd  down wg : dW2[e]       = sum_pos (w dY[t])^T A[pos]
+//   bwd  gate wg : dW1[e]       = sum_pos dH[pos]^T Xp[pos]
+// One kernel template runs them all. A workgroup (256 threads, 4 waves) owns a BM x BN output
+// tile. Tiles of BK stream through double-buffered LDS, stored K-contiguous with 8 elements of
+// padding per row, so every MFMA fragment is one 16-byte LDS read. Operands whose K axis is
+// not contiguous in memory (the weights in dgrad, both operands in wgrad) are loaded as 8x8
+// blocks and transposed in registers on their way into LDS.
+//
+// Determinism: every output element is produced by exactly one workgroup, which reduces K in a
+// fixed order. There are no atomics and no split-K.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kThreads = 256;
+
+// ------------------------------------------------------------------------------------------
+// Tile loaders (global -> registers -> LDS)
+
+// ROWS x BK tile whose rows are K-contiguous in memory. Row pointers are fixed per tile; a null
+// row pointer loads zeros.
+template <int ROWS, int BK, int LDK>
+struct LoadK {
+  static constexpr int VPR = BK / 8;
+  static constexpr int NV = ROWS * VPR;
+  static constexpr int PT = (NV + kThreads - 1) / kThreads;
+  const uint16_t* rp[PT];
+  uint4 r[PT];
+
+  template <class RowPtr>
+  MOE_DEV void init(RowPtr rowptr) {
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int v = threadIdx.x + kThreads * j;
+      rp[j] = (v < NV) ? rowptr(v / VPR) : nullptr;
+    }
+  }
+  MOE_DEV void load(int k0) {
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int v = threadIdx.x + kThreads * j;
+      r[j] = rp[j] ? *reinterpret_cast<const uint4*>(rp[j] + k0 + (v % VPR) * 8)
+                   : make_uint4(0, 0, 0, 0);
+    }
+  }
+  MOE_DEV void store(uint16_t* s) const {
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int v = threadIdx.x + kThreads * j;
+      if (v < NV) *reinterpret_cast<uint4*>(s + (v / VPR) * LDK + (v % VPR) * 8) = r[j];
+    }
+  }
+};
+
+// BK x MN tile stored MN-contiguous in memory (K is the slow axis). Loaded as 8x8 blocks whose
+// k-block index runs fastest across lanes (each wave instruction reads 8 rows x 128 contiguous
+// bytes, and the transposed LDS writes of 16 lanes cover all 64 banks), then transposed so
+// LDS holds [MN][K]. krow(k) returns the row pointer already offset to the tile's first MN
+// column, or null for a zero row; kscale(k) multiplies a row (rounded back to bf16) when SCALED.
+template <int MN, int BK, int LDK, bool SCALED>
+struct LoadMN {
+  static constexpr int BKB = BK / 8;
+  static constexpr int NB = (MN / 8) * BKB;
+  static constexpr int PT = (NB + kThreads - 1) / kThreads;
+  uint4 r[PT][8];
+
+  template <class KRow, class KScale>
+  MOE_DEV void load(int k0, KRow krow, KScale kscale) {
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int b = threadIdx.x + kThreads * j;
+      if (b < NB) {
+        const int kb = b % BKB, mb = b / BKB;
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          const int k = k0 + kb * 8 + rr;
+          const uint16_t* p = krow(k);
+          uint4 v = p ? *reinterpret_cast<const uint4*>(p + mb * 8) : make_uint4(0, 0, 0, 0);
+          if constexpr (SCALED) {
+            if (p) {
+              const float s = kscale(k);
+              v.x = pack_bf2(bf2f_lo(v.x) * s, bf2f_hi(v.x) * s);
+              v.y = pack_bf2(bf2f_lo(v.y) * s, bf2f_hi(v.y) * s);
+              v.z = pack_bf2(bf2f_lo(v.z) * s, bf2f_hi(v.z) * s);
+              v.w = pack_bf2(bf2f_lo(v.w) * s, bf2f_hi(v.w) * s);
+            }
+          }
+          r[j][rr] = v;
+        }
+      }
+    }
+  }
+  MOE_DEV void store(uint16_t* s) const {
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int b = threadIdx.x + kThreads * j;
+      if (b < NB) {
+        const int kb = b % BKB, mb = b / BKB;
+        uint4 t[8];
+        transpose8x8_b16(r[j], t);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          *reinterpret_cast<uint4*>(s + (mb * 8 + c) * LDK + kb * 8) = t[c];
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------------
+// Tile geometry shared by all problems
+
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+struct Geo {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int MB = WM / 16, NB = WN / 16;
+  static constexpr int LDK = BK + 8;
+  static constexpr int STAGE = (BM + BN) * LDK;  // uint16 elements per LDS stage
+  static_assert(WAVES_M * WAVES_N == 4, "4 waves per workgroup");
+  static_assert(BK % 32 == 0 && WM % 16 == 0 && WN % 16 == 0, "tile shape");
+};
+
+// Row segment of one expert for dynamic-M problems: table entry -> (expert, first row).
+struct MTile {
+  int e, row0, mcount;
+};
+MOE_DEV MTile decode_mtile(const int2* sched, const int32_t* offsets, int mt, int BM) {
+  const int2 ent = sched[1 + mt];
+  MTile t;
+  t.e = ent.x;
+  t.row0 = offsets[ent.x] + ent.y;
+  t.mcount = min(BM, offsets[ent.x + 1] - t.row0);
+  return t;
+}
+
+// ------------------------------------------------------------------------------------------
+// Problem 1: forward gate/up GEMM with the SwiGLU epilogue.
+// B rows 0..BN/2-1 of the LDS tile are gate rows n0.. of W1[e], rows BN/2.. the matching up
+// rows I+n0..; wave w owns gate columns [w*WN/2, (w+1)*WN/2) and the same up columns, so each
+// lane holds g and u for the same (row, column) and can finish SwiGLU in registers.
+struct FwdGateUp {
+  using G = Geo<128, 128, 64, 1, 4>;
+  struct Args {
+    const uint16_t* xp;    // [T*k, d]
+    const uint16_t* w1;    // [E, 2I, d]
+    uint16_t* H;           // [T*k, 2I]
+    uint16_t* A;           // [T*k, I]
+    const int32_t* offsets;
+    const int2* sched;
+    int d, I;
+  };
+  struct Tile {
+    MTile m;
+    int n0;  // first gate column
+  };
+  static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.I / (G::BN / 2)); }
+  static MOE_DEV Tile decode(const Args& a, int lt) {
+    const int nt_count = a.I / (G::BN / 2);
+    Tile t;
+    t.m = decode_mtile(a.sched, a.offsets, lt / nt_count, G::BM);
+    t.n0 = (lt % nt_count) * (G::BN / 2);
+    return t;
+  }
+  static MOE_DEV int num_k(const Args& a, const Tile&) { return a.d / G::BK; }
+  static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
+  static MOE_DEV int brow(int wn, int nb) {  // LDS B row of n-block nb for wave wn
+    constexpr int H2 = G::BN / 2, WH = G::WN / 2;
+    return nb < G::NB / 2 ? wn * WH + nb * 16 : H2 + wn * WH + (nb - G::NB / 2) * 16;
+  }
+  struct Loader {
+    LoadK<G::BM, G::BK, G::LDK> la;
+    LoadK<G::BN, G::BK, G::LDK> lb;
+    MOE_DEV void init(const Args& a, const Tile& t) {
+      const uint16_t* xp = a.xp;
+      const int d = a.d, mc = t.m.mcount, row0 = t.m.row0;
+      la.init([&](int m) { return m < mc ? xp + (size_t)(row0 + m) * d : nullptr; });
+      const uint16_t* w = a.w1 + (size_t)t.m.e * 2 * a.I * d;
+      const int n0 = t.n0, I = a.I;
+      lb.init([&](int n) {
+        const int row = n < G::BN / 2 ? n0 + n : I + n0 + n - G::BN / 2;
+        return w + (size_t)row * d;
+      });
+    }
+    MOE_DEV void load(int kt) {
+      la.load(kt * G::BK);
+      lb.load(kt * G::BK);
+    }
+    MOE_DEV void store(uint16_t* s) const {
+      la.store(s);
+      lb.store(s + G::BM * G::LDK);
+    }
+  };
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
+                               uint16_t*) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int wn = wave % G::WAVES_N;
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+      const int m = mb * 16 + lane % 16;
+      if (m >= t.m.mcount) continue;
+      const size_t pos = t.m.row0 + m;
+#pragma unroll
+      for (int nb = 0; nb < G::NB / 2; ++nb) {
+        const int j = t.n0 + wn * (G::WN / 2) + nb * 16 + 4 * (lane / 16);
+        const f32x4 g = acc[mb][nb], u = acc[mb][nb + G::NB / 2];
+        uint2 hg, hu, av;
+        hg.x = pack_bf2(g[0], g[1]);
+        hg.y = pack_bf2(g[2], g[3]);
+        hu.x = pack_bf2(u[0], u[1]);
+        hu.y = pack_bf2(u[2], u[3]);
+        av.x = pack_bf2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
+        av.y = pack_bf2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
+        *reinterpret_cast<uint2*>(a.H + pos * 2 * a.I + j) = hg;
+        *reinterpret_cast<uint2*>(a.H + pos * 2 * a.I + a.I + j) = hu;
+        *reinterpret_cast<uint2*>(a.A + pos * a.I + j) = av;
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------------
+// Problem 2: forward down GEMM. O[pos] = A[pos] . W2[e]^T, stored bf16.
+struct FwdDown {
+  using G = Geo<128, 128, 64, 1, 4>;
+  struct Args {
+    const uint16_t* A;   // [T*k, I]
+    const uint16_t* w2;  // [E, d, I]
+    uint16_t* O;         // [T*k, d]
+    const int32_t* offsets;
+    const int2* sched;
+    int d, I;
+  };
+  struct Tile {
+    MTile m;
+    int n0;
+  };
+  static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.d / G::BN); }
+  static MOE_DEV Tile decode(const Args& a, int lt) {
+    const int ntc = a.d / G::BN;
+    Tile t;
+    t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
+    t.n0 = (lt % ntc) * G::BN;
+    return t;
+  }
+  static MOE_DEV int num_k(const Args& a, const Tile&) { return a.I / G::BK; }
+  static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
+  static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
+  struct Loader {
+    LoadK<G::BM, G::BK, G::LDK> la;
+    LoadK<G::BN, G::BK, G::LDK> lb;
+    MOE_DEV void init(const Args& a, const Tile& t) {
+      const uint16_t* A = a.A;
+      const int I = a.I, mc = t.m.mcount, row0 = t.m.row0;
+      la.init([&](int m) { return m < mc ? A + (size_t)(row0 + m) * I : nullptr; });
+      const uint16_t* w = a.w2 + ((size_t)t.m.e * a.d + t.n0) * I;
+      lb.init([&](int n) { return w + (size_t)n * I; });
+    }
+    MOE_DEV void load(int kt) {
+      la.load(kt * G::BK);
+      lb.load(kt * G::BK);
+    }
+    MOE_DEV void store(uint16_t* s) const {
+      la.store(s);
+      lb.store(s + G::BM * G::LDK);
+    }
+  };
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
+                               uint16_t*) {
+    const int lane = threadIdx.x % kWave, wn = (threadIdx.x / kWave) % G::WAVES_N;
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+      const int m = mb * 16 + lane % 16;
+      if (m >= t.m.mcount) continue;
+      const size_t pos = t.m.row0 + m;
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) {
+        const int n = t.n0 + wn * G::WN + nb * 16 + 4 * (lane / 16);
+        uint2 o;
+        o.x = pack_bf2(acc[mb][nb][0], acc[mb][nb][1]);
+        o.y = pack_bf2(acc[mb][nb][2], acc[mb][nb][3]);
+        *reinterpret_cast<uint2*>(a.O + pos * a.d + n) = o;
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------------
+// Problem 3: backward down dgrad with the SwiGLU backward and the router-weight gradient fused
+// into the epilogue. dA'[pos, i] = sum_n dY[t, n] W2[e][n, i] with t = row_src[pos] / k.
+// Epilogue per (pos, i): partial dw += dA' * A (summed over the tile's columns in a fixed
+// order: register, then lane groups, then waves), dA = w dA', and the SwiGLU derivative.
+struct BwdDownDgrad {
+  using G = Geo<128, 128, 64, 1, 4>;
+  struct Args {
+    const uint16_t* dy;      // [T, d]
+    const int32_t* row_src;  // [T*k]
+    const float* topk_w;     // [T*k] flat (row r)
+    const uint16_t* w2;      // [E, d, I]
+    const uint16_t* H;       // [T*k, 2I]
+    const uint16_t* A;       // [T*k, I]
+    uint16_t* dH;            // [T*k, 2I]
+    float* dwpart;           // [T*k, I / BN]
+    const int32_t* offsets;
+    const int2* sched;
+    int d, I, k;
+  };
+  struct Tile {
+    MTile m;
+    int n0;
+  };
+  static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.I / G::BN); }
+  static MOE_DEV Tile decode(const Args& a, int lt) {
+    const int ntc = a.I / G::BN;
+    Tile t;
+    t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
+    t.n0 = (lt % ntc) * G::BN;
+    return t;
+  }
+  static MOE_DEV int num_k(const Args& a, const Tile&) { return a.d / G::BK; }
+  static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
+  static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
+  struct Loader {
+    LoadK<G::BM, G::BK, G::LDK> la;
+    LoadMN<G::BN, G::BK, G::LDK, false> lb;
+    const uint16_t* wb;
+    int ldw;
+    MOE_DEV void init(const Args& a, const Tile& t) {
+      const uint16_t* dy = a.dy;
+      const int32_t* rs = a.row_src;
+      const int d = a.d, k = a.k, mc = t.m.mcount, row0 = t.m.row0;
+      la.init([&](int m) { return m < mc ? dy + (size_t)(rs[row0 + m] / k) * d : nullptr; });
+      wb = a.w2 + (size_t)t.m.e * a.d * a.I + t.n0;
+      ldw = a.I;
+    }
+    MOE_DEV void load(int kt) {
+      la.load(kt * G::BK);
+      const uint16_t* w = wb;
+      const int ld = ldw;
+      lb.load(kt * G::BK, [&](int k) { return w + (size_t)k * ld; }, [](int) { return 1.0f; });
+    }
+    MOE_DEV void store(uint16_t* s) const {
+      la.store(s);
+      lb.store(s + G::BM * G::LDK);
+    }
+  };
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
+                               uint16_t* smem) {
+    const int lane = threadIdx.x % kWave, wn = (threadIdx.x / kWave) % G::WAVES_N;
+    float* red = reinterpret_cast<float*>(smem);  // [WAVES_N][BM]; LDS is free after the K loop
+    const int I = a.I;
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+      const int m = mb * 16 + lane % 16;
+      const bool live = m < t.m.mcount;
+      float part = 0.f;
+      if (live) {
+        const size_t pos = t.m.row0 + m;
+        const float w = a.topk_w[a.row_src[pos]];
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb) {
+          const int i = t.n0 + wn * G::WN + nb * 16 + 4 * (lane / 16);
+          const uint2 av = *reinterpret_cast<const uint2*>(a.A + pos * I + i);
+          const uint2 gv = *reinterpret_cast<const uint2*>(a.H + pos * 2 * I + i);
+          const uint2 uv = *reinterpret_cast<const uint2*>(a.H + pos * 2 * I + I + i);
+          const float av4[4] = {bf2f_lo(av.x), bf2f_hi(av.x), bf2f_lo(av.y), bf2f_hi(av.y)};
+          const float g4[4] = {bf2f_lo(gv.x), bf2f_hi(gv.x), bf2f_lo(gv.y), bf2f_hi(gv.y)};
+          const float u4[4] = {bf2f_lo(uv.x), bf2f_hi(uv.x), bf2f_lo(uv.y), bf2f_hi(uv.y)};
+          float dg[4], du[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float dap = acc[mb][nb][r];
+            part = __builtin_fmaf(dap, av4[r], part);
+            const float dA = w * dap;
+            const float s = sigmoid(g4[r]);
+            dg[r] = dA * u4[r] * s * (1.0f + g4[r] * (1.0f - s));
+            du[r] = dA * (g4[r] * s);
+          }
+          uint2 o;
+          o.x = pack_bf2(dg[0], dg[1]);
+          o.y = pack_bf2(dg[2], dg[3]);
+          *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + i) = o;
+          o.x = pack_bf2(du[0], du[1]);
+          o.y = pack_bf2(du[2], du[3]);
+          *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + I + i) = o;
+        }
+      }
+      // lanes l, l^16, l^32, l^48 share row m: butterfly in a fixed pattern
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      if (lane < 16) red[wn * G::BM + m] = part;
+    }
+    __syncthreads();
+    if (threadIdx.x < G::BM && threadIdx.x < t.m.mcount) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < G::WAVES_N; ++w) s += red[w * G::BM + threadIdx.x];
+      const size_t pos = t.m.row0 + threadIdx.x;
+      a.dwpart[pos * (a.I / G::BN) + t.n0 / G::BN] = s;
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------------
+// Problem 4: backward gate/up dgrad. dXp[pos] = dH[pos] . W1[e], stored bf16.
+struct BwdGateDgrad {
+  using G = Geo<128, 128, 64, 1, 4>;
+  struct Args {
+    const uint16_t* dH;  // [T*k, 2I]
+    const uint16_t* w1;  // [E, 2I, d]
+    uint16_t* dXp;       // [T*k, d]
+    const int32_t* offsets;
+    const int2* sched;
+    int d, I;
+  };
+  struct Tile {
+    MTile m;
+    int n0;
+  };
+  static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.d / G::BN); }
+  static MOE_DEV Tile decode(const Args& a, int lt) {
+    const int ntc = a.d / G::BN;
+    Tile t;
+    t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
+    t.n0 = (lt % ntc) * G::BN;
+    return t;
+  }
+  static MOE_DEV int num_k(const Args& a, const Tile&) { return 2 * a.I / G::BK; }
+  static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
+  static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
+  struct Loader {
+    LoadK<G::BM, G::BK, G::LDK> la;
+    LoadMN<G::BN, G::BK, G::LDK, false> lb;
+    const uint16_t* wb;
+    int ldw;
+    MOE_DEV void init(const Args& a, const Tile& t) {
+      const uint16_t* dH = a.dH;
+      const int twoI = 2 * a.I, mc = t.m.mcount, row0 = t.m.row0;
+      la.init([&](int m) { return m < mc ? dH + (size_t)(row0 + m) * twoI : nullptr; });
+      wb = a.w1 + (size_t)t.m.e * 2 * a.I * a.d + t.n0;
+      ldw = a.d;
+    }
+    MOE_DEV void load(int kt) {
+      la.load(kt * G::BK);
+      const uint16_t* w = wb;
+      const int ld = ldw;
+      lb.load(kt * G::BK, [&](int k) { return w + (size_t)k * ld; }, [](int) { return 1.0f; });
+    }
+    MOE_DEV void store(uint16_t* s) const {
+      la.store(s);
+      lb.store(s + G::BM * G::LDK);
+    }
+  };
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
+                               uint16_t*) {
+    const int lane = threadIdx.x % kWave, wn = (threadIdx.x / kWave) % G::WAVES_N;
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+      const int m = mb * 16 + lane % 16;
+      if (m >= t.m.mcount) continue;
+      const size_t pos = t.m.row0 + m;
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) {
+        const int n = t.n0 + wn * G::WN + nb * 16 + 4 * (lane / 16);
+        uint2 o;
+        o.x = pack_bf2(acc[mb][nb][0], acc[mb][nb][1]);
+        o.y = pack_bf2(acc[mb][nb][2], acc[mb][nb][3]);
+        *reinterpret_cast<uint2*>(a.dXp + pos * a.d + n) = o;
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------------
+// Weight gradients: K runs over the positions of one expert, in ascending order, in chunks of
+// BK; the ragged tail is zero-filled. Output rows are weight rows (no position mapping); empty
+// experts write zero blocks (or leave accumulated ones untouched).
+struct WgradTile {
+  int e, m0, n0, p0, p1;
+};
+
+// Problem 5: dW2[e][n, i] = sum_pos bf16(w[pos] dY[t(pos), n]) * A[pos, i].
+struct BwdDownWgrad {
+  using G = Geo<128, 128, 32, 2, 2>;
+  struct Args {
+    const uint16_t* dy;      // [T, d]
+    const int32_t* row_src;  // [T*k]
+    const float* topk_w;     // [T*k]
+    const uint16_t* A;       // [T*k, I]
+    float* dw2;              // [E, d, I]
+    const int32_t* offsets;
+    int d, I, k, E, accumulate;
+  };
+  using Tile = WgradTile;
+  static MOE_DEV int ntiles(const Args& a) { return a.E * (a.d / G::BM) * (a.I / G::BN); }
+  static MOE_DEV Tile decode(const Args& a, int lt) {
+    const int ntn = a.I / G::BN, ntm = a.d / G::BM;
+    Tile t;
+    t.e = lt / (ntm * ntn);
+    const int r = lt % (ntm * ntn);
+    t.m0 = (r / ntn) * G::BM;
+    t.n0 = (r % ntn) * G::BN;
+    t.p0 = a.offsets[t.e];
+    t.p1 = a.offsets[t.e + 1];
+    return t;
+  }
+  static MOE_DEV int num_k(const Args&, const Tile& t) { return (t.p1 - t.p0 + G::BK - 1) / G::BK; }
+  static MOE_DEV bool m_active(const Tile&, int) { return true; }
+  static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
+  struct Loader {
+    LoadMN<G::BM, G::BK, G::LDK, true> la;
+    LoadMN<G::BN, G::BK, G::LDK, false> lb;
+    const uint16_t* dy;  // offset to the tile's first row m0
+    const uint16_t* A;   // offset to the tile's first column n0
+    const int32_t* rs;
+    const float* tw;
+    int p0, p1, d, I, k;
+    MOE_DEV void init(const Args& a, const Tile& t) {
+      dy = a.dy + t.m0;
+      A = a.A + t.n0;
+      rs = a.row_src;
+      tw = a.topk_w;
+      p0 = t.p0;
+      p1 = t.p1;
+      d = a.d;
+      I = a.I;
+      k = a.k;
+    }
+    MOE_DEV void load(int kt) {
+      const int pbase = p0 + kt * G::BK;
+      la.load(
+          pbase,
+          [&](int p) { return p < p1 ? dy + (size_t)(rs[p] / k) * d : nullptr; },
+          [&](int p) { return tw[rs[p]]; });
+      lb.load(
+          pbase, [&](int p) { return p < p1 ? A + (size_t)p * I : nullptr; },
+          [](int) { return 1.0f; });
+    }
+    MOE_DEV void store(uint16_t* s) const {
+      la.store(s);
+      lb.store(s + G::BM * G::LDK);
+    }
+  };
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
+                               uint16_t*) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
+    float* out = a.dw2 + (size_t)t.e * a.d * a.I;
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+      const int m = t.m0 + wm * G::WM + mb * 16 + lane % 16;
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) {
+        const int n = t.n0 + wn * G::WN + nb * 16 + 4 * (lane / 16);
+        float4* dst = reinterpret_cast<float4*>(out + (size_t)m * a.I + n);
+        float4 v = make_float4(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]);
+        if (a.accumulate) {
+          const float4 o = *dst;
+          v.x += o.x;
+          v.y += o.y;
+          v.z += o.z;
+          v.w += o.w;
+        }
+        *dst = v;
+      }
+    }
+  }
+};
+
+// Problem 6: dW1[e][n, c] = sum_pos dH[pos, n] * Xp[pos, c].
+struct BwdGateWgrad {
+  using G = Geo<128, 128, 32, 2, 2>;
+  struct Args {
+    const uint16_t* dH;  // [T*k, 2I]
+    const uint16_t* xp;  // [T*k, d]
+    float* dw1;          // [E, 2I, d]
+    const int32_t* offsets;
+    int d, I, E, accumulate;
+  };
+  using Tile = WgradTile;
+  static MOE_DEV int ntiles(const Args& a) { return a.E * (2 * a.I / G::BM) * (a.d / G::BN); }
+  static MOE_DEV Tile decode(const Args& a, int lt) {
+    const int ntn = a.d / G::BN, ntm = 2 * a.I / G::BM;
+    Tile t;
+    t.e = lt / (ntm * ntn);
+    const int r = lt % (ntm * ntn);
+    t.m0 = (r / ntn) * G::BM;
+    t.n0 = (r % ntn) * G::BN;
+    t.p0 = a.offsets[t.e];
+    t.p1 = a.offsets[t.e + 1];
+    return t;
+  }
+  static MOE_DEV int num_k(const Args&, const Tile& t) { return (t.p1 - t.p0 + G::BK - 1) / G::BK; }
+  static MOE_DEV bool m_active(const Tile&, int) { return true; }
+  static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
+  struct Loader {
+    LoadMN<G::BM, G::BK, G::LDK, false> la;
+    LoadMN<G::BN, G::BK, G::LDK, false> lb;
+    const uint16_t* dH;  // offset to the tile's first row m0
+    const uint16_t* xp;  // offset to the tile's first column n0
+    int p0, p1, twoI, d;
+    MOE_DEV void init(const Args& a, const Tile& t) {
+      dH = a.dH + t.m0;
+      xp = a.xp + t.n0;
+      p0 = t.p0;
+      p1 = t.p1;
+      twoI = 2 * a.I;
+      d = a.d;
+    }
+    MOE_DEV void load(int kt) {
+      const int pbase = p0 + kt * G::BK;
+      la.load(
+          pbase, [&](int p) { return p < p1 ? dH + (size_t)p * twoI : nullptr; },
+          [](int) { return 1.0f; });
+      lb.load(
+          pbase, [&](int p) { return p < p1 ? xp + (size_t)p * d : nullptr; },
+          [](int) { return 1.0f; });
+    }
+    MOE_DEV void store(uint16_t* s) const {
+      la.store(s);
+      lb.store(s + G::BM * G::LDK);
+    }
+  };
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
+                               uint16_t*) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
+    float* out = a.dw1 + (size_t)t.e * 2 * a.I * a.d;
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+      const int m = t.m0 + wm * G::WM + mb * 16 + lane % 16;
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) {
+        const int n = t.n0 + wn * G::WN + nb * 16 + 4 * (lane / 16);
+        float4* dst = reinterpret_cast<float4*>(out + (size_t)m * a.d + n);
+        float4 v = make_float4(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]);
+        if (a.accumulate) {
+          const float4 o = *dst;
+          v.x += o.x;
+          v.y += o.y;
+          v.z += o.z;
+          v.w += o.w;
+        }
+        *dst = v;
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------------
+// The kernel: walks logical tiles. Each XCD owns one contiguous range of them (so the
+// workgroups sharing an expert's activations share that XCD's L2), striding by the grid within
+// the range. One-shot launches size the grid to cover every tile once; persistent launches
+// use a resident grid that loops.
+
+template <class P>
+MOE_DEV void run_tile(const typename P::Args& a, const typename P::Tile& t, uint16_t* smem) {
+  using G = typename P::G;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
+  f32x4 acc[G::MB][G::NB];
+#pragma unroll
+  for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = P::num_k(a, t);
+  if (nk > 0) {
+    typename P::Loader ld;
+    ld.init(a, t);
+    ld.load(0);
+    ld.store(smem);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      uint16_t* cur = smem + (kt & 1) * G::STAGE;
+      if (kt + 1 < nk) ld.load(kt + 1);
+      const uint16_t* sA = cur;
+      const uint16_t* sB = cur + G::BM * G::LDK;
+#pragma unroll
+      for (int ks = 0; ks < G::BK / 32; ++ks) {
+        const int koff = ks * 32 + (lane / 16) * 8;
+        uint4 bf[G::NB];
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb)
+          bf[nb] = *reinterpret_cast<const uint4*>(sB + (P::brow(wn, nb) + lane % 16) * G::LDK + koff);
+#pragma unroll
+        for (int mb = 0; mb < G::MB; ++mb) {
+          if (!P::m_active(t, wm * G::WM + mb * 16)) continue;
+          const uint4 af =
+              *reinterpret_cast<const uint4*>(sA + (wm * G::WM + mb * 16 + lane % 16) * G::LDK + koff);
+#pragma unroll
+          for (int nb = 0; nb < G::NB; ++nb) acc[mb][nb] = mfma16(bf[nb], af, acc[mb][nb]);
+        }
+      }
+      if (kt + 1 < nk) ld.store(smem + ((kt + 1) & 1) * G::STAGE);
+      __syncthreads();
+    }
+  }
+  P::epilogue(a, t, acc, smem);
+  __syncthreads();
+}
+
+template <class P>
+__global__ void __launch_bounds__(kThreads, 2) gg_kernel(const typename P::Args a) {
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int ntiles = P::ntiles(a);
+  const int R = (ntiles + kXcds - 1) / kXcds;
+  const int b = blockIdx.x, step = gridDim.x / kXcds;
+  for (int s = b / kXcds; s < R; s += step) {
+    const int lt = (b % kXcds) * R + s;
+    if (lt >= ntiles) break;
+    const typename P::Tile t = P::decode(a, lt);
+    run_tile<P>(a, t, smem);
+  }
+}
+
+template <class P>
+static size_t smem_bytes() {
+  return 2 * P::G::STAGE * sizeof(uint16_t);
+}
+
+// Grid: one-shot grids cover `max_tiles` (rounded up to a multiple of 8); persistent grids
+// are the resident workgroup count, also a multiple of 8.
+template <class P>
+static hipError_t launch(const typename P::Args& a, int max_tiles, bool persistent,
+                         hipStream_t stream) {
+  if (max_tiles <= 0) return hipSuccess;
+  const size_t sm = smem_bytes<P>();
+  static bool attr_set = false;  // benign race: every caller sets the same value
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gg_kernel<P>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  int grid = (max_tiles + kXcds - 1) / kXcds * kXcds;
+  if (persistent) {
+    static int resident = 0;  // per kernel; every device of one process is an MI355X
+    if (resident == 0) {
+      int dev = 0, cus = 0, per_cu = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&gg_kernel<P>), kThreads, sm);
+      if (e != hipSuccess) return e;
+      resident = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
+    }
+    if (resident > 0 && resident < grid) grid = resident;
+  }
+  hipLaunchKernelGGL(gg_kernel<P>, dim3(grid), dim3(kThreads), sm, stream, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Schedule table: one entry per (expert, 128-row block) of the permuted rows, built on the
+// device from the offsets so the host never learns the counts. Entry 0 holds the count.
+
+__global__ void __launch_bounds__(1024) sched_build_kernel(const int32_t* offsets, int E, int BM,
+                                                           int2* sched) {
+  __shared__ int scan[1024];
+  const int e = threadIdx.x;
+  const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+  const int tiles = (c + BM - 1) / BM;
+  scan[e] = tiles;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over 1024 entries
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = e >= off ? scan[e - off] : 0;
+    __syncthreads();
+    scan[e] += v;
+    __syncthreads();
+  }
+  const int start = scan[e] - tiles;
+  for (int i = 0; i < tiles; ++i) sched[1 + start + i] = make_int2(e, i * BM);
+  if (e == 1023) sched[0] = make_int2(scan[1023], 0);
+}
+
+int sched_max_mtiles(int Tk, int E) { return (Tk + E * (kSchedBM - 1)) / kSchedBM; }
+
+hipError_t launch_sched_build(const int32_t* offsets, int E, int2* sched, hipStream_t s) {
+  hipLaunchKernelGGL(sched_build_kernel, dim3(1), dim3(1024), 0, s, offsets, E, kSchedBM, sched);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_gateup(const GemmFwdGateUpArgs& x, bool persistent, hipStream_t s) {
+  FwdGateUp::Args a{x.xp, x.w1, x.H, x.A, x.offsets, x.sched, x.d, x.I};
+  return launch<FwdGateUp>(a, sched_max_mtiles(x.Tk, x.E) * (x.I / 64), persistent, s);
+}
+
+hipError_t launch_fwd_down(const GemmFwdDownArgs& x, bool persistent, hipStream_t s) {
+  FwdDown::Args a{x.A, x.w2, x.O, x.offsets, x.sched, x.d, x.I};
+  return launch<FwdDown>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
+}
+
+hipError_t launch_bwd_down_dgrad(const GemmBwdDownDgradArgs& x, bool persistent, hipStream_t s) {
+  BwdDownDgrad::Args a{x.dy, x.row_src, x.topk_w, x.w2, x.H, x.A, x.dH, x.dwpart,
+                       x.offsets, x.sched, x.d, x.I, x.k};
+  return launch<BwdDownDgrad>(a, sched_max_mtiles(x.Tk, x.E) * (x.I / 128), persistent, s);
+}
+
+hipError_t launch_bwd_gate_dgrad(const GemmBwdGateDgradArgs& x, bool persistent, hipStream_t s) {
+  BwdGateDgrad::Args a{x.dH, x.w1, x.dXp, x.offsets, x.sched, x.d, x.I};
+  return launch<BwdGateDgrad>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
+}
+
+hipError_t launch_bwd_down_wgrad(const GemmBwdDownWgradArgs& x, bool persistent, hipStream_t s) {
+  BwdDownWgrad::Args a{x.dy, x.row_src, x.topk_w, x.A, x.dw2, x.offsets,
+                       x.d, x.I, x.k, x.E, x.accumulate};
+  return launch<BwdDownWgrad>(a, x.E * (x.d / 128) * (x.I / 128), persistent, s);
+}
+
+hipError_t launch_bwd_gate_wgrad(const GemmBwdGateWgradArgs& x, bool persistent, hipStream_t s) {
+  BwdGateWgrad::Args a{x.dH, x.xp, x.dw1, x.offsets, x.d, x.I, x.E, x.accumulate};
+  return launch<BwdGateWgrad>(a, x.E * (2 * x.I / 128) * (x.d / 128), persistent, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,107 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels. Every function
+// only enqueues on the given stream and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kSchedBM = 128;   // rows per M-tile of the forward/dgrad grouped GEMMs
+constexpr int kDgradBN = 128;   // columns per N-tile of the down dgrad (dw partials per row)
+constexpr int kPermRows = 256;  // rows per histogram block of the permutation
+constexpr int kMaxTopK = 64;
+
+// router.hip
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, float* logits, int T,
+                                int d, int E, hipStream_t s);
+hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                              hipStream_t s);
+
+// permute.hip
+hipError_t launch_perm_hist(const int32_t* idx, int Tk, int E, int32_t* blk_cnt, int32_t* rank,
+                            int32_t* blk_flag, hipStream_t s);
+hipError_t launch_perm_scan(int32_t* blk_cnt, int nb, int E, const int32_t* blk_flag,
+                            int32_t* counts, int32_t* offsets, int32_t* status, hipStream_t s);
+hipError_t launch_perm_place(const int32_t* idx, const int32_t* rank, const int32_t* blk_base,
+                             int Tk, int E, int k, int32_t* row_src, int32_t* tk_row,
+                             const uint16_t* x, uint16_t* xp, int d, hipStream_t s);
+
+// gemm.hip
+int sched_max_mtiles(int Tk, int E);
+hipError_t launch_sched_build(const int32_t* offsets, int E, int2* sched, hipStream_t s);
+
+struct GemmFwdGateUpArgs {
+  const uint16_t* xp;
+  const uint16_t* w1;
+  uint16_t* H;
+  uint16_t* A;
+  const int32_t* offsets;
+  const int2* sched;
+  int d, I, Tk, E;
+};
+struct GemmFwdDownArgs {
+  const uint16_t* A;
+  const uint16_t* w2;
+  uint16_t* O;
+  const int32_t* offsets;
+  const int2* sched;
+  int d, I, Tk, E;
+};
+struct GemmBwdDownDgradArgs {
+  const uint16_t* dy;
+  const int32_t* row_src;
+  const float* topk_w;
+  const uint16_t* w2;
+  const uint16_t* H;
+  const uint16_t* A;
+  uint16_t* dH;
+  float* dwpart;
+  const int32_t* offsets;
+  const int2* sched;
+  int d, I, k, Tk, E;
+};
+struct GemmBwdGateDgradArgs {
+  const uint16_t* dH;
+  const uint16_t* w1;
+  uint16_t* dXp;
+  const int32_t* offsets;
+  const int2* sched;
+  int d, I, Tk, E;
+};
+struct GemmBwdDownWgradArgs {
+  const uint16_t* dy;
+  const int32_t* row_src;
+  const float* topk_w;
+  const uint16_t* A;
+  float* dw2;
+  const int32_t* offsets;
+  int d, I, k, E, accumulate;
+};
+struct GemmBwdGateWgradArgs {
+  const uint16_t* dH;
+  const uint16_t* xp;
+  float* dw1;
+  const int32_t* offsets;
+  int d, I, E, accumulate;
+};
+hipError_t launch_fwd_gateup(const GemmFwdGateUpArgs& a, bool persistent, hipStream_t s);
+hipError_t launch_fwd_down(const GemmFwdDownArgs& a, bool persistent, hipStream_t s);
+hipError_t launch_bwd_down_dgrad(const GemmBwdDownDgradArgs& a, bool persistent, hipStream_t s);
+hipError_t launch_bwd_gate_dgrad(const GemmBwdGateDgradArgs& a, bool persistent, hipStream_t s);
+hipError_t launch_bwd_down_wgrad(const GemmBwdDownWgradArgs& a, bool persistent, hipStream_t s);
+hipError_t launch_bwd_gate_wgrad(const GemmBwdGateWgradArgs& a, bool persistent, hipStream_t s);
+
+// elementwise.hip
+hipError_t launch_combine(const uint16_t* O, const int32_t* tk_row, const float* topk_w, int T,
+                          int k, int d, uint16_t* y, hipStream_t s);
+hipError_t launch_dw_router(const float* dwpart, int nIt, const int32_t* tk_row,
+                            const float* topk_w, int T, int k, float* d_topk_w, float* dl_pos,
+                            int routed, hipStream_t s);
+hipError_t launch_uncombine(const uint16_t* dXp, const int32_t* tk_row, const int32_t* topk_idx,
+                            const float* dl_pos, const uint16_t* wr, int T, int k, int d,
+                            uint16_t* dx, hipStream_t s);
+hipError_t launch_dwr(const float* dl_pos, const uint16_t* xp, const int32_t* offsets, int E,
+                      int d, float* dwr, int accumulate, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,147 @@
+// Deterministic expert permutation into a ring slot: per-block histograms, an exclusive scan,
+// then a stable placement of every row and the copy of its token into the slot.
+//
+// The ring token buffer of the MarkTechPost page ("Three design decisions that matter") has a
+// fixed size, drops no tokens and keeps the CPU out of the loop. Here the slot holds T*k rows,
+// the worst case, so no expert imbalance can overflow it. The counts stay on the device.
+// Row r = t*k + j of expert e lands at offsets[e] + (rows r' < r of expert e), so segments
+// ascend by r.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// Block b owns rows [256 b, 256 b + 256): per-expert counts of the block, and each row's rank
+// among the block's earlier rows of the same expert (a direct count, so it is stable).
+__global__ void __launch_bounds__(kPermRows) perm_hist_kernel(const int32_t* __restrict__ idx,
+                                                              int Tk, int E,
+                                                              int32_t* __restrict__ blk_cnt,
+                                                              int32_t* __restrict__ rank,
+                                                              int32_t* __restrict__ blk_flag) {
+  __shared__ int sh_e[kPermRows];
+  __shared__ int sh_cnt[1024];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int r = b * kPermRows + tid;
+  for (int i = tid; i < E; i += kPermRows) sh_cnt[i] = 0;
+  int e = -1;
+  int bad = 0;
+  if (r < Tk) {
+    e = idx[r];
+    if (e < 0 || e >= E) {
+      bad = 1;
+      e = -1;
+    }
+  }
+  sh_e[tid] = e;
+  __syncthreads();
+  if (e >= 0) atomicAdd(&sh_cnt[e], 1);  // integer counts: the result is order independent
+  int rk = 0;
+  for (int j = 0; j < tid; ++j) rk += (sh_e[j] == e);
+  const int any_bad = __syncthreads_or(bad);
+  if (r < Tk) rank[r] = e >= 0 ? rk : -1;
+  for (int i = tid; i < E; i += kPermRows) blk_cnt[(size_t)b * E + i] = sh_cnt[i];
+  if (tid == 0) blk_flag[b] = any_bad;
+}
+
+// One workgroup: column-wise exclusive scan of the block counts (block order), expert totals,
+// an exclusive scan over experts, and the per-block base positions.
+__global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ blk_cnt, int nb,
+                                                         int E, const int32_t* __restrict__ blk_flag,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ status) {
+  __shared__ int sc[1024];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) {
+      const int c = blk_cnt[(size_t)b * E + e];
+      blk_cnt[(size_t)b * E + e] = total;
+      total += c;
+    }
+    counts[e] = total;
+  }
+  sc[e] = total;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = e >= off ? sc[e - off] : 0;
+    __syncthreads();
+    sc[e] += v;
+    __syncthreads();
+  }
+  const int excl = sc[e] - total;
+  if (e < E) {
+    offsets[e] = excl;
+    for (int b = 0; b < nb; ++b) blk_cnt[(size_t)b * E + e] += excl;
+  }
+  if (e == 1023) offsets[E] = sc[1023];
+  if (e == 0) {
+    int f = 0;
+    for (int b = 0; b < nb; ++b) f |= blk_flag[b];
+    status[0] = f ? 1 : 0;
+  }
+}
+
+// Places rows [r0, r0 + rpb) and copies their tokens: Xp[pos] = x[r / k].
+__global__ void __launch_bounds__(256) perm_place_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ rank,
+    const int32_t* __restrict__ blk_base, int Tk, int E, int k, int32_t* __restrict__ row_src,
+    int32_t* __restrict__ tk_row, const uint16_t* __restrict__ x, uint16_t* __restrict__ xp,
+    int d, int rpb) {
+  __shared__ int sh_pos[256];
+  const int tid = threadIdx.x;
+  const int r0 = blockIdx.x * rpb;
+  if (tid < rpb) {
+    const int r = r0 + tid;
+    int pos = -1;
+    if (r < Tk) {
+      const int rk = rank[r];
+      if (rk >= 0) {
+        pos = blk_base[(size_t)(r / kPermRows) * E + idx[r]] + rk;
+        row_src[pos] = r;
+      }
+      tk_row[r] = pos;
+    }
+    sh_pos[tid] = pos;
+  }
+  __syncthreads();
+  const int vpr = d / 8;
+  for (int i = tid; i < rpb * vpr; i += 256) {
+    const int rr = i / vpr, v = i % vpr;
+    const int r = r0 + rr;
+    const int pos = sh_pos[rr];
+    if (r >= Tk || pos < 0) continue;
+    const uint4 val = *reinterpret_cast<const uint4*>(x + (size_t)(r / k) * d + v * 8);
+    *reinterpret_cast<uint4*>(xp + (size_t)pos * d + v * 8) = val;
+  }
+}
+
+hipError_t launch_perm_hist(const int32_t* idx, int Tk, int E, int32_t* blk_cnt, int32_t* rank,
+                            int32_t* blk_flag, hipStream_t s) {
+  const int nb = (Tk + kPermRows - 1) / kPermRows;
+  hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(kPermRows), 0, s, idx, Tk, E, blk_cnt, rank,
+                     blk_flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_perm_scan(int32_t* blk_cnt, int nb, int E, const int32_t* blk_flag,
+                            int32_t* counts, int32_t* offsets, int32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, blk_cnt, nb, E, blk_flag, counts,
+                     offsets, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_perm_place(const int32_t* idx, const int32_t* rank, const int32_t* blk_base,
+                             int Tk, int E, int k, int32_t* row_src, int32_t* tk_row,
+                             const uint16_t* x, uint16_t* xp, int d, hipStream_t s) {
+  const int vpr = d / 8;
+  int rpb = 2048 / vpr;
+  if (rpb < 1) rpb = 1;
+  if (rpb > 256) rpb = 256;
+  const int grid = (Tk + rpb - 1) / rpb;
+  hipLaunchKernelGGL(perm_place_kernel, dim3(grid), dim3(256), 0, s, idx, rank, blk_base, Tk, E, k,
+                     row_src, tk_row, x, xp, d, rpb);
+  return hipGetLastError();
+}
+
+}  // namespace moe

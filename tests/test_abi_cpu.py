@@ -1,0 +1,92 @@
+"""The C-ABI library loads without a GPU, exports every function include/moe.h declares, sizes
+buffers and rejects bad arguments on the host before touching the device."""
+import ctypes
+
+import pytest
+
+from tests._util import ensure_built
+
+m = ensure_built()
+
+
+def test_every_declared_function_is_exported():
+    names = m.header_functions()
+    assert set(names) >= {"moe_query", "moe_route", "moe_permute", "moe_forward",
+                          "moe_backward", "moe_status_string"}
+    L = m.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_query_sizes_follow_the_shapes():
+    T, d, E, k, I = 2048, 7168, 256, 8, 2048
+    s = m.moe_query(m.make_cfg(T, d, E, k, I))
+    Tk = T * k
+    assert s.ring_slot == Tk * d * 2
+    assert s.saved >= Tk * (2 * I + I) * 2
+    assert s.saved_A >= s.saved_H + Tk * 2 * I * 2
+    assert s.workspace >= s.ws_dXp + Tk * d * 2
+    for off in (s.saved_H, s.saved_A, s.ws_O, s.ws_dH, s.ws_dXp):
+        assert off % 256 == 0
+    # disjoint intermediates in the workspace
+    spans = sorted([(s.ws_O, Tk * d * 2), (s.ws_dH, Tk * 2 * I * 2), (s.ws_dXp, Tk * d * 2)])
+    for (a, n), (b, _) in zip(spans, spans[1:]):
+        assert a + n <= b
+
+
+@pytest.mark.parametrize("shape", [
+    (0, 256, 8, 2, 128),      # no tokens
+    (16, 200, 8, 2, 128),     # d not a multiple of 256
+    (16, 256, 8, 2, 100),     # I not a multiple of 128
+    (16, 256, 8, 9, 128),     # k > E
+    (16, 256, 2000, 2, 128),  # E > 1024
+    (16, 256, 128, 65, 128),  # k > 64
+])
+def test_query_rejects_bad_shapes(shape):
+    with pytest.raises(m.MoeError) as ei:
+        m.moe_query(m.make_cfg(*shape))
+    assert ei.value.status == -1
+
+
+def _fake(addr=1 << 20):
+    return ctypes.c_void_p(addr)
+
+
+def test_entry_points_reject_bad_arguments_before_launching():
+    L = m.lib()
+    cfg = m.make_cfg(64, 256, 8, 2, 128)
+    s = m.moe_query(cfg)
+    p = _fake()
+    null = None
+    # null pointer
+    assert L.moe_route(ctypes.byref(cfg), null, p, p, p, p, None) == -1
+    # misaligned bf16 matrix
+    assert L.moe_route(ctypes.byref(cfg), _fake((1 << 20) + 2), p, p, p, p, None) == -1
+    # ring too small for the slot, and negative slot
+    assert L.moe_permute(ctypes.byref(cfg), p, p, p, s.ring_slot - 1, 0, p, p, p, p, p,
+                         s.workspace, None) == -2
+    assert L.moe_permute(ctypes.byref(cfg), p, p, p, 2 * s.ring_slot, 2, p, p, p, p, p,
+                         s.workspace, None) == -2
+    assert L.moe_permute(ctypes.byref(cfg), p, p, p, 2 * s.ring_slot, -1, p, p, p, p, p,
+                         s.workspace, None) == -2
+    # workspace too small
+    assert L.moe_permute(ctypes.byref(cfg), p, p, p, s.ring_slot, 0, p, p, p, p, p,
+                         s.workspace - 1, None) == -5
+    assert L.moe_forward(ctypes.byref(cfg), p, s.ring_slot, 0, p, p, p, p, p, None, p, p,
+                         s.saved - 1, p, s.workspace, None) == -5
+    # MXFP8 is not provided by this build
+    cfg8 = m.make_cfg(64, 256, 8, 2, 128, m.MOE_PREC_MXFP8)
+    assert L.moe_forward(ctypes.byref(cfg8), p, s.ring_slot, 0, p, p, p, p, p, None, p, p,
+                         s.saved, p, s.workspace, None) == -3
+    # unknown flag bits
+    cfgf = m.make_cfg(64, 256, 8, 2, 128, 0, 8)
+    assert L.moe_route(ctypes.byref(cfgf), p, p, p, p, p, None) == -1
+    # backward: bad dwr when the router weight is given
+    assert L.moe_backward(ctypes.byref(cfg), p, s.ring_slot, 0, p, p, p, p, p, p, p, p, None,
+                          p, s.saved, p, p, p, p, null, p, 0, p, s.workspace, None) == -1
+
+
+def test_status_strings():
+    assert m.status_string(0) == "ok"
+    assert "ring" in m.status_string(-2)
+    assert m.status_string(-99) == "unknown status"

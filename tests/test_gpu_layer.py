@@ -1,0 +1,252 @@
+"""GPU parity of the whole layer against the CPU oracle, through the C ABI.
+
+Integer outputs are compared bit for bit: router logits (fp32 in a stated order), top-k
+indices, counts, offsets and both permutation maps, plus the permuted tokens, which are a pure
+copy. Floating outputs use the layer's tolerances. The bf16 output Y and the input gradient dX
+must be within 1e-2 relative error, both max-abs and RMS. The weight, router and routing-weight
+gradients must be within 2e-2 relative Frobenius error. The oracle is the float64 CPU
+implementation with bf16 rounding at the same storage points.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+from tests._util import assert_act, assert_grad, ensure_built, rel_rms
+
+pytestmark = pytest.mark.gpu
+
+m = ensure_built()
+from mixture_experts_layer_deterministic_amd.layer import MoeLayer  # noqa: E402
+
+DEV = "cuda"
+
+
+def _np(t):
+    return workload.to_numpy(t)
+
+
+def _announce(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(inp, persistent=False, slot=0, ring_slots=1):
+    cfg = inp["cfg"]
+    T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
+    L = MoeLayer(T, d, E, k, I, device=DEV, ring_slots=ring_slots, persistent=persistent)
+    wr = inp.get("Wr")
+    if wr is None:
+        L.set_routing(inp["topk_idx"], inp["topk_w"])
+    L.step(inp["X"], wr, inp["W1"], inp["W2"], inp["dY"], slot=slot)
+    torch.cuda.synchronize()
+    return L
+
+
+def run_oracle(inp):
+    X, W1, W2, dY = (_np(inp[n]) for n in ("X", "W1", "W2", "dY"))
+    if "Wr" in inp:
+        Wr = _np(inp["Wr"])
+        f = oracle.forward(X, W1, W2, Wr=Wr, k=inp["cfg"]["k"])
+        b = oracle.backward(f, X, W1, W2, dY, Wr=Wr)
+    else:
+        f = oracle.forward(X, W1, W2, topk_idx=_np(inp["topk_idx"]), topk_w=_np(inp["topk_w"]))
+        b = oracle.backward(f, X, W1, W2, dY)
+    return f, b
+
+
+def check_parity(L, inp, f, b, slot=0):
+    routed = "Wr" in inp
+    k = inp["cfg"]["k"]
+    if routed:
+        np.testing.assert_array_equal(_np(L.logits), f["logits"])
+        np.testing.assert_array_equal(_np(L.topk_idx), f["idx"])
+        np.testing.assert_allclose(_np(L.topk_w), f["w"], rtol=0, atol=1e-6)
+    np.testing.assert_array_equal(_np(L.counts), f["counts"])
+    np.testing.assert_array_equal(_np(L.offsets), f["offsets"])
+    np.testing.assert_array_equal(_np(L.row_src), f["row_src"])
+    np.testing.assert_array_equal(_np(L.tk_row), f["tk_row"])
+    xp = _np(L.xp(slot))
+    np.testing.assert_array_equal(xp, _np(inp["X"])[f["row_src"] // k])
+    assert_act("H", _np(L.H()), f["H"])
+    assert_act("A", _np(L.A()), f["A"])
+    assert_act("O", _np(L.O()), f["O"])
+    assert_act("Y", _np(L.y), f["Y"])
+    assert_act("dH", _np(L.dH()), b["dH"])
+    assert_act("dXp", _np(L.dXp()), b["dXp"])
+    assert_act("dX", _np(L.dx), b["dX"])
+    assert_grad("dW1", _np(L.dw1), b["dW1"])
+    assert_grad("dW2", _np(L.dw2), b["dW2"])
+    assert_grad("d_topk_w", _np(L.d_topk_w), b["dw"])
+    if routed:
+        assert_grad("dWr", _np(L.dwr), b["dWr"])
+
+
+def outputs(L, routed):
+    outs = [L.logits, L.topk_idx, L.topk_w] if routed else []
+    outs += [L.counts, L.offsets, L.row_src, L.tk_row, L.y, L.H(), L.A(), L.dx, L.dw1, L.dw2,
+             L.d_topk_w]
+    if routed:
+        outs.append(L.dwr)
+    return [o.clone() for o in outs]
+
+
+def assert_bitwise_equal(a, b):
+    assert len(a) == len(b)
+    for i, (x, y) in enumerate(zip(a, b)):
+        assert x.dtype == y.dtype and x.shape == y.shape, i
+        assert torch.equal(x.view(torch.uint8) if x.dtype != torch.bool else x,
+                           y.view(torch.uint8) if y.dtype != torch.bool else y), i
+
+
+# ---------------------------------------------------------------------------------------------
+
+SMALL = {
+    "tiny": dict(name="tiny"),
+    "ragged": dict(name="tiny", T=300, E=16, k=3, d=512, I=256),
+    "multi_mtile": dict(name="tiny", T=1024, E=4, k=2, d=512, I=256),
+    "single_token": dict(name="tiny", T=1, E=4, k=2, d=256, I=128),
+    "k_equals_E": dict(name="tiny", T=64, E=4, k=4, d=256, I=128),
+    "zipf_local": dict(name="local_zipf", T=2048, d=256, I=256),
+}
+
+
+@pytest.mark.parametrize("case", list(SMALL))
+def test_layer_parity(case):
+    spec = dict(SMALL[case])
+    name = spec.pop("name")
+    _announce(f"[parity] case={case} shape={spec} seed=0")
+    inp = workload.make_inputs(name, seed=0, device=DEV, **spec)
+    L = run_gpu(inp)
+    f, b = run_oracle(inp)
+    check_parity(L, inp, f, b)
+
+
+def test_persistent_grid_is_bitwise_identical_to_one_shot():
+    _announce("[persistent] tiny and zipf_local")
+    for name, spec in (("tiny", {}), ("local_zipf", dict(T=2048, d=256, I=256))):
+        inp = workload.make_inputs(name, seed=1, device=DEV, **spec)
+        a = outputs(run_gpu(inp, persistent=False), "Wr" in inp)
+        b = outputs(run_gpu(inp, persistent=True), "Wr" in inp)
+        assert_bitwise_equal(a, b)
+
+
+def test_two_runs_are_bitwise_identical():
+    _announce("[determinism] multi_mtile twice")
+    inp = workload.make_inputs("tiny", seed=2, device=DEV, T=1024, E=8, k=2, d=512, I=256)
+    a = outputs(run_gpu(inp), True)
+    # a concurrent kernel on another stream perturbs timing between the runs
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        junk = torch.randn(4096, 4096, device=DEV)
+        for _ in range(4):
+            junk = junk @ junk.T
+            junk = junk / junk.norm()
+    b = outputs(run_gpu(inp), True)
+    torch.cuda.synchronize()
+    assert_bitwise_equal(a, b)
+
+
+def test_ring_slot_one_matches_slot_zero():
+    _announce("[ring] slot 1 of 2")
+    inp = workload.make_inputs("tiny", seed=3, device=DEV)
+    a = outputs(run_gpu(inp, slot=0, ring_slots=1), True)
+    b = outputs(run_gpu(inp, slot=1, ring_slots=2), True)
+    assert_bitwise_equal(a, b)
+
+
+def test_all_rows_to_one_expert_and_empty_experts():
+    _announce("[imbalance] every row to expert 2")
+    T, d, E, I = 512, 256, 4, 128
+    inp = workload.make_inputs("local_zipf", seed=4, device=DEV, T=T, d=d, E=E, I=I)
+    inp["topk_idx"] = torch.full((T, 1), 2, dtype=torch.int32, device=DEV)
+    L = run_gpu(inp)
+    f, b = run_oracle(inp)
+    check_parity(L, inp, f, b)
+    for e in (0, 1, 3):
+        assert torch.count_nonzero(L.dw1[e]) == 0 and torch.count_nonzero(L.dw2[e]) == 0
+
+
+def test_zero_router_and_duplicate_router_rows():
+    _announce("[ties] zero router, duplicate rows")
+    inp = workload.make_inputs("tiny", seed=5, device=DEV)
+    inp["Wr"] = torch.zeros_like(inp["Wr"])
+    L = run_gpu(inp)
+    k = inp["cfg"]["k"]
+    want = torch.arange(k, dtype=torch.int32, device=DEV).expand(inp["cfg"]["T"], k)
+    assert torch.equal(L.topk_idx, want)
+    assert torch.all(L.topk_w == 1.0 / k)
+    inp = workload.make_inputs("tiny", seed=6, device=DEV)
+    inp["Wr"][5] = inp["Wr"][1]
+    inp["Wr"][6] = inp["Wr"][1]
+    L = run_gpu(inp)
+    f, b = run_oracle(inp)
+    check_parity(L, inp, f, b)
+
+
+def test_bad_expert_index_sets_the_device_status():
+    _announce("[status] out-of-range expert index")
+    T, d, E, I = 64, 256, 4, 128
+    inp = workload.make_inputs("local_zipf", seed=7, device=DEV, T=T, d=d, E=E, I=I)
+    inp["topk_idx"] = inp["topk_idx"] % E
+    inp["topk_idx"][10, 0] = E + 3
+    L = run_gpu(inp)
+    assert L.device_status() == m.MOE_DEVICE_BAD_EXPERT_INDEX
+    assert int(L.tk_row[10].item()) == -1
+    assert int(L.offsets[E].item()) == T - 1
+    assert torch.all(L.dx[10] == 0)
+    good = workload.make_inputs("local_zipf", seed=7, device=DEV, T=T, d=d, E=E, I=I)
+    good["topk_idx"] = good["topk_idx"] % E
+    assert run_gpu(good).device_status() == 0
+
+
+def test_streaming_microbatches_with_ring_replay():
+    """Microbatches 0..n-1 go forward through a 2-slot ring, and backward walks n-1..0. Slots
+    overwritten by later microbatches are re-permuted (replayed) before their backward. The
+    weight gradients accumulate across microbatches."""
+    _announce("[stream] 4 microbatches, 2 slots, reverse walk with replay")
+    nmb, S = 4, 2
+    inp = workload.make_inputs("stream", seed=8, device=DEV, T=64, d=256, E=16, k=4, I=128,
+                               microbatches=nmb)
+    cfg = inp["cfg"]
+    T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
+    L = MoeLayer(T, d, E, k, I, device=DEV, ring_slots=S)
+    saved = [torch.empty_like(L.saved) for _ in range(nmb)]
+    routing = []
+    ys = []
+    for i in range(nmb):
+        L.route(inp["X"][i], inp["Wr"])
+        L.permute(inp["X"][i], slot=i % S)
+        L.forward(inp["W1"], inp["W2"], slot=i % S, saved=saved[i])
+        ys.append(L.y.clone())
+        routing.append((L.topk_idx.clone(), L.topk_w.clone(), L.counts.clone(),
+                        L.offsets.clone(), L.row_src.clone(), L.tk_row.clone()))
+    dxs = [None] * nmb
+    for i in reversed(range(nmb)):
+        for dst, src in zip((L.topk_idx, L.topk_w, L.counts, L.offsets, L.row_src, L.tk_row),
+                            routing[i]):
+            dst.copy_(src)
+        if i < nmb - S:
+            L.permute(inp["X"][i], slot=i % S)   # replay: the slot was overwritten
+        L.backward(inp["Wr"], inp["W1"], inp["W2"], inp["dY"][i], slot=i % S,
+                   accumulate=(i != nmb - 1), saved=saved[i])
+        dxs[i] = L.dx.clone()
+    torch.cuda.synchronize()
+    X, W1, W2, dY, Wr = (_np(inp[n]) for n in ("X", "W1", "W2", "dY", "Wr"))
+    dW1 = np.zeros_like(W1, dtype=np.float64)
+    dW2 = np.zeros_like(W2, dtype=np.float64)
+    dWr = np.zeros_like(Wr, dtype=np.float64)
+    for i in range(nmb):
+        f = oracle.forward(X[i], W1, W2, Wr=Wr, k=k)
+        b = oracle.backward(f, X[i], W1, W2, dY[i], Wr=Wr)
+        assert_act(f"Y[{i}]", _np(ys[i]), f["Y"])
+        assert_act(f"dX[{i}]", _np(dxs[i]), b["dX"])
+        dW1 += b["dW1"]
+        dW2 += b["dW2"]
+        dWr += b["dWr"]
+    assert_grad("dW1 (sum)", _np(L.dw1), dW1)
+    assert_grad("dW2 (sum)", _np(L.dw2), dW2)
+    assert_grad("dWr (sum)", _np(L.dwr), dWr)
