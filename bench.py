@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""MoE layer fwd+bwd throughput on one MI355X, with per-kernel roofline and the CPU oracle.
+
+A step is one pass of the whole layer over one synthetic batch: route, permute into the ring,
+the forward grouped GEMMs and combine, and the full backward. Inputs are resident in HBM
+before timing starts. The default workload is the DeepSeek-V3-shaped routed layer: T=2048
+tokens, d=7168, 256 experts, top-8, SwiGLU intermediate 2048, BF16.
+
+Prints one JSON line. `value` is tokens/s over the timed steps (hipEvents on the layer's
+stream). `roofline` is the dominant kernel's algorithmic bytes (or flops) per launch divided
+by its average launch time. Those times come from events the library records around each of
+its launches on that same stream, during the timed steps. `cpu_baseline` times the float64
+CPU oracle on a bounded sample of the same workload, extrapolated to the whole layer.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_GBPS = 8000.0         # MI355X HBM3E, GB/s
+MFMA_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, TFLOP/s
+VALU_FP32_TFLOPS = 157.3   # fp32 vector
+RIDGE_BF16 = MFMA_BF16_TFLOPS * 1e12 / (HBM_GBPS * 1e9)
+
+
+def algorithmic(cfg, routed=True, accumulate=False):
+    """Algorithmic bytes and flops per launch of each kernel: what the method must move and
+    compute (each tensor read or written once, no padding, no re-reads). M = T*k rows."""
+    T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
+    M = T * k
+    nb = (M + 255) // 256
+    acc = 2 if accumulate else 1
+    b = {}
+    if routed:
+        b["router_logits"] = (T * d * 2 + E * d * 2 + T * E * 4, 2 * T * d * E)
+        b["router_topk"] = (T * E * 4 + T * k * 8, 0)
+    b["perm_hist"] = (M * 8 + nb * E * 4, 0)
+    b["perm_scan"] = (2 * nb * E * 4 + E * 8, 0)
+    b["perm_place"] = (T * d * 2 + M * d * 2 + M * 16, 0)
+    b["sched_build"] = (E * 4, 0)
+    b["fwd_gateup"] = (E * 2 * I * d * 2 + M * d * 2 + M * 2 * I * 2 + M * I * 2, 2 * M * d * 2 * I)
+    b["fwd_down"] = (E * d * I * 2 + M * I * 2 + M * d * 2, 2 * M * I * d)
+    b["combine"] = (M * d * 2 + T * d * 2 + M * 8, 2 * M * d)
+    b["bwd_down_dgrad"] = (E * d * I * 2 + T * d * 2 + M * 2 * I * 2 * 2 + M * I * 2
+                           + M * (I // 128) * 4, 2 * M * d * I)
+    b["dw_router"] = (M * (I // 128) * 4 + M * 12, 0)
+    b["bwd_down_wgrad"] = (acc * E * d * I * 4 + T * d * 2 + M * I * 2, 2 * M * d * I)
+    b["bwd_gate_dgrad"] = (E * 2 * I * d * 2 + M * 2 * I * 2 + M * d * 2, 2 * M * 2 * I * d)
+    b["bwd_gate_wgrad"] = (acc * E * 2 * I * d * 4 + M * 2 * I * 2 + M * d * 2, 2 * M * 2 * I * d)
+    b["uncombine"] = (M * d * 2 + T * d * 2 + (E * d * 2 if routed else 0) + M * 8, M * d)
+    if routed:
+        b["dwr"] = (M * d * 2 + acc * E * d * 4 + M * 4, 2 * M * d)
+    return b
+
+
+GEMMS = ("fwd_gateup", "fwd_down", "bwd_down_dgrad", "bwd_down_wgrad", "bwd_gate_dgrad",
+         "bwd_gate_wgrad")
+
+
+def kernel_roofline(name, nbytes, flops, us):
+    """Achieved rate against the roofline that bounds the kernel."""
+    s = us * 1e-6
+    if name == "router_logits":
+        ach = flops / s / 1e12
+        return {"bound": "alu", "achieved": ach, "peak": VALU_FP32_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / VALU_FP32_TFLOPS}
+    if flops and flops / nbytes > RIDGE_BF16 and name in GEMMS:
+        ach = flops / s / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / MFMA_BF16_TFLOPS}
+    ach = nbytes / s / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": HBM_GBPS, "unit": "GB/s",
+            "frac": ach / HBM_GBPS}
+
+
+def cpu_baseline(inp, cfg, s_small=4, s_large=12):
+    """The CPU oracle on a bounded sample: the full router and bookkeeping plus the expert math
+    of the first `s` experts, for two values of s. Its time is linear in the expert count, so
+    the whole-layer time is extrapolated to all E experts."""
+    import numpy as np
+    import oracle
+    import workload
+    from threadpoolctl import threadpool_info
+
+    X = workload.to_numpy(inp["X"])
+    dY = workload.to_numpy(inp["dY"])
+    W1 = workload.HostExperts(inp["W1"])
+    W2 = workload.HostExperts(inp["W2"])
+    routed = "Wr" in inp
+    kw = dict(Wr=workload.to_numpy(inp["Wr"]), k=cfg["k"]) if routed else dict(
+        topk_idx=workload.to_numpy(inp["topk_idx"]), topk_w=workload.to_numpy(inp["topk_w"]))
+    E = cfg["E"]
+    times = {}
+    for s in (s_small, s_large):
+        ex = list(range(min(s, E)))
+        t0 = time.perf_counter()
+        f = oracle.forward(X, W1, W2, experts=ex, **kw)
+        oracle.backward(f, X, W1, W2, dY, Wr=kw.get("Wr"), experts=ex)
+        times[len(ex)] = time.perf_counter() - t0
+        del f
+    (sa, ta), (sb, tb) = sorted(times.items())
+    slope = (tb - ta) / max(sb - sa, 1)
+    full = ta + slope * (E - sa)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": cfg["T"] / full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{cfg['name']} seed 0, full router and bookkeeping, expert math of "
+                       f"experts 0..{sa - 1} ({ta:.2f} s) and 0..{sb - 1} ({tb:.2f} s) "
+                       f"fwd+bwd; whole-layer time extrapolated linearly to {E} experts "
+                       f"= {full:.1f} s"),
+            "layer_seconds": full}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--persistent", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true", help="skip per-kernel events")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path "
+              "(no collectives, no sharding); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_layer_deterministic_amd as m
+    import workload
+    from mixture_experts_layer_deterministic_amd.layer import MoeLayer
+
+    if not os.path.exists(m.LIB_PATH):
+        from mixture_experts_layer_deterministic_amd import build
+        build.build(verbose=False)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = workload.config(args.workload)
+    if cfg.get("microbatches"):
+        print("the streaming workload is a parity case, not a bench line", file=sys.stderr)
+        sys.exit(2)
+    print(f"[bench] generating {args.workload} inputs (seed {args.seed})", file=sys.stderr,
+          flush=True)
+    inp = workload.make_inputs(args.workload, seed=args.seed, device=dev)
+    T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
+    routed = "Wr" in inp
+    L = MoeLayer(T, d, E, k, I, device=dev, persistent=args.persistent)
+    wr = inp.get("Wr")
+    if not routed:
+        L.set_routing(inp["topk_idx"], inp["topk_w"])
+    X, W1, W2, dY = inp["X"], inp["W1"], inp["W2"], inp["dY"]
+    stream = torch.cuda.current_stream()
+
+    def step():
+        L.step(X, wr, W1, W2, dY, stream=stream)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # launches per step (traced once, untimed)
+    probe = [torch.cuda.Event(enable_timing=True) for _ in range(128)]
+    for e in probe:
+        e.record(stream)
+    torch.cuda.synchronize()
+    keep = m.moe_trace_begin([e.cuda_event for e in probe])
+    step()
+    per_step = m.moe_trace_end()
+    torch.cuda.synchronize()
+    del keep
+
+    ev = []
+    names = None
+    keep = None
+    if not args.no_trace:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * per_step * args.steps)]
+        for e in ev:
+            e.record(stream)
+        torch.cuda.synchronize()
+        names = (ctypes.c_char_p * (per_step * args.steps))()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps ({per_step} launches each)", file=sys.stderr,
+          flush=True)
+    if ev:
+        keep = m.moe_trace_begin([e.cuda_event for e in ev], names)
+    t_host = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
+    if ev:
+        m.moe_trace_end()
+    ms = start.elapsed_time(end) / args.steps
+    tokens_per_s = T / (ms * 1e-3)
+
+    alg = algorithmic(cfg, routed=routed)
+    kernels = {}
+    if ev:
+        tot = {}
+        cnt = {}
+        for i in range(per_step * args.steps):
+            n = names[i].decode()
+            tot[n] = tot.get(n, 0.0) + ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3
+            cnt[n] = cnt.get(n, 0) + 1
+        for n in tot:
+            us = tot[n] / cnt[n]
+            nbytes, flops = alg.get(n, (0, 0))
+            r = kernel_roofline(n, nbytes, flops, us) if nbytes else {}
+            kernels[n] = {"us": round(us, 2), "launches_per_step": cnt[n] // args.steps,
+                          "alg_bytes": nbytes, "alg_flops": flops,
+                          **{kk: (round(v, 4) if isinstance(v, float) else v)
+                             for kk, v in r.items()}}
+    dominant = max(kernels, key=lambda n: kernels[n]["us"] * kernels[n]["launches_per_step"]) \
+        if kernels else None
+    roof = None
+    if dominant:
+        kd = kernels[dominant]
+        roof = {"kernel": dominant, "bound": kd["bound"], "achieved": kd["achieved"],
+                "peak": kd["peak"], "unit": kd["unit"], "frac": kd["frac"], "traffic": None,
+                "us_per_launch": kd["us"]}
+    gemm_us = sum(kernels[g]["us"] for g in GEMMS if g in kernels)
+    gemm_flops = sum(alg[g][1] for g in GEMMS)
+    gemm_bytes = sum(alg[g][0] for g in GEMMS)
+    gemm = None
+    if gemm_us:
+        tf = gemm_flops / (gemm_us * 1e-6) / 1e12
+        attainable = min(MFMA_BF16_TFLOPS, HBM_GBPS * 1e9 * gemm_flops / gemm_bytes / 1e12)
+        gemm = {"tflops": round(tf, 2), "frac_mfma_peak": round(tf / MFMA_BF16_TFLOPS, 4),
+                "attainable_tflops": round(attainable, 2),
+                "frac_attainable": round(tf / attainable, 4),
+                "share_of_step": round(gemm_us / 1e3 / ms, 4)}
+    pc = {}
+    for n in ("perm_place", "combine"):
+        if n in kernels:
+            pc[n] = {"GB/s": kernels[n].get("achieved"), "frac_hbm": kernels[n].get("frac")}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp, cfg)
+
+    line = {
+        "metric": "MoE layer fwd+bwd tokens/s",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "d": d, "E": E, "k": k, "I": I,
+                   "weight_grad_dtype": "fp32", "persistent": bool(args.persistent),
+                   "seed": args.seed},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "grouped_gemm": gemm,
+        "permute_combine": pc,
+        "kernels": kernels,
+        "host_seconds_timed": round(t_host, 4),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

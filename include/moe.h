@@ -205,6 +205,21 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
                  float* dwr, float* d_topk_w, int32_t accumulate, void* workspace,
                  size_t ws_bytes, moe_stream_t stream);
 
+/*
+ * Launch tracing, for benchmarks and profilers; the layer never needs it.
+ * moe_trace_begin: until moe_trace_end, every kernel the library enqueues is bracketed by two
+ * hipEventRecord calls on the kernel's own stream: events[2i] before and events[2i+1] after the
+ * i-th launch, for 2i+1 < capacity. names[i] receives the kernel's static name when names is
+ * non-NULL. The caller creates the hipEvent_t handles (with timing enabled) and keeps them
+ * alive. Not meant for concurrent use from several threads.
+ *   events   hipEvent_t [capacity]   host array of caller-created events
+ *   names    const char* [capacity/2] host array, or NULL
+ * moe_trace_end stops tracing and returns the number of launches seen since moe_trace_begin
+ * (launches beyond capacity/2 were counted but not timed).
+ */
+int moe_trace_begin(void* const* events, int capacity, const char** names);
+int moe_trace_end(void);
+
 /* A static string for a moe_status value. */
 const char* moe_status_string(int status);
 

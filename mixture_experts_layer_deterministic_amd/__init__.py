@@ -74,10 +74,26 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        L.moe_trace_begin.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                      ctypes.POINTER(ctypes.c_char_p)]
+        L.moe_trace_begin.restype = ctypes.c_int
+        L.moe_trace_end.argtypes = []
+        L.moe_trace_end.restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         _lib = L
     return _lib
+
+
+def moe_trace_begin(event_handles, names_buf=None):
+    """Starts launch tracing into caller-created events (raw hipEvent_t handles)."""
+    arr = (ctypes.c_void_p * len(event_handles))(*event_handles)
+    _check(lib().moe_trace_begin(arr, len(event_handles), names_buf), "moe_trace_begin")
+    return arr
+
+
+def moe_trace_end() -> int:
+    return lib().moe_trace_end()
 
 
 def header_functions() -> list[str]:

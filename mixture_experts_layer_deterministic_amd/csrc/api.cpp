@@ -3,6 +3,9 @@
 // stream. It never allocates, synchronises or prints.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "kernels.h"
 
@@ -96,9 +99,56 @@ int check_ring(const Layout& L, const void* ring, size_t ring_bytes, int32_t slo
   return MOE_OK;
 }
 
+// Launch tracing (moe_trace_begin / moe_trace_end).
+std::atomic<void* const*> g_trace_events{nullptr};
+std::mutex g_trace_mu;
+const char** g_trace_names = nullptr;
+int g_trace_cap = 0;
+int g_trace_count = 0;
+
 }  // namespace
 
+namespace moe {
+void trace_pre(const char* name, hipStream_t s) {
+  if (!g_trace_events.load(std::memory_order_acquire)) return;
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  void* const* ev = g_trace_events.load(std::memory_order_relaxed);
+  const int i = g_trace_count;
+  if (ev && 2 * i + 1 < g_trace_cap) {
+    (void)hipEventRecord(static_cast<hipEvent_t>(ev[2 * i]), s);
+    if (g_trace_names) g_trace_names[i] = name;
+  }
+}
+void trace_post(hipStream_t s) {
+  if (!g_trace_events.load(std::memory_order_acquire)) return;
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  void* const* ev = g_trace_events.load(std::memory_order_relaxed);
+  const int i = g_trace_count++;
+  if (ev && 2 * i + 1 < g_trace_cap) (void)hipEventRecord(static_cast<hipEvent_t>(ev[2 * i + 1]), s);
+}
+}  // namespace moe
+
 extern "C" {
+
+int moe_trace_begin(void* const* events, int capacity, const char** names) {
+  if (!events || capacity < 2) return MOE_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  g_trace_names = names;
+  g_trace_cap = capacity;
+  g_trace_count = 0;
+  g_trace_events.store(events, std::memory_order_release);
+  return MOE_OK;
+}
+
+int moe_trace_end(void) {
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  g_trace_events.store(nullptr, std::memory_order_release);
+  const int n = g_trace_count;
+  g_trace_count = 0;
+  g_trace_cap = 0;
+  g_trace_names = nullptr;
+  return n;
+}
 
 int moe_query(const moe_cfg* cfg, moe_sizes* out) {
   if (!out || !cfg_ok(cfg)) return MOE_ERR_INVALID_ARG;

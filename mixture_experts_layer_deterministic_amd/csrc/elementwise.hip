@@ -160,16 +160,22 @@ __global__ void __launch_bounds__(64) dwr_kernel(const float* __restrict__ dl_po
 hipError_t launch_combine(const uint16_t* O, const int32_t* tk_row, const float* topk_w, int T,
                           int k, int d, uint16_t* y, hipStream_t s) {
   const int tpb = rows_per_block(d);
-  hipLaunchKernelGGL(combine_kernel, dim3((T + tpb - 1) / tpb), dim3(256), 0, s, O, tk_row, topk_w,
-                     T, k, d, y, tpb);
+  {
+    TraceScope trace("combine", s);
+    hipLaunchKernelGGL(combine_kernel, dim3((T + tpb - 1) / tpb), dim3(256), 0, s, O, tk_row, topk_w,
+                       T, k, d, y, tpb);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_dw_router(const float* dwpart, int nIt, const int32_t* tk_row,
                             const float* topk_w, int T, int k, float* d_topk_w, float* dl_pos,
                             int routed, hipStream_t s) {
-  hipLaunchKernelGGL(dw_router_kernel, dim3((T + 255) / 256), dim3(256), 0, s, dwpart, nIt, tk_row,
-                     topk_w, T, k, d_topk_w, dl_pos, routed);
+  {
+    TraceScope trace("dw_router", s);
+    hipLaunchKernelGGL(dw_router_kernel, dim3((T + 255) / 256), dim3(256), 0, s, dwpart, nIt, tk_row,
+                       topk_w, T, k, d_topk_w, dl_pos, routed);
+  }
   return hipGetLastError();
 }
 
@@ -177,15 +183,21 @@ hipError_t launch_uncombine(const uint16_t* dXp, const int32_t* tk_row, const in
                             const float* dl_pos, const uint16_t* wr, int T, int k, int d,
                             uint16_t* dx, hipStream_t s) {
   const int tpb = rows_per_block(d);
-  hipLaunchKernelGGL(uncombine_kernel, dim3((T + tpb - 1) / tpb), dim3(256), 0, s, dXp, tk_row,
-                     topk_idx, dl_pos, wr, T, k, d, dx, tpb);
+  {
+    TraceScope trace("uncombine", s);
+    hipLaunchKernelGGL(uncombine_kernel, dim3((T + tpb - 1) / tpb), dim3(256), 0, s, dXp, tk_row,
+                       topk_idx, dl_pos, wr, T, k, d, dx, tpb);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_dwr(const float* dl_pos, const uint16_t* xp, const int32_t* offsets, int E,
                       int d, float* dwr, int accumulate, hipStream_t s) {
-  hipLaunchKernelGGL(dwr_kernel, dim3((d + 511) / 512, E), dim3(64), 0, s, dl_pos, xp, offsets, d,
-                     dwr, accumulate);
+  {
+    TraceScope trace("dwr", s);
+    hipLaunchKernelGGL(dwr_kernel, dim3((d + 511) / 512, E), dim3(64), 0, s, dl_pos, xp, offsets, d,
+                       dwr, accumulate);
+  }
   return hipGetLastError();
 }
 

@@ -149,6 +149,7 @@ MOE_DEV MTile decode_mtile(const int2* sched, const int32_t* offsets, int mt, in
 // rows I+n0..; wave w owns gate columns [w*WN/2, (w+1)*WN/2) and the same up columns, so each
 // lane holds g and u for the same (row, column) and can finish SwiGLU in registers.
 struct FwdGateUp {
+  static constexpr const char* kName = "fwd_gateup";
   using G = Geo<128, 128, 64, 1, 4>;
   struct Args {
     const uint16_t* xp;    // [T*k, d]
@@ -231,6 +232,7 @@ struct FwdGateUp {
 // ------------------------------------------------------------------------------------------
 // Problem 2: forward down GEMM. O[pos] = A[pos] . W2[e]^T, stored bf16.
 struct FwdDown {
+  static constexpr const char* kName = "fwd_down";
   using G = Geo<128, 128, 64, 1, 4>;
   struct Args {
     const uint16_t* A;   // [T*k, I]
@@ -300,6 +302,7 @@ struct FwdDown {
 // Epilogue per (pos, i): partial dw += dA' * A (summed over the tile's columns in a fixed
 // order: register, then lane groups, then waves), dA = w dA', and the SwiGLU derivative.
 struct BwdDownDgrad {
+  static constexpr const char* kName = "bwd_down_dgrad";
   using G = Geo<128, 128, 64, 1, 4>;
   struct Args {
     const uint16_t* dy;      // [T, d]
@@ -413,6 +416,7 @@ struct BwdDownDgrad {
 // ------------------------------------------------------------------------------------------
 // Problem 4: backward gate/up dgrad. dXp[pos] = dH[pos] . W1[e], stored bf16.
 struct BwdGateDgrad {
+  static constexpr const char* kName = "bwd_gate_dgrad";
   using G = Geo<128, 128, 64, 1, 4>;
   struct Args {
     const uint16_t* dH;  // [T*k, 2I]
@@ -490,6 +494,7 @@ struct WgradTile {
 
 // Problem 5: dW2[e][n, i] = sum_pos bf16(w[pos] dY[t(pos), n]) * A[pos, i].
 struct BwdDownWgrad {
+  static constexpr const char* kName = "bwd_down_wgrad";
   using G = Geo<128, 128, 32, 2, 2>;
   struct Args {
     const uint16_t* dy;      // [T, d]
@@ -578,6 +583,7 @@ struct BwdDownWgrad {
 
 // Problem 6: dW1[e][n, c] = sum_pos dH[pos, n] * Xp[pos, c].
 struct BwdGateWgrad {
+  static constexpr const char* kName = "bwd_gate_wgrad";
   using G = Geo<128, 128, 32, 2, 2>;
   struct Args {
     const uint16_t* dH;  // [T*k, 2I]
@@ -757,7 +763,10 @@ static hipError_t launch(const typename P::Args& a, int max_tiles, bool persiste
     }
     if (resident > 0 && resident < grid) grid = resident;
   }
-  hipLaunchKernelGGL(gg_kernel<P>, dim3(grid), dim3(kThreads), sm, stream, a);
+  {
+    TraceScope trace(P::kName, stream);
+    hipLaunchKernelGGL(gg_kernel<P>, dim3(grid), dim3(kThreads), sm, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -788,7 +797,10 @@ __global__ void __launch_bounds__(1024) sched_build_kernel(const int32_t* offset
 int sched_max_mtiles(int Tk, int E) { return (Tk + E * (kSchedBM - 1)) / kSchedBM; }
 
 hipError_t launch_sched_build(const int32_t* offsets, int E, int2* sched, hipStream_t s) {
-  hipLaunchKernelGGL(sched_build_kernel, dim3(1), dim3(1024), 0, s, offsets, E, kSchedBM, sched);
+  {
+    TraceScope trace("sched_build", s);
+    hipLaunchKernelGGL(sched_build_kernel, dim3(1), dim3(1024), 0, s, offsets, E, kSchedBM, sched);
+  }
   return hipGetLastError();
 }
 

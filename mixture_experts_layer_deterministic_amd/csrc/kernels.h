@@ -7,6 +7,17 @@
 
 namespace moe {
 
+// Optional per-launch timing (moe_trace_begin / moe_trace_end): each launch site opens a
+// TraceScope, which records a caller-provided event before the launch and another after it,
+// both on the launching stream. With tracing off this costs one atomic load.
+void trace_pre(const char* name, hipStream_t s);
+void trace_post(hipStream_t s);
+struct TraceScope {
+  hipStream_t s;
+  TraceScope(const char* name, hipStream_t st) : s(st) { trace_pre(name, s); }
+  ~TraceScope() { trace_post(s); }
+};
+
 constexpr int kSchedBM = 128;   // rows per M-tile of the forward/dgrad grouped GEMMs
 constexpr int kDgradBN = 128;   // columns per N-tile of the down dgrad (dw partials per row)
 constexpr int kPermRows = 256;  // rows per histogram block of the permutation

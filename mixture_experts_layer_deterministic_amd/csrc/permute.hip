@@ -119,15 +119,21 @@ __global__ void __launch_bounds__(256) perm_place_kernel(
 hipError_t launch_perm_hist(const int32_t* idx, int Tk, int E, int32_t* blk_cnt, int32_t* rank,
                             int32_t* blk_flag, hipStream_t s) {
   const int nb = (Tk + kPermRows - 1) / kPermRows;
-  hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(kPermRows), 0, s, idx, Tk, E, blk_cnt, rank,
-                     blk_flag);
+  {
+    TraceScope trace("perm_hist", s);
+    hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(kPermRows), 0, s, idx, Tk, E, blk_cnt, rank,
+                       blk_flag);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_perm_scan(int32_t* blk_cnt, int nb, int E, const int32_t* blk_flag,
                             int32_t* counts, int32_t* offsets, int32_t* status, hipStream_t s) {
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, blk_cnt, nb, E, blk_flag, counts,
-                     offsets, status);
+  {
+    TraceScope trace("perm_scan", s);
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, blk_cnt, nb, E, blk_flag, counts,
+                       offsets, status);
+  }
   return hipGetLastError();
 }
 
@@ -139,8 +145,11 @@ hipError_t launch_perm_place(const int32_t* idx, const int32_t* rank, const int3
   if (rpb < 1) rpb = 1;
   if (rpb > 256) rpb = 256;
   const int grid = (Tk + rpb - 1) / rpb;
-  hipLaunchKernelGGL(perm_place_kernel, dim3(grid), dim3(256), 0, s, idx, rank, blk_base, Tk, E, k,
-                     row_src, tk_row, x, xp, d, rpb);
+  {
+    TraceScope trace("perm_place", s);
+    hipLaunchKernelGGL(perm_place_kernel, dim3(grid), dim3(256), 0, s, idx, rank, blk_base, Tk, E, k,
+                       row_src, tk_row, x, xp, d, rpb);
+  }
   return hipGetLastError();
 }
 

@@ -122,15 +122,21 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, float* lo
                                 int d, int E, hipStream_t s) {
   constexpr int TT = 8, CH = 64;
   dim3 grid((T + TT - 1) / TT, (E + 255) / 256);
-  hipLaunchKernelGGL((router_logits_kernel<TT, CH>), grid, dim3(256), 0, s, x, wr, logits, T, d,
-                     E);
+  {
+    TraceScope trace("router_logits", s);
+    hipLaunchKernelGGL((router_logits_kernel<TT, CH>), grid, dim3(256), 0, s, x, wr, logits, T, d,
+                       E);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                               hipStream_t s) {
-  hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx,
-                     w);
+  {
+    TraceScope trace("router_topk", s);
+    hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx,
+                       w);
+  }
   return hipGetLastError();
 }
 

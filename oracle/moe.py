@@ -209,6 +209,8 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None) -> dict:
     * dWr = dlogits^T X.
     With bf16 storage, dH, dXp and dX are rounded where the GPU stores them, and the stored H,
     A and dH feed the later steps. Empty experts get all-zero dW1_e and dW2_e blocks.
+    ``experts`` limits the expert math to a subset (rows of other experts stay NaN). dW1 and dW2
+    then hold one block per listed expert, in the order listed in out["experts"].
     """
     X = np.asarray(X, np.float64)
     dY = np.asarray(dY, np.float64)
@@ -224,10 +226,10 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None) -> dict:
     dw_pos = np.full(Tk, np.nan)
     dH = np.full((Tk, twoI), np.nan)
     dXp = np.full((Tk, d), np.nan)
-    dW1 = np.zeros((E, twoI, d))
-    dW2 = np.zeros((E, d, I))
-    ex = range(E) if experts is None else experts
-    for e in ex:
+    ex = list(range(E)) if experts is None else list(experts)
+    dW1 = np.zeros((len(ex), twoI, d))
+    dW2 = np.zeros((len(ex), d, I))
+    for slot, e in enumerate(ex):
         p0, p1 = int(offsets[e]), int(offsets[e + 1])
         if p1 == p0:
             continue
@@ -247,13 +249,13 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None) -> dict:
         dh = rnd(np.concatenate([dg, du], axis=1))
         dH[p0:p1] = dh
         dXp[p0:p1] = rnd(dh @ w1)
-        dW2[e] = (wv * dy).T @ fwd["A"][p0:p1]
-        dW1[e] = dh.T @ X[tok]
+        dW2[slot] = (wv * dy).T @ fwd["A"][p0:p1]
+        dW1[slot] = dh.T @ X[tok]
     dw = dw_pos[tk_row].reshape(T, k)
     dXsum = np.zeros((T, d))
     for j in range(k):
         dXsum += dXp[tk_row[np.arange(T) * k + j]]
-    out = dict(dw=dw, dH=dH, dXp=dXp, dW1=dW1, dW2=dW2)
+    out = dict(dw=dw, dH=dH, dXp=dXp, dW1=dW1, dW2=dW2, experts=ex)
     if fwd["routed"]:
         w = fwd["w"]
         idx = fwd["idx"]

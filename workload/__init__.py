@@ -128,3 +128,19 @@ def to_numpy(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         t = t.float()
     return t.detach().cpu().numpy()
+
+
+class HostExperts:
+    """Per-expert host view of a device weight tensor [E, ...]. Indexing copies one expert's
+    block to the host (float32), so a CPU consumer can walk the experts without holding the
+    whole tensor in host memory."""
+
+    def __init__(self, t: torch.Tensor):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, e):
+        return to_numpy(self.t[e])
+
+    def __len__(self):
+        return self.shape[0]
