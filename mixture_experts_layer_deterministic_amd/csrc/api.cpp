@@ -18,7 +18,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   // workspace
-  size_t status, sched, blk_cnt, blk_flag, rank, O, dH, dXp, dwpart, dl_pos, total;
+  size_t status, sched, blk_cnt, blk_flag, rank, O, dH, dXp, dyw, dwpart, dl_pos, wg_count,
+      wg_table1, wg_table2, total;
   // saved
   size_t H, A, saved_total;
   size_t slot;
@@ -54,6 +55,10 @@ Layout layout(const moe_cfg* c) {
   L.O = take(2 * Tk * d);
   L.dH = take(2 * Tk * 2 * I);
   L.dXp = take(2 * Tk * d);
+  L.dyw = take(2 * Tk * d);
+  L.wg_count = take(2 * sizeof(int32_t));
+  L.wg_table1 = take(16 * wgrad_table_entries((int)Tk, c->E, 2 * c->I, c->d));
+  L.wg_table2 = take(16 * wgrad_table_entries((int)Tk, c->E, c->d, c->I));
   L.dwpart = take(sizeof(float) * Tk * L.nIt);
   L.dl_pos = take(sizeof(float) * Tk);
   L.total = o;
@@ -280,18 +285,24 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
   const uint16_t* w1p = static_cast<const uint16_t*>(w1);
   const uint16_t* w2p = static_cast<const uint16_t*>(w2);
   Launches L;
+  uint16_t* dyw = at<uint16_t>(workspace, Y.dyw);
+  int32_t* wg_count = at<int32_t>(workspace, Y.wg_count);
   L(launch_sched_build(offsets, E, sched, s));
   if (!L.err)
-    L(launch_bwd_down_dgrad({dyp, row_src, topk_w, w2p, H, A, dH, dwpart, offsets, sched, d, I, k,
-                             Tk, E},
+    L(launch_bwd_down_dgrad({dyp, row_src, topk_w, w2p, H, A, dH, dwpart, dyw, offsets, sched, d,
+                             I, k, Tk, E},
                             pers, s));
   if (!L.err)
     L(launch_dw_router(dwpart, Y.nIt, tk_row, topk_w, cfg->T, k, d_topk_w, dl_pos, routed, s));
   if (!L.err)
-    L(launch_bwd_down_wgrad({dyp, row_src, topk_w, A, dw2, offsets, d, I, k, E, accumulate}, pers,
-                            s));
+    L(launch_wgrad({dyw, A, dw2, offsets, at<int4>(workspace, Y.wg_table2), wg_count + 1, E, d, I,
+                    accumulate, "bwd_down_wgrad", "wgrad_sched_down"},
+                   s));
   if (!L.err) L(launch_bwd_gate_dgrad({dH, w1p, dXp, offsets, sched, d, I, Tk, E}, pers, s));
-  if (!L.err) L(launch_bwd_gate_wgrad({dH, xp, dw1, offsets, d, I, E, accumulate}, pers, s));
+  if (!L.err)
+    L(launch_wgrad({dH, xp, dw1, offsets, at<int4>(workspace, Y.wg_table1), wg_count, E, 2 * I, d,
+                    accumulate, "bwd_gate_wgrad", "wgrad_sched_gate"},
+                   s));
   if (!L.err)
     L(launch_uncombine(dXp, tk_row, topk_idx, dl_pos,
                        routed ? static_cast<const uint16_t*>(w_router) : nullptr, cfg->T, k, d,

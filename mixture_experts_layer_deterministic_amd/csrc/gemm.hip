@@ -1,18 +1,17 @@
 // Expert-grouped GEMMs of the MoE layer on gfx950 MFMA (bf16 in, fp32 accumulate).
 //
 // The expert-grouped GEMMs are named in the MarkTechPost page on Mixture-of-Kittens (MoK),
-// section "Three design decisions that matter". There are six products:
+// section "Three design decisions that matter". This file holds the four whose rows are
+// token positions:
 //   fwd  gate/up : [g|u][pos]   = Xp[pos]  . W1[e]^T      SwiGLU in the epilogue
 //   fwd  down    : O[pos]       = A[pos]   . W2[e]^T
 //   bwd  down dg : dA'[pos]     = dY[t]    . W2[e]        SwiGLU backward + router-weight grad
 //   bwd  gate dg : dXp[pos]     = dH[pos]  . W1[e]
-//   bwd  down wg : dW2[e]       = sum_pos (w dY[t])^T A[pos]
-//   bwd  gate wg : dW1[e]       = sum_pos dH[pos]^T Xp[pos]
-// One kernel template runs them all. A workgroup (256 threads, 4 waves) owns a BM x BN output
-// tile. Tiles of BK stream through double-buffered LDS, stored K-contiguous with 8 elements of
-// padding per row, so every MFMA fragment is one 16-byte LDS read. Operands whose K axis is
-// not contiguous in memory (the weights in dgrad, both operands in wgrad) are loaded as 8x8
-// blocks and transposed in registers on their way into LDS.
+// The two weight gradients have their own kernel (wgrad.hip). One kernel template runs the
+// four. A workgroup (256 threads, 4 waves) owns a BM x BN output tile. Tiles of BK stream
+// through double-buffered LDS, stored K-contiguous with 8 elements of padding per row, so every
+// MFMA fragment is one 16-byte LDS read. The weights in dgrad, whose K axis is not contiguous
+// in memory, are loaded as 8x8 blocks and transposed in registers on their way into LDS.
 //
 // Determinism: every output element is produced by exactly one workgroup, which reduces K in a
 // fixed order. There are no atomics and no split-K.
@@ -313,6 +312,7 @@ struct BwdDownDgrad {
     const uint16_t* A;       // [T*k, I]
     uint16_t* dH;            // [T*k, 2I]
     float* dwpart;           // [T*k, I / BN]
+    uint16_t* dyw;           // [T*k, d]: bf16(w dY[t]) in position order
     const int32_t* offsets;
     const int2* sched;
     int d, I, k;
@@ -332,21 +332,52 @@ struct BwdDownDgrad {
   static MOE_DEV int num_k(const Args& a, const Tile&) { return a.d / G::BK; }
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
+  // Every workgroup of an M-tile reads the same gathered dY rows. The one with N-tile index
+  // kt % (I / BN) also writes K-chunk kt of those rows, scaled by the routing weight and
+  // rounded to bf16, to dyw in position order, so the down wgrad reads contiguous rows.
   struct Loader {
-    LoadK<G::BM, G::BK, G::LDK> la;
+    using LA = LoadK<G::BM, G::BK, G::LDK>;
+    LA la;
     LoadMN<G::BN, G::BK, G::LDK, false> lb;
     const uint16_t* wb;
     int ldw;
+    uint16_t* yw[LA::PT];  // dyw row pointer (+ column) per loaded vector, or null
+    float wv[LA::PT];
+    int ntc, nidx;
     MOE_DEV void init(const Args& a, const Tile& t) {
       const uint16_t* dy = a.dy;
       const int32_t* rs = a.row_src;
       const int d = a.d, k = a.k, mc = t.m.mcount, row0 = t.m.row0;
       la.init([&](int m) { return m < mc ? dy + (size_t)(rs[row0 + m] / k) * d : nullptr; });
+#pragma unroll
+      for (int j = 0; j < LA::PT; ++j) {
+        const int v = threadIdx.x + kThreads * j;
+        const int m = v / LA::VPR;
+        const bool live = v < LA::NV && m < mc;
+        yw[j] = live ? a.dyw + (size_t)(row0 + m) * d + (v % LA::VPR) * 8 : nullptr;
+        wv[j] = live ? a.topk_w[rs[row0 + m]] : 0.f;
+      }
+      ntc = a.I / G::BN;
+      nidx = t.n0 / G::BN;
       wb = a.w2 + (size_t)t.m.e * a.d * a.I + t.n0;
       ldw = a.I;
     }
     MOE_DEV void load(int kt) {
       la.load(kt * G::BK);
+      if (kt % ntc == nidx) {
+#pragma unroll
+        for (int j = 0; j < LA::PT; ++j) {
+          if (!yw[j]) continue;
+          const uint4 v = la.r[j];
+          const float s = wv[j];
+          uint4 o;
+          o.x = pack_bf2(bf2f_lo(v.x) * s, bf2f_hi(v.x) * s);
+          o.y = pack_bf2(bf2f_lo(v.y) * s, bf2f_hi(v.y) * s);
+          o.z = pack_bf2(bf2f_lo(v.z) * s, bf2f_hi(v.z) * s);
+          o.w = pack_bf2(bf2f_lo(v.w) * s, bf2f_hi(v.w) * s);
+          *reinterpret_cast<uint4*>(yw[j] + kt * G::BK) = o;
+        }
+      }
       const uint16_t* w = wb;
       const int ld = ldw;
       lb.load(kt * G::BK, [&](int k) { return w + (size_t)k * ld; }, [](int) { return 1.0f; });
@@ -479,184 +510,6 @@ struct BwdGateDgrad {
         o.x = pack_bf2(acc[mb][nb][0], acc[mb][nb][1]);
         o.y = pack_bf2(acc[mb][nb][2], acc[mb][nb][3]);
         *reinterpret_cast<uint2*>(a.dXp + pos * a.d + n) = o;
-      }
-    }
-  }
-};
-
-// ------------------------------------------------------------------------------------------
-// Weight gradients: K runs over the positions of one expert, in ascending order, in chunks of
-// BK; the ragged tail is zero-filled. Output rows are weight rows (no position mapping); empty
-// experts write zero blocks (or leave accumulated ones untouched).
-struct WgradTile {
-  int e, m0, n0, p0, p1;
-};
-
-// Problem 5: dW2[e][n, i] = sum_pos bf16(w[pos] dY[t(pos), n]) * A[pos, i].
-struct BwdDownWgrad {
-  static constexpr const char* kName = "bwd_down_wgrad";
-  using G = Geo<128, 128, 32, 2, 2>;
-  struct Args {
-    const uint16_t* dy;      // [T, d]
-    const int32_t* row_src;  // [T*k]
-    const float* topk_w;     // [T*k]
-    const uint16_t* A;       // [T*k, I]
-    float* dw2;              // [E, d, I]
-    const int32_t* offsets;
-    int d, I, k, E, accumulate;
-  };
-  using Tile = WgradTile;
-  static MOE_DEV int ntiles(const Args& a) { return a.E * (a.d / G::BM) * (a.I / G::BN); }
-  static MOE_DEV Tile decode(const Args& a, int lt) {
-    const int ntn = a.I / G::BN, ntm = a.d / G::BM;
-    Tile t;
-    t.e = lt / (ntm * ntn);
-    const int r = lt % (ntm * ntn);
-    t.m0 = (r / ntn) * G::BM;
-    t.n0 = (r % ntn) * G::BN;
-    t.p0 = a.offsets[t.e];
-    t.p1 = a.offsets[t.e + 1];
-    return t;
-  }
-  static MOE_DEV int num_k(const Args&, const Tile& t) { return (t.p1 - t.p0 + G::BK - 1) / G::BK; }
-  static MOE_DEV bool m_active(const Tile&, int) { return true; }
-  static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
-  struct Loader {
-    LoadMN<G::BM, G::BK, G::LDK, true> la;
-    LoadMN<G::BN, G::BK, G::LDK, false> lb;
-    const uint16_t* dy;  // offset to the tile's first row m0
-    const uint16_t* A;   // offset to the tile's first column n0
-    const int32_t* rs;
-    const float* tw;
-    int p0, p1, d, I, k;
-    MOE_DEV void init(const Args& a, const Tile& t) {
-      dy = a.dy + t.m0;
-      A = a.A + t.n0;
-      rs = a.row_src;
-      tw = a.topk_w;
-      p0 = t.p0;
-      p1 = t.p1;
-      d = a.d;
-      I = a.I;
-      k = a.k;
-    }
-    MOE_DEV void load(int kt) {
-      const int pbase = p0 + kt * G::BK;
-      la.load(
-          pbase,
-          [&](int p) { return p < p1 ? dy + (size_t)(rs[p] / k) * d : nullptr; },
-          [&](int p) { return tw[rs[p]]; });
-      lb.load(
-          pbase, [&](int p) { return p < p1 ? A + (size_t)p * I : nullptr; },
-          [](int) { return 1.0f; });
-    }
-    MOE_DEV void store(uint16_t* s) const {
-      la.store(s);
-      lb.store(s + G::BM * G::LDK);
-    }
-  };
-  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
-                               uint16_t*) {
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
-    float* out = a.dw2 + (size_t)t.e * a.d * a.I;
-#pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb) {
-      const int m = t.m0 + wm * G::WM + mb * 16 + lane % 16;
-#pragma unroll
-      for (int nb = 0; nb < G::NB; ++nb) {
-        const int n = t.n0 + wn * G::WN + nb * 16 + 4 * (lane / 16);
-        float4* dst = reinterpret_cast<float4*>(out + (size_t)m * a.I + n);
-        float4 v = make_float4(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]);
-        if (a.accumulate) {
-          const float4 o = *dst;
-          v.x += o.x;
-          v.y += o.y;
-          v.z += o.z;
-          v.w += o.w;
-        }
-        *dst = v;
-      }
-    }
-  }
-};
-
-// Problem 6: dW1[e][n, c] = sum_pos dH[pos, n] * Xp[pos, c].
-struct BwdGateWgrad {
-  static constexpr const char* kName = "bwd_gate_wgrad";
-  using G = Geo<128, 128, 32, 2, 2>;
-  struct Args {
-    const uint16_t* dH;  // [T*k, 2I]
-    const uint16_t* xp;  // [T*k, d]
-    float* dw1;          // [E, 2I, d]
-    const int32_t* offsets;
-    int d, I, E, accumulate;
-  };
-  using Tile = WgradTile;
-  static MOE_DEV int ntiles(const Args& a) { return a.E * (2 * a.I / G::BM) * (a.d / G::BN); }
-  static MOE_DEV Tile decode(const Args& a, int lt) {
-    const int ntn = a.d / G::BN, ntm = 2 * a.I / G::BM;
-    Tile t;
-    t.e = lt / (ntm * ntn);
-    const int r = lt % (ntm * ntn);
-    t.m0 = (r / ntn) * G::BM;
-    t.n0 = (r % ntn) * G::BN;
-    t.p0 = a.offsets[t.e];
-    t.p1 = a.offsets[t.e + 1];
-    return t;
-  }
-  static MOE_DEV int num_k(const Args&, const Tile& t) { return (t.p1 - t.p0 + G::BK - 1) / G::BK; }
-  static MOE_DEV bool m_active(const Tile&, int) { return true; }
-  static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
-  struct Loader {
-    LoadMN<G::BM, G::BK, G::LDK, false> la;
-    LoadMN<G::BN, G::BK, G::LDK, false> lb;
-    const uint16_t* dH;  // offset to the tile's first row m0
-    const uint16_t* xp;  // offset to the tile's first column n0
-    int p0, p1, twoI, d;
-    MOE_DEV void init(const Args& a, const Tile& t) {
-      dH = a.dH + t.m0;
-      xp = a.xp + t.n0;
-      p0 = t.p0;
-      p1 = t.p1;
-      twoI = 2 * a.I;
-      d = a.d;
-    }
-    MOE_DEV void load(int kt) {
-      const int pbase = p0 + kt * G::BK;
-      la.load(
-          pbase, [&](int p) { return p < p1 ? dH + (size_t)p * twoI : nullptr; },
-          [](int) { return 1.0f; });
-      lb.load(
-          pbase, [&](int p) { return p < p1 ? xp + (size_t)p * d : nullptr; },
-          [](int) { return 1.0f; });
-    }
-    MOE_DEV void store(uint16_t* s) const {
-      la.store(s);
-      lb.store(s + G::BM * G::LDK);
-    }
-  };
-  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
-                               uint16_t*) {
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
-    float* out = a.dw1 + (size_t)t.e * 2 * a.I * a.d;
-#pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb) {
-      const int m = t.m0 + wm * G::WM + mb * 16 + lane % 16;
-#pragma unroll
-      for (int nb = 0; nb < G::NB; ++nb) {
-        const int n = t.n0 + wn * G::WN + nb * 16 + 4 * (lane / 16);
-        float4* dst = reinterpret_cast<float4*>(out + (size_t)m * a.d + n);
-        float4 v = make_float4(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]);
-        if (a.accumulate) {
-          const float4 o = *dst;
-          v.x += o.x;
-          v.y += o.y;
-          v.z += o.z;
-          v.w += o.w;
-        }
-        *dst = v;
       }
     }
   }
@@ -815,25 +668,14 @@ hipError_t launch_fwd_down(const GemmFwdDownArgs& x, bool persistent, hipStream_
 }
 
 hipError_t launch_bwd_down_dgrad(const GemmBwdDownDgradArgs& x, bool persistent, hipStream_t s) {
-  BwdDownDgrad::Args a{x.dy, x.row_src, x.topk_w, x.w2, x.H, x.A, x.dH, x.dwpart,
-                       x.offsets, x.sched, x.d, x.I, x.k};
+  BwdDownDgrad::Args a{x.dy,     x.row_src, x.topk_w, x.w2, x.H, x.A, x.dH, x.dwpart,
+                       x.dyw,    x.offsets, x.sched,  x.d,  x.I, x.k};
   return launch<BwdDownDgrad>(a, sched_max_mtiles(x.Tk, x.E) * (x.I / 128), persistent, s);
 }
 
 hipError_t launch_bwd_gate_dgrad(const GemmBwdGateDgradArgs& x, bool persistent, hipStream_t s) {
   BwdGateDgrad::Args a{x.dH, x.w1, x.dXp, x.offsets, x.sched, x.d, x.I};
   return launch<BwdGateDgrad>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
-}
-
-hipError_t launch_bwd_down_wgrad(const GemmBwdDownWgradArgs& x, bool persistent, hipStream_t s) {
-  BwdDownWgrad::Args a{x.dy, x.row_src, x.topk_w, x.A, x.dw2, x.offsets,
-                       x.d, x.I, x.k, x.E, x.accumulate};
-  return launch<BwdDownWgrad>(a, x.E * (x.d / 128) * (x.I / 128), persistent, s);
-}
-
-hipError_t launch_bwd_gate_wgrad(const GemmBwdGateWgradArgs& x, bool persistent, hipStream_t s) {
-  BwdGateWgrad::Args a{x.dH, x.xp, x.dw1, x.offsets, x.d, x.I, x.E, x.accumulate};
-  return launch<BwdGateWgrad>(a, x.E * (2 * x.I / 128) * (x.d / 128), persistent, s);
 }
 
 }  // namespace moe

@@ -68,6 +68,7 @@ struct GemmBwdDownDgradArgs {
   const uint16_t* A;
   uint16_t* dH;
   float* dwpart;
+  uint16_t* dyw;  // [T*k, d]: bf16(w * dY[t]) in position order, for the down wgrad
   const int32_t* offsets;
   const int2* sched;
   int d, I, k, Tk, E;
@@ -80,28 +81,28 @@ struct GemmBwdGateDgradArgs {
   const int2* sched;
   int d, I, Tk, E;
 };
-struct GemmBwdDownWgradArgs {
-  const uint16_t* dy;
-  const int32_t* row_src;
-  const float* topk_w;
-  const uint16_t* A;
-  float* dw2;
-  const int32_t* offsets;
-  int d, I, k, E, accumulate;
-};
-struct GemmBwdGateWgradArgs {
-  const uint16_t* dH;
-  const uint16_t* xp;
-  float* dw1;
-  const int32_t* offsets;
-  int d, I, E, accumulate;
-};
 hipError_t launch_fwd_gateup(const GemmFwdGateUpArgs& a, bool persistent, hipStream_t s);
 hipError_t launch_fwd_down(const GemmFwdDownArgs& a, bool persistent, hipStream_t s);
 hipError_t launch_bwd_down_dgrad(const GemmBwdDownDgradArgs& a, bool persistent, hipStream_t s);
 hipError_t launch_bwd_gate_dgrad(const GemmBwdGateDgradArgs& a, bool persistent, hipStream_t s);
-hipError_t launch_bwd_down_wgrad(const GemmBwdDownWgradArgs& a, bool persistent, hipStream_t s);
-hipError_t launch_bwd_gate_wgrad(const GemmBwdGateWgradArgs& a, bool persistent, hipStream_t s);
+
+// wgrad.hip
+constexpr int kWgradBM = 128;         // dW rows per task stripe
+constexpr int kWgradBN = 128;         // dW columns per tile
+constexpr int kWgradTaskSteps = 64;   // K-steps of 32 positions per task (target)
+struct WgradArgs {
+  const uint16_t* L;  // [T*k, Mdim], position-major
+  const uint16_t* R;  // [T*k, Ndim], position-major
+  float* dw;          // [E, Mdim, Ndim]
+  const int32_t* offsets;
+  int4* table;        // task table, wgrad_table_entries(...) entries
+  int32_t* count;     // task count (device)
+  int E, Mdim, Ndim, accumulate;
+  const char* name;
+  const char* name_sched;
+};
+size_t wgrad_table_entries(int Tk, int E, int Mdim, int Ndim);
+hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
 
 // elementwise.hip
 hipError_t launch_combine(const uint16_t* O, const int32_t* tk_row, const float* topk_w, int T,

@@ -1,0 +1,338 @@
+// Expert weight gradients on gfx950 MFMA: dW[e] = sum over the positions p of expert e, in
+// ascending order, of L[p]^T (x) R[p], accumulated in fp32.
+//   gate/up : L = dH  [T*k, 2I], R = Xp [T*k, d]  -> dW1 [E, 2I, d]
+//   down    : L = dYw [T*k, d],  R = A  [T*k, I]  -> dW2 [E, d, I]   (dYw = bf16(w * dY[t]))
+// The expert-grouped GEMMs are named in the MarkTechPost page on Mixture-of-Kittens (MoK),
+// section "Three design decisions that matter"; their wgrad is a plain sum over the tokens an
+// expert received.
+//
+// Both operands are position-major in memory (K is the slow axis), and the output is the big
+// tensor: with tens of positions per expert the kernel is bound by writing dW. It is a
+// persistent grid that walks a device-built task table. Each task is one 128-row stripe of
+// one expert's dW and a run of consecutive 128-column tiles. Inside a task the
+// double-buffered pipeline runs on across tile boundaries. The table orders experts by
+// decreasing row count (ties to the lower index), so the longest tasks start first. Each task
+// holds roughly the same number of K-steps: an expert with few rows gets long runs of tiles, a
+// heavy expert runs of one tile.
+//
+// The waves are specialised. On gfx950 a wave's vector-memory counter covers its loads and
+// stores in issue order, so a wave that stores a 64 KB dW tile and then waits for its next
+// operand load also waits for those stores to land. Here four consumer waves run the MFMAs and
+// store dW, and never load; two producer waves only load the operands into LDS. The two sides
+// meet at a barrier that waits for LDS traffic only, so stores of many tiles stay in flight.
+//
+// Determinism: every dW element belongs to exactly one task, whose workgroup reduces K in
+// ascending position order. No atomics, no split-K.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int BM = kWgradBM, BN = kWgradBN, BK = 32;
+constexpr int KRES = 128;           // positions of L kept resident in LDS for a whole task
+constexpr int LDL = KRES + 8;       // row pitch of the L buffer [BM][LDL]
+constexpr int LDR = BK + 8;         // row pitch of an R stage [BN][LDR]
+constexpr int kConsumers = 256;                 // waves 0..3: MFMA and dW stores
+constexpr int kProducers = 4;                   // waves 4..7: operand loads
+constexpr int kThreads = kConsumers + kWave * kProducers;
+constexpr int R_STAGE = BN * LDR;   // uint16 elements per R stage
+
+struct Args {
+  const uint16_t* L;  // [T*k, Mdim]
+  const uint16_t* R;  // [T*k, Ndim]
+  float* dw;          // [E, Mdim, Ndim]
+  const int32_t* offsets;
+  const int4* table;  // (expert, first row, first n-tile, n-tile count)
+  const int32_t* count;
+  int Mdim, Ndim, accumulate;
+};
+
+// One producer wave moves a whole 32 x 128 chunk of an operand: 128 blocks of 4 positions x
+// 8 columns, two per lane (block b = lane + 64 h covers positions [4 (b % 8), +4) and columns
+// [8 (b / 8), +8)). Rows are read as 16-byte vectors and transposed in registers, so LDS holds
+// [MN][K] and each MFMA fragment is one 16-byte LDS read.
+struct Mover {
+  const uint16_t* base;  // operand base, already offset to the task's first column
+  int ld;                // row pitch of the operand (elements)
+  uint4 r[2][4];
+
+  MOE_DEV void load(int pbase, int p1, int col0, int lane) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int b = lane + kWave * h, kq = b % 8, mb = b / 8;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int p = pbase + kq * 4 + rr;
+        r[h][rr] = p < p1 ? *reinterpret_cast<const uint4*>(base + (size_t)p * ld + col0 + mb * 8)
+                          : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  // Writes the transposed blocks into an LDS buffer [MN][ldk] at K column kcol.
+  MOE_DEV void store(uint16_t* s, int ldk, int kcol, int lane) const {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int b = lane + kWave * h, kq = b % 8, mb = b / 8;
+      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[h][0]);
+      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[h][1]);
+      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[h][2]);
+      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[h][3]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int q = c >> 1;
+        uint2 v;
+        if (c & 1) {
+          v.x = (w0[q] >> 16) | (w1[q] & 0xffff0000u);
+          v.y = (w2[q] >> 16) | (w3[q] & 0xffff0000u);
+        } else {
+          v.x = (w0[q] & 0xffffu) | (w1[q] << 16);
+          v.y = (w2[q] & 0xffffu) | (w3[q] << 16);
+        }
+        *reinterpret_cast<uint2*>(s + (mb * 8 + c) * ldk + kcol + kq * 4) = v;
+      }
+    }
+  }
+};
+
+template <bool ACC>
+MOE_DEV void store_tile(const Args& a, float* out, int n0, const f32x4 (&acc)[4][4]) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int wm = wave / 2, wn = wave % 2;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int m = wm * 64 + mb * 16 + lane % 16;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int n = n0 + wn * 64 + nb * 16 + 4 * (lane / 16);
+      float4* dst = reinterpret_cast<float4*>(out + (size_t)m * a.Ndim + n);
+      float4 v = make_float4(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]);
+      if (ACC) {
+        const float4 o = *dst;
+        v.x += o.x;
+        v.y += o.y;
+        v.z += o.z;
+        v.w += o.w;
+      }
+      *dst = v;
+    }
+  }
+}
+
+// Workgroup barrier that waits for this wave's LDS operations only; global stores stay in
+// flight across it.
+MOE_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// L lives in LDS as [BM][LDL]. When the expert has at most KRES positions (nk <= KRES / BK
+// K-chunks), all of its chunks are loaded once per task at columns 32 kt, and only R streams
+// through the two R stages. Otherwise L streams too, chunk c into columns 32 (c & 1).
+//
+// Chunk c of a task (tile c / nk, K-chunk c % nk) belongs to producer wave c % kProducers. That
+// wave issues its global loads at iteration c - kProducers and writes it to LDS at iteration
+// c - 1, so every load has kProducers - 1 iterations to arrive. Producers and consumers run
+// separate loops with the same number of barriers per task (1 + nt * nk); the role is a
+// wave-uniform scalar, so each wave branches over the other role's code.
+template <bool ACC>
+__global__ void __launch_bounds__(kThreads, 2) wgrad_kernel(const Args a,
+                                                           const int4* __restrict__ table,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ count) {
+  __shared__ __align__(16) uint16_t lbuf[BM * LDL];
+  __shared__ __align__(16) uint16_t rbuf[2 * R_STAGE];
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const bool producer = wave >= kConsumers / kWave;
+  const int pq = wave - kConsumers / kWave;  // producer index 0..kProducers-1
+  const int wm = (wave / 2) & 1, wn = wave % 2;
+  const int ntasks = *count;
+  const int G = gridDim.x, G8 = G / kXcds, xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+
+  for (int round = 0;; ++round) {
+    // Round r gives XCD x the contiguous task range [r G + x G/8, r G + (x+1) G/8), so tasks
+    // of one expert (adjacent in the table) share that XCD's L2.
+    const int ti = round * G + xcd * G8 + slot;
+    if (ti >= ntasks) break;
+    const int4 task = table[ti];
+    const int e = task.x, m0 = task.y, nt = task.w;
+    const int nfirst = task.z * BN;
+    const int p0 = offsets[e], p1 = offsets[e + 1];
+    const int nk = (p1 - p0 + BK - 1) / BK;
+    const bool resident = nk <= KRES / BK;
+    const int total = nt * nk;
+
+    if (producer) {
+      if (nk == 0) continue;
+      Mover ml, mr;
+      ml.base = a.L + m0;
+      ml.ld = a.Mdim;
+      mr.base = a.R;
+      mr.ld = a.Ndim;
+      if (resident) {
+        for (int kt = pq; kt < nk; kt += kProducers) {
+          ml.load(p0 + kt * BK, p1, 0, lane);
+          ml.store(lbuf, LDL, kt * BK, lane);
+        }
+      }
+      // chunk pq: loads now; chunk 0 is written before the first barrier
+      if (pq < total) {
+        const int pb = p0 + (pq % nk) * BK;
+        mr.load(pb, p1, nfirst + (pq / nk) * BN, lane);
+        if (!resident) ml.load(pb, p1, 0, lane);
+        if (pq == 0) {
+          mr.store(rbuf, LDR, 0, lane);
+          if (!resident) ml.store(lbuf, LDL, 0, lane);
+        }
+      }
+      lds_barrier();
+      for (int it = 0; it < total; ++it) {
+        const int c = it + 1;
+        if (c < total && c % kProducers == pq) {  // its loads were issued kProducers - 1 ago
+          mr.store(rbuf + (c & 1) * R_STAGE, LDR, 0, lane);
+          if (!resident) ml.store(lbuf, LDL, (c & 1) * BK, lane);
+        }
+        const int cn = it + kProducers;
+        if (it % kProducers == pq && cn < total) {
+          const int pb = p0 + (cn % nk) * BK;
+          mr.load(pb, p1, nfirst + (cn / nk) * BN, lane);
+          if (!resident) ml.load(pb, p1, 0, lane);
+        }
+        lds_barrier();
+      }
+    } else {
+      float* out = a.dw + ((size_t)e * a.Mdim + m0) * a.Ndim;
+      f32x4 acc[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (nk == 0) {  // an expert with no rows: its dW block is zero
+        if (!ACC)
+          for (int j = 0; j < nt; ++j) store_tile<false>(a, out, nfirst + j * BN, acc);
+        continue;
+      }
+      lds_barrier();
+      const int koff = (lane / 16) * 8;
+      int j = 0, kt = 0;
+      for (int it = 0; it < total; ++it) {
+        const uint16_t* rs = rbuf + (it & 1) * R_STAGE;
+        const int lcol = (resident ? kt : (it & 1)) * BK + koff;
+        uint4 bf[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          bf[nb] = *reinterpret_cast<const uint4*>(rs + (wn * 64 + nb * 16 + lane % 16) * LDR + koff);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const uint4 af =
+              *reinterpret_cast<const uint4*>(lbuf + (wm * 64 + mb * 16 + lane % 16) * LDL + lcol);
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(bf[nb], af, acc[mb][nb]);
+        }
+        if (kt == nk - 1) {
+          store_tile<ACC>(a, out, nfirst + j * BN, acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        if (++kt == nk) {
+          kt = 0;
+          ++j;
+        }
+        lds_barrier();
+      }
+    }
+  }
+}
+
+// Task table for one weight gradient, built by one workgroup from the device offsets. Thread
+// e handles expert e: its K-steps nk = max(ceil(c_e / BK), 1), its run length
+// nt = min(ceil(kWgradTaskSteps / nk), ntn) tiles, and its tasks
+// mstripes * ceil(ntn / nt). Experts are laid out by decreasing row count (ties to the lower
+// index), each expert's tasks stripe-major. count[0] receives the number of tasks.
+__global__ void __launch_bounds__(1024) wgrad_sched_kernel(const int32_t* __restrict__ offsets,
+                                                           int E, int mstripes, int ntn,
+                                                           int4* __restrict__ table,
+                                                           int32_t* __restrict__ count) {
+  __shared__ int cnt[1024];
+  __shared__ int scan[1024];
+  const int e = threadIdx.x;
+  const int c = e < E ? offsets[e + 1] - offsets[e] : -1;
+  cnt[e] = c;
+  __syncthreads();
+  int rank = e;
+  int ntask = 0, nt = 1, nchunks = 0;
+  if (e < E) {
+    rank = 0;
+    for (int j = 0; j < E; ++j) {
+      const int cj = cnt[j];
+      rank += (cj > c) || (cj == c && j < e);
+    }
+    const int nk = max((c + BK - 1) / BK, 1);
+    nt = min((kWgradTaskSteps + nk - 1) / nk, ntn);
+    nchunks = (ntn + nt - 1) / nt;
+    ntask = mstripes * nchunks;
+  }
+  scan[rank] = ntask;  // ranks of the E experts are a permutation of 0..E-1
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = rank >= off ? scan[rank - off] : 0;
+    __syncthreads();
+    scan[rank] += v;
+    __syncthreads();
+  }
+  const int start = scan[rank] - ntask;
+  for (int s = 0; s < mstripes; ++s)
+    for (int ch = 0; ch < nchunks; ++ch)
+      table[start + s * nchunks + ch] = make_int4(e, s * BM, ch * nt, min(nt, ntn - ch * nt));
+  if (rank == 1023) count[0] = scan[1023];
+}
+
+int resident_grid() {
+  static int grid = 0;  // every device of one process is an MI355X
+  if (grid == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&wgrad_kernel<false>), kThreads, 0) != hipSuccess)
+      return 0;
+    grid = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
+  }
+  return grid;
+}
+
+}  // namespace
+
+size_t wgrad_table_entries(int Tk, int E, int Mdim, int Ndim) {
+  const long long mstripes = Mdim / BM, ntn = Ndim / BN;
+  const long long per_stripe = ntn * ((long long)Tk + (long long)E * BK) / (BK * kWgradTaskSteps) + E;
+  const long long cap = (long long)E * ntn;
+  return (size_t)(mstripes * (per_stripe < cap ? per_stripe : cap));
+}
+
+hipError_t launch_wgrad(const WgradArgs& x, hipStream_t s) {
+  {
+    TraceScope trace(x.name_sched, s);
+    hipLaunchKernelGGL(wgrad_sched_kernel, dim3(1), dim3(1024), 0, s, x.offsets, x.E, x.Mdim / BM,
+                       x.Ndim / BN, x.table, x.count);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int grid = resident_grid();
+  if (grid <= 0) return hipErrorInvalidValue;
+  Args a{x.L, x.R, x.dw, x.offsets, x.table, x.count, x.Mdim, x.Ndim, x.accumulate};
+  {
+    TraceScope trace(x.name, s);
+    if (x.accumulate)
+      hipLaunchKernelGGL(wgrad_kernel<true>, dim3(grid), dim3(kThreads), 0, s, a, x.table,
+                         x.offsets, x.count);
+    else
+      hipLaunchKernelGGL(wgrad_kernel<false>, dim3(grid), dim3(kThreads), 0, s, a, x.table,
+                         x.offsets, x.count);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe
