@@ -26,7 +26,9 @@ sys.path.insert(0, ROOT)
 
 HBM_GBPS = 8000.0         # MI355X HBM3E, GB/s
 MFMA_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, TFLOP/s
-VALU_FP32_TFLOPS = 157.3   # fp32 vector
+# fp32 FMA on the vector ALUs without packed-fp32 instructions (the library is built without
+# them): 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz. Packed fp32 would double it (157.3).
+VALU_FP32_TFLOPS = 78.6
 RIDGE_BF16 = MFMA_BF16_TFLOPS * 1e12 / (HBM_GBPS * 1e9)
 
 
@@ -78,6 +80,21 @@ def kernel_roofline(name, nbytes, flops, us):
     ach = nbytes / s / 1e9
     return {"bound": "hbm", "achieved": ach, "peak": HBM_GBPS, "unit": "GB/s",
             "frac": ach / HBM_GBPS}
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel's sources changed since the counters were taken."""
+    import json as _json
+    from mixture_experts_layer_deterministic_amd.profsum import KERNELS, source_hash
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = _json.load(open(path)).get("kernels", {}).get(kernel)
+    src = {n: f for _, n, f in KERNELS}.get(kernel)
+    if not rec or not src or rec["source_sha"] != source_hash(src):
+        return None
+    return rec["read_bytes"] + rec["write_bytes"]
 
 
 def cpu_baseline(inp, cfg, s_small=4, s_large=12):
@@ -244,8 +261,9 @@ def main():
     if dominant:
         kd = kernels[dominant]
         roof = {"kernel": dominant, "bound": kd["bound"], "achieved": kd["achieved"],
-                "peak": kd["peak"], "unit": kd["unit"], "frac": kd["frac"], "traffic": None,
-                "us_per_launch": kd["us"]}
+                "peak": kd["peak"], "unit": kd["unit"], "frac": kd["frac"],
+                "traffic": measured_traffic(args.workload, dominant),
+                "alg_bytes": kd["alg_bytes"], "us_per_launch": kd["us"]}
     gemm_us = sum(kernels[g]["us"] for g in GEMMS if g in kernels)
     gemm_flops = sum(alg[g][1] for g in GEMMS)
     gemm_bytes = sum(alg[g][0] for g in GEMMS)
@@ -261,6 +279,22 @@ def main():
     for n in ("perm_place", "combine"):
         if n in kernels:
             pc[n] = {"GB/s": kernels[n].get("achieved"), "frac_hbm": kernels[n].get("frac")}
+
+    # practical HBM ceiling: one plain 2 GiB device copy (read + write), best of 3
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    best = None
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b)
+        best = t if best is None else min(best, t)
+    hbm_copy = round(2 * n / (best * 1e-3) / 1e9, 1)
+    del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -287,6 +321,7 @@ def main():
         "cpu_baseline": cpu,
         "grouped_gemm": gemm,
         "permute_combine": pc,
+        "hbm_copy": {"GB/s": hbm_copy, "bytes": 2 * n, "what": "one plain device copy, read + write"},
         "kernels": kernels,
         "host_seconds_timed": round(t_host, 4),
     }

@@ -296,12 +296,12 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
     L(launch_dw_router(dwpart, Y.nIt, tk_row, topk_w, cfg->T, k, d_topk_w, dl_pos, routed, s));
   if (!L.err)
     L(launch_wgrad({dyw, A, dw2, offsets, at<int4>(workspace, Y.wg_table2), wg_count + 1, E, d, I,
-                    accumulate, "bwd_down_wgrad", "wgrad_sched_down"},
+                    accumulate, false, "bwd_down_wgrad", "wgrad_sched_down"},
                    s));
   if (!L.err) L(launch_bwd_gate_dgrad({dH, w1p, dXp, offsets, sched, d, I, Tk, E}, pers, s));
   if (!L.err)
     L(launch_wgrad({dH, xp, dw1, offsets, at<int4>(workspace, Y.wg_table1), wg_count, E, 2 * I, d,
-                    accumulate, "bwd_gate_wgrad", "wgrad_sched_gate"},
+                    accumulate, true, "bwd_gate_wgrad", "wgrad_sched_gate"},
                    s));
   if (!L.err)
     L(launch_uncombine(dXp, tk_row, topk_idx, dl_pos,

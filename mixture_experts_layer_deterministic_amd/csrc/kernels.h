@@ -98,6 +98,7 @@ struct WgradArgs {
   int4* table;        // task table, wgrad_table_entries(...) entries
   int32_t* count;     // task count (device)
   int E, Mdim, Ndim, accumulate;
+  bool gate;  // dW1 (true) or dW2 (false)
   const char* name;
   const char* name_sched;
 };

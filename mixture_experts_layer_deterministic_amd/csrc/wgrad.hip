@@ -133,7 +133,8 @@ MOE_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::
 // c - 1, so every load has kProducers - 1 iterations to arrive. Producers and consumers run
 // separate loops with the same number of barriers per task (1 + nt * nk); the role is a
 // wave-uniform scalar, so each wave branches over the other role's code.
-template <bool ACC>
+// GATE only separates the two instances (dW1 and dW2) for profilers.
+template <bool ACC, bool GATE>
 __global__ void __launch_bounds__(kThreads, 2) wgrad_kernel(const Args a,
                                                            const int4* __restrict__ table,
                                                            const int32_t* __restrict__ offsets,
@@ -296,7 +297,7 @@ int resident_grid() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&wgrad_kernel<false>), kThreads, 0) != hipSuccess)
+            &per_cu, reinterpret_cast<const void*>(&wgrad_kernel<false, false>), kThreads, 0) != hipSuccess)
       return 0;
     grid = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
   }
@@ -325,12 +326,9 @@ hipError_t launch_wgrad(const WgradArgs& x, hipStream_t s) {
   Args a{x.L, x.R, x.dw, x.offsets, x.table, x.count, x.Mdim, x.Ndim, x.accumulate};
   {
     TraceScope trace(x.name, s);
-    if (x.accumulate)
-      hipLaunchKernelGGL(wgrad_kernel<true>, dim3(grid), dim3(kThreads), 0, s, a, x.table,
-                         x.offsets, x.count);
-    else
-      hipLaunchKernelGGL(wgrad_kernel<false>, dim3(grid), dim3(kThreads), 0, s, a, x.table,
-                         x.offsets, x.count);
+    auto kern = x.accumulate ? (x.gate ? wgrad_kernel<true, true> : wgrad_kernel<true, false>)
+                             : (x.gate ? wgrad_kernel<false, true> : wgrad_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, s, a, x.table, x.offsets, x.count);
   }
   return hipGetLastError();
 }

@@ -1,0 +1,140 @@
+"""Summaries of rocprofv3 output for the MoE layer's kernels.
+
+Usage (after a kernel-trace run and two counter runs of bench.py):
+    python -m mixture_experts_layer_deterministic_amd.profsum \
+        --stats DIR/run_kernel_stats.csv --fetch DIR/run_counter_collection.csv \
+        --write DIR/run_counter_collection.csv --calib-mib 1024 \
+        --workload dsv3 --command "..." --out profiles/NAME.md --traffic profiles/traffic_dsv3.json
+
+It writes a short markdown table (per-kernel launches, average duration, HBM bytes per launch)
+and a JSON record of the HBM bytes per launch of every kernel. Each kernel's entry in the JSON
+record carries a hash of the source files it is built from. bench.py reports a kernel's traffic
+only while that hash still matches the sources, so counters taken on older code never appear.
+
+HBM bytes come from the TCC counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by
+what the same counter reads for one plain device copy of known size in the same run: the copy
+reads and writes exactly calib-mib MiB.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+
+# rocprofv3 kernel-name pattern -> (bench name, source file)
+KERNELS = [
+    (r"router_logits_kernel", "router_logits", "router.hip"),
+    (r"router_topk_kernel", "router_topk", "router.hip"),
+    (r"perm_hist_kernel", "perm_hist", "permute.hip"),
+    (r"perm_scan_kernel", "perm_scan", "permute.hip"),
+    (r"perm_place_kernel", "perm_place", "permute.hip"),
+    (r"wgrad_sched_kernel", "wgrad_sched", "wgrad.hip"),
+    (r"sched_build_kernel", "sched_build", "gemm.hip"),
+    (r"gg_kernel<moe::FwdGateUp", "fwd_gateup", "gemm.hip"),
+    (r"gg_kernel<moe::FwdDown", "fwd_down", "gemm.hip"),
+    (r"gg_kernel<moe::BwdDownDgrad", "bwd_down_dgrad", "gemm.hip"),
+    (r"gg_kernel<moe::BwdGateDgrad", "bwd_gate_dgrad", "gemm.hip"),
+    (r"wgrad_kernel<(true|false), false>", "bwd_down_wgrad", "wgrad.hip"),
+    (r"wgrad_kernel<(true|false), true>", "bwd_gate_wgrad", "wgrad.hip"),
+    (r"moe::combine_kernel", "combine", "elementwise.hip"),
+    (r"dw_router_kernel", "dw_router", "elementwise.hip"),
+    (r"uncombine_kernel", "uncombine", "elementwise.hip"),
+    (r"dwr_kernel", "dwr", "elementwise.hip"),
+]
+COMMON_SOURCES = ("common.h", "kernels.h")
+
+
+def bench_name(raw: str):
+    """(bench name, source file) of a rocprofv3 kernel name, or None for other kernels."""
+    if "moe::" not in raw:
+        return None
+    for pat, name, src in KERNELS:
+        if re.search(pat, raw):
+            return name, src
+    return None
+
+
+def source_hash(src: str) -> str:
+    h = hashlib.sha256()
+    for f in (src, *COMMON_SOURCES):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_per_kernel(path, calib_bytes):
+    rows = list(csv.DictReader(open(path)))
+    copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+    if not copies:
+        raise SystemExit(f"{path}: no calibration copy found")
+    scale = calib_bytes / (max(copies) * 1024.0)  # bytes per counted byte
+    out = {}
+    for r in rows:
+        bn = bench_name(r["Kernel_Name"])
+        if bn:
+            out.setdefault(bn[0], []).append(float(r["Counter_Value"]) * 1024.0 * scale)
+    return {k: sum(v) / len(v) for k, v in out.items()}, scale
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--stats", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--calib-mib", type=int, default=1024)
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--command", required=True)
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--traffic")
+    args = ap.parse_args()
+
+    stats = {}
+    srcs = {}
+    for r in csv.DictReader(open(args.stats)):
+        bn = bench_name(r["Name"])
+        if not bn:
+            continue
+        name, src = bn
+        srcs[name] = src
+        s = stats.setdefault(name, [0, 0.0])
+        s[0] += int(r["Calls"])
+        s[1] += float(r["TotalDurationNs"])
+    total = sum(v[1] for v in stats.values())
+    fetch = write = None
+    if args.fetch and args.write:
+        fetch, fs = _counter_per_kernel(args.fetch, args.calib_mib << 20)
+        write, ws = _counter_per_kernel(args.write, args.calib_mib << 20)
+
+    lines = [f"# rocprofv3 kernel summary: {args.workload}", "",
+             f"Command: `{args.command}`", ""]
+    if fetch is not None:
+        lines += [f"HBM bytes: FETCH_SIZE x {fs:.3f} and WRITE_SIZE x {ws:.3f}, the factors that "
+                  f"map a plain {args.calib_mib} MiB device copy onto its true size.", ""]
+    lines += ["| kernel | launches | avg us | share of layer time | HBM read GB/launch | "
+              "HBM write GB/launch |", "|---|---|---|---|---|---|"]
+    for name, (calls, dur) in sorted(stats.items(), key=lambda kv: -kv[1][1]):
+        fr = f"{fetch[name] / 1e9:.3f}" if fetch and name in fetch else "-"
+        wr = f"{write[name] / 1e9:.3f}" if write and name in write else "-"
+        lines.append(f"| {name} | {calls} | {dur / calls / 1e3:.1f} | {dur / total:.1%} | {fr} | {wr} |")
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if args.traffic and fetch is not None:
+        rec = {"workload": args.workload, "command": args.command, "kernels": {}}
+        for name in sorted(set(fetch) & set(write)):
+            rec["kernels"][name] = {"read_bytes": round(fetch[name]), "write_bytes": round(write[name]),
+                                    "source_sha": source_hash(srcs.get(name) or
+                                                              dict((n, s) for _, n, s in KERNELS)[name])}
+        with open(args.traffic, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()
