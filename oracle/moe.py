@@ -76,9 +76,13 @@ def router_logits_fp32(X, Wr) -> np.ndarray:
     assert _is_bf16(X32) and _is_bf16(W32), "router inputs must hold bfloat16 values"
     T, d = X32.shape
     E = W32.shape[0]
+    XT = np.ascontiguousarray(X32.T)  # row i holds x[:, i] (contiguous reads; same values)
+    WT = np.ascontiguousarray(W32.T)
     acc = np.zeros((T, E), dtype=np.float32)
+    prod = np.empty_like(acc)
     for i in range(d):
-        acc += np.multiply.outer(X32[:, i], W32[:, i])
+        np.multiply.outer(XT[i], WT[i], out=prod)  # exact: bf16 x bf16 fits in fp32
+        acc += prod                                # one fp32 rounding per step, i ascending
     return acc
 
 

@@ -1,0 +1,92 @@
+"""Helpers of the GPU tests: running the layer through the C ABI, the oracle on the same inputs,
+and the parity and bitwise comparisons."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import workload
+from tests._util import assert_act, assert_grad, ensure_built
+
+m = ensure_built()
+from mixture_experts_layer_deterministic_amd.layer import MoeLayer  # noqa: E402
+
+DEV = "cuda"
+
+
+def _np(t):
+    return workload.to_numpy(t)
+
+
+def _announce(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(inp, persistent=False, slot=0, ring_slots=1):
+    cfg = inp["cfg"]
+    T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
+    L = MoeLayer(T, d, E, k, I, device=DEV, ring_slots=ring_slots, persistent=persistent)
+    wr = inp.get("Wr")
+    if wr is None:
+        L.set_routing(inp["topk_idx"], inp["topk_w"])
+    L.step(inp["X"], wr, inp["W1"], inp["W2"], inp["dY"], slot=slot)
+    torch.cuda.synchronize()
+    return L
+
+
+def run_oracle(inp):
+    X, W1, W2, dY = (_np(inp[n]) for n in ("X", "W1", "W2", "dY"))
+    if "Wr" in inp:
+        Wr = _np(inp["Wr"])
+        f = oracle.forward(X, W1, W2, Wr=Wr, k=inp["cfg"]["k"])
+        b = oracle.backward(f, X, W1, W2, dY, Wr=Wr)
+    else:
+        f = oracle.forward(X, W1, W2, topk_idx=_np(inp["topk_idx"]), topk_w=_np(inp["topk_w"]))
+        b = oracle.backward(f, X, W1, W2, dY)
+    return f, b
+
+
+def check_parity(L, inp, f, b, slot=0):
+    routed = "Wr" in inp
+    k = inp["cfg"]["k"]
+    if routed:
+        np.testing.assert_array_equal(_np(L.logits), f["logits"])
+        np.testing.assert_array_equal(_np(L.topk_idx), f["idx"])
+        np.testing.assert_allclose(_np(L.topk_w), f["w"], rtol=0, atol=1e-6)
+    np.testing.assert_array_equal(_np(L.counts), f["counts"])
+    np.testing.assert_array_equal(_np(L.offsets), f["offsets"])
+    np.testing.assert_array_equal(_np(L.row_src), f["row_src"])
+    np.testing.assert_array_equal(_np(L.tk_row), f["tk_row"])
+    xp = _np(L.xp(slot))
+    np.testing.assert_array_equal(xp, _np(inp["X"])[f["row_src"] // k])
+    assert_act("H", _np(L.H()), f["H"])
+    assert_act("A", _np(L.A()), f["A"])
+    assert_act("O", _np(L.O()), f["O"])
+    assert_act("Y", _np(L.y), f["Y"])
+    assert_act("dH", _np(L.dH()), b["dH"])
+    assert_act("dXp", _np(L.dXp()), b["dXp"])
+    assert_act("dX", _np(L.dx), b["dX"])
+    assert_grad("dW1", _np(L.dw1), b["dW1"])
+    assert_grad("dW2", _np(L.dw2), b["dW2"])
+    assert_grad("d_topk_w", _np(L.d_topk_w), b["dw"])
+    if routed:
+        assert_grad("dWr", _np(L.dwr), b["dWr"])
+
+
+def outputs(L, routed, clone=True):
+    outs = [L.logits, L.topk_idx, L.topk_w] if routed else []
+    outs += [L.counts, L.offsets, L.row_src, L.tk_row, L.y, L.H(), L.A(), L.dx, L.dw1, L.dw2,
+             L.d_topk_w]
+    if routed:
+        outs.append(L.dwr)
+    return [o.clone() for o in outs] if clone else outs
+
+
+def assert_bitwise_equal(a, b):
+    assert len(a) == len(b)
+    for i, (x, y) in enumerate(zip(a, b)):
+        assert x.dtype == y.dtype and x.shape == y.shape, i
+        assert torch.equal(x.view(torch.uint8) if x.dtype != torch.bool else x,
+                           y.view(torch.uint8) if y.dtype != torch.bool else y), i
