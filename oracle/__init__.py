@@ -26,14 +26,20 @@ experts a token visits), so both sides compute them in float32, in one stated or
 path, and downstream steps use the rounded values. ``storage="exact"`` skips that rounding and
 gives the mathematical reference.
 
+MXFP8 mode (``precision="mxfp8"``) applies OCP MXFP8 quantisation (``oracle/mx.py``) to the
+operands of the forward and dgrad expert GEMMs, along each GEMM's reduction axis.
+
 Pins: tests/test_oracle_*.py check this module against things other than itself:
 * brute force over all k-subsets;
 * a dense evaluation of every token through every expert, masked;
 * central finite differences;
 * torch autograd on an independent dense formulation;
 * closed forms, special cases and invariants;
-* a hand-worked fp32 summation-order example in tests/golden/.
+* a hand-worked fp32 summation-order example in tests/golden/;
+* for MXFP8: torch's float8_e4m3fn decode and cast, brute-force rounding, exact power-of-two
+  scale bounds, and quantisation-axis checks on inputs that are exact in MXFP8.
 """
+from . import mx  # noqa: F401
 from .moe import (  # noqa: F401
     bf16_round,
     router_logits_fp32,

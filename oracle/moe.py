@@ -12,6 +12,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import mx
+
 readings = {
     "gate": "softmax over all E router logits, keep the k largest, renormalise over those k; "
             "no bias, no capacity, no auxiliary loss (toknow.ai summary: each input goes to a "
@@ -33,6 +35,13 @@ readings = {
                    "SwiGLU backward), flowing on to the logits, the router weight and the input",
     "storage_bf16": "H = [g|u], A, O, Y, dH, dXp, dX stored as bf16; A is rounded once from "
                     "the unrounded g, u; every later step reads the stored value",
+    "mxfp8": "MXFP8 mode (MarkTechPost, closing paragraph of 'Three design decisions that "
+             "matter': BF16 and MXFP8 modes): every expert GEMM of forward and dgrad takes both "
+             "operands as MXFP8 images quantised along that GEMM's reduction axis - Xp and W1 "
+             "along d, the stored A and W2 along I (forward); dY and W2 along d, the stored dH "
+             "and W1 along 2I (dgrad). The router-weight gradient is the fused <dA', A> with dA' "
+             "from the quantised dgrad GEMM. The weight gradients stay on bf16 operands, with Xp "
+             "taken as its MXFP8 image (the ring holds the quantised tokens); so does dWr",
 }
 
 
@@ -141,7 +150,7 @@ def _sigmoid(z):
 
 
 def forward(X, W1, W2, *, Wr=None, k=None, topk_idx=None, topk_w=None,
-            storage="bf16", logits="fp32", experts=None) -> dict:
+            storage="bf16", logits="fp32", experts=None, precision="bf16") -> dict:
     """Forward pass of the MoE layer.
 
     Routing comes from the router (Wr, k) or is given (topk_idx, topk_w). ``experts`` limits
@@ -149,8 +158,10 @@ def forward(X, W1, W2, *, Wr=None, k=None, topk_idx=None, topk_w=None,
 
     Per expert e and each of its rows (readings "expert", "storage_bf16"):
     [g | u] = x W1_e^T, a = silu(g) * u, o = a W2_e^T. Then y_t = sum_j w_tj o_tj, j ascending
-    (reading "combine"). Returns a dict of every intermediate the GPU path also produces.
+    (reading "combine"). With precision="mxfp8" the two GEMMs take MXFP8 images of their
+    operands (reading "mxfp8"). Returns a dict of every intermediate the GPU path also produces.
     """
+    mxq = mx.qdq if precision == "mxfp8" else (lambda a, axis=-1: a)
     X = np.asarray(X, np.float64)
     T, d = X.shape
     E, twoI, _ = W1.shape
@@ -177,15 +188,15 @@ def forward(X, W1, W2, *, Wr=None, k=None, topk_idx=None, topk_w=None,
         if p1 == p0:
             continue
         tok = row_src[p0:p1] // k
-        x = X[tok]
-        w1 = np.asarray(W1[e], np.float64)
+        x = mxq(X[tok])
+        w1 = mxq(np.asarray(W1[e], np.float64))
         g = x @ w1[:I].T
         u = x @ w1[I:].T
         H[p0:p1, :I] = rnd(g)
         H[p0:p1, I:] = rnd(u)
         a = rnd(_silu(g) * u)
         A[p0:p1] = a
-        o = a @ np.asarray(W2[e], np.float64).T
+        o = mxq(a) @ mxq(np.asarray(W2[e], np.float64)).T
         O_exact[p0:p1] = o
         O[p0:p1] = rnd(o)
     Y = np.zeros((T, d))
@@ -193,7 +204,7 @@ def forward(X, W1, W2, *, Wr=None, k=None, topk_idx=None, topk_w=None,
         Y += w[:, j:j + 1] * O[tk_row[np.arange(T) * k + j]]
     out.update(idx=idx, w=w, counts=counts, offsets=offsets, row_src=row_src, tk_row=tk_row,
                H=H, A=A, O=O, O_exact=O_exact, Y=rnd(Y), k=k, storage=storage,
-               routed=topk_idx is None)
+               routed=topk_idx is None, precision=precision)
     return out
 
 
@@ -215,7 +226,10 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None) -> dict:
     A and dH feed the later steps. Empty experts get all-zero dW1_e and dW2_e blocks.
     ``experts`` limits the expert math to a subset (rows of other experts stay NaN). dW1 and dW2
     then hold one block per listed expert, in the order listed in out["experts"].
+    In MXFP8 mode (reading "mxfp8") both dgrad GEMMs take MXFP8 images of their operands, dw is
+    <dA', A>, and Xp enters dW1 and dWr as its MXFP8 image.
     """
+    mxmode = fwd.get("precision", "bf16") == "mxfp8"
     X = np.asarray(X, np.float64)
     dY = np.asarray(dY, np.float64)
     T, d = X.shape
@@ -243,8 +257,13 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None) -> dict:
         dy = dY[tok]
         w2 = np.asarray(W2[e], np.float64)
         w1 = np.asarray(W1[e], np.float64)
-        dw_pos[p0:p1] = np.sum(dy * O_used[p0:p1], axis=1)
-        dA = wv * (dy @ w2)
+        if mxmode:
+            dAp = mx.qdq(dy) @ mx.qdq(w2.T).T      # W2 [d, I] quantised along d
+            dw_pos[p0:p1] = np.sum(dAp * fwd["A"][p0:p1], axis=1)
+        else:
+            dAp = dy @ w2
+            dw_pos[p0:p1] = np.sum(dy * O_used[p0:p1], axis=1)
+        dA = wv * dAp
         g = fwd["H"][p0:p1, :I]
         u = fwd["H"][p0:p1, I:]
         s = _sigmoid(g)
@@ -252,9 +271,12 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None) -> dict:
         du = dA * (g * s)
         dh = rnd(np.concatenate([dg, du], axis=1))
         dH[p0:p1] = dh
-        dXp[p0:p1] = rnd(dh @ w1)
+        if mxmode:
+            dXp[p0:p1] = rnd(mx.qdq(dh) @ mx.qdq(w1.T).T)  # W1 [2I, d] quantised along 2I
+        else:
+            dXp[p0:p1] = rnd(dh @ w1)
         dW2[slot] = (wv * dy).T @ fwd["A"][p0:p1]
-        dW1[slot] = dh.T @ X[tok]
+        dW1[slot] = dh.T @ (mx.qdq(X[tok]) if mxmode else X[tok])
     dw = dw_pos[tk_row].reshape(T, k)
     dXsum = np.zeros((T, d))
     for j in range(k):
@@ -269,6 +291,6 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None) -> dict:
         Wr64 = np.asarray(Wr, np.float64)
         dXsum = dXsum + dlogits @ Wr64
         out["dlogits"] = dlogits
-        out["dWr"] = dlogits.T @ X
+        out["dWr"] = dlogits.T @ (mx.qdq(X) if mxmode else X)
     out["dX"] = rnd(dXsum)
     return out

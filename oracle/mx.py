@@ -1,0 +1,92 @@
+"""MXFP8 quantisation for the oracle. Test infrastructure only: the GPU library never uses it.
+
+The pages name an MXFP8 precision mode next to BF16 (MarkTechPost, "Cursor Open-Sources
+Mixture-of-Kittens (MoK)", closing paragraph of "Three design decisions that matter") and give
+no recipe. The format is the OCP Microscaling (MX) v1.0 MXFP8 format:
+* the element is E4M3: sign, 4 exponent bits with bias 7, 3 mantissa bits. Exponent field 0
+  encodes subnormals m/8 * 2^-6. There is no infinity. S.1111.111 is NaN, so the largest
+  finite magnitude is 1.75 * 2^8 = 448;
+* every block of 32 consecutive elements along the reduction axis shares one E8M0 scale, a bare
+  power of two 2^(code - 127) with code 0..254 (255 is NaN).
+
+Readings (the pages are silent):
+* The scale exponent is floor(log2(amax)) - 8, with 8 the largest normal exponent of E4M3,
+  clamped to the E8M0 range. An all-zero block gets code 0.
+* Each element v becomes E4M3(v / scale), rounded to nearest with ties to the even code.
+  Magnitudes beyond 448 saturate to 448. After scaling the block maximum lies in [256, 512), so
+  only values in (448, 512) saturate.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 32
+E4M3_MAX = 448.0
+E4M3_EMAX = 8  # exponent of the largest normal E4M3 value
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """float64 value of each E4M3 code (uint8); NaN for S.1111.111."""
+    c = np.asarray(codes, dtype=np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 0xF
+    m = c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+# The 127 non-negative finite values in code order; the order is ascending.
+_POS = e4m3_value(np.arange(127))
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """E4M3 codes of float64 values: round to nearest, ties to the even code, and saturate to
+    +-448. The sign bit is the sign of v."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    hi = np.clip(np.searchsorted(_POS, a, side="left"), 0, 126)  # first value >= a
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo = a - _POS[lo]
+    d_hi = _POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def e8m0_code(amax) -> np.ndarray:
+    """Shared-scale code of blocks with the given max magnitudes: floor(log2 amax) - 8 + 127,
+    clamped to 0..254, and 0 for an all-zero block. frexp gives amax = f 2^x with f in [0.5, 1),
+    so floor(log2 amax) = x - 1 exactly."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, x = np.frexp(amax)
+    code = np.clip(x - 1 - E4M3_EMAX + 127, 0, 254)
+    return np.where(amax > 0, code, 0).astype(np.uint8)
+
+
+def quantize(x, axis=-1):
+    """MXFP8 quantisation along `axis` (its length a multiple of 32). Returns (codes uint8 with
+    the shape of x, scale codes uint8 with that axis divided by 32)."""
+    x = np.moveaxis(np.asarray(x, dtype=np.float64), axis, -1)
+    n = x.shape[-1]
+    assert n % BLOCK == 0, "the quantised axis must be a multiple of 32"
+    b = x.reshape(*x.shape[:-1], n // BLOCK, BLOCK)
+    sc = e8m0_code(np.max(np.abs(b), axis=-1))
+    q = e4m3_encode(b / np.exp2(sc.astype(np.float64) - 127.0)[..., None])
+    q = q.reshape(x.shape)
+    return np.moveaxis(q, -1, axis), np.moveaxis(sc, -1, axis)
+
+
+def dequantize(q, sc, axis=-1) -> np.ndarray:
+    """float64 values of MXFP8 codes with their block scales along `axis`."""
+    q = np.moveaxis(np.asarray(q), axis, -1)
+    sc = np.moveaxis(np.asarray(sc), axis, -1)
+    v = e4m3_value(q).reshape(*q.shape[:-1], q.shape[-1] // BLOCK, BLOCK)
+    v = v * np.exp2(sc.astype(np.float64) - 127.0)[..., None]
+    return np.moveaxis(v.reshape(q.shape), -1, axis)
+
+
+def qdq(x, axis=-1) -> np.ndarray:
+    """The float64 image of x after MXFP8 quantisation along `axis`."""
+    q, sc = quantize(x, axis)
+    return dequantize(q, sc, axis)
