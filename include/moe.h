@@ -61,7 +61,16 @@ enum {
 enum { MOE_DEVICE_BAD_EXPERT_INDEX = 1 /* a topk_idx entry outside [0, E): that row is skipped */ };
 
 /* Layer shape and mode. Constraints checked on the host: T >= 1; 1 <= k <= E <= 1024;
- * d % 256 == 0; I % 128 == 0; T * k < 2^31; precision MOE_PREC_BF16. */
+ * d % 256 == 0; I % 128 == 0; T * k < 2^31; precision MOE_PREC_BF16 or MOE_PREC_MXFP8.
+ *
+ * MXFP8 mode (the pages name BF16 and MXFP8 modes: MarkTechPost, closing paragraph of "Three
+ * design decisions that matter") follows the OCP MX v1.0 MXFP8 format. Elements are E4M3; every
+ * 32 consecutive elements along a GEMM's reduction axis share one E8M0 scale 2^(code - 127),
+ * code = floor(log2 amax) - 8 + 127 clamped to 0..254 (0 for an all-zero block). Elements round
+ * to nearest even and saturate to +-448. The forward GEMMs read Xp and W1 quantised along d,
+ * and A and W2 along I. The dgrad GEMMs read dY and W2 along d, and dH and W1 along 2I. The
+ * weight gradients and dWr read bf16 operands, with Xp taken as the MXFP8 image the ring
+ * holds. All accumulation is fp32; outputs are bf16 as in BF16 mode. */
 typedef struct moe_cfg {
     int32_t T;         /* tokens entering the layer */
     int32_t d;         /* hidden size */
@@ -82,10 +91,28 @@ typedef struct moe_sizes {
     size_t ws_O;           /* offset of the expert outputs O, bf16 [T*k, d], valid after forward */
     size_t ws_dH;          /* offset of dH, bf16 [T*k, 2I], valid after backward */
     size_t ws_dXp;         /* offset of dXp, bf16 [T*k, d], valid after backward */
+    size_t wq;             /* MXFP8: bytes of the quantised-weight buffer (0 in BF16 mode) */
 } moe_sizes;
 
-/* Sizes of every caller buffer for `cfg`. Host only; enqueues nothing. */
+/* Sizes of every caller buffer for `cfg`. Host only; enqueues nothing.
+ * In MXFP8 mode a ring slot holds the E4M3 codes of Xp [T*k, d] followed (at the next 256-byte
+ * boundary) by their scales [T*k, d/32]. */
 int moe_query(const moe_cfg* cfg, moe_sizes* out);
+
+/*
+ * moe_quantize_weights - MXFP8 mode only: the quantised expert weights every MXFP8 forward and
+ * backward reads. Call it once per weight update; the result serves any number of batches.
+ *
+ *   w1  bf16 [E, 2I, d]   in
+ *   w2  bf16 [E, d, I]    in
+ *   wq  bytes [wq_bytes]  out, wq_bytes >= moe_sizes.wq. It receives four MXFP8 tensors, each
+ *       with its per-32 scales: W1 along d [E, 2I, d] and W2 along I [E, d, I] (forward), and W2
+ *       along d stored transposed [E, I, d] and W1 along 2I stored transposed [E, d, 2I]
+ *       (dgrad). The layout inside wq is private to the library.
+ * Errors: MOE_ERR_INVALID_ARG in BF16 mode; MOE_ERR_WORKSPACE_TOO_SMALL for a short wq.
+ */
+int moe_quantize_weights(const moe_cfg* cfg, const void* w1, const void* w2, void* wq,
+                         size_t wq_bytes, moe_stream_t stream);
 
 /*
  * moe_route - router logits, top-k selection and renormalised softmax weights.
@@ -121,7 +148,8 @@ int moe_route(const moe_cfg* cfg, const void* x, const void* w_router, float* lo
  *   topk_idx int32 [T, k]          in   (from moe_route, or given by the caller)
  *   x        bf16 [T, d]           in
  *   ring     bytes [ring_bytes]    out: slot `slot` (at slot * ring_slot bytes) receives
- *                                       Xp[pos] = x[row_src[pos] / k], bf16 [T*k, d]
+ *                                       Xp[pos] = x[row_src[pos] / k], bf16 [T*k, d]; in MXFP8
+ *                                       mode its MXFP8 image (codes, then scales)
  *   counts   int32 [E]             out: rows per expert
  *   offsets  int32 [E+1]           out: exclusive scan of counts, offsets[E] = T*k
  *   row_src  int32 [T*k]           out: pos -> r
@@ -150,15 +178,17 @@ int moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, void
  *   topk_w   fp32 [T, k]     in
  *   w1       bf16 [E, 2I, d] in
  *   w2       bf16 [E, d, I]  in
- *   wq                       in: MXFP8 weights (NULL in BF16 mode)
+ *   wq, wq_bytes             in: MXFP8 mode, the buffer moe_quantize_weights filled (ignored in
+ *                                BF16 mode, may be NULL)
  *   y        bf16 [T, d]     out
  *   saved    bytes [saved_bytes]   out: H and A at the offsets moe_query reports
  *   workspace bytes [ws_bytes]     scratch
  */
 int moe_forward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t slot,
                 const int32_t* offsets, const int32_t* tk_row, const float* topk_w,
-                const void* w1, const void* w2, const void* wq, void* y, void* saved,
-                size_t saved_bytes, void* workspace, size_t ws_bytes, moe_stream_t stream);
+                const void* w1, const void* w2, const void* wq, size_t wq_bytes, void* y,
+                void* saved, size_t saved_bytes, void* workspace, size_t ws_bytes,
+                moe_stream_t stream);
 
 /*
  * moe_backward - gradients of L = <y, dy> with respect to x, the router weight, w1, w2 and the
@@ -187,7 +217,7 @@ int moe_forward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t
  *   offsets, row_src, tk_row      in: from moe_permute
  *   topk_idx int32 [T, k], topk_w fp32 [T, k]   in
  *   w_router bf16 [E, d] or NULL  in
- *   w1, w2, wq                    in (as in moe_forward)
+ *   w1, w2, wq, wq_bytes          in (as in moe_forward)
  *   saved                         in: from moe_forward of the same batch
  *   dy       bf16 [T, d]          in
  *   dx       bf16 [T, d]          out
@@ -200,9 +230,9 @@ int moe_forward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t
 int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t slot,
                  const int32_t* offsets, const int32_t* row_src, const int32_t* tk_row,
                  const int32_t* topk_idx, const float* topk_w, const void* w_router,
-                 const void* w1, const void* w2, const void* wq, const void* saved,
-                 size_t saved_bytes, const void* dy, void* dx, float* dw1, float* dw2,
-                 float* dwr, float* d_topk_w, int32_t accumulate, void* workspace,
+                 const void* w1, const void* w2, const void* wq, size_t wq_bytes,
+                 const void* saved, size_t saved_bytes, const void* dy, void* dx, float* dw1,
+                 float* dw2, float* dwr, float* d_topk_w, int32_t accumulate, void* workspace,
                  size_t ws_bytes, moe_stream_t stream);
 
 /*

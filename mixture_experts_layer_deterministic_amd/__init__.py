@@ -44,7 +44,8 @@ class MoeSizes(ctypes.Structure):
     _fields_ = [("ring_slot", ctypes.c_size_t), ("saved", ctypes.c_size_t),
                 ("saved_H", ctypes.c_size_t), ("saved_A", ctypes.c_size_t),
                 ("workspace", ctypes.c_size_t), ("ws_O", ctypes.c_size_t),
-                ("ws_dH", ctypes.c_size_t), ("ws_dXp", ctypes.c_size_t)]
+                ("ws_dH", ctypes.c_size_t), ("ws_dXp", ctypes.c_size_t),
+                ("wq", ctypes.c_size_t)]
 
 
 _lib = None
@@ -55,10 +56,11 @@ _SIGS = {
     "moe_query": [ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeSizes)],
     "moe_route": [ctypes.POINTER(MoeCfg), _P, _P, _P, _P, _P, _P],
     "moe_permute": [ctypes.POINTER(MoeCfg), _P, _P, _P, _SZ, _I32, _P, _P, _P, _P, _P, _SZ, _P],
-    "moe_forward": [ctypes.POINTER(MoeCfg), _P, _SZ, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
-                    _P, _SZ, _P],
+    "moe_forward": [ctypes.POINTER(MoeCfg), _P, _SZ, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P, _P,
+                    _SZ, _P, _SZ, _P],
     "moe_backward": [ctypes.POINTER(MoeCfg), _P, _SZ, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                     _P, _SZ, _P, _P, _P, _P, _P, _P, _I32, _P, _SZ, _P],
+                     _SZ, _P, _SZ, _P, _P, _P, _P, _P, _P, _I32, _P, _SZ, _P],
+    "moe_quantize_weights": [ctypes.POINTER(MoeCfg), _P, _P, _P, _SZ, _P],
 }
 
 
@@ -152,19 +154,28 @@ def moe_permute(cfg, topk_idx, x, ring, slot, counts, offsets, row_src, tk_row, 
            "moe_permute")
 
 
+def _wq_bytes(wq):
+    return 0 if wq is None else _nbytes(wq)
+
+
+def moe_quantize_weights(cfg, w1, w2, wq, stream=None):
+    _check(lib().moe_quantize_weights(ctypes.byref(cfg), _ptr(w1), _ptr(w2), _ptr(wq),
+                                      _nbytes(wq), _stream(stream)), "moe_quantize_weights")
+
+
 def moe_forward(cfg, ring, slot, offsets, tk_row, topk_w, w1, w2, wq, y, saved, workspace,
                 stream=None):
     _check(lib().moe_forward(ctypes.byref(cfg), _ptr(ring), _nbytes(ring), slot, _ptr(offsets),
-                             _ptr(tk_row), _ptr(topk_w), _ptr(w1), _ptr(w2), _ptr(wq), _ptr(y),
-                             _ptr(saved), _nbytes(saved), _ptr(workspace), _nbytes(workspace),
-                             _stream(stream)), "moe_forward")
+                             _ptr(tk_row), _ptr(topk_w), _ptr(w1), _ptr(w2), _ptr(wq),
+                             _wq_bytes(wq), _ptr(y), _ptr(saved), _nbytes(saved),
+                             _ptr(workspace), _nbytes(workspace), _stream(stream)), "moe_forward")
 
 
 def moe_backward(cfg, ring, slot, offsets, row_src, tk_row, topk_idx, topk_w, w_router, w1, w2,
                  wq, saved, dy, dx, dw1, dw2, dwr, d_topk_w, accumulate, workspace, stream=None):
     _check(lib().moe_backward(ctypes.byref(cfg), _ptr(ring), _nbytes(ring), slot, _ptr(offsets),
                               _ptr(row_src), _ptr(tk_row), _ptr(topk_idx), _ptr(topk_w),
-                              _ptr(w_router), _ptr(w1), _ptr(w2), _ptr(wq), _ptr(saved),
-                              _nbytes(saved), _ptr(dy), _ptr(dx), _ptr(dw1), _ptr(dw2),
+                              _ptr(w_router), _ptr(w1), _ptr(w2), _ptr(wq), _wq_bytes(wq),
+                              _ptr(saved), _nbytes(saved), _ptr(dy), _ptr(dx), _ptr(dw1), _ptr(dw2),
                               _ptr(dwr), _ptr(d_topk_w), int(accumulate), _ptr(workspace),
                               _nbytes(workspace), _stream(stream)), "moe_backward")

@@ -17,12 +17,19 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
+  bool mx;
   // workspace
   size_t status, sched, blk_cnt, blk_flag, rank, O, dH, dXp, dyw, dwpart, dl_pos, wg_count,
       wg_table1, wg_table2, total;
+  // workspace, MXFP8 only: dY, A and dH quantised along their GEMM's K (codes, scales)
+  size_t dyq, dys, aq, aqs, dhq, dhs;
   // saved
   size_t H, A, saved_total;
-  size_t slot;
+  // ring slot: bf16 Xp, or MXFP8 Xp codes at 0 and scales at slot_sc
+  size_t slot, slot_sc;
+  // quantised weights (MXFP8): W1 and W2 along their forward K, and transposed along their
+  // dgrad K: W1f [E,2I,d], W2f [E,d,I], W2b [E,I,d], W1b [E,d,2I], each with per-32 scales
+  size_t w1f, w1fs, w2f, w2fs, w2b, w2bs, w1b, w1bs, wq_total;
   int nb, nIt, max_mtiles;
 };
 
@@ -61,12 +68,38 @@ Layout layout(const moe_cfg* c) {
   L.wg_table2 = take(16 * wgrad_table_entries((int)Tk, c->E, c->d, c->I));
   L.dwpart = take(sizeof(float) * Tk * L.nIt);
   L.dl_pos = take(sizeof(float) * Tk);
+  L.mx = c->precision == MOE_PREC_MXFP8;
+  const size_t T = c->T, mxs = L.mx ? 1 : 0;
+  L.dyq = take(mxs * T * d);
+  L.dys = take(mxs * T * d / 32);
+  L.aq = take(mxs * Tk * I);
+  L.aqs = take(mxs * Tk * I / 32);
+  L.dhq = take(mxs * Tk * 2 * I);
+  L.dhs = take(mxs * Tk * 2 * I / 32);
   L.total = o;
   o = 0;
   L.H = take(2 * Tk * 2 * I);
   L.A = take(2 * Tk * I);
   L.saved_total = o;
-  L.slot = 2 * Tk * d;
+  if (L.mx) {
+    o = 0;
+    take(Tk * d);
+    L.slot_sc = o;
+    take(Tk * d / 32);
+    L.slot = o;
+    o = 0;
+    L.w1f = take(E * 2 * I * d);
+    L.w1fs = take(E * 2 * I * d / 32);
+    L.w2f = take(E * d * I);
+    L.w2fs = take(E * d * I / 32);
+    L.w2b = take(E * I * d);
+    L.w2bs = take(E * I * d / 32);
+    L.w1b = take(E * d * 2 * I);
+    L.w1bs = take(E * d * 2 * I / 32);
+    L.wq_total = o;
+  } else {
+    L.slot = 2 * Tk * d;
+  }
   return L;
 }
 
@@ -93,7 +126,7 @@ struct Launches {
 
 int check_mode(const moe_cfg* c) {
   if (!cfg_ok(c)) return MOE_ERR_INVALID_ARG;
-  if (c->precision != MOE_PREC_BF16) return MOE_ERR_UNSUPPORTED;
+  if (c->precision != MOE_PREC_BF16 && c->precision != MOE_PREC_MXFP8) return MOE_ERR_UNSUPPORTED;
   if (c->flags & ~MOE_FLAG_PERSISTENT) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
@@ -101,6 +134,14 @@ int check_mode(const moe_cfg* c) {
 int check_ring(const Layout& L, const void* ring, size_t ring_bytes, int32_t slot) {
   if (!aligned16(ring)) return MOE_ERR_INVALID_ARG;
   if (slot < 0 || (size_t)(slot + 1) * L.slot > ring_bytes) return MOE_ERR_RING_TOO_SMALL;
+  return MOE_OK;
+}
+
+// The quantised weights of MXFP8 mode, or an error code when they are missing.
+int check_wq(const Layout& Y, const void* wq, size_t wq_bytes) {
+  if (!Y.mx) return MOE_OK;
+  if (!aligned16(wq)) return MOE_ERR_INVALID_ARG;
+  if (wq_bytes < Y.wq_total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   return MOE_OK;
 }
 
@@ -166,7 +207,35 @@ int moe_query(const moe_cfg* cfg, moe_sizes* out) {
   out->ws_O = L.O;
   out->ws_dH = L.dH;
   out->ws_dXp = L.dXp;
+  out->wq = L.mx ? L.wq_total : 0;
   return MOE_OK;
+}
+
+int moe_quantize_weights(const moe_cfg* cfg, const void* w1, const void* w2, void* wq,
+                         size_t wq_bytes, moe_stream_t stream) {
+  int st = check_mode(cfg);
+  if (st) return st;
+  if (cfg->precision != MOE_PREC_MXFP8) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w1) || !aligned16(w2) || !aligned16(wq)) return MOE_ERR_INVALID_ARG;
+  const Layout Y = layout(cfg);
+  if (wq_bytes < Y.wq_total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int E = cfg->E, d = cfg->d, I = cfg->I;
+  const uint16_t* a1 = static_cast<const uint16_t*>(w1);
+  const uint16_t* a2 = static_cast<const uint16_t*>(w2);
+  Launches L;
+  L(launch_quant_rows(a1, (long long)E * 2 * I, d, at<uint8_t>(wq, Y.w1f), at<uint8_t>(wq, Y.w1fs),
+                      "quant_w1_fwd", s));
+  if (!L.err)
+    L(launch_quant_rows(a2, (long long)E * d, I, at<uint8_t>(wq, Y.w2f), at<uint8_t>(wq, Y.w2fs),
+                        "quant_w2_fwd", s));
+  if (!L.err)
+    L(launch_quant_cols_t(a2, E, d, I, at<uint8_t>(wq, Y.w2b), at<uint8_t>(wq, Y.w2bs),
+                          "quant_w2_bwd", s));
+  if (!L.err)
+    L(launch_quant_cols_t(a1, E, 2 * I, d, at<uint8_t>(wq, Y.w1b), at<uint8_t>(wq, Y.w1bs),
+                          "quant_w1_bwd", s));
+  return L.status();
 }
 
 int moe_route(const moe_cfg* cfg, const void* x, const void* w_router, float* logits,
@@ -202,7 +271,10 @@ int moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, void
   int32_t* blk = at<int32_t>(workspace, Y.blk_cnt);
   int32_t* flag = at<int32_t>(workspace, Y.blk_flag);
   int32_t* rank = at<int32_t>(workspace, Y.rank);
-  uint16_t* xp = at<uint16_t>(ring, (size_t)slot * Y.slot);
+  uint8_t* slot_base = at<uint8_t>(ring, (size_t)slot * Y.slot);
+  uint16_t* xp = Y.mx ? nullptr : reinterpret_cast<uint16_t*>(slot_base);
+  uint8_t* xp8 = Y.mx ? slot_base : nullptr;
+  uint8_t* xps = Y.mx ? slot_base + Y.slot_sc : nullptr;
   Launches L;
   L(launch_perm_hist(topk_idx, Tk, cfg->E, blk, rank, flag, s));
   if (!L.err)
@@ -210,15 +282,15 @@ int moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, void
                        s));
   if (!L.err)
     L(launch_perm_place(topk_idx, rank, blk, Tk, cfg->E, cfg->k, row_src, tk_row,
-                        static_cast<const uint16_t*>(x), xp, cfg->d, s));
+                        static_cast<const uint16_t*>(x), xp, xp8, xps, cfg->d, s));
   return L.status();
 }
 
 int moe_forward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t slot,
                 const int32_t* offsets, const int32_t* tk_row, const float* topk_w,
-                const void* w1, const void* w2, const void* wq, void* y, void* saved,
-                size_t saved_bytes, void* workspace, size_t ws_bytes, moe_stream_t stream) {
-  (void)wq;
+                const void* w1, const void* w2, const void* wq, size_t wq_bytes, void* y,
+                void* saved, size_t saved_bytes, void* workspace, size_t ws_bytes,
+                moe_stream_t stream) {
   int st = check_mode(cfg);
   if (st) return st;
   const Layout Y = layout(cfg);
@@ -226,38 +298,50 @@ int moe_forward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t
       !aligned16(w2) || !aligned16(y) || !aligned16(saved) || !aligned16(workspace))
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ring(Y, ring, ring_bytes, slot))) return st;
+  if ((st = check_wq(Y, wq, wq_bytes))) return st;
   if (saved_bytes < Y.saved_total || ws_bytes < Y.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool pers = cfg->flags & MOE_FLAG_PERSISTENT;
-  const int Tk = cfg->T * cfg->k;
-  const uint16_t* xp = at<uint16_t>(ring, (size_t)slot * Y.slot);
+  const int Tk = cfg->T * cfg->k, d = cfg->d, I = cfg->I, E = cfg->E;
+  const uint8_t* slot_base = at<uint8_t>(ring, (size_t)slot * Y.slot);
   int2* sched = at<int2>(workspace, Y.sched);
   uint16_t* H = at<uint16_t>(saved, Y.H);
   uint16_t* A = at<uint16_t>(saved, Y.A);
   uint16_t* O = at<uint16_t>(workspace, Y.O);
   Launches L;
-  L(launch_sched_build(offsets, cfg->E, sched, s));
+  L(launch_sched_build(offsets, E, sched, s));
+  if (Y.mx) {
+    uint8_t* aq = at<uint8_t>(workspace, Y.aq);
+    uint8_t* aqs = at<uint8_t>(workspace, Y.aqs);
+    if (!L.err)
+      L(launch_fwd_gateup_mx({slot_base, slot_base + Y.slot_sc, at<uint8_t>(wq, Y.w1f),
+                              at<uint8_t>(wq, Y.w1fs), H, A, aq, aqs, offsets, sched, d, I, Tk, E},
+                             pers, s));
+    if (!L.err)
+      L(launch_fwd_down_mx({aq, aqs, at<uint8_t>(wq, Y.w2f), at<uint8_t>(wq, Y.w2fs), O, offsets,
+                            sched, d, I, Tk, E},
+                           pers, s));
+  } else {
+    const uint16_t* xp = reinterpret_cast<const uint16_t*>(slot_base);
+    if (!L.err)
+      L(launch_fwd_gateup({xp, static_cast<const uint16_t*>(w1), H, A, offsets, sched, d, I, Tk, E},
+                          pers, s));
+    if (!L.err)
+      L(launch_fwd_down({A, static_cast<const uint16_t*>(w2), O, offsets, sched, d, I, Tk, E}, pers,
+                        s));
+  }
   if (!L.err)
-    L(launch_fwd_gateup({xp, static_cast<const uint16_t*>(w1), H, A, offsets, sched, cfg->d,
-                         cfg->I, Tk, cfg->E},
-                        pers, s));
-  if (!L.err)
-    L(launch_fwd_down({A, static_cast<const uint16_t*>(w2), O, offsets, sched, cfg->d, cfg->I, Tk,
-                       cfg->E},
-                      pers, s));
-  if (!L.err)
-    L(launch_combine(O, tk_row, topk_w, cfg->T, cfg->k, cfg->d, static_cast<uint16_t*>(y), s));
+    L(launch_combine(O, tk_row, topk_w, cfg->T, cfg->k, d, static_cast<uint16_t*>(y), s));
   return L.status();
 }
 
 int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t slot,
                  const int32_t* offsets, const int32_t* row_src, const int32_t* tk_row,
                  const int32_t* topk_idx, const float* topk_w, const void* w_router,
-                 const void* w1, const void* w2, const void* wq, const void* saved,
-                 size_t saved_bytes, const void* dy, void* dx, float* dw1, float* dw2,
-                 float* dwr, float* d_topk_w, int32_t accumulate, void* workspace,
+                 const void* w1, const void* w2, const void* wq, size_t wq_bytes,
+                 const void* saved, size_t saved_bytes, const void* dy, void* dx, float* dw1,
+                 float* dw2, float* dwr, float* d_topk_w, int32_t accumulate, void* workspace,
                  size_t ws_bytes, moe_stream_t stream) {
-  (void)wq;
   int st = check_mode(cfg);
   if (st) return st;
   const Layout Y = layout(cfg);
@@ -269,11 +353,15 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
     return MOE_ERR_INVALID_ARG;
   if (routed && (!aligned16(w_router) || !aligned16(dwr))) return MOE_ERR_INVALID_ARG;
   if ((st = check_ring(Y, ring, ring_bytes, slot))) return st;
+  if ((st = check_wq(Y, wq, wq_bytes))) return st;
   if (saved_bytes < Y.saved_total || ws_bytes < Y.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool pers = cfg->flags & MOE_FLAG_PERSISTENT;
   const int Tk = cfg->T * cfg->k, d = cfg->d, I = cfg->I, E = cfg->E, k = cfg->k;
-  const uint16_t* xp = at<uint16_t>(ring, (size_t)slot * Y.slot);
+  const uint8_t* slot_base = at<uint8_t>(ring, (size_t)slot * Y.slot);
+  const uint16_t* xp = Y.mx ? nullptr : reinterpret_cast<const uint16_t*>(slot_base);
+  const uint8_t* xp8 = Y.mx ? slot_base : nullptr;
+  const uint8_t* xps = Y.mx ? slot_base + Y.slot_sc : nullptr;
   const uint16_t* H = at<uint16_t>(saved, Y.H);
   const uint16_t* A = at<uint16_t>(saved, Y.A);
   int2* sched = at<int2>(workspace, Y.sched);
@@ -281,33 +369,65 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
   uint16_t* dXp = at<uint16_t>(workspace, Y.dXp);
   float* dwpart = at<float>(workspace, Y.dwpart);
   float* dl_pos = at<float>(workspace, Y.dl_pos);
+  uint16_t* dyw = at<uint16_t>(workspace, Y.dyw);
+  int32_t* wg_count = at<int32_t>(workspace, Y.wg_count);
   const uint16_t* dyp = static_cast<const uint16_t*>(dy);
   const uint16_t* w1p = static_cast<const uint16_t*>(w1);
   const uint16_t* w2p = static_cast<const uint16_t*>(w2);
   Launches L;
-  uint16_t* dyw = at<uint16_t>(workspace, Y.dyw);
-  int32_t* wg_count = at<int32_t>(workspace, Y.wg_count);
   L(launch_sched_build(offsets, E, sched, s));
-  if (!L.err)
-    L(launch_bwd_down_dgrad({dyp, row_src, topk_w, w2p, H, A, dH, dwpart, dyw, offsets, sched, d,
-                             I, k, Tk, E},
-                            pers, s));
-  if (!L.err)
-    L(launch_dw_router(dwpart, Y.nIt, tk_row, topk_w, cfg->T, k, d_topk_w, dl_pos, routed, s));
-  if (!L.err)
-    L(launch_wgrad({dyw, A, dw2, offsets, at<int4>(workspace, Y.wg_table2), wg_count + 1, E, d, I,
-                    accumulate, false, "bwd_down_wgrad", "wgrad_sched_down"},
-                   s));
-  if (!L.err) L(launch_bwd_gate_dgrad({dH, w1p, dXp, offsets, sched, d, I, Tk, E}, pers, s));
-  if (!L.err)
-    L(launch_wgrad({dH, xp, dw1, offsets, at<int4>(workspace, Y.wg_table1), wg_count, E, 2 * I, d,
-                    accumulate, true, "bwd_gate_wgrad", "wgrad_sched_gate"},
-                   s));
+  if (Y.mx) {
+    uint8_t* dyq = at<uint8_t>(workspace, Y.dyq);
+    uint8_t* dys = at<uint8_t>(workspace, Y.dys);
+    uint8_t* dhq = at<uint8_t>(workspace, Y.dhq);
+    uint8_t* dhs = at<uint8_t>(workspace, Y.dhs);
+    if (!L.err) L(launch_quant_rows(dyp, cfg->T, d, dyq, dys, "quant_dy", s));
+    if (!L.err) L(launch_scale_gather(dyp, offsets, row_src, topk_w, E, k, d, Tk, dyw, s));
+    if (!L.err)
+      L(launch_bwd_down_dgrad_mx({dyq, dys, row_src, topk_w, at<uint8_t>(wq, Y.w2b),
+                                  at<uint8_t>(wq, Y.w2bs), H, A, dH, dwpart, dhq, dhs, offsets,
+                                  sched, d, I, k, Tk, E},
+                                 pers, s));
+    if (!L.err)
+      L(launch_dw_router(dwpart, Y.nIt, tk_row, topk_w, cfg->T, k, d_topk_w, dl_pos, routed, s));
+    if (!L.err)
+      L(launch_wgrad({dyw, A, nullptr, nullptr, dw2, offsets, at<int4>(workspace, Y.wg_table2),
+                      wg_count + 1, E, d, I, accumulate, false, "bwd_down_wgrad",
+                      "wgrad_sched_down"},
+                     s));
+    if (!L.err)
+      L(launch_bwd_gate_dgrad_mx({dhq, dhs, at<uint8_t>(wq, Y.w1b), at<uint8_t>(wq, Y.w1bs), dXp,
+                                  offsets, sched, d, I, Tk, E},
+                                 pers, s));
+    if (!L.err)
+      L(launch_wgrad({dH, nullptr, xp8, xps, dw1, offsets, at<int4>(workspace, Y.wg_table1),
+                      wg_count, E, 2 * I, d, accumulate, true, "bwd_gate_wgrad",
+                      "wgrad_sched_gate"},
+                     s));
+  } else {
+    if (!L.err)
+      L(launch_bwd_down_dgrad({dyp, row_src, topk_w, w2p, H, A, dH, dwpart, dyw, offsets, sched, d,
+                               I, k, Tk, E},
+                              pers, s));
+    if (!L.err)
+      L(launch_dw_router(dwpart, Y.nIt, tk_row, topk_w, cfg->T, k, d_topk_w, dl_pos, routed, s));
+    if (!L.err)
+      L(launch_wgrad({dyw, A, nullptr, nullptr, dw2, offsets, at<int4>(workspace, Y.wg_table2),
+                      wg_count + 1, E, d, I, accumulate, false, "bwd_down_wgrad",
+                      "wgrad_sched_down"},
+                     s));
+    if (!L.err) L(launch_bwd_gate_dgrad({dH, w1p, dXp, offsets, sched, d, I, Tk, E}, pers, s));
+    if (!L.err)
+      L(launch_wgrad({dH, xp, nullptr, nullptr, dw1, offsets, at<int4>(workspace, Y.wg_table1),
+                      wg_count, E, 2 * I, d, accumulate, true, "bwd_gate_wgrad",
+                      "wgrad_sched_gate"},
+                     s));
+  }
   if (!L.err)
     L(launch_uncombine(dXp, tk_row, topk_idx, dl_pos,
                        routed ? static_cast<const uint16_t*>(w_router) : nullptr, cfg->T, k, d,
                        static_cast<uint16_t*>(dx), s));
-  if (!L.err && routed) L(launch_dwr(dl_pos, xp, offsets, E, d, dwr, accumulate, s));
+  if (!L.err && routed) L(launch_dwr(dl_pos, xp, xp8, xps, offsets, E, d, dwr, accumulate, s));
   return L.status();
 }
 

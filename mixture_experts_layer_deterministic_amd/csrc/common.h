@@ -13,6 +13,7 @@ constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin over 8 XCD
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 // bfloat16 <-> fp32. The widening is exact; the narrowing rounds to nearest, ties to even
 // (finite inputs; the layer never produces NaN or Inf from finite data of its scale).
@@ -33,6 +34,39 @@ MOE_DEV uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 1
 MOE_DEV f32x4 mfma16(const uint4& bfrag, const uint4& afrag, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfrag),
                                                  __builtin_bit_cast(bf16x8, afrag), acc, 0, 0, 0);
+}
+
+// MXFP8 (OCP MX): E4M3 elements sharing one E8M0 scale per 32 along the reduction axis.
+// Scale code of a block with max magnitude amax: floor(log2 amax) - 8 + 127, clamped to 0..254;
+// 0 for an all-zero block. The fp32 exponent field is floor(log2 amax) + 127 for normal amax and
+// 0 for zero or subnormal amax, so code = clamp(field - 8, 0, 254).
+MOE_DEV uint32_t mx_scale_code(float amax) {
+  const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu);
+  return static_cast<uint32_t>(min(max(e - 8, 0), 254));
+}
+// 2^(127 - code): multiplying by it maps a block onto the E4M3 range (fp32 amax keeps
+// code <= 246, so the result is a normal float).
+MOE_DEV float mx_inv_scale(uint32_t code) { return __uint_as_float((254u - code) << 23); }
+// 2^(code - 127); code 0 is the fp32 subnormal 2^-127.
+MOE_DEV float mx_scale(uint32_t code) {
+  return code ? __uint_as_float(code << 23) : __uint_as_float(0x00400000u);
+}
+// Two scaled fp32 values to two E4M3 codes (low 16 bits): saturate to +-448, then the
+// hardware conversion rounds to nearest even (it does not saturate by itself).
+MOE_DEV uint32_t e4m3x2(float a, float b) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xffffu;
+}
+// Four E4M3 codes packed in a dword to fp32 (exact).
+MOE_DEV void e4m3x4_to_f32(uint32_t w, float (&f)[4]) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+  f[0] = lo[0];
+  f[1] = lo[1];
+  f[2] = hi[0];
+  f[3] = hi[1];
 }
 
 MOE_DEV float silu(float g) { return g / (1.0f + __expf(-g)); }

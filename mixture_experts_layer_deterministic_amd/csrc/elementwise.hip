@@ -125,9 +125,13 @@ __global__ void __launch_bounds__(256) uncombine_kernel(
 }
 
 // dWr[e, c] = sum over positions p of expert e, ascending, of dl_pos[p] * Xp[p, c] (fp32).
-// Block (cx, e) covers columns [512 cx, 512 cx + 512); each thread owns 8 columns.
+// Block (cx, e) covers columns [512 cx, 512 cx + 512); each thread owns 8 columns. MX reads Xp
+// as its MXFP8 image (codes xp8, one scale per 32 columns in xps).
+template <bool MX>
 __global__ void __launch_bounds__(64) dwr_kernel(const float* __restrict__ dl_pos,
                                                  const uint16_t* __restrict__ xp,
+                                                 const uint8_t* __restrict__ xp8,
+                                                 const uint8_t* __restrict__ xps,
                                                  const int32_t* __restrict__ offsets, int d,
                                                  float* __restrict__ dwr, int accumulate) {
   const int e = blockIdx.y;
@@ -137,13 +141,29 @@ __global__ void __launch_bounds__(64) dwr_kernel(const float* __restrict__ dl_po
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int p = p0; p < p1; ++p) {
     const float dl = dl_pos[p];
-    const uint4 g = *reinterpret_cast<const uint4*>(xp + (size_t)p * d + c0);
-    const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+    float xv[8];
+    if constexpr (MX) {
+      const uint2 q = *reinterpret_cast<const uint2*>(xp8 + (size_t)p * d + c0);
+      const float s = mx_scale(xps[(size_t)p * (d / 32) + c0 / 32]);
+      float f[4], g[4];
+      e4m3x4_to_f32(q.x, f);
+      e4m3x4_to_f32(q.y, g);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] = __builtin_fmaf(dl, bf2f_lo(gw[q]), acc[2 * q]);
-      acc[2 * q + 1] = __builtin_fmaf(dl, bf2f_hi(gw[q]), acc[2 * q + 1]);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        xv[q4] = f[q4] * s;
+        xv[4 + q4] = g[q4] * s;
+      }
+    } else {
+      const uint4 g = *reinterpret_cast<const uint4*>(xp + (size_t)p * d + c0);
+      const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xv[2 * q] = bf2f_lo(gw[q]);
+        xv[2 * q + 1] = bf2f_hi(gw[q]);
+      }
     }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(dl, xv[q], acc[q]);
   }
   float4* dst = reinterpret_cast<float4*>(dwr + (size_t)e * d + c0);
   float4 a = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -191,12 +211,17 @@ hipError_t launch_uncombine(const uint16_t* dXp, const int32_t* tk_row, const in
   return hipGetLastError();
 }
 
-hipError_t launch_dwr(const float* dl_pos, const uint16_t* xp, const int32_t* offsets, int E,
-                      int d, float* dwr, int accumulate, hipStream_t s) {
+hipError_t launch_dwr(const float* dl_pos, const uint16_t* xp, const uint8_t* xp8,
+                      const uint8_t* xps, const int32_t* offsets, int E, int d, float* dwr,
+                      int accumulate, hipStream_t s) {
   {
     TraceScope trace("dwr", s);
-    hipLaunchKernelGGL(dwr_kernel, dim3((d + 511) / 512, E), dim3(64), 0, s, dl_pos, xp, offsets, d,
-                       dwr, accumulate);
+    if (xp8)
+      hipLaunchKernelGGL(dwr_kernel<true>, dim3((d + 511) / 512, E), dim3(64), 0, s, dl_pos, xp,
+                         xp8, xps, offsets, d, dwr, accumulate);
+    else
+      hipLaunchKernelGGL(dwr_kernel<false>, dim3((d + 511) / 512, E), dim3(64), 0, s, dl_pos, xp,
+                         xp8, xps, offsets, d, dwr, accumulate);
   }
   return hipGetLastError();
 }

@@ -125,6 +125,8 @@ struct Geo {
   static constexpr int MB = WM / 16, NB = WN / 16;
   static constexpr int LDK = BK + 8;
   static constexpr int STAGE = (BM + BN) * LDK;  // uint16 elements per LDS stage
+  static constexpr int kSmem = 2 * STAGE * 2;    // bytes, two stages
+  static constexpr bool kMx = false;
   static_assert(WAVES_M * WAVES_N == 4, "4 waves per workgroup");
   static_assert(BK % 32 == 0 && WM % 16 == 0 && WN % 16 == 0, "tile shape");
 };
@@ -515,6 +517,546 @@ struct BwdGateDgrad {
   }
 };
 
+
+// ------------------------------------------------------------------------------------------
+// MXFP8 mode. Both operands are E4M3 codes, K-contiguous, with one E8M0 scale per 32 along K;
+// one v_mfma_scale_f32_16x16x128_f8f6f4 covers 16 x 16 outputs and 128 K. Operand layout of
+// that instruction on gfx950 (lane l, row or column l % 16, group g = l / 16): bytes 0..15 hold
+// K [16 g, 16 g + 16) and bytes 16..31 hold K [64 + 16 g, 64 + 16 g + 16); the scale of K
+// block b = [32 b, 32 b + 32) comes from byte 0 of lane (row + 16 b). LDS holds each stage as
+// [BM][LDK] A codes, [BN][LDK] B codes, then one 32-bit word of four block scales per row.
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+struct GeoMx {
+  static constexpr int BM = BM_, BN = BN_, BK = 128;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int MB = WM / 16, NB = WN / 16;
+  static constexpr int LDK = BK + 16;              // bytes per LDS row
+  static constexpr int SC_OFF = (BM + BN) * LDK;   // byte offset of the scale words
+  static constexpr int STAGE = SC_OFF + (BM + BN) * 4;
+  static constexpr int kSmem = 2 * STAGE;
+  static constexpr bool kMx = true;
+  static_assert(WAVES_M * WAVES_N == 4, "4 waves per workgroup");
+};
+
+// ROWS rows of fp8 codes, K-contiguous: 8 vectors of 16 bytes per 128-K step. Thread t < ROWS
+// also moves row t's scale word (four block scales of the step). A null row loads zeros with
+// unit scales.
+template <int ROWS, int LDK>
+struct LoadK8 {
+  static constexpr int VPR = 8;
+  static constexpr int NV = ROWS * VPR;
+  static constexpr int PT = (NV + kThreads - 1) / kThreads;
+  const uint8_t* rp[PT];
+  uint4 r[PT];
+  const uint8_t* sp;
+  uint32_t s;
+
+  template <class RowPtr, class ScalePtr>
+  MOE_DEV void init(RowPtr rowptr, ScalePtr scaleptr) {
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int v = threadIdx.x + kThreads * j;
+      rp[j] = (v < NV) ? rowptr(v / VPR) : nullptr;
+    }
+    sp = threadIdx.x < ROWS ? scaleptr(threadIdx.x) : nullptr;
+  }
+  MOE_DEV void load(int kt) {
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int v = threadIdx.x + kThreads * j;
+      r[j] = rp[j] ? *reinterpret_cast<const uint4*>(rp[j] + (size_t)kt * 128 + (v % VPR) * 16)
+                   : make_uint4(0, 0, 0, 0);
+    }
+    s = sp ? *reinterpret_cast<const uint32_t*>(sp + (size_t)kt * 4) : 0x7f7f7f7fu;
+  }
+  MOE_DEV void store(uint8_t* rows, uint32_t* scales) const {
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int v = threadIdx.x + kThreads * j;
+      if (v < NV) *reinterpret_cast<uint4*>(rows + (v / VPR) * LDK + (v % VPR) * 16) = r[j];
+    }
+    if (threadIdx.x < ROWS) scales[threadIdx.x] = s;
+  }
+};
+
+template <class G>
+MOE_DEV void mx_store_stage(const LoadK8<G::BM, G::LDK>& la, const LoadK8<G::BN, G::LDK>& lb,
+                            uint8_t* stage) {
+  la.store(stage, reinterpret_cast<uint32_t*>(stage + G::SC_OFF));
+  lb.store(stage + G::BM * G::LDK, reinterpret_cast<uint32_t*>(stage + G::SC_OFF) + G::BM);
+}
+
+MOE_DEV i32x8 mx_frag(const uint8_t* row, int g) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * g);
+  const uint4 hi = *reinterpret_cast<const uint4*>(row + 64 + 16 * g);
+  i32x8 v;
+  v[0] = static_cast<int>(lo.x);
+  v[1] = static_cast<int>(lo.y);
+  v[2] = static_cast<int>(lo.z);
+  v[3] = static_cast<int>(lo.w);
+  v[4] = static_cast<int>(hi.x);
+  v[5] = static_cast<int>(hi.y);
+  v[6] = static_cast<int>(hi.z);
+  v[7] = static_cast<int>(hi.w);
+  return v;
+}
+
+template <class P>
+MOE_DEV void run_tile_mx(const typename P::Args& a, const typename P::Tile& t, uint8_t* smem) {
+  using G = typename P::G;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
+  const int r16 = lane % 16, g = lane / 16;
+  f32x4 acc[G::MB][G::NB];
+#pragma unroll
+  for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = P::num_k(a, t);
+  if (nk > 0) {
+    typename P::Loader ld;
+    ld.init(a, t);
+    ld.load(0);
+    mx_store_stage<G>(ld.la, ld.lb, smem);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      uint8_t* cur = smem + (kt & 1) * G::STAGE;
+      if (kt + 1 < nk) ld.load(kt + 1);
+      const uint8_t* sA = cur;
+      const uint8_t* sB = cur + G::BM * G::LDK;
+      const uint32_t* scA = reinterpret_cast<const uint32_t*>(cur + G::SC_OFF);
+      const uint32_t* scB = scA + G::BM;
+      i32x8 bf[G::NB];
+      int bs[G::NB];
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) {
+        const int row = P::brow(wn, nb) + r16;
+        bf[nb] = mx_frag(sB + row * G::LDK, g);
+        bs[nb] = static_cast<int>((scB[row] >> (8 * g)) & 0xffu);
+      }
+#pragma unroll
+      for (int mb = 0; mb < G::MB; ++mb) {
+        if (!P::m_active(t, wm * G::WM + mb * 16)) continue;
+        const int row = wm * G::WM + mb * 16 + r16;
+        const i32x8 af = mx_frag(sA + row * G::LDK, g);
+        const int as = static_cast<int>((scA[row] >> (8 * g)) & 0xffu);
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bf[nb], af, acc[mb][nb], 0, 0, 0, bs[nb], 0, as);
+      }
+      if (kt + 1 < nk) mx_store_stage<G>(ld.la, ld.lb, smem + ((kt + 1) & 1) * G::STAGE);
+      __syncthreads();
+    }
+  }
+  P::epilogue(a, t, acc, smem);
+  __syncthreads();
+}
+
+// MXFP8 image of 8 values held by one lane, as 2 dwords of E4M3 codes, with the block scale
+// shared by the four lanes l, l^16, l^32, l^48 (one row's 32 consecutive columns). Every lane
+// must call it.
+MOE_DEV uint32_t mx_block_code(const float (&v)[8]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  return mx_scale_code(amax);
+}
+MOE_DEV uint32_t mx_pack4(const float* v, float inv) {
+  return e4m3x2(v[0] * inv, v[1] * inv) | (e4m3x2(v[2] * inv, v[3] * inv) << 16);
+}
+
+// Problem 1 (MXFP8): forward gate/up with SwiGLU. Waves form 2 x 2: wave (wm, wn) owns rows
+// [64 wm, +64) and gate columns [32 wn, +32) of the tile's 64 with the matching up columns, so
+// one row's 32 consecutive A columns sit in four lanes of one wave and A is quantised (along I,
+// for the down GEMM) in registers.
+struct MxFwdGateUp {
+  static constexpr const char* kName = "fwd_gateup";
+  using G = GeoMx<128, 128, 2, 2>;
+  struct Args {
+    const uint8_t* xp8;  // [T*k, d] codes (ring slot)
+    const uint8_t* xps;  // [T*k, d/32]
+    const uint8_t* w8;   // [E, 2I, d]
+    const uint8_t* ws;   // [E, 2I, d/32]
+    uint16_t* H;         // [T*k, 2I]
+    uint16_t* A;         // [T*k, I]
+    uint8_t* aq;         // [T*k, I]
+    uint8_t* aqs;        // [T*k, I/32]
+    const int32_t* offsets;
+    const int2* sched;
+    int d, I;
+  };
+  struct Tile {
+    MTile m;
+    int n0;
+  };
+  static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.I / 64); }
+  static MOE_DEV Tile decode(const Args& a, int lt) {
+    const int ntc = a.I / 64;
+    Tile t;
+    t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
+    t.n0 = (lt % ntc) * 64;
+    return t;
+  }
+  static MOE_DEV int num_k(const Args& a, const Tile&) { return a.d / G::BK; }
+  static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
+  static MOE_DEV int brow(int wn, int nb) {
+    return nb < 2 ? wn * 32 + nb * 16 : 64 + wn * 32 + (nb - 2) * 16;
+  }
+  struct Loader {
+    LoadK8<G::BM, G::LDK> la;
+    LoadK8<G::BN, G::LDK> lb;
+    MOE_DEV void init(const Args& a, const Tile& t) {
+      const int d = a.d, I = a.I, mc = t.m.mcount, row0 = t.m.row0, n0 = t.n0;
+      const uint8_t* xp8 = a.xp8;
+      const uint8_t* xps = a.xps;
+      la.init([&](int m) { return m < mc ? xp8 + (size_t)(row0 + m) * d : nullptr; },
+              [&](int m) { return m < mc ? xps + (size_t)(row0 + m) * (d / 32) : nullptr; });
+      const size_t wrow0 = (size_t)t.m.e * 2 * I;
+      const uint8_t* w8 = a.w8;
+      const uint8_t* ws = a.ws;
+      auto wrow = [=](int n) { return wrow0 + (n < 64 ? n0 + n : I + n0 + n - 64); };
+      lb.init([&](int n) { return w8 + wrow(n) * d; },
+              [&](int n) { return ws + wrow(n) * (d / 32); });
+    }
+    MOE_DEV void load(int kt) {
+      la.load(kt);
+      lb.load(kt);
+    }
+  };
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
+                               uint8_t*) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
+    const int I = a.I;
+    const int c0 = t.n0 + wn * 32;  // first of this wave's 32 A columns: a 32-block
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+      const int m = wm * G::WM + mb * 16 + lane % 16;
+      const bool live = m < t.m.mcount;
+      const size_t pos = t.m.row0 + m;
+      float av[8];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int j = c0 + nb * 16 + 4 * (lane / 16);
+        const f32x4 gv = acc[mb][nb], uv = acc[mb][nb + 2];
+        uint2 hg, hu, aw;
+        hg.x = pack_bf2(gv[0], gv[1]);
+        hg.y = pack_bf2(gv[2], gv[3]);
+        hu.x = pack_bf2(uv[0], uv[1]);
+        hu.y = pack_bf2(uv[2], uv[3]);
+        aw.x = pack_bf2(silu(gv[0]) * uv[0], silu(gv[1]) * uv[1]);
+        aw.y = pack_bf2(silu(gv[2]) * uv[2], silu(gv[3]) * uv[3]);
+        av[4 * nb + 0] = bf2f_lo(aw.x);
+        av[4 * nb + 1] = bf2f_hi(aw.x);
+        av[4 * nb + 2] = bf2f_lo(aw.y);
+        av[4 * nb + 3] = bf2f_hi(aw.y);
+        if (live) {
+          *reinterpret_cast<uint2*>(a.H + pos * 2 * I + j) = hg;
+          *reinterpret_cast<uint2*>(a.H + pos * 2 * I + I + j) = hu;
+          *reinterpret_cast<uint2*>(a.A + pos * I + j) = aw;
+        }
+      }
+      const uint32_t code = mx_block_code(av);
+      const float inv = mx_inv_scale(code);
+      if (live) {
+        *reinterpret_cast<uint32_t*>(a.aq + pos * I + c0 + 4 * (lane / 16)) = mx_pack4(av, inv);
+        *reinterpret_cast<uint32_t*>(a.aq + pos * I + c0 + 16 + 4 * (lane / 16)) =
+            mx_pack4(av + 4, inv);
+        if (lane < 16) a.aqs[pos * (I / 32) + c0 / 32] = static_cast<uint8_t>(code);
+      }
+    }
+  }
+};
+
+// Problem 2 (MXFP8): forward down. O[pos] = A[pos] . W2[e]^T, with A and W2 quantised along I.
+struct MxFwdDown {
+  static constexpr const char* kName = "fwd_down";
+  using G = GeoMx<128, 128, 1, 4>;
+  struct Args {
+    const uint8_t* aq;   // [T*k, I]
+    const uint8_t* aqs;  // [T*k, I/32]
+    const uint8_t* w8;   // [E, d, I]
+    const uint8_t* ws;   // [E, d, I/32]
+    uint16_t* O;         // [T*k, d]
+    const int32_t* offsets;
+    const int2* sched;
+    int d, I;
+  };
+  struct Tile {
+    MTile m;
+    int n0;
+  };
+  static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.d / G::BN); }
+  static MOE_DEV Tile decode(const Args& a, int lt) {
+    const int ntc = a.d / G::BN;
+    Tile t;
+    t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
+    t.n0 = (lt % ntc) * G::BN;
+    return t;
+  }
+  static MOE_DEV int num_k(const Args& a, const Tile&) { return a.I / G::BK; }
+  static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
+  static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
+  struct Loader {
+    LoadK8<G::BM, G::LDK> la;
+    LoadK8<G::BN, G::LDK> lb;
+    MOE_DEV void init(const Args& a, const Tile& t) {
+      const int I = a.I, mc = t.m.mcount, row0 = t.m.row0;
+      const uint8_t* aq = a.aq;
+      const uint8_t* aqs = a.aqs;
+      la.init([&](int m) { return m < mc ? aq + (size_t)(row0 + m) * I : nullptr; },
+              [&](int m) { return m < mc ? aqs + (size_t)(row0 + m) * (I / 32) : nullptr; });
+      const size_t wrow0 = (size_t)t.m.e * a.d + t.n0;
+      const uint8_t* w8 = a.w8;
+      const uint8_t* ws = a.ws;
+      lb.init([&](int n) { return w8 + (wrow0 + n) * I; },
+              [&](int n) { return ws + (wrow0 + n) * (I / 32); });
+    }
+    MOE_DEV void load(int kt) {
+      la.load(kt);
+      lb.load(kt);
+    }
+  };
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
+                               uint8_t*) {
+    const int lane = threadIdx.x % kWave, wn = (threadIdx.x / kWave) % G::WAVES_N;
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+      const int m = mb * 16 + lane % 16;
+      if (m >= t.m.mcount) continue;
+      const size_t pos = t.m.row0 + m;
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) {
+        const int n = t.n0 + wn * G::WN + nb * 16 + 4 * (lane / 16);
+        uint2 o;
+        o.x = pack_bf2(acc[mb][nb][0], acc[mb][nb][1]);
+        o.y = pack_bf2(acc[mb][nb][2], acc[mb][nb][3]);
+        *reinterpret_cast<uint2*>(a.O + pos * a.d + n) = o;
+      }
+    }
+  }
+};
+
+// Problem 3 (MXFP8): down dgrad, dA'[pos] = dY[t] . W2[e] with dY and W2 quantised along d
+// (W2 stored transposed, [E, I, d]). The epilogue is the BF16 one (router-weight-gradient
+// partials, SwiGLU backward, dH in bf16) plus dH quantised along 2I: the wave's 32 consecutive
+// I columns make one 32-block of the gate half and one of the up half.
+struct MxBwdDownDgrad {
+  static constexpr const char* kName = "bwd_down_dgrad";
+  using G = GeoMx<128, 128, 1, 4>;
+  struct Args {
+    const uint8_t* dyq;      // [T, d]
+    const uint8_t* dys;      // [T, d/32]
+    const int32_t* row_src;  // [T*k]
+    const float* topk_w;     // [T*k]
+    const uint8_t* w8;       // [E, I, d]
+    const uint8_t* ws;       // [E, I, d/32]
+    const uint16_t* H;       // [T*k, 2I]
+    const uint16_t* A;       // [T*k, I]
+    uint16_t* dH;            // [T*k, 2I]
+    float* dwpart;           // [T*k, I / BN]
+    uint8_t* dhq;            // [T*k, 2I]
+    uint8_t* dhs;            // [T*k, 2I/32]
+    const int32_t* offsets;
+    const int2* sched;
+    int d, I, k;
+  };
+  struct Tile {
+    MTile m;
+    int n0;
+  };
+  static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.I / G::BN); }
+  static MOE_DEV Tile decode(const Args& a, int lt) {
+    const int ntc = a.I / G::BN;
+    Tile t;
+    t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
+    t.n0 = (lt % ntc) * G::BN;
+    return t;
+  }
+  static MOE_DEV int num_k(const Args& a, const Tile&) { return a.d / G::BK; }
+  static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
+  static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
+  struct Loader {
+    LoadK8<G::BM, G::LDK> la;
+    LoadK8<G::BN, G::LDK> lb;
+    MOE_DEV void init(const Args& a, const Tile& t) {
+      const int d = a.d, k = a.k, mc = t.m.mcount, row0 = t.m.row0;
+      const uint8_t* dyq = a.dyq;
+      const uint8_t* dys = a.dys;
+      const int32_t* rs = a.row_src;
+      la.init([&](int m) { return m < mc ? dyq + (size_t)(rs[row0 + m] / k) * d : nullptr; },
+              [&](int m) { return m < mc ? dys + (size_t)(rs[row0 + m] / k) * (d / 32) : nullptr; });
+      const size_t wrow0 = (size_t)t.m.e * a.I + t.n0;
+      const uint8_t* w8 = a.w8;
+      const uint8_t* ws = a.ws;
+      lb.init([&](int n) { return w8 + (wrow0 + n) * d; },
+              [&](int n) { return ws + (wrow0 + n) * (d / 32); });
+    }
+    MOE_DEV void load(int kt) {
+      la.load(kt);
+      lb.load(kt);
+    }
+  };
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
+                               uint8_t* smem) {
+    const int lane = threadIdx.x % kWave, wn = (threadIdx.x / kWave) % G::WAVES_N;
+    float* red = reinterpret_cast<float*>(smem);  // [WAVES_N][BM]; LDS is free after the K loop
+    const int I = a.I;
+    const int c0 = t.n0 + wn * G::WN;  // this wave's 32 I columns: one 32-block
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+      const int m = mb * 16 + lane % 16;
+      const bool live = m < t.m.mcount;
+      const size_t pos = t.m.row0 + m;
+      float part = 0.f;
+      float dgv[8], duv[8];
+      const float w = live ? a.topk_w[a.row_src[pos]] : 0.f;
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) {
+        const int i = c0 + nb * 16 + 4 * (lane / 16);
+        uint2 av = make_uint2(0, 0), gv = make_uint2(0, 0), uv = make_uint2(0, 0);
+        if (live) {
+          av = *reinterpret_cast<const uint2*>(a.A + pos * I + i);
+          gv = *reinterpret_cast<const uint2*>(a.H + pos * 2 * I + i);
+          uv = *reinterpret_cast<const uint2*>(a.H + pos * 2 * I + I + i);
+        }
+        const float av4[4] = {bf2f_lo(av.x), bf2f_hi(av.x), bf2f_lo(av.y), bf2f_hi(av.y)};
+        const float g4[4] = {bf2f_lo(gv.x), bf2f_hi(gv.x), bf2f_lo(gv.y), bf2f_hi(gv.y)};
+        const float u4[4] = {bf2f_lo(uv.x), bf2f_hi(uv.x), bf2f_lo(uv.y), bf2f_hi(uv.y)};
+        float dg[4], du[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float dap = acc[mb][nb][r];
+          part = __builtin_fmaf(dap, av4[r], part);
+          const float dA = w * dap;
+          const float s = sigmoid(g4[r]);
+          dg[r] = dA * u4[r] * s * (1.0f + g4[r] * (1.0f - s));
+          du[r] = dA * (g4[r] * s);
+        }
+        uint2 og, ou;
+        og.x = pack_bf2(dg[0], dg[1]);
+        og.y = pack_bf2(dg[2], dg[3]);
+        ou.x = pack_bf2(du[0], du[1]);
+        ou.y = pack_bf2(du[2], du[3]);
+        dgv[4 * nb + 0] = bf2f_lo(og.x);
+        dgv[4 * nb + 1] = bf2f_hi(og.x);
+        dgv[4 * nb + 2] = bf2f_lo(og.y);
+        dgv[4 * nb + 3] = bf2f_hi(og.y);
+        duv[4 * nb + 0] = bf2f_lo(ou.x);
+        duv[4 * nb + 1] = bf2f_hi(ou.x);
+        duv[4 * nb + 2] = bf2f_lo(ou.y);
+        duv[4 * nb + 3] = bf2f_hi(ou.y);
+        if (live) {
+          *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + i) = og;
+          *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + I + i) = ou;
+        }
+      }
+      const uint32_t cg = mx_block_code(dgv), cu = mx_block_code(duv);
+      const float ig = mx_inv_scale(cg), iu = mx_inv_scale(cu);
+      if (live) {
+        uint8_t* q = a.dhq + pos * 2 * I;
+        const int o = 4 * (lane / 16);
+        *reinterpret_cast<uint32_t*>(q + c0 + o) = mx_pack4(dgv, ig);
+        *reinterpret_cast<uint32_t*>(q + c0 + 16 + o) = mx_pack4(dgv + 4, ig);
+        *reinterpret_cast<uint32_t*>(q + I + c0 + o) = mx_pack4(duv, iu);
+        *reinterpret_cast<uint32_t*>(q + I + c0 + 16 + o) = mx_pack4(duv + 4, iu);
+        if (lane < 16) {
+          a.dhs[pos * (2 * I / 32) + c0 / 32] = static_cast<uint8_t>(cg);
+          a.dhs[pos * (2 * I / 32) + (I + c0) / 32] = static_cast<uint8_t>(cu);
+        }
+      }
+      // lanes l, l^16, l^32, l^48 share row m: butterfly in a fixed pattern
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      if (lane < 16) red[wn * G::BM + m] = part;
+    }
+    __syncthreads();
+    if (threadIdx.x < G::BM && threadIdx.x < t.m.mcount) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < G::WAVES_N; ++w) s += red[w * G::BM + threadIdx.x];
+      const size_t pos = t.m.row0 + threadIdx.x;
+      a.dwpart[pos * (a.I / G::BN) + t.n0 / G::BN] = s;
+    }
+  }
+};
+
+// Problem 4 (MXFP8): gate/up dgrad, dXp[pos] = dH[pos] . W1[e] with dH and W1 quantised along
+// 2I (W1 stored transposed, [E, d, 2I]).
+struct MxBwdGateDgrad {
+  static constexpr const char* kName = "bwd_gate_dgrad";
+  using G = GeoMx<128, 128, 1, 4>;
+  struct Args {
+    const uint8_t* dhq;  // [T*k, 2I]
+    const uint8_t* dhs;  // [T*k, 2I/32]
+    const uint8_t* w8;   // [E, d, 2I]
+    const uint8_t* ws;   // [E, d, 2I/32]
+    uint16_t* dXp;       // [T*k, d]
+    const int32_t* offsets;
+    const int2* sched;
+    int d, I;
+  };
+  struct Tile {
+    MTile m;
+    int n0;
+  };
+  static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.d / G::BN); }
+  static MOE_DEV Tile decode(const Args& a, int lt) {
+    const int ntc = a.d / G::BN;
+    Tile t;
+    t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
+    t.n0 = (lt % ntc) * G::BN;
+    return t;
+  }
+  static MOE_DEV int num_k(const Args& a, const Tile&) { return 2 * a.I / G::BK; }
+  static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
+  static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
+  struct Loader {
+    LoadK8<G::BM, G::LDK> la;
+    LoadK8<G::BN, G::LDK> lb;
+    MOE_DEV void init(const Args& a, const Tile& t) {
+      const int twoI = 2 * a.I, mc = t.m.mcount, row0 = t.m.row0;
+      const uint8_t* dhq = a.dhq;
+      const uint8_t* dhs = a.dhs;
+      la.init([&](int m) { return m < mc ? dhq + (size_t)(row0 + m) * twoI : nullptr; },
+              [&](int m) { return m < mc ? dhs + (size_t)(row0 + m) * (twoI / 32) : nullptr; });
+      const size_t wrow0 = (size_t)t.m.e * a.d + t.n0;
+      const uint8_t* w8 = a.w8;
+      const uint8_t* ws = a.ws;
+      lb.init([&](int n) { return w8 + (wrow0 + n) * twoI; },
+              [&](int n) { return ws + (wrow0 + n) * (twoI / 32); });
+    }
+    MOE_DEV void load(int kt) {
+      la.load(kt);
+      lb.load(kt);
+    }
+  };
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
+                               uint8_t*) {
+    const int lane = threadIdx.x % kWave, wn = (threadIdx.x / kWave) % G::WAVES_N;
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+      const int m = mb * 16 + lane % 16;
+      if (m >= t.m.mcount) continue;
+      const size_t pos = t.m.row0 + m;
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) {
+        const int n = t.n0 + wn * G::WN + nb * 16 + 4 * (lane / 16);
+        uint2 o;
+        o.x = pack_bf2(acc[mb][nb][0], acc[mb][nb][1]);
+        o.y = pack_bf2(acc[mb][nb][2], acc[mb][nb][3]);
+        *reinterpret_cast<uint2*>(a.dXp + pos * a.d + n) = o;
+      }
+    }
+  }
+};
+
 // ------------------------------------------------------------------------------------------
 // The kernel: walks logical tiles. Each XCD owns one contiguous range of them (so the
 // workgroups sharing an expert's activations share that XCD's L2), striding by the grid within
@@ -578,13 +1120,16 @@ __global__ void __launch_bounds__(kThreads, 2) gg_kernel(const typename P::Args 
     const int lt = (b % kXcds) * R + s;
     if (lt >= ntiles) break;
     const typename P::Tile t = P::decode(a, lt);
-    run_tile<P>(a, t, smem);
+    if constexpr (P::G::kMx)
+      run_tile_mx<P>(a, t, reinterpret_cast<uint8_t*>(smem));
+    else
+      run_tile<P>(a, t, smem);
   }
 }
 
 template <class P>
 static size_t smem_bytes() {
-  return 2 * P::G::STAGE * sizeof(uint16_t);
+  return P::G::kSmem;
 }
 
 // Grid: one-shot grids cover `max_tiles` (rounded up to a multiple of 8); persistent grids
@@ -676,6 +1221,27 @@ hipError_t launch_bwd_down_dgrad(const GemmBwdDownDgradArgs& x, bool persistent,
 hipError_t launch_bwd_gate_dgrad(const GemmBwdGateDgradArgs& x, bool persistent, hipStream_t s) {
   BwdGateDgrad::Args a{x.dH, x.w1, x.dXp, x.offsets, x.sched, x.d, x.I};
   return launch<BwdGateDgrad>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
+}
+
+hipError_t launch_fwd_gateup_mx(const GemmMxGateUpArgs& x, bool persistent, hipStream_t s) {
+  MxFwdGateUp::Args a{x.xp8, x.xps, x.w8, x.ws, x.H, x.A, x.aq, x.aqs, x.offsets, x.sched, x.d, x.I};
+  return launch<MxFwdGateUp>(a, sched_max_mtiles(x.Tk, x.E) * (x.I / 64), persistent, s);
+}
+
+hipError_t launch_fwd_down_mx(const GemmMxDownArgs& x, bool persistent, hipStream_t s) {
+  MxFwdDown::Args a{x.aq, x.aqs, x.w8, x.ws, x.O, x.offsets, x.sched, x.d, x.I};
+  return launch<MxFwdDown>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
+}
+
+hipError_t launch_bwd_down_dgrad_mx(const GemmMxDownDgradArgs& x, bool persistent, hipStream_t s) {
+  MxBwdDownDgrad::Args a{x.dyq, x.dys, x.row_src, x.topk_w, x.w8,     x.ws,    x.H,     x.A, x.dH,
+                         x.dwpart, x.dhq, x.dhs,  x.offsets, x.sched, x.d, x.I, x.k};
+  return launch<MxBwdDownDgrad>(a, sched_max_mtiles(x.Tk, x.E) * (x.I / 128), persistent, s);
+}
+
+hipError_t launch_bwd_gate_dgrad_mx(const GemmMxGateDgradArgs& x, bool persistent, hipStream_t s) {
+  MxBwdGateDgrad::Args a{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, x.sched, x.d, x.I};
+  return launch<MxBwdGateDgrad>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
 }
 
 }  // namespace moe

@@ -34,9 +34,12 @@ hipError_t launch_perm_hist(const int32_t* idx, int Tk, int E, int32_t* blk_cnt,
                             int32_t* blk_flag, hipStream_t s);
 hipError_t launch_perm_scan(int32_t* blk_cnt, int nb, int E, const int32_t* blk_flag,
                             int32_t* counts, int32_t* offsets, int32_t* status, hipStream_t s);
+// With xp8 non-null the slot receives the MXFP8 image of each token (xp8 codes, xps scales)
+// instead of the bf16 copy xp.
 hipError_t launch_perm_place(const int32_t* idx, const int32_t* rank, const int32_t* blk_base,
                              int Tk, int E, int k, int32_t* row_src, int32_t* tk_row,
-                             const uint16_t* x, uint16_t* xp, int d, hipStream_t s);
+                             const uint16_t* x, uint16_t* xp, uint8_t* xp8, uint8_t* xps, int d,
+                             hipStream_t s);
 
 // gemm.hip
 int sched_max_mtiles(int Tk, int E);
@@ -81,6 +84,61 @@ struct GemmBwdGateDgradArgs {
   const int2* sched;
   int d, I, Tk, E;
 };
+// MXFP8 mode: E4M3 codes (uint8) with one E8M0 scale (uint8) per 32 along each GEMM's K.
+struct GemmMxGateUpArgs {
+  const uint8_t* xp8;  // [T*k, d], scales xps [T*k, d/32]
+  const uint8_t* xps;
+  const uint8_t* w8;   // [E, 2I, d], scales ws [E, 2I, d/32]
+  const uint8_t* ws;
+  uint16_t* H;
+  uint16_t* A;
+  uint8_t* aq;         // A quantised along I: [T*k, I], scales aqs [T*k, I/32]
+  uint8_t* aqs;
+  const int32_t* offsets;
+  const int2* sched;
+  int d, I, Tk, E;
+};
+struct GemmMxDownArgs {
+  const uint8_t* aq;
+  const uint8_t* aqs;
+  const uint8_t* w8;   // [E, d, I], scales [E, d, I/32]
+  const uint8_t* ws;
+  uint16_t* O;
+  const int32_t* offsets;
+  const int2* sched;
+  int d, I, Tk, E;
+};
+struct GemmMxDownDgradArgs {
+  const uint8_t* dyq;  // [T, d], scales [T, d/32]
+  const uint8_t* dys;
+  const int32_t* row_src;
+  const float* topk_w;
+  const uint8_t* w8;   // W2 transposed [E, I, d], scales [E, I, d/32]
+  const uint8_t* ws;
+  const uint16_t* H;
+  const uint16_t* A;
+  uint16_t* dH;
+  float* dwpart;
+  uint8_t* dhq;        // dH quantised along 2I: [T*k, 2I], scales [T*k, 2I/32]
+  uint8_t* dhs;
+  const int32_t* offsets;
+  const int2* sched;
+  int d, I, k, Tk, E;
+};
+struct GemmMxGateDgradArgs {
+  const uint8_t* dhq;
+  const uint8_t* dhs;
+  const uint8_t* w8;   // W1 transposed [E, d, 2I], scales [E, d, 2I/32]
+  const uint8_t* ws;
+  uint16_t* dXp;
+  const int32_t* offsets;
+  const int2* sched;
+  int d, I, Tk, E;
+};
+hipError_t launch_fwd_gateup_mx(const GemmMxGateUpArgs& a, bool persistent, hipStream_t s);
+hipError_t launch_fwd_down_mx(const GemmMxDownArgs& a, bool persistent, hipStream_t s);
+hipError_t launch_bwd_down_dgrad_mx(const GemmMxDownDgradArgs& a, bool persistent, hipStream_t s);
+hipError_t launch_bwd_gate_dgrad_mx(const GemmMxGateDgradArgs& a, bool persistent, hipStream_t s);
 hipError_t launch_fwd_gateup(const GemmFwdGateUpArgs& a, bool persistent, hipStream_t s);
 hipError_t launch_fwd_down(const GemmFwdDownArgs& a, bool persistent, hipStream_t s);
 hipError_t launch_bwd_down_dgrad(const GemmBwdDownDgradArgs& a, bool persistent, hipStream_t s);
@@ -92,7 +150,9 @@ constexpr int kWgradBN = 128;         // dW columns per tile
 constexpr int kWgradTaskSteps = 64;   // K-steps of 32 positions per task (target)
 struct WgradArgs {
   const uint16_t* L;  // [T*k, Mdim], position-major
-  const uint16_t* R;  // [T*k, Ndim], position-major
+  const uint16_t* R;  // [T*k, Ndim], position-major (bf16), or null when R8 is given
+  const uint8_t* R8;  // MXFP8 R: codes [T*k, Ndim] (gate wgrad only), or null
+  const uint8_t* R8s; // its scales [T*k, Ndim/32]
   float* dw;          // [E, Mdim, Ndim]
   const int32_t* offsets;
   int4* table;        // task table, wgrad_table_entries(...) entries
@@ -105,6 +165,15 @@ struct WgradArgs {
 size_t wgrad_table_entries(int Tk, int E, int Mdim, int Ndim);
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
 
+// mx.hip
+hipError_t launch_quant_rows(const uint16_t* src, long long rows, int cols, uint8_t* dst,
+                             uint8_t* sc, const char* name, hipStream_t s);
+hipError_t launch_quant_cols_t(const uint16_t* src, int B, int R, int C, uint8_t* dst,
+                               uint8_t* sc, const char* name, hipStream_t s);
+hipError_t launch_scale_gather(const uint16_t* dy, const int32_t* offsets, const int32_t* row_src,
+                               const float* topk_w, int E, int k, int d, int Tk, uint16_t* dyw,
+                               hipStream_t s);
+
 // elementwise.hip
 hipError_t launch_combine(const uint16_t* O, const int32_t* tk_row, const float* topk_w, int T,
                           int k, int d, uint16_t* y, hipStream_t s);
@@ -114,7 +183,9 @@ hipError_t launch_dw_router(const float* dwpart, int nIt, const int32_t* tk_row,
 hipError_t launch_uncombine(const uint16_t* dXp, const int32_t* tk_row, const int32_t* topk_idx,
                             const float* dl_pos, const uint16_t* wr, int T, int k, int d,
                             uint16_t* dx, hipStream_t s);
-hipError_t launch_dwr(const float* dl_pos, const uint16_t* xp, const int32_t* offsets, int E,
-                      int d, float* dwr, int accumulate, hipStream_t s);
+// With xp8 non-null, Xp is read as MXFP8 (codes xp8, scales xps) instead of bf16 xp.
+hipError_t launch_dwr(const float* dl_pos, const uint16_t* xp, const uint8_t* xp8,
+                      const uint8_t* xps, const int32_t* offsets, int E, int d, float* dwr,
+                      int accumulate, hipStream_t s);
 
 }  // namespace moe

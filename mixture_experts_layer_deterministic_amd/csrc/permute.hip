@@ -82,12 +82,16 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ b
   }
 }
 
-// Places rows [r0, r0 + rpb) and copies their tokens: Xp[pos] = x[r / k].
+// Places rows [r0, r0 + rpb) and copies their tokens: Xp[pos] = x[r / k]. With MX the copy is
+// the token's MXFP8 image: E4M3 codes xp8 [T*k, d] and one scale per 32 along d in xps
+// [T*k, d/32]. Four consecutive lanes own one 32-block (d is a multiple of 32, so blocks never
+// straddle rows), and every lane runs the shuffles.
+template <bool MX>
 __global__ void __launch_bounds__(256) perm_place_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ rank,
     const int32_t* __restrict__ blk_base, int Tk, int E, int k, int32_t* __restrict__ row_src,
     int32_t* __restrict__ tk_row, const uint16_t* __restrict__ x, uint16_t* __restrict__ xp,
-    int d, int rpb) {
+    uint8_t* __restrict__ xp8, uint8_t* __restrict__ xps, int d, int rpb) {
   __shared__ int sh_pos[256];
   const int tid = threadIdx.x;
   const int r0 = blockIdx.x * rpb;
@@ -106,13 +110,40 @@ __global__ void __launch_bounds__(256) perm_place_kernel(
   }
   __syncthreads();
   const int vpr = d / 8;
-  for (int i = tid; i < rpb * vpr; i += 256) {
+  const int n = rpb * vpr;
+  for (int i0 = 0; i0 < n; i0 += 256) {
+    const int i = i0 + tid;
     const int rr = i / vpr, v = i % vpr;
     const int r = r0 + rr;
-    const int pos = sh_pos[rr];
-    if (r >= Tk || pos < 0) continue;
-    const uint4 val = *reinterpret_cast<const uint4*>(x + (size_t)(r / k) * d + v * 8);
-    *reinterpret_cast<uint4*>(xp + (size_t)pos * d + v * 8) = val;
+    const int pos = i < n ? sh_pos[rr] : -1;
+    const bool live = i < n && r < Tk && pos >= 0;
+    const uint4 val =
+        live ? *reinterpret_cast<const uint4*>(x + (size_t)(r / k) * d + v * 8) : make_uint4(0, 0, 0, 0);
+    if constexpr (!MX) {
+      if (live) *reinterpret_cast<uint4*>(xp + (size_t)pos * d + v * 8) = val;
+    } else {
+      const uint32_t xw[4] = {val.x, val.y, val.z, val.w};
+      float f[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f[2 * q] = bf2f_lo(xw[q]);
+        f[2 * q + 1] = bf2f_hi(xw[q]);
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      const uint32_t code = mx_scale_code(amax);
+      const float inv = mx_inv_scale(code);
+      uint2 o;
+      o.x = e4m3x2(f[0] * inv, f[1] * inv) | (e4m3x2(f[2] * inv, f[3] * inv) << 16);
+      o.y = e4m3x2(f[4] * inv, f[5] * inv) | (e4m3x2(f[6] * inv, f[7] * inv) << 16);
+      if (live) {
+        *reinterpret_cast<uint2*>(xp8 + (size_t)pos * d + v * 8) = o;
+        if ((v & 3) == 0) xps[(size_t)pos * (d / 32) + v / 4] = static_cast<uint8_t>(code);
+      }
+    }
   }
 }
 
@@ -139,7 +170,8 @@ hipError_t launch_perm_scan(int32_t* blk_cnt, int nb, int E, const int32_t* blk_
 
 hipError_t launch_perm_place(const int32_t* idx, const int32_t* rank, const int32_t* blk_base,
                              int Tk, int E, int k, int32_t* row_src, int32_t* tk_row,
-                             const uint16_t* x, uint16_t* xp, int d, hipStream_t s) {
+                             const uint16_t* x, uint16_t* xp, uint8_t* xp8, uint8_t* xps, int d,
+                             hipStream_t s) {
   const int vpr = d / 8;
   int rpb = 2048 / vpr;
   if (rpb < 1) rpb = 1;
@@ -147,8 +179,12 @@ hipError_t launch_perm_place(const int32_t* idx, const int32_t* rank, const int3
   const int grid = (Tk + rpb - 1) / rpb;
   {
     TraceScope trace("perm_place", s);
-    hipLaunchKernelGGL(perm_place_kernel, dim3(grid), dim3(256), 0, s, idx, rank, blk_base, Tk, E, k,
-                       row_src, tk_row, x, xp, d, rpb);
+    if (xp8)
+      hipLaunchKernelGGL(perm_place_kernel<true>, dim3(grid), dim3(256), 0, s, idx, rank, blk_base,
+                         Tk, E, k, row_src, tk_row, x, xp, xp8, xps, d, rpb);
+    else
+      hipLaunchKernelGGL(perm_place_kernel<false>, dim3(grid), dim3(256), 0, s, idx, rank,
+                         blk_base, Tk, E, k, row_src, tk_row, x, xp, xp8, xps, d, rpb);
   }
   return hipGetLastError();
 }

@@ -41,7 +41,9 @@ constexpr int R_STAGE = BN * LDR;   // uint16 elements per R stage
 
 struct Args {
   const uint16_t* L;  // [T*k, Mdim]
-  const uint16_t* R;  // [T*k, Ndim]
+  const uint16_t* R;  // [T*k, Ndim] bf16, or (R8) fp8 codes R8 [T*k, Ndim] with scales R8s
+  const uint8_t* R8;
+  const uint8_t* R8s; // [T*k, Ndim/32]
   float* dw;          // [E, Mdim, Ndim]
   const int32_t* offsets;
   const int4* table;  // (expert, first row, first n-tile, n-tile count)
@@ -55,9 +57,14 @@ struct Args {
 // [MN][K] and each MFMA fragment is one 16-byte LDS read.
 struct Mover {
   const uint16_t* base;  // operand base, already offset to the task's first column
+  const uint8_t* base8;  // fp8 operand: codes and per-32 scales (FP8 loads only)
+  const uint8_t* sc8;
   int ld;                // row pitch of the operand (elements)
   uint4 r[2][4];
 
+  // FP8: the operand is MXFP8 (E4M3 codes with one scale per 32 along the row); each element
+  // is expanded to its exact bf16 value.
+  template <bool FP8 = false>
   MOE_DEV void load(int pbase, int p1, int col0, int lane) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -65,8 +72,25 @@ struct Mover {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int p = pbase + kq * 4 + rr;
-        r[h][rr] = p < p1 ? *reinterpret_cast<const uint4*>(base + (size_t)p * ld + col0 + mb * 8)
-                          : make_uint4(0, 0, 0, 0);
+        if constexpr (!FP8) {
+          r[h][rr] = p < p1 ? *reinterpret_cast<const uint4*>(base + (size_t)p * ld + col0 + mb * 8)
+                            : make_uint4(0, 0, 0, 0);
+        } else {
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (p < p1) {
+            const int c = col0 + mb * 8;
+            const uint2 q = *reinterpret_cast<const uint2*>(base8 + (size_t)p * ld + c);
+            const float s = mx_scale(sc8[(size_t)p * (ld / 32) + c / 32]);
+            float f[4], g[4];
+            e4m3x4_to_f32(q.x, f);
+            e4m3x4_to_f32(q.y, g);
+            v.x = pack_bf2(f[0] * s, f[1] * s);
+            v.y = pack_bf2(f[2] * s, f[3] * s);
+            v.z = pack_bf2(g[0] * s, g[1] * s);
+            v.w = pack_bf2(g[2] * s, g[3] * s);
+          }
+          r[h][rr] = v;
+        }
       }
     }
   }
@@ -133,8 +157,8 @@ MOE_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::
 // c - 1, so every load has kProducers - 1 iterations to arrive. Producers and consumers run
 // separate loops with the same number of barriers per task (1 + nt * nk); the role is a
 // wave-uniform scalar, so each wave branches over the other role's code.
-// GATE only separates the two instances (dW1 and dW2) for profilers.
-template <bool ACC, bool GATE>
+// GATE only separates the two instances (dW1 and dW2) for profilers. R8: R is MXFP8.
+template <bool ACC, bool GATE, bool R8>
 __global__ void __launch_bounds__(kThreads, 2) wgrad_kernel(const Args a,
                                                            const int4* __restrict__ table,
                                                            const int32_t* __restrict__ offsets,
@@ -168,6 +192,8 @@ __global__ void __launch_bounds__(kThreads, 2) wgrad_kernel(const Args a,
       ml.base = a.L + m0;
       ml.ld = a.Mdim;
       mr.base = a.R;
+      mr.base8 = a.R8;
+      mr.sc8 = a.R8s;
       mr.ld = a.Ndim;
       if (resident) {
         for (int kt = pq; kt < nk; kt += kProducers) {
@@ -178,7 +204,7 @@ __global__ void __launch_bounds__(kThreads, 2) wgrad_kernel(const Args a,
       // chunk pq: loads now; chunk 0 is written before the first barrier
       if (pq < total) {
         const int pb = p0 + (pq % nk) * BK;
-        mr.load(pb, p1, nfirst + (pq / nk) * BN, lane);
+        mr.load<R8>(pb, p1, nfirst + (pq / nk) * BN, lane);
         if (!resident) ml.load(pb, p1, 0, lane);
         if (pq == 0) {
           mr.store(rbuf, LDR, 0, lane);
@@ -195,7 +221,7 @@ __global__ void __launch_bounds__(kThreads, 2) wgrad_kernel(const Args a,
         const int cn = it + kProducers;
         if (it % kProducers == pq && cn < total) {
           const int pb = p0 + (cn % nk) * BK;
-          mr.load(pb, p1, nfirst + (cn / nk) * BN, lane);
+          mr.load<R8>(pb, p1, nfirst + (cn / nk) * BN, lane);
           if (!resident) ml.load(pb, p1, 0, lane);
         }
         lds_barrier();
@@ -297,7 +323,7 @@ int resident_grid() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&wgrad_kernel<false, false>), kThreads, 0) != hipSuccess)
+            &per_cu, reinterpret_cast<const void*>(&wgrad_kernel<false, false, false>), kThreads, 0) != hipSuccess)
       return 0;
     grid = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
   }
@@ -323,11 +349,13 @@ hipError_t launch_wgrad(const WgradArgs& x, hipStream_t s) {
   if (err != hipSuccess) return err;
   const int grid = resident_grid();
   if (grid <= 0) return hipErrorInvalidValue;
-  Args a{x.L, x.R, x.dw, x.offsets, x.table, x.count, x.Mdim, x.Ndim, x.accumulate};
+  Args a{x.L, x.R, x.R8, x.R8s, x.dw, x.offsets, x.table, x.count, x.Mdim, x.Ndim, x.accumulate};
   {
     TraceScope trace(x.name, s);
-    auto kern = x.accumulate ? (x.gate ? wgrad_kernel<true, true> : wgrad_kernel<true, false>)
-                             : (x.gate ? wgrad_kernel<false, true> : wgrad_kernel<false, false>);
+    auto kern = x.R8 ? (x.accumulate ? wgrad_kernel<true, true, true> : wgrad_kernel<false, true, true>)
+                     : x.accumulate
+                         ? (x.gate ? wgrad_kernel<true, true, false> : wgrad_kernel<true, false, false>)
+                         : (x.gate ? wgrad_kernel<false, true, false> : wgrad_kernel<false, false, false>);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, s, a, x.table, x.offsets, x.count);
   }
   return hipGetLastError();

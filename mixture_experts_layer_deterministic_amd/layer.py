@@ -6,15 +6,16 @@ from __future__ import annotations
 
 import torch
 
-from . import (MOE_FLAG_PERSISTENT, MOE_PREC_BF16, make_cfg, moe_backward, moe_forward,
-               moe_permute, moe_query, moe_route)
+from . import (MOE_FLAG_PERSISTENT, MOE_PREC_BF16, MOE_PREC_MXFP8, make_cfg, moe_backward,
+               moe_forward, moe_permute, moe_query, moe_quantize_weights, moe_route)
 
 
 class MoeLayer:
     """Caller-owned buffers for one (T, d, E, k, I) shape on one device.
 
     ``ring_slots`` slots of T*k permuted rows make up the ring. Forward writes slot ``slot``,
-    and backward reads the slot its batch was permuted into.
+    and backward reads the slot its batch was permuted into. With ``precision=MOE_PREC_MXFP8``
+    the layer also owns the quantised-weight buffer ``wq``; ``quantize_weights`` fills it.
     """
 
     def __init__(self, T, d, E, k, I, device="cuda", ring_slots=1, persistent=False,
@@ -42,6 +43,8 @@ class MoeLayer:
         self.dw1 = torch.zeros(E, 2 * I, d, dtype=f32, device=dev)
         self.dw2 = torch.zeros(E, d, I, dtype=f32, device=dev)
         self.dwr = torch.zeros(E, d, dtype=f32, device=dev)
+        self.mx = precision == MOE_PREC_MXFP8
+        self.wq = torch.empty(s.wq, dtype=u8, device=dev) if self.mx else None
 
     # views of intermediates -----------------------------------------------------------------
     def _view(self, buf, off, rows, cols):
@@ -49,7 +52,15 @@ class MoeLayer:
         return buf[off:off + n].view(torch.bfloat16).view(rows, cols)
 
     def xp(self, slot=0):
-        return self._view(self.ring, slot * self.sizes.ring_slot, self.T * self.k, self.d)
+        """The slot's bf16 Xp (BF16 mode), or (E4M3 codes [T*k, d], scale codes [T*k, d/32]) as
+        uint8 tensors (MXFP8 mode)."""
+        base = slot * self.sizes.ring_slot
+        if not self.mx:
+            return self._view(self.ring, base, self.T * self.k, self.d)
+        Tk, d = self.T * self.k, self.d
+        codes = self.ring[base:base + Tk * d].view(Tk, d)
+        sc0 = base + (Tk * d + 255) // 256 * 256
+        return codes, self.ring[sc0:sc0 + Tk * d // 32].view(Tk, d // 32)
 
     def H(self):
         return self._view(self.saved, self.sizes.saved_H, self.T * self.k, 2 * self.I)
@@ -81,13 +92,17 @@ class MoeLayer:
         moe_permute(self.cfg, self.topk_idx, x, self.ring, slot, self.counts, self.offsets,
                     self.row_src, self.tk_row, self.workspace, stream)
 
+    def quantize_weights(self, w1, w2, stream=None):
+        moe_quantize_weights(self.cfg, w1, w2, self.wq, stream)
+
     def forward(self, w1, w2, slot=0, saved=None, stream=None):
         moe_forward(self.cfg, self.ring, slot, self.offsets, self.tk_row, self.topk_w, w1, w2,
-                    None, self.y, self.saved if saved is None else saved, self.workspace, stream)
+                    self.wq, self.y, self.saved if saved is None else saved, self.workspace,
+                    stream)
 
     def backward(self, w_router, w1, w2, dy, slot=0, accumulate=False, saved=None, stream=None):
         moe_backward(self.cfg, self.ring, slot, self.offsets, self.row_src, self.tk_row,
-                     self.topk_idx, self.topk_w, w_router, w1, w2, None,
+                     self.topk_idx, self.topk_w, w_router, w1, w2, self.wq,
                      self.saved if saved is None else saved, dy, self.dx, self.dw1, self.dw2,
                      self.dwr if w_router is not None else None, self.d_topk_w, accumulate,
                      self.workspace, stream)

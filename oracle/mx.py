@@ -25,8 +25,8 @@ E4M3_MAX = 448.0
 E4M3_EMAX = 8  # exponent of the largest normal E4M3 value
 
 
-def e4m3_value(codes) -> np.ndarray:
-    """float64 value of each E4M3 code (uint8); NaN for S.1111.111."""
+def _e4m3_formula(codes) -> np.ndarray:
+    """float64 value of each E4M3 code by the format's definition; NaN for S.1111.111."""
     c = np.asarray(codes, dtype=np.int64)
     s = (c >> 7) & 1
     e = (c >> 3) & 0xF
@@ -36,22 +36,32 @@ def e4m3_value(codes) -> np.ndarray:
     return np.where(s == 1, -mag, mag)
 
 
-# The 127 non-negative finite values in code order; the order is ascending.
-_POS = e4m3_value(np.arange(127))
+_VALUES = _e4m3_formula(np.arange(256))  # value of every code
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """float64 value of each E4M3 code (uint8); NaN for S.1111.111."""
+    return _VALUES[np.asarray(codes, dtype=np.uint8)]
 
 
 def e4m3_encode(v) -> np.ndarray:
     """E4M3 codes of float64 values: round to nearest, ties to the even code, and saturate to
-    +-448. The sign bit is the sign of v."""
+    +-448. The sign bit is the sign of v.
+
+    A magnitude a <= 448 lies in the binade [2^e, 2^(e+1)), where E4M3 values are spaced
+    2^(e-3); the subnormals below 2^-6 share the spacing 2^-9. The nearest value is
+    n * 2^(e-3) with n = a / 2^(e-3) rounded half-to-even. n's parity is the code's last bit,
+    so ties go to the even code. n = 16 carries into the next binade."""
     v = np.asarray(v, dtype=np.float64)
     a = np.minimum(np.abs(v), E4M3_MAX)
-    hi = np.clip(np.searchsorted(_POS, a, side="left"), 0, 126)  # first value >= a
-    lo = np.clip(hi - 1, 0, 126)
-    d_lo = a - _POS[lo]
-    d_hi = _POS[hi] - a
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
-    code = np.where(pick_hi, hi, lo)
-    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+    _, x = np.frexp(a)                       # a = f 2^x, f in [0.5, 1): floor(log2 a) = x - 1
+    e = np.maximum(x - 1, -6)
+    n = np.rint(a / np.exp2(e - 3.0))        # 0..16; round half to even
+    carry = n == 16
+    e = np.where(carry, e + 1, e)
+    n = np.where(carry, 8, n)
+    code = np.where(n < 8, n, (e + 7) * 8 + (n - 8)).astype(np.uint8)
+    return code | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
 
 
 def e8m0_code(amax) -> np.ndarray:

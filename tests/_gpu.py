@@ -24,10 +24,18 @@ def _announce(msg):
     sys.stdout.flush()
 
 
+def is_mx(inp):
+    return inp["cfg"].get("precision") == "mxfp8"
+
+
 def run_gpu(inp, persistent=False, slot=0, ring_slots=1):
     cfg = inp["cfg"]
     T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
-    L = MoeLayer(T, d, E, k, I, device=DEV, ring_slots=ring_slots, persistent=persistent)
+    prec = m.MOE_PREC_MXFP8 if is_mx(inp) else m.MOE_PREC_BF16
+    L = MoeLayer(T, d, E, k, I, device=DEV, ring_slots=ring_slots, persistent=persistent,
+                 precision=prec)
+    if is_mx(inp):
+        L.quantize_weights(inp["W1"], inp["W2"])
     wr = inp.get("Wr")
     if wr is None:
         L.set_routing(inp["topk_idx"], inp["topk_w"])
@@ -38,19 +46,37 @@ def run_gpu(inp, persistent=False, slot=0, ring_slots=1):
 
 def run_oracle(inp):
     X, W1, W2, dY = (_np(inp[n]) for n in ("X", "W1", "W2", "dY"))
+    prec = "mxfp8" if is_mx(inp) else "bf16"
     if "Wr" in inp:
         Wr = _np(inp["Wr"])
-        f = oracle.forward(X, W1, W2, Wr=Wr, k=inp["cfg"]["k"])
+        f = oracle.forward(X, W1, W2, Wr=Wr, k=inp["cfg"]["k"], precision=prec)
         b = oracle.backward(f, X, W1, W2, dY, Wr=Wr)
     else:
-        f = oracle.forward(X, W1, W2, topk_idx=_np(inp["topk_idx"]), topk_w=_np(inp["topk_w"]))
+        f = oracle.forward(X, W1, W2, topk_idx=_np(inp["topk_idx"]), topk_w=_np(inp["topk_w"]),
+                           precision=prec)
         b = oracle.backward(f, X, W1, W2, dY)
     return f, b
 
 
-def check_parity(L, inp, f, b, slot=0):
-    routed = "Wr" in inp
+def check_xp(L, inp, f, slot=0):
+    """The slot's permuted tokens: a bit-exact copy of X (BF16 mode), or the MXFP8 codes and
+    scales of X, bit-exact against the oracle's quantiser (MXFP8 mode)."""
     k = inp["cfg"]["k"]
+    src = _np(inp["X"])[f["row_src"] // k]
+    if not is_mx(inp):
+        np.testing.assert_array_equal(_np(L.xp(slot)), src)
+        return
+    codes, scales = L.xp(slot)
+    q, sc = oracle.mx.quantize(src)
+    np.testing.assert_array_equal(_np(scales), sc)
+    np.testing.assert_array_equal(_np(codes), q)
+
+
+def check_parity(L, inp, f, b, slot=0, tol_act=None, tol_grad=None):
+    from tests._util import TOL_ACT, TOL_GRAD
+    ta = TOL_ACT if tol_act is None else tol_act
+    tg = TOL_GRAD if tol_grad is None else tol_grad
+    routed = "Wr" in inp
     if routed:
         np.testing.assert_array_equal(_np(L.logits), f["logits"])
         np.testing.assert_array_equal(_np(L.topk_idx), f["idx"])
@@ -59,26 +85,29 @@ def check_parity(L, inp, f, b, slot=0):
     np.testing.assert_array_equal(_np(L.offsets), f["offsets"])
     np.testing.assert_array_equal(_np(L.row_src), f["row_src"])
     np.testing.assert_array_equal(_np(L.tk_row), f["tk_row"])
-    xp = _np(L.xp(slot))
-    np.testing.assert_array_equal(xp, _np(inp["X"])[f["row_src"] // k])
-    assert_act("H", _np(L.H()), f["H"])
-    assert_act("A", _np(L.A()), f["A"])
-    assert_act("O", _np(L.O()), f["O"])
-    assert_act("Y", _np(L.y), f["Y"])
-    assert_act("dH", _np(L.dH()), b["dH"])
-    assert_act("dXp", _np(L.dXp()), b["dXp"])
-    assert_act("dX", _np(L.dx), b["dX"])
-    assert_grad("dW1", _np(L.dw1), b["dW1"])
-    assert_grad("dW2", _np(L.dw2), b["dW2"])
-    assert_grad("d_topk_w", _np(L.d_topk_w), b["dw"])
+    check_xp(L, inp, f, slot)
+    assert_act("H", _np(L.H()), f["H"], ta)
+    assert_act("A", _np(L.A()), f["A"], ta)
+    assert_act("O", _np(L.O()), f["O"], ta)
+    assert_act("Y", _np(L.y), f["Y"], ta)
+    assert_act("dH", _np(L.dH()), b["dH"], ta)
+    assert_act("dXp", _np(L.dXp()), b["dXp"], ta)
+    assert_act("dX", _np(L.dx), b["dX"], ta)
+    assert_grad("dW1", _np(L.dw1), b["dW1"], tg)
+    assert_grad("dW2", _np(L.dw2), b["dW2"], tg)
+    assert_grad("d_topk_w", _np(L.d_topk_w), b["dw"], tg)
     if routed:
-        assert_grad("dWr", _np(L.dwr), b["dWr"])
+        assert_grad("dWr", _np(L.dwr), b["dWr"], tg)
 
 
 def outputs(L, routed, clone=True):
     outs = [L.logits, L.topk_idx, L.topk_w] if routed else []
     outs += [L.counts, L.offsets, L.row_src, L.tk_row, L.y, L.H(), L.A(), L.dx, L.dw1, L.dw2,
              L.d_topk_w]
+    if L.mx:
+        outs += list(L.xp())
+        if L.wq.numel() < (1 << 30):  # the full-size quantised weights are too big to clone
+            outs.append(L.wq)
     if routed:
         outs.append(L.dwr)
     return [o.clone() for o in outs] if clone else outs

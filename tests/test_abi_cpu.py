@@ -72,18 +72,37 @@ def test_entry_points_reject_bad_arguments_before_launching():
     # workspace too small
     assert L.moe_permute(ctypes.byref(cfg), p, p, p, s.ring_slot, 0, p, p, p, p, p,
                          s.workspace - 1, None) == -5
-    assert L.moe_forward(ctypes.byref(cfg), p, s.ring_slot, 0, p, p, p, p, p, None, p, p,
+    assert L.moe_forward(ctypes.byref(cfg), p, s.ring_slot, 0, p, p, p, p, p, None, 0, p, p,
                          s.saved - 1, p, s.workspace, None) == -5
-    # MXFP8 is not provided by this build
+    # an unknown precision is not provided by this build
+    cfgx = m.make_cfg(64, 256, 8, 2, 128, 2)
+    assert L.moe_route(ctypes.byref(cfgx), p, p, p, p, p, None) == -3
+    # MXFP8: the quantised weights are required, and sized
     cfg8 = m.make_cfg(64, 256, 8, 2, 128, m.MOE_PREC_MXFP8)
-    assert L.moe_forward(ctypes.byref(cfg8), p, s.ring_slot, 0, p, p, p, p, p, None, p, p,
-                         s.saved, p, s.workspace, None) == -3
+    s8 = m.moe_query(cfg8)
+    assert L.moe_forward(ctypes.byref(cfg8), p, s8.ring_slot, 0, p, p, p, p, p, None, 0, p, p,
+                         s8.saved, p, s8.workspace, None) == -1
+    assert L.moe_forward(ctypes.byref(cfg8), p, s8.ring_slot, 0, p, p, p, p, p, p, s8.wq - 1, p,
+                         p, s8.saved, p, s8.workspace, None) == -5
+    assert L.moe_quantize_weights(ctypes.byref(cfg), p, p, p, 1 << 30, None) == -1
+    assert L.moe_quantize_weights(ctypes.byref(cfg8), p, p, p, s8.wq - 1, None) == -5
     # unknown flag bits
     cfgf = m.make_cfg(64, 256, 8, 2, 128, 0, 8)
     assert L.moe_route(ctypes.byref(cfgf), p, p, p, p, p, None) == -1
     # backward: bad dwr when the router weight is given
-    assert L.moe_backward(ctypes.byref(cfg), p, s.ring_slot, 0, p, p, p, p, p, p, p, p, None,
+    assert L.moe_backward(ctypes.byref(cfg), p, s.ring_slot, 0, p, p, p, p, p, p, p, p, None, 0,
                           p, s.saved, p, p, p, p, null, p, 0, p, s.workspace, None) == -1
+
+
+def test_mxfp8_sizes():
+    T, d, E, k, I = 2048, 7168, 256, 8, 2048
+    s = m.moe_query(m.make_cfg(T, d, E, k, I, m.MOE_PREC_MXFP8))
+    Tk = T * k
+    up = lambda v: (v + 255) // 256 * 256
+    assert s.ring_slot == up(Tk * d) + up(Tk * d // 32)
+    wq = 2 * (up(E * 2 * I * d) + up(E * 2 * I * d // 32)) + 2 * (up(E * d * I) + up(E * d * I // 32))
+    assert s.wq == wq
+    assert m.moe_query(m.make_cfg(T, d, E, k, I)).wq == 0
 
 
 def test_status_strings():

@@ -1,0 +1,139 @@
+"""GPU parity of the MXFP8 mode against the oracle that emulates the same quantisation.
+
+* The quantised weights and the permuted tokens are integer codes: they must equal the oracle's
+  quantiser bit for bit.
+* Routing and the permutation maps are bit-exact, as in BF16 mode.
+* Floating outputs and gradients must be within 6e-2 of the MXFP8-emulating oracle. Y and dX
+  are checked as max-abs and RMS relative error; the weight, router and routing-weight
+  gradients as relative Frobenius error.
+* Two runs are bitwise identical, at a small shape and at the DeepSeek-V3 shape (sampled
+  checks there, as in tests/test_gpu_sizes_full.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+from tests._gpu import (DEV, _announce, _np, assert_bitwise_equal, check_parity, m, outputs,
+                        run_gpu, run_oracle)
+from tests._util import assert_act, assert_grad
+
+pytestmark = pytest.mark.gpu
+
+TOL_MX = 6e-2
+
+
+def _up(v):
+    return (v + 255) // 256 * 256
+
+
+def _wq_parts(L):
+    """The four MXFP8 weight tensors and their scales inside L.wq, in the order the header
+    lists them: W1 along d, W2 along I, W2 transposed along d, W1 transposed along 2I."""
+    E, d, I = L.E, L.d, L.I
+    shapes = [(E, 2 * I, d), (E, d, I), (E, I, d), (E, d, 2 * I)]
+    out, o = [], 0
+    for sh in shapes:
+        n = sh[0] * sh[1] * sh[2]
+        codes = L.wq[o:o + n].view(*sh)
+        o += _up(n)
+        sc = L.wq[o:o + n // 32].view(sh[0], sh[1], sh[2] // 32)
+        o += _up(n // 32)
+        out.append((codes, sc))
+    return out
+
+
+def _mx_inputs(name="tiny", seed=0, **over):
+    return workload.make_inputs(name, seed=seed, device=DEV, precision="mxfp8", **over)
+
+
+def test_weight_quantisation_is_bit_exact():
+    _announce("[mxfp8] quantised weights, tiny shape")
+    inp = _mx_inputs(seed=0, E=4)
+    L = run_gpu(inp)
+    W1, W2 = _np(inp["W1"]), _np(inp["W2"])
+    refs = [oracle.mx.quantize(W1), oracle.mx.quantize(W2),
+            oracle.mx.quantize(np.swapaxes(W2, 1, 2)), oracle.mx.quantize(np.swapaxes(W1, 1, 2))]
+    for i, ((codes, sc), (q, s)) in enumerate(zip(_wq_parts(L), refs)):
+        np.testing.assert_array_equal(_np(sc), s, err_msg=f"scales of part {i}")
+        np.testing.assert_array_equal(_np(codes), q, err_msg=f"codes of part {i}")
+
+
+MX_CASES = {
+    "tiny": dict(name="tiny"),
+    "ragged": dict(name="tiny", T=300, E=16, k=3, d=512, I=256),
+    "multi_mtile": dict(name="tiny", T=1024, E=4, k=2, d=512, I=256),
+    "zipf_local": dict(name="local_zipf", T=2048, d=256, I=256),
+}
+
+
+@pytest.mark.parametrize("case", list(MX_CASES))
+def test_mxfp8_layer_parity(case):
+    spec = dict(MX_CASES[case])
+    name = spec.pop("name")
+    _announce(f"[mxfp8] case={case} shape={spec} seed=0")
+    inp = _mx_inputs(name, seed=0, **spec)
+    L = run_gpu(inp)
+    f, b = run_oracle(inp)
+    check_parity(L, inp, f, b, tol_act=TOL_MX, tol_grad=TOL_MX)
+
+
+def test_mxfp8_two_runs_are_bitwise_identical():
+    _announce("[mxfp8] determinism, multi-m-tile shape")
+    inp = _mx_inputs("tiny", seed=2, T=1024, E=8, k=2, d=512, I=256)
+    a = outputs(run_gpu(inp), True)
+    b = outputs(run_gpu(inp, persistent=True), True)
+    assert_bitwise_equal(a, b)
+
+
+def test_mxfp8_full_size_sampled_parity_and_determinism():
+    """At the DeepSeek-V3 shape the oracle's quantiser costs seconds per expert, so this checks
+    one sampled token (its 8 experts) and the heaviest expert's weights and weight gradients."""
+    _announce("[mxfp8] dsv3_mxfp8 T=2048 d=7168 E=256 k=8 I=2048 seed 0")
+    inp = workload.make_inputs("dsv3_mxfp8", seed=0, device=DEV)
+    L = run_gpu(inp)
+    X, dY, Wr = _np(inp["X"]), _np(inp["dY"]), _np(inp["Wr"])
+    k = inp["cfg"]["k"]
+    logits = oracle.router_logits_fp32(X, Wr)
+    np.testing.assert_array_equal(_np(L.logits), logits)
+    idx, _ = oracle.route_topk(logits, k)
+    np.testing.assert_array_equal(_np(L.topk_idx), idx)
+    counts, offsets, row_src, tk_row = oracle.permute(idx, inp["cfg"]["E"])
+    np.testing.assert_array_equal(_np(L.row_src), row_src)
+    _announce("  routing and permutation bit-exact")
+    pos = np.unique(np.concatenate([[0, len(row_src) - 1],
+                                    np.random.default_rng(5).choice(len(row_src), 64)]))
+    codes, scales = L.xp()
+    q, sc = oracle.mx.quantize(X[row_src[pos] // k])
+    p_dev = torch.from_numpy(pos).to(DEV)
+    np.testing.assert_array_equal(_np(codes[p_dev]), q)
+    np.testing.assert_array_equal(_np(scales[p_dev]), sc)
+    _announce("  ring codes and scales bit-exact on sampled positions")
+    heavy = int(np.argmax(counts))
+    W1e, W2e = _np(inp["W1"][heavy]), _np(inp["W2"][heavy])
+    refs = [oracle.mx.quantize(W1e), oracle.mx.quantize(W2e),
+            oracle.mx.quantize(W2e.T), oracle.mx.quantize(W1e.T)]
+    for i, ((cq, cs), (rq, rs)) in enumerate(zip(_wq_parts(L), refs)):
+        np.testing.assert_array_equal(_np(cs[heavy]), rs, err_msg=f"scales of part {i}")
+        np.testing.assert_array_equal(_np(cq[heavy]), rq, err_msg=f"codes of part {i}")
+    _announce(f"  quantised weights of expert {heavy} bit-exact")
+    W1h, W2h = workload.HostExperts(inp["W1"]), workload.HostExperts(inp["W2"])
+    tok = np.array([int(np.random.default_rng(6).integers(X.shape[0]))])
+    f = oracle.forward(X[tok], W1h, W2h, Wr=Wr, k=k, precision="mxfp8")
+    _announce("  oracle forward of the sampled token done")
+    bk = oracle.backward(f, X[tok], W1h, W2h, dY[tok], Wr=Wr)
+    t_dev = torch.from_numpy(tok).to(DEV)
+    assert_act("Y[token]", _np(L.y[t_dev]), f["Y"], TOL_MX)
+    assert_act("dX[token]", _np(L.dx[t_dev]), bk["dX"], TOL_MX)
+    assert_grad("d_topk_w[token]", _np(L.d_topk_w[t_dev]), bk["dw"], TOL_MX)
+    fe = oracle.forward(X, W1h, W2h, Wr=Wr, k=k, experts=[heavy], precision="mxfp8")
+    _announce("  oracle forward of the heavy expert done")
+    be = oracle.backward(fe, X, W1h, W2h, dY, Wr=Wr, experts=[heavy])
+    assert_grad(f"dW1[{heavy}]", _np(L.dw1[heavy]), be["dW1"][0], TOL_MX)
+    assert_grad(f"dW2[{heavy}]", _np(L.dw2[heavy]), be["dW2"][0], TOL_MX)
+    ref = outputs(L, True)
+    del L
+    torch.cuda.empty_cache()
+    assert_bitwise_equal(ref, outputs(run_gpu(inp), True, clone=False))
+    _announce("  two full-size runs bitwise identical")

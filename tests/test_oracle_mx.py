@@ -42,7 +42,7 @@ def test_e4m3_decode_all_codes_match_torch():
 
 def test_e4m3_encode_matches_torch_rne_including_ties_and_subnormals():
     rng = np.random.default_rng(0)
-    pos = mx.e4m3_value(np.arange(127))
+    pos = mx.e4m3_value(np.arange(127))  # the non-negative finite values, ascending
     mids = (pos[:-1] + pos[1:]) / 2  # exact ties, representable in float32
     vals = np.concatenate([
         rng.uniform(-448, 448, 20000), rng.uniform(-2 ** -6, 2 ** -6, 5000),
@@ -56,7 +56,7 @@ def test_e4m3_encode_matches_torch_rne_including_ties_and_subnormals():
 
 def test_e4m3_encode_brute_force_nearest_even():
     rng = np.random.default_rng(1)
-    pos = mx.e4m3_value(np.arange(127))
+    pos = mx.e4m3_value(np.arange(127))  # the non-negative finite values, ascending
     vals = np.concatenate([rng.uniform(0, 450, 3000), (pos[:-1] + pos[1:]) / 2])
     got = mx.e4m3_encode(vals)
     for v, c in zip(vals, got):
