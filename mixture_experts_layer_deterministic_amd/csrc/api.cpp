@@ -6,7 +6,7 @@
 #include <atomic>
 #include <mutex>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "kernels.h"
 
 namespace {

@@ -145,7 +145,7 @@ hipError_t launch_bwd_down_dgrad(const GemmBwdDownDgradArgs& a, bool persistent,
 hipError_t launch_bwd_gate_dgrad(const GemmBwdGateDgradArgs& a, bool persistent, hipStream_t s);
 
 // wgrad.hip
-constexpr int kWgradBM = 128;         // dW rows per task stripe
+constexpr int kWgradBM = 256;         // dW rows per task stripe
 constexpr int kWgradBN = 128;         // dW columns per tile
 constexpr int kWgradTaskSteps = 64;   // K-steps of 32 positions per task (target)
 struct WgradArgs {

@@ -34,9 +34,11 @@ constexpr int BM = kWgradBM, BN = kWgradBN, BK = 32;
 constexpr int KRES = 128;           // positions of L kept resident in LDS for a whole task
 constexpr int LDL = KRES + 8;       // row pitch of the L buffer [BM][LDL]
 constexpr int LDR = BK + 8;         // row pitch of an R stage [BN][LDR]
-constexpr int kConsumers = 256;                 // waves 0..3: MFMA and dW stores
-constexpr int kProducers = 4;                   // waves 4..7: operand loads
+constexpr int kConsumerWaves = (BM / 64) * (BN / 64);  // one 64 x 64 block of dW each
+constexpr int kConsumers = kWave * kConsumerWaves;      // MFMA and dW stores
+constexpr int kProducers = 4;                           // the next waves: operand loads
 constexpr int kThreads = kConsumers + kWave * kProducers;
+constexpr int kWavesPerSimd = (kThreads / kWave + 3) / 4;
 constexpr int R_STAGE = BN * LDR;   // uint16 elements per R stage
 
 struct Args {
@@ -51,23 +53,24 @@ struct Args {
   int Mdim, Ndim, accumulate;
 };
 
-// One producer wave moves a whole 32 x 128 chunk of an operand: 128 blocks of 4 positions x
-// 8 columns, two per lane (block b = lane + 64 h covers positions [4 (b % 8), +4) and columns
-// [8 (b / 8), +8)). Rows are read as 16-byte vectors and transposed in registers, so LDS holds
-// [MN][K] and each MFMA fragment is one 16-byte LDS read.
+// One producer wave moves a whole chunk of 32 positions x 64 NH columns of an operand: blocks
+// of 4 positions x 8 columns, NH per lane (block b = lane + 64 h covers positions [4 (b % 8),
+// +4) and columns [8 (b / 8), +8)). Rows are read as 16-byte vectors and transposed in
+// registers, so LDS holds [MN][K] and each MFMA fragment is one 16-byte LDS read.
+template <int NH>
 struct Mover {
   const uint16_t* base;  // operand base, already offset to the task's first column
   const uint8_t* base8;  // fp8 operand: codes and per-32 scales (FP8 loads only)
   const uint8_t* sc8;
   int ld;                // row pitch of the operand (elements)
-  uint4 r[2][4];
+  uint4 r[NH][4];
 
   // FP8: the operand is MXFP8 (E4M3 codes with one scale per 32 along the row); each element
   // is expanded to its exact bf16 value.
   template <bool FP8 = false>
   MOE_DEV void load(int pbase, int p1, int col0, int lane) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NH; ++h) {
       const int b = lane + kWave * h, kq = b % 8, mb = b / 8;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
@@ -97,7 +100,7 @@ struct Mover {
   // Writes the transposed blocks into an LDS buffer [MN][ldk] at K column kcol.
   MOE_DEV void store(uint16_t* s, int ldk, int kcol, int lane) const {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NH; ++h) {
       const int b = lane + kWave * h, kq = b % 8, mb = b / 8;
       const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[h][0]);
       const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[h][1]);
@@ -120,13 +123,16 @@ struct Mover {
   }
 };
 
+constexpr int WMR = 64;        // dW rows per consumer wave (BM / 64 x BN / 64 waves)
+constexpr int MBW = WMR / 16;  // 16-row MFMA blocks per consumer wave
+
 template <bool ACC>
-MOE_DEV void store_tile(const Args& a, float* out, int n0, const f32x4 (&acc)[4][4]) {
+MOE_DEV void store_tile(const Args& a, float* out, int n0, const f32x4 (&acc)[MBW][4]) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int wm = wave / 2, wn = wave % 2;
+  const int wm = wave / (BN / 64), wn = wave % (BN / 64);
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const int m = wm * 64 + mb * 16 + lane % 16;
+  for (int mb = 0; mb < MBW; ++mb) {
+    const int m = wm * WMR + mb * 16 + lane % 16;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int n = n0 + wn * 64 + nb * 16 + 4 * (lane / 16);
@@ -159,7 +165,7 @@ MOE_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::
 // wave-uniform scalar, so each wave branches over the other role's code.
 // GATE only separates the two instances (dW1 and dW2) for profilers. R8: R is MXFP8.
 template <bool ACC, bool GATE, bool R8>
-__global__ void __launch_bounds__(kThreads, 2) wgrad_kernel(const Args a,
+__global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Args a,
                                                            const int4* __restrict__ table,
                                                            const int32_t* __restrict__ offsets,
                                                            const int32_t* __restrict__ count) {
@@ -169,27 +175,43 @@ __global__ void __launch_bounds__(kThreads, 2) wgrad_kernel(const Args a,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const bool producer = wave >= kConsumers / kWave;
   const int pq = wave - kConsumers / kWave;  // producer index 0..kProducers-1
-  const int wm = (wave / 2) & 1, wn = wave % 2;
+  const int wm = wave / (BN / 64), wn = wave % (BN / 64);  // consumer waves only
   const int ntasks = *count;
   const int G = gridDim.x, G8 = G / kXcds, xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
 
-  for (int round = 0;; ++round) {
-    // Round r gives XCD x the contiguous task range [r G + x G/8, r G + (x+1) G/8), so tasks
-    // of one expert (adjacent in the table) share that XCD's L2.
-    const int ti = round * G + xcd * G8 + slot;
-    if (ti >= ntasks) break;
+  // Round r gives XCD x the contiguous task range [r G + x G/8, r G + (x+1) G/8), so tasks of
+  // one expert (adjacent in the table) share that XCD's L2. Producers and consumers walk the
+  // same tasks in separate loops, which keeps their register live ranges apart.
+  struct TaskInfo {
+    int e, m0, nt, nfirst, p0, p1, nk, total;
+    bool resident;
+  };
+  auto task_at = [&](int ti) {
     const int4 task = table[ti];
-    const int e = task.x, m0 = task.y, nt = task.w;
-    const int nfirst = task.z * BN;
-    const int p0 = offsets[e], p1 = offsets[e + 1];
-    const int nk = (p1 - p0 + BK - 1) / BK;
-    const bool resident = nk <= KRES / BK;
-    const int total = nt * nk;
+    TaskInfo t;
+    t.e = task.x;
+    t.m0 = task.y;
+    t.nt = task.w;
+    t.nfirst = task.z * BN;
+    t.p0 = offsets[t.e];
+    t.p1 = offsets[t.e + 1];
+    t.nk = (t.p1 - t.p0 + BK - 1) / BK;
+    t.resident = t.nk <= KRES / BK;
+    t.total = t.nt * t.nk;
+    return t;
+  };
 
-    if (producer) {
-      if (nk == 0) continue;
-      Mover ml, mr;
-      ml.base = a.L + m0;
+  if (producer) {
+    for (int round = 0;; ++round) {
+      const int ti = round * G + xcd * G8 + slot;
+      if (ti >= ntasks) break;
+      const TaskInfo t = task_at(ti);
+      if (t.nk == 0) continue;
+      const int p0 = t.p0, p1 = t.p1, nk = t.nk, total = t.total, nfirst = t.nfirst;
+      const bool resident = t.resident;
+      Mover<BM / 64> ml;
+      Mover<BN / 64> mr;
+      ml.base = a.L + t.m0;
       ml.ld = a.Mdim;
       mr.base = a.R;
       mr.base8 = a.R8;
@@ -226,20 +248,27 @@ __global__ void __launch_bounds__(kThreads, 2) wgrad_kernel(const Args a,
         }
         lds_barrier();
       }
-    } else {
-      float* out = a.dw + ((size_t)e * a.Mdim + m0) * a.Ndim;
-      f32x4 acc[4][4];
+    }
+  } else {
+    const int koff = (lane / 16) * 8;
+    for (int round = 0;; ++round) {
+      const int ti = round * G + xcd * G8 + slot;
+      if (ti >= ntasks) break;
+      const TaskInfo t = task_at(ti);
+      const int nk = t.nk, total = t.total, nfirst = t.nfirst;
+      const bool resident = t.resident;
+      float* out = a.dw + ((size_t)t.e * a.Mdim + t.m0) * a.Ndim;
+      f32x4 acc[MBW][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MBW; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (nk == 0) {  // an expert with no rows: its dW block is zero
         if (!ACC)
-          for (int j = 0; j < nt; ++j) store_tile<false>(a, out, nfirst + j * BN, acc);
+          for (int j = 0; j < t.nt; ++j) store_tile<false>(a, out, nfirst + j * BN, acc);
         continue;
       }
       lds_barrier();
-      const int koff = (lane / 16) * 8;
       int j = 0, kt = 0;
       for (int it = 0; it < total; ++it) {
         const uint16_t* rs = rbuf + (it & 1) * R_STAGE;
@@ -249,16 +278,16 @@ __global__ void __launch_bounds__(kThreads, 2) wgrad_kernel(const Args a,
         for (int nb = 0; nb < 4; ++nb)
           bf[nb] = *reinterpret_cast<const uint4*>(rs + (wn * 64 + nb * 16 + lane % 16) * LDR + koff);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < MBW; ++mb) {
           const uint4 af =
-              *reinterpret_cast<const uint4*>(lbuf + (wm * 64 + mb * 16 + lane % 16) * LDL + lcol);
+              *reinterpret_cast<const uint4*>(lbuf + (wm * WMR + mb * 16 + lane % 16) * LDL + lcol);
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(bf[nb], af, acc[mb][nb]);
         }
         if (kt == nk - 1) {
           store_tile<ACC>(a, out, nfirst + j * BN, acc);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < MBW; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
