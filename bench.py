@@ -53,6 +53,7 @@ def algorithmic(cfg, routed=True, accumulate=False):
     b["bwd_down_dgrad"] = (E * d * I * 2 + T * d * 2 + M * 2 * I * 2 * 2 + M * I * 2
                            + M * (I // 128) * 4, 2 * M * d * I)
     b["dw_router"] = (M * (I // 128) * 4 + M * 12, 0)
+    b["scale_gather"] = (T * d * 2 + M * d * 2 + M * 8, M * d)
     b["bwd_down_wgrad"] = (acc * E * d * I * 4 + T * d * 2 + M * I * 2, 2 * M * d * I)
     b["bwd_gate_dgrad"] = (E * 2 * I * d * 2 + M * 2 * I * 2 + M * d * 2, 2 * M * 2 * I * d)
     b["bwd_gate_wgrad"] = (acc * E * 2 * I * d * 4 + M * 2 * I * 2 + M * d * 2, 2 * M * 2 * I * d)

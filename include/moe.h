@@ -132,9 +132,12 @@ int moe_quantize_weights(const moe_cfg* cfg, const void* w1, const void* w2, voi
  *   logits   fp32 [T, E]    out
  *   topk_idx int32 [T, k]   out
  *   topk_w   fp32 [T, k]    out
+ *   workspace bytes [ws_bytes]  scratch (the router weight widened to fp32), the same
+ *                               workspace the other calls take
  */
 int moe_route(const moe_cfg* cfg, const void* x, const void* w_router, float* logits,
-              int32_t* topk_idx, float* topk_w, moe_stream_t stream);
+              int32_t* topk_idx, float* topk_w, void* workspace, size_t ws_bytes,
+              moe_stream_t stream);
 
 /*
  * moe_permute - expert histogram, exclusive scan, and a stable grouping of the T*k rows by

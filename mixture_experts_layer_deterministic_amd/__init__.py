@@ -54,7 +54,7 @@ _I32 = ctypes.c_int32
 _SZ = ctypes.c_size_t
 _SIGS = {
     "moe_query": [ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeSizes)],
-    "moe_route": [ctypes.POINTER(MoeCfg), _P, _P, _P, _P, _P, _P],
+    "moe_route": [ctypes.POINTER(MoeCfg), _P, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_permute": [ctypes.POINTER(MoeCfg), _P, _P, _P, _SZ, _I32, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_forward": [ctypes.POINTER(MoeCfg), _P, _SZ, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P, _P,
                     _SZ, _P, _SZ, _P],
@@ -141,9 +141,10 @@ def moe_query(cfg: MoeCfg) -> MoeSizes:
     return out
 
 
-def moe_route(cfg, x, w_router, logits, topk_idx, topk_w, stream=None):
+def moe_route(cfg, x, w_router, logits, topk_idx, topk_w, workspace, stream=None):
     _check(lib().moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(logits),
-                           _ptr(topk_idx), _ptr(topk_w), _stream(stream)), "moe_route")
+                           _ptr(topk_idx), _ptr(topk_w), _ptr(workspace), _nbytes(workspace),
+                           _stream(stream)), "moe_route")
 
 
 def moe_permute(cfg, topk_idx, x, ring, slot, counts, offsets, row_src, tk_row, workspace,

@@ -20,7 +20,7 @@ struct Layout {
   bool mx;
   // workspace
   size_t status, sched, blk_cnt, blk_flag, rank, O, dH, dXp, dyw, dwpart, dl_pos, wg_count,
-      wg_table1, wg_table2, total;
+      wg_table1, wg_table2, wr32, total;
   // workspace, MXFP8 only: dY, A and dH quantised along their GEMM's K (codes, scales)
   size_t dyq, dys, aq, aqs, dhq, dhs;
   // saved
@@ -68,6 +68,7 @@ Layout layout(const moe_cfg* c) {
   L.wg_table2 = take(16 * wgrad_table_entries((int)Tk, c->E, c->d, c->I));
   L.dwpart = take(sizeof(float) * Tk * L.nIt);
   L.dl_pos = take(sizeof(float) * Tk);
+  L.wr32 = take(sizeof(float) * E * d);
   L.mx = c->precision == MOE_PREC_MXFP8;
   const size_t T = c->T, mxs = L.mx ? 1 : 0;
   L.dyq = take(mxs * T * d);
@@ -239,16 +240,19 @@ int moe_quantize_weights(const moe_cfg* cfg, const void* w1, const void* w2, voi
 }
 
 int moe_route(const moe_cfg* cfg, const void* x, const void* w_router, float* logits,
-              int32_t* topk_idx, float* topk_w, moe_stream_t stream) {
+              int32_t* topk_idx, float* topk_w, void* workspace, size_t ws_bytes,
+              moe_stream_t stream) {
   int st = check_mode(cfg);
   if (st) return st;
   if (!aligned16(x) || !aligned16(w_router) || !aligned4(logits) || !aligned4(topk_idx) ||
-      !aligned4(topk_w))
+      !aligned4(topk_w) || !aligned16(workspace))
     return MOE_ERR_INVALID_ARG;
+  const Layout Y = layout(cfg);
+  if (ws_bytes < Y.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Launches L;
   L(launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
-                         logits, cfg->T, cfg->d, cfg->E, s));
+                         at<float>(workspace, Y.wr32), logits, cfg->T, cfg->d, cfg->E, s));
   if (L.err == hipSuccess)
     L(launch_router_topk(logits, cfg->T, cfg->E, cfg->k, topk_idx, topk_w, s));
   return L.status();
@@ -405,9 +409,10 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
                       "wgrad_sched_gate"},
                      s));
   } else {
+    if (!L.err) L(launch_scale_gather(dyp, offsets, row_src, topk_w, E, k, d, Tk, dyw, s));
     if (!L.err)
-      L(launch_bwd_down_dgrad({dyp, row_src, topk_w, w2p, H, A, dH, dwpart, dyw, offsets, sched, d,
-                               I, k, Tk, E},
+      L(launch_bwd_down_dgrad({dyp, row_src, topk_w, w2p, H, A, dH, dwpart, offsets, sched, d, I,
+                               k, Tk, E},
                               pers, s));
     if (!L.err)
       L(launch_dw_router(dwpart, Y.nIt, tk_row, topk_w, cfg->T, k, d_topk_w, dl_pos, routed, s));

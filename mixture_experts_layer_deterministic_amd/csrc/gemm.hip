@@ -314,7 +314,6 @@ struct BwdDownDgrad {
     const uint16_t* A;       // [T*k, I]
     uint16_t* dH;            // [T*k, 2I]
     float* dwpart;           // [T*k, I / BN]
-    uint16_t* dyw;           // [T*k, d]: bf16(w dY[t]) in position order
     const int32_t* offsets;
     const int2* sched;
     int d, I, k;
@@ -334,52 +333,21 @@ struct BwdDownDgrad {
   static MOE_DEV int num_k(const Args& a, const Tile&) { return a.d / G::BK; }
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
-  // Every workgroup of an M-tile reads the same gathered dY rows. The one with N-tile index
-  // kt % (I / BN) also writes K-chunk kt of those rows, scaled by the routing weight and
-  // rounded to bf16, to dyw in position order, so the down wgrad reads contiguous rows.
   struct Loader {
-    using LA = LoadK<G::BM, G::BK, G::LDK>;
-    LA la;
+    LoadK<G::BM, G::BK, G::LDK> la;
     LoadMN<G::BN, G::BK, G::LDK, false> lb;
     const uint16_t* wb;
     int ldw;
-    uint16_t* yw[LA::PT];  // dyw row pointer (+ column) per loaded vector, or null
-    float wv[LA::PT];
-    int ntc, nidx;
     MOE_DEV void init(const Args& a, const Tile& t) {
       const uint16_t* dy = a.dy;
       const int32_t* rs = a.row_src;
       const int d = a.d, k = a.k, mc = t.m.mcount, row0 = t.m.row0;
       la.init([&](int m) { return m < mc ? dy + (size_t)(rs[row0 + m] / k) * d : nullptr; });
-#pragma unroll
-      for (int j = 0; j < LA::PT; ++j) {
-        const int v = threadIdx.x + kThreads * j;
-        const int m = v / LA::VPR;
-        const bool live = v < LA::NV && m < mc;
-        yw[j] = live ? a.dyw + (size_t)(row0 + m) * d + (v % LA::VPR) * 8 : nullptr;
-        wv[j] = live ? a.topk_w[rs[row0 + m]] : 0.f;
-      }
-      ntc = a.I / G::BN;
-      nidx = t.n0 / G::BN;
       wb = a.w2 + (size_t)t.m.e * a.d * a.I + t.n0;
       ldw = a.I;
     }
     MOE_DEV void load(int kt) {
       la.load(kt * G::BK);
-      if (kt % ntc == nidx) {
-#pragma unroll
-        for (int j = 0; j < LA::PT; ++j) {
-          if (!yw[j]) continue;
-          const uint4 v = la.r[j];
-          const float s = wv[j];
-          uint4 o;
-          o.x = pack_bf2(bf2f_lo(v.x) * s, bf2f_hi(v.x) * s);
-          o.y = pack_bf2(bf2f_lo(v.y) * s, bf2f_hi(v.y) * s);
-          o.z = pack_bf2(bf2f_lo(v.z) * s, bf2f_hi(v.z) * s);
-          o.w = pack_bf2(bf2f_lo(v.w) * s, bf2f_hi(v.w) * s);
-          *reinterpret_cast<uint4*>(yw[j] + kt * G::BK) = o;
-        }
-      }
       const uint16_t* w = wb;
       const int ld = ldw;
       lb.load(kt * G::BK, [&](int k) { return w + (size_t)k * ld; }, [](int) { return 1.0f; });
@@ -1213,8 +1181,8 @@ hipError_t launch_fwd_down(const GemmFwdDownArgs& x, bool persistent, hipStream_
 }
 
 hipError_t launch_bwd_down_dgrad(const GemmBwdDownDgradArgs& x, bool persistent, hipStream_t s) {
-  BwdDownDgrad::Args a{x.dy,     x.row_src, x.topk_w, x.w2, x.H, x.A, x.dH, x.dwpart,
-                       x.dyw,    x.offsets, x.sched,  x.d,  x.I, x.k};
+  BwdDownDgrad::Args a{x.dy, x.row_src, x.topk_w, x.w2, x.H, x.A, x.dH, x.dwpart,
+                       x.offsets, x.sched, x.d, x.I, x.k};
   return launch<BwdDownDgrad>(a, sched_max_mtiles(x.Tk, x.E) * (x.I / 128), persistent, s);
 }
 

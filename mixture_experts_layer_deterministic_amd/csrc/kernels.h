@@ -24,8 +24,9 @@ constexpr int kPermRows = 256;  // rows per histogram block of the permutation
 constexpr int kMaxTopK = 64;
 
 // router.hip
-hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, float* logits, int T,
-                                int d, int E, hipStream_t s);
+// w32: scratch of E * d floats for the router weight widened to fp32.
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, float* w32, float* logits,
+                                int T, int d, int E, hipStream_t s);
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                               hipStream_t s);
 
@@ -71,7 +72,6 @@ struct GemmBwdDownDgradArgs {
   const uint16_t* A;
   uint16_t* dH;
   float* dwpart;
-  uint16_t* dyw;  // [T*k, d]: bf16(w * dY[t]) in position order, for the down wgrad
   const int32_t* offsets;
   const int2* sched;
   int d, I, k, Tk, E;

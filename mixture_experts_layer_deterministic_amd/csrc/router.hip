@@ -8,55 +8,71 @@
 
 namespace moe {
 
-// One thread per expert (256 experts per workgroup), TT tokens per workgroup. For every
-// (token, expert) a single fp32 accumulator gains x[i] * w[i] for i = 0, 1, ..., d-1 in
-// ascending order with one rounding per step. The bf16 x bf16 products are exact in fp32, so
-// fma(x, w, acc) equals fl(acc + x * w). Tokens are staged in LDS as fp32 (read as lane-uniform
-// broadcasts); router rows are staged as bf16 with 16 bytes of padding per row, so the 64 lanes'
-// 16-byte reads of 64 different rows are bank-conflict free.
-template <int TT, int CH>
+// Logits: one lane per token, RE experts per wave, so a wave covers 64 tokens x RE experts.
+// For every (token, expert) a single fp32 accumulator gains x[i] * w[i] for i = 0, 1, ..., d-1
+// in ascending order with one rounding per step. The bf16 x bf16 products are exact in fp32, so
+// fma(x, w, acc) equals fl(acc + x * w). A lane streams its token's row with vector loads. The
+// router rows, widened to fp32 beforehand (exactly), are the same for the whole wave: they
+// arrive through scalar loads straight into FMA operands, and each x value feeds RE chains.
+constexpr int RE = 4;      // experts per wave
+constexpr int RSTEP = 32;  // hidden elements per step
+
+__global__ void __launch_bounds__(256) widen_router_kernel(const uint16_t* __restrict__ wr,
+                                                           float* __restrict__ w32, long long n) {
+  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  const uint2 v = *reinterpret_cast<const uint2*>(wr + i);
+  *reinterpret_cast<float4*>(w32 + i) =
+      make_float4(bf2f_lo(v.x), bf2f_hi(v.x), bf2f_lo(v.y), bf2f_hi(v.y));
+}
+
 __global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ wr,
+                                                            const float* __restrict__ w32,
                                                             float* __restrict__ logits, int T,
                                                             int d, int E) {
-  __shared__ float xs[TT][CH];
-  __shared__ __align__(16) uint16_t ws[256][CH + 8];
-  const int t0 = blockIdx.x * TT;
-  const int e0 = blockIdx.y * 256;
-  const int tid = threadIdx.x;
-  float acc[TT];
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int e0 = (blockIdx.y * 4 + wave) * RE;
+  if (e0 >= E) return;  // whole wave
+  const int t = blockIdx.x * kWave + lane;
+  const uint16_t* xr = x + (size_t)min(t, T - 1) * d;
+  const float* w0 = w32 + (size_t)e0 * d;
+  const int ecount = min(RE, E - e0);
+  float acc[RE];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.f;
-
-  for (int i0 = 0; i0 < d; i0 += CH) {
-    for (int v = tid; v < TT * CH; v += 256) {
-      const int tt = v / CH, ii = v % CH, t = t0 + tt;
-      xs[tt][ii] = t < T ? bf2f(x[(size_t)t * d + i0 + ii]) : 0.f;
-    }
-    for (int v = tid; v < 256 * (CH / 8); v += 256) {
-      const int row = v / (CH / 8), cv = v % (CH / 8), e = e0 + row;
-      const uint4 val = e < E ? *reinterpret_cast<const uint4*>(wr + (size_t)e * d + i0 + cv * 8)
-                              : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&ws[row][cv * 8]) = val;
-    }
-    __syncthreads();
-#pragma unroll 2
-    for (int ii = 0; ii < CH; ii += 8) {
-      const uint4 wv = *reinterpret_cast<const uint4*>(&ws[tid][ii]);
-      const float w8[8] = {bf2f_lo(wv.x), bf2f_hi(wv.x), bf2f_lo(wv.y), bf2f_hi(wv.y),
-                           bf2f_lo(wv.z), bf2f_hi(wv.z), bf2f_lo(wv.w), bf2f_hi(wv.w)};
+  for (int q = 0; q < RE; ++q) acc[q] = 0.f;
+  // the next step's row vectors are loaded while the current step computes
+  uint4 xn[RSTEP / 8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
+  for (int v = 0; v < RSTEP / 8; ++v) xn[v] = *reinterpret_cast<const uint4*>(xr + 8 * v);
+  for (int i0 = 0; i0 < d; i0 += RSTEP) {
+    float xv[RSTEP];
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) acc[tt] = __builtin_fmaf(xs[tt][ii + q], w8[q], acc[tt]);
+    for (int v = 0; v < RSTEP / 8; ++v) {
+      const uint32_t xw[4] = {xn[v].x, xn[v].y, xn[v].z, xn[v].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xv[8 * v + 2 * q] = bf2f_lo(xw[q]);
+        xv[8 * v + 2 * q + 1] = bf2f_hi(xw[q]);
+      }
     }
-    __syncthreads();
+    if (i0 + RSTEP < d) {
+#pragma unroll
+      for (int v = 0; v < RSTEP / 8; ++v)
+        xn[v] = *reinterpret_cast<const uint4*>(xr + i0 + RSTEP + 8 * v);
+    }
+#pragma unroll
+    for (int ee = 0; ee < RE; ++ee) {
+      if (ee >= ecount) break;  // wave-uniform
+      const float* wp = w0 + (size_t)ee * d + i0;
+#pragma unroll
+      for (int q = 0; q < RSTEP; ++q) acc[ee] = __builtin_fmaf(xv[q], wp[q], acc[ee]);
+    }
   }
-  const int e = e0 + tid;
-  if (e < E) {
+  if (t < T) {
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-      if (t0 + tt < T) logits[(size_t)(t0 + tt) * E + e] = acc[tt];
+    for (int ee = 0; ee < RE; ++ee)
+      if (ee < ecount) logits[(size_t)t * E + e0 + ee] = acc[ee];
   }
 }
 
@@ -118,14 +134,20 @@ __global__ void __launch_bounds__(256) router_topk_kernel(const float* __restric
   }
 }
 
-hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, float* logits, int T,
-                                int d, int E, hipStream_t s) {
-  constexpr int TT = 8, CH = 64;
-  dim3 grid((T + TT - 1) / TT, (E + 255) / 256);
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, float* w32, float* logits,
+                                int T, int d, int E, hipStream_t s) {
+  const long long n = (long long)E * d;
+  {
+    TraceScope trace("widen_router", s);
+    hipLaunchKernelGGL(widen_router_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
+                       wr, w32, n);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  dim3 grid((T + kWave - 1) / kWave, (E + 4 * RE - 1) / (4 * RE));
   {
     TraceScope trace("router_logits", s);
-    hipLaunchKernelGGL((router_logits_kernel<TT, CH>), grid, dim3(256), 0, s, x, wr, logits, T, d,
-                       E);
+    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, s, x, w32, logits, T, d, E);
   }
   return hipGetLastError();
 }

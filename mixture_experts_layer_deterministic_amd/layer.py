@@ -82,7 +82,8 @@ class MoeLayer:
 
     # steps ----------------------------------------------------------------------------------
     def route(self, x, w_router, stream=None):
-        moe_route(self.cfg, x, w_router, self.logits, self.topk_idx, self.topk_w, stream)
+        moe_route(self.cfg, x, w_router, self.logits, self.topk_idx, self.topk_w, self.workspace,
+                  stream)
 
     def set_routing(self, topk_idx, topk_w):
         self.topk_idx.copy_(topk_idx)

@@ -46,6 +46,9 @@ KERNELS = [
     (r"dw_router_kernel", "dw_router", "elementwise.hip"),
     (r"uncombine_kernel", "uncombine", "elementwise.hip"),
     (r"dwr_kernel", "dwr", "elementwise.hip"),
+    (r"scale_gather_kernel", "scale_gather", "mx.hip"),
+    (r"quant_rows_kernel", "quant_rows", "mx.hip"),
+    (r"quant_cols_t_kernel", "quant_cols_t", "mx.hip"),
 ]
 COMMON_SOURCES = ("common.h", "kernels.h")
 

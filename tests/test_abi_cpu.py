@@ -59,9 +59,11 @@ def test_entry_points_reject_bad_arguments_before_launching():
     p = _fake()
     null = None
     # null pointer
-    assert L.moe_route(ctypes.byref(cfg), null, p, p, p, p, None) == -1
+    assert L.moe_route(ctypes.byref(cfg), null, p, p, p, p, p, s.workspace, None) == -1
     # misaligned bf16 matrix
-    assert L.moe_route(ctypes.byref(cfg), _fake((1 << 20) + 2), p, p, p, p, None) == -1
+    assert L.moe_route(ctypes.byref(cfg), _fake((1 << 20) + 2), p, p, p, p, p, s.workspace,
+                       None) == -1
+    assert L.moe_route(ctypes.byref(cfg), p, p, p, p, p, p, s.workspace - 1, None) == -5
     # ring too small for the slot, and negative slot
     assert L.moe_permute(ctypes.byref(cfg), p, p, p, s.ring_slot - 1, 0, p, p, p, p, p,
                          s.workspace, None) == -2
@@ -76,7 +78,7 @@ def test_entry_points_reject_bad_arguments_before_launching():
                          s.saved - 1, p, s.workspace, None) == -5
     # an unknown precision is not provided by this build
     cfgx = m.make_cfg(64, 256, 8, 2, 128, 2)
-    assert L.moe_route(ctypes.byref(cfgx), p, p, p, p, p, None) == -3
+    assert L.moe_route(ctypes.byref(cfgx), p, p, p, p, p, p, s.workspace, None) == -3
     # MXFP8: the quantised weights are required, and sized
     cfg8 = m.make_cfg(64, 256, 8, 2, 128, m.MOE_PREC_MXFP8)
     s8 = m.moe_query(cfg8)
@@ -88,7 +90,7 @@ def test_entry_points_reject_bad_arguments_before_launching():
     assert L.moe_quantize_weights(ctypes.byref(cfg8), p, p, p, s8.wq - 1, None) == -5
     # unknown flag bits
     cfgf = m.make_cfg(64, 256, 8, 2, 128, 0, 8)
-    assert L.moe_route(ctypes.byref(cfgf), p, p, p, p, p, None) == -1
+    assert L.moe_route(ctypes.byref(cfgf), p, p, p, p, p, p, s.workspace, None) == -1
     # backward: bad dwr when the router weight is given
     assert L.moe_backward(ctypes.byref(cfg), p, s.ring_slot, 0, p, p, p, p, p, p, p, p, None, 0,
                           p, s.saved, p, p, p, p, null, p, 0, p, s.workspace, None) == -1
