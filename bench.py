@@ -26,40 +26,63 @@ sys.path.insert(0, ROOT)
 
 HBM_GBPS = 8000.0         # MI355X HBM3E, GB/s
 MFMA_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, TFLOP/s
+MFMA_FP8_TFLOPS = 5000.0   # dense fp8 MFMA (the MXFP8 scaled MFMA), TFLOP/s
 # fp32 FMA on the vector ALUs without packed-fp32 instructions (the library is built without
 # them): 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz. Packed fp32 would double it (157.3).
 VALU_FP32_TFLOPS = 78.6
-RIDGE_BF16 = MFMA_BF16_TFLOPS * 1e12 / (HBM_GBPS * 1e9)
 
 
-def algorithmic(cfg, routed=True, accumulate=False):
+def algorithmic(cfg, routed=True, accumulate=False, mx=False):
     """Algorithmic bytes and flops per launch of each kernel: what the method must move and
-    compute (each tensor read or written once, no padding, no re-reads). M = T*k rows."""
+    compute (each tensor read or written once, no padding, no re-reads). M = T*k rows.
+    In MXFP8 mode (`mx`) a quantised tensor of n elements is n code bytes plus n/32 scale
+    bytes, and the weights are read in the quantised copies."""
     T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
     M = T * k
     nb = (M + 255) // 256
     acc = 2 if accumulate else 1
+    q = lambda n: n + n // 32  # bytes of n MXFP8 elements with their scales
     b = {}
     if routed:
+        b["widen_router"] = (E * d * 2 + E * d * 4, 0)
         b["router_logits"] = (T * d * 2 + E * d * 2 + T * E * 4, 2 * T * d * E)
         b["router_topk"] = (T * E * 4 + T * k * 8, 0)
     b["perm_hist"] = (M * 8 + nb * E * 4, 0)
     b["perm_scan"] = (2 * nb * E * 4 + E * 8, 0)
-    b["perm_place"] = (T * d * 2 + M * d * 2 + M * 16, 0)
     b["sched_build"] = (E * 4, 0)
-    b["fwd_gateup"] = (E * 2 * I * d * 2 + M * d * 2 + M * 2 * I * 2 + M * I * 2, 2 * M * d * 2 * I)
-    b["fwd_down"] = (E * d * I * 2 + M * I * 2 + M * d * 2, 2 * M * I * d)
     b["combine"] = (M * d * 2 + T * d * 2 + M * 8, 2 * M * d)
-    b["bwd_down_dgrad"] = (E * d * I * 2 + T * d * 2 + M * 2 * I * 2 * 2 + M * I * 2
-                           + M * (I // 128) * 4, 2 * M * d * I)
     b["dw_router"] = (M * (I // 128) * 4 + M * 12, 0)
     b["scale_gather"] = (T * d * 2 + M * d * 2 + M * 8, M * d)
     b["bwd_down_wgrad"] = (acc * E * d * I * 4 + T * d * 2 + M * I * 2, 2 * M * d * I)
-    b["bwd_gate_dgrad"] = (E * 2 * I * d * 2 + M * 2 * I * 2 + M * d * 2, 2 * M * 2 * I * d)
-    b["bwd_gate_wgrad"] = (acc * E * 2 * I * d * 4 + M * 2 * I * 2 + M * d * 2, 2 * M * 2 * I * d)
     b["uncombine"] = (M * d * 2 + T * d * 2 + (E * d * 2 if routed else 0) + M * 8, M * d)
-    if routed:
-        b["dwr"] = (M * d * 2 + acc * E * d * 4 + M * 4, 2 * M * d)
+    if not mx:
+        b["perm_place"] = (T * d * 2 + M * d * 2 + M * 16, 0)
+        b["fwd_gateup"] = (E * 2 * I * d * 2 + M * d * 2 + M * 2 * I * 2 + M * I * 2,
+                           2 * M * d * 2 * I)
+        b["fwd_down"] = (E * d * I * 2 + M * I * 2 + M * d * 2, 2 * M * I * d)
+        b["bwd_down_dgrad"] = (E * d * I * 2 + T * d * 2 + M * 2 * I * 2 * 2 + M * I * 2
+                               + M * (I // 128) * 4, 2 * M * d * I)
+        b["bwd_gate_dgrad"] = (E * 2 * I * d * 2 + M * 2 * I * 2 + M * d * 2, 2 * M * 2 * I * d)
+        b["bwd_gate_wgrad"] = (acc * E * 2 * I * d * 4 + M * 2 * I * 2 + M * d * 2,
+                               2 * M * 2 * I * d)
+        if routed:
+            b["dwr"] = (M * d * 2 + acc * E * d * 4 + M * 4, 2 * M * d)
+    else:
+        # one pass per weight: read it once, write both quantised copies
+        b["quant_w1"] = (E * 2 * I * d * 2 + 2 * q(E * 2 * I * d), 0)
+        b["quant_w2"] = (E * d * I * 2 + 2 * q(E * d * I), 0)
+        b["perm_place"] = (T * d * 2 + q(M * d) + M * 16, 0)
+        b["fwd_gateup"] = (q(E * 2 * I * d) + q(M * d) + M * 2 * I * 2 + M * I * 2 + q(M * I),
+                           2 * M * d * 2 * I)
+        b["fwd_down"] = (q(E * d * I) + q(M * I) + M * d * 2, 2 * M * I * d)
+        b["quant_dy"] = (T * d * 2 + q(T * d), 0)
+        b["bwd_down_dgrad"] = (q(E * d * I) + q(T * d) + M * 2 * I * 2 + M * I * 2
+                               + M * 2 * I * 2 + q(M * 2 * I) + M * (I // 128) * 4, 2 * M * d * I)
+        b["bwd_gate_dgrad"] = (q(E * 2 * I * d) + q(M * 2 * I) + M * d * 2, 2 * M * 2 * I * d)
+        b["bwd_gate_wgrad"] = (acc * E * 2 * I * d * 4 + M * 2 * I * 2 + q(M * d),
+                               2 * M * 2 * I * d)
+        if routed:
+            b["dwr"] = (q(M * d) + acc * E * d * 4 + M * 4, 2 * M * d)
     return b
 
 
@@ -67,17 +90,27 @@ GEMMS = ("fwd_gateup", "fwd_down", "bwd_down_dgrad", "bwd_down_wgrad", "bwd_gate
          "bwd_gate_wgrad")
 
 
-def kernel_roofline(name, nbytes, flops, us):
+MX_GEMMS = ("fwd_gateup", "fwd_down", "bwd_down_dgrad", "bwd_gate_dgrad")  # scaled fp8 MFMA
+
+
+def mfma_peak(name, mx):
+    """Dense MFMA peak of a GEMM kernel: fp8 for the MXFP8 scaled-MFMA GEMMs, else bf16 (the
+    weight-gradient GEMMs run bf16 MFMA in both modes)."""
+    return MFMA_FP8_TFLOPS if mx and name in MX_GEMMS else MFMA_BF16_TFLOPS
+
+
+def kernel_roofline(name, nbytes, flops, us, mx=False):
     """Achieved rate against the roofline that bounds the kernel."""
     s = us * 1e-6
     if name == "router_logits":
         ach = flops / s / 1e12
         return {"bound": "alu", "achieved": ach, "peak": VALU_FP32_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / VALU_FP32_TFLOPS}
-    if flops and flops / nbytes > RIDGE_BF16 and name in GEMMS:
+    peak = mfma_peak(name, mx)
+    if flops and name in GEMMS and flops / nbytes > peak * 1e12 / (HBM_GBPS * 1e9):
         ach = flops / s / 1e12
-        return {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / MFMA_BF16_TFLOPS}
+        return {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                "frac": ach / peak}
     ach = nbytes / s / 1e9
     return {"bound": "hbm", "achieved": ach, "peak": HBM_GBPS, "unit": "GB/s",
             "frac": ach / HBM_GBPS}
@@ -145,6 +178,8 @@ def main():
     ap.add_argument("--persistent", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="skip per-kernel events")
+    ap.add_argument("--no-mxfp8", action="store_true",
+                    help="skip the MXFP8-mode run on the same inputs")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB, a known-size "
                          "reference for HBM byte counters")
@@ -176,15 +211,8 @@ def main():
     inp = workload.make_inputs(args.workload, seed=args.seed, device=dev)
     T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
     routed = "Wr" in inp
-    L = MoeLayer(T, d, E, k, I, device=dev, persistent=args.persistent)
-    wr = inp.get("Wr")
-    if not routed:
-        L.set_routing(inp["topk_idx"], inp["topk_w"])
-    X, W1, W2, dY = inp["X"], inp["W1"], inp["W2"], inp["dY"]
+    mx = cfg["precision"] == "mxfp8"
     stream = torch.cuda.current_stream()
-
-    def step():
-        L.step(X, wr, W1, W2, dY, stream=stream)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
@@ -194,7 +222,111 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    print("[bench] warmup", file=sys.stderr, flush=True)
+
+    main_run = run_layer(m, MoeLayer, inp, cfg, stream, args, mx=mx)
+    ms, kernels = main_run["ms"], main_run["kernels"]
+    # in MXFP8 mode a step also re-quantises the weights (they change every optimizer step)
+    tokens_per_s = T / (ms * 1e-3)
+
+    dominant = max(kernels, key=lambda n: kernels[n]["us"] * kernels[n]["launches_per_step"]) \
+        if kernels else None
+    roof = None
+    if dominant:
+        kd = kernels[dominant]
+        roof = {"kernel": dominant, "bound": kd["bound"], "achieved": kd["achieved"],
+                "peak": kd["peak"], "unit": kd["unit"], "frac": kd["frac"],
+                "traffic": measured_traffic(args.workload, dominant),
+                "alg_bytes": kd["alg_bytes"], "us_per_launch": kd["us"]}
+    pc = {}
+    for n in ("perm_place", "combine"):
+        if n in kernels:
+            pc[n] = {"GB/s": kernels[n].get("achieved"), "frac_hbm": kernels[n].get("frac")}
+
+    # The same layer in MXFP8 mode on the same inputs: the second precision the metric names.
+    mx_line = None
+    if not mx and not args.no_mxfp8 and routed:
+        print("[bench] MXFP8 mode on the same inputs", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        r = run_layer(m, MoeLayer, inp, cfg, stream, args, mx=True)
+        mx_line = {"tokens_per_s": round(T / (r["ms"] * 1e-3), 1),
+                   "ms_per_step": round(r["ms"], 4),
+                   "weight_quantize_ms": round(r["quant_ms"], 4),
+                   "layer_ms_without_weight_quantize": round(r["ms"] - r["quant_ms"], 4),
+                   "grouped_gemm": r["gemm"], "kernels": r["kernels"]}
+        torch.cuda.empty_cache()
+
+    # practical HBM ceiling: one plain 2 GiB device copy (read + write), best of 3. Skipped in
+    # counter runs, where the only device copy must be the calibration copy.
+    n = 2 << 30
+    hbm_copy = None
+    if not args.calib_copy_mib:
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        best = None
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            dst.copy_(src)
+            b.record(stream)
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b)
+            best = t if best is None else min(best, t)
+        hbm_copy = round(2 * n / (best * 1e-3) / 1e9, 1)
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline and not mx:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp, cfg)
+
+    line = {
+        "metric": "MoE layer fwd+bwd tokens/s",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8-e4m3/bf16" if mx else "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "d": d, "E": E, "k": k, "I": I,
+                   "precision": cfg["precision"], "weight_grad_dtype": "fp32",
+                   "persistent": bool(args.persistent), "seed": args.seed},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "grouped_gemm": main_run["gemm"],
+        "permute_combine": pc,
+        "mxfp8": mx_line,
+        "hbm_copy": {"GB/s": hbm_copy, "bytes": 2 * n, "what": "one plain device copy, read + write"},
+        "kernels": kernels,
+        "host_seconds_timed": round(main_run["t_host"], 4),
+    }
+    print(json.dumps(line))
+
+
+def run_layer(m, MoeLayer, inp, cfg, stream, args, mx):
+    """Warm up and time `args.steps` layer steps; per-kernel times from the library's own
+    events on the layer's stream. In MXFP8 mode each step first quantises the weights."""
+    import torch
+    T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
+    dev = inp["X"].device
+    routed = "Wr" in inp
+    prec = m.MOE_PREC_MXFP8 if mx else m.MOE_PREC_BF16
+    L = MoeLayer(T, d, E, k, I, device=dev, persistent=args.persistent, precision=prec)
+    wr = inp.get("Wr")
+    if not routed:
+        L.set_routing(inp["topk_idx"], inp["topk_w"])
+    X, W1, W2, dY = inp["X"], inp["W1"], inp["W2"], inp["dY"]
+
+    def step():
+        if mx:
+            L.quantize_weights(W1, W2, stream)
+        L.step(X, wr, W1, W2, dY, stream=stream)
+
+    print(f"[bench] warmup ({'mxfp8' if mx else 'bf16'})", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -237,9 +369,8 @@ def main():
     if ev:
         m.moe_trace_end()
     ms = start.elapsed_time(end) / args.steps
-    tokens_per_s = T / (ms * 1e-3)
 
-    alg = algorithmic(cfg, routed=routed)
+    alg = algorithmic(cfg, routed=routed, mx=mx)
     kernels = {}
     if ev:
         tot = {}
@@ -251,82 +382,31 @@ def main():
         for n in tot:
             us = tot[n] / cnt[n]
             nbytes, flops = alg.get(n, (0, 0))
-            r = kernel_roofline(n, nbytes, flops, us) if nbytes else {}
+            r = kernel_roofline(n, nbytes, flops, us, mx) if nbytes else {}
             kernels[n] = {"us": round(us, 2), "launches_per_step": cnt[n] // args.steps,
                           "alg_bytes": nbytes, "alg_flops": flops,
                           **{kk: (round(v, 4) if isinstance(v, float) else v)
                              for kk, v in r.items()}}
-    dominant = max(kernels, key=lambda n: kernels[n]["us"] * kernels[n]["launches_per_step"]) \
-        if kernels else None
-    roof = None
-    if dominant:
-        kd = kernels[dominant]
-        roof = {"kernel": dominant, "bound": kd["bound"], "achieved": kd["achieved"],
-                "peak": kd["peak"], "unit": kd["unit"], "frac": kd["frac"],
-                "traffic": measured_traffic(args.workload, dominant),
-                "alg_bytes": kd["alg_bytes"], "us_per_launch": kd["us"]}
-    gemm_us = sum(kernels[g]["us"] for g in GEMMS if g in kernels)
-    gemm_flops = sum(alg[g][1] for g in GEMMS)
-    gemm_bytes = sum(alg[g][0] for g in GEMMS)
+    quant_ms = sum(kernels[n]["us"] for n in kernels if n.startswith("quant_w")) / 1e3
     gemm = None
+    gemm_us = sum(kernels[g]["us"] for g in GEMMS if g in kernels)
     if gemm_us:
-        tf = gemm_flops / (gemm_us * 1e-6) / 1e12
-        attainable = min(MFMA_BF16_TFLOPS, HBM_GBPS * 1e9 * gemm_flops / gemm_bytes / 1e12)
-        gemm = {"tflops": round(tf, 2), "frac_mfma_peak": round(tf / MFMA_BF16_TFLOPS, 4),
+        flops = sum(alg[g][1] for g in GEMMS)
+        nbytes = sum(alg[g][0] for g in GEMMS)
+        # the time-weighted MFMA peak of the six GEMMs at their own dtypes
+        peak = sum(kernels[g]["us"] * mfma_peak(g, mx) for g in GEMMS if g in kernels) / gemm_us
+        tf = flops / (gemm_us * 1e-6) / 1e12
+        attainable = sum(
+            kernels[g]["us"] * min(mfma_peak(g, mx), HBM_GBPS * 1e9 * alg[g][1] / alg[g][0] / 1e12)
+            for g in GEMMS if g in kernels) / gemm_us
+        gemm = {"tflops": round(tf, 2), "mfma_peak_tflops": round(peak, 1),
+                "frac_mfma_peak": round(tf / peak, 4),
                 "attainable_tflops": round(attainable, 2),
                 "frac_attainable": round(tf / attainable, 4),
+                "alg_bytes": nbytes, "hbm_gbps": round(nbytes / (gemm_us * 1e-6) / 1e9, 1),
                 "share_of_step": round(gemm_us / 1e3 / ms, 4)}
-    pc = {}
-    for n in ("perm_place", "combine"):
-        if n in kernels:
-            pc[n] = {"GB/s": kernels[n].get("achieved"), "frac_hbm": kernels[n].get("frac")}
-
-    # practical HBM ceiling: one plain 2 GiB device copy (read + write), best of 3
-    n = 2 << 30
-    src = torch.empty(n, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    best = None
-    for _ in range(3):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        dst.copy_(src)
-        b.record(stream)
-        torch.cuda.synchronize()
-        t = a.elapsed_time(b)
-        best = t if best is None else min(best, t)
-    hbm_copy = round(2 * n / (best * 1e-3) / 1e9, 1)
-    del src, dst
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(inp, cfg)
-
-    line = {
-        "metric": "MoE layer fwd+bwd tokens/s",
-        "value": round(tokens_per_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": args.workload, "T": T, "d": d, "E": E, "k": k, "I": I,
-                   "weight_grad_dtype": "fp32", "persistent": bool(args.persistent),
-                   "seed": args.seed},
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "grouped_gemm": gemm,
-        "permute_combine": pc,
-        "hbm_copy": {"GB/s": hbm_copy, "bytes": 2 * n, "what": "one plain device copy, read + write"},
-        "kernels": kernels,
-        "host_seconds_timed": round(t_host, 4),
-    }
-    print(json.dumps(line))
+    del L
+    return {"ms": ms, "kernels": kernels, "gemm": gemm, "quant_ms": quant_ms, "t_host": t_host}
 
 
 if __name__ == "__main__":

@@ -225,17 +225,11 @@ int moe_quantize_weights(const moe_cfg* cfg, const void* w1, const void* w2, voi
   const uint16_t* a1 = static_cast<const uint16_t*>(w1);
   const uint16_t* a2 = static_cast<const uint16_t*>(w2);
   Launches L;
-  L(launch_quant_rows(a1, (long long)E * 2 * I, d, at<uint8_t>(wq, Y.w1f), at<uint8_t>(wq, Y.w1fs),
-                      "quant_w1_fwd", s));
+  L(launch_quant_weight(a1, E, 2 * I, d, at<uint8_t>(wq, Y.w1f), at<uint8_t>(wq, Y.w1fs),
+                        at<uint8_t>(wq, Y.w1b), at<uint8_t>(wq, Y.w1bs), "quant_w1", s));
   if (!L.err)
-    L(launch_quant_rows(a2, (long long)E * d, I, at<uint8_t>(wq, Y.w2f), at<uint8_t>(wq, Y.w2fs),
-                        "quant_w2_fwd", s));
-  if (!L.err)
-    L(launch_quant_cols_t(a2, E, d, I, at<uint8_t>(wq, Y.w2b), at<uint8_t>(wq, Y.w2bs),
-                          "quant_w2_bwd", s));
-  if (!L.err)
-    L(launch_quant_cols_t(a1, E, 2 * I, d, at<uint8_t>(wq, Y.w1b), at<uint8_t>(wq, Y.w1bs),
-                          "quant_w1_bwd", s));
+    L(launch_quant_weight(a2, E, d, I, at<uint8_t>(wq, Y.w2f), at<uint8_t>(wq, Y.w2fs),
+                          at<uint8_t>(wq, Y.w2b), at<uint8_t>(wq, Y.w2bs), "quant_w2", s));
   return L.status();
 }
 

@@ -168,8 +168,10 @@ hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
 // mx.hip
 hipError_t launch_quant_rows(const uint16_t* src, long long rows, int cols, uint8_t* dst,
                              uint8_t* sc, const char* name, hipStream_t s);
-hipError_t launch_quant_cols_t(const uint16_t* src, int B, int R, int C, uint8_t* dst,
-                               uint8_t* sc, const char* name, hipStream_t s);
+// Both MXFP8 copies of src [B][R][C]: along C into (dq, dqs), along R transposed into (tq, tqs).
+hipError_t launch_quant_weight(const uint16_t* src, int B, int R, int C, uint8_t* dq,
+                               uint8_t* dqs, uint8_t* tq, uint8_t* tqs, const char* name,
+                               hipStream_t s);
 hipError_t launch_scale_gather(const uint16_t* dy, const int32_t* offsets, const int32_t* row_src,
                                const float* topk_w, int E, int k, int d, int Tk, uint16_t* dyw,
                                hipStream_t s);

@@ -43,46 +43,94 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restr
   }
 }
 
-// src [B][R][C] bf16 quantised along R (blocks of 32 rows per column) and written transposed:
-// dst [B][C][R] fp8, sc [B][C][R/32]. One workgroup of 128 threads per 32 x 128 tile; thread c
-// owns column c of the tile and writes its 32 codes contiguously.
-__global__ void __launch_bounds__(128) quant_cols_t_kernel(const uint16_t* __restrict__ src,
-                                                           uint8_t* __restrict__ dst,
-                                                           uint8_t* __restrict__ sc, int R,
+// Both MXFP8 copies of a weight src [B][R][C] bf16 in one pass over it:
+//  * along C (the forward GEMM's reduction axis): dq [B][R][C] codes, dqs [B][R][C/32] scales;
+//  * along R, transposed (the dgrad's reduction axis): tq [B][C][R] codes, tqs [B][C][R/32].
+// One workgroup of 256 threads per 128 x 128 tile (R and C are multiples of 128). The tile is
+// read once: each row's 32-blocks are quantised from registers as they arrive, and the tile goes
+// to LDS, where wave w quantises rows [32 w, 32 w + 32) of every column. The column codes are
+// staged in LDS so that each column's 128 codes leave as 128 contiguous bytes.
+constexpr int kQT = 128;
+__global__ void __launch_bounds__(256) quant_weight_kernel(const uint16_t* __restrict__ src,
+                                                           uint8_t* __restrict__ dq,
+                                                           uint8_t* __restrict__ dqs,
+                                                           uint8_t* __restrict__ tq,
+                                                           uint8_t* __restrict__ tqs, int R,
                                                            int C) {
-  __shared__ uint16_t tile[32][128 + 2];
-  const int b = blockIdx.z, r0 = blockIdx.y * 32, c0 = blockIdx.x * 128;
+  __shared__ uint32_t tile[kQT][kQT / 2 + 1];  // bf16 pairs, row-major, padded pitch
+  __shared__ uint32_t outT[kQT][kQT / 4 + 1];  // codes of column c along R, padded pitch
+  __shared__ uint32_t scT[kQT];                // the column's four scale codes, one per byte
+  const int b = blockIdx.z, r0 = blockIdx.y * kQT, c0 = blockIdx.x * kQT;
+  const int t = threadIdx.x;
   const uint16_t* s = src + ((size_t)b * R + r0) * C + c0;
-  for (int i = threadIdx.x; i < 32 * 16; i += 128) {  // 32 rows x 16 vectors of 8
-    const int r = i / 16, cv = i % 16;
+  // Phase 1: sixteen lanes per row, eight elements per lane; lanes 4q..4q+3 make one 32-block.
+  const int cv = t % 16;
+#pragma unroll
+  for (int j = 0; j < kQT / 16; ++j) {
+    const int r = t / 16 + 16 * j;
     const uint4 x = *reinterpret_cast<const uint4*>(s + (size_t)r * C + cv * 8);
+    tile[r][cv * 4 + 0] = x.x;
+    tile[r][cv * 4 + 1] = x.y;
+    tile[r][cv * 4 + 2] = x.z;
+    tile[r][cv * 4 + 3] = x.w;
     const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+    float f[8];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      tile[r][cv * 8 + 2 * q] = static_cast<uint16_t>(xw[q] & 0xffffu);
-      tile[r][cv * 8 + 2 * q + 1] = static_cast<uint16_t>(xw[q] >> 16);
+      f[2 * q] = bf2f_lo(xw[q]);
+      f[2 * q + 1] = bf2f_hi(xw[q]);
     }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const uint32_t code = mx_scale_code(amax);
+    const float inv = mx_inv_scale(code);
+    uint2 o;
+    o.x = e4m3x2(f[0] * inv, f[1] * inv) | (e4m3x2(f[2] * inv, f[3] * inv) << 16);
+    o.y = e4m3x2(f[4] * inv, f[5] * inv) | (e4m3x2(f[6] * inv, f[7] * inv) << 16);
+    const size_t row = (size_t)b * R + r0 + r;
+    *reinterpret_cast<uint2*>(dq + row * C + c0 + cv * 8) = o;
+    if ((cv & 3) == 0) dqs[row * (C / 32) + (c0 + cv * 8) / 32] = static_cast<uint8_t>(code);
   }
   __syncthreads();
-  const int c = threadIdx.x;
-  float f[32];
-  float amax = 0.f;
+  // Phase 2: wave w takes rows [32 w, 32 w + 32); lane l the column pair (2 l, 2 l + 1).
+  {
+    const int w = t / kWave, l = t % kWave;
+    float lo[32], hi[32];
+    float alo = 0.f, ahi = 0.f;
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    f[r] = bf2f(tile[r][c]);
-    amax = fmaxf(amax, fabsf(f[r]));
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t v = tile[w * 32 + i][l];
+      lo[i] = bf2f_lo(v);
+      hi[i] = bf2f_hi(v);
+      alo = fmaxf(alo, fabsf(lo[i]));
+      ahi = fmaxf(ahi, fabsf(hi[i]));
+    }
+    const uint32_t clo = mx_scale_code(alo), chi = mx_scale_code(ahi);
+    const float ilo = mx_inv_scale(clo), ihi = mx_inv_scale(chi);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      outT[2 * l][w * 8 + q] = e4m3x2(lo[4 * q] * ilo, lo[4 * q + 1] * ilo) |
+                               (e4m3x2(lo[4 * q + 2] * ilo, lo[4 * q + 3] * ilo) << 16);
+      outT[2 * l + 1][w * 8 + q] = e4m3x2(hi[4 * q] * ihi, hi[4 * q + 1] * ihi) |
+                                   (e4m3x2(hi[4 * q + 2] * ihi, hi[4 * q + 3] * ihi) << 16);
+    }
+    reinterpret_cast<uint8_t*>(scT)[(2 * l) * 4 + w] = static_cast<uint8_t>(clo);
+    reinterpret_cast<uint8_t*>(scT)[(2 * l + 1) * 4 + w] = static_cast<uint8_t>(chi);
   }
-  const uint32_t code = mx_scale_code(amax);
-  const float inv = mx_inv_scale(code);
-  uint32_t w[8];
+  __syncthreads();
+  // Phase 3: each column's 128 codes as eight 16-byte stores, and its four scales as one word.
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
-    w[q] = e4m3x2(f[4 * q] * inv, f[4 * q + 1] * inv) |
-           (e4m3x2(f[4 * q + 2] * inv, f[4 * q + 3] * inv) << 16);
-  uint8_t* d = dst + ((size_t)b * C + c0 + c) * R + r0;
-  reinterpret_cast<uint4*>(d)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-  reinterpret_cast<uint4*>(d)[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  sc[((size_t)b * C + c0 + c) * (R / 32) + r0 / 32] = static_cast<uint8_t>(code);
+  for (int j = 0; j < kQT * 8 / 256; ++j) {
+    const int idx = t + 256 * j, c = idx / 8, part = idx % 8;
+    const uint4 v = make_uint4(outT[c][part * 4], outT[c][part * 4 + 1], outT[c][part * 4 + 2],
+                               outT[c][part * 4 + 3]);
+    *reinterpret_cast<uint4*>(tq + ((size_t)b * C + c0 + c) * R + r0 + part * 16) = v;
+  }
+  if (t < kQT)
+    *reinterpret_cast<uint32_t*>(tqs + ((size_t)b * C + c0 + t) * (R / 32) + r0 / 32) = scT[t];
 }
 
 // dyw[pos] = bf16(w[row_src[pos]] * dy[row_src[pos] / k]): the down wgrad's left operand in
@@ -123,12 +171,15 @@ hipError_t launch_quant_rows(const uint16_t* src, long long rows, int cols, uint
   return hipGetLastError();
 }
 
-hipError_t launch_quant_cols_t(const uint16_t* src, int B, int R, int C, uint8_t* dst,
-                               uint8_t* sc, const char* name, hipStream_t s) {
+hipError_t launch_quant_weight(const uint16_t* src, int B, int R, int C, uint8_t* dq,
+                               uint8_t* dqs, uint8_t* tq, uint8_t* tqs, const char* name,
+                               hipStream_t s) {
+  if (R % kQT != 0 || C % kQT != 0) return hipErrorInvalidValue;
+  if (B == 0) return hipSuccess;
   {
     TraceScope trace(name, s);
-    hipLaunchKernelGGL(quant_cols_t_kernel, dim3(C / 128, R / 32, B), dim3(128), 0, s, src, dst,
-                       sc, R, C);
+    hipLaunchKernelGGL(quant_weight_kernel, dim3(C / kQT, R / kQT, B), dim3(256), 0, s, src, dq,
+                       dqs, tq, tqs, R, C);
   }
   return hipGetLastError();
 }

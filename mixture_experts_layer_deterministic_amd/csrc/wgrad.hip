@@ -65,8 +65,9 @@ struct Mover {
   int ld;                // row pitch of the operand (elements)
   uint4 r[NH][4];
 
-  // FP8: the operand is MXFP8 (E4M3 codes with one scale per 32 along the row); each element
-  // is expanded to its exact bf16 value.
+  // FP8: the operand is MXFP8 (E4M3 codes with one scale per 32 along the row). The load keeps
+  // the raw codes (x, y) and the scale code (z) of each 8-column piece; `store` expands them to
+  // their exact bf16 values, so the conversion waits for data only when the chunk is written.
   template <bool FP8 = false>
   MOE_DEV void load(int pbase, int p1, int col0, int lane) {
 #pragma unroll
@@ -83,29 +84,40 @@ struct Mover {
           if (p < p1) {
             const int c = col0 + mb * 8;
             const uint2 q = *reinterpret_cast<const uint2*>(base8 + (size_t)p * ld + c);
-            const float s = mx_scale(sc8[(size_t)p * (ld / 32) + c / 32]);
-            float f[4], g[4];
-            e4m3x4_to_f32(q.x, f);
-            e4m3x4_to_f32(q.y, g);
-            v.x = pack_bf2(f[0] * s, f[1] * s);
-            v.y = pack_bf2(f[2] * s, f[3] * s);
-            v.z = pack_bf2(g[0] * s, g[1] * s);
-            v.w = pack_bf2(g[2] * s, g[3] * s);
+            v.x = q.x;
+            v.y = q.y;
+            v.z = sc8[(size_t)p * (ld / 32) + c / 32];
           }
           r[h][rr] = v;
         }
       }
     }
   }
+  static MOE_DEV uint4 expand_fp8(const uint4 raw) {
+    const float s = mx_scale(raw.z);
+    float f[4], g[4];
+    e4m3x4_to_f32(raw.x, f);
+    e4m3x4_to_f32(raw.y, g);
+    uint4 v;
+    v.x = pack_bf2(f[0] * s, f[1] * s);
+    v.y = pack_bf2(f[2] * s, f[3] * s);
+    v.z = pack_bf2(g[0] * s, g[1] * s);
+    v.w = pack_bf2(g[2] * s, g[3] * s);
+    return v;
+  }
   // Writes the transposed blocks into an LDS buffer [MN][ldk] at K column kcol.
+  template <bool FP8 = false>
   MOE_DEV void store(uint16_t* s, int ldk, int kcol, int lane) const {
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const int b = lane + kWave * h, kq = b % 8, mb = b / 8;
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[h][0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[h][1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[h][2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[h][3]);
+      uint4 e[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) e[rr] = FP8 ? expand_fp8(r[h][rr]) : r[h][rr];
+      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&e[0]);
+      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&e[1]);
+      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&e[2]);
+      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&e[3]);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int q = c >> 1;
@@ -229,7 +241,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
         mr.load<R8>(pb, p1, nfirst + (pq / nk) * BN, lane);
         if (!resident) ml.load(pb, p1, 0, lane);
         if (pq == 0) {
-          mr.store(rbuf, LDR, 0, lane);
+          mr.store<R8>(rbuf, LDR, 0, lane);
           if (!resident) ml.store(lbuf, LDL, 0, lane);
         }
       }
@@ -237,7 +249,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
       for (int it = 0; it < total; ++it) {
         const int c = it + 1;
         if (c < total && c % kProducers == pq) {  // its loads were issued kProducers - 1 ago
-          mr.store(rbuf + (c & 1) * R_STAGE, LDR, 0, lane);
+          mr.store<R8>(rbuf + (c & 1) * R_STAGE, LDR, 0, lane);
           if (!resident) ml.store(lbuf, LDL, (c & 1) * BK, lane);
         }
         const int cn = it + kProducers;

@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 output for the MoE layer's kernels.
 
-Usage (after a kernel-trace run and two counter runs of bench.py):
+Usage, after one kernel-trace run and two counter runs (FETCH_SIZE, then WRITE_SIZE) of bench.py:
     python -m mixture_experts_layer_deterministic_amd.profsum \
         --stats DIR/run_kernel_stats.csv --fetch DIR/run_counter_collection.csv \
         --write DIR/run_counter_collection.csv --calib-mib 1024 \
@@ -29,6 +29,7 @@ CSRC = os.path.join(HERE, "csrc")
 
 # rocprofv3 kernel-name pattern -> (bench name, source file)
 KERNELS = [
+    (r"widen_router_kernel", "widen_router", "router.hip"),
     (r"router_logits_kernel", "router_logits", "router.hip"),
     (r"router_topk_kernel", "router_topk", "router.hip"),
     (r"perm_hist_kernel", "perm_hist", "permute.hip"),
@@ -40,15 +41,19 @@ KERNELS = [
     (r"gg_kernel<moe::FwdDown", "fwd_down", "gemm.hip"),
     (r"gg_kernel<moe::BwdDownDgrad", "bwd_down_dgrad", "gemm.hip"),
     (r"gg_kernel<moe::BwdGateDgrad", "bwd_gate_dgrad", "gemm.hip"),
-    (r"wgrad_kernel<(true|false), false>", "bwd_down_wgrad", "wgrad.hip"),
-    (r"wgrad_kernel<(true|false), true>", "bwd_gate_wgrad", "wgrad.hip"),
+    (r"gg_kernel<moe::MxFwdGateUp", "fwd_gateup", "gemm.hip"),
+    (r"gg_kernel<moe::MxFwdDown", "fwd_down", "gemm.hip"),
+    (r"gg_kernel<moe::MxBwdDownDgrad", "bwd_down_dgrad", "gemm.hip"),
+    (r"gg_kernel<moe::MxBwdGateDgrad", "bwd_gate_dgrad", "gemm.hip"),
+    (r"wgrad_kernel<(true|false), false", "bwd_down_wgrad", "wgrad.hip"),
+    (r"wgrad_kernel<(true|false), true", "bwd_gate_wgrad", "wgrad.hip"),
     (r"moe::combine_kernel", "combine", "elementwise.hip"),
     (r"dw_router_kernel", "dw_router", "elementwise.hip"),
     (r"uncombine_kernel", "uncombine", "elementwise.hip"),
     (r"dwr_kernel", "dwr", "elementwise.hip"),
     (r"scale_gather_kernel", "scale_gather", "mx.hip"),
     (r"quant_rows_kernel", "quant_rows", "mx.hip"),
-    (r"quant_cols_t_kernel", "quant_cols_t", "mx.hip"),
+    (r"quant_weight_kernel", "quant_weight", "mx.hip"),
 ]
 COMMON_SOURCES = ("common.h", "kernels.h")
 
@@ -72,11 +77,13 @@ def source_hash(src: str) -> str:
 
 
 def _counter_per_kernel(path, calib_bytes):
-    rows = list(csv.DictReader(open(path)))
-    copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+    # the calibration copy is the last device copy before the layer's first kernel
+    first = next((i for i, r in enumerate(rows) if bench_name(r["Kernel_Name"])), len(rows))
+    copies = [float(r["Counter_Value"]) for r in rows[:first] if "copyBuffer" in r["Kernel_Name"]]
     if not copies:
         raise SystemExit(f"{path}: no calibration copy found")
-    scale = calib_bytes / (max(copies) * 1024.0)  # bytes per counted byte
+    scale = calib_bytes / (copies[-1] * 1024.0)  # bytes per counted byte
     out = {}
     for r in rows:
         bn = bench_name(r["Kernel_Name"])
