@@ -8,18 +8,20 @@
 //
 // Both operands are position-major in memory (K is the slow axis), and the output is the big
 // tensor: with tens of positions per expert the kernel is bound by writing dW. It is a
-// persistent grid that walks a device-built task table. Each task is one 128-row stripe of
-// one expert's dW and a run of consecutive 128-column tiles. Inside a task the
-// double-buffered pipeline runs on across tile boundaries. The table orders experts by
+// persistent grid that walks a device-built task table. Each task is one 256-row stripe of
+// one expert's dW and a run of consecutive 128-column tiles; the stripe's L rows are loaded
+// once per task and shared by all its tiles, which halves the R traffic of 128-row stripes.
+// Inside a task the pipeline runs on across tile boundaries. The table orders experts by
 // decreasing row count (ties to the lower index), so the longest tasks start first. Each task
 // holds roughly the same number of K-steps: an expert with few rows gets long runs of tiles, a
 // heavy expert runs of one tile.
 //
 // The waves are specialised. On gfx950 a wave's vector-memory counter covers its loads and
 // stores in issue order, so a wave that stores a 64 KB dW tile and then waits for its next
-// operand load also waits for those stores to land. Here four consumer waves run the MFMAs and
-// store dW, and never load; two producer waves only load the operands into LDS. The two sides
-// meet at a barrier that waits for LDS traffic only, so stores of many tiles stay in flight.
+// operand load also waits for those stores to land. Here eight consumer waves (one 64 x 64 block
+// of the 256 x 128 tile each) run the MFMAs and store dW, and never load; four producer waves
+// only load the operands into LDS. The two sides meet at a barrier that waits for LDS traffic
+// only, so stores of many tiles stay in flight.
 //
 // Determinism: every dW element belongs to exactly one task, whose workgroup reduces K in
 // ascending position order. No atomics, no split-K.
