@@ -174,6 +174,7 @@ struct FwdGateUp {
     return t;
   }
   static MOE_DEV int num_k(const Args& a, const Tile&) { return a.d / G::BK; }
+  static MOE_DEV int k_first(const Tile&, int) { return 0; }
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) {  // LDS B row of n-block nb for wave wn
     constexpr int H2 = G::BN / 2, WH = G::WN / 2;
@@ -256,6 +257,9 @@ struct FwdDown {
     return t;
   }
   static MOE_DEV int num_k(const Args& a, const Tile&) { return a.I / G::BK; }
+  // W2's rows are 2I bytes apart (4 KB at I = 2048): tiles that start K together read the same
+  // column of 128 rows, which alias in HBM. Each n-tile starts at its own K-chunk and wraps.
+  static MOE_DEV int k_first(const Tile& t, int nk) { return (t.n0 / G::BN) % nk; }
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
@@ -331,6 +335,7 @@ struct BwdDownDgrad {
     return t;
   }
   static MOE_DEV int num_k(const Args& a, const Tile&) { return a.d / G::BK; }
+  static MOE_DEV int k_first(const Tile&, int) { return 0; }
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
@@ -440,6 +445,7 @@ struct BwdGateDgrad {
     return t;
   }
   static MOE_DEV int num_k(const Args& a, const Tile&) { return 2 * a.I / G::BK; }
+  static MOE_DEV int k_first(const Tile&, int) { return 0; }
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
@@ -585,14 +591,15 @@ MOE_DEV void run_tile_mx(const typename P::Args& a, const typename P::Tile& t, u
 
   const int nk = P::num_k(a, t);
   if (nk > 0) {
+    const int k0 = P::k_first(t, nk);  // K-chunks run k0, k0 + 1, .., nk - 1, 0, .., k0 - 1
     typename P::Loader ld;
     ld.init(a, t);
-    ld.load(0);
+    ld.load(k0);
     mx_store_stage<G>(ld.la, ld.lb, smem);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       uint8_t* cur = smem + (kt & 1) * G::STAGE;
-      if (kt + 1 < nk) ld.load(kt + 1);
+      if (kt + 1 < nk) ld.load(kt + 1 + k0 < nk ? kt + 1 + k0 : kt + 1 + k0 - nk);
       const uint8_t* sA = cur;
       const uint8_t* sB = cur + G::BM * G::LDK;
       const uint32_t* scA = reinterpret_cast<const uint32_t*>(cur + G::SC_OFF);
@@ -672,6 +679,7 @@ struct MxFwdGateUp {
     return t;
   }
   static MOE_DEV int num_k(const Args& a, const Tile&) { return a.d / G::BK; }
+  static MOE_DEV int k_first(const Tile&, int) { return 0; }
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) {
     return nb < 2 ? wn * 32 + nb * 16 : 64 + wn * 32 + (nb - 2) * 16;
@@ -769,6 +777,9 @@ struct MxFwdDown {
     return t;
   }
   static MOE_DEV int num_k(const Args& a, const Tile&) { return a.I / G::BK; }
+  // The quantised W2's rows are I bytes apart: as in the BF16 down GEMM, each n-tile starts at
+  // its own K-chunk so that concurrent tiles do not read one aliased column of rows.
+  static MOE_DEV int k_first(const Tile& t, int nk) { return (t.n0 / G::BN) % nk; }
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
@@ -848,6 +859,7 @@ struct MxBwdDownDgrad {
     return t;
   }
   static MOE_DEV int num_k(const Args& a, const Tile&) { return a.d / G::BK; }
+  static MOE_DEV int k_first(const Tile&, int) { return 0; }
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
@@ -983,6 +995,7 @@ struct MxBwdGateDgrad {
     return t;
   }
   static MOE_DEV int num_k(const Args& a, const Tile&) { return 2 * a.I / G::BK; }
+  static MOE_DEV int k_first(const Tile&, int) { return 0; }
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
@@ -1044,14 +1057,15 @@ MOE_DEV void run_tile(const typename P::Args& a, const typename P::Tile& t, uint
 
   const int nk = P::num_k(a, t);
   if (nk > 0) {
+    const int k0 = P::k_first(t, nk);  // K-chunks run k0, k0 + 1, .., nk - 1, 0, .., k0 - 1
     typename P::Loader ld;
     ld.init(a, t);
-    ld.load(0);
+    ld.load(k0);
     ld.store(smem);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       uint16_t* cur = smem + (kt & 1) * G::STAGE;
-      if (kt + 1 < nk) ld.load(kt + 1);
+      if (kt + 1 < nk) ld.load(kt + 1 + k0 < nk ? kt + 1 + k0 : kt + 1 + k0 - nk);
       const uint16_t* sA = cur;
       const uint16_t* sB = cur + G::BM * G::LDK;
 #pragma unroll
