@@ -13,6 +13,11 @@ static int rows_per_block(int d) {
   return rpb < 1 ? 1 : (rpb > 256 ? 256 : rpb);
 }
 
+// Rows of a token are gathered in groups of kGather: all loads of a group are issued before its
+// first FMA, so each thread keeps up to kGather 16-byte loads in flight. Sums still run in
+// ascending j.
+constexpr int kGather = 8;
+
 // y[t] = bf16( sum_{j=0..k-1} w[t,j] * O[tk_row[t*k+j]] ), fp32 fma with j ascending.
 __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict__ O,
                                                       const int32_t* __restrict__ tk_row,
@@ -25,16 +30,26 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
     const int t = t0 + i / vpr, v = i % vpr;
     if (t >= T) continue;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int pos = tk_row[(size_t)t * k + j];
-      if (pos < 0) continue;
-      const float wj = topk_w[(size_t)t * k + j];
-      const uint4 o = *reinterpret_cast<const uint4*>(O + (size_t)pos * d + v * 8);
-      const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+    for (int j0 = 0; j0 < k; j0 += kGather) {
+      int pos[kGather];
+      uint4 o[kGather];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] = __builtin_fmaf(wj, bf2f_lo(ow[q]), acc[2 * q]);
-        acc[2 * q + 1] = __builtin_fmaf(wj, bf2f_hi(ow[q]), acc[2 * q + 1]);
+      for (int jj = 0; jj < kGather; ++jj) {
+        const int j = j0 + jj;
+        pos[jj] = j < k ? tk_row[(size_t)t * k + j] : -1;
+        o[jj] = pos[jj] >= 0 ? *reinterpret_cast<const uint4*>(O + (size_t)pos[jj] * d + v * 8)
+                             : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < kGather; ++jj) {
+        if (pos[jj] < 0) continue;
+        const float wj = topk_w[(size_t)t * k + j0 + jj];
+        const uint32_t ow[4] = {o[jj].x, o[jj].y, o[jj].z, o[jj].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = __builtin_fmaf(wj, bf2f_lo(ow[q]), acc[2 * q]);
+          acc[2 * q + 1] = __builtin_fmaf(wj, bf2f_hi(ow[q]), acc[2 * q + 1]);
+        }
       }
     }
     uint4 out;
@@ -89,29 +104,49 @@ __global__ void __launch_bounds__(256) uncombine_kernel(
     const int t = t0 + i / vpr, v = i % vpr;
     if (t >= T) continue;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int pos = tk_row[(size_t)t * k + j];
-      if (pos < 0) continue;
-      const uint4 g = *reinterpret_cast<const uint4*>(dXp + (size_t)pos * d + v * 8);
-      const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+    for (int j0 = 0; j0 < k; j0 += kGather) {
+      int pos[kGather];
+      uint4 g[kGather];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += bf2f_lo(gw[q]);
-        acc[2 * q + 1] += bf2f_hi(gw[q]);
+      for (int jj = 0; jj < kGather; ++jj) {
+        const int j = j0 + jj;
+        pos[jj] = j < k ? tk_row[(size_t)t * k + j] : -1;
+        g[jj] = pos[jj] >= 0 ? *reinterpret_cast<const uint4*>(dXp + (size_t)pos[jj] * d + v * 8)
+                             : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < kGather; ++jj) {
+        if (pos[jj] < 0) continue;
+        const uint32_t gw[4] = {g[jj].x, g[jj].y, g[jj].z, g[jj].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += bf2f_lo(gw[q]);
+          acc[2 * q + 1] += bf2f_hi(gw[q]);
+        }
       }
     }
     if (wr) {
-      for (int j = 0; j < k; ++j) {
-        const int pos = tk_row[(size_t)t * k + j];
-        if (pos < 0) continue;
-        const float dl = dl_pos[pos];
-        const int e = topk_idx[(size_t)t * k + j];
-        const uint4 g = *reinterpret_cast<const uint4*>(wr + (size_t)e * d + v * 8);
-        const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+      for (int j0 = 0; j0 < k; j0 += kGather) {
+        int pos[kGather];
+        uint4 g[kGather];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = __builtin_fmaf(dl, bf2f_lo(gw[q]), acc[2 * q]);
-          acc[2 * q + 1] = __builtin_fmaf(dl, bf2f_hi(gw[q]), acc[2 * q + 1]);
+        for (int jj = 0; jj < kGather; ++jj) {
+          const int j = j0 + jj;
+          pos[jj] = j < k ? tk_row[(size_t)t * k + j] : -1;
+          const int e = pos[jj] >= 0 ? topk_idx[(size_t)t * k + j] : 0;
+          g[jj] = pos[jj] >= 0 ? *reinterpret_cast<const uint4*>(wr + (size_t)e * d + v * 8)
+                               : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int jj = 0; jj < kGather; ++jj) {
+          if (pos[jj] < 0) continue;
+          const float dl = dl_pos[pos[jj]];
+          const uint32_t gw[4] = {g[jj].x, g[jj].y, g[jj].z, g[jj].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] = __builtin_fmaf(dl, bf2f_lo(gw[q]), acc[2 * q]);
+            acc[2 * q + 1] = __builtin_fmaf(dl, bf2f_hi(gw[q]), acc[2 * q + 1]);
+          }
         }
       }
     }

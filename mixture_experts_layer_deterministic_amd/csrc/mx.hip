@@ -134,7 +134,9 @@ __global__ void __launch_bounds__(256) quant_weight_kernel(const uint16_t* __res
 }
 
 // dyw[pos] = bf16(w[row_src[pos]] * dy[row_src[pos] / k]): the down wgrad's left operand in
-// position order. Thread v handles 8 elements of one position's row.
+// position order. A grid-strided loop in which each thread issues four 16-byte loads before
+// their stores; vector v covers 8 elements of one position's row.
+constexpr int kSgUnroll = 4;
 __global__ void __launch_bounds__(256) scale_gather_kernel(const uint16_t* __restrict__ dy,
                                                            const int32_t* __restrict__ offsets,
                                                            const int32_t* __restrict__ row_src,
@@ -142,21 +144,37 @@ __global__ void __launch_bounds__(256) scale_gather_kernel(const uint16_t* __res
                                                            int E, int k, int d,
                                                            uint16_t* __restrict__ dyw,
                                                            long long nvec) {
-  const long long v = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (v >= nvec) return;
   const int vpr = d / 8;
-  const long long pos = v / vpr;
-  if (pos >= offsets[E]) return;  // rows skipped for a bad expert index
-  const int c = static_cast<int>(v % vpr) * 8;
-  const int r = row_src[pos];
-  const float w = topk_w[r];
-  const uint4 x = *reinterpret_cast<const uint4*>(dy + (size_t)(r / k) * d + c);
-  uint4 o;
-  o.x = pack_bf2(bf2f_lo(x.x) * w, bf2f_hi(x.x) * w);
-  o.y = pack_bf2(bf2f_lo(x.y) * w, bf2f_hi(x.y) * w);
-  o.z = pack_bf2(bf2f_lo(x.z) * w, bf2f_hi(x.z) * w);
-  o.w = pack_bf2(bf2f_lo(x.w) * w, bf2f_hi(x.w) * w);
-  *reinterpret_cast<uint4*>(dyw + (size_t)pos * d + c) = o;
+  const long long npos = offsets[E];  // rows past it are skipped for a bad expert index
+  const long long stride = (long long)gridDim.x * 256 * kSgUnroll;
+  for (long long v0 = (long long)blockIdx.x * 256 * kSgUnroll + threadIdx.x; v0 < nvec;
+       v0 += stride) {
+    uint4 x[kSgUnroll];
+    float w[kSgUnroll];
+    bool live[kSgUnroll];
+#pragma unroll
+    for (int u = 0; u < kSgUnroll; ++u) {
+      const long long v = v0 + 256 * u;
+      const long long pos = v / vpr;
+      live[u] = v < nvec && pos < npos;
+      const int r = live[u] ? row_src[pos] : 0;
+      w[u] = live[u] ? topk_w[r] : 0.f;
+      x[u] = live[u] ? *reinterpret_cast<const uint4*>(dy + (size_t)(r / k) * d +
+                                                      static_cast<int>(v % vpr) * 8)
+                     : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kSgUnroll; ++u) {
+      if (!live[u]) continue;
+      const float wu = w[u];
+      uint4 o;
+      o.x = pack_bf2(bf2f_lo(x[u].x) * wu, bf2f_hi(x[u].x) * wu);
+      o.y = pack_bf2(bf2f_lo(x[u].y) * wu, bf2f_hi(x[u].y) * wu);
+      o.z = pack_bf2(bf2f_lo(x[u].z) * wu, bf2f_hi(x[u].z) * wu);
+      o.w = pack_bf2(bf2f_lo(x[u].w) * wu, bf2f_hi(x[u].w) * wu);
+      *reinterpret_cast<uint4*>(dyw + (size_t)(v0 + 256 * u) * 8) = o;
+    }
+  }
 }
 
 hipError_t launch_quant_rows(const uint16_t* src, long long rows, int cols, uint8_t* dst,
@@ -188,9 +206,12 @@ hipError_t launch_scale_gather(const uint16_t* dy, const int32_t* offsets, const
                                const float* topk_w, int E, int k, int d, int Tk, uint16_t* dyw,
                                hipStream_t s) {
   const long long nvec = (long long)Tk * d / 8;
+  if (nvec == 0) return hipSuccess;
   {
     TraceScope trace("scale_gather", s);
-    hipLaunchKernelGGL(scale_gather_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0, s,
+    const long long per_block = 256LL * kSgUnroll;
+    const long long blocks = (nvec + per_block - 1) / per_block;
+    hipLaunchKernelGGL(scale_gather_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, s,
                        dy, offsets, row_src, topk_w, E, k, d, dyw, nvec);
   }
   return hipGetLastError();

@@ -111,6 +111,30 @@ __global__ void __launch_bounds__(256) perm_place_kernel(
   __syncthreads();
   const int vpr = d / 8;
   const int n = rpb * vpr;
+  if constexpr (!MX) {
+    // plain copy: four 16-byte loads in flight per thread before their stores
+    constexpr int U = 4;
+    for (int i0 = 0; i0 < n; i0 += 256 * U) {
+      uint4 val[U];
+      size_t dst[U];
+      bool live[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + 256 * u + tid;
+        const int rr = i / vpr, v = i % vpr;
+        const int r = r0 + rr;
+        const int pos = i < n ? sh_pos[rr] : -1;
+        live[u] = i < n && r < Tk && pos >= 0;
+        dst[u] = (size_t)pos * d + v * 8;
+        val[u] = live[u] ? *reinterpret_cast<const uint4*>(x + (size_t)(r / k) * d + v * 8)
+                         : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (live[u]) *reinterpret_cast<uint4*>(xp + dst[u]) = val[u];
+    }
+    return;
+  }
   for (int i0 = 0; i0 < n; i0 += 256) {
     const int i = i0 + tid;
     const int rr = i / vpr, v = i % vpr;
@@ -119,9 +143,7 @@ __global__ void __launch_bounds__(256) perm_place_kernel(
     const bool live = i < n && r < Tk && pos >= 0;
     const uint4 val =
         live ? *reinterpret_cast<const uint4*>(x + (size_t)(r / k) * d + v * 8) : make_uint4(0, 0, 0, 0);
-    if constexpr (!MX) {
-      if (live) *reinterpret_cast<uint4*>(xp + (size_t)pos * d + v * 8) = val;
-    } else {
+    {
       const uint32_t xw[4] = {val.x, val.y, val.z, val.w};
       float f[8];
 #pragma unroll
