@@ -15,8 +15,8 @@ import torch
 
 import oracle
 import workload
-from tests._gpu import (DEV, _announce, _np, assert_bitwise_equal, check_parity, m, outputs,
-                        run_gpu, run_oracle)
+from tests._gpu import (DEV, MoeLayer, _announce, _np, assert_bitwise_equal, check_parity, m,
+                        outputs, run_gpu, run_oracle)
 from tests._util import assert_act, assert_grad
 
 pytestmark = pytest.mark.gpu
@@ -137,3 +137,66 @@ def test_mxfp8_full_size_sampled_parity_and_determinism():
     torch.cuda.empty_cache()
     assert_bitwise_equal(ref, outputs(run_gpu(inp), True, clone=False))
     _announce("  two full-size runs bitwise identical")
+
+
+def _special_blocks(rows, cols, seed):
+    """bf16 values [rows, cols] whose 32-blocks along the row exercise the edges of the MXFP8
+    quantiser: all +0 and all -0 blocks, blocks of bf16 subnormals, blocks at the top of the
+    bf16 range, exact powers of two, E4M3 rounding ties at unit scale, values in (448, 512)
+    after scaling (saturation), one large value over tiny ones (underflow to zero), and plain
+    normal values."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    nb = cols // 32
+    for r in range(rows):
+        for b in range(nb):
+            kind = (r * nb + b) % 10
+            blk = x[r, 32 * b:32 * b + 32]
+            if kind == 0:
+                blk[:] = 0.0
+            elif kind == 1:
+                blk[:] = -0.0
+            elif kind == 2:  # bf16 subnormals, mixed signs
+                blk[:] = rng.choice([-1, 1], 32) * rng.integers(1, 128, 32) * 2.0 ** -133
+            elif kind == 3:  # near the top of the bf16 range
+                blk[:] = rng.choice([-1, 1], 32) * rng.uniform(1.0, 1.99, 32) * 2.0 ** 127
+            elif kind == 4:  # exact powers of two
+                blk[:] = rng.choice([-1, 1], 32) * 2.0 ** rng.integers(-20, 20, 32)
+            elif kind == 5:  # amax 256 -> scale 1; ties between E4M3 neighbours
+                blk[:] = [256.0] + [1.0625, 1.1875, 3.25, 9.5, 0.015625 * 1.5, 2.0 ** -9 * 1.5,
+                                    -1.0625, -3.75, 17.0, 232.0, 240.0, 248.0] + [0.5] * 19
+            elif kind == 6:  # block max in (448, 512) after scaling: saturates
+                blk[:] = rng.uniform(-1, 1, 32) * 256.0
+                blk[0] = 480.0
+                blk[1] = -500.0
+            elif kind == 7:  # one large value over tiny ones
+                blk[:] = rng.standard_normal(32) * 1e-6
+                blk[5] = 3.0e4
+    return torch.from_numpy(x).to(torch.bfloat16)
+
+
+def test_mxfp8_quantiser_edge_values_are_bit_exact():
+    """Weights and tokens built from the quantiser's edge cases: the GPU codes and scales of
+    W1, W2 (both axes) and of the permuted tokens equal the oracle's quantiser bit for bit."""
+    _announce("[mxfp8] quantiser edge values, E=4 d=256 I=128 T=64 k=2")
+    T, d, E, k, I = 64, 256, 4, 2, 128
+    W1 = _special_blocks(E * 2 * I, d, 1).reshape(E, 2 * I, d).to(DEV)
+    W2 = _special_blocks(E * d, I, 2).reshape(E, d, I).to(DEV)
+    X = _special_blocks(T, d, 3).to(DEV)
+    L = MoeLayer(T, d, E, k, I, device=DEV, precision=m.MOE_PREC_MXFP8)
+    L.quantize_weights(W1, W2)
+    idx = torch.tensor([[t % E, (t + 1) % E] for t in range(T)], dtype=torch.int32)
+    L.set_routing(idx.to(DEV), torch.full((T, k), 0.5, dtype=torch.float32, device=DEV))
+    L.permute(X)
+    torch.cuda.synchronize()
+    W1n, W2n, Xn = _np(W1), _np(W2), _np(X)
+    refs = [oracle.mx.quantize(W1n), oracle.mx.quantize(W2n),
+            oracle.mx.quantize(np.swapaxes(W2n, 1, 2)), oracle.mx.quantize(np.swapaxes(W1n, 1, 2))]
+    for i, ((codes, sc), (q, s)) in enumerate(zip(_wq_parts(L), refs)):
+        np.testing.assert_array_equal(_np(sc), s, err_msg=f"scales of part {i}")
+        np.testing.assert_array_equal(_np(codes), q, err_msg=f"codes of part {i}")
+    row_src = _np(L.row_src)
+    codes, scales = L.xp()
+    q, sc = oracle.mx.quantize(Xn[row_src // k])
+    np.testing.assert_array_equal(_np(scales), sc)
+    np.testing.assert_array_equal(_np(codes), q)
