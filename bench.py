@@ -131,7 +131,7 @@ def measured_traffic(workload, kernel):
     return rec["read_bytes"] + rec["write_bytes"]
 
 
-def cpu_baseline(inp, cfg, s_small=4, s_large=12):
+def cpu_baseline(inp, cfg, s_small=8, s_large=40):
     """The CPU oracle on a bounded sample: the full router and bookkeeping plus the expert math
     of the first `s` experts, for two values of s. Its time is linear in the expert count, so
     the whole-layer time is extrapolated to all E experts."""
@@ -180,6 +180,8 @@ def main():
     ap.add_argument("--no-trace", action="store_true", help="skip per-kernel events")
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the MXFP8-mode run on the same inputs")
+    ap.add_argument("--no-expert-slice", action="store_true",
+                    help="skip the local expert-slice (local_zipf) run")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB, a known-size "
                          "reference for HBM byte counters")
@@ -255,6 +257,23 @@ def main():
                    "grouped_gemm": r["gemm"], "kernels": r["kernels"]}
         torch.cuda.empty_cache()
 
+    # The local expert slice (16,384 received rows over 8 experts, Zipf-skewed): there the
+    # grouped GEMMs are MFMA-bound, so it is where their fraction of the MFMA peak means something.
+    slice_line = None
+    if args.workload == "dsv3" and not args.no_expert_slice:
+        print("[bench] local expert slice (local_zipf)", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        cz = workload.config("local_zipf")
+        iz = workload.make_inputs("local_zipf", seed=args.seed, device=dev)
+        r = run_layer(m, MoeLayer, iz, cz, stream, args, mx=False)
+        slice_line = {"workload": "local_zipf", "rows": cz["T"] * cz["k"], "E": cz["E"],
+                      "ms_per_step": round(r["ms"], 4),
+                      "rows_per_s": round(cz["T"] * cz["k"] / (r["ms"] * 1e-3), 1),
+                      "grouped_gemm": r["gemm"],
+                      "gemm_us": {g: r["kernels"][g]["us"] for g in GEMMS if g in r["kernels"]}}
+        del iz
+        torch.cuda.empty_cache()
+
     # practical HBM ceiling: one plain 2 GiB device copy (read + write), best of 3. Skipped in
     # counter runs, where the only device copy must be the calibration copy.
     n = 2 << 30
@@ -287,6 +306,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(main_run["ms_median"], 4),
+        "ms_per_step_min": round(main_run["ms_min"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -300,6 +321,7 @@ def main():
         "grouped_gemm": main_run["gemm"],
         "permute_combine": pc,
         "mxfp8": mx_line,
+        "expert_slice": slice_line,
         "hbm_copy": {"GB/s": hbm_copy, "bytes": 2 * n, "what": "one plain device copy, read + write"},
         "kernels": kernels,
         "host_seconds_timed": round(main_run["t_host"], 4),
@@ -359,16 +381,23 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx):
           flush=True)
     if ev:
         keep = m.moe_trace_begin([e.cuda_event for e in ev], names)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t_host = time.perf_counter()
     start.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
+        marks[i + 1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
     if ev:
         m.moe_trace_end()
     ms = start.elapsed_time(end) / args.steps
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    h = len(step_ms) // 2
+    ms_median = step_ms[h] if len(step_ms) % 2 else 0.5 * (step_ms[h - 1] + step_ms[h])
+    ms_min = step_ms[0]
 
     alg = algorithmic(cfg, routed=routed, mx=mx)
     kernels = {}
@@ -406,7 +435,8 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx):
                 "alg_bytes": nbytes, "hbm_gbps": round(nbytes / (gemm_us * 1e-6) / 1e9, 1),
                 "share_of_step": round(gemm_us / 1e3 / ms, 4)}
     del L
-    return {"ms": ms, "kernels": kernels, "gemm": gemm, "quant_ms": quant_ms, "t_host": t_host}
+    return {"ms": ms, "ms_median": ms_median, "ms_min": ms_min, "kernels": kernels, "gemm": gemm,
+            "quant_ms": quant_ms, "t_host": t_host}
 
 
 if __name__ == "__main__":
