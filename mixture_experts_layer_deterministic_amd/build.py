@@ -31,16 +31,30 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, obj: str) -> None:
+def _compile(src: str, obj: str) -> dict:
+    """Compiles one source. Returns {kernel: scratch bytes per lane} from the compiler's
+    resource-usage remarks."""
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, *lang, "-Rpass-analysis=kernel-resource-usage",
+           "-fno-caret-diagnostics",
+           "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    scratch, name, other = {}, None, []
+    for line in r.stderr.splitlines():
+        if "kernel-resource-usage" in line:
+            if "Function Name:" in line:
+                name = line.split("Function Name:")[1].split("[")[0].strip()
+            elif "ScratchSize [bytes/lane]:" in line and name:
+                scratch[name] = int(line.split("ScratchSize [bytes/lane]:")[1].split("[")[0])
+        elif noise not in line:
+            other.append(line)
+    err = "\n".join(other)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{err}")
     if err.strip():
         print(err)
+    return scratch
 
 
 def build(verbose: bool = True) -> str:
@@ -49,7 +63,12 @@ def build(verbose: bool = True) -> str:
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        list(ex.map(lambda so: _compile(*so), zip(SOURCES, objs)))
+        usage = list(ex.map(lambda so: _compile(*so), zip(SOURCES, objs)))
+    # Every kernel keeps its state in registers and LDS: a private (scratch) array or a spill
+    # puts memory waits into its inner loop, so the build refuses one.
+    scratch = {k: v for u in usage for k, v in u.items() if v}
+    if scratch:
+        raise RuntimeError(f"kernels using scratch memory (bytes per lane): {scratch}")
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -64,16 +64,16 @@ struct LoadK {
 // k-block index runs fastest across lanes (each wave instruction reads 8 rows x 128 contiguous
 // bytes, and the transposed LDS writes of 16 lanes cover all 64 banks), then transposed so
 // LDS holds [MN][K]. krow(k) returns the row pointer already offset to the tile's first MN
-// column, or null for a zero row; kscale(k) multiplies a row (rounded back to bf16) when SCALED.
-template <int MN, int BK, int LDK, bool SCALED>
+// column. Only the first NB threads hold a block.
+template <int MN, int BK, int LDK>
 struct LoadMN {
   static constexpr int BKB = BK / 8;
   static constexpr int NB = (MN / 8) * BKB;
   static constexpr int PT = (NB + kThreads - 1) / kThreads;
   uint4 r[PT][8];
 
-  template <class KRow, class KScale>
-  MOE_DEV void load(int k0, KRow krow, KScale kscale) {
+  template <class KRow>
+  MOE_DEV void load(int k0, KRow krow) {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const int b = threadIdx.x + kThreads * j;
@@ -81,19 +81,7 @@ struct LoadMN {
         const int kb = b % BKB, mb = b / BKB;
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
-          const int k = k0 + kb * 8 + rr;
-          const uint16_t* p = krow(k);
-          uint4 v = p ? *reinterpret_cast<const uint4*>(p + mb * 8) : make_uint4(0, 0, 0, 0);
-          if constexpr (SCALED) {
-            if (p) {
-              const float s = kscale(k);
-              v.x = pack_bf2(bf2f_lo(v.x) * s, bf2f_hi(v.x) * s);
-              v.y = pack_bf2(bf2f_lo(v.y) * s, bf2f_hi(v.y) * s);
-              v.z = pack_bf2(bf2f_lo(v.z) * s, bf2f_hi(v.z) * s);
-              v.w = pack_bf2(bf2f_lo(v.w) * s, bf2f_hi(v.w) * s);
-            }
-          }
-          r[j][rr] = v;
+          r[j][rr] = *reinterpret_cast<const uint4*>(krow(k0 + kb * 8 + rr) + mb * 8);
         }
       }
     }
@@ -340,7 +328,7 @@ struct BwdDownDgrad {
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
     LoadK<G::BM, G::BK, G::LDK> la;
-    LoadMN<G::BN, G::BK, G::LDK, false> lb;
+    LoadMN<G::BN, G::BK, G::LDK> lb;
     const uint16_t* wb;
     int ldw;
     MOE_DEV void init(const Args& a, const Tile& t) {
@@ -355,7 +343,7 @@ struct BwdDownDgrad {
       la.load(kt * G::BK);
       const uint16_t* w = wb;
       const int ld = ldw;
-      lb.load(kt * G::BK, [&](int k) { return w + (size_t)k * ld; }, [](int) { return 1.0f; });
+      lb.load(kt * G::BK, [&](int k) { return w + (size_t)k * ld; });
     }
     MOE_DEV void store(uint16_t* s) const {
       la.store(s);
@@ -450,7 +438,7 @@ struct BwdGateDgrad {
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
     LoadK<G::BM, G::BK, G::LDK> la;
-    LoadMN<G::BN, G::BK, G::LDK, false> lb;
+    LoadMN<G::BN, G::BK, G::LDK> lb;
     const uint16_t* wb;
     int ldw;
     MOE_DEV void init(const Args& a, const Tile& t) {
@@ -464,7 +452,7 @@ struct BwdGateDgrad {
       la.load(kt * G::BK);
       const uint16_t* w = wb;
       const int ld = ldw;
-      lb.load(kt * G::BK, [&](int k) { return w + (size_t)k * ld; }, [](int) { return 1.0f; });
+      lb.load(kt * G::BK, [&](int k) { return w + (size_t)k * ld; });
     }
     MOE_DEV void store(uint16_t* s) const {
       la.store(s);
@@ -515,8 +503,8 @@ struct GeoMx {
 };
 
 // ROWS rows of fp8 codes, K-contiguous: 8 vectors of 16 bytes per 128-K step. Thread t < ROWS
-// also moves row t's scale word (four block scales of the step). A null row loads zeros with
-// unit scales.
+// also moves row t's scale word (four block scales of the step), loading the words of four
+// steps at once where the row length allows. A null row loads zeros with unit scales.
 template <int ROWS, int LDK>
 struct LoadK8 {
   static constexpr int VPR = 8;
@@ -525,17 +513,26 @@ struct LoadK8 {
   const uint8_t* rp[PT];
   uint4 r[PT];
   const uint8_t* sp;
-  uint32_t s;
+  uint4 s4;     // the scale words of four consecutive steps (or of one, in s4.x)
+  int sg, sidx; // group held in s4 and this step's word in it
+  bool grouped; // rows hold a multiple of 16 scale bytes: load them 16 bytes at a time
 
+  // kdim: the K extent of a row (elements), so a row holds kdim / 32 scale bytes. The scale
+  // arrays start 16-byte aligned.
   template <class RowPtr, class ScalePtr>
-  MOE_DEV void init(RowPtr rowptr, ScalePtr scaleptr) {
+  MOE_DEV void init(RowPtr rowptr, ScalePtr scaleptr, int kdim) {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const int v = threadIdx.x + kThreads * j;
       rp[j] = (v < NV) ? rowptr(v / VPR) : nullptr;
     }
     sp = threadIdx.x < ROWS ? scaleptr(threadIdx.x) : nullptr;
+    grouped = kdim % 512 == 0;
+    sg = -1;
+    s4 = make_uint4(0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu);
+    sidx = 0;
   }
+  // The scale word is picked in store(), so no load result is waited for here.
   MOE_DEV void load(int kt) {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
@@ -543,7 +540,17 @@ struct LoadK8 {
       r[j] = rp[j] ? *reinterpret_cast<const uint4*>(rp[j] + (size_t)kt * 128 + (v % VPR) * 16)
                    : make_uint4(0, 0, 0, 0);
     }
-    s = sp ? *reinterpret_cast<const uint32_t*>(sp + (size_t)kt * 4) : 0x7f7f7f7fu;
+    if (!sp) return;
+    if (grouped) {
+      if ((kt >> 2) != sg) {
+        sg = kt >> 2;
+        s4 = *reinterpret_cast<const uint4*>(sp + (size_t)sg * 16);
+      }
+      sidx = kt & 3;
+    } else {
+      s4.x = *reinterpret_cast<const uint32_t*>(sp + (size_t)kt * 4);
+      sidx = 0;
+    }
   }
   MOE_DEV void store(uint8_t* rows, uint32_t* scales) const {
 #pragma unroll
@@ -551,7 +558,12 @@ struct LoadK8 {
       const int v = threadIdx.x + kThreads * j;
       if (v < NV) *reinterpret_cast<uint4*>(rows + (v / VPR) * LDK + (v % VPR) * 16) = r[j];
     }
-    if (threadIdx.x < ROWS) scales[threadIdx.x] = s;
+    if (threadIdx.x < ROWS) {
+      // masks rather than a selected vector element, which the compiler would index in scratch
+      const uint32_t m0 = 0u - (sidx == 0), m1 = 0u - (sidx == 1), m2 = 0u - (sidx == 2),
+                     m3 = 0u - (sidx == 3);
+      scales[threadIdx.x] = (s4.x & m0) | (s4.y & m1) | (s4.z & m2) | (s4.w & m3);
+    }
   }
 };
 
@@ -692,13 +704,13 @@ struct MxFwdGateUp {
       const uint8_t* xp8 = a.xp8;
       const uint8_t* xps = a.xps;
       la.init([&](int m) { return m < mc ? xp8 + (size_t)(row0 + m) * d : nullptr; },
-              [&](int m) { return m < mc ? xps + (size_t)(row0 + m) * (d / 32) : nullptr; });
+              [&](int m) { return m < mc ? xps + (size_t)(row0 + m) * (d / 32) : nullptr; }, d);
       const size_t wrow0 = (size_t)t.m.e * 2 * I;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
       auto wrow = [=](int n) { return wrow0 + (n < 64 ? n0 + n : I + n0 + n - 64); };
       lb.init([&](int n) { return w8 + wrow(n) * d; },
-              [&](int n) { return ws + wrow(n) * (d / 32); });
+              [&](int n) { return ws + wrow(n) * (d / 32); }, d);
     }
     MOE_DEV void load(int kt) {
       la.load(kt);
@@ -790,12 +802,12 @@ struct MxFwdDown {
       const uint8_t* aq = a.aq;
       const uint8_t* aqs = a.aqs;
       la.init([&](int m) { return m < mc ? aq + (size_t)(row0 + m) * I : nullptr; },
-              [&](int m) { return m < mc ? aqs + (size_t)(row0 + m) * (I / 32) : nullptr; });
+              [&](int m) { return m < mc ? aqs + (size_t)(row0 + m) * (I / 32) : nullptr; }, I);
       const size_t wrow0 = (size_t)t.m.e * a.d + t.n0;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
       lb.init([&](int n) { return w8 + (wrow0 + n) * I; },
-              [&](int n) { return ws + (wrow0 + n) * (I / 32); });
+              [&](int n) { return ws + (wrow0 + n) * (I / 32); }, I);
     }
     MOE_DEV void load(int kt) {
       la.load(kt);
@@ -871,12 +883,12 @@ struct MxBwdDownDgrad {
       const uint8_t* dys = a.dys;
       const int32_t* rs = a.row_src;
       la.init([&](int m) { return m < mc ? dyq + (size_t)(rs[row0 + m] / k) * d : nullptr; },
-              [&](int m) { return m < mc ? dys + (size_t)(rs[row0 + m] / k) * (d / 32) : nullptr; });
+              [&](int m) { return m < mc ? dys + (size_t)(rs[row0 + m] / k) * (d / 32) : nullptr; }, d);
       const size_t wrow0 = (size_t)t.m.e * a.I + t.n0;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
       lb.init([&](int n) { return w8 + (wrow0 + n) * d; },
-              [&](int n) { return ws + (wrow0 + n) * (d / 32); });
+              [&](int n) { return ws + (wrow0 + n) * (d / 32); }, d);
     }
     MOE_DEV void load(int kt) {
       la.load(kt);
@@ -1006,12 +1018,12 @@ struct MxBwdGateDgrad {
       const uint8_t* dhq = a.dhq;
       const uint8_t* dhs = a.dhs;
       la.init([&](int m) { return m < mc ? dhq + (size_t)(row0 + m) * twoI : nullptr; },
-              [&](int m) { return m < mc ? dhs + (size_t)(row0 + m) * (twoI / 32) : nullptr; });
+              [&](int m) { return m < mc ? dhs + (size_t)(row0 + m) * (twoI / 32) : nullptr; }, twoI);
       const size_t wrow0 = (size_t)t.m.e * a.d + t.n0;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
       lb.init([&](int n) { return w8 + (wrow0 + n) * twoI; },
-              [&](int n) { return ws + (wrow0 + n) * (twoI / 32); });
+              [&](int n) { return ws + (wrow0 + n) * (twoI / 32); }, twoI);
     }
     MOE_DEV void load(int kt) {
       la.load(kt);
