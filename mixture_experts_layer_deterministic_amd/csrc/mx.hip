@@ -49,7 +49,8 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restr
 // One workgroup of 256 threads per 128 x 128 tile (R and C are multiples of 128). The tile is
 // read once: each row's 32-blocks are quantised from registers as they arrive, and the tile goes
 // to LDS, where wave w quantises rows [32 w, 32 w + 32) of every column. The column codes are
-// staged in LDS so that each column's 128 codes leave as 128 contiguous bytes.
+// then staged in the same LDS (about 33 KB per workgroup in all, so four fit on a CU) and each
+// column's 128 codes leave as 128 contiguous bytes. Scale codes leave four bytes at a time.
 constexpr int kQT = 128;
 __global__ void __launch_bounds__(256) quant_weight_kernel(const uint16_t* __restrict__ src,
                                                            uint8_t* __restrict__ dq,
@@ -57,23 +58,28 @@ __global__ void __launch_bounds__(256) quant_weight_kernel(const uint16_t* __res
                                                            uint8_t* __restrict__ tq,
                                                            uint8_t* __restrict__ tqs, int R,
                                                            int C) {
-  __shared__ uint32_t tile[kQT][kQT / 2 + 1];  // bf16 pairs, row-major, padded pitch
-  __shared__ uint32_t outT[kQT][kQT / 4 + 1];  // codes of column c along R, padded pitch
-  __shared__ uint32_t scT[kQT];                // the column's four scale codes, one per byte
+  constexpr int TP = kQT / 2 + 1;  // tile pitch in words (bf16 pairs)
+  constexpr int OP = kQT / 4 + 1;  // pitch of the staged column codes in words
+  static_assert(kQT * OP <= kQT * TP, "column codes fit in the tile's LDS");
+  __shared__ uint32_t tile[kQT * TP];
+  __shared__ uint32_t scT[kQT];  // the column's four scale codes, one per byte
   const int b = blockIdx.z, r0 = blockIdx.y * kQT, c0 = blockIdx.x * kQT;
   const int t = threadIdx.x;
   const uint16_t* s = src + ((size_t)b * R + r0) * C + c0;
   // Phase 1: sixteen lanes per row, eight elements per lane; lanes 4q..4q+3 make one 32-block.
   const int cv = t % 16;
+  uint4 x[kQT / 16];
+#pragma unroll
+  for (int j = 0; j < kQT / 16; ++j)
+    x[j] = *reinterpret_cast<const uint4*>(s + (size_t)(t / 16 + 16 * j) * C + cv * 8);
 #pragma unroll
   for (int j = 0; j < kQT / 16; ++j) {
     const int r = t / 16 + 16 * j;
-    const uint4 x = *reinterpret_cast<const uint4*>(s + (size_t)r * C + cv * 8);
-    tile[r][cv * 4 + 0] = x.x;
-    tile[r][cv * 4 + 1] = x.y;
-    tile[r][cv * 4 + 2] = x.z;
-    tile[r][cv * 4 + 3] = x.w;
-    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+    tile[r * TP + cv * 4 + 0] = x[j].x;
+    tile[r * TP + cv * 4 + 1] = x[j].y;
+    tile[r * TP + cv * 4 + 2] = x[j].z;
+    tile[r * TP + cv * 4 + 3] = x[j].w;
+    const uint32_t xw[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
     float f[8];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -92,41 +98,53 @@ __global__ void __launch_bounds__(256) quant_weight_kernel(const uint16_t* __res
     o.y = e4m3x2(f[4] * inv, f[5] * inv) | (e4m3x2(f[6] * inv, f[7] * inv) << 16);
     const size_t row = (size_t)b * R + r0 + r;
     *reinterpret_cast<uint2*>(dq + row * C + c0 + cv * 8) = o;
-    if ((cv & 3) == 0) dqs[row * (C / 32) + (c0 + cv * 8) / 32] = static_cast<uint8_t>(code);
+    // the row's four block scales (lanes cv = 0, 4, 8, 12 of its group) as one word
+    const int g0 = (t % kWave) & ~15;
+    const uint32_t w4 = __shfl(code, g0) | (__shfl(code, g0 + 4) << 8) |
+                        (__shfl(code, g0 + 8) << 16) | (__shfl(code, g0 + 12) << 24);
+    if (cv == 0) *reinterpret_cast<uint32_t*>(dqs + row * (C / 32) + c0 / 32) = w4;
   }
   __syncthreads();
   // Phase 2: wave w takes rows [32 w, 32 w + 32); lane l the column pair (2 l, 2 l + 1).
+  const int w = t / kWave, l = t % kWave;
+  uint32_t clo[8], chi[8];
   {
-    const int w = t / kWave, l = t % kWave;
     float lo[32], hi[32];
     float alo = 0.f, ahi = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const uint32_t v = tile[w * 32 + i][l];
+      const uint32_t v = tile[(w * 32 + i) * TP + l];
       lo[i] = bf2f_lo(v);
       hi[i] = bf2f_hi(v);
       alo = fmaxf(alo, fabsf(lo[i]));
       ahi = fmaxf(ahi, fabsf(hi[i]));
     }
-    const uint32_t clo = mx_scale_code(alo), chi = mx_scale_code(ahi);
-    const float ilo = mx_inv_scale(clo), ihi = mx_inv_scale(chi);
+    const uint32_t slo = mx_scale_code(alo), shi = mx_scale_code(ahi);
+    const float ilo = mx_inv_scale(slo), ihi = mx_inv_scale(shi);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      outT[2 * l][w * 8 + q] = e4m3x2(lo[4 * q] * ilo, lo[4 * q + 1] * ilo) |
-                               (e4m3x2(lo[4 * q + 2] * ilo, lo[4 * q + 3] * ilo) << 16);
-      outT[2 * l + 1][w * 8 + q] = e4m3x2(hi[4 * q] * ihi, hi[4 * q + 1] * ihi) |
-                                   (e4m3x2(hi[4 * q + 2] * ihi, hi[4 * q + 3] * ihi) << 16);
+      clo[q] = e4m3x2(lo[4 * q] * ilo, lo[4 * q + 1] * ilo) |
+               (e4m3x2(lo[4 * q + 2] * ilo, lo[4 * q + 3] * ilo) << 16);
+      chi[q] = e4m3x2(hi[4 * q] * ihi, hi[4 * q + 1] * ihi) |
+               (e4m3x2(hi[4 * q + 2] * ihi, hi[4 * q + 3] * ihi) << 16);
     }
-    reinterpret_cast<uint8_t*>(scT)[(2 * l) * 4 + w] = static_cast<uint8_t>(clo);
-    reinterpret_cast<uint8_t*>(scT)[(2 * l + 1) * 4 + w] = static_cast<uint8_t>(chi);
+    reinterpret_cast<uint8_t*>(scT)[(2 * l) * 4 + w] = static_cast<uint8_t>(slo);
+    reinterpret_cast<uint8_t*>(scT)[(2 * l + 1) * 4 + w] = static_cast<uint8_t>(shi);
+  }
+  __syncthreads();  // every wave has read the tile: its LDS now holds the column codes
+  uint32_t* outT = tile;  // [kQT][OP]
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    outT[(2 * l) * OP + w * 8 + q] = clo[q];
+    outT[(2 * l + 1) * OP + w * 8 + q] = chi[q];
   }
   __syncthreads();
   // Phase 3: each column's 128 codes as eight 16-byte stores, and its four scales as one word.
 #pragma unroll
   for (int j = 0; j < kQT * 8 / 256; ++j) {
     const int idx = t + 256 * j, c = idx / 8, part = idx % 8;
-    const uint4 v = make_uint4(outT[c][part * 4], outT[c][part * 4 + 1], outT[c][part * 4 + 2],
-                               outT[c][part * 4 + 3]);
+    const uint4 v = make_uint4(outT[c * OP + part * 4], outT[c * OP + part * 4 + 1],
+                               outT[c * OP + part * 4 + 2], outT[c * OP + part * 4 + 3]);
     *reinterpret_cast<uint4*>(tq + ((size_t)b * C + c0 + c) * R + r0 + part * 16) = v;
   }
   if (t < kQT)
