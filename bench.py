@@ -230,15 +230,15 @@ def main():
     # in MXFP8 mode a step also re-quantises the weights (they change every optimizer step)
     tokens_per_s = T / (ms * 1e-3)
 
-    dominant = max(kernels, key=lambda n: kernels[n]["us"] * kernels[n]["launches_per_step"]) \
-        if kernels else None
+    dominant = max(kernels, key=lambda n: kernels[n]["us"]) if kernels else None
     roof = None
     if dominant:
         kd = kernels[dominant]
         roof = {"kernel": dominant, "bound": kd["bound"], "achieved": kd["achieved"],
                 "peak": kd["peak"], "unit": kd["unit"], "frac": kd["frac"],
                 "traffic": measured_traffic(args.workload, dominant),
-                "alg_bytes": kd["alg_bytes"], "us_per_launch": kd["us"]}
+                "alg_bytes": kd["alg_bytes"], "us_per_step": kd["us"],
+                "launches_per_step": kd["launches_per_step"]}
     pc = {}
     for n in ("perm_place", "combine"):
         if n in kernels:
@@ -408,14 +408,24 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx):
             n = names[i].decode()
             tot[n] = tot.get(n, 0.0) + ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3
             cnt[n] = cnt.get(n, 0) + 1
-        for n in tot:
-            us = tot[n] / cnt[n]
+        # A step's work of one kind may take several launches (the forward GEMMs run their
+        # 256-row blocks and their remainders as two, "<name>_big" and "<name>"): a kernel's
+        # `us` is its time per step, summed over them, and `parts` splits it.
+        parts = {}
+        for n in list(tot):
+            base = n[:-4] if n.endswith("_big") else n
+            parts.setdefault(base, {})[n] = tot[n] / args.steps
+        for n, pt in parts.items():
+            us = sum(pt.values())
+            launches = sum(cnt[p] for p in pt) // args.steps
             nbytes, flops = alg.get(n, (0, 0))
             r = kernel_roofline(n, nbytes, flops, us, mx) if nbytes else {}
-            kernels[n] = {"us": round(us, 2), "launches_per_step": cnt[n] // args.steps,
+            kernels[n] = {"us": round(us, 2), "launches_per_step": launches,
                           "alg_bytes": nbytes, "alg_flops": flops,
                           **{kk: (round(v, 4) if isinstance(v, float) else v)
                              for kk, v in r.items()}}
+            if len(pt) > 1:
+                kernels[n]["parts_us"] = {p: round(v, 2) for p, v in pt.items()}
     quant_ms = sum(kernels[n]["us"] for n in kernels if n.startswith("quant_w")) / 1e3
     gemm = None
     gemm_us = sum(kernels[g]["us"] for g in GEMMS if g in kernels)

@@ -39,6 +39,7 @@ bool cfg_ok(const moe_cfg* c) {
   if (c->E < 1 || c->E > 1024 || c->k < 1 || c->k > c->E || c->k > kMaxTopK) return false;
   const long long Tk = (long long)c->T * c->k;
   if (Tk >= (1LL << 31) || (long long)c->T * c->E >= (1LL << 31)) return false;
+  if ((long long)c->T * c->d >= (1LL << 31)) return false;  // 32-bit row offsets into X and dY
   return true;
 }
 
@@ -55,7 +56,7 @@ Layout layout(const moe_cfg* c) {
     return at;
   };
   L.status = take(16);
-  L.sched = take(sizeof(int2) * (1 + (size_t)L.max_mtiles));
+  L.sched = take(sizeof(int2) * sched_entries((int)Tk, (int)E));
   L.blk_cnt = take(sizeof(int32_t) * (size_t)L.nb * E);
   L.blk_flag = take(sizeof(int32_t) * (size_t)L.nb);
   L.rank = take(sizeof(int32_t) * Tk);
@@ -307,7 +308,7 @@ int moe_forward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t
   uint16_t* A = at<uint16_t>(saved, Y.A);
   uint16_t* O = at<uint16_t>(workspace, Y.O);
   Launches L;
-  L(launch_sched_build(offsets, E, sched, s));
+  L(launch_sched_build(offsets, E, Tk, sched, s));
   if (Y.mx) {
     uint8_t* aq = at<uint8_t>(workspace, Y.aq);
     uint8_t* aqs = at<uint8_t>(workspace, Y.aqs);
@@ -373,7 +374,7 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
   const uint16_t* w1p = static_cast<const uint16_t*>(w1);
   const uint16_t* w2p = static_cast<const uint16_t*>(w2);
   Launches L;
-  L(launch_sched_build(offsets, E, sched, s));
+  L(launch_sched_build(offsets, E, Tk, sched, s));
   if (Y.mx) {
     uint8_t* dyq = at<uint8_t>(workspace, Y.dyq);
     uint8_t* dys = at<uint8_t>(workspace, Y.dys);

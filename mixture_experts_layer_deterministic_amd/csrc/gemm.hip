@@ -15,6 +15,8 @@
 //
 // Determinism: every output element is produced by exactly one workgroup, which reduces K in a
 // fixed order. There are no atomics and no split-K.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -25,31 +27,34 @@ constexpr int kThreads = 256;
 // ------------------------------------------------------------------------------------------
 // Tile loaders (global -> registers -> LDS)
 
-// ROWS x BK tile whose rows are K-contiguous in memory. Row pointers are fixed per tile; a null
-// row pointer loads zeros.
+// ROWS x BK tile whose rows are K-contiguous in memory. Rows are element offsets from one base
+// pointer (32 bits each, so a thread holds one register per row rather than a pointer);
+// rowoff(r) < 0 marks a row that loads zeros.
 template <int ROWS, int BK, int LDK>
 struct LoadK {
   static constexpr int VPR = BK / 8;
   static constexpr int NV = ROWS * VPR;
   static constexpr int PT = (NV + kThreads - 1) / kThreads;
-  const uint16_t* rp[PT];
+  static constexpr uint32_t kNull = 0xffffffffu;
+  const uint16_t* base;
+  uint32_t off[PT];
   uint4 r[PT];
 
-  template <class RowPtr>
-  MOE_DEV void init(RowPtr rowptr) {
+  template <class RowOff>
+  MOE_DEV void init(const uint16_t* b, RowOff rowoff) {
+    base = b;
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const int v = threadIdx.x + kThreads * j;
-      rp[j] = (v < NV) ? rowptr(v / VPR) : nullptr;
+      const long long o = v < NV ? rowoff(v / VPR) : -1;
+      off[j] = o < 0 ? kNull : static_cast<uint32_t>(o + (v % VPR) * 8);
     }
   }
   MOE_DEV void load(int k0) {
 #pragma unroll
-    for (int j = 0; j < PT; ++j) {
-      const int v = threadIdx.x + kThreads * j;
-      r[j] = rp[j] ? *reinterpret_cast<const uint4*>(rp[j] + k0 + (v % VPR) * 8)
-                   : make_uint4(0, 0, 0, 0);
-    }
+    for (int j = 0; j < PT; ++j)
+      r[j] = off[j] != kNull ? *reinterpret_cast<const uint4*>(base + off[j] + k0)
+                             : make_uint4(0, 0, 0, 0);
   }
   MOE_DEV void store(uint16_t* s) const {
 #pragma unroll
@@ -115,9 +120,15 @@ struct Geo {
   static constexpr int STAGE = (BM + BN) * LDK;  // uint16 elements per LDS stage
   static constexpr int kSmem = 2 * STAGE * 2;    // bytes, two stages
   static constexpr bool kMx = false;
+  static constexpr int kWavesPerEU = 2;  // two workgroups per CU
   static_assert(WAVES_M * WAVES_N == 4, "4 waves per workgroup");
   static_assert(BK % 32 == 0 && WM % 16 == 0 && WN % 16 == 0, "tile shape");
 };
+using GeoSmall = Geo<128, 128, 64, 1, 4>;
+// Tiles of 256 full rows of one expert, for experts whose row count makes the GEMM MFMA-bound:
+// four waves of 128 x 64 each read 12 KB of LDS per 32 MFMAs, against 10 KB per 16 for the
+// 128 x 32 waves of GeoSmall. K steps of 32 keep the staged loads within the register budget.
+using GeoBig = Geo<256, 128, 32, 2, 2>;
 
 // Row segment of one expert for dynamic-M problems: table entry -> (expert, first row).
 struct MTile {
@@ -137,9 +148,10 @@ MOE_DEV MTile decode_mtile(const int2* sched, const int32_t* offsets, int mt, in
 // B rows 0..BN/2-1 of the LDS tile are gate rows n0.. of W1[e], rows BN/2.. the matching up
 // rows I+n0..; wave w owns gate columns [w*WN/2, (w+1)*WN/2) and the same up columns, so each
 // lane holds g and u for the same (row, column) and can finish SwiGLU in registers.
-struct FwdGateUp {
-  static constexpr const char* kName = "fwd_gateup";
-  using G = Geo<128, 128, 64, 1, 4>;
+template <class G_>
+struct FwdGateUpT {
+  static constexpr const char* kName = G_::BM == 256 ? "fwd_gateup_big" : "fwd_gateup";
+  using G = G_;
   struct Args {
     const uint16_t* xp;    // [T*k, d]
     const uint16_t* w1;    // [E, 2I, d]
@@ -172,14 +184,13 @@ struct FwdGateUp {
     LoadK<G::BM, G::BK, G::LDK> la;
     LoadK<G::BN, G::BK, G::LDK> lb;
     MOE_DEV void init(const Args& a, const Tile& t) {
-      const uint16_t* xp = a.xp;
-      const int d = a.d, mc = t.m.mcount, row0 = t.m.row0;
-      la.init([&](int m) { return m < mc ? xp + (size_t)(row0 + m) * d : nullptr; });
-      const uint16_t* w = a.w1 + (size_t)t.m.e * 2 * a.I * d;
+      const int d = a.d, mc = t.m.mcount;
+      la.init(a.xp + (size_t)t.m.row0 * d,
+              [&](int m) { return m < mc ? (long long)m * d : -1LL; });
       const int n0 = t.n0, I = a.I;
-      lb.init([&](int n) {
+      lb.init(a.w1 + (size_t)t.m.e * 2 * I * d, [&](int n) {
         const int row = n < G::BN / 2 ? n0 + n : I + n0 + n - G::BN / 2;
-        return w + (size_t)row * d;
+        return (long long)row * d;
       });
     }
     MOE_DEV void load(int kt) {
@@ -194,10 +205,10 @@ struct FwdGateUp {
   static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
                                uint16_t*) {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int wn = wave % G::WAVES_N;
+    const int wn = wave % G::WAVES_N, wm = wave / G::WAVES_N;
 #pragma unroll
     for (int mb = 0; mb < G::MB; ++mb) {
-      const int m = mb * 16 + lane % 16;
+      const int m = wm * G::WM + mb * 16 + lane % 16;
       if (m >= t.m.mcount) continue;
       const size_t pos = t.m.row0 + m;
 #pragma unroll
@@ -219,11 +230,15 @@ struct FwdGateUp {
   }
 };
 
+using FwdGateUp = FwdGateUpT<GeoSmall>;
+using FwdGateUpBig = FwdGateUpT<GeoBig>;
+
 // ------------------------------------------------------------------------------------------
 // Problem 2: forward down GEMM. O[pos] = A[pos] . W2[e]^T, stored bf16.
-struct FwdDown {
-  static constexpr const char* kName = "fwd_down";
-  using G = Geo<128, 128, 64, 1, 4>;
+template <class G_>
+struct FwdDownT {
+  static constexpr const char* kName = G_::BM == 256 ? "fwd_down_big" : "fwd_down";
+  using G = G_;
   struct Args {
     const uint16_t* A;   // [T*k, I]
     const uint16_t* w2;  // [E, d, I]
@@ -254,11 +269,9 @@ struct FwdDown {
     LoadK<G::BM, G::BK, G::LDK> la;
     LoadK<G::BN, G::BK, G::LDK> lb;
     MOE_DEV void init(const Args& a, const Tile& t) {
-      const uint16_t* A = a.A;
-      const int I = a.I, mc = t.m.mcount, row0 = t.m.row0;
-      la.init([&](int m) { return m < mc ? A + (size_t)(row0 + m) * I : nullptr; });
-      const uint16_t* w = a.w2 + ((size_t)t.m.e * a.d + t.n0) * I;
-      lb.init([&](int n) { return w + (size_t)n * I; });
+      const int I = a.I, mc = t.m.mcount;
+      la.init(a.A + (size_t)t.m.row0 * I, [&](int m) { return m < mc ? (long long)m * I : -1LL; });
+      lb.init(a.w2 + ((size_t)t.m.e * a.d + t.n0) * I, [&](int n) { return (long long)n * I; });
     }
     MOE_DEV void load(int kt) {
       la.load(kt * G::BK);
@@ -272,9 +285,10 @@ struct FwdDown {
   static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
                                uint16_t*) {
     const int lane = threadIdx.x % kWave, wn = (threadIdx.x / kWave) % G::WAVES_N;
+    const int wm = (threadIdx.x / kWave) / G::WAVES_N;
 #pragma unroll
     for (int mb = 0; mb < G::MB; ++mb) {
-      const int m = mb * 16 + lane % 16;
+      const int m = wm * G::WM + mb * 16 + lane % 16;
       if (m >= t.m.mcount) continue;
       const size_t pos = t.m.row0 + m;
 #pragma unroll
@@ -288,6 +302,9 @@ struct FwdDown {
     }
   }
 };
+
+using FwdDown = FwdDownT<GeoSmall>;
+using FwdDownBig = FwdDownT<GeoBig>;
 
 // ------------------------------------------------------------------------------------------
 // Problem 3: backward down dgrad with the SwiGLU backward and the router-weight gradient fused
@@ -332,10 +349,9 @@ struct BwdDownDgrad {
     const uint16_t* wb;
     int ldw;
     MOE_DEV void init(const Args& a, const Tile& t) {
-      const uint16_t* dy = a.dy;
       const int32_t* rs = a.row_src;
       const int d = a.d, k = a.k, mc = t.m.mcount, row0 = t.m.row0;
-      la.init([&](int m) { return m < mc ? dy + (size_t)(rs[row0 + m] / k) * d : nullptr; });
+      la.init(a.dy, [&](int m) { return m < mc ? (long long)(rs[row0 + m] / k) * d : -1LL; });
       wb = a.w2 + (size_t)t.m.e * a.d * a.I + t.n0;
       ldw = a.I;
     }
@@ -442,9 +458,9 @@ struct BwdGateDgrad {
     const uint16_t* wb;
     int ldw;
     MOE_DEV void init(const Args& a, const Tile& t) {
-      const uint16_t* dH = a.dH;
-      const int twoI = 2 * a.I, mc = t.m.mcount, row0 = t.m.row0;
-      la.init([&](int m) { return m < mc ? dH + (size_t)(row0 + m) * twoI : nullptr; });
+      const int twoI = 2 * a.I, mc = t.m.mcount;
+      la.init(a.dH + (size_t)t.m.row0 * twoI,
+              [&](int m) { return m < mc ? (long long)m * twoI : -1LL; });
       wb = a.w1 + (size_t)t.m.e * 2 * a.I * a.d + t.n0;
       ldw = a.d;
     }
@@ -499,6 +515,7 @@ struct GeoMx {
   static constexpr int STAGE = SC_OFF + (BM + BN) * 4;
   static constexpr int kSmem = 2 * STAGE;
   static constexpr bool kMx = true;
+  static constexpr int kWavesPerEU = 2;
   static_assert(WAVES_M * WAVES_N == 4, "4 waves per workgroup");
 };
 
@@ -1083,17 +1100,20 @@ MOE_DEV void run_tile(const typename P::Args& a, const typename P::Tile& t, uint
 #pragma unroll
       for (int ks = 0; ks < G::BK / 32; ++ks) {
         const int koff = ks * 32 + (lane / 16) * 8;
-        uint4 bf[G::NB];
+        // All fragments of the step are read before the first MFMA, so the LDS latency is paid
+        // once per step rather than once per 16-row block.
+        uint4 bf[G::NB], af[G::MB];
 #pragma unroll
         for (int nb = 0; nb < G::NB; ++nb)
           bf[nb] = *reinterpret_cast<const uint4*>(sB + (P::brow(wn, nb) + lane % 16) * G::LDK + koff);
 #pragma unroll
+        for (int mb = 0; mb < G::MB; ++mb)
+          af[mb] = *reinterpret_cast<const uint4*>(sA + (wm * G::WM + mb * 16 + lane % 16) * G::LDK + koff);
+#pragma unroll
         for (int mb = 0; mb < G::MB; ++mb) {
           if (!P::m_active(t, wm * G::WM + mb * 16)) continue;
-          const uint4 af =
-              *reinterpret_cast<const uint4*>(sA + (wm * G::WM + mb * 16 + lane % 16) * G::LDK + koff);
 #pragma unroll
-          for (int nb = 0; nb < G::NB; ++nb) acc[mb][nb] = mfma16(bf[nb], af, acc[mb][nb]);
+          for (int nb = 0; nb < G::NB; ++nb) acc[mb][nb] = mfma16(bf[nb], af[mb], acc[mb][nb]);
         }
       }
       if (kt + 1 < nk) ld.store(smem + ((kt + 1) & 1) * G::STAGE);
@@ -1105,7 +1125,7 @@ MOE_DEV void run_tile(const typename P::Args& a, const typename P::Tile& t, uint
 }
 
 template <class P>
-__global__ void __launch_bounds__(kThreads, 2) gg_kernel(const typename P::Args a) {
+__global__ void __launch_bounds__(kThreads, P::G::kWavesPerEU) gg_kernel(const typename P::Args a) {
   extern __shared__ __align__(16) uint16_t smem[];
   const int ntiles = P::ntiles(a);
   const int R = (ntiles + kXcds - 1) / kXcds;
@@ -1163,47 +1183,94 @@ static hipError_t launch(const typename P::Args& a, int max_tiles, bool persiste
 }
 
 // ------------------------------------------------------------------------------------------
-// Schedule table: one entry per (expert, 128-row block) of the permuted rows, built on the
-// device from the offsets so the host never learns the counts. Entry 0 holds the count.
+// Schedule tables, built on the device from the offsets so the host never learns the counts.
+// Entry 0 of each holds its count; entry i >= 1 is (expert, first row within the expert).
+//  * full: every 128-row block of every expert;
+//  * big:  every full 256-row block (the experts' first 256 * floor(c / 256) rows);
+//  * rem:  the 128-row blocks of what the big blocks leave of each expert (at most two).
+// Problems with a 256-row kernel run big + rem; the others run full.
 
-__global__ void __launch_bounds__(1024) sched_build_kernel(const int32_t* offsets, int E, int BM,
-                                                           int2* sched) {
+MOE_DEV int block_scan_1024(int v, int* scan) {  // inclusive scan of one value per thread
+  const int e = threadIdx.x;
+  scan[e] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int u = e >= off ? scan[e - off] : 0;
+    __syncthreads();
+    scan[e] += u;
+    __syncthreads();
+  }
+  const int r = scan[e];
+  __syncthreads();
+  return r;
+}
+
+__global__ void __launch_bounds__(1024) sched_build_kernel(const int32_t* offsets, int E,
+                                                           int2* full, int2* big, int2* rem) {
   __shared__ int scan[1024];
   const int e = threadIdx.x;
   const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
-  const int tiles = (c + BM - 1) / BM;
-  scan[e] = tiles;
-  __syncthreads();
-  // inclusive Hillis-Steele scan over 1024 entries
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = e >= off ? scan[e - off] : 0;
-    __syncthreads();
-    scan[e] += v;
-    __syncthreads();
+  const int nfull = (c + kSchedBM - 1) / kSchedBM;
+  const int nbig = c / kSchedBigBM;
+  const int nrem = (c - nbig * kSchedBigBM + kSchedBM - 1) / kSchedBM;
+  const int efull = block_scan_1024(nfull, scan);
+  const int ebig = block_scan_1024(nbig, scan);
+  const int erem = block_scan_1024(nrem, scan);
+  for (int i = 0; i < nfull; ++i) full[1 + efull - nfull + i] = make_int2(e, i * kSchedBM);
+  for (int i = 0; i < nbig; ++i) big[1 + ebig - nbig + i] = make_int2(e, i * kSchedBigBM);
+  for (int i = 0; i < nrem; ++i)
+    rem[1 + erem - nrem + i] = make_int2(e, nbig * kSchedBigBM + i * kSchedBM);
+  if (e == 1023) {
+    full[0] = make_int2(efull, 0);
+    big[0] = make_int2(ebig, 0);
+    rem[0] = make_int2(erem, 0);
   }
-  const int start = scan[e] - tiles;
-  for (int i = 0; i < tiles; ++i) sched[1 + start + i] = make_int2(e, i * BM);
-  if (e == 1023) sched[0] = make_int2(scan[1023], 0);
 }
 
 int sched_max_mtiles(int Tk, int E) { return (Tk + E * (kSchedBM - 1)) / kSchedBM; }
+int sched_max_big(int Tk) { return Tk / kSchedBigBM; }
+int sched_max_rem(int Tk, int E) { return std::min(2 * E, sched_max_mtiles(Tk, E)); }
+size_t sched_entries(int Tk, int E) {
+  return 3 + (size_t)sched_max_mtiles(Tk, E) + sched_max_big(Tk) + sched_max_rem(Tk, E);
+}
+namespace {
+struct SchedTables {
+  int2 *full, *big, *rem;
+};
+SchedTables sched_tables(const int2* sched, int Tk, int E) {
+  int2* f = const_cast<int2*>(sched);
+  int2* b = f + 1 + sched_max_mtiles(Tk, E);
+  return {f, b, b + 1 + sched_max_big(Tk)};
+}
+}  // namespace
 
-hipError_t launch_sched_build(const int32_t* offsets, int E, int2* sched, hipStream_t s) {
+hipError_t launch_sched_build(const int32_t* offsets, int E, int Tk, int2* sched, hipStream_t s) {
+  const SchedTables t = sched_tables(sched, Tk, E);
   {
     TraceScope trace("sched_build", s);
-    hipLaunchKernelGGL(sched_build_kernel, dim3(1), dim3(1024), 0, s, offsets, E, kSchedBM, sched);
+    hipLaunchKernelGGL(sched_build_kernel, dim3(1), dim3(1024), 0, s, offsets, E, t.full, t.big,
+                       t.rem);
   }
   return hipGetLastError();
 }
 
+// The forward GEMMs run the 256-row blocks with the big-tile kernel, then the remainders.
 hipError_t launch_fwd_gateup(const GemmFwdGateUpArgs& x, bool persistent, hipStream_t s) {
-  FwdGateUp::Args a{x.xp, x.w1, x.H, x.A, x.offsets, x.sched, x.d, x.I};
-  return launch<FwdGateUp>(a, sched_max_mtiles(x.Tk, x.E) * (x.I / 64), persistent, s);
+  const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
+  FwdGateUpBig::Args ab{x.xp, x.w1, x.H, x.A, x.offsets, st.big, x.d, x.I};
+  hipError_t e = launch<FwdGateUpBig>(ab, sched_max_big(x.Tk) * (x.I / 64), persistent, s);
+  if (e != hipSuccess) return e;
+  FwdGateUp::Args a{x.xp, x.w1, x.H, x.A, x.offsets, st.rem, x.d, x.I};
+  return launch<FwdGateUp>(a, sched_max_rem(x.Tk, x.E) * (x.I / 64), persistent, s);
 }
 
 hipError_t launch_fwd_down(const GemmFwdDownArgs& x, bool persistent, hipStream_t s) {
-  FwdDown::Args a{x.A, x.w2, x.O, x.offsets, x.sched, x.d, x.I};
-  return launch<FwdDown>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
+  const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
+  FwdDownBig::Args ab{x.A, x.w2, x.O, x.offsets, st.big, x.d, x.I};
+  hipError_t e = launch<FwdDownBig>(ab, sched_max_big(x.Tk) * (x.d / 128), persistent, s);
+  if (e != hipSuccess) return e;
+  FwdDown::Args a{x.A, x.w2, x.O, x.offsets, st.rem, x.d, x.I};
+  return launch<FwdDown>(a, sched_max_rem(x.Tk, x.E) * (x.d / 128), persistent, s);
 }
 
 hipError_t launch_bwd_down_dgrad(const GemmBwdDownDgradArgs& x, bool persistent, hipStream_t s) {

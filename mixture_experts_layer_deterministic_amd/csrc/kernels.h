@@ -19,6 +19,7 @@ struct TraceScope {
 };
 
 constexpr int kSchedBM = 128;   // rows per M-tile of the forward/dgrad grouped GEMMs
+constexpr int kSchedBigBM = 256;  // rows per M-tile of the big-tile forward GEMMs
 constexpr int kDgradBN = 128;   // columns per N-tile of the down dgrad (dw partials per row)
 constexpr int kPermRows = 256;  // rows per histogram block of the permutation
 constexpr int kMaxTopK = 64;
@@ -44,7 +45,11 @@ hipError_t launch_perm_place(const int32_t* idx, const int32_t* rank, const int3
 
 // gemm.hip
 int sched_max_mtiles(int Tk, int E);
-hipError_t launch_sched_build(const int32_t* offsets, int E, int2* sched, hipStream_t s);
+int sched_max_big(int Tk);
+int sched_max_rem(int Tk, int E);
+// int2 entries of the schedule region: the full, big and remainder tables back to back
+size_t sched_entries(int Tk, int E);
+hipError_t launch_sched_build(const int32_t* offsets, int E, int Tk, int2* sched, hipStream_t s);
 
 struct GemmFwdGateUpArgs {
   const uint16_t* xp;

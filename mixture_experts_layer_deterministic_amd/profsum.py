@@ -37,6 +37,8 @@ KERNELS = [
     (r"perm_place_kernel", "perm_place", "permute.hip"),
     (r"wgrad_sched_kernel", "wgrad_sched", "wgrad.hip"),
     (r"sched_build_kernel", "sched_build", "gemm.hip"),
+    (r"gg_kernel<moe::FwdGateUpT<moe::Geo<256", "fwd_gateup_big", "gemm.hip"),
+    (r"gg_kernel<moe::FwdDownT<moe::Geo<256", "fwd_down_big", "gemm.hip"),
     (r"gg_kernel<moe::FwdGateUp", "fwd_gateup", "gemm.hip"),
     (r"gg_kernel<moe::FwdDown", "fwd_down", "gemm.hip"),
     (r"gg_kernel<moe::BwdDownDgrad", "bwd_down_dgrad", "gemm.hip"),
