@@ -148,6 +148,25 @@ MOE_DEV MTile decode_mtile(const int2* sched, const int32_t* offsets, int mt, in
 // B rows 0..BN/2-1 of the LDS tile are gate rows n0.. of W1[e], rows BN/2.. the matching up
 // rows I+n0..; wave w owns gate columns [w*WN/2, (w+1)*WN/2) and the same up columns, so each
 // lane holds g and u for the same (row, column) and can finish SwiGLU in registers.
+// Linear tile index -> (m-tile, n-tile). Ungrouped, n runs fastest: the workgroups an XCD runs
+// at once share one m-tile's activations in its L2. Grouped, kGroupM consecutive m-tiles take
+// each n-tile in turn, so the workgroups in flight on an XCD share a few activation panels and
+// a few weight panels: an expert with many row blocks re-reads each weight panel once per block,
+// and grouped blocks fetch it from L2 rather than from beyond it.
+constexpr int kGroupM = 4;
+template <bool kGrouped>
+MOE_DEV int2 tile_mn(int lt, int nm, int ntc) {
+  if constexpr (!kGrouped) {
+    return make_int2(lt / ntc, lt % ntc);
+  } else {
+    const int group = lt / (kGroupM * ntc);
+    const int m_first = group * kGroupM;
+    const int gm = min(kGroupM, nm - m_first);
+    const int r = lt - m_first * ntc;
+    return make_int2(m_first + r % gm, r / gm);
+  }
+}
+
 template <class G_>
 struct FwdGateUpT {
   static constexpr const char* kName = G_::BM == 256 ? "fwd_gateup_big" : "fwd_gateup";
@@ -168,9 +187,10 @@ struct FwdGateUpT {
   static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.I / (G::BN / 2)); }
   static MOE_DEV Tile decode(const Args& a, int lt) {
     const int nt_count = a.I / (G::BN / 2);
+    const int2 mn = tile_mn<(G::BM > 128)>(lt, a.sched[0].x, nt_count);
     Tile t;
-    t.m = decode_mtile(a.sched, a.offsets, lt / nt_count, G::BM);
-    t.n0 = (lt % nt_count) * (G::BN / 2);
+    t.m = decode_mtile(a.sched, a.offsets, mn.x, G::BM);
+    t.n0 = mn.y * (G::BN / 2);
     return t;
   }
   static MOE_DEV int num_k(const Args& a, const Tile&) { return a.d / G::BK; }
@@ -254,9 +274,10 @@ struct FwdDownT {
   static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.d / G::BN); }
   static MOE_DEV Tile decode(const Args& a, int lt) {
     const int ntc = a.d / G::BN;
+    const int2 mn = tile_mn<(G::BM > 128)>(lt, a.sched[0].x, ntc);
     Tile t;
-    t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
-    t.n0 = (lt % ntc) * G::BN;
+    t.m = decode_mtile(a.sched, a.offsets, mn.x, G::BM);
+    t.n0 = mn.y * G::BN;
     return t;
   }
   static MOE_DEV int num_k(const Args& a, const Tile&) { return a.I / G::BK; }
@@ -334,9 +355,10 @@ struct BwdDownDgrad {
   static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.I / G::BN); }
   static MOE_DEV Tile decode(const Args& a, int lt) {
     const int ntc = a.I / G::BN;
+    const int2 mn = tile_mn<true>(lt, a.sched[0].x, ntc);
     Tile t;
-    t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
-    t.n0 = (lt % ntc) * G::BN;
+    t.m = decode_mtile(a.sched, a.offsets, mn.x, G::BM);
+    t.n0 = mn.y * G::BN;
     return t;
   }
   static MOE_DEV int num_k(const Args& a, const Tile&) { return a.d / G::BK; }
@@ -443,9 +465,10 @@ struct BwdGateDgrad {
   static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.d / G::BN); }
   static MOE_DEV Tile decode(const Args& a, int lt) {
     const int ntc = a.d / G::BN;
+    const int2 mn = tile_mn<true>(lt, a.sched[0].x, ntc);
     Tile t;
-    t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
-    t.n0 = (lt % ntc) * G::BN;
+    t.m = decode_mtile(a.sched, a.offsets, mn.x, G::BM);
+    t.n0 = mn.y * G::BN;
     return t;
   }
   static MOE_DEV int num_k(const Args& a, const Tile&) { return 2 * a.I / G::BK; }
@@ -800,9 +823,10 @@ struct MxFwdDown {
   static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.d / G::BN); }
   static MOE_DEV Tile decode(const Args& a, int lt) {
     const int ntc = a.d / G::BN;
+    const int2 mn = tile_mn<(G::BM > 128)>(lt, a.sched[0].x, ntc);
     Tile t;
-    t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
-    t.n0 = (lt % ntc) * G::BN;
+    t.m = decode_mtile(a.sched, a.offsets, mn.x, G::BM);
+    t.n0 = mn.y * G::BN;
     return t;
   }
   static MOE_DEV int num_k(const Args& a, const Tile&) { return a.I / G::BK; }
