@@ -30,11 +30,11 @@ constexpr int kThreads = 256;
 // ROWS x BK tile whose rows are K-contiguous in memory. Rows are element offsets from one base
 // pointer (32 bits each, so a thread holds one register per row rather than a pointer);
 // rowoff(r) < 0 marks a row that loads zeros.
-template <int ROWS, int BK, int LDK>
+template <int ROWS, int BK, int LDK, int THREADS = kThreads>
 struct LoadK {
   static constexpr int VPR = BK / 8;
   static constexpr int NV = ROWS * VPR;
-  static constexpr int PT = (NV + kThreads - 1) / kThreads;
+  static constexpr int PT = (NV + THREADS - 1) / THREADS;
   static constexpr uint32_t kNull = 0xffffffffu;
   const uint16_t* base;
   uint32_t off[PT];
@@ -45,7 +45,7 @@ struct LoadK {
     base = b;
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
-      const int v = threadIdx.x + kThreads * j;
+      const int v = threadIdx.x + THREADS * j;
       const long long o = v < NV ? rowoff(v / VPR) : -1;
       off[j] = o < 0 ? kNull : static_cast<uint32_t>(o + (v % VPR) * 8);
     }
@@ -59,7 +59,7 @@ struct LoadK {
   MOE_DEV void store(uint16_t* s) const {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
-      const int v = threadIdx.x + kThreads * j;
+      const int v = threadIdx.x + THREADS * j;
       if (v < NV) *reinterpret_cast<uint4*>(s + (v / VPR) * LDK + (v % VPR) * 8) = r[j];
     }
   }
@@ -120,15 +120,17 @@ struct Geo {
   static constexpr int STAGE = (BM + BN) * LDK;  // uint16 elements per LDS stage
   static constexpr int kSmem = 2 * STAGE * 2;    // bytes, two stages
   static constexpr bool kMx = false;
-  static constexpr int kWavesPerEU = 2;  // two workgroups per CU
-  static_assert(WAVES_M * WAVES_N == 4, "4 waves per workgroup");
+  static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
+  static constexpr int kWavesPerEU = 2;  // at most 256 registers per lane
+  static_assert(WAVES_M * WAVES_N == 4 || WAVES_M * WAVES_N == 8, "4 or 8 waves per workgroup");
   static_assert(BK % 32 == 0 && WM % 16 == 0 && WN % 16 == 0, "tile shape");
 };
 using GeoSmall = Geo<128, 128, 64, 1, 4>;
-// Tiles of 256 full rows of one expert, for experts whose row count makes the GEMM MFMA-bound:
-// four waves of 128 x 64 each read 12 KB of LDS per 32 MFMAs, against 10 KB per 16 for the
-// 128 x 32 waves of GeoSmall. K steps of 32 keep the staged loads within the register budget.
-using GeoBig = Geo<256, 128, 32, 2, 2>;
+// Tiles of 256 full rows of one expert, for experts whose row count makes the GEMM MFMA-bound.
+// There the operands come from L2, whose delivery to the CUs (about 8-9 TB/s measured) bounds
+// the rate at (flops per tile byte) x 8 TB/s: 64 flop/B for 128 x 128 tiles, 128 for 256 x 256.
+// Eight waves of 128 x 64 (128 accumulators each) make the 256 x 256 tile; one workgroup per CU.
+using GeoBig = Geo<256, 256, 64, 2, 4>;
 
 // Row segment of one expert for dynamic-M problems: table entry -> (expert, first row).
 struct MTile {
@@ -201,8 +203,8 @@ struct FwdGateUpT {
     return nb < G::NB / 2 ? wn * WH + nb * 16 : H2 + wn * WH + (nb - G::NB / 2) * 16;
   }
   struct Loader {
-    LoadK<G::BM, G::BK, G::LDK> la;
-    LoadK<G::BN, G::BK, G::LDK> lb;
+    LoadK<G::BM, G::BK, G::LDK, G::THREADS> la;
+    LoadK<G::BN, G::BK, G::LDK, G::THREADS> lb;
     MOE_DEV void init(const Args& a, const Tile& t) {
       const int d = a.d, mc = t.m.mcount;
       la.init(a.xp + (size_t)t.m.row0 * d,
@@ -287,8 +289,8 @@ struct FwdDownT {
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
-    LoadK<G::BM, G::BK, G::LDK> la;
-    LoadK<G::BN, G::BK, G::LDK> lb;
+    LoadK<G::BM, G::BK, G::LDK, G::THREADS> la;
+    LoadK<G::BN, G::BK, G::LDK, G::THREADS> lb;
     MOE_DEV void init(const Args& a, const Tile& t) {
       const int I = a.I, mc = t.m.mcount;
       la.init(a.A + (size_t)t.m.row0 * I, [&](int m) { return m < mc ? (long long)m * I : -1LL; });
@@ -538,6 +540,7 @@ struct GeoMx {
   static constexpr int STAGE = SC_OFF + (BM + BN) * 4;
   static constexpr int kSmem = 2 * STAGE;
   static constexpr bool kMx = true;
+  static constexpr int THREADS = kThreads;
   static constexpr int kWavesPerEU = 2;
   static_assert(WAVES_M * WAVES_N == 4, "4 waves per workgroup");
 };
@@ -1149,7 +1152,7 @@ MOE_DEV void run_tile(const typename P::Args& a, const typename P::Tile& t, uint
 }
 
 template <class P>
-__global__ void __launch_bounds__(kThreads, P::G::kWavesPerEU) gg_kernel(const typename P::Args a) {
+__global__ void __launch_bounds__(P::G::THREADS, P::G::kWavesPerEU) gg_kernel(const typename P::Args a) {
   extern __shared__ __align__(16) uint16_t smem[];
   const int ntiles = P::ntiles(a);
   const int R = (ntiles + kXcds - 1) / kXcds;
@@ -1193,7 +1196,7 @@ static hipError_t launch(const typename P::Args& a, int max_tiles, bool persiste
       if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
       if (e == hipSuccess)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&gg_kernel<P>), kThreads, sm);
+            &per_cu, reinterpret_cast<const void*>(&gg_kernel<P>), P::G::THREADS, sm);
       if (e != hipSuccess) return e;
       resident = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
     }
@@ -1201,7 +1204,7 @@ static hipError_t launch(const typename P::Args& a, int max_tiles, bool persiste
   }
   {
     TraceScope trace(P::kName, stream);
-    hipLaunchKernelGGL(gg_kernel<P>, dim3(grid), dim3(kThreads), sm, stream, a);
+    hipLaunchKernelGGL(gg_kernel<P>, dim3(grid), dim3(P::G::THREADS), sm, stream, a);
   }
   return hipGetLastError();
 }
@@ -1282,7 +1285,7 @@ hipError_t launch_sched_build(const int32_t* offsets, int E, int Tk, int2* sched
 hipError_t launch_fwd_gateup(const GemmFwdGateUpArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
   FwdGateUpBig::Args ab{x.xp, x.w1, x.H, x.A, x.offsets, st.big, x.d, x.I};
-  hipError_t e = launch<FwdGateUpBig>(ab, sched_max_big(x.Tk) * (x.I / 64), persistent, s);
+  hipError_t e = launch<FwdGateUpBig>(ab, sched_max_big(x.Tk) * (x.I / 128), persistent, s);
   if (e != hipSuccess) return e;
   FwdGateUp::Args a{x.xp, x.w1, x.H, x.A, x.offsets, st.rem, x.d, x.I};
   return launch<FwdGateUp>(a, sched_max_rem(x.Tk, x.E) * (x.I / 64), persistent, s);
@@ -1291,7 +1294,7 @@ hipError_t launch_fwd_gateup(const GemmFwdGateUpArgs& x, bool persistent, hipStr
 hipError_t launch_fwd_down(const GemmFwdDownArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
   FwdDownBig::Args ab{x.A, x.w2, x.O, x.offsets, st.big, x.d, x.I};
-  hipError_t e = launch<FwdDownBig>(ab, sched_max_big(x.Tk) * (x.d / 128), persistent, s);
+  hipError_t e = launch<FwdDownBig>(ab, sched_max_big(x.Tk) * (x.d / 256), persistent, s);
   if (e != hipSuccess) return e;
   FwdDown::Args a{x.A, x.w2, x.O, x.offsets, st.rem, x.d, x.I};
   return launch<FwdDown>(a, sched_max_rem(x.Tk, x.E) * (x.d / 128), persistent, s);
