@@ -87,6 +87,26 @@ def test_all_rows_to_one_expert_and_empty_experts():
         assert torch.count_nonzero(L.dw1[e]) == 0 and torch.count_nonzero(L.dw2[e]) == 0
 
 
+def test_expert_sizes_at_the_256_row_block_boundaries():
+    """Experts of 0, 1, 128, 255, 256, 257, 384, 511, 512 and 513 rows: the forward GEMMs split
+    each expert into full 256-row blocks (big-tile kernel) and 128-row remainder tiles. Parity
+    against the oracle, and persistent grids bitwise equal to one-shot grids."""
+    counts = [255, 256, 257, 0, 511, 512, 513, 1, 128, 384]
+    _announce(f"[blocks] expert sizes {counts}, d=256 I=256 k=1")
+    E, d, I = len(counts), 256, 256
+    T = sum(counts)
+    inp = workload.make_inputs("local_zipf", seed=9, device=DEV, T=T, d=d, E=E, I=I)
+    idx = np.repeat(np.arange(E, dtype=np.int32), counts)
+    np.random.default_rng(9).shuffle(idx)
+    inp["topk_idx"] = torch.from_numpy(idx.reshape(T, 1)).to(DEV)
+    L = run_gpu(inp)
+    f, b = run_oracle(inp)
+    assert list(f["counts"]) == counts
+    check_parity(L, inp, f, b)
+    a = outputs(L, False)
+    assert_bitwise_equal(a, outputs(run_gpu(inp, persistent=True), False))
+
+
 def test_zero_router_and_duplicate_router_rows():
     _announce("[ties] zero router, duplicate rows")
     inp = workload.make_inputs("tiny", seed=5, device=DEV)
