@@ -8,10 +8,11 @@
 //   bwd  down dg : dA'[pos]     = dY[t]    . W2[e]        SwiGLU backward + router-weight grad
 //   bwd  gate dg : dXp[pos]     = dH[pos]  . W1[e]
 // The two weight gradients have their own kernel (wgrad.hip). One kernel template runs the
-// four. A workgroup (256 threads, 4 waves) owns a BM x BN output tile. Tiles of BK stream
-// through double-buffered LDS, stored K-contiguous with 8 elements of padding per row, so every
-// MFMA fragment is one 16-byte LDS read. The weights in dgrad, whose K axis is not contiguous
-// in memory, are loaded as 8x8 blocks and transposed in registers on their way into LDS.
+// four, in BF16 and (further down) in MXFP8. A workgroup owns a BM x BN output tile: 128 x 128
+// with 4 waves, or 256 x 256 with 8 waves for the forward GEMMs' full 256-row expert blocks.
+// Tiles of BK stream through double-buffered LDS, stored K-contiguous with padding per row, so
+// every MFMA fragment is one 16-byte LDS read. The weights in dgrad, whose K axis is not
+// contiguous in memory, are loaded as 8x8 blocks and transposed in registers on their way in.
 //
 // Determinism: every output element is produced by exactly one workgroup, which reduces K in a
 // fixed order. There are no atomics and no split-K.
@@ -127,9 +128,10 @@ struct Geo {
 };
 using GeoSmall = Geo<128, 128, 64, 1, 4>;
 // Tiles of 256 full rows of one expert, for experts whose row count makes the GEMM MFMA-bound.
-// There the operands come from L2, whose delivery to the CUs (about 8-9 TB/s measured) bounds
-// the rate at (flops per tile byte) x 8 TB/s: 64 flop/B for 128 x 128 tiles, 128 for 256 x 256.
-// Eight waves of 128 x 64 (128 accumulators each) make the 256 x 256 tile; one workgroup per CU.
+// There the kernel's rate follows the flops per byte its tile loads (mostly L2 hits): 64 flop/B
+// for 128 x 128 tiles, 128 for 256 x 256. Eight waves of 128 x 64 (128 accumulators each) make
+// the 256 x 256 tile, one workgroup per CU; K steps of 64 keep each row load a whole 128-byte
+// line (steps of 32 fetched half lines and ran 16% slower).
 using GeoBig = Geo<256, 256, 64, 2, 4>;
 
 // Row segment of one expert for dynamic-M problems: table entry -> (expert, first row).
@@ -145,11 +147,6 @@ MOE_DEV MTile decode_mtile(const int2* sched, const int32_t* offsets, int mt, in
   return t;
 }
 
-// ------------------------------------------------------------------------------------------
-// Problem 1: forward gate/up GEMM with the SwiGLU epilogue.
-// B rows 0..BN/2-1 of the LDS tile are gate rows n0.. of W1[e], rows BN/2.. the matching up
-// rows I+n0..; wave w owns gate columns [w*WN/2, (w+1)*WN/2) and the same up columns, so each
-// lane holds g and u for the same (row, column) and can finish SwiGLU in registers.
 // Linear tile index -> (m-tile, n-tile). Ungrouped, n runs fastest: the workgroups an XCD runs
 // at once share one m-tile's activations in its L2. Grouped, kGroupM consecutive m-tiles take
 // each n-tile in turn, so the workgroups in flight on an XCD share a few activation panels and
@@ -169,6 +166,11 @@ MOE_DEV int2 tile_mn(int lt, int nm, int ntc) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Problem 1: forward gate/up GEMM with the SwiGLU epilogue.
+// B rows 0..BN/2-1 of the LDS tile are gate rows n0.. of W1[e], rows BN/2.. the matching up
+// rows I+n0..; wave w owns gate columns [w*WN/2, (w+1)*WN/2) and the same up columns, so each
+// lane holds g and u for the same (row, column) and can finish SwiGLU in registers.
 template <class G_>
 struct FwdGateUpT {
   static constexpr const char* kName = G_::BM == 256 ? "fwd_gateup_big" : "fwd_gateup";
