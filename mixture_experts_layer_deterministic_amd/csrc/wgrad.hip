@@ -196,9 +196,18 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
   // Round r gives XCD x the contiguous task range [r G + x G/8, r G + (x+1) G/8), so tasks of
   // one expert (adjacent in the table) share that XCD's L2. Producers and consumers walk the
   // same tasks in separate loops, which keeps their register live ranges apart.
+  // A task's tiles are its stripe's n-tiles [tfirst, tfirst + nt), taken rotated by rot: the
+  // stripes of one expert run at the same time on one XCD, and without the rotation they would
+  // all write the same columns of rows a stripe apart, which alias in HBM. The rotation is a
+  // bijection of the stripe's tiles and changes no value.
+  const int ntn = a.Ndim / BN;
   struct TaskInfo {
-    int e, m0, nt, nfirst, p0, p1, nk, total;
+    int e, m0, nt, tfirst, rot, p0, p1, nk, total;
     bool resident;
+    MOE_DEV int col(int j, int ntn) const {
+      const int q = tfirst + j + rot;
+      return (q < ntn ? q : q - ntn) * BN;
+    }
   };
   auto task_at = [&](int ti) {
     const int4 task = table[ti];
@@ -206,7 +215,8 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
     t.e = task.x;
     t.m0 = task.y;
     t.nt = task.w;
-    t.nfirst = task.z * BN;
+    t.tfirst = task.z;
+    t.rot = (5 * (task.y / BM) + 3 * task.x) % ntn;
     t.p0 = offsets[t.e];
     t.p1 = offsets[t.e + 1];
     t.nk = (t.p1 - t.p0 + BK - 1) / BK;
@@ -221,7 +231,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
       if (ti >= ntasks) break;
       const TaskInfo t = task_at(ti);
       if (t.nk == 0) continue;
-      const int p0 = t.p0, p1 = t.p1, nk = t.nk, total = t.total, nfirst = t.nfirst;
+      const int p0 = t.p0, p1 = t.p1, nk = t.nk, total = t.total;
       const bool resident = t.resident;
       Mover<BM / 64> ml;
       Mover<BN / 64> mr;
@@ -240,7 +250,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
       // chunk pq: loads now; chunk 0 is written before the first barrier
       if (pq < total) {
         const int pb = p0 + (pq % nk) * BK;
-        mr.load<R8>(pb, p1, nfirst + (pq / nk) * BN, lane);
+        mr.load<R8>(pb, p1, t.col(pq / nk, ntn), lane);
         if (!resident) ml.load(pb, p1, 0, lane);
         if (pq == 0) {
           mr.store<R8>(rbuf, LDR, 0, lane);
@@ -257,7 +267,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
         const int cn = it + kProducers;
         if (it % kProducers == pq && cn < total) {
           const int pb = p0 + (cn % nk) * BK;
-          mr.load<R8>(pb, p1, nfirst + (cn / nk) * BN, lane);
+          mr.load<R8>(pb, p1, t.col(cn / nk, ntn), lane);
           if (!resident) ml.load(pb, p1, 0, lane);
         }
         lds_barrier();
@@ -269,7 +279,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
       const int ti = round * G + xcd * G8 + slot;
       if (ti >= ntasks) break;
       const TaskInfo t = task_at(ti);
-      const int nk = t.nk, total = t.total, nfirst = t.nfirst;
+      const int nk = t.nk, total = t.total;
       const bool resident = t.resident;
       float* out = a.dw + ((size_t)t.e * a.Mdim + t.m0) * a.Ndim;
       f32x4 acc[MBW][4];
@@ -279,7 +289,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
         for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (nk == 0) {  // an expert with no rows: its dW block is zero
         if (!ACC)
-          for (int j = 0; j < t.nt; ++j) store_tile<false>(a, out, nfirst + j * BN, acc);
+          for (int j = 0; j < t.nt; ++j) store_tile<false>(a, out, t.col(j, ntn), acc);
         continue;
       }
       lds_barrier();
@@ -299,7 +309,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
           for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(bf[nb], af, acc[mb][nb]);
         }
         if (kt == nk - 1) {
-          store_tile<ACC>(a, out, nfirst + j * BN, acc);
+          store_tile<ACC>(a, out, t.col(j, ntn), acc);
 #pragma unroll
           for (int i = 0; i < MBW; ++i)
 #pragma unroll
