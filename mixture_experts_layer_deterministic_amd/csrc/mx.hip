@@ -63,7 +63,13 @@ __global__ void __launch_bounds__(256) quant_weight_kernel(const uint16_t* __res
   static_assert(kQT * OP <= kQT * TP, "column codes fit in the tile's LDS");
   __shared__ uint32_t tile[kQT * TP];
   __shared__ uint32_t scT[kQT];  // the column's four scale codes, one per byte
-  const int b = blockIdx.z, r0 = blockIdx.y * kQT, c0 = blockIdx.x * kQT;
+  // Tiles in diagonal order: workgroups adjacent in launch order differ in both tile row and
+  // tile column, so those in flight at once neither write the transposed codes at one column
+  // of rows R bytes apart nor the row codes at one column of rows C bytes apart.
+  const int b = blockIdx.z, nx = gridDim.x, ny = gridDim.y;
+  const int lin = blockIdx.y * nx + blockIdx.x;
+  const int ty = lin % ny, tx = (lin / ny + ty) % nx;
+  const int r0 = ty * kQT, c0 = tx * kQT;
   const int t = threadIdx.x;
   const uint16_t* s = src + ((size_t)b * R + r0) * C + c0;
   // Phase 1: sixteen lanes per row, eight elements per lane; lanes 4q..4q+3 make one 32-block.
