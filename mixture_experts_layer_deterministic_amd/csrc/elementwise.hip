@@ -93,7 +93,10 @@ __global__ void __launch_bounds__(256) dw_router_kernel(const float* __restrict_
 }
 
 // dx[t] = bf16( sum_j dXp[tk_row[t*k+j]] + sum_j dl_j * Wr[e_j] ), j ascending, fp32; the
-// router term only when wr is given.
+// router term only when wr is given. ONE_GROUP (k <= kGather): the row indices and expert
+// indices are loaded first, then every dXp row, router row and dl together, so a token costs
+// two round trips to memory; the sums keep the order above.
+template <bool ONE_GROUP>
 __global__ void __launch_bounds__(256) uncombine_kernel(
     const uint16_t* __restrict__ dXp, const int32_t* __restrict__ tk_row,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ dl_pos,
@@ -104,6 +107,54 @@ __global__ void __launch_bounds__(256) uncombine_kernel(
     const int t = t0 + i / vpr, v = i % vpr;
     if (t >= T) continue;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if constexpr (ONE_GROUP) {
+      int pos[kGather], e[kGather];
+#pragma unroll
+      for (int j = 0; j < kGather; ++j) {
+        pos[j] = j < k ? tk_row[(size_t)t * k + j] : -1;
+        e[j] = wr && j < k ? topk_idx[(size_t)t * k + j] : 0;
+      }
+      uint4 g[kGather], h[kGather];
+      float dl[kGather];
+#pragma unroll
+      for (int j = 0; j < kGather; ++j) {
+        const bool live = pos[j] >= 0;
+        g[j] = live ? *reinterpret_cast<const uint4*>(dXp + (size_t)pos[j] * d + v * 8)
+                    : make_uint4(0, 0, 0, 0);
+        h[j] = wr && live ? *reinterpret_cast<const uint4*>(wr + (size_t)e[j] * d + v * 8)
+                          : make_uint4(0, 0, 0, 0);
+        dl[j] = wr && live ? dl_pos[pos[j]] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < kGather; ++j) {
+        if (pos[j] < 0) continue;
+        const uint32_t gw[4] = {g[j].x, g[j].y, g[j].z, g[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += bf2f_lo(gw[q]);
+          acc[2 * q + 1] += bf2f_hi(gw[q]);
+        }
+      }
+      if (wr) {
+#pragma unroll
+        for (int j = 0; j < kGather; ++j) {
+          if (pos[j] < 0) continue;
+          const uint32_t hw[4] = {h[j].x, h[j].y, h[j].z, h[j].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] = __builtin_fmaf(dl[j], bf2f_lo(hw[q]), acc[2 * q]);
+            acc[2 * q + 1] = __builtin_fmaf(dl[j], bf2f_hi(hw[q]), acc[2 * q + 1]);
+          }
+        }
+      }
+      uint4 out;
+      out.x = pack_bf2(acc[0], acc[1]);
+      out.y = pack_bf2(acc[2], acc[3]);
+      out.z = pack_bf2(acc[4], acc[5]);
+      out.w = pack_bf2(acc[6], acc[7]);
+      *reinterpret_cast<uint4*>(dx + (size_t)t * d + v * 8) = out;
+      continue;
+    }
     for (int j0 = 0; j0 < k; j0 += kGather) {
       int pos[kGather];
       uint4 g[kGather];
@@ -240,8 +291,13 @@ hipError_t launch_uncombine(const uint16_t* dXp, const int32_t* tk_row, const in
   const int tpb = rows_per_block(d);
   {
     TraceScope trace("uncombine", s);
-    hipLaunchKernelGGL(uncombine_kernel, dim3((T + tpb - 1) / tpb), dim3(256), 0, s, dXp, tk_row,
-                       topk_idx, dl_pos, wr, T, k, d, dx, tpb);
+    const dim3 grid((T + tpb - 1) / tpb);
+    if (k <= kGather)
+      hipLaunchKernelGGL(uncombine_kernel<true>, grid, dim3(256), 0, s, dXp, tk_row, topk_idx,
+                         dl_pos, wr, T, k, d, dx, tpb);
+    else
+      hipLaunchKernelGGL(uncombine_kernel<false>, grid, dim3(256), 0, s, dXp, tk_row, topk_idx,
+                         dl_pos, wr, T, k, d, dx, tpb);
   }
   return hipGetLastError();
 }
