@@ -225,31 +225,53 @@ __global__ void __launch_bounds__(64) dwr_kernel(const float* __restrict__ dl_po
   if (c0 >= d) return;
   const int p0 = offsets[e], p1 = offsets[e + 1];
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int p = p0; p < p1; ++p) {
-    const float dl = dl_pos[p];
-    float xv[8];
-    if constexpr (MX) {
-      const uint2 q = *reinterpret_cast<const uint2*>(xp8 + (size_t)p * d + c0);
-      const float s = mx_scale(xps[(size_t)p * (d / 32) + c0 / 32]);
-      float f[4], g[4];
-      e4m3x4_to_f32(q.x, f);
-      e4m3x4_to_f32(q.y, g);
+  // positions in groups of U: the group's loads are issued before its FMAs (p ascending)
+  constexpr int U = 8;
+  for (int pg = p0; pg < p1; pg += U) {
+    float dl[U];
+    uint4 raw[U];
+    uint32_t sc[U];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        xv[q4] = f[q4] * s;
-        xv[4 + q4] = g[q4] * s;
-      }
-    } else {
-      const uint4 g = *reinterpret_cast<const uint4*>(xp + (size_t)p * d + c0);
-      const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        xv[2 * q] = bf2f_lo(gw[q]);
-        xv[2 * q + 1] = bf2f_hi(gw[q]);
+    for (int u = 0; u < U; ++u) {
+      const int p = pg + u;
+      const bool live = p < p1;
+      dl[u] = live ? dl_pos[p] : 0.f;
+      if constexpr (MX) {
+        const uint2 q = live ? *reinterpret_cast<const uint2*>(xp8 + (size_t)p * d + c0)
+                             : make_uint2(0, 0);
+        raw[u] = make_uint4(q.x, q.y, 0, 0);
+        sc[u] = live ? xps[(size_t)p * (d / 32) + c0 / 32] : 0u;
+      } else {
+        raw[u] = live ? *reinterpret_cast<const uint4*>(xp + (size_t)p * d + c0)
+                      : make_uint4(0, 0, 0, 0);
+        sc[u] = 0u;
       }
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(dl, xv[q], acc[q]);
+    for (int u = 0; u < U; ++u) {
+      if (pg + u >= p1) break;
+      float xv[8];
+      if constexpr (MX) {
+        const float s = mx_scale(sc[u]);
+        float f[4], g[4];
+        e4m3x4_to_f32(raw[u].x, f);
+        e4m3x4_to_f32(raw[u].y, g);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          xv[q4] = f[q4] * s;
+          xv[4 + q4] = g[q4] * s;
+        }
+      } else {
+        const uint32_t gw[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xv[2 * q] = bf2f_lo(gw[q]);
+          xv[2 * q + 1] = bf2f_hi(gw[q]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(dl[u], xv[q], acc[q]);
+    }
   }
   float4* dst = reinterpret_cast<float4*>(dwr + (size_t)e * d + c0);
   float4 a = make_float4(acc[0], acc[1], acc[2], acc[3]);
