@@ -61,35 +61,30 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
   }
 }
 
-// One thread per token: dw of each of its rows (the down-dgrad epilogue's per-tile partials,
-// summed in ascending tile order) -> d_topk_w; and, when the layer routed itself, the top-k
-// softmax backward dl_j = w_j (dw_j - sum_i w_i dw_i) stored per position.
+// One wave per token, lane j for its row j (k <= 64): dw_j is the sum of that row's per-tile
+// partials from the down-dgrad epilogue, in ascending tile order -> d_topk_w; and, when the
+// layer routed itself, the top-k softmax backward dl_j = w_j (dw_j - sum_i w_i dw_i) stored per
+// position, the sum taken in ascending i by every lane alike.
 __global__ void __launch_bounds__(256) dw_router_kernel(const float* __restrict__ dwpart, int nIt,
                                                         const int32_t* __restrict__ tk_row,
                                                         const float* __restrict__ topk_w, int T,
                                                         int k, float* __restrict__ d_topk_w,
                                                         float* __restrict__ dl_pos, int routed) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= T) return;
-  float s = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const size_t r = (size_t)t * k + j;
-    const int pos = tk_row[r];
-    float dw = 0.f;
-    if (pos >= 0)
-      for (int it = 0; it < nIt; ++it) dw += dwpart[(size_t)pos * nIt + it];
-    d_topk_w[r] = dw;
-    s = __builtin_fmaf(topk_w[r], dw, s);
-  }
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;  // whole wave
+  const bool live = lane < k;
+  const size_t r = (size_t)t * k + lane;
+  const int pos = live ? tk_row[r] : -1;
+  const float w = live ? topk_w[r] : 0.f;
+  float dw = 0.f;
+  if (pos >= 0)
+    for (int it = 0; it < nIt; ++it) dw += dwpart[(size_t)pos * nIt + it];
+  if (live) d_topk_w[r] = dw;
   if (!routed) return;
-  for (int j = 0; j < k; ++j) {
-    const size_t r = (size_t)t * k + j;
-    const int pos = tk_row[r];
-    if (pos >= 0) {
-      const float w = topk_w[r];
-      dl_pos[pos] = w * (d_topk_w[r] - s);
-    }
-  }
+  float s = 0.f;
+  for (int j = 0; j < k; ++j) s = __builtin_fmaf(__shfl(w, j), __shfl(dw, j), s);
+  if (pos >= 0) dl_pos[pos] = w * (dw - s);
 }
 
 // dx[t] = bf16( sum_j dXp[tk_row[t*k+j]] + sum_j dl_j * Wr[e_j] ), j ascending, fp32; the
@@ -301,8 +296,10 @@ hipError_t launch_dw_router(const float* dwpart, int nIt, const int32_t* tk_row,
                             int routed, hipStream_t s) {
   {
     TraceScope trace("dw_router", s);
-    hipLaunchKernelGGL(dw_router_kernel, dim3((T + 255) / 256), dim3(256), 0, s, dwpart, nIt, tk_row,
-                       topk_w, T, k, d_topk_w, dl_pos, routed);
+    const int tokens_per_block = 256 / kWave;
+    hipLaunchKernelGGL(dw_router_kernel, dim3((T + tokens_per_block - 1) / tokens_per_block),
+                       dim3(256), 0, s, dwpart, nIt, tk_row, topk_w, T, k, d_topk_w, dl_pos,
+                       routed);
   }
   return hipGetLastError();
 }
