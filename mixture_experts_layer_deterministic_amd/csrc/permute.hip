@@ -52,12 +52,18 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ b
                                                          int32_t* __restrict__ status) {
   __shared__ int sc[1024];
   const int e = threadIdx.x;
+  constexpr int U = 16;  // block counts loaded together before their running sum
   int total = 0;
   if (e < E) {
-    for (int b = 0; b < nb; ++b) {
-      const int c = blk_cnt[(size_t)b * E + e];
-      blk_cnt[(size_t)b * E + e] = total;
-      total += c;
+    for (int b0 = 0; b0 < nb; b0 += U) {
+      int c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) c[u] = b0 + u < nb ? blk_cnt[(size_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (b0 + u < nb) blk_cnt[(size_t)(b0 + u) * E + e] = total;
+        total += c[u];
+      }
     }
     counts[e] = total;
   }
@@ -72,14 +78,20 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ b
   const int excl = sc[e] - total;
   if (e < E) {
     offsets[e] = excl;
-    for (int b = 0; b < nb; ++b) blk_cnt[(size_t)b * E + e] += excl;
+    for (int b0 = 0; b0 < nb; b0 += U) {
+      int c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) c[u] = b0 + u < nb ? blk_cnt[(size_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (b0 + u < nb) blk_cnt[(size_t)(b0 + u) * E + e] = c[u] + excl;
+    }
   }
   if (e == 1023) offsets[E] = sc[1023];
-  if (e == 0) {
-    int f = 0;
-    for (int b = 0; b < nb; ++b) f |= blk_flag[b];
-    status[0] = f ? 1 : 0;
-  }
+  int f = 0;
+  for (int b = e; b < nb; b += 1024) f |= blk_flag[b];
+  f = __syncthreads_or(f);
+  if (e == 0) status[0] = f ? 1 : 0;
 }
 
 // Places rows [r0, r0 + rpb) and copies their tokens: Xp[pos] = x[r / k]. With MX the copy is
