@@ -8,57 +8,55 @@
 
 namespace moe {
 
-static int rows_per_block(int d) {
-  int rpb = 2048 / (d / 8);
-  return rpb < 1 ? 1 : (rpb > 256 ? 256 : rpb);
-}
-
 // Rows of a token are gathered in groups of kGather: all loads of a group are issued before its
 // first FMA, so each thread keeps up to kGather 16-byte loads in flight. Sums still run in
 // ascending j.
 constexpr int kGather = 8;
 
 // y[t] = bf16( sum_{j=0..k-1} w[t,j] * O[tk_row[t*k+j]] ), fp32 fma with j ascending.
+// One thread per 16-byte slice (t, v) of y, no loop: the token's row indices and weights are
+// loaded first, then its gathered slices (kGather at a time), so every thread of the grid has
+// its loads in flight at once.
 __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict__ O,
                                                       const int32_t* __restrict__ tk_row,
                                                       const float* __restrict__ topk_w, int T,
-                                                      int k, int d, uint16_t* __restrict__ y,
-                                                      int tpb) {
+                                                      int k, int d, uint16_t* __restrict__ y) {
   const int vpr = d / 8;
-  const int t0 = blockIdx.x * tpb;
-  for (int i = threadIdx.x; i < tpb * vpr; i += 256) {
-    const int t = t0 + i / vpr, v = i % vpr;
-    if (t >= T) continue;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < k; j0 += kGather) {
-      int pos[kGather];
-      uint4 o[kGather];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * vpr) return;
+  const int t = i / vpr, v = i % vpr;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < k; j0 += kGather) {
+    int pos[kGather];
+    float w[kGather];
+    uint4 o[kGather];
 #pragma unroll
-      for (int jj = 0; jj < kGather; ++jj) {
-        const int j = j0 + jj;
-        pos[jj] = j < k ? tk_row[(size_t)t * k + j] : -1;
-        o[jj] = pos[jj] >= 0 ? *reinterpret_cast<const uint4*>(O + (size_t)pos[jj] * d + v * 8)
-                             : make_uint4(0, 0, 0, 0);
-      }
+    for (int jj = 0; jj < kGather; ++jj) {
+      const int j = j0 + jj;
+      pos[jj] = j < k ? tk_row[(size_t)t * k + j] : -1;
+      w[jj] = j < k ? topk_w[(size_t)t * k + j] : 0.f;
+    }
 #pragma unroll
-      for (int jj = 0; jj < kGather; ++jj) {
-        if (pos[jj] < 0) continue;
-        const float wj = topk_w[(size_t)t * k + j0 + jj];
-        const uint32_t ow[4] = {o[jj].x, o[jj].y, o[jj].z, o[jj].w};
+    for (int jj = 0; jj < kGather; ++jj)
+      o[jj] = pos[jj] >= 0 ? *reinterpret_cast<const uint4*>(O + (size_t)pos[jj] * d + v * 8)
+                           : make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = __builtin_fmaf(wj, bf2f_lo(ow[q]), acc[2 * q]);
-          acc[2 * q + 1] = __builtin_fmaf(wj, bf2f_hi(ow[q]), acc[2 * q + 1]);
-        }
+    for (int jj = 0; jj < kGather; ++jj) {
+      if (pos[jj] < 0) continue;
+      const uint32_t ow[4] = {o[jj].x, o[jj].y, o[jj].z, o[jj].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = __builtin_fmaf(w[jj], bf2f_lo(ow[q]), acc[2 * q]);
+        acc[2 * q + 1] = __builtin_fmaf(w[jj], bf2f_hi(ow[q]), acc[2 * q + 1]);
       }
     }
-    uint4 out;
-    out.x = pack_bf2(acc[0], acc[1]);
-    out.y = pack_bf2(acc[2], acc[3]);
-    out.z = pack_bf2(acc[4], acc[5]);
-    out.w = pack_bf2(acc[6], acc[7]);
-    *reinterpret_cast<uint4*>(y + (size_t)t * d + v * 8) = out;
   }
+  uint4 out;
+  out.x = pack_bf2(acc[0], acc[1]);
+  out.y = pack_bf2(acc[2], acc[3]);
+  out.z = pack_bf2(acc[4], acc[5]);
+  out.w = pack_bf2(acc[6], acc[7]);
+  *reinterpret_cast<uint4*>(y + (size_t)t * d + v * 8) = out;
 }
 
 // One wave per token, lane j for its row j (k <= 64): dw_j is the sum of that row's per-tile
@@ -88,111 +86,57 @@ __global__ void __launch_bounds__(256) dw_router_kernel(const float* __restrict_
 }
 
 // dx[t] = bf16( sum_j dXp[tk_row[t*k+j]] + sum_j dl_j * Wr[e_j] ), j ascending, fp32; the
-// router term only when wr is given. ONE_GROUP (k <= kGather): the row indices and expert
-// indices are loaded first, then every dXp row, router row and dl together, so a token costs
-// two round trips to memory; the sums keep the order above.
+// router term only when wr is given. One thread per 16-byte slice (t, v) of dx, no loop.
+// ONE_GROUP (k <= kGather): the row indices and expert indices are loaded first, then every dXp
+// row, router row and dl together, so a token costs two round trips to memory; the sums keep
+// the order above.
 template <bool ONE_GROUP>
 __global__ void __launch_bounds__(256) uncombine_kernel(
     const uint16_t* __restrict__ dXp, const int32_t* __restrict__ tk_row,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ dl_pos,
-    const uint16_t* __restrict__ wr, int T, int k, int d, uint16_t* __restrict__ dx, int tpb) {
+    const uint16_t* __restrict__ wr, int T, int k, int d, uint16_t* __restrict__ dx) {
   const int vpr = d / 8;
-  const int t0 = blockIdx.x * tpb;
-  for (int i = threadIdx.x; i < tpb * vpr; i += 256) {
-    const int t = t0 + i / vpr, v = i % vpr;
-    if (t >= T) continue;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if constexpr (ONE_GROUP) {
-      int pos[kGather], e[kGather];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * vpr) return;
+  const int t = i / vpr, v = i % vpr;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if constexpr (ONE_GROUP) {
+    int pos[kGather], e[kGather];
 #pragma unroll
-      for (int j = 0; j < kGather; ++j) {
-        pos[j] = j < k ? tk_row[(size_t)t * k + j] : -1;
-        e[j] = wr && j < k ? topk_idx[(size_t)t * k + j] : 0;
-      }
-      uint4 g[kGather], h[kGather];
-      float dl[kGather];
-#pragma unroll
-      for (int j = 0; j < kGather; ++j) {
-        const bool live = pos[j] >= 0;
-        g[j] = live ? *reinterpret_cast<const uint4*>(dXp + (size_t)pos[j] * d + v * 8)
-                    : make_uint4(0, 0, 0, 0);
-        h[j] = wr && live ? *reinterpret_cast<const uint4*>(wr + (size_t)e[j] * d + v * 8)
-                          : make_uint4(0, 0, 0, 0);
-        dl[j] = wr && live ? dl_pos[pos[j]] : 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < kGather; ++j) {
-        if (pos[j] < 0) continue;
-        const uint32_t gw[4] = {g[j].x, g[j].y, g[j].z, g[j].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += bf2f_lo(gw[q]);
-          acc[2 * q + 1] += bf2f_hi(gw[q]);
-        }
-      }
-      if (wr) {
-#pragma unroll
-        for (int j = 0; j < kGather; ++j) {
-          if (pos[j] < 0) continue;
-          const uint32_t hw[4] = {h[j].x, h[j].y, h[j].z, h[j].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[2 * q] = __builtin_fmaf(dl[j], bf2f_lo(hw[q]), acc[2 * q]);
-            acc[2 * q + 1] = __builtin_fmaf(dl[j], bf2f_hi(hw[q]), acc[2 * q + 1]);
-          }
-        }
-      }
-      uint4 out;
-      out.x = pack_bf2(acc[0], acc[1]);
-      out.y = pack_bf2(acc[2], acc[3]);
-      out.z = pack_bf2(acc[4], acc[5]);
-      out.w = pack_bf2(acc[6], acc[7]);
-      *reinterpret_cast<uint4*>(dx + (size_t)t * d + v * 8) = out;
-      continue;
+    for (int j = 0; j < kGather; ++j) {
+      pos[j] = j < k ? tk_row[(size_t)t * k + j] : -1;
+      e[j] = wr && j < k ? topk_idx[(size_t)t * k + j] : 0;
     }
-    for (int j0 = 0; j0 < k; j0 += kGather) {
-      int pos[kGather];
-      uint4 g[kGather];
+    uint4 g[kGather], h[kGather];
+    float dl[kGather];
 #pragma unroll
-      for (int jj = 0; jj < kGather; ++jj) {
-        const int j = j0 + jj;
-        pos[jj] = j < k ? tk_row[(size_t)t * k + j] : -1;
-        g[jj] = pos[jj] >= 0 ? *reinterpret_cast<const uint4*>(dXp + (size_t)pos[jj] * d + v * 8)
-                             : make_uint4(0, 0, 0, 0);
-      }
+    for (int j = 0; j < kGather; ++j) {
+      const bool live = pos[j] >= 0;
+      g[j] = live ? *reinterpret_cast<const uint4*>(dXp + (size_t)pos[j] * d + v * 8)
+                  : make_uint4(0, 0, 0, 0);
+      h[j] = wr && live ? *reinterpret_cast<const uint4*>(wr + (size_t)e[j] * d + v * 8)
+                        : make_uint4(0, 0, 0, 0);
+      dl[j] = wr && live ? dl_pos[pos[j]] : 0.f;
+    }
 #pragma unroll
-      for (int jj = 0; jj < kGather; ++jj) {
-        if (pos[jj] < 0) continue;
-        const uint32_t gw[4] = {g[jj].x, g[jj].y, g[jj].z, g[jj].w};
+    for (int j = 0; j < kGather; ++j) {
+      if (pos[j] < 0) continue;
+      const uint32_t gw[4] = {g[j].x, g[j].y, g[j].z, g[j].w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += bf2f_lo(gw[q]);
-          acc[2 * q + 1] += bf2f_hi(gw[q]);
-        }
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf2f_lo(gw[q]);
+        acc[2 * q + 1] += bf2f_hi(gw[q]);
       }
     }
     if (wr) {
-      for (int j0 = 0; j0 < k; j0 += kGather) {
-        int pos[kGather];
-        uint4 g[kGather];
 #pragma unroll
-        for (int jj = 0; jj < kGather; ++jj) {
-          const int j = j0 + jj;
-          pos[jj] = j < k ? tk_row[(size_t)t * k + j] : -1;
-          const int e = pos[jj] >= 0 ? topk_idx[(size_t)t * k + j] : 0;
-          g[jj] = pos[jj] >= 0 ? *reinterpret_cast<const uint4*>(wr + (size_t)e * d + v * 8)
-                               : make_uint4(0, 0, 0, 0);
-        }
+      for (int j = 0; j < kGather; ++j) {
+        if (pos[j] < 0) continue;
+        const uint32_t hw[4] = {h[j].x, h[j].y, h[j].z, h[j].w};
 #pragma unroll
-        for (int jj = 0; jj < kGather; ++jj) {
-          if (pos[jj] < 0) continue;
-          const float dl = dl_pos[pos[jj]];
-          const uint32_t gw[4] = {g[jj].x, g[jj].y, g[jj].z, g[jj].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[2 * q] = __builtin_fmaf(dl, bf2f_lo(gw[q]), acc[2 * q]);
-            acc[2 * q + 1] = __builtin_fmaf(dl, bf2f_hi(gw[q]), acc[2 * q + 1]);
-          }
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = __builtin_fmaf(dl[j], bf2f_lo(hw[q]), acc[2 * q]);
+          acc[2 * q + 1] = __builtin_fmaf(dl[j], bf2f_hi(hw[q]), acc[2 * q + 1]);
         }
       }
     }
@@ -202,7 +146,60 @@ __global__ void __launch_bounds__(256) uncombine_kernel(
     out.z = pack_bf2(acc[4], acc[5]);
     out.w = pack_bf2(acc[6], acc[7]);
     *reinterpret_cast<uint4*>(dx + (size_t)t * d + v * 8) = out;
+    return;
   }
+  for (int j0 = 0; j0 < k; j0 += kGather) {
+    int pos[kGather];
+    uint4 g[kGather];
+#pragma unroll
+    for (int jj = 0; jj < kGather; ++jj) {
+      const int j = j0 + jj;
+      pos[jj] = j < k ? tk_row[(size_t)t * k + j] : -1;
+      g[jj] = pos[jj] >= 0 ? *reinterpret_cast<const uint4*>(dXp + (size_t)pos[jj] * d + v * 8)
+                           : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int jj = 0; jj < kGather; ++jj) {
+      if (pos[jj] < 0) continue;
+      const uint32_t gw[4] = {g[jj].x, g[jj].y, g[jj].z, g[jj].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf2f_lo(gw[q]);
+        acc[2 * q + 1] += bf2f_hi(gw[q]);
+      }
+    }
+  }
+  if (wr) {
+    for (int j0 = 0; j0 < k; j0 += kGather) {
+      int pos[kGather];
+      uint4 g[kGather];
+#pragma unroll
+      for (int jj = 0; jj < kGather; ++jj) {
+        const int j = j0 + jj;
+        pos[jj] = j < k ? tk_row[(size_t)t * k + j] : -1;
+        const int e = pos[jj] >= 0 ? topk_idx[(size_t)t * k + j] : 0;
+        g[jj] = pos[jj] >= 0 ? *reinterpret_cast<const uint4*>(wr + (size_t)e * d + v * 8)
+                             : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < kGather; ++jj) {
+        if (pos[jj] < 0) continue;
+        const float dl = dl_pos[pos[jj]];
+        const uint32_t gw[4] = {g[jj].x, g[jj].y, g[jj].z, g[jj].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = __builtin_fmaf(dl, bf2f_lo(gw[q]), acc[2 * q]);
+          acc[2 * q + 1] = __builtin_fmaf(dl, bf2f_hi(gw[q]), acc[2 * q + 1]);
+        }
+      }
+    }
+  }
+  uint4 out;
+  out.x = pack_bf2(acc[0], acc[1]);
+  out.y = pack_bf2(acc[2], acc[3]);
+  out.z = pack_bf2(acc[4], acc[5]);
+  out.w = pack_bf2(acc[6], acc[7]);
+  *reinterpret_cast<uint4*>(dx + (size_t)t * d + v * 8) = out;
 }
 
 // dWr[e, c] = sum over positions p of expert e, ascending, of dl_pos[p] * Xp[p, c] (fp32).
@@ -282,11 +279,11 @@ __global__ void __launch_bounds__(64) dwr_kernel(const float* __restrict__ dl_po
 
 hipError_t launch_combine(const uint16_t* O, const int32_t* tk_row, const float* topk_w, int T,
                           int k, int d, uint16_t* y, hipStream_t s) {
-  const int tpb = rows_per_block(d);
+  const int grid = (T * (d / 8) + 255) / 256;
   {
     TraceScope trace("combine", s);
-    hipLaunchKernelGGL(combine_kernel, dim3((T + tpb - 1) / tpb), dim3(256), 0, s, O, tk_row, topk_w,
-                       T, k, d, y, tpb);
+    hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(256), 0, s, O, tk_row, topk_w, T, k, d,
+                       y);
   }
   return hipGetLastError();
 }
@@ -307,16 +304,15 @@ hipError_t launch_dw_router(const float* dwpart, int nIt, const int32_t* tk_row,
 hipError_t launch_uncombine(const uint16_t* dXp, const int32_t* tk_row, const int32_t* topk_idx,
                             const float* dl_pos, const uint16_t* wr, int T, int k, int d,
                             uint16_t* dx, hipStream_t s) {
-  const int tpb = rows_per_block(d);
   {
     TraceScope trace("uncombine", s);
-    const dim3 grid((T + tpb - 1) / tpb);
+    const dim3 grid((T * (d / 8) + 255) / 256);
     if (k <= kGather)
       hipLaunchKernelGGL(uncombine_kernel<true>, grid, dim3(256), 0, s, dXp, tk_row, topk_idx,
-                         dl_pos, wr, T, k, d, dx, tpb);
+                         dl_pos, wr, T, k, d, dx);
     else
       hipLaunchKernelGGL(uncombine_kernel<false>, grid, dim3(256), 0, s, dXp, tk_row, topk_idx,
-                         dl_pos, wr, T, k, d, dx, tpb);
+                         dl_pos, wr, T, k, d, dx);
   }
   return hipGetLastError();
 }

@@ -94,21 +94,25 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ b
   if (e == 0) status[0] = f ? 1 : 0;
 }
 
-// Places rows [r0, r0 + rpb) and copies their tokens: Xp[pos] = x[r / k]. With MX the copy is
-// the token's MXFP8 image: E4M3 codes xp8 [T*k, d] and one scale per 32 along d in xps
-// [T*k, d/32]. Four consecutive lanes own one 32-block (d is a multiple of 32, so blocks never
-// straddle rows), and every lane runs the shuffles.
+// Block b owns tokens [tpb b, tpb b + tpb) and their rows r = t*k + j (tpb*k <= 256). It
+// places every row, then copies each token slice ONCE from x and stores it to the token's k
+// positions: Xp[pos(t*k+j)] = x[t]. With MX the stored image is the token's MXFP8 form: E4M3
+// codes xp8 [T*k, d] and one scale per 32 along d in xps [T*k, d/32]. Four consecutive lanes
+// own one 32-block (d is a multiple of 32, so blocks never straddle rows), and every lane runs
+// the shuffles.
 template <bool MX>
 __global__ void __launch_bounds__(256) perm_place_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ rank,
-    const int32_t* __restrict__ blk_base, int Tk, int E, int k, int32_t* __restrict__ row_src,
+    const int32_t* __restrict__ blk_base, int T, int E, int k, int32_t* __restrict__ row_src,
     int32_t* __restrict__ tk_row, const uint16_t* __restrict__ x, uint16_t* __restrict__ xp,
-    uint8_t* __restrict__ xp8, uint8_t* __restrict__ xps, int d, int rpb) {
+    uint8_t* __restrict__ xp8, uint8_t* __restrict__ xps, int d, int tpb) {
   __shared__ int sh_pos[256];
   const int tid = threadIdx.x;
-  const int r0 = blockIdx.x * rpb;
-  if (tid < rpb) {
-    const int r = r0 + tid;
+  const int t0 = blockIdx.x * tpb;
+  const int Tk = T * k;
+  const int nr = tpb * k;
+  if (tid < nr) {
+    const int r = t0 * k + tid;
     int pos = -1;
     if (r < Tk) {
       const int rk = rank[r];
@@ -122,61 +126,63 @@ __global__ void __launch_bounds__(256) perm_place_kernel(
   }
   __syncthreads();
   const int vpr = d / 8;
-  const int n = rpb * vpr;
+  const int n = tpb * vpr;
   if constexpr (!MX) {
-    // plain copy: four 16-byte loads in flight per thread before their stores
+    // U token slices loaded together, then each stored to its k positions
     constexpr int U = 4;
     for (int i0 = 0; i0 < n; i0 += 256 * U) {
       uint4 val[U];
-      size_t dst[U];
-      bool live[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = i0 + 256 * u + tid;
-        const int rr = i / vpr, v = i % vpr;
-        const int r = r0 + rr;
-        const int pos = i < n ? sh_pos[rr] : -1;
-        live[u] = i < n && r < Tk && pos >= 0;
-        dst[u] = (size_t)pos * d + v * 8;
-        val[u] = live[u] ? *reinterpret_cast<const uint4*>(x + (size_t)(r / k) * d + v * 8)
-                         : make_uint4(0, 0, 0, 0);
+        const int t = t0 + i / vpr;
+        val[u] = i < n && t < T
+                     ? *reinterpret_cast<const uint4*>(x + (size_t)t * d + (i % vpr) * 8)
+                     : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (live[u]) *reinterpret_cast<uint4*>(xp + dst[u]) = val[u];
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + 256 * u + tid;
+        const int tt = i / vpr, v = i % vpr;
+        if (i >= n || t0 + tt >= T) continue;
+        for (int j = 0; j < k; ++j) {
+          const int pos = sh_pos[tt * k + j];
+          if (pos >= 0) *reinterpret_cast<uint4*>(xp + (size_t)pos * d + v * 8) = val[u];
+        }
+      }
     }
     return;
   }
   for (int i0 = 0; i0 < n; i0 += 256) {
     const int i = i0 + tid;
-    const int rr = i / vpr, v = i % vpr;
-    const int r = r0 + rr;
-    const int pos = i < n ? sh_pos[rr] : -1;
-    const bool live = i < n && r < Tk && pos >= 0;
+    const int tt = i / vpr, v = i % vpr;
+    const int t = t0 + tt;
+    const bool live = i < n && t < T;
     const uint4 val =
-        live ? *reinterpret_cast<const uint4*>(x + (size_t)(r / k) * d + v * 8) : make_uint4(0, 0, 0, 0);
-    {
-      const uint32_t xw[4] = {val.x, val.y, val.z, val.w};
-      float f[8];
+        live ? *reinterpret_cast<const uint4*>(x + (size_t)t * d + v * 8) : make_uint4(0, 0, 0, 0);
+    const uint32_t xw[4] = {val.x, val.y, val.z, val.w};
+    float f[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f[2 * q] = bf2f_lo(xw[q]);
-        f[2 * q + 1] = bf2f_hi(xw[q]);
-      }
-      float amax = 0.f;
+    for (int q = 0; q < 4; ++q) {
+      f[2 * q] = bf2f_lo(xw[q]);
+      f[2 * q + 1] = bf2f_hi(xw[q]);
+    }
+    float amax = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
-      amax = fmaxf(amax, __shfl_xor(amax, 1));
-      amax = fmaxf(amax, __shfl_xor(amax, 2));
-      const uint32_t code = mx_scale_code(amax);
-      const float inv = mx_inv_scale(code);
-      uint2 o;
-      o.x = e4m3x2(f[0] * inv, f[1] * inv) | (e4m3x2(f[2] * inv, f[3] * inv) << 16);
-      o.y = e4m3x2(f[4] * inv, f[5] * inv) | (e4m3x2(f[6] * inv, f[7] * inv) << 16);
-      if (live) {
-        *reinterpret_cast<uint2*>(xp8 + (size_t)pos * d + v * 8) = o;
-        if ((v & 3) == 0) xps[(size_t)pos * (d / 32) + v / 4] = static_cast<uint8_t>(code);
-      }
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const uint32_t code = mx_scale_code(amax);
+    const float inv = mx_inv_scale(code);
+    uint2 o;
+    o.x = e4m3x2(f[0] * inv, f[1] * inv) | (e4m3x2(f[2] * inv, f[3] * inv) << 16);
+    o.y = e4m3x2(f[4] * inv, f[5] * inv) | (e4m3x2(f[6] * inv, f[7] * inv) << 16);
+    if (!live) continue;
+    for (int j = 0; j < k; ++j) {
+      const int pos = sh_pos[tt * k + j];
+      if (pos < 0) continue;
+      *reinterpret_cast<uint2*>(xp8 + (size_t)pos * d + v * 8) = o;
+      if ((v & 3) == 0) xps[(size_t)pos * (d / 32) + v / 4] = static_cast<uint8_t>(code);
     }
   }
 }
@@ -206,19 +212,20 @@ hipError_t launch_perm_place(const int32_t* idx, const int32_t* rank, const int3
                              int Tk, int E, int k, int32_t* row_src, int32_t* tk_row,
                              const uint16_t* x, uint16_t* xp, uint8_t* xp8, uint8_t* xps, int d,
                              hipStream_t s) {
-  const int vpr = d / 8;
-  int rpb = 2048 / vpr;
-  if (rpb < 1) rpb = 1;
-  if (rpb > 256) rpb = 256;
-  const int grid = (Tk + rpb - 1) / rpb;
+  const int T = Tk / k;
+  // about 1024 slices of 16 bytes per block, and at most 256 rows
+  int tpb = 1024 / (d / 8);
+  if (tpb < 1) tpb = 1;
+  if (tpb > 256 / k) tpb = 256 / k;
+  const int grid = (T + tpb - 1) / tpb;
   {
     TraceScope trace("perm_place", s);
     if (xp8)
       hipLaunchKernelGGL(perm_place_kernel<true>, dim3(grid), dim3(256), 0, s, idx, rank, blk_base,
-                         Tk, E, k, row_src, tk_row, x, xp, xp8, xps, d, rpb);
+                         T, E, k, row_src, tk_row, x, xp, xp8, xps, d, tpb);
     else
       hipLaunchKernelGGL(perm_place_kernel<false>, dim3(grid), dim3(256), 0, s, idx, rank,
-                         blk_base, Tk, E, k, row_src, tk_row, x, xp, xp8, xps, d, rpb);
+                         blk_base, T, E, k, row_src, tk_row, x, xp, xp8, xps, d, tpb);
   }
   return hipGetLastError();
 }
