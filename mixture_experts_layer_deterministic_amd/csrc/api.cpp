@@ -381,7 +381,7 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
     uint8_t* dhq = at<uint8_t>(workspace, Y.dhq);
     uint8_t* dhs = at<uint8_t>(workspace, Y.dhs);
     if (!L.err) L(launch_quant_rows(dyp, cfg->T, d, dyq, dys, "quant_dy", s));
-    if (!L.err) L(launch_scale_gather(dyp, offsets, row_src, topk_w, E, k, d, Tk, dyw, s));
+    if (!L.err) L(launch_scale_gather(dyp, tk_row, topk_w, cfg->T, k, d, dyw, s));
     if (!L.err)
       L(launch_bwd_down_dgrad_mx({dyq, dys, row_src, topk_w, at<uint8_t>(wq, Y.w2b),
                                   at<uint8_t>(wq, Y.w2bs), H, A, dH, dwpart, dhq, dhs, offsets,
@@ -404,7 +404,7 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
                       "wgrad_sched_gate"},
                      s));
   } else {
-    if (!L.err) L(launch_scale_gather(dyp, offsets, row_src, topk_w, E, k, d, Tk, dyw, s));
+    if (!L.err) L(launch_scale_gather(dyp, tk_row, topk_w, cfg->T, k, d, dyw, s));
     if (!L.err)
       L(launch_bwd_down_dgrad({dyp, row_src, topk_w, w2p, H, A, dH, dwpart, offsets, sched, d, I,
                                k, Tk, E},

@@ -202,31 +202,37 @@ __global__ void __launch_bounds__(256) uncombine_kernel(
   *reinterpret_cast<uint4*>(dx + (size_t)t * d + v * 8) = out;
 }
 
-// dWr[e, c] = sum over positions p of expert e, ascending, of dl_pos[p] * Xp[p, c] (fp32).
-// Block (cx, e) covers columns [512 cx, 512 cx + 512); each thread owns 8 columns. MX reads Xp
-// as its MXFP8 image (codes xp8, one scale per 32 columns in xps).
+// dWr[e, c] = sum over positions p of expert e of dl_pos[p] * Xp[p, c] (fp32). Block (cx, e)
+// covers columns [512 cx, 512 cx + 512); each lane owns 8 columns. The expert's positions are
+// split into four contiguous quarters, one per wave, each summed in ascending p; the quarters
+// are then added in order ((q0 + q1) + q2) + q3, so the result is the same on every run. MX
+// reads Xp as its MXFP8 image (codes xp8, one scale per 32 columns in xps).
 template <bool MX>
-__global__ void __launch_bounds__(64) dwr_kernel(const float* __restrict__ dl_pos,
-                                                 const uint16_t* __restrict__ xp,
-                                                 const uint8_t* __restrict__ xp8,
-                                                 const uint8_t* __restrict__ xps,
-                                                 const int32_t* __restrict__ offsets, int d,
-                                                 float* __restrict__ dwr, int accumulate) {
+__global__ void __launch_bounds__(256) dwr_kernel(const float* __restrict__ dl_pos,
+                                                  const uint16_t* __restrict__ xp,
+                                                  const uint8_t* __restrict__ xp8,
+                                                  const uint8_t* __restrict__ xps,
+                                                  const int32_t* __restrict__ offsets, int d,
+                                                  float* __restrict__ dwr, int accumulate) {
+  __shared__ float part[3][8][64];
   const int e = blockIdx.y;
-  const int c0 = (blockIdx.x * 64 + threadIdx.x) * 8;
-  if (c0 >= d) return;
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int c0 = (blockIdx.x * 64 + lane) * 8;
+  const bool col = c0 < d;
   const int p0 = offsets[e], p1 = offsets[e + 1];
+  const int quarter = (p1 - p0 + 3) / 4;
+  const int q0 = min(p1, p0 + wave * quarter), q1 = min(p1, q0 + quarter);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   // positions in groups of U: the group's loads are issued before its FMAs (p ascending)
   constexpr int U = 8;
-  for (int pg = p0; pg < p1; pg += U) {
+  for (int pg = q0; pg < q1; pg += U) {
     float dl[U];
     uint4 raw[U];
     uint32_t sc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = pg + u;
-      const bool live = p < p1;
+      const bool live = col && p < q1;
       dl[u] = live ? dl_pos[p] : 0.f;
       if constexpr (MX) {
         const uint2 q = live ? *reinterpret_cast<const uint2*>(xp8 + (size_t)p * d + c0)
@@ -241,7 +247,7 @@ __global__ void __launch_bounds__(64) dwr_kernel(const float* __restrict__ dl_po
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (pg + u >= p1) break;
+      if (pg + u >= q1) break;
       float xv[8];
       if constexpr (MX) {
         const float s = mx_scale(sc[u]);
@@ -265,6 +271,15 @@ __global__ void __launch_bounds__(64) dwr_kernel(const float* __restrict__ dl_po
       for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(dl[u], xv[q], acc[q]);
     }
   }
+  if (wave > 0)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) part[wave - 1][q][lane] = acc[q];
+  __syncthreads();
+  if (wave > 0 || !col) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += part[w][q][lane];
   float4* dst = reinterpret_cast<float4*>(dwr + (size_t)e * d + c0);
   float4 a = make_float4(acc[0], acc[1], acc[2], acc[3]);
   float4 b = make_float4(acc[4], acc[5], acc[6], acc[7]);
@@ -323,10 +338,10 @@ hipError_t launch_dwr(const float* dl_pos, const uint16_t* xp, const uint8_t* xp
   {
     TraceScope trace("dwr", s);
     if (xp8)
-      hipLaunchKernelGGL(dwr_kernel<true>, dim3((d + 511) / 512, E), dim3(64), 0, s, dl_pos, xp,
+      hipLaunchKernelGGL(dwr_kernel<true>, dim3((d + 511) / 512, E), dim3(256), 0, s, dl_pos, xp,
                          xp8, xps, offsets, d, dwr, accumulate);
     else
-      hipLaunchKernelGGL(dwr_kernel<false>, dim3((d + 511) / 512, E), dim3(64), 0, s, dl_pos, xp,
+      hipLaunchKernelGGL(dwr_kernel<false>, dim3((d + 511) / 512, E), dim3(256), 0, s, dl_pos, xp,
                          xp8, xps, offsets, d, dwr, accumulate);
   }
   return hipGetLastError();

@@ -177,9 +177,8 @@ hipError_t launch_quant_rows(const uint16_t* src, long long rows, int cols, uint
 hipError_t launch_quant_weight(const uint16_t* src, int B, int R, int C, uint8_t* dq,
                                uint8_t* dqs, uint8_t* tq, uint8_t* tqs, const char* name,
                                hipStream_t s);
-hipError_t launch_scale_gather(const uint16_t* dy, const int32_t* offsets, const int32_t* row_src,
-                               const float* topk_w, int E, int k, int d, int Tk, uint16_t* dyw,
-                               hipStream_t s);
+hipError_t launch_scale_gather(const uint16_t* dy, const int32_t* tk_row, const float* topk_w,
+                               int T, int k, int d, uint16_t* dyw, hipStream_t s);
 
 // elementwise.hip
 hipError_t launch_combine(const uint16_t* O, const int32_t* tk_row, const float* topk_w, int T,

@@ -157,46 +157,40 @@ __global__ void __launch_bounds__(256) quant_weight_kernel(const uint16_t* __res
     *reinterpret_cast<uint32_t*>(tqs + ((size_t)b * C + c0 + t) * (R / 32) + r0 / 32) = scT[t];
 }
 
-// dyw[pos] = bf16(w[row_src[pos]] * dy[row_src[pos] / k]): the down wgrad's left operand in
-// position order. A grid-strided loop in which each thread issues four 16-byte loads before
-// their stores; vector v covers 8 elements of one position's row.
-constexpr int kSgUnroll = 4;
+// dyw[pos] = bf16(w[r] * dy[r / k]) for every row r placed at pos = tk_row[r]: the down
+// wgrad's left operand in position order. One thread per 16-byte slice (t, v) of dy: the slice
+// is loaded once, together with the token's row positions and weights, and stored scaled to
+// each of its k positions. Rows that were not placed (tk_row < 0) store nothing.
+constexpr int kSgGroup = 8;
 __global__ void __launch_bounds__(256) scale_gather_kernel(const uint16_t* __restrict__ dy,
-                                                           const int32_t* __restrict__ offsets,
-                                                           const int32_t* __restrict__ row_src,
+                                                           const int32_t* __restrict__ tk_row,
                                                            const float* __restrict__ topk_w,
-                                                           int E, int k, int d,
-                                                           uint16_t* __restrict__ dyw,
-                                                           long long nvec) {
+                                                           int T, int k, int d,
+                                                           uint16_t* __restrict__ dyw) {
   const int vpr = d / 8;
-  const long long npos = offsets[E];  // rows past it are skipped for a bad expert index
-  const long long stride = (long long)gridDim.x * 256 * kSgUnroll;
-  for (long long v0 = (long long)blockIdx.x * 256 * kSgUnroll + threadIdx.x; v0 < nvec;
-       v0 += stride) {
-    uint4 x[kSgUnroll];
-    float w[kSgUnroll];
-    bool live[kSgUnroll];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * vpr) return;
+  const int t = i / vpr, v = i % vpr;
+  const uint4 x = *reinterpret_cast<const uint4*>(dy + (size_t)t * d + v * 8);
+  for (int j0 = 0; j0 < k; j0 += kSgGroup) {
+    int pos[kSgGroup];
+    float w[kSgGroup];
 #pragma unroll
-    for (int u = 0; u < kSgUnroll; ++u) {
-      const long long v = v0 + 256 * u;
-      const long long pos = v / vpr;
-      live[u] = v < nvec && pos < npos;
-      const int r = live[u] ? row_src[pos] : 0;
-      w[u] = live[u] ? topk_w[r] : 0.f;
-      x[u] = live[u] ? *reinterpret_cast<const uint4*>(dy + (size_t)(r / k) * d +
-                                                      static_cast<int>(v % vpr) * 8)
-                     : make_uint4(0, 0, 0, 0);
+    for (int jj = 0; jj < kSgGroup; ++jj) {
+      const int j = j0 + jj;
+      pos[jj] = j < k ? tk_row[(size_t)t * k + j] : -1;
+      w[jj] = j < k ? topk_w[(size_t)t * k + j] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < kSgUnroll; ++u) {
-      if (!live[u]) continue;
-      const float wu = w[u];
+    for (int jj = 0; jj < kSgGroup; ++jj) {
+      if (pos[jj] < 0) continue;
+      const float wu = w[jj];
       uint4 o;
-      o.x = pack_bf2(bf2f_lo(x[u].x) * wu, bf2f_hi(x[u].x) * wu);
-      o.y = pack_bf2(bf2f_lo(x[u].y) * wu, bf2f_hi(x[u].y) * wu);
-      o.z = pack_bf2(bf2f_lo(x[u].z) * wu, bf2f_hi(x[u].z) * wu);
-      o.w = pack_bf2(bf2f_lo(x[u].w) * wu, bf2f_hi(x[u].w) * wu);
-      *reinterpret_cast<uint4*>(dyw + (size_t)(v0 + 256 * u) * 8) = o;
+      o.x = pack_bf2(bf2f_lo(x.x) * wu, bf2f_hi(x.x) * wu);
+      o.y = pack_bf2(bf2f_lo(x.y) * wu, bf2f_hi(x.y) * wu);
+      o.z = pack_bf2(bf2f_lo(x.z) * wu, bf2f_hi(x.z) * wu);
+      o.w = pack_bf2(bf2f_lo(x.w) * wu, bf2f_hi(x.w) * wu);
+      *reinterpret_cast<uint4*>(dyw + (size_t)pos[jj] * d + v * 8) = o;
     }
   }
 }
@@ -226,17 +220,14 @@ hipError_t launch_quant_weight(const uint16_t* src, int B, int R, int C, uint8_t
   return hipGetLastError();
 }
 
-hipError_t launch_scale_gather(const uint16_t* dy, const int32_t* offsets, const int32_t* row_src,
-                               const float* topk_w, int E, int k, int d, int Tk, uint16_t* dyw,
-                               hipStream_t s) {
-  const long long nvec = (long long)Tk * d / 8;
+hipError_t launch_scale_gather(const uint16_t* dy, const int32_t* tk_row, const float* topk_w,
+                               int T, int k, int d, uint16_t* dyw, hipStream_t s) {
+  const long long nvec = (long long)T * d / 8;
   if (nvec == 0) return hipSuccess;
   {
     TraceScope trace("scale_gather", s);
-    const long long per_block = 256LL * kSgUnroll;
-    const long long blocks = (nvec + per_block - 1) / per_block;
-    hipLaunchKernelGGL(scale_gather_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, s,
-                       dy, offsets, row_src, topk_w, E, k, d, dyw, nvec);
+    hipLaunchKernelGGL(scale_gather_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0, s,
+                       dy, tk_row, topk_w, T, k, d, dyw);
   }
   return hipGetLastError();
 }
