@@ -23,6 +23,10 @@
 // only load the operands into LDS. The two sides meet at a barrier that waits for LDS traffic
 // only, so stores of many tiles stay in flight.
 //
+// Experts with many rows (at least kWgradBigRows) make the product MFMA-bound rather than
+// write-bound. They go to a second kernel with 256 x 256 output tiles and 64-position K steps,
+// twice the flops per loaded byte of the 256 x 128 tiles (see wgrad_big_kernel).
+//
 // Determinism: every dW element belongs to exactly one task, whose workgroup reduces K in
 // ascending position order. No atomics, no split-K.
 #include "common.h"
@@ -33,6 +37,7 @@ namespace moe {
 namespace {
 
 constexpr int BM = kWgradBM, BN = kWgradBN, BK = 32;
+constexpr int kWgradBigRows = 512;  // experts with at least this many rows: wgrad_big_kernel
 constexpr int KRES = 128;           // positions of L kept resident in LDS for a whole task
 constexpr int LDL = KRES + 8;       // row pitch of the L buffer [BM][LDL]
 constexpr int LDR = BK + 8;         // row pitch of an R stage [BN][LDR]
@@ -330,14 +335,19 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
 // nt = min(ceil(kWgradTaskSteps / nk), ntn) tiles, and its tasks
 // mstripes * ceil(ntn / nt). Experts are laid out by decreasing row count (ties to the lower
 // index), each expert's tasks stripe-major. count[0] receives the number of tasks.
+// Experts with c_e >= big_rows get no tasks here: big[0].x receives their number and
+// big[1 + i] = (expert, rows) their list in the same order (they hold the first ranks).
 __global__ void __launch_bounds__(1024) wgrad_sched_kernel(const int32_t* __restrict__ offsets,
                                                            int E, int mstripes, int ntn,
+                                                           int big_rows, int4* __restrict__ big,
                                                            int4* __restrict__ table,
                                                            int32_t* __restrict__ count) {
   __shared__ int cnt[1024];
   __shared__ int scan[1024];
   const int e = threadIdx.x;
   const int c = e < E ? offsets[e + 1] - offsets[e] : -1;
+  const bool isbig = e < E && c >= big_rows;
+  const int nbig = __syncthreads_count(isbig);
   cnt[e] = c;
   __syncthreads();
   int rank = e;
@@ -348,10 +358,12 @@ __global__ void __launch_bounds__(1024) wgrad_sched_kernel(const int32_t* __rest
       const int cj = cnt[j];
       rank += (cj > c) || (cj == c && j < e);
     }
-    const int nk = max((c + BK - 1) / BK, 1);
-    nt = min((kWgradTaskSteps + nk - 1) / nk, ntn);
-    nchunks = (ntn + nt - 1) / nt;
-    ntask = mstripes * nchunks;
+    if (!isbig) {
+      const int nk = max((c + BK - 1) / BK, 1);
+      nt = min((kWgradTaskSteps + nk - 1) / nk, ntn);
+      nchunks = (ntn + nt - 1) / nt;
+      ntask = mstripes * nchunks;
+    }
   }
   scan[rank] = ntask;  // ranks of the E experts are a permutation of 0..E-1
   __syncthreads();
@@ -362,10 +374,173 @@ __global__ void __launch_bounds__(1024) wgrad_sched_kernel(const int32_t* __rest
     __syncthreads();
   }
   const int start = scan[rank] - ntask;
-  for (int s = 0; s < mstripes; ++s)
+  for (int s = 0; s < mstripes && nchunks > 0; ++s)
     for (int ch = 0; ch < nchunks; ++ch)
       table[start + s * nchunks + ch] = make_int4(e, s * BM, ch * nt, min(nt, ntn - ch * nt));
+  if (isbig) big[1 + rank] = make_int4(e, c, 0, 0);
+  if (e == 0) big[0] = make_int4(nbig, 0, 0, 0);
   if (rank == 1023) count[0] = scan[1023];
+}
+
+// ------------------------------------------------------------------------------------------
+// Experts with many rows. With thousands of positions per expert the product is MFMA-bound,
+// and the kernel's rate follows the flops per byte its tiles load into LDS: 256 x 256 output
+// tiles with 64-position K steps carry 128 flop/B, against 85 for the 256 x 128 stripes with
+// 32-position steps above. Eight waves of 128 x 64 outputs (128 accumulators each), one
+// workgroup per CU, two LDS stages.
+//
+// Both operands are position-major, so a K step of either is 64 rows of 256 contiguous values.
+// They are copied into LDS as they are, [64][256] per operand in 16-byte vectors, with the
+// 32-byte column groups of row k permuted by XOR with big_swz(k). The MFMA fragments (8
+// consecutive positions of one row or column per lane) are then read with gfx950's
+// transposing LDS read, so neither operand is transposed in registers.
+constexpr int kBigT = 256;                    // dW tile edge
+constexpr int kBigK = 64;                     // positions per K step
+constexpr int kBigThreads = 512;              // 8 waves: 2 along M x 4 along N
+constexpr int kBigWM = 128, kBigWN = 64;      // outputs per wave
+constexpr int kBigStage = 2 * kBigK * kBigT;  // uint16 elements per stage: L rows, then R rows
+
+// Column-group permutation of LDS row k (a multiple of 16 elements, below 128): the four rows
+// a 16-lane group reads at once, and the rows 8 further on, fall on different bank groups.
+MOE_DEV int big_swz(int k) { return 16 * ((k & 3) | ((k >> 1) & 4)); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+MOE_DEV s16x4 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4* lds_ptr;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p));
+}
+
+// MFMA fragment from a K-major LDS tile: lane l gets index base + l % 16 (a dW row or column)
+// at positions kb + 8 (l / 16) .. + 8. Within each group of 16 lanes, ds_read_b64_tr_b16 gives
+// lane i element j of the 8 bytes that lane 4 j + i / 4 points at, taking element i % 4 of them
+// (the layout was checked on the GPU with a one-hot matrix). Lane q of group g points at
+// position kb + 8 g + q / 4, indices base + 4 (q % 4) .. + 4; so lane i receives positions
+// kb + 8 g + 0..3 of index base + i, and the second read (4 positions on) the next four.
+MOE_DEV uint4 big_frag(const uint16_t* s, int base, int kb, int lane) {
+  const int g = lane / 16, q = lane % 16;
+  const int k1 = kb + 8 * g + q / 4, k2 = k1 + 4, n = base + 4 * (q % 4);
+  const s16x4 a = lds_read_tr16(s + k1 * kBigT + (n ^ big_swz(k1)));
+  const s16x4 b = lds_read_tr16(s + k2 * kBigT + (n ^ big_swz(k2)));
+  uint4 v;
+  v.x = (uint32_t)(uint16_t)a[0] | ((uint32_t)(uint16_t)a[1] << 16);
+  v.y = (uint32_t)(uint16_t)a[2] | ((uint32_t)(uint16_t)a[3] << 16);
+  v.z = (uint32_t)(uint16_t)b[0] | ((uint32_t)(uint16_t)b[1] << 16);
+  v.w = (uint32_t)(uint16_t)b[2] | ((uint32_t)(uint16_t)b[3] << 16);
+  return v;
+}
+
+// One K step of one operand: positions [p, p + 64) x 256 columns from `base` (row pitch ld),
+// rows at or past p1 as zeros. Four 16-byte vectors per thread; a wave instruction covers two
+// whole 512-byte rows.
+struct BigLoader {
+  const uint16_t* base;
+  int ld;
+  uint4 r[4];
+  MOE_DEV void load(int p, int p1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = threadIdx.x + kBigThreads * j, row = v / 32, col = (v % 32) * 8;
+      r[j] = p + row < p1 ? *reinterpret_cast<const uint4*>(base + (size_t)(p + row) * ld + col)
+                          : make_uint4(0, 0, 0, 0);
+    }
+  }
+  MOE_DEV void store(uint16_t* s) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = threadIdx.x + kBigThreads * j, row = v / 32, col = (v % 32) * 8;
+      *reinterpret_cast<uint4*>(s + row * kBigT + (col ^ big_swz(row))) = r[j];
+    }
+  }
+};
+
+// Tiles of the listed experts, expert by expert in list order (decreasing rows); inside an
+// expert, groups of four 256-row blocks take each 256-column block in turn. Round r gives XCD x
+// the tiles [r G + x G/8, r G + (x+1) G/8): neighbouring tiles share operand panels in its L2.
+// GATE only separates the two instances (dW1 and dW2) for profilers.
+template <bool ACC, bool GATE>
+__global__ void __launch_bounds__(kBigThreads, 1) wgrad_big_kernel(const Args a,
+                                                                   const int4* __restrict__ big,
+                                                                   const int32_t* __restrict__ offsets) {
+  __shared__ __align__(16) uint16_t sm[2 * kBigStage];
+  const int ntm = a.Mdim / kBigT, ntn = a.Ndim / kBigT, tpe = ntm * ntn;
+  const int ntiles = big[0].x * tpe;
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = wave / (kBigT / kBigWN), wn = wave % (kBigT / kBigWN);
+  const int G = gridDim.x, G8 = G / kXcds, xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  for (int round = 0;; ++round) {
+    const int ti = round * G + xcd * G8 + slot;
+    if (ti >= ntiles) break;
+    const int e = big[1 + ti / tpe].x;
+    const int lt = ti % tpe;
+    const int group = lt / (4 * ntn), mfirst = group * 4, gm = min(4, ntm - mfirst);
+    const int rr = lt - mfirst * ntn;
+    const int m0 = (mfirst + rr % gm) * kBigT, n0 = (rr / gm) * kBigT;
+    const int p0 = offsets[e], p1 = offsets[e + 1];
+    const int nk = (p1 - p0 + kBigK - 1) / kBigK;
+    BigLoader la, lb;
+    la.base = a.L + m0;
+    la.ld = a.Mdim;
+    lb.base = a.R + n0;
+    lb.ld = a.Ndim;
+    f32x4 acc[kBigWM / 16][kBigWN / 16];
+#pragma unroll
+    for (int i = 0; i < kBigWM / 16; ++i)
+#pragma unroll
+      for (int j = 0; j < kBigWN / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    la.load(p0, p1);
+    lb.load(p0, p1);
+    la.store(sm);
+    lb.store(sm + kBigK * kBigT);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint16_t* sl = sm + (kt & 1) * kBigStage;
+      const uint16_t* sr = sl + kBigK * kBigT;
+      if (kt + 1 < nk) {
+        la.load(p0 + (kt + 1) * kBigK, p1);
+        lb.load(p0 + (kt + 1) * kBigK, p1);
+      }
+#pragma unroll
+      for (int ks = 0; ks < kBigK / 32; ++ks) {
+        uint4 bf[kBigWN / 16], af[kBigWM / 16];
+#pragma unroll
+        for (int nb = 0; nb < kBigWN / 16; ++nb)
+          bf[nb] = big_frag(sr, wn * kBigWN + nb * 16, ks * 32, lane);
+#pragma unroll
+        for (int mb = 0; mb < kBigWM / 16; ++mb)
+          af[mb] = big_frag(sl, wm * kBigWM + mb * 16, ks * 32, lane);
+#pragma unroll
+        for (int mb = 0; mb < kBigWM / 16; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < kBigWN / 16; ++nb) acc[mb][nb] = mfma16(bf[nb], af[mb], acc[mb][nb]);
+      }
+      if (kt + 1 < nk) {
+        uint16_t* nx = sm + ((kt + 1) & 1) * kBigStage;
+        la.store(nx);
+        lb.store(nx + kBigK * kBigT);
+      }
+      __syncthreads();
+    }
+    float* out = a.dw + ((size_t)e * a.Mdim + m0) * a.Ndim + n0;
+#pragma unroll
+    for (int mb = 0; mb < kBigWM / 16; ++mb) {
+      const int m = wm * kBigWM + mb * 16 + lane % 16;
+#pragma unroll
+      for (int nb = 0; nb < kBigWN / 16; ++nb) {
+        const int n = wn * kBigWN + nb * 16 + 4 * (lane / 16);
+        float4* dst = reinterpret_cast<float4*>(out + (size_t)m * a.Ndim + n);
+        float4 v = make_float4(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]);
+        if (ACC) {
+          const float4 o = *dst;
+          v.x += o.x;
+          v.y += o.y;
+          v.z += o.z;
+          v.w += o.w;
+        }
+        *dst = v;
+      }
+    }
+  }
 }
 
 int resident_grid() {
@@ -383,33 +558,64 @@ int resident_grid() {
   return grid;
 }
 
+int resident_grid_big() {
+  static int grid = 0;
+  if (grid == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&wgrad_big_kernel<false, false>), kBigThreads, 0) != hipSuccess)
+      return 0;
+    grid = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
+  }
+  return grid;
+}
+
 }  // namespace
 
+// Entries: the list of big experts (1 + E), then the task table of the others.
 size_t wgrad_table_entries(int Tk, int E, int Mdim, int Ndim) {
   const long long mstripes = Mdim / BM, ntn = Ndim / BN;
   const long long per_stripe = ntn * ((long long)Tk + (long long)E * BK) / (BK * kWgradTaskSteps) + E;
   const long long cap = (long long)E * ntn;
-  return (size_t)(mstripes * (per_stripe < cap ? per_stripe : cap));
+  return (size_t)(1 + E + mstripes * (per_stripe < cap ? per_stripe : cap));
 }
 
 hipError_t launch_wgrad(const WgradArgs& x, hipStream_t s) {
+  // the big-expert kernel takes bf16 operands whose dW dimensions are multiples of its tile
+  const bool big_ok = !x.R8 && x.Mdim % kBigT == 0 && x.Ndim % kBigT == 0;
+  const int big_rows = big_ok ? kWgradBigRows : 0x7fffffff;
+  int4* big = x.table;
+  int4* table = x.table + 1 + x.E;
   {
     TraceScope trace(x.name_sched, s);
     hipLaunchKernelGGL(wgrad_sched_kernel, dim3(1), dim3(1024), 0, s, x.offsets, x.E, x.Mdim / BM,
-                       x.Ndim / BN, x.table, x.count);
+                       x.Ndim / BN, big_rows, big, table, x.count);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int grid = resident_grid();
   if (grid <= 0) return hipErrorInvalidValue;
-  Args a{x.L, x.R, x.R8, x.R8s, x.dw, x.offsets, x.table, x.count, x.Mdim, x.Ndim, x.accumulate};
+  Args a{x.L, x.R, x.R8, x.R8s, x.dw, x.offsets, table, x.count, x.Mdim, x.Ndim, x.accumulate};
   {
     TraceScope trace(x.name, s);
     auto kern = x.R8 ? (x.accumulate ? wgrad_kernel<true, true, true> : wgrad_kernel<false, true, true>)
                      : x.accumulate
                          ? (x.gate ? wgrad_kernel<true, true, false> : wgrad_kernel<true, false, false>)
                          : (x.gate ? wgrad_kernel<false, true, false> : wgrad_kernel<false, false, false>);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, s, a, x.table, x.offsets, x.count);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, s, a, table, x.offsets, x.count);
+  }
+  err = hipGetLastError();
+  if (err != hipSuccess || !big_ok) return err;
+  const int gbig = resident_grid_big();
+  if (gbig <= 0) return hipErrorInvalidValue;
+  {
+    TraceScope trace(x.gate ? "bwd_gate_wgrad_big" : "bwd_down_wgrad_big", s);
+    auto kern = x.accumulate ? (x.gate ? wgrad_big_kernel<true, true> : wgrad_big_kernel<true, false>)
+                             : (x.gate ? wgrad_big_kernel<false, true> : wgrad_big_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3(gbig), dim3(kBigThreads), 0, s, a, big, x.offsets);
   }
   return hipGetLastError();
 }
