@@ -91,6 +91,42 @@ MOE_DEV void transpose8x8_b16(const uint4 (&in)[8], uint4 (&out)[8]) {
   }
 }
 
+// K-major LDS tiles read as MFMA fragments. A tile of K rows x PITCH values (16-bit) is stored
+// row by row as it sits in memory, with the 32-byte column groups of row k permuted by XOR
+// with kmajor_swz(k) (a multiple of 16 elements, below 128): the four rows a 16-lane group
+// reads at once, and the rows 8 further on, fall on different bank groups.
+MOE_DEV int kmajor_swz(int k) { return 16 * ((k & 3) | ((k >> 1) & 4)); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+MOE_DEV s16x4 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4* lds_ptr;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p));
+}
+
+// MFMA fragment from a K-major LDS tile: lane l gets index base + l % 16 (a row or column of the
+// product) at K rows kb + 8 (l / 16) .. + 8; base is a multiple of 16 and kb of 32. Within each
+// group of 16 lanes, ds_read_b64_tr_b16 gives lane i element j of the 8 bytes that lane
+// 4 j + i / 4 points at, taking element i % 4 of them (the layout was checked on the GPU with a
+// one-hot matrix). Lane q of group g points at row kb + 8 g + q / 4, indices base + 4 (q % 4)
+// .. + 4; so lane i receives rows kb + 8 g + 0..3 of index base + i, and the second read (4 rows
+// on) the next four. The permutation of those rows does not depend on kb or on the 4-row step
+// (kb is a multiple of 32, and q / 4 + 4 < 8), so both reads share one column and differ from
+// other steps only by constant offsets.
+template <int PITCH>
+MOE_DEV uint4 kmajor_frag(const uint16_t* s, int base, int kb, int lane) {
+  const int g = lane / 16, q = lane % 16, kr = 8 * g + q / 4;
+  const int n = (base ^ kmajor_swz(kr)) + 4 * (q % 4);
+  const uint16_t* p = s + (kb + kr) * PITCH + n;
+  const s16x4 a = lds_read_tr16(p);
+  const s16x4 b = lds_read_tr16(p + 4 * PITCH);
+  uint4 v;
+  v.x = (uint32_t)(uint16_t)a[0] | ((uint32_t)(uint16_t)a[1] << 16);
+  v.y = (uint32_t)(uint16_t)a[2] | ((uint32_t)(uint16_t)a[3] << 16);
+  v.z = (uint32_t)(uint16_t)b[0] | ((uint32_t)(uint16_t)b[1] << 16);
+  v.w = (uint32_t)(uint16_t)b[2] | ((uint32_t)(uint16_t)b[3] << 16);
+  return v;
+}
+
 // Workgroup id remapped so that each XCD gets one contiguous range of logical tiles. The
 // hardware deals workgroup b to XCD b % 8; the logical id (b % 8) * R + b / 8 gives XCD x the
 // range [x R, (x+1) R). `total` must be rounded up to a multiple of 8 by the launch.

@@ -523,6 +523,123 @@ struct BwdGateDgrad {
 };
 
 
+// Problem 4 on full 256-row blocks, where an expert's rows make it MFMA-bound: 256 x 256 tiles,
+// eight waves of 128 x 64, two LDS stages of 64 K. W1[e] is d-contiguous, and a register
+// transpose of a 256-wide tile does not fit beside 128 accumulators; so its K step (64 rows of
+// W1, 256 columns each) is copied into LDS as it is, with kmajor_swz-permuted column groups,
+// and its MFMA fragments are read with gfx950's transposing LDS read (kmajor_frag). dH rows are
+// K-contiguous and go to LDS as [256][72].
+constexpr int kDgT = 256, kDgK = 64, kDgThreads = 512, kDgLdA = kDgK + 8;
+constexpr int kDgWM = 128, kDgWN = 64;
+constexpr int kDgStage = kDgT * kDgLdA + kDgK * kDgT;  // uint16 elements: dH tile, then W1 tile
+
+struct GateDgradBigArgs {
+  const uint16_t* dH;  // [T*k, 2I]
+  const uint16_t* w1;  // [E, 2I, d]
+  uint16_t* dXp;       // [T*k, d]
+  const int32_t* offsets;
+  const int2* big;     // full 256-row blocks: count, then (expert, first row)
+  int d, I;
+};
+
+__global__ void __launch_bounds__(kDgThreads, 1) gate_dgrad_big_kernel(const GateDgradBigArgs a) {
+  __shared__ __align__(16) uint16_t sm[2 * kDgStage];
+  const int ntc = a.d / kDgT;
+  const int nblk = a.big[0].x;
+  const int ntiles = nblk * ntc;
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = wave / (kDgT / kDgWN), wn = wave % (kDgT / kDgWN);
+  const int twoI = 2 * a.I;
+  const int R = (ntiles + kXcds - 1) / kXcds;
+  const int step = gridDim.x / kXcds;
+  for (int sidx = blockIdx.x / kXcds; sidx < R; sidx += step) {
+    const int lt = (blockIdx.x % kXcds) * R + sidx;  // XCD x takes tiles [x R, (x+1) R)
+    if (lt >= ntiles) break;
+    const int2 mn = tile_mn<true>(lt, nblk, ntc);
+    const MTile mt = decode_mtile(a.big, a.offsets, mn.x, kDgT);
+    const int n0 = mn.y * kDgT;
+    const uint16_t* ab = a.dH + (size_t)mt.row0 * twoI;
+    const uint16_t* bb = a.w1 + (size_t)mt.e * twoI * a.d + n0;
+    // per thread four 16-byte vectors of each operand per K step
+    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+#define MOE_DG_LOAD(k0)                                                                         \
+  do {                                                                                          \
+    const int t_ = threadIdx.x;                                                                 \
+    const uint16_t* a_ = ab + (size_t)(t_ / 8) * twoI + (k0) + (t_ % 8) * 8;                     \
+    const uint16_t* b_ = bb + (size_t)((k0) + t_ / 32) * a.d + (t_ % 32) * 8;                   \
+    ra0 = *reinterpret_cast<const uint4*>(a_);                                                  \
+    ra1 = *reinterpret_cast<const uint4*>(a_ + (size_t)64 * twoI);                              \
+    ra2 = *reinterpret_cast<const uint4*>(a_ + (size_t)128 * twoI);                             \
+    ra3 = *reinterpret_cast<const uint4*>(a_ + (size_t)192 * twoI);                             \
+    rb0 = *reinterpret_cast<const uint4*>(b_);                                                  \
+    rb1 = *reinterpret_cast<const uint4*>(b_ + (size_t)16 * a.d);                               \
+    rb2 = *reinterpret_cast<const uint4*>(b_ + (size_t)32 * a.d);                               \
+    rb3 = *reinterpret_cast<const uint4*>(b_ + (size_t)48 * a.d);                               \
+  } while (0)
+#define MOE_DG_STORE(st)                                                                        \
+  do {                                                                                          \
+    const int t_ = threadIdx.x, kr_ = t_ / 32;                                                  \
+    uint16_t* sa_ = (st) + (t_ / 8) * kDgLdA + (t_ % 8) * 8;                                    \
+    uint16_t* sb_ = (st) + kDgT * kDgLdA + kr_ * kDgT + (((t_ % 32) * 8) ^ kmajor_swz(kr_));     \
+    *reinterpret_cast<uint4*>(sa_) = ra0;                                                       \
+    *reinterpret_cast<uint4*>(sa_ + 64 * kDgLdA) = ra1;                                         \
+    *reinterpret_cast<uint4*>(sa_ + 128 * kDgLdA) = ra2;                                        \
+    *reinterpret_cast<uint4*>(sa_ + 192 * kDgLdA) = ra3;                                        \
+    *reinterpret_cast<uint4*>(sb_) = rb0;                                                       \
+    *reinterpret_cast<uint4*>(sb_ + 16 * kDgT) = rb1;                                           \
+    *reinterpret_cast<uint4*>(sb_ + 32 * kDgT) = rb2;                                           \
+    *reinterpret_cast<uint4*>(sb_ + 48 * kDgT) = rb3;                                           \
+  } while (0)
+    f32x4 acc[kDgWM / 16][kDgWN / 16];
+#pragma unroll
+    for (int i = 0; i < kDgWM / 16; ++i)
+#pragma unroll
+      for (int j = 0; j < kDgWN / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nk = twoI / kDgK;
+    MOE_DG_LOAD(0);
+    MOE_DG_STORE(sm);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint16_t* sA = sm + (kt & 1) * kDgStage;
+      const uint16_t* sB = sA + kDgT * kDgLdA;
+      if (kt + 1 < nk) MOE_DG_LOAD((kt + 1) * kDgK);
+#pragma unroll
+      for (int ks = 0; ks < kDgK / 32; ++ks) {
+        const int koff = ks * 32 + (lane / 16) * 8;
+        uint4 bf[kDgWN / 16];
+#pragma unroll
+        for (int nb = 0; nb < kDgWN / 16; ++nb)
+          bf[nb] = kmajor_frag<kDgT>(sB, wn * kDgWN + nb * 16, ks * 32, lane);
+        uint4 af[kDgWM / 16];
+#pragma unroll
+        for (int mb = 0; mb < kDgWM / 16; ++mb)
+          af[mb] = *reinterpret_cast<const uint4*>(sA + (wm * kDgWM + mb * 16 + lane % 16) * kDgLdA + koff);
+#pragma unroll
+        for (int mb = 0; mb < kDgWM / 16; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < kDgWN / 16; ++nb) acc[mb][nb] = mfma16(bf[nb], af[mb], acc[mb][nb]);
+      }
+      if (kt + 1 < nk) MOE_DG_STORE(sm + ((kt + 1) & 1) * kDgStage);
+      __syncthreads();
+    }
+#undef MOE_DG_LOAD
+#undef MOE_DG_STORE
+#pragma unroll
+    for (int mb = 0; mb < kDgWM / 16; ++mb) {
+      const size_t pos = mt.row0 + wm * kDgWM + mb * 16 + lane % 16;
+      uint16_t* orow = a.dXp + pos * a.d + n0 + wn * kDgWN + 4 * (lane / 16);
+#pragma unroll
+      for (int nb = 0; nb < kDgWN / 16; ++nb) {
+        uint2 o;
+        o.x = pack_bf2(acc[mb][nb][0], acc[mb][nb][1]);
+        o.y = pack_bf2(acc[mb][nb][2], acc[mb][nb][3]);
+        *reinterpret_cast<uint2*>(orow + nb * 16) = o;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // MXFP8 mode. Both operands are E4M3 codes, K-contiguous, with one E8M0 scale per 32 along K;
 // one v_mfma_scale_f32_16x16x128_f8f6f4 covers 16 x 16 outputs and 128 K. Operand layout of
@@ -1308,9 +1425,33 @@ hipError_t launch_bwd_down_dgrad(const GemmBwdDownDgradArgs& x, bool persistent,
   return launch<BwdDownDgrad>(a, sched_max_mtiles(x.Tk, x.E) * (x.I / 128), persistent, s);
 }
 
+// The gate dgrad runs the 256-row blocks with gate_dgrad_big_kernel, then the remainders.
 hipError_t launch_bwd_gate_dgrad(const GemmBwdGateDgradArgs& x, bool persistent, hipStream_t s) {
-  BwdGateDgrad::Args a{x.dH, x.w1, x.dXp, x.offsets, x.sched, x.d, x.I};
-  return launch<BwdGateDgrad>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
+  const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
+  const int max_big = sched_max_big(x.Tk) * (x.d / kDgT);
+  if (max_big > 0) {
+    static int resident = 0;  // every device of one process is an MI355X
+    if (resident == 0) {
+      int dev = 0, cus = 0, per_cu = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&gate_dgrad_big_kernel), kDgThreads, 0);
+      if (e != hipSuccess) return e;
+      resident = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
+    }
+    const int grid = std::min(resident, (max_big + kXcds - 1) / kXcds * kXcds);
+    GateDgradBigArgs ab{x.dH, x.w1, x.dXp, x.offsets, st.big, x.d, x.I};
+    {
+      TraceScope trace("bwd_gate_dgrad_big", s);
+      hipLaunchKernelGGL(gate_dgrad_big_kernel, dim3(grid), dim3(kDgThreads), 0, s, ab);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  BwdGateDgrad::Args a{x.dH, x.w1, x.dXp, x.offsets, st.rem, x.d, x.I};
+  return launch<BwdGateDgrad>(a, sched_max_rem(x.Tk, x.E) * (x.d / 128), persistent, s);
 }
 
 hipError_t launch_fwd_gateup_mx(const GemmMxGateUpArgs& x, bool persistent, hipStream_t s) {

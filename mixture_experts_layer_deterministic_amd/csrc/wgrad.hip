@@ -391,43 +391,14 @@ __global__ void __launch_bounds__(1024) wgrad_sched_kernel(const int32_t* __rest
 //
 // Both operands are position-major, so a K step of either is 64 rows of 256 contiguous values.
 // They are copied into LDS as they are, [64][256] per operand in 16-byte vectors, with the
-// 32-byte column groups of row k permuted by XOR with big_swz(k). The MFMA fragments (8
+// 32-byte column groups of row k permuted by XOR with kmajor_swz(k). The MFMA fragments (8
 // consecutive positions of one row or column per lane) are then read with gfx950's
-// transposing LDS read, so neither operand is transposed in registers.
+// transposing LDS read (kmajor_frag), so neither operand is transposed in registers.
 constexpr int kBigT = 256;                    // dW tile edge
 constexpr int kBigK = 64;                     // positions per K step
 constexpr int kBigThreads = 512;              // 8 waves: 2 along M x 4 along N
 constexpr int kBigWM = 128, kBigWN = 64;      // outputs per wave
 constexpr int kBigStage = 2 * kBigK * kBigT;  // uint16 elements per stage: L rows, then R rows
-
-// Column-group permutation of LDS row k (a multiple of 16 elements, below 128): the four rows
-// a 16-lane group reads at once, and the rows 8 further on, fall on different bank groups.
-MOE_DEV int big_swz(int k) { return 16 * ((k & 3) | ((k >> 1) & 4)); }
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-MOE_DEV s16x4 lds_read_tr16(const uint16_t* p) {
-  typedef __attribute__((address_space(3))) s16x4* lds_ptr;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p));
-}
-
-// MFMA fragment from a K-major LDS tile: lane l gets index base + l % 16 (a dW row or column)
-// at positions kb + 8 (l / 16) .. + 8. Within each group of 16 lanes, ds_read_b64_tr_b16 gives
-// lane i element j of the 8 bytes that lane 4 j + i / 4 points at, taking element i % 4 of them
-// (the layout was checked on the GPU with a one-hot matrix). Lane q of group g points at
-// position kb + 8 g + q / 4, indices base + 4 (q % 4) .. + 4; so lane i receives positions
-// kb + 8 g + 0..3 of index base + i, and the second read (4 positions on) the next four.
-MOE_DEV uint4 big_frag(const uint16_t* s, int base, int kb, int lane) {
-  const int g = lane / 16, q = lane % 16;
-  const int k1 = kb + 8 * g + q / 4, k2 = k1 + 4, n = base + 4 * (q % 4);
-  const s16x4 a = lds_read_tr16(s + k1 * kBigT + (n ^ big_swz(k1)));
-  const s16x4 b = lds_read_tr16(s + k2 * kBigT + (n ^ big_swz(k2)));
-  uint4 v;
-  v.x = (uint32_t)(uint16_t)a[0] | ((uint32_t)(uint16_t)a[1] << 16);
-  v.y = (uint32_t)(uint16_t)a[2] | ((uint32_t)(uint16_t)a[3] << 16);
-  v.z = (uint32_t)(uint16_t)b[0] | ((uint32_t)(uint16_t)b[1] << 16);
-  v.w = (uint32_t)(uint16_t)b[2] | ((uint32_t)(uint16_t)b[3] << 16);
-  return v;
-}
 
 // One K step of one operand: positions [p, p + 64) x 256 columns from `base` (row pitch ld),
 // rows at or past p1 as zeros. Four 16-byte vectors per thread; a wave instruction covers two
@@ -448,7 +419,7 @@ struct BigLoader {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int v = threadIdx.x + kBigThreads * j, row = v / 32, col = (v % 32) * 8;
-      *reinterpret_cast<uint4*>(s + row * kBigT + (col ^ big_swz(row))) = r[j];
+      *reinterpret_cast<uint4*>(s + row * kBigT + (col ^ kmajor_swz(row))) = r[j];
     }
   }
 };
@@ -505,10 +476,10 @@ __global__ void __launch_bounds__(kBigThreads, 1) wgrad_big_kernel(const Args a,
         uint4 bf[kBigWN / 16], af[kBigWM / 16];
 #pragma unroll
         for (int nb = 0; nb < kBigWN / 16; ++nb)
-          bf[nb] = big_frag(sr, wn * kBigWN + nb * 16, ks * 32, lane);
+          bf[nb] = kmajor_frag<kBigT>(sr, wn * kBigWN + nb * 16, ks * 32, lane);
 #pragma unroll
         for (int mb = 0; mb < kBigWM / 16; ++mb)
-          af[mb] = big_frag(sl, wm * kBigWM + mb * 16, ks * 32, lane);
+          af[mb] = kmajor_frag<kBigT>(sl, wm * kBigWM + mb * 16, ks * 32, lane);
 #pragma unroll
         for (int mb = 0; mb < kBigWM / 16; ++mb)
 #pragma unroll
