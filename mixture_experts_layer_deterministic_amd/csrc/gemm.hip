@@ -640,6 +640,165 @@ __global__ void __launch_bounds__(kDgThreads, 1) gate_dgrad_big_kernel(const Gat
   }
 }
 
+// Problem 3 on full 256-row blocks: the same 256 x 256 structure as gate_dgrad_big_kernel, with
+// dY rows gathered through row_src and W2[e] ([d, I], I-contiguous) as the K-major operand. The
+// epilogue is Problem 3's: per (pos, i) the SwiGLU backward into dH, and the router-weight
+// partials dw = sum_i dA'[pos, i] A[pos, i] of each 128-column half, summed in a fixed order
+// (a lane's columns, then its lane groups, then the two waves of the half).
+struct DownDgradBigArgs {
+  const uint16_t* dy;      // [T, d]
+  const int32_t* row_src;  // [T*k]
+  const float* topk_w;     // [T*k] flat (row r)
+  const uint16_t* w2;      // [E, d, I]
+  const uint16_t* H;       // [T*k, 2I]
+  const uint16_t* A;       // [T*k, I]
+  uint16_t* dH;            // [T*k, 2I]
+  float* dwpart;           // [T*k, I / 128]
+  const int32_t* offsets;
+  const int2* big;         // full 256-row blocks: count, then (expert, first row)
+  int d, I, k;
+};
+
+__global__ void __launch_bounds__(kDgThreads, 1) down_dgrad_big_kernel(const DownDgradBigArgs a) {
+  __shared__ __align__(16) uint16_t sm[2 * kDgStage];
+  const int ntc = a.I / kDgT;
+  const int nblk = a.big[0].x;
+  const int ntiles = nblk * ntc;
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = wave / (kDgT / kDgWN), wn = wave % (kDgT / kDgWN);
+  const int I = a.I, d = a.d;
+  const int R = (ntiles + kXcds - 1) / kXcds;
+  const int step = gridDim.x / kXcds;
+  for (int sidx = blockIdx.x / kXcds; sidx < R; sidx += step) {
+    const int lt = (blockIdx.x % kXcds) * R + sidx;  // XCD x takes tiles [x R, (x+1) R)
+    if (lt >= ntiles) break;
+    const int2 mn = tile_mn<true>(lt, nblk, ntc);
+    const MTile mt = decode_mtile(a.big, a.offsets, mn.x, kDgT);
+    const int n0 = mn.y * kDgT;
+    const int tid = threadIdx.x;
+    // this thread's four dY rows (block rows tid / 8 + 64 j) as element offsets
+    uint32_t ao0, ao1, ao2, ao3;
+    {
+      const int32_t* rs = a.row_src + mt.row0 + tid / 8;
+      const uint32_t c = (tid % 8) * 8;
+      ao0 = (uint32_t)(rs[0] / a.k) * (uint32_t)d + c;
+      ao1 = (uint32_t)(rs[64] / a.k) * (uint32_t)d + c;
+      ao2 = (uint32_t)(rs[128] / a.k) * (uint32_t)d + c;
+      ao3 = (uint32_t)(rs[192] / a.k) * (uint32_t)d + c;
+    }
+    const uint16_t* bb = a.w2 + (size_t)mt.e * d * I + n0 + (tid % 32) * 8;
+    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+#define MOE_DD_LOAD(k0)                                                                         \
+  do {                                                                                          \
+    const uint16_t* b_ = bb + (size_t)((k0) + tid / 32) * I;                                    \
+    ra0 = *reinterpret_cast<const uint4*>(a.dy + ao0 + (k0));                                   \
+    ra1 = *reinterpret_cast<const uint4*>(a.dy + ao1 + (k0));                                   \
+    ra2 = *reinterpret_cast<const uint4*>(a.dy + ao2 + (k0));                                   \
+    ra3 = *reinterpret_cast<const uint4*>(a.dy + ao3 + (k0));                                   \
+    rb0 = *reinterpret_cast<const uint4*>(b_);                                                  \
+    rb1 = *reinterpret_cast<const uint4*>(b_ + (size_t)16 * I);                                 \
+    rb2 = *reinterpret_cast<const uint4*>(b_ + (size_t)32 * I);                                 \
+    rb3 = *reinterpret_cast<const uint4*>(b_ + (size_t)48 * I);                                 \
+  } while (0)
+#define MOE_DD_STORE(st)                                                                        \
+  do {                                                                                          \
+    const int kr_ = tid / 32;                                                                   \
+    uint16_t* sa_ = (st) + (tid / 8) * kDgLdA + (tid % 8) * 8;                                  \
+    uint16_t* sb_ = (st) + kDgT * kDgLdA + kr_ * kDgT + (((tid % 32) * 8) ^ kmajor_swz(kr_));   \
+    *reinterpret_cast<uint4*>(sa_) = ra0;                                                       \
+    *reinterpret_cast<uint4*>(sa_ + 64 * kDgLdA) = ra1;                                         \
+    *reinterpret_cast<uint4*>(sa_ + 128 * kDgLdA) = ra2;                                        \
+    *reinterpret_cast<uint4*>(sa_ + 192 * kDgLdA) = ra3;                                        \
+    *reinterpret_cast<uint4*>(sb_) = rb0;                                                       \
+    *reinterpret_cast<uint4*>(sb_ + 16 * kDgT) = rb1;                                           \
+    *reinterpret_cast<uint4*>(sb_ + 32 * kDgT) = rb2;                                           \
+    *reinterpret_cast<uint4*>(sb_ + 48 * kDgT) = rb3;                                           \
+  } while (0)
+    f32x4 acc[kDgWM / 16][kDgWN / 16];
+#pragma unroll
+    for (int i = 0; i < kDgWM / 16; ++i)
+#pragma unroll
+      for (int j = 0; j < kDgWN / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nk = d / kDgK;
+    MOE_DD_LOAD(0);
+    MOE_DD_STORE(sm);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint16_t* sA = sm + (kt & 1) * kDgStage;
+      const uint16_t* sB = sA + kDgT * kDgLdA;
+      if (kt + 1 < nk) MOE_DD_LOAD((kt + 1) * kDgK);
+#pragma unroll
+      for (int ks = 0; ks < kDgK / 32; ++ks) {
+        const int koff = ks * 32 + (lane / 16) * 8;
+        uint4 bf[kDgWN / 16];
+#pragma unroll
+        for (int nb = 0; nb < kDgWN / 16; ++nb)
+          bf[nb] = kmajor_frag<kDgT>(sB, wn * kDgWN + nb * 16, ks * 32, lane);
+        uint4 af[kDgWM / 16];
+#pragma unroll
+        for (int mb = 0; mb < kDgWM / 16; ++mb)
+          af[mb] = *reinterpret_cast<const uint4*>(sA + (wm * kDgWM + mb * 16 + lane % 16) * kDgLdA + koff);
+#pragma unroll
+        for (int mb = 0; mb < kDgWM / 16; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < kDgWN / 16; ++nb) acc[mb][nb] = mfma16(bf[nb], af[mb], acc[mb][nb]);
+      }
+      if (kt + 1 < nk) MOE_DD_STORE(sm + ((kt + 1) & 1) * kDgStage);
+      __syncthreads();
+    }
+#undef MOE_DD_LOAD
+#undef MOE_DD_STORE
+    float* red = reinterpret_cast<float*>(sm);  // [4][256] row sums per wave column; LDS is free
+#pragma unroll
+    for (int mb = 0; mb < kDgWM / 16; ++mb) {
+      const int m = wm * kDgWM + mb * 16 + lane % 16;
+      const size_t pos = mt.row0 + m;
+      const float w = a.topk_w[a.row_src[pos]];
+      float part = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < kDgWN / 16; ++nb) {
+        const int i = n0 + wn * kDgWN + nb * 16 + 4 * (lane / 16);
+        const uint2 av = *reinterpret_cast<const uint2*>(a.A + pos * I + i);
+        const uint2 gv = *reinterpret_cast<const uint2*>(a.H + pos * 2 * I + i);
+        const uint2 uv = *reinterpret_cast<const uint2*>(a.H + pos * 2 * I + I + i);
+        const float av4[4] = {bf2f_lo(av.x), bf2f_hi(av.x), bf2f_lo(av.y), bf2f_hi(av.y)};
+        const float g4[4] = {bf2f_lo(gv.x), bf2f_hi(gv.x), bf2f_lo(gv.y), bf2f_hi(gv.y)};
+        const float u4[4] = {bf2f_lo(uv.x), bf2f_hi(uv.x), bf2f_lo(uv.y), bf2f_hi(uv.y)};
+        float dg[4], du[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float dap = acc[mb][nb][r];
+          part = __builtin_fmaf(dap, av4[r], part);
+          const float dA = w * dap;
+          const float sg = sigmoid(g4[r]);
+          dg[r] = dA * u4[r] * sg * (1.0f + g4[r] * (1.0f - sg));
+          du[r] = dA * (g4[r] * sg);
+        }
+        uint2 o;
+        o.x = pack_bf2(dg[0], dg[1]);
+        o.y = pack_bf2(dg[2], dg[3]);
+        *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + i) = o;
+        o.x = pack_bf2(du[0], du[1]);
+        o.y = pack_bf2(du[2], du[3]);
+        *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + I + i) = o;
+      }
+      // lanes l, l^16, l^32, l^48 share row m: butterfly in a fixed pattern
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      if (lane < 16) red[wn * kDgT + m] = part;
+    }
+    __syncthreads();
+    if (tid < kDgT) {
+      const size_t pos = mt.row0 + tid;
+      float* dst = a.dwpart + pos * (I / 128) + n0 / 128;
+      dst[0] = red[0 * kDgT + tid] + red[1 * kDgT + tid];  // columns [n0, n0 + 128)
+      dst[1] = red[2 * kDgT + tid] + red[3 * kDgT + tid];  // columns [n0 + 128, n0 + 256)
+    }
+    __syncthreads();  // red aliases the next tile's first LDS stage
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // MXFP8 mode. Both operands are E4M3 codes, K-contiguous, with one E8M0 scale per 32 along K;
 // one v_mfma_scale_f32_16x16x128_f8f6f4 covers 16 x 16 outputs and 128 K. Operand layout of
@@ -1419,10 +1578,46 @@ hipError_t launch_fwd_down(const GemmFwdDownArgs& x, bool persistent, hipStream_
   return launch<FwdDown>(a, sched_max_rem(x.Tk, x.E) * (x.d / 128), persistent, s);
 }
 
+// Resident workgroup count of a 512-thread big-tile kernel (one per CU), a multiple of 8.
+template <class K>
+static hipError_t big_resident(K kernel, int* resident) {
+  if (*resident == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(kernel), kDgThreads, 0);
+    if (e != hipSuccess) return e;
+    *resident = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
+  }
+  return hipSuccess;
+}
+
+// With I a multiple of 256 the down dgrad runs the 256-row blocks with down_dgrad_big_kernel,
+// then the remainders; otherwise every 128-row block with the 128 x 128 kernel.
 hipError_t launch_bwd_down_dgrad(const GemmBwdDownDgradArgs& x, bool persistent, hipStream_t s) {
+  const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
+  const bool big = x.I % kDgT == 0;
+  const int max_big = big ? sched_max_big(x.Tk) * (x.I / kDgT) : 0;
+  if (max_big > 0) {
+    static int resident = 0;  // every device of one process is an MI355X
+    hipError_t e = big_resident(down_dgrad_big_kernel, &resident);
+    if (e != hipSuccess) return e;
+    const int grid = std::min(resident, (max_big + kXcds - 1) / kXcds * kXcds);
+    DownDgradBigArgs ab{x.dy, x.row_src, x.topk_w, x.w2, x.H, x.A, x.dH, x.dwpart,
+                        x.offsets, st.big, x.d, x.I, x.k};
+    {
+      TraceScope trace("bwd_down_dgrad_big", s);
+      hipLaunchKernelGGL(down_dgrad_big_kernel, dim3(grid), dim3(kDgThreads), 0, s, ab);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   BwdDownDgrad::Args a{x.dy, x.row_src, x.topk_w, x.w2, x.H, x.A, x.dH, x.dwpart,
-                       x.offsets, x.sched, x.d, x.I, x.k};
-  return launch<BwdDownDgrad>(a, sched_max_mtiles(x.Tk, x.E) * (x.I / 128), persistent, s);
+                       x.offsets, big ? st.rem : st.full, x.d, x.I, x.k};
+  const int max_small = big ? sched_max_rem(x.Tk, x.E) : sched_max_mtiles(x.Tk, x.E);
+  return launch<BwdDownDgrad>(a, max_small * (x.I / 128), persistent, s);
 }
 
 // The gate dgrad runs the 256-row blocks with gate_dgrad_big_kernel, then the remainders.
@@ -1431,16 +1626,8 @@ hipError_t launch_bwd_gate_dgrad(const GemmBwdGateDgradArgs& x, bool persistent,
   const int max_big = sched_max_big(x.Tk) * (x.d / kDgT);
   if (max_big > 0) {
     static int resident = 0;  // every device of one process is an MI355X
-    if (resident == 0) {
-      int dev = 0, cus = 0, per_cu = 0;
-      hipError_t e = hipGetDevice(&dev);
-      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-      if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&gate_dgrad_big_kernel), kDgThreads, 0);
-      if (e != hipSuccess) return e;
-      resident = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
-    }
+    hipError_t e0 = big_resident(gate_dgrad_big_kernel, &resident);
+    if (e0 != hipSuccess) return e0;
     const int grid = std::min(resident, (max_big + kXcds - 1) / kXcds * kXcds);
     GateDgradBigArgs ab{x.dH, x.w1, x.dXp, x.offsets, st.big, x.d, x.I};
     {

@@ -41,6 +41,7 @@ KERNELS = [
     (r"gg_kernel<moe::FwdDownT<moe::Geo<256", "fwd_down_big", "gemm.hip"),
     (r"gg_kernel<moe::BwdGateDgradT<moe::Geo<256", "bwd_gate_dgrad_big", "gemm.hip"),
     (r"gate_dgrad_big_kernel", "bwd_gate_dgrad_big", "gemm.hip"),
+    (r"down_dgrad_big_kernel", "bwd_down_dgrad_big", "gemm.hip"),
     (r"gg_kernel<moe::FwdGateUp", "fwd_gateup", "gemm.hip"),
     (r"gg_kernel<moe::FwdDown", "fwd_down", "gemm.hip"),
     (r"gg_kernel<moe::BwdDownDgrad", "bwd_down_dgrad", "gemm.hip"),
