@@ -13,10 +13,19 @@ namespace moe {
 // ascending j.
 constexpr int kGather = 8;
 
+// Token of slice i (vpr slices per row). WAVE_TOKEN: vpr is a multiple of the wave size, so
+// the 64 slices of a wave belong to one token; saying so lets the token's row indices, weights
+// and expert ids arrive through scalar loads, once per wave instead of once per lane.
+template <bool WAVE_TOKEN>
+MOE_DEV int slice_token(int i, int vpr) {
+  return WAVE_TOKEN ? __builtin_amdgcn_readfirstlane(i / vpr) : i / vpr;
+}
+
 // y[t] = bf16( sum_{j=0..k-1} w[t,j] * O[tk_row[t*k+j]] ), fp32 fma with j ascending.
 // One thread per 16-byte slice (t, v) of y, no loop: the token's row indices and weights are
 // loaded first, then its gathered slices (kGather at a time), so every thread of the grid has
 // its loads in flight at once.
+template <bool WAVE_TOKEN>
 __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict__ O,
                                                       const int32_t* __restrict__ tk_row,
                                                       const float* __restrict__ topk_w, int T,
@@ -24,7 +33,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
   const int vpr = d / 8;
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= T * vpr) return;
-  const int t = i / vpr, v = i % vpr;
+  const int t = slice_token<WAVE_TOKEN>(i, vpr), v = i % vpr;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < k; j0 += kGather) {
     int pos[kGather];
@@ -90,7 +99,7 @@ __global__ void __launch_bounds__(256) dw_router_kernel(const float* __restrict_
 // ONE_GROUP (k <= kGather): the row indices and expert indices are loaded first, then every dXp
 // row, router row and dl together, so a token costs two round trips to memory; the sums keep
 // the order above.
-template <bool ONE_GROUP>
+template <bool ONE_GROUP, bool WAVE_TOKEN>
 __global__ void __launch_bounds__(256) uncombine_kernel(
     const uint16_t* __restrict__ dXp, const int32_t* __restrict__ tk_row,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ dl_pos,
@@ -98,7 +107,7 @@ __global__ void __launch_bounds__(256) uncombine_kernel(
   const int vpr = d / 8;
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= T * vpr) return;
-  const int t = i / vpr, v = i % vpr;
+  const int t = slice_token<WAVE_TOKEN>(i, vpr), v = i % vpr;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if constexpr (ONE_GROUP) {
     int pos[kGather], e[kGather];
@@ -297,8 +306,12 @@ hipError_t launch_combine(const uint16_t* O, const int32_t* tk_row, const float*
   const int grid = (T * (d / 8) + 255) / 256;
   {
     TraceScope trace("combine", s);
-    hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(256), 0, s, O, tk_row, topk_w, T, k, d,
-                       y);
+    if ((d / 8) % kWave == 0)
+      hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, s, O, tk_row, topk_w, T,
+                         k, d, y);
+    else
+      hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, s, O, tk_row, topk_w, T,
+                         k, d, y);
   }
   return hipGetLastError();
 }
@@ -322,12 +335,19 @@ hipError_t launch_uncombine(const uint16_t* dXp, const int32_t* tk_row, const in
   {
     TraceScope trace("uncombine", s);
     const dim3 grid((T * (d / 8) + 255) / 256);
-    if (k <= kGather)
-      hipLaunchKernelGGL(uncombine_kernel<true>, grid, dim3(256), 0, s, dXp, tk_row, topk_idx,
-                         dl_pos, wr, T, k, d, dx);
+    const bool wt = (d / 8) % kWave == 0;
+    if (k <= kGather && wt)
+      hipLaunchKernelGGL((uncombine_kernel<true, true>), grid, dim3(256), 0, s, dXp, tk_row,
+                         topk_idx, dl_pos, wr, T, k, d, dx);
+    else if (k <= kGather)
+      hipLaunchKernelGGL((uncombine_kernel<true, false>), grid, dim3(256), 0, s, dXp, tk_row,
+                         topk_idx, dl_pos, wr, T, k, d, dx);
+    else if (wt)
+      hipLaunchKernelGGL((uncombine_kernel<false, true>), grid, dim3(256), 0, s, dXp, tk_row,
+                         topk_idx, dl_pos, wr, T, k, d, dx);
     else
-      hipLaunchKernelGGL(uncombine_kernel<false>, grid, dim3(256), 0, s, dXp, tk_row, topk_idx,
-                         dl_pos, wr, T, k, d, dx);
+      hipLaunchKernelGGL((uncombine_kernel<false, false>), grid, dim3(256), 0, s, dXp, tk_row,
+                         topk_idx, dl_pos, wr, T, k, d, dx);
   }
   return hipGetLastError();
 }

@@ -161,7 +161,10 @@ __global__ void __launch_bounds__(256) quant_weight_kernel(const uint16_t* __res
 // wgrad's left operand in position order. One thread per 16-byte slice (t, v) of dy: the slice
 // is loaded once, together with the token's row positions and weights, and stored scaled to
 // each of its k positions. Rows that were not placed (tk_row < 0) store nothing.
+// WAVE_TOKEN: the 64 slices of a wave belong to one token (vpr a multiple of 64), so its row
+// positions and weights arrive through scalar loads.
 constexpr int kSgGroup = 8;
+template <bool WAVE_TOKEN>
 __global__ void __launch_bounds__(256) scale_gather_kernel(const uint16_t* __restrict__ dy,
                                                            const int32_t* __restrict__ tk_row,
                                                            const float* __restrict__ topk_w,
@@ -170,7 +173,7 @@ __global__ void __launch_bounds__(256) scale_gather_kernel(const uint16_t* __res
   const int vpr = d / 8;
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= T * vpr) return;
-  const int t = i / vpr, v = i % vpr;
+  const int t = WAVE_TOKEN ? __builtin_amdgcn_readfirstlane(i / vpr) : i / vpr, v = i % vpr;
   const uint4 x = *reinterpret_cast<const uint4*>(dy + (size_t)t * d + v * 8);
   for (int j0 = 0; j0 < k; j0 += kSgGroup) {
     int pos[kSgGroup];
@@ -226,8 +229,13 @@ hipError_t launch_scale_gather(const uint16_t* dy, const int32_t* tk_row, const 
   if (nvec == 0) return hipSuccess;
   {
     TraceScope trace("scale_gather", s);
-    hipLaunchKernelGGL(scale_gather_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0, s,
-                       dy, tk_row, topk_w, T, k, d, dyw);
+    const dim3 grid((unsigned)((nvec + 255) / 256));
+    if ((d / 8) % 64 == 0)
+      hipLaunchKernelGGL(scale_gather_kernel<true>, grid, dim3(256), 0, s, dy, tk_row, topk_w, T,
+                         k, d, dyw);
+    else
+      hipLaunchKernelGGL(scale_gather_kernel<false>, grid, dim3(256), 0, s, dy, tk_row, topk_w, T,
+                         k, d, dyw);
   }
   return hipGetLastError();
 }
