@@ -107,6 +107,31 @@ def test_expert_sizes_at_the_256_row_block_boundaries():
     assert_bitwise_equal(a, outputs(run_gpu(inp, persistent=True), False))
 
 
+def test_large_experts_on_the_256_tile_kernels_and_accumulation():
+    """Experts of 2500, 1000, 596 and 0 rows at d=1024, I=512: the 256 x 256 dgrad kernels
+    (several K steps and column tiles, with 128-row remainders on the small kernel) and the
+    big-expert wgrad kernel, against the oracle. A second backward with accumulate=1 must then
+    double every weight gradient exactly (x + x is exact in fp32), which covers the
+    accumulating forms of both wgrad kernels."""
+    counts = [2500, 1000, 596, 0]
+    _announce(f"[large] expert sizes {counts}, d=1024 I=512 k=1")
+    E, d, I = len(counts), 1024, 512
+    T = sum(counts)
+    inp = workload.make_inputs("local_zipf", seed=11, device=DEV, T=T, d=d, E=E, I=I)
+    idx = np.repeat(np.arange(E, dtype=np.int32), counts)
+    np.random.default_rng(11).shuffle(idx)
+    inp["topk_idx"] = torch.from_numpy(idx.reshape(T, 1)).to(DEV)
+    L = run_gpu(inp)
+    f, b = run_oracle(inp)
+    assert list(f["counts"]) == counts
+    check_parity(L, inp, f, b)
+    first = [g.clone() for g in (L.dw1, L.dw2)]
+    L.backward(None, inp["W1"], inp["W2"], inp["dY"], accumulate=True)
+    torch.cuda.synchronize()
+    for g0, g in zip(first, (L.dw1, L.dw2)):
+        assert torch.equal(g, 2 * g0)
+
+
 def test_zero_router_and_duplicate_router_rows():
     _announce("[ties] zero router, duplicate rows")
     inp = workload.make_inputs("tiny", seed=5, device=DEV)
