@@ -38,6 +38,7 @@ namespace {
 
 constexpr int BM = kWgradBM, BN = kWgradBN, BK = 32;
 constexpr int kWgradBigRows = 512;  // experts with at least this many rows: wgrad_big_kernel
+constexpr int kEmptyRun = 4;        // tiles per task of an expert with no rows (zero fill)
 constexpr int KRES = 128;           // positions of L kept resident in LDS for a whole task
 constexpr int LDL = KRES + 8;       // row pitch of the L buffer [BM][LDL]
 constexpr int LDR = BK + 8;         // row pitch of an R stage [BN][LDR]
@@ -333,8 +334,10 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
 // Task table for one weight gradient, built by one workgroup from the device offsets. Thread
 // e handles expert e: its K-steps nk = max(ceil(c_e / BK), 1), its run length
 // nt = min(ceil(kWgradTaskSteps / nk), ntn) tiles, and its tasks
-// mstripes * ceil(ntn / nt). Experts are laid out by decreasing row count (ties to the lower
-// index), each expert's tasks stripe-major. count[0] receives the number of tasks.
+// mstripes * ceil(ntn / nt). An expert with no rows only writes zeros; its runs are kEmptyRun
+// tiles, so the zero fill spreads over the grid. Experts are laid out by decreasing row count
+// (ties to the lower index), each expert's tasks stripe-major. count[0] receives the number of
+// tasks.
 // Experts with c_e >= big_rows get no tasks here: big[0].x receives their number and
 // big[1 + i] = (expert, rows) their list in the same order (they hold the first ranks).
 __global__ void __launch_bounds__(1024) wgrad_sched_kernel(const int32_t* __restrict__ offsets,
@@ -360,7 +363,7 @@ __global__ void __launch_bounds__(1024) wgrad_sched_kernel(const int32_t* __rest
     }
     if (!isbig) {
       const int nk = max((c + BK - 1) / BK, 1);
-      nt = min((kWgradTaskSteps + nk - 1) / nk, ntn);
+      nt = min(c == 0 ? kEmptyRun : (kWgradTaskSteps + nk - 1) / nk, ntn);
       nchunks = (ntn + nt - 1) / nt;
       ntask = mstripes * nchunks;
     }
@@ -549,7 +552,8 @@ int resident_grid_big() {
 // Entries: the list of big experts (1 + E), then the task table of the others.
 size_t wgrad_table_entries(int Tk, int E, int Mdim, int Ndim) {
   const long long mstripes = Mdim / BM, ntn = Ndim / BN;
-  const long long per_stripe = ntn * ((long long)Tk + (long long)E * BK) / (BK * kWgradTaskSteps) + E;
+  const long long per_stripe = ntn * ((long long)Tk + (long long)E * BK) / (BK * kWgradTaskSteps) + E +
+                               (long long)E * ((ntn + kEmptyRun - 1) / kEmptyRun);
   const long long cap = (long long)E * ntn;
   return (size_t)(1 + E + mstripes * (per_stripe < cap ? per_stripe : cap));
 }

@@ -85,12 +85,13 @@ def source_hash(src: str) -> str:
 
 def _counter_per_kernel(path, calib_bytes):
     rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
-    # the calibration copy is the last device copy before the layer's first kernel
+    # the calibration copy is the largest device copy before the layer's first kernel (input
+    # set-up may add small copies after it)
     first = next((i for i, r in enumerate(rows) if bench_name(r["Kernel_Name"])), len(rows))
     copies = [float(r["Counter_Value"]) for r in rows[:first] if "copyBuffer" in r["Kernel_Name"]]
     if not copies:
         raise SystemExit(f"{path}: no calibration copy found")
-    scale = calib_bytes / (copies[-1] * 1024.0)  # bytes per counted byte
+    scale = calib_bytes / (max(copies) * 1024.0)  # bytes per counted byte
     out = {}
     for r in rows:
         bn = bench_name(r["Kernel_Name"])
