@@ -127,6 +127,52 @@ MOE_DEV uint4 kmajor_frag(const uint16_t* s, int base, int kb, int lane) {
   return v;
 }
 
+// One 64-deep K step of a wave's MB x NB grid of 16 x 16 output blocks, as two 32-deep
+// substeps, with fragments read from LDS: fa(ks, mb) returns the A fragment of row block mb and
+// fb(ks, nb) the B fragment of column block nb for substep ks, issuing RA and RB LDS reads
+// respectively. Both substeps walk the grid column by column. The reads go out ahead of the
+// MFMAs that use them: all of substep 0's fragments first; then each B fragment's registers
+// take its substep-1 successor once its column is issued, and during the last column each A
+// fragment's registers take theirs. Every accumulator still sees substep 0 before substep 1.
+// sched_group_barrier pins that order; left alone, the scheduler keeps fewer registers live by
+// waiting for each fragment just before its MFMAs, which exposes the LDS latency eight times
+// per substep.
+template <int MB, int NB, int RA, int RB, class FA, class FB>
+MOE_DEV void mma_k64(f32x4 (&acc)[MB][NB], FA fa, FB fb) {
+  uint4 b[NB], a[MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) b[nb] = fb(0, nb);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) a[mb] = fa(0, mb);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      acc[mb][nb] = mfma16(b[nb], a[mb], acc[mb][nb]);
+      if (nb == NB - 1) a[mb] = fa(1, mb);
+    }
+    b[nb] = fb(1, nb);
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mfma16(b[nb], a[mb], acc[mb][nb]);
+  // masks: 0x008 MFMA, 0x100 LDS read
+  __builtin_amdgcn_sched_group_barrier(0x100, NB * RB + MB * RA, 0);
+#pragma unroll
+  for (int nb = 0; nb < NB - 1; ++nb) {
+    __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, MB * NB, 0);
+}
+
 // Workgroup id remapped so that each XCD gets one contiguous range of logical tiles. The
 // hardware deals workgroup b to XCD b % 8; the logical id (b % 8) * R + b / 8 gives XCD x the
 // range [x R, (x+1) R). `total` must be rounded up to a multiple of 8 by the launch.

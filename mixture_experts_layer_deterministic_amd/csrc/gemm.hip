@@ -30,8 +30,9 @@ constexpr int kThreads = 256;
 
 // ROWS x BK tile whose rows are K-contiguous in memory. Rows are element offsets from one base
 // pointer (32 bits each, so a thread holds one register per row rather than a pointer);
-// rowoff(r) < 0 marks a row that loads zeros.
-template <int ROWS, int BK, int LDK, int THREADS = kThreads>
+// rowoff(r) < 0 marks a row that loads zeros. With MAYBE_NULL false every row is real, and the
+// loads carry no per-row condition (no branches around them).
+template <int ROWS, int BK, int LDK, int THREADS = kThreads, bool MAYBE_NULL = true>
 struct LoadK {
   static constexpr int VPR = BK / 8;
   static constexpr int NV = ROWS * VPR;
@@ -54,8 +55,8 @@ struct LoadK {
   MOE_DEV void load(int k0) {
 #pragma unroll
     for (int j = 0; j < PT; ++j)
-      r[j] = off[j] != kNull ? *reinterpret_cast<const uint4*>(base + off[j] + k0)
-                             : make_uint4(0, 0, 0, 0);
+      r[j] = !MAYBE_NULL || off[j] != kNull ? *reinterpret_cast<const uint4*>(base + off[j] + k0)
+                                            : make_uint4(0, 0, 0, 0);
   }
   MOE_DEV void store(uint16_t* s) const {
 #pragma unroll
@@ -123,6 +124,8 @@ struct Geo {
   static constexpr bool kMx = false;
   static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
   static constexpr int kWavesPerEU = 2;  // at most 256 registers per lane
+  // 256-row tiles only ever cover full 256-row blocks of one expert: every row is real
+  static constexpr bool kFull = BM == 256;
   static_assert(WAVES_M * WAVES_N == 4 || WAVES_M * WAVES_N == 8, "4 or 8 waves per workgroup");
   static_assert(BK % 32 == 0 && WM % 16 == 0 && WN % 16 == 0, "tile shape");
 };
@@ -205,8 +208,8 @@ struct FwdGateUpT {
     return nb < G::NB / 2 ? wn * WH + nb * 16 : H2 + wn * WH + (nb - G::NB / 2) * 16;
   }
   struct Loader {
-    LoadK<G::BM, G::BK, G::LDK, G::THREADS> la;
-    LoadK<G::BN, G::BK, G::LDK, G::THREADS> lb;
+    LoadK<G::BM, G::BK, G::LDK, G::THREADS, !G::kFull> la;
+    LoadK<G::BN, G::BK, G::LDK, G::THREADS, false> lb;
     MOE_DEV void init(const Args& a, const Tile& t) {
       const int d = a.d, mc = t.m.mcount;
       la.init(a.xp + (size_t)t.m.row0 * d,
@@ -291,8 +294,8 @@ struct FwdDownT {
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
-    LoadK<G::BM, G::BK, G::LDK, G::THREADS> la;
-    LoadK<G::BN, G::BK, G::LDK, G::THREADS> lb;
+    LoadK<G::BM, G::BK, G::LDK, G::THREADS, !G::kFull> la;
+    LoadK<G::BN, G::BK, G::LDK, G::THREADS, false> lb;
     MOE_DEV void init(const Args& a, const Tile& t) {
       const int I = a.I, mc = t.m.mcount;
       la.init(a.A + (size_t)t.m.row0 * I, [&](int m) { return m < mc ? (long long)m * I : -1LL; });
@@ -604,22 +607,13 @@ __global__ void __launch_bounds__(kDgThreads, 1) gate_dgrad_big_kernel(const Gat
       const uint16_t* sA = sm + (kt & 1) * kDgStage;
       const uint16_t* sB = sA + kDgT * kDgLdA;
       if (kt + 1 < nk) MOE_DG_LOAD((kt + 1) * kDgK);
-#pragma unroll
-      for (int ks = 0; ks < kDgK / 32; ++ks) {
-        const int koff = ks * 32 + (lane / 16) * 8;
-        uint4 bf[kDgWN / 16];
-#pragma unroll
-        for (int nb = 0; nb < kDgWN / 16; ++nb)
-          bf[nb] = kmajor_frag<kDgT>(sB, wn * kDgWN + nb * 16, ks * 32, lane);
-        uint4 af[kDgWM / 16];
-#pragma unroll
-        for (int mb = 0; mb < kDgWM / 16; ++mb)
-          af[mb] = *reinterpret_cast<const uint4*>(sA + (wm * kDgWM + mb * 16 + lane % 16) * kDgLdA + koff);
-#pragma unroll
-        for (int mb = 0; mb < kDgWM / 16; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < kDgWN / 16; ++nb) acc[mb][nb] = mfma16(bf[nb], af[mb], acc[mb][nb]);
-      }
+      const uint16_t* aw = sA + (wm * kDgWM + lane % 16) * kDgLdA + (lane / 16) * 8;
+      mma_k64<kDgWM / 16, kDgWN / 16, 1, 2>(
+          acc,
+          [&](int ks, int mb) {
+            return *reinterpret_cast<const uint4*>(aw + mb * 16 * kDgLdA + ks * 32);
+          },
+          [&](int ks, int nb) { return kmajor_frag<kDgT>(sB, wn * kDgWN + nb * 16, ks * 32, lane); });
       if (kt + 1 < nk) MOE_DG_STORE(sm + ((kt + 1) & 1) * kDgStage);
       __syncthreads();
     }
@@ -728,22 +722,13 @@ __global__ void __launch_bounds__(kDgThreads, 1) down_dgrad_big_kernel(const Dow
       const uint16_t* sA = sm + (kt & 1) * kDgStage;
       const uint16_t* sB = sA + kDgT * kDgLdA;
       if (kt + 1 < nk) MOE_DD_LOAD((kt + 1) * kDgK);
-#pragma unroll
-      for (int ks = 0; ks < kDgK / 32; ++ks) {
-        const int koff = ks * 32 + (lane / 16) * 8;
-        uint4 bf[kDgWN / 16];
-#pragma unroll
-        for (int nb = 0; nb < kDgWN / 16; ++nb)
-          bf[nb] = kmajor_frag<kDgT>(sB, wn * kDgWN + nb * 16, ks * 32, lane);
-        uint4 af[kDgWM / 16];
-#pragma unroll
-        for (int mb = 0; mb < kDgWM / 16; ++mb)
-          af[mb] = *reinterpret_cast<const uint4*>(sA + (wm * kDgWM + mb * 16 + lane % 16) * kDgLdA + koff);
-#pragma unroll
-        for (int mb = 0; mb < kDgWM / 16; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < kDgWN / 16; ++nb) acc[mb][nb] = mfma16(bf[nb], af[mb], acc[mb][nb]);
-      }
+      const uint16_t* aw = sA + (wm * kDgWM + lane % 16) * kDgLdA + (lane / 16) * 8;
+      mma_k64<kDgWM / 16, kDgWN / 16, 1, 2>(
+          acc,
+          [&](int ks, int mb) {
+            return *reinterpret_cast<const uint4*>(aw + mb * 16 * kDgLdA + ks * 32);
+          },
+          [&](int ks, int nb) { return kmajor_frag<kDgT>(sB, wn * kDgWN + nb * 16, ks * 32, lane); });
       if (kt + 1 < nk) MOE_DD_STORE(sm + ((kt + 1) & 1) * kDgStage);
       __syncthreads();
     }
@@ -1402,6 +1387,18 @@ MOE_DEV void run_tile(const typename P::Args& a, const typename P::Tile& t, uint
       if (kt + 1 < nk) ld.load(kt + 1 + k0 < nk ? kt + 1 + k0 : kt + 1 + k0 - nk);
       const uint16_t* sA = cur;
       const uint16_t* sB = cur + G::BM * G::LDK;
+      if constexpr (G::kFull && G::BK == 64) {
+        const uint16_t* aw = sA + (wm * G::WM + lane % 16) * G::LDK + (lane / 16) * 8;
+        const uint16_t* bw = sB + (lane % 16) * G::LDK + (lane / 16) * 8;
+        mma_k64<G::MB, G::NB, 1, 1>(
+            acc,
+            [&](int ks, int mb) {
+              return *reinterpret_cast<const uint4*>(aw + mb * 16 * G::LDK + ks * 32);
+            },
+            [&](int ks, int nb) {
+              return *reinterpret_cast<const uint4*>(bw + P::brow(wn, nb) * G::LDK + ks * 32);
+            });
+      } else
 #pragma unroll
       for (int ks = 0; ks < G::BK / 32; ++ks) {
         const int koff = ks * 32 + (lane / 16) * 8;
