@@ -8,14 +8,23 @@
 
 namespace moe {
 
-// Logits: one lane per token, RE experts per wave, so a wave covers 64 tokens x RE experts.
-// For every (token, expert) a single fp32 accumulator gains x[i] * w[i] for i = 0, 1, ..., d-1
-// in ascending order with one rounding per step. The bf16 x bf16 products are exact in fp32, so
-// fma(x, w, acc) equals fl(acc + x * w). A lane streams its token's row with vector loads. The
-// router rows, widened to fp32 beforehand (exactly), are the same for the whole wave: they
-// arrive through scalar loads straight into FMA operands, and each x value feeds RE chains.
-constexpr int RE = 4;      // experts per wave
-constexpr int RSTEP = 32;  // hidden elements per step
+// Logits: one lane per token and one expert per wave (RE = 1), so a wave covers 64 tokens x 1
+// expert and a block of RW waves the same 64 tokens x RW experts. For every (token, expert) a
+// single fp32 accumulator gains x[i] * w[i] for i = 0, 1, ..., d-1 in ascending order with one
+// rounding per step. The bf16 x bf16 products are exact in fp32, so fma(x, w, acc) equals
+// fl(acc + x * w). The router rows, widened to fp32 beforehand (exactly), are the same for the
+// whole wave: they arrive through scalar loads straight into FMA operands. What sets the rate is
+// how many waves hide those scalar loads' latency: with one expert per wave the grid holds
+// T/64 x E waves (8 per SIMD at T = 2048, E = 256); 4 experts per wave gave 2 per SIMD and ran
+// 1.5x slower, although each x value then fed 4 FMAs. The block's 64 token rows go through
+// LDS, RSTEP hidden elements at a time (double-buffered, each row one whole 128-byte line per
+// step, staged by the first four waves), so the RW waves share one read of them.
+constexpr int RE = 1;       // experts per wave
+constexpr int RW = 8;       // waves per block
+constexpr int RSTEP = 64;   // hidden elements per step (staged in LDS)
+constexpr int RHALF = 32;   // hidden elements per FMA pass (bounds the scalar registers)
+constexpr int RLD = RSTEP + 8;  // LDS row pitch (144 bytes: a lane group's 16-byte reads miss
+                                // each other's banks)
 
 __global__ void __launch_bounds__(256) widen_router_kernel(const uint16_t* __restrict__ wr,
                                                            float* __restrict__ w32, long long n) {
@@ -26,49 +35,67 @@ __global__ void __launch_bounds__(256) widen_router_kernel(const uint16_t* __res
       make_float4(bf2f_lo(v.x), bf2f_hi(v.x), bf2f_lo(v.y), bf2f_hi(v.y));
 }
 
-__global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __restrict__ x,
+__global__ void __launch_bounds__(RW * 64) router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ w32,
                                                             float* __restrict__ logits, int T,
                                                             int d, int E) {
+  __shared__ __align__(16) uint16_t xs[2][kWave * RLD];
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int e0 = (blockIdx.y * 4 + wave) * RE;
-  if (e0 >= E) return;  // whole wave
-  const int t = blockIdx.x * kWave + lane;
-  const uint16_t* xr = x + (size_t)min(t, T - 1) * d;
-  const float* w0 = w32 + (size_t)e0 * d;
-  const int ecount = min(RE, E - e0);
+  const int e0 = (blockIdx.y * RW + wave) * RE;
+  // waves past E still load and meet every barrier; they only skip the FMAs and the store
+  const int ecount = max(0, min(RE, E - e0));
+  const int t0 = blockIdx.x * kWave;
+  // this thread's two 16-byte pieces of each step: token row tid / 4 (a clamped copy of the last
+  // row past T), columns 16 (tid % 4) .. + 16
+  const int lt = (threadIdx.x / 4) % kWave, lc = (threadIdx.x % 4) * 16;
+  const bool stager = threadIdx.x < 256;  // four waves stage the tile
+  const uint16_t* xr = x + (size_t)min(t0 + lt, T - 1) * d + lc;
+  const float* w0 = w32 + (size_t)min(e0, E - 1) * d;
   float acc[RE];
 #pragma unroll
   for (int q = 0; q < RE; ++q) acc[q] = 0.f;
-  // the next step's row vectors are loaded while the current step computes
-  uint4 xn[RSTEP / 8];
-#pragma unroll
-  for (int v = 0; v < RSTEP / 8; ++v) xn[v] = *reinterpret_cast<const uint4*>(xr + 8 * v);
+  uint4 p0 = make_uint4(0, 0, 0, 0), p1 = p0;
+  if (stager) {
+    p0 = *reinterpret_cast<const uint4*>(xr);
+    p1 = *reinterpret_cast<const uint4*>(xr + 8);
+  }
+  int buf = 0;
   for (int i0 = 0; i0 < d; i0 += RSTEP) {
-    float xv[RSTEP];
+    if (stager) {
+      *reinterpret_cast<uint4*>(&xs[buf][lt * RLD + lc]) = p0;
+      *reinterpret_cast<uint4*>(&xs[buf][lt * RLD + lc + 8]) = p1;
+    }
+    __syncthreads();
+    if (stager && i0 + RSTEP < d) {
+      p0 = *reinterpret_cast<const uint4*>(xr + i0 + RSTEP);
+      p1 = *reinterpret_cast<const uint4*>(xr + i0 + RSTEP + 8);
+    }
+    const uint16_t* row = &xs[buf][lane * RLD];
 #pragma unroll
-    for (int v = 0; v < RSTEP / 8; ++v) {
-      const uint32_t xw[4] = {xn[v].x, xn[v].y, xn[v].z, xn[v].w};
+    for (int h = 0; h < RSTEP; h += RHALF) {
+      float xv[RHALF];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        xv[8 * v + 2 * q] = bf2f_lo(xw[q]);
-        xv[8 * v + 2 * q + 1] = bf2f_hi(xw[q]);
+      for (int v = 0; v < RHALF / 8; ++v) {
+        const uint4 q4 = *reinterpret_cast<const uint4*>(row + h + 8 * v);
+        const uint32_t xw[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xv[8 * v + 2 * q] = bf2f_lo(xw[q]);
+          xv[8 * v + 2 * q + 1] = bf2f_hi(xw[q]);
+        }
+      }
+#pragma unroll
+      for (int ee = 0; ee < RE; ++ee) {
+        if (ee >= ecount) break;  // wave-uniform
+        const float* wp = w0 + (size_t)ee * d + i0 + h;
+#pragma unroll
+        for (int q = 0; q < RHALF; ++q) acc[ee] = __builtin_fmaf(xv[q], wp[q], acc[ee]);
       }
     }
-    if (i0 + RSTEP < d) {
-#pragma unroll
-      for (int v = 0; v < RSTEP / 8; ++v)
-        xn[v] = *reinterpret_cast<const uint4*>(xr + i0 + RSTEP + 8 * v);
-    }
-#pragma unroll
-    for (int ee = 0; ee < RE; ++ee) {
-      if (ee >= ecount) break;  // wave-uniform
-      const float* wp = w0 + (size_t)ee * d + i0;
-#pragma unroll
-      for (int q = 0; q < RSTEP; ++q) acc[ee] = __builtin_fmaf(xv[q], wp[q], acc[ee]);
-    }
+    buf ^= 1;
   }
+  const int t = t0 + lane;
   if (t < T) {
 #pragma unroll
     for (int ee = 0; ee < RE; ++ee)
@@ -144,10 +171,10 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, float* w3
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  dim3 grid((T + kWave - 1) / kWave, (E + 4 * RE - 1) / (4 * RE));
+  dim3 grid((T + kWave - 1) / kWave, (E + RW * RE - 1) / (RW * RE));
   {
     TraceScope trace("router_logits", s);
-    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, s, x, w32, logits, T, d, E);
+    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(RW * 64), 0, s, x, w32, logits, T, d, E);
   }
   return hipGetLastError();
 }
