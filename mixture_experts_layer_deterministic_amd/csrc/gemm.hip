@@ -814,7 +814,9 @@ struct GeoMx {
 
 // ROWS rows of fp8 codes, K-contiguous: 8 vectors of 16 bytes per 128-K step. Thread t < ROWS
 // also moves row t's scale word (four block scales of the step), loading the words of four
-// steps at once where the row length allows. A null row loads zeros with unit scales.
+// steps at once where the row length allows. Every row is real (a tile's rows past its expert's
+// count repeat the expert's last row; their outputs are never stored), so the code loads carry
+// no per-row condition, as in LoadK.
 template <int ROWS, int LDK>
 struct LoadK8 {
   static constexpr int VPR = 8;
@@ -834,7 +836,7 @@ struct LoadK8 {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const int v = threadIdx.x + kThreads * j;
-      rp[j] = (v < NV) ? rowptr(v / VPR) : nullptr;
+      rp[j] = rowptr(min(v / VPR, ROWS - 1));
     }
     sp = threadIdx.x < ROWS ? scaleptr(threadIdx.x) : nullptr;
     grouped = kdim % 512 == 0;
@@ -847,8 +849,7 @@ struct LoadK8 {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const int v = threadIdx.x + kThreads * j;
-      r[j] = rp[j] ? *reinterpret_cast<const uint4*>(rp[j] + (size_t)kt * 128 + (v % VPR) * 16)
-                   : make_uint4(0, 0, 0, 0);
+      r[j] = *reinterpret_cast<const uint4*>(rp[j] + (size_t)kt * 128 + (v % VPR) * 16);
     }
     if (!sp) return;
     if (grouped) {
@@ -1013,8 +1014,8 @@ struct MxFwdGateUp {
       const int d = a.d, I = a.I, mc = t.m.mcount, row0 = t.m.row0, n0 = t.n0;
       const uint8_t* xp8 = a.xp8;
       const uint8_t* xps = a.xps;
-      la.init([&](int m) { return m < mc ? xp8 + (size_t)(row0 + m) * d : nullptr; },
-              [&](int m) { return m < mc ? xps + (size_t)(row0 + m) * (d / 32) : nullptr; }, d);
+      la.init([&](int m) { return xp8 + (size_t)(row0 + min(m, mc - 1)) * d; },
+              [&](int m) { return xps + (size_t)(row0 + min(m, mc - 1)) * (d / 32); }, d);
       const size_t wrow0 = (size_t)t.m.e * 2 * I;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
@@ -1022,9 +1023,9 @@ struct MxFwdGateUp {
       lb.init([&](int n) { return w8 + wrow(n) * d; },
               [&](int n) { return ws + wrow(n) * (d / 32); }, d);
     }
-    MOE_DEV void load(int kt) {
-      la.load(kt);
+    MOE_DEV void load(int kt) {  // weights first: they are the HBM stream
       lb.load(kt);
+      la.load(kt);
     }
   };
   static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
@@ -1112,17 +1113,17 @@ struct MxFwdDown {
       const int I = a.I, mc = t.m.mcount, row0 = t.m.row0;
       const uint8_t* aq = a.aq;
       const uint8_t* aqs = a.aqs;
-      la.init([&](int m) { return m < mc ? aq + (size_t)(row0 + m) * I : nullptr; },
-              [&](int m) { return m < mc ? aqs + (size_t)(row0 + m) * (I / 32) : nullptr; }, I);
+      la.init([&](int m) { return aq + (size_t)(row0 + min(m, mc - 1)) * I; },
+              [&](int m) { return aqs + (size_t)(row0 + min(m, mc - 1)) * (I / 32); }, I);
       const size_t wrow0 = (size_t)t.m.e * a.d + t.n0;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
       lb.init([&](int n) { return w8 + (wrow0 + n) * I; },
               [&](int n) { return ws + (wrow0 + n) * (I / 32); }, I);
     }
-    MOE_DEV void load(int kt) {
-      la.load(kt);
+    MOE_DEV void load(int kt) {  // weights first: they are the HBM stream
       lb.load(kt);
+      la.load(kt);
     }
   };
   static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
@@ -1193,17 +1194,17 @@ struct MxBwdDownDgrad {
       const uint8_t* dyq = a.dyq;
       const uint8_t* dys = a.dys;
       const int32_t* rs = a.row_src;
-      la.init([&](int m) { return m < mc ? dyq + (size_t)(rs[row0 + m] / k) * d : nullptr; },
-              [&](int m) { return m < mc ? dys + (size_t)(rs[row0 + m] / k) * (d / 32) : nullptr; }, d);
+      la.init([&](int m) { return dyq + (size_t)(rs[row0 + min(m, mc - 1)] / k) * d; },
+              [&](int m) { return dys + (size_t)(rs[row0 + min(m, mc - 1)] / k) * (d / 32); }, d);
       const size_t wrow0 = (size_t)t.m.e * a.I + t.n0;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
       lb.init([&](int n) { return w8 + (wrow0 + n) * d; },
               [&](int n) { return ws + (wrow0 + n) * (d / 32); }, d);
     }
-    MOE_DEV void load(int kt) {
-      la.load(kt);
+    MOE_DEV void load(int kt) {  // weights first: they are the HBM stream
       lb.load(kt);
+      la.load(kt);
     }
   };
   static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
@@ -1328,17 +1329,17 @@ struct MxBwdGateDgrad {
       const int twoI = 2 * a.I, mc = t.m.mcount, row0 = t.m.row0;
       const uint8_t* dhq = a.dhq;
       const uint8_t* dhs = a.dhs;
-      la.init([&](int m) { return m < mc ? dhq + (size_t)(row0 + m) * twoI : nullptr; },
-              [&](int m) { return m < mc ? dhs + (size_t)(row0 + m) * (twoI / 32) : nullptr; }, twoI);
+      la.init([&](int m) { return dhq + (size_t)(row0 + min(m, mc - 1)) * twoI; },
+              [&](int m) { return dhs + (size_t)(row0 + min(m, mc - 1)) * (twoI / 32); }, twoI);
       const size_t wrow0 = (size_t)t.m.e * a.d + t.n0;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
       lb.init([&](int n) { return w8 + (wrow0 + n) * twoI; },
               [&](int n) { return ws + (wrow0 + n) * (twoI / 32); }, twoI);
     }
-    MOE_DEV void load(int kt) {
-      la.load(kt);
+    MOE_DEV void load(int kt) {  // weights first: they are the HBM stream
       lb.load(kt);
+      la.load(kt);
     }
   };
   static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
