@@ -31,7 +31,9 @@ constexpr int kThreads = 256;
 // ROWS x BK tile whose rows are K-contiguous in memory. Rows are element offsets from one base
 // pointer (32 bits each, so a thread holds one register per row rather than a pointer);
 // rowoff(r) < 0 marks a row that loads zeros. With MAYBE_NULL false every row is real, and the
-// loads carry no per-row condition (no branches around them).
+// loads carry no per-row condition (no branches around them). Every loader here passes real
+// rows (a tile's rows past its expert's count repeat the last row). The null form stays: the
+// same loaders written without it allocate registers differently and spill 32-56 bytes a lane.
 template <int ROWS, int BK, int LDK, int THREADS = kThreads, bool MAYBE_NULL = true>
 struct LoadK {
   static constexpr int VPR = BK / 8;
