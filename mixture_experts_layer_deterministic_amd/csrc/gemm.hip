@@ -10,8 +10,9 @@
 // The two weight gradients have their own kernel (wgrad.hip). One kernel template runs the
 // four, in BF16 and (further down) in MXFP8. A workgroup owns a BM x BN output tile: 128 x 128
 // with 4 waves, or 256 x 256 with 8 waves for the forward GEMMs' full 256-row expert blocks.
-// Tiles of BK stream through double-buffered LDS, stored K-contiguous with padding per row, so
-// every MFMA fragment is one 16-byte LDS read. The weights in dgrad, whose K axis is not
+// Tiles of BK stream through double-buffered LDS, stored K-contiguous in rows of 64 values whose
+// 16-byte chunks are permuted per row (rowswz), so every MFMA fragment is one 16-byte LDS read
+// and neither those reads nor the row stores conflict on banks. The weights in dgrad, whose K axis is not
 // contiguous in memory, are loaded as 8x8 blocks and transposed in registers on their way in.
 //
 // Determinism: every output element is produced by exactly one workgroup, which reduces K in a
@@ -40,6 +41,7 @@ struct LoadK {
   static constexpr int NV = ROWS * VPR;
   static constexpr int PT = (NV + THREADS - 1) / THREADS;
   static constexpr uint32_t kNull = 0xffffffffu;
+  static_assert(BK == 64 && LDK == 64, "rows of 64 values in the chunk-permuted LDS layout");
   const uint16_t* base;
   uint32_t off[PT];
   uint4 r[PT];
@@ -64,16 +66,15 @@ struct LoadK {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const int v = threadIdx.x + THREADS * j;
-      if (v < NV) *reinterpret_cast<uint4*>(s + (v / VPR) * LDK + (v % VPR) * 8) = r[j];
+      if (v < NV) *reinterpret_cast<uint4*>(s + rowswz(v / VPR, v % VPR)) = r[j];
     }
   }
 };
 
 // BK x MN tile stored MN-contiguous in memory (K is the slow axis). Loaded as 8x8 blocks whose
 // k-block index runs fastest across lanes (each wave instruction reads 8 rows x 128 contiguous
-// bytes, and the transposed LDS writes of 16 lanes cover all 64 banks), then transposed so
-// LDS holds [MN][K]. krow(k) returns the row pointer already offset to the tile's first MN
-// column. Only the first NB threads hold a block.
+// bytes), then transposed so LDS holds [MN][K] in rowswz's chunk-permuted rows. Only the first
+// NB threads hold a block.
 template <int MN, int BK, int LDK>
 struct LoadMN {
   static constexpr int BKB = BK / 8;
@@ -81,17 +82,18 @@ struct LoadMN {
   static constexpr int PT = (NB + kThreads - 1) / kThreads;
   uint4 r[PT][8];
 
-  template <class KRow>
-  MOE_DEV void load(int k0, KRow krow) {
+  // w: the tile's first column in its first K row of this step (the same in every lane); ld:
+  // the row pitch. A lane's eight rows are one 32-bit offset plus workgroup-uniform strides.
+  MOE_DEV void load(const uint16_t* w, int ld) {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const int b = threadIdx.x + kThreads * j;
       if (b < NB) {
         const int kb = b % BKB, mb = b / BKB;
+        const uint16_t* p = w + (uint32_t)(kb * 8 * ld + mb * 8);
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-          r[j][rr] = *reinterpret_cast<const uint4*>(krow(k0 + kb * 8 + rr) + mb * 8);
-        }
+        for (int rr = 0; rr < 8; ++rr)
+          r[j][rr] = *reinterpret_cast<const uint4*>(p + (size_t)rr * ld);
       }
     }
   }
@@ -103,9 +105,11 @@ struct LoadMN {
         const int kb = b % BKB, mb = b / BKB;
         uint4 t[8];
         transpose8x8_b16(r[j], t);
+        // rowswz(mb * 8 + c, kb) = mb * 512 + 64 c + 8 (kb ^ c), which is x ^ (72 c) for
+        // x = mb * 512 + 8 kb: one address and a constant per row
+        const int x = rowswz(mb * 8, kb);
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-          *reinterpret_cast<uint4*>(s + (mb * 8 + c) * LDK + kb * 8) = t[c];
+        for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(s + (x ^ (72 * c))) = t[c];
       }
     }
   }
@@ -120,7 +124,7 @@ struct Geo {
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int MB = WM / 16, NB = WN / 16;
-  static constexpr int LDK = BK + 8;
+  static constexpr int LDK = BK;                 // LDS row pitch (chunk-permuted rows, rowswz)
   static constexpr int STAGE = (BM + BN) * LDK;  // uint16 elements per LDS stage
   static constexpr int kSmem = 2 * STAGE * 2;    // bytes, two stages
   static constexpr bool kMx = false;
@@ -394,7 +398,7 @@ struct BwdDownDgrad {
       la.load(kt * G::BK);
       const uint16_t* w = wb;
       const int ld = ldw;
-      lb.load(kt * G::BK, [&](int k) { return w + (size_t)k * ld; });
+      lb.load(w + (size_t)(kt * G::BK) * ld, ld);
     }
     MOE_DEV void store(uint16_t* s) const {
       la.store(s);
@@ -506,7 +510,7 @@ struct BwdGateDgrad {
       la.load(kt * G::BK);
       const uint16_t* w = wb;
       const int ld = ldw;
-      lb.load(kt * G::BK, [&](int k) { return w + (size_t)k * ld; });
+      lb.load(w + (size_t)(kt * G::BK) * ld, ld);
     }
     MOE_DEV void store(uint16_t* s) const {
       la.store(s);
@@ -540,7 +544,7 @@ struct BwdGateDgrad {
 // W1, 256 columns each) is copied into LDS as it is, with kmajor_swz-permuted column groups,
 // and its MFMA fragments are read with gfx950's transposing LDS read (kmajor_frag). dH rows are
 // K-contiguous and go to LDS as [256][72].
-constexpr int kDgT = 256, kDgK = 64, kDgThreads = 512, kDgLdA = kDgK + 8;
+constexpr int kDgT = 256, kDgK = 64, kDgThreads = 512, kDgLdA = kDgK;  // A rows: rowswz
 constexpr int kDgWM = 128, kDgWN = 64;
 constexpr int kDgStage = kDgT * kDgLdA + kDgK * kDgT;  // uint16 elements: dH tile, then W1 tile
 
@@ -591,7 +595,7 @@ __global__ void __launch_bounds__(kDgThreads, 1) gate_dgrad_big_kernel(const Gat
 #define MOE_DG_STORE(st)                                                                        \
   do {                                                                                          \
     const int t_ = threadIdx.x, kr_ = t_ / 32;                                                  \
-    uint16_t* sa_ = (st) + (t_ / 8) * kDgLdA + (t_ % 8) * 8;                                    \
+    uint16_t* sa_ = (st) + rowswz(t_ / 8, t_ % 8); /* rows + 64 j keep the permutation */       \
     uint16_t* sb_ = (st) + kDgT * kDgLdA + kr_ * kDgT + (((t_ % 32) * 8) ^ kmajor_swz(kr_));     \
     *reinterpret_cast<uint4*>(sa_) = ra0;                                                       \
     *reinterpret_cast<uint4*>(sa_ + 64 * kDgLdA) = ra1;                                         \
@@ -615,11 +619,11 @@ __global__ void __launch_bounds__(kDgThreads, 1) gate_dgrad_big_kernel(const Gat
       const uint16_t* sA = sm + (kt & 1) * kDgStage;
       const uint16_t* sB = sA + kDgT * kDgLdA;
       if (kt + 1 < nk) MOE_DG_LOAD((kt + 1) * kDgK);
-      const uint16_t* aw = sA + (wm * kDgWM + lane % 16) * kDgLdA + (lane / 16) * 8;
       mma_k64<kDgWM / 16, kDgWN / 16, 1, 2>(
           acc,
           [&](int ks, int mb) {
-            return *reinterpret_cast<const uint4*>(aw + mb * 16 * kDgLdA + ks * 32);
+            return *reinterpret_cast<const uint4*>(
+                sA + rowswz(wm * kDgWM + mb * 16 + lane % 16, ks * 4 + lane / 16));
           },
           [&](int ks, int nb) { return kmajor_frag<kDgT>(sB, wn * kDgWN + nb * 16, ks * 32, lane); });
       if (kt + 1 < nk) MOE_DG_STORE(sm + ((kt + 1) & 1) * kDgStage);
@@ -706,7 +710,7 @@ __global__ void __launch_bounds__(kDgThreads, 1) down_dgrad_big_kernel(const Dow
 #define MOE_DD_STORE(st)                                                                        \
   do {                                                                                          \
     const int kr_ = tid / 32;                                                                   \
-    uint16_t* sa_ = (st) + (tid / 8) * kDgLdA + (tid % 8) * 8;                                  \
+    uint16_t* sa_ = (st) + rowswz(tid / 8, tid % 8); /* rows + 64 j keep the permutation */     \
     uint16_t* sb_ = (st) + kDgT * kDgLdA + kr_ * kDgT + (((tid % 32) * 8) ^ kmajor_swz(kr_));   \
     *reinterpret_cast<uint4*>(sa_) = ra0;                                                       \
     *reinterpret_cast<uint4*>(sa_ + 64 * kDgLdA) = ra1;                                         \
@@ -730,11 +734,11 @@ __global__ void __launch_bounds__(kDgThreads, 1) down_dgrad_big_kernel(const Dow
       const uint16_t* sA = sm + (kt & 1) * kDgStage;
       const uint16_t* sB = sA + kDgT * kDgLdA;
       if (kt + 1 < nk) MOE_DD_LOAD((kt + 1) * kDgK);
-      const uint16_t* aw = sA + (wm * kDgWM + lane % 16) * kDgLdA + (lane / 16) * 8;
       mma_k64<kDgWM / 16, kDgWN / 16, 1, 2>(
           acc,
           [&](int ks, int mb) {
-            return *reinterpret_cast<const uint4*>(aw + mb * 16 * kDgLdA + ks * 32);
+            return *reinterpret_cast<const uint4*>(
+                sA + rowswz(wm * kDgWM + mb * 16 + lane % 16, ks * 4 + lane / 16));
           },
           [&](int ks, int nb) { return kmajor_frag<kDgT>(sB, wn * kDgWN + nb * 16, ks * 32, lane); });
       if (kt + 1 < nk) MOE_DD_STORE(sm + ((kt + 1) & 1) * kDgStage);
@@ -1394,32 +1398,34 @@ MOE_DEV void run_tile(const typename P::Args& a, const typename P::Tile& t, uint
     for (int kt = 0; kt < nk; ++kt) {
       uint16_t* cur = smem + (kt & 1) * G::STAGE;
       if (kt + 1 < nk) ld.load(kt + 1 + k0 < nk ? kt + 1 + k0 : kt + 1 + k0 - nk);
-      const uint16_t* sA = cur;
-      const uint16_t* sB = cur + G::BM * G::LDK;
+      // fragment rows are 16-row blocks, so rowswz's permutation is the lane's own: chunk
+      // (4 ks + lane / 16) ^ (lane & 7) of row (block + lane % 16)
+      const uint16_t* sA = cur + (wm * G::WM + lane % 16) * G::LDK;
+      const uint16_t* sB = cur + G::BM * G::LDK + (lane % 16) * G::LDK;
+      const int c0 = ((lane / 16) ^ (lane & 7)) << 3, c1 = ((4 + lane / 16) ^ (lane & 7)) << 3;
       if constexpr (G::kFull && G::BK == 64) {
-        const uint16_t* aw = sA + (wm * G::WM + lane % 16) * G::LDK + (lane / 16) * 8;
-        const uint16_t* bw = sB + (lane % 16) * G::LDK + (lane / 16) * 8;
         mma_k64<G::MB, G::NB, 1, 1>(
             acc,
             [&](int ks, int mb) {
-              return *reinterpret_cast<const uint4*>(aw + mb * 16 * G::LDK + ks * 32);
+              return *reinterpret_cast<const uint4*>(sA + mb * 16 * G::LDK + (ks ? c1 : c0));
             },
             [&](int ks, int nb) {
-              return *reinterpret_cast<const uint4*>(bw + P::brow(wn, nb) * G::LDK + ks * 32);
+              return *reinterpret_cast<const uint4*>(sB + P::brow(wn, nb) * G::LDK +
+                                                     (ks ? c1 : c0));
             });
       } else
 #pragma unroll
       for (int ks = 0; ks < G::BK / 32; ++ks) {
-        const int koff = ks * 32 + (lane / 16) * 8;
+        const int co = ks ? c1 : c0;
         // All fragments of the step are read before the first MFMA, so the LDS latency is paid
         // once per step rather than once per 16-row block.
         uint4 bf[G::NB], af[G::MB];
 #pragma unroll
         for (int nb = 0; nb < G::NB; ++nb)
-          bf[nb] = *reinterpret_cast<const uint4*>(sB + (P::brow(wn, nb) + lane % 16) * G::LDK + koff);
+          bf[nb] = *reinterpret_cast<const uint4*>(sB + P::brow(wn, nb) * G::LDK + co);
 #pragma unroll
         for (int mb = 0; mb < G::MB; ++mb)
-          af[mb] = *reinterpret_cast<const uint4*>(sA + (wm * G::WM + mb * 16 + lane % 16) * G::LDK + koff);
+          af[mb] = *reinterpret_cast<const uint4*>(sA + mb * 16 * G::LDK + co);
 #pragma unroll
         for (int mb = 0; mb < G::MB; ++mb) {
           if (!P::m_active(t, wm * G::WM + mb * 16)) continue;
