@@ -802,7 +802,8 @@ __global__ void __launch_bounds__(kDgThreads, 1) down_dgrad_big_kernel(const Dow
 // that instruction on gfx950 (lane l, row or column l % 16, group g = l / 16): bytes 0..15 hold
 // K [16 g, 16 g + 16) and bytes 16..31 hold K [64 + 16 g, 64 + 16 g + 16); the scale of K
 // block b = [32 b, 32 b + 32) comes from byte 0 of lane (row + 16 b). LDS holds each stage as
-// [BM][LDK] A codes, [BN][LDK] B codes, then one 32-bit word of four block scales per row.
+// [BM][LDK] A codes, [BN][LDK] B codes (chunk-permuted rows, mxswz), then one 32-bit word of
+// four block scales per row.
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct GeoMx {
@@ -810,7 +811,7 @@ struct GeoMx {
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int MB = WM / 16, NB = WN / 16;
-  static constexpr int LDK = BK + 16;              // bytes per LDS row
+  static constexpr int LDK = BK;                   // bytes per LDS row (chunks permuted)
   static constexpr int SC_OFF = (BM + BN) * LDK;   // byte offset of the scale words
   static constexpr int STAGE = SC_OFF + (BM + BN) * 4;
   static constexpr int kSmem = 2 * STAGE;
@@ -819,6 +820,11 @@ struct GeoMx {
   static constexpr int kWavesPerEU = 2;
   static_assert(WAVES_M * WAVES_N == 4, "4 waves per workgroup");
 };
+
+// Byte offset of 16-byte chunk `chunk` of row `row` in an fp8 code tile of 128-byte rows, with
+// the chunks permuted per row as in rowswz (chunk c of row r at c ^ (r & 7)): fragment reads
+// and row stores then spread over all banks, where rows padded to 144 bytes conflicted.
+MOE_DEV int mxswz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
 // ROWS rows of fp8 codes, K-contiguous: 8 vectors of 16 bytes per 128-K step. Thread t < ROWS
 // also moves row t's scale word (four block scales of the step), loading the words of four
@@ -875,7 +881,7 @@ struct LoadK8 {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const int v = threadIdx.x + kThreads * j;
-      if (v < NV) *reinterpret_cast<uint4*>(rows + (v / VPR) * LDK + (v % VPR) * 16) = r[j];
+      if (v < NV) *reinterpret_cast<uint4*>(rows + mxswz(v / VPR, v % VPR)) = r[j];
     }
     if (threadIdx.x < ROWS) {
       // masks rather than a selected vector element, which the compiler would index in scratch
@@ -893,9 +899,9 @@ MOE_DEV void mx_store_stage(const LoadK8<G::BM, G::LDK>& la, const LoadK8<G::BN,
   lb.store(stage + G::BM * G::LDK, reinterpret_cast<uint32_t*>(stage + G::SC_OFF) + G::BM);
 }
 
-MOE_DEV i32x8 mx_frag(const uint8_t* row, int g) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * g);
-  const uint4 hi = *reinterpret_cast<const uint4*>(row + 64 + 16 * g);
+MOE_DEV i32x8 mx_frag(const uint8_t* tile, int row, int g) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(tile + mxswz(row, g));
+  const uint4 hi = *reinterpret_cast<const uint4*>(tile + mxswz(row, 4 + g));
   i32x8 v;
   v[0] = static_cast<int>(lo.x);
   v[1] = static_cast<int>(lo.y);
@@ -940,14 +946,14 @@ MOE_DEV void run_tile_mx(const typename P::Args& a, const typename P::Tile& t, u
 #pragma unroll
       for (int nb = 0; nb < G::NB; ++nb) {
         const int row = P::brow(wn, nb) + r16;
-        bf[nb] = mx_frag(sB + row * G::LDK, g);
+        bf[nb] = mx_frag(sB, row, g);
         bs[nb] = static_cast<int>((scB[row] >> (8 * g)) & 0xffu);
       }
 #pragma unroll
       for (int mb = 0; mb < G::MB; ++mb) {
         if (!P::m_active(t, wm * G::WM + mb * 16)) continue;
         const int row = wm * G::WM + mb * 16 + r16;
-        const i32x8 af = mx_frag(sA + row * G::LDK, g);
+        const i32x8 af = mx_frag(sA, row, g);
         const int as = static_cast<int>((scA[row] >> (8 * g)) & 0xffu);
 #pragma unroll
         for (int nb = 0; nb < G::NB; ++nb)
