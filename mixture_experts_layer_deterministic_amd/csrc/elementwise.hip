@@ -47,8 +47,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
     }
 #pragma unroll
     for (int jj = 0; jj < kGather; ++jj)
-      o[jj] = pos[jj] >= 0 ? *reinterpret_cast<const uint4*>(O + (size_t)pos[jj] * d + v * 8)
-                           : make_uint4(0, 0, 0, 0);
+      o[jj] = pos[jj] >= 0 ? nt_load16(O + (size_t)pos[jj] * d + v * 8) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int jj = 0; jj < kGather; ++jj) {
       if (pos[jj] < 0) continue;
@@ -121,8 +120,7 @@ __global__ void __launch_bounds__(256) uncombine_kernel(
 #pragma unroll
     for (int j = 0; j < kGather; ++j) {
       const bool live = pos[j] >= 0;
-      g[j] = live ? *reinterpret_cast<const uint4*>(dXp + (size_t)pos[j] * d + v * 8)
-                  : make_uint4(0, 0, 0, 0);
+      g[j] = live ? nt_load16(dXp + (size_t)pos[j] * d + v * 8) : make_uint4(0, 0, 0, 0);
       h[j] = wr && live ? *reinterpret_cast<const uint4*>(wr + (size_t)e[j] * d + v * 8)
                         : make_uint4(0, 0, 0, 0);
       dl[j] = wr && live ? dl_pos[pos[j]] : 0.f;
@@ -164,8 +162,7 @@ __global__ void __launch_bounds__(256) uncombine_kernel(
     for (int jj = 0; jj < kGather; ++jj) {
       const int j = j0 + jj;
       pos[jj] = j < k ? tk_row[(size_t)t * k + j] : -1;
-      g[jj] = pos[jj] >= 0 ? *reinterpret_cast<const uint4*>(dXp + (size_t)pos[jj] * d + v * 8)
-                           : make_uint4(0, 0, 0, 0);
+      g[jj] = pos[jj] >= 0 ? nt_load16(dXp + (size_t)pos[jj] * d + v * 8) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int jj = 0; jj < kGather; ++jj) {
@@ -244,13 +241,15 @@ __global__ void __launch_bounds__(256) dwr_kernel(const float* __restrict__ dl_p
       const bool live = col && p < q1;
       dl[u] = live ? dl_pos[p] : 0.f;
       if constexpr (MX) {
-        const uint2 q = live ? *reinterpret_cast<const uint2*>(xp8 + (size_t)p * d + c0)
-                             : make_uint2(0, 0);
+        typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+        const u32x2 q2 = live ? __builtin_nontemporal_load(
+                                    reinterpret_cast<const u32x2*>(xp8 + (size_t)p * d + c0))
+                              : u32x2{0u, 0u};
+        const uint2 q = make_uint2(q2[0], q2[1]);
         raw[u] = make_uint4(q.x, q.y, 0, 0);
         sc[u] = live ? xps[(size_t)p * (d / 32) + c0 / 32] : 0u;
       } else {
-        raw[u] = live ? *reinterpret_cast<const uint4*>(xp + (size_t)p * d + c0)
-                      : make_uint4(0, 0, 0, 0);
+        raw[u] = live ? nt_load16(xp + (size_t)p * d + c0) : make_uint4(0, 0, 0, 0);
         sc[u] = 0u;
       }
     }
