@@ -1506,6 +1506,243 @@ static hipError_t launch(const typename P::Args& a, int max_tiles, bool persiste
 }
 
 // ------------------------------------------------------------------------------------------
+// The forward products' full 256-row blocks with direct global -> LDS loads.
+//
+// In run_tile a K step's loads are issued at the start of the step and written to LDS at its
+// end, so they have one step to arrive, and a second step in flight would need 32 more staging
+// registers a lane does not have. Here each load writes LDS itself (buffer_load_dwordx4 with
+// the LDS bit: lane l's 16 bytes land at byte 16 l of a 1 KB block whose base is M0), so no
+// register holds a stage. Activations move through two stages and weights through three, 32 KB
+// each, 160 KB in all: the activation loads of a step have one step to arrive, the weight
+// loads two.
+//
+// The stages hold run_tile's chunk-permuted rows (row r's 16-byte chunk c at position
+// c ^ (r & 7)), so the fragment reads and MFMAs are run_tile's and so are the results, bit for
+// bit. One load instruction covers 8 rows: lane l fetches chunk (l % 8) ^ (l / 8) of row l / 8,
+// each row one whole 128-byte line.
+//
+// The five stages are distinct LDS arrays and the K loop is unrolled by six (both stage
+// cycles), so the compiler can tell which stage each load writes and each read reads, and does
+// not wait for every load in flight before an LDS read. A wave's loads complete in issue order;
+// a step issues the activations of step kt + 1 before the weights of step kt + 2, so at the top
+// of step kt only the four weight loads issued last may still be in flight. The step waits for
+// the rest, then meets the other waves at a bare barrier: a workgroup fence there would wait
+// for every load, since loads into LDS count as LDS writes. Loads past the last K chunk reload
+// the last chunk into a free stage, so every step issues the same eight loads and the count
+// holds.
+constexpr int kDmaStage = 256 * 64;  // uint16 per stage: 256 rows of 64 K values
+__shared__ __align__(1024) uint16_t dma_a0[kDmaStage];
+__shared__ __align__(1024) uint16_t dma_a1[kDmaStage];
+__shared__ __align__(1024) uint16_t dma_b0[kDmaStage];
+__shared__ __align__(1024) uint16_t dma_b1[kDmaStage];
+__shared__ __align__(1024) uint16_t dma_b2[kDmaStage];
+
+template <int S>
+MOE_DEV uint16_t* dma_stage_a() {
+  if constexpr (S == 0) return dma_a0;
+  else return dma_a1;
+}
+template <int S>
+MOE_DEV uint16_t* dma_stage_b() {
+  if constexpr (S == 0) return dma_b0;
+  else if constexpr (S == 1) return dma_b1;
+  else return dma_b2;
+}
+
+// Buffer resource over a whole tensor: raw (stride 0), no range limit, gfx9 data format word.
+MOE_DEV __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
+}
+
+// 16 bytes per lane from rsrc's base + soff + voff bytes to LDS at lds + 16 * lane bytes (rsrc,
+// soff and lds the same in every lane). The 32-bit lane offset lives in one register for the
+// whole tile; the K advance rides in soff.
+MOE_DEV void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint16_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds,
+                                           16, voff, soff, 0, 0);
+}
+
+// A 16-byte LDS read as one vector load. Read as a uint4 struct, the load is split into four
+// 32-bit loads and put back together late, and the rebuilt load loses the alias scope that
+// tells the stages apart: the compiler then waits for every load in flight before it.
+MOE_DEV uint4 lds_read16(const uint16_t* p) {
+  typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// gfx9 s_waitcnt immediates: vmcnt [3:0], expcnt [6:4], lgkmcnt [11:8]
+constexpr int kWaitVm4Lgkm0 = 0x0074;  // vmcnt(4) lgkmcnt(0)
+constexpr int kWaitVm0Lgkm0 = 0x0070;  // vmcnt(0) lgkmcnt(0)
+
+// A lane's sources for one tile: byte offsets of its four activation rows and four weight rows
+// (one per load instruction) from the tile's bases.
+struct DmaSrc {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t ao[4], bo[4];
+  int k0, nk;
+};
+
+// Problem 1's full blocks: rows of xp (pitch d) against W1[e]'s gate rows n0.. and up rows
+// I + n0.. (pitch d), in the LDS row order of Problem 1's B tile.
+struct DmaGateUp {
+  using P = FwdGateUpBig;
+  static MOE_DEV int ld(const P::Args& a) { return a.d; }
+  static MOE_DEV const uint16_t* abase(const P::Args& a, const P::Tile& t) {
+    return a.xp + (size_t)t.m.row0 * a.d;
+  }
+  static MOE_DEV const uint16_t* bbase(const P::Args& a, const P::Tile& t) {
+    return a.w1 + (size_t)t.m.e * 2 * a.I * a.d;
+  }
+  static MOE_DEV int brow(const P::Args& a, const P::Tile& t, int n) {
+    return n < 128 ? t.n0 + n : a.I + t.n0 + n - 128;
+  }
+};
+
+// Problem 2's full blocks: rows of A (pitch I) against W2[e]'s rows n0.. (pitch I).
+struct DmaDown {
+  using P = FwdDownBig;
+  static MOE_DEV int ld(const P::Args& a) { return a.I; }
+  static MOE_DEV const uint16_t* abase(const P::Args& a, const P::Tile& t) {
+    return a.A + (size_t)t.m.row0 * a.I;
+  }
+  static MOE_DEV const uint16_t* bbase(const P::Args& a, const P::Tile& t) {
+    return a.w2 + ((size_t)t.m.e * a.d + t.n0) * a.I;
+  }
+  static MOE_DEV int brow(const P::Args&, const P::Tile&, int n) { return n; }
+};
+
+// K chunk kt of the tile (rotated by k0, clamped to the last) into activation stage S: the
+// wave's 32 rows, 8 per instruction.
+template <int S>
+MOE_DEV void dma_issue_a(const DmaSrc& s, int kt, int wave) {
+  int kk = min(kt, s.nk - 1) + s.k0;
+  kk = kk >= s.nk ? kk - s.nk : kk;
+  uint16_t* st = dma_stage_a<S>() + wave * 32 * 64;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma16(s.ra, s.ao[j], (uint32_t)kk * 128u, st + j * 8 * 64);
+}
+template <int S>
+MOE_DEV void dma_issue_b(const DmaSrc& s, int kt, int wave) {
+  int kk = min(kt, s.nk - 1) + s.k0;
+  kk = kk >= s.nk ? kk - s.nk : kk;
+  uint16_t* st = dma_stage_b<S>() + wave * 32 * 64;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma16(s.rb, s.bo[j], (uint32_t)kk * 128u, st + j * 8 * 64);
+}
+
+// K step kt on activation stage SA and weight stage SB: wait for them, refill the stages the
+// previous step read (activations of step kt + 1, weights of step kt + 2), then run_tile's
+// 64-deep MFMA step.
+template <class D, int SA, int SB>
+MOE_DEV void dma_step(f32x4 (&acc)[8][4], const DmaSrc& s, int kt, int wave, int wm, int wn,
+                      int lane) {
+  using P = typename D::P;
+  __builtin_amdgcn_s_waitcnt(kWaitVm4Lgkm0);
+  __builtin_amdgcn_s_barrier();
+  dma_issue_a<SA ^ 1>(s, kt + 1, wave);
+  dma_issue_b<(SB + 2) % 3>(s, kt + 2, wave);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint16_t* sA = dma_stage_a<SA>() + (wm * 128 + lane % 16) * 64;
+  const uint16_t* sB = dma_stage_b<SB>() + (lane % 16) * 64;
+  const int c0 = ((lane / 16) ^ (lane & 7)) << 3, c1 = ((4 + lane / 16) ^ (lane & 7)) << 3;
+  mma_k64<8, 4, 1, 1>(
+      acc,
+      [&](int ks, int mb) {
+        return lds_read16(sA + mb * 16 * 64 + (ks ? c1 : c0));
+      },
+      [&](int ks, int nb) { return lds_read16(sB + P::brow(wn, nb) * 64 + (ks ? c1 : c0)); });
+}
+
+template <class D>
+__global__ void __launch_bounds__(512, 2) dma_kernel(const typename D::P::Args a) {
+  using P = typename D::P;
+  static_assert(P::G::BM == 256 && P::G::BN == 256 && P::G::BK == 64 && P::G::THREADS == 512,
+                "256 x 256 tiles, K steps of 64, eight waves");
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = wave / 4, wn = wave % 4;
+  const int ntiles = P::ntiles(a);
+  const int R = (ntiles + kXcds - 1) / kXcds;
+  const int step = gridDim.x / kXcds;
+  for (int sidx = blockIdx.x / kXcds; sidx < R; sidx += step) {
+    const int lt = (blockIdx.x % kXcds) * R + sidx;  // XCD x takes tiles [x R, (x+1) R)
+    if (lt >= ntiles) break;
+    const typename P::Tile t = P::decode(a, lt);
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    DmaSrc s;
+    s.nk = P::num_k(a, t);
+    if (s.nk > 0) {
+      s.k0 = P::k_first(t, s.nk);
+      s.ra = raw_rsrc(D::abase(a, t));
+      s.rb = raw_rsrc(D::bbase(a, t));
+      const int ld = D::ld(a), r8 = lane / 8, c = (lane % 8) ^ r8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 32 * wave + 8 * j + r8;
+        // rows past the expert's count (none, on full blocks) would repeat its last row
+        s.ao[j] = 2u * ((uint32_t)min(row, t.m.mcount - 1) * ld + c * 8);
+        s.bo[j] = 2u * ((uint32_t)D::brow(a, t, row) * ld + c * 8);
+      }
+      dma_issue_a<0>(s, 0, wave);
+      dma_issue_b<0>(s, 0, wave);
+      dma_issue_b<1>(s, 1, wave);
+      for (int kt = 0;; kt += 6) {
+        dma_step<D, 0, 0>(acc, s, kt, wave, wm, wn, lane);
+        if (kt + 1 >= s.nk) break;
+        dma_step<D, 1, 1>(acc, s, kt + 1, wave, wm, wn, lane);
+        if (kt + 2 >= s.nk) break;
+        dma_step<D, 0, 2>(acc, s, kt + 2, wave, wm, wn, lane);
+        if (kt + 3 >= s.nk) break;
+        dma_step<D, 1, 0>(acc, s, kt + 3, wave, wm, wn, lane);
+        if (kt + 4 >= s.nk) break;
+        dma_step<D, 0, 1>(acc, s, kt + 4, wave, wm, wn, lane);
+        if (kt + 5 >= s.nk) break;
+        dma_step<D, 1, 2>(acc, s, kt + 5, wave, wm, wn, lane);
+        if (kt + 6 >= s.nk) break;
+      }
+      // the trailing reloads have landed and no wave still reads a stage: the next tile's
+      // first loads may go out as soon as its epilogue is done
+      __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+      __builtin_amdgcn_s_barrier();
+    }
+    P::epilogue(a, t, acc, nullptr);
+  }
+}
+
+// Grid as launch's: one-shot grids cover every tile, persistent grids are the resident
+// workgroup count (one per CU: the stages take all of its LDS); both multiples of 8.
+template <class D>
+static hipError_t launch_dma(const typename D::P::Args& a, int max_tiles, bool persistent,
+                             hipStream_t stream) {
+  if (max_tiles <= 0) return hipSuccess;
+  int grid = (max_tiles + kXcds - 1) / kXcds * kXcds;
+  if (persistent) {
+    static int resident = 0;  // per kernel; every device of one process is an MI355X
+    if (resident == 0) {
+      int dev = 0, cus = 0, per_cu = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&dma_kernel<D>), 512, 0);
+      if (e != hipSuccess) return e;
+      resident = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
+    }
+    if (resident > 0 && resident < grid) grid = resident;
+  }
+  {
+    TraceScope trace(D::P::kName, stream);
+    hipLaunchKernelGGL(dma_kernel<D>, dim3(grid), dim3(512), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
 // Schedule tables, built on the device from the offsets so the host never learns the counts.
 // Entry 0 of each holds its count; entry i >= 1 is (expert, first row within the expert).
 //  * full: every 128-row block of every expert;
@@ -1581,7 +1818,7 @@ hipError_t launch_sched_build(const int32_t* offsets, int E, int Tk, int2* sched
 hipError_t launch_fwd_gateup(const GemmFwdGateUpArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
   FwdGateUpBig::Args ab{x.xp, x.w1, x.H, x.A, x.offsets, st.big, x.d, x.I};
-  hipError_t e = launch<FwdGateUpBig>(ab, sched_max_big(x.Tk) * (x.I / 128), persistent, s);
+  hipError_t e = launch_dma<DmaGateUp>(ab, sched_max_big(x.Tk) * (x.I / 128), persistent, s);
   if (e != hipSuccess) return e;
   FwdGateUp::Args a{x.xp, x.w1, x.H, x.A, x.offsets, st.rem, x.d, x.I};
   return launch<FwdGateUp>(a, sched_max_rem(x.Tk, x.E) * (x.I / 64), persistent, s);
@@ -1590,7 +1827,7 @@ hipError_t launch_fwd_gateup(const GemmFwdGateUpArgs& x, bool persistent, hipStr
 hipError_t launch_fwd_down(const GemmFwdDownArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
   FwdDownBig::Args ab{x.A, x.w2, x.O, x.offsets, st.big, x.d, x.I};
-  hipError_t e = launch<FwdDownBig>(ab, sched_max_big(x.Tk) * (x.d / 256), persistent, s);
+  hipError_t e = launch_dma<DmaDown>(ab, sched_max_big(x.Tk) * (x.d / 256), persistent, s);
   if (e != hipSuccess) return e;
   FwdDown::Args a{x.A, x.w2, x.O, x.offsets, st.rem, x.d, x.I};
   return launch<FwdDown>(a, sched_max_rem(x.Tk, x.E) * (x.d / 128), persistent, s);
