@@ -537,16 +537,13 @@ struct BwdGateDgrad {
   }
 };
 
-
-// Problem 4 on full 256-row blocks, where an expert's rows make it MFMA-bound: 256 x 256 tiles,
-// eight waves of 128 x 64, two LDS stages of 64 K. W1[e] is d-contiguous, and a register
-// transpose of a 256-wide tile does not fit beside 128 accumulators; so its K step (64 rows of
-// W1, 256 columns each) is copied into LDS as it is, with kmajor_swz-permuted column groups,
-// and its MFMA fragments are read with gfx950's transposing LDS read (kmajor_frag). dH rows are
-// K-contiguous and go to LDS as [256][72].
-constexpr int kDgT = 256, kDgK = 64, kDgThreads = 512, kDgLdA = kDgK;  // A rows: rowswz
-constexpr int kDgWM = 128, kDgWN = 64;
-constexpr int kDgStage = kDgT * kDgLdA + kDgK * kDgT;  // uint16 elements: dH tile, then W1 tile
+// Problems 4 and 3 on full 256-row blocks, where an expert's rows make them MFMA-bound: 256 x
+// 256 tiles of eight 128 x 64 wave tiles. The weights (W1[e] d-contiguous, W2[e] I-contiguous)
+// are K-major here, and a register transpose of a 256-wide tile does not fit beside 128
+// accumulators; so a K step of weights (64 rows, 256 columns) sits in LDS as it is in memory,
+// with kmajor_swz-permuted column groups, and its MFMA fragments come from gfx950's transposing
+// LDS read. The kernel (dma_kernel, with the forward products) is further on.
+constexpr int kDgT = 256;  // tile rows and columns
 
 struct GateDgradBigArgs {
   const uint16_t* dH;  // [T*k, 2I]
@@ -557,100 +554,6 @@ struct GateDgradBigArgs {
   int d, I;
 };
 
-__global__ void __launch_bounds__(kDgThreads, 1) gate_dgrad_big_kernel(const GateDgradBigArgs a) {
-  __shared__ __align__(16) uint16_t sm[2 * kDgStage];
-  const int ntc = a.d / kDgT;
-  const int nblk = a.big[0].x;
-  const int ntiles = nblk * ntc;
-  const int lane = threadIdx.x % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int wm = wave / (kDgT / kDgWN), wn = wave % (kDgT / kDgWN);
-  const int twoI = 2 * a.I;
-  const int R = (ntiles + kXcds - 1) / kXcds;
-  const int step = gridDim.x / kXcds;
-  for (int sidx = blockIdx.x / kXcds; sidx < R; sidx += step) {
-    const int lt = (blockIdx.x % kXcds) * R + sidx;  // XCD x takes tiles [x R, (x+1) R)
-    if (lt >= ntiles) break;
-    const int2 mn = tile_mn<true>(lt, nblk, ntc);
-    const MTile mt = decode_mtile(a.big, a.offsets, mn.x, kDgT);
-    const int n0 = mn.y * kDgT;
-    const uint16_t* ab = a.dH + (size_t)mt.row0 * twoI;
-    const uint16_t* bb = a.w1 + (size_t)mt.e * twoI * a.d + n0;
-    // per thread four 16-byte vectors of each operand per K step
-    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-#define MOE_DG_LOAD(k0)                                                                         \
-  do {                                                                                          \
-    const int t_ = threadIdx.x;                                                                 \
-    const uint16_t* a_ = ab + (size_t)(t_ / 8) * twoI + (k0) + (t_ % 8) * 8;                     \
-    const uint16_t* b_ = bb + (size_t)((k0) + t_ / 32) * a.d + (t_ % 32) * 8;                   \
-    ra0 = *reinterpret_cast<const uint4*>(a_);                                                  \
-    ra1 = *reinterpret_cast<const uint4*>(a_ + (size_t)64 * twoI);                              \
-    ra2 = *reinterpret_cast<const uint4*>(a_ + (size_t)128 * twoI);                             \
-    ra3 = *reinterpret_cast<const uint4*>(a_ + (size_t)192 * twoI);                             \
-    rb0 = *reinterpret_cast<const uint4*>(b_);                                                  \
-    rb1 = *reinterpret_cast<const uint4*>(b_ + (size_t)16 * a.d);                               \
-    rb2 = *reinterpret_cast<const uint4*>(b_ + (size_t)32 * a.d);                               \
-    rb3 = *reinterpret_cast<const uint4*>(b_ + (size_t)48 * a.d);                               \
-  } while (0)
-#define MOE_DG_STORE(st)                                                                        \
-  do {                                                                                          \
-    const int t_ = threadIdx.x, kr_ = t_ / 32;                                                  \
-    uint16_t* sa_ = (st) + rowswz(t_ / 8, t_ % 8); /* rows + 64 j keep the permutation */       \
-    uint16_t* sb_ = (st) + kDgT * kDgLdA + kr_ * kDgT + (((t_ % 32) * 8) ^ kmajor_swz(kr_));     \
-    *reinterpret_cast<uint4*>(sa_) = ra0;                                                       \
-    *reinterpret_cast<uint4*>(sa_ + 64 * kDgLdA) = ra1;                                         \
-    *reinterpret_cast<uint4*>(sa_ + 128 * kDgLdA) = ra2;                                        \
-    *reinterpret_cast<uint4*>(sa_ + 192 * kDgLdA) = ra3;                                        \
-    *reinterpret_cast<uint4*>(sb_) = rb0;                                                       \
-    *reinterpret_cast<uint4*>(sb_ + 16 * kDgT) = rb1;                                           \
-    *reinterpret_cast<uint4*>(sb_ + 32 * kDgT) = rb2;                                           \
-    *reinterpret_cast<uint4*>(sb_ + 48 * kDgT) = rb3;                                           \
-  } while (0)
-    f32x4 acc[kDgWM / 16][kDgWN / 16];
-#pragma unroll
-    for (int i = 0; i < kDgWM / 16; ++i)
-#pragma unroll
-      for (int j = 0; j < kDgWN / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int nk = twoI / kDgK;
-    MOE_DG_LOAD(0);
-    MOE_DG_STORE(sm);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint16_t* sA = sm + (kt & 1) * kDgStage;
-      const uint16_t* sB = sA + kDgT * kDgLdA;
-      if (kt + 1 < nk) MOE_DG_LOAD((kt + 1) * kDgK);
-      mma_k64<kDgWM / 16, kDgWN / 16, 1, 2>(
-          acc,
-          [&](int ks, int mb) {
-            return *reinterpret_cast<const uint4*>(
-                sA + rowswz(wm * kDgWM + mb * 16 + lane % 16, ks * 4 + lane / 16));
-          },
-          [&](int ks, int nb) { return kmajor_frag<kDgT>(sB, wn * kDgWN + nb * 16, ks * 32, lane); });
-      if (kt + 1 < nk) MOE_DG_STORE(sm + ((kt + 1) & 1) * kDgStage);
-      __syncthreads();
-    }
-#undef MOE_DG_LOAD
-#undef MOE_DG_STORE
-#pragma unroll
-    for (int mb = 0; mb < kDgWM / 16; ++mb) {
-      const size_t pos = mt.row0 + wm * kDgWM + mb * 16 + lane % 16;
-      uint16_t* orow = a.dXp + pos * a.d + n0 + wn * kDgWN + 4 * (lane / 16);
-#pragma unroll
-      for (int nb = 0; nb < kDgWN / 16; ++nb) {
-        uint2 o;
-        o.x = pack_bf2(acc[mb][nb][0], acc[mb][nb][1]);
-        o.y = pack_bf2(acc[mb][nb][2], acc[mb][nb][3]);
-        *reinterpret_cast<uint2*>(orow + nb * 16) = o;
-      }
-    }
-  }
-}
-
-// Problem 3 on full 256-row blocks: the same 256 x 256 structure as gate_dgrad_big_kernel, with
-// dY rows gathered through row_src and W2[e] ([d, I], I-contiguous) as the K-major operand. The
-// epilogue is Problem 3's: per (pos, i) the SwiGLU backward into dH, and the router-weight
-// partials dw = sum_i dA'[pos, i] A[pos, i] of each 128-column half, summed in a fixed order
-// (a lane's columns, then its lane groups, then the two waves of the half).
 struct DownDgradBigArgs {
   const uint16_t* dy;      // [T, d]
   const int32_t* row_src;  // [T*k]
@@ -665,136 +568,6 @@ struct DownDgradBigArgs {
   int d, I, k;
 };
 
-__global__ void __launch_bounds__(kDgThreads, 1) down_dgrad_big_kernel(const DownDgradBigArgs a) {
-  __shared__ __align__(16) uint16_t sm[2 * kDgStage];
-  const int ntc = a.I / kDgT;
-  const int nblk = a.big[0].x;
-  const int ntiles = nblk * ntc;
-  const int lane = threadIdx.x % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int wm = wave / (kDgT / kDgWN), wn = wave % (kDgT / kDgWN);
-  const int I = a.I, d = a.d;
-  const int R = (ntiles + kXcds - 1) / kXcds;
-  const int step = gridDim.x / kXcds;
-  for (int sidx = blockIdx.x / kXcds; sidx < R; sidx += step) {
-    const int lt = (blockIdx.x % kXcds) * R + sidx;  // XCD x takes tiles [x R, (x+1) R)
-    if (lt >= ntiles) break;
-    const int2 mn = tile_mn<true>(lt, nblk, ntc);
-    const MTile mt = decode_mtile(a.big, a.offsets, mn.x, kDgT);
-    const int n0 = mn.y * kDgT;
-    const int tid = threadIdx.x;
-    // this thread's four dY rows (block rows tid / 8 + 64 j) as element offsets
-    uint32_t ao0, ao1, ao2, ao3;
-    {
-      const int32_t* rs = a.row_src + mt.row0 + tid / 8;
-      const uint32_t c = (tid % 8) * 8;
-      ao0 = (uint32_t)(rs[0] / a.k) * (uint32_t)d + c;
-      ao1 = (uint32_t)(rs[64] / a.k) * (uint32_t)d + c;
-      ao2 = (uint32_t)(rs[128] / a.k) * (uint32_t)d + c;
-      ao3 = (uint32_t)(rs[192] / a.k) * (uint32_t)d + c;
-    }
-    const uint16_t* bb = a.w2 + (size_t)mt.e * d * I + n0 + (tid % 32) * 8;
-    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-#define MOE_DD_LOAD(k0)                                                                         \
-  do {                                                                                          \
-    const uint16_t* b_ = bb + (size_t)((k0) + tid / 32) * I;                                    \
-    ra0 = *reinterpret_cast<const uint4*>(a.dy + ao0 + (k0));                                   \
-    ra1 = *reinterpret_cast<const uint4*>(a.dy + ao1 + (k0));                                   \
-    ra2 = *reinterpret_cast<const uint4*>(a.dy + ao2 + (k0));                                   \
-    ra3 = *reinterpret_cast<const uint4*>(a.dy + ao3 + (k0));                                   \
-    rb0 = *reinterpret_cast<const uint4*>(b_);                                                  \
-    rb1 = *reinterpret_cast<const uint4*>(b_ + (size_t)16 * I);                                 \
-    rb2 = *reinterpret_cast<const uint4*>(b_ + (size_t)32 * I);                                 \
-    rb3 = *reinterpret_cast<const uint4*>(b_ + (size_t)48 * I);                                 \
-  } while (0)
-#define MOE_DD_STORE(st)                                                                        \
-  do {                                                                                          \
-    const int kr_ = tid / 32;                                                                   \
-    uint16_t* sa_ = (st) + rowswz(tid / 8, tid % 8); /* rows + 64 j keep the permutation */     \
-    uint16_t* sb_ = (st) + kDgT * kDgLdA + kr_ * kDgT + (((tid % 32) * 8) ^ kmajor_swz(kr_));   \
-    *reinterpret_cast<uint4*>(sa_) = ra0;                                                       \
-    *reinterpret_cast<uint4*>(sa_ + 64 * kDgLdA) = ra1;                                         \
-    *reinterpret_cast<uint4*>(sa_ + 128 * kDgLdA) = ra2;                                        \
-    *reinterpret_cast<uint4*>(sa_ + 192 * kDgLdA) = ra3;                                        \
-    *reinterpret_cast<uint4*>(sb_) = rb0;                                                       \
-    *reinterpret_cast<uint4*>(sb_ + 16 * kDgT) = rb1;                                           \
-    *reinterpret_cast<uint4*>(sb_ + 32 * kDgT) = rb2;                                           \
-    *reinterpret_cast<uint4*>(sb_ + 48 * kDgT) = rb3;                                           \
-  } while (0)
-    f32x4 acc[kDgWM / 16][kDgWN / 16];
-#pragma unroll
-    for (int i = 0; i < kDgWM / 16; ++i)
-#pragma unroll
-      for (int j = 0; j < kDgWN / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int nk = d / kDgK;
-    MOE_DD_LOAD(0);
-    MOE_DD_STORE(sm);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint16_t* sA = sm + (kt & 1) * kDgStage;
-      const uint16_t* sB = sA + kDgT * kDgLdA;
-      if (kt + 1 < nk) MOE_DD_LOAD((kt + 1) * kDgK);
-      mma_k64<kDgWM / 16, kDgWN / 16, 1, 2>(
-          acc,
-          [&](int ks, int mb) {
-            return *reinterpret_cast<const uint4*>(
-                sA + rowswz(wm * kDgWM + mb * 16 + lane % 16, ks * 4 + lane / 16));
-          },
-          [&](int ks, int nb) { return kmajor_frag<kDgT>(sB, wn * kDgWN + nb * 16, ks * 32, lane); });
-      if (kt + 1 < nk) MOE_DD_STORE(sm + ((kt + 1) & 1) * kDgStage);
-      __syncthreads();
-    }
-#undef MOE_DD_LOAD
-#undef MOE_DD_STORE
-    float* red = reinterpret_cast<float*>(sm);  // [4][256] row sums per wave column; LDS is free
-#pragma unroll
-    for (int mb = 0; mb < kDgWM / 16; ++mb) {
-      const int m = wm * kDgWM + mb * 16 + lane % 16;
-      const size_t pos = mt.row0 + m;
-      const float w = a.topk_w[a.row_src[pos]];
-      float part = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < kDgWN / 16; ++nb) {
-        const int i = n0 + wn * kDgWN + nb * 16 + 4 * (lane / 16);
-        const uint2 av = *reinterpret_cast<const uint2*>(a.A + pos * I + i);
-        const uint2 gv = *reinterpret_cast<const uint2*>(a.H + pos * 2 * I + i);
-        const uint2 uv = *reinterpret_cast<const uint2*>(a.H + pos * 2 * I + I + i);
-        const float av4[4] = {bf2f_lo(av.x), bf2f_hi(av.x), bf2f_lo(av.y), bf2f_hi(av.y)};
-        const float g4[4] = {bf2f_lo(gv.x), bf2f_hi(gv.x), bf2f_lo(gv.y), bf2f_hi(gv.y)};
-        const float u4[4] = {bf2f_lo(uv.x), bf2f_hi(uv.x), bf2f_lo(uv.y), bf2f_hi(uv.y)};
-        float dg[4], du[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float dap = acc[mb][nb][r];
-          part = __builtin_fmaf(dap, av4[r], part);
-          const float dA = w * dap;
-          const float sg = sigmoid(g4[r]);
-          dg[r] = dA * u4[r] * sg * (1.0f + g4[r] * (1.0f - sg));
-          du[r] = dA * (g4[r] * sg);
-        }
-        uint2 o;
-        o.x = pack_bf2(dg[0], dg[1]);
-        o.y = pack_bf2(dg[2], dg[3]);
-        *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + i) = o;
-        o.x = pack_bf2(du[0], du[1]);
-        o.y = pack_bf2(du[2], du[3]);
-        *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + I + i) = o;
-      }
-      // lanes l, l^16, l^32, l^48 share row m: butterfly in a fixed pattern
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      if (lane < 16) red[wn * kDgT + m] = part;
-    }
-    __syncthreads();
-    if (tid < kDgT) {
-      const size_t pos = mt.row0 + tid;
-      float* dst = a.dwpart + pos * (I / 128) + n0 / 128;
-      dst[0] = red[0 * kDgT + tid] + red[1 * kDgT + tid];  // columns [n0, n0 + 128)
-      dst[1] = red[2 * kDgT + tid] + red[3 * kDgT + tid];  // columns [n0 + 128, n0 + 256)
-    }
-    __syncthreads();  // red aliases the next tile's first LDS stage
-  }
-}
 
 // ------------------------------------------------------------------------------------------
 // MXFP8 mode. Both operands are E4M3 codes, K-contiguous, with one E8M0 scale per 32 along K;
@@ -1506,31 +1279,35 @@ static hipError_t launch(const typename P::Args& a, int max_tiles, bool persiste
 }
 
 // ------------------------------------------------------------------------------------------
-// The forward products' full 256-row blocks with direct global -> LDS loads.
+// Full 256-row blocks with direct global -> LDS loads: the forward products and the dgrads.
 //
-// In run_tile a K step's loads are issued at the start of the step and written to LDS at its
-// end, so they have one step to arrive, and a second step in flight would need 32 more staging
-// registers a lane does not have. Here each load writes LDS itself (buffer_load_dwordx4 with
-// the LDS bit: lane l's 16 bytes land at byte 16 l of a 1 KB block whose base is M0), so no
-// register holds a stage. Activations move through two stages and weights through three, 32 KB
-// each, 160 KB in all: the activation loads of a step have one step to arrive, the weight
-// loads two.
+// In a register-staged K loop a step's loads are issued at the start of the step and written to
+// LDS at its end, so they have one step to arrive, and a second step in flight would need 32
+// more staging registers a lane does not have. Here each load writes LDS itself
+// (buffer_load_dwordx4 with the LDS bit: lane l's 16 bytes land at byte 16 l of a 1 KB block
+// whose base is M0), so no register holds a stage. The token-row operand moves through two
+// stages and the weights through three, 32 KB each, 160 KB in all: a step's token-row loads
+// have one step to arrive, its weight loads two.
 //
-// The stages hold run_tile's chunk-permuted rows (row r's 16-byte chunk c at position
-// c ^ (r & 7)), so the fragment reads and MFMAs are run_tile's and so are the results, bit for
-// bit. One load instruction covers 8 rows: lane l fetches chunk (l % 8) ^ (l / 8) of row l / 8,
-// each row one whole 128-byte line.
+// The stages hold the register-staged layouts, so the fragment reads and MFMAs are unchanged
+// and so are the results, bit for bit:
+//  * K-contiguous rows (the token rows; the forward weights) in rowswz's chunk-permuted rows.
+//    One load instruction covers 8 rows: lane l fetches chunk (l % 8) ^ (l / 8) of row l / 8,
+//    each row one whole 128-byte line.
+//  * K-major weights (the dgrads) as 64 K rows of 256 values with kmajor_swz-permuted column
+//    groups, read with the transposing LDS read. One instruction covers 2 K rows: lane l
+//    fetches 8 values of row l / 32, the ones that belong at position l % 32.
 //
 // The five stages are distinct LDS arrays and the K loop is unrolled by six (both stage
 // cycles), so the compiler can tell which stage each load writes and each read reads, and does
 // not wait for every load in flight before an LDS read. A wave's loads complete in issue order;
-// a step issues the activations of step kt + 1 before the weights of step kt + 2, so at the top
+// a step issues the token rows of step kt + 1 before the weights of step kt + 2, so at the top
 // of step kt only the four weight loads issued last may still be in flight. The step waits for
 // the rest, then meets the other waves at a bare barrier: a workgroup fence there would wait
 // for every load, since loads into LDS count as LDS writes. Loads past the last K chunk reload
 // the last chunk into a free stage, so every step issues the same eight loads and the count
 // holds.
-constexpr int kDmaStage = 256 * 64;  // uint16 per stage: 256 rows of 64 K values
+constexpr int kDmaStage = 256 * 64;  // uint16 per stage: 256 rows of 64 K values, or 64 x 256
 __shared__ __align__(1024) uint16_t dma_a0[kDmaStage];
 __shared__ __align__(1024) uint16_t dma_a1[kDmaStage];
 __shared__ __align__(1024) uint16_t dma_b0[kDmaStage];
@@ -1571,123 +1348,316 @@ MOE_DEV uint4 lds_read16(const uint16_t* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// kmajor_frag with each transposing read through a restrict pointer of its own: the inlined
+// intrinsic then carries an alias scope, and the compiler can tell it apart from the loads
+// still writing other stages.
+MOE_DEV s16x4 lds_read_tr16_scoped(const uint16_t* __restrict__ p) {
+  typedef __attribute__((address_space(3))) s16x4* lds_ptr;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p));
+}
+MOE_DEV uint4 kmajor_frag_dma(const uint16_t* s, int base, int kb, int lane) {
+  const int g = lane / 16, q = lane % 16, kr = 8 * g + q / 4;
+  const int n = (base ^ kmajor_swz(kr)) + 4 * (q % 4);
+  const s16x4 a = lds_read_tr16_scoped(s + (kb + kr) * 256 + n);
+  const s16x4 b = lds_read_tr16_scoped(s + (kb + kr + 4) * 256 + n);
+  uint4 v;
+  v.x = (uint32_t)(uint16_t)a[0] | ((uint32_t)(uint16_t)a[1] << 16);
+  v.y = (uint32_t)(uint16_t)a[2] | ((uint32_t)(uint16_t)a[3] << 16);
+  v.z = (uint32_t)(uint16_t)b[0] | ((uint32_t)(uint16_t)b[1] << 16);
+  v.w = (uint32_t)(uint16_t)b[2] | ((uint32_t)(uint16_t)b[3] << 16);
+  return v;
+}
+
 // gfx9 s_waitcnt immediates: vmcnt [3:0], expcnt [6:4], lgkmcnt [11:8]
 constexpr int kWaitVm4Lgkm0 = 0x0074;  // vmcnt(4) lgkmcnt(0)
 constexpr int kWaitVm0Lgkm0 = 0x0070;  // vmcnt(0) lgkmcnt(0)
 
-// A lane's sources for one tile: byte offsets of its four activation rows and four weight rows
-// (one per load instruction) from the tile's bases.
+// A lane's loads for one tile: the two operands' buffer resources, the byte offsets of the
+// pieces its four token-row and four weight load instructions fetch, and the bytes one K chunk
+// advances each operand; K chunks run k0, k0 + 1, .., nk - 1, 0, .., k0 - 1.
 struct DmaSrc {
   __amdgpu_buffer_rsrc_t ra, rb;
   uint32_t ao[4], bo[4];
+  uint32_t astep, bstep;
   int k0, nk;
 };
+
+// Row (of 256) that load j of a lane fetches in a K-contiguous tile, and the byte offset of its
+// 16-byte piece within the 64-value K chunk.
+MOE_DEV int dma_row(int wave, int j, int lane) { return 32 * wave + 8 * j + lane / 8; }
+MOE_DEV uint32_t dma_piece(int lane) { return 16u * ((lane % 8) ^ (lane / 8)); }
+// K row (of 64) that load j of a lane fetches in a K-major tile, and the byte offset of its
+// 8 values within the row's 256.
+MOE_DEV int dma_krow(int wave, int j, int lane) { return 8 * wave + 2 * j + lane / 32; }
+MOE_DEV uint32_t dma_kpiece(int kr, int lane) {
+  return 2u * (((lane % 32) * 8) ^ kmajor_swz(kr));
+}
 
 // Problem 1's full blocks: rows of xp (pitch d) against W1[e]'s gate rows n0.. and up rows
 // I + n0.. (pitch d), in the LDS row order of Problem 1's B tile.
 struct DmaGateUp {
   using P = FwdGateUpBig;
-  static MOE_DEV int ld(const P::Args& a) { return a.d; }
-  static MOE_DEV const uint16_t* abase(const P::Args& a, const P::Tile& t) {
-    return a.xp + (size_t)t.m.row0 * a.d;
+  using Args = P::Args;
+  using Tile = P::Tile;
+  static constexpr const char* kName = "fwd_gateup_big";
+  static constexpr bool kBKmajor = false;
+  static MOE_DEV int ntiles(const Args& a) { return P::ntiles(a); }
+  static MOE_DEV Tile decode(const Args& a, int lt) { return P::decode(a, lt); }
+  static MOE_DEV int brow(int wn, int nb) { return P::brow(wn, nb); }
+  static MOE_DEV void src(const Args& a, const Tile& t, int wave, int lane, DmaSrc& s) {
+    const int d = a.d, I = a.I;
+    s.nk = d / 64;
+    s.k0 = 0;
+    s.ra = raw_rsrc(a.xp + (size_t)t.m.row0 * d);
+    s.rb = raw_rsrc(a.w1 + (size_t)t.m.e * 2 * I * d);
+    s.astep = s.bstep = 128;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = dma_row(wave, j, lane);
+      const int wrow = row < 128 ? t.n0 + row : I + t.n0 + row - 128;
+      // rows past the expert's count (none, on full blocks) would repeat its last row
+      s.ao[j] = 2u * (uint32_t)min(row, t.m.mcount - 1) * d + dma_piece(lane);
+      s.bo[j] = 2u * (uint32_t)wrow * d + dma_piece(lane);
+    }
   }
-  static MOE_DEV const uint16_t* bbase(const P::Args& a, const P::Tile& t) {
-    return a.w1 + (size_t)t.m.e * 2 * a.I * a.d;
-  }
-  static MOE_DEV int brow(const P::Args& a, const P::Tile& t, int n) {
-    return n < 128 ? t.n0 + n : a.I + t.n0 + n - 128;
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[8][4]) {
+    P::epilogue(a, t, acc, nullptr);
   }
 };
 
-// Problem 2's full blocks: rows of A (pitch I) against W2[e]'s rows n0.. (pitch I).
+// Problem 2's full blocks: rows of A (pitch I) against W2[e]'s rows n0.. (pitch I). W2's rows
+// are 2I bytes apart, so each n-tile starts at its own K chunk, as in Problem 2.
 struct DmaDown {
   using P = FwdDownBig;
-  static MOE_DEV int ld(const P::Args& a) { return a.I; }
-  static MOE_DEV const uint16_t* abase(const P::Args& a, const P::Tile& t) {
-    return a.A + (size_t)t.m.row0 * a.I;
+  using Args = P::Args;
+  using Tile = P::Tile;
+  static constexpr const char* kName = "fwd_down_big";
+  static constexpr bool kBKmajor = false;
+  static MOE_DEV int ntiles(const Args& a) { return P::ntiles(a); }
+  static MOE_DEV Tile decode(const Args& a, int lt) { return P::decode(a, lt); }
+  static MOE_DEV int brow(int wn, int nb) { return P::brow(wn, nb); }
+  static MOE_DEV void src(const Args& a, const Tile& t, int wave, int lane, DmaSrc& s) {
+    const int I = a.I;
+    s.nk = I / 64;
+    s.k0 = P::k_first(t, s.nk);
+    s.ra = raw_rsrc(a.A + (size_t)t.m.row0 * I);
+    s.rb = raw_rsrc(a.w2 + ((size_t)t.m.e * a.d + t.n0) * I);
+    s.astep = s.bstep = 128;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = dma_row(wave, j, lane);
+      s.ao[j] = 2u * (uint32_t)min(row, t.m.mcount - 1) * I + dma_piece(lane);
+      s.bo[j] = 2u * (uint32_t)row * I + dma_piece(lane);
+    }
   }
-  static MOE_DEV const uint16_t* bbase(const P::Args& a, const P::Tile& t) {
-    return a.w2 + ((size_t)t.m.e * a.d + t.n0) * a.I;
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[8][4]) {
+    P::epilogue(a, t, acc, nullptr);
   }
-  static MOE_DEV int brow(const P::Args&, const P::Tile&, int n) { return n; }
 };
 
-// K chunk kt of the tile (rotated by k0, clamped to the last) into activation stage S: the
-// wave's 32 rows, 8 per instruction.
+struct DgradTile {
+  MTile m;
+  int n0;
+};
+
+// Problem 4's full blocks: dXp = dH . W1[e]. dH rows (pitch 2I) are K-contiguous; W1[e]
+// ([2I, d], d-contiguous) is K-major, 256 columns from n0.
+struct DmaGateDgrad {
+  using Args = GateDgradBigArgs;
+  using Tile = DgradTile;
+  static constexpr const char* kName = "bwd_gate_dgrad_big";
+  static constexpr bool kBKmajor = true;
+  static MOE_DEV int ntiles(const Args& a) { return a.big[0].x * (a.d / 256); }
+  static MOE_DEV Tile decode(const Args& a, int lt) {
+    const int2 mn = tile_mn<true>(lt, a.big[0].x, a.d / 256);
+    return Tile{decode_mtile(a.big, a.offsets, mn.x, 256), mn.y * 256};
+  }
+  static MOE_DEV int brow(int, int) { return 0; }
+  static MOE_DEV void src(const Args& a, const Tile& t, int wave, int lane, DmaSrc& s) {
+    const int twoI = 2 * a.I, d = a.d;
+    s.nk = twoI / 64;
+    s.k0 = 0;
+    s.ra = raw_rsrc(a.dH + (size_t)t.m.row0 * twoI);
+    s.rb = raw_rsrc(a.w1 + (size_t)t.m.e * twoI * d + t.n0);
+    s.astep = 128;
+    s.bstep = 128u * (uint32_t)d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = dma_row(wave, j, lane), kr = dma_krow(wave, j, lane);
+      s.ao[j] = 2u * (uint32_t)min(row, t.m.mcount - 1) * twoI + dma_piece(lane);
+      s.bo[j] = 2u * (uint32_t)kr * d + dma_kpiece(kr, lane);
+    }
+  }
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[8][4]) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int wm = wave / 4, wn = wave % 4;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const size_t pos = t.m.row0 + wm * 128 + mb * 16 + lane % 16;
+      uint16_t* orow = a.dXp + pos * a.d + t.n0 + wn * 64 + 4 * (lane / 16);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        uint2 o;
+        o.x = pack_bf2(acc[mb][nb][0], acc[mb][nb][1]);
+        o.y = pack_bf2(acc[mb][nb][2], acc[mb][nb][3]);
+        *reinterpret_cast<uint2*>(orow + nb * 16) = o;
+      }
+    }
+  }
+};
+
+// Problem 3's full blocks: dA' = dY[t] . W2[e] with dY rows (pitch d) gathered through row_src
+// and W2[e] ([d, I], I-contiguous) K-major, 256 columns from n0. The epilogue is Problem 3's:
+// per (pos, i) the SwiGLU backward into dH, and the router-weight partials
+// dw = sum_i dA'[pos, i] A[pos, i] of each 128-column half, summed in a fixed order (a lane's
+// columns, then its lane groups, then the two waves of the half).
+struct DmaDownDgrad {
+  using Args = DownDgradBigArgs;
+  using Tile = DgradTile;
+  static constexpr const char* kName = "bwd_down_dgrad_big";
+  static constexpr bool kBKmajor = true;
+  static MOE_DEV int ntiles(const Args& a) { return a.big[0].x * (a.I / 256); }
+  static MOE_DEV Tile decode(const Args& a, int lt) {
+    const int2 mn = tile_mn<true>(lt, a.big[0].x, a.I / 256);
+    return Tile{decode_mtile(a.big, a.offsets, mn.x, 256), mn.y * 256};
+  }
+  static MOE_DEV int brow(int, int) { return 0; }
+  static MOE_DEV void src(const Args& a, const Tile& t, int wave, int lane, DmaSrc& s) {
+    const int d = a.d, I = a.I;
+    s.nk = d / 64;
+    s.k0 = 0;
+    s.ra = raw_rsrc(a.dy);  // byte offsets into dY fit 32 bits: T d < 2^31 is an API limit
+    s.rb = raw_rsrc(a.w2 + (size_t)t.m.e * d * I + t.n0);
+    s.astep = 128;
+    s.bstep = 128u * (uint32_t)I;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = dma_row(wave, j, lane), kr = dma_krow(wave, j, lane);
+      const int tok = a.row_src[t.m.row0 + min(row, t.m.mcount - 1)] / a.k;
+      s.ao[j] = 2u * (uint32_t)tok * d + dma_piece(lane);
+      s.bo[j] = 2u * (uint32_t)kr * I + dma_kpiece(kr, lane);
+    }
+  }
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[8][4]) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int wm = wave / 4, wn = wave % 4;
+    const int I = a.I;
+    float* red = reinterpret_cast<float*>(dma_a0);  // [4][256] row sums per wave column
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const int m = wm * 128 + mb * 16 + lane % 16;
+      const size_t pos = t.m.row0 + m;
+      const float w = a.topk_w[a.row_src[pos]];
+      float part = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int i = t.n0 + wn * 64 + nb * 16 + 4 * (lane / 16);
+        const uint2 av = *reinterpret_cast<const uint2*>(a.A + pos * I + i);
+        const uint2 gv = *reinterpret_cast<const uint2*>(a.H + pos * 2 * I + i);
+        const uint2 uv = *reinterpret_cast<const uint2*>(a.H + pos * 2 * I + I + i);
+        const float av4[4] = {bf2f_lo(av.x), bf2f_hi(av.x), bf2f_lo(av.y), bf2f_hi(av.y)};
+        const float g4[4] = {bf2f_lo(gv.x), bf2f_hi(gv.x), bf2f_lo(gv.y), bf2f_hi(gv.y)};
+        const float u4[4] = {bf2f_lo(uv.x), bf2f_hi(uv.x), bf2f_lo(uv.y), bf2f_hi(uv.y)};
+        float dg[4], du[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float dap = acc[mb][nb][r];
+          part = __builtin_fmaf(dap, av4[r], part);
+          const float dA = w * dap;
+          const float sg = sigmoid(g4[r]);
+          dg[r] = dA * u4[r] * sg * (1.0f + g4[r] * (1.0f - sg));
+          du[r] = dA * (g4[r] * sg);
+        }
+        uint2 o;
+        o.x = pack_bf2(dg[0], dg[1]);
+        o.y = pack_bf2(dg[2], dg[3]);
+        *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + i) = o;
+        o.x = pack_bf2(du[0], du[1]);
+        o.y = pack_bf2(du[2], du[3]);
+        *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + I + i) = o;
+      }
+      // lanes l, l^16, l^32, l^48 share row m: butterfly in a fixed pattern
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      if (lane < 16) red[wn * 256 + m] = part;
+    }
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      const size_t pos = t.m.row0 + threadIdx.x;
+      float* dst = a.dwpart + pos * (I / 128) + t.n0 / 128;
+      dst[0] = red[0 * 256 + threadIdx.x] + red[1 * 256 + threadIdx.x];  // [n0, n0 + 128)
+      dst[1] = red[2 * 256 + threadIdx.x] + red[3 * 256 + threadIdx.x];  // [n0 + 128, n0 + 256)
+    }
+    __syncthreads();  // red is the next tile's first token-row stage
+  }
+};
+
+// K chunk kt of the tile (clamped to the last) into token-row stage S, or weight stage S: the
+// wave's 1 KB quarter of the stage, four load instructions.
 template <int S>
 MOE_DEV void dma_issue_a(const DmaSrc& s, int kt, int wave) {
   int kk = min(kt, s.nk - 1) + s.k0;
   kk = kk >= s.nk ? kk - s.nk : kk;
-  uint16_t* st = dma_stage_a<S>() + wave * 32 * 64;
+  uint16_t* st = dma_stage_a<S>() + wave * 2048;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dma16(s.ra, s.ao[j], (uint32_t)kk * 128u, st + j * 8 * 64);
+  for (int j = 0; j < 4; ++j) dma16(s.ra, s.ao[j], (uint32_t)kk * s.astep, st + j * 512);
 }
 template <int S>
 MOE_DEV void dma_issue_b(const DmaSrc& s, int kt, int wave) {
   int kk = min(kt, s.nk - 1) + s.k0;
   kk = kk >= s.nk ? kk - s.nk : kk;
-  uint16_t* st = dma_stage_b<S>() + wave * 32 * 64;
+  uint16_t* st = dma_stage_b<S>() + wave * 2048;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dma16(s.rb, s.bo[j], (uint32_t)kk * 128u, st + j * 8 * 64);
+  for (int j = 0; j < 4; ++j) dma16(s.rb, s.bo[j], (uint32_t)kk * s.bstep, st + j * 512);
 }
 
-// K step kt on activation stage SA and weight stage SB: wait for them, refill the stages the
-// previous step read (activations of step kt + 1, weights of step kt + 2), then run_tile's
-// 64-deep MFMA step.
+// K step kt on token-row stage SA and weight stage SB: wait for them, refill the stages the
+// previous step read (token rows of step kt + 1, weights of step kt + 2), then the 64-deep MFMA
+// step of a 128 x 64 wave tile.
 template <class D, int SA, int SB>
 MOE_DEV void dma_step(f32x4 (&acc)[8][4], const DmaSrc& s, int kt, int wave, int wm, int wn,
                       int lane) {
-  using P = typename D::P;
   __builtin_amdgcn_s_waitcnt(kWaitVm4Lgkm0);
   __builtin_amdgcn_s_barrier();
   dma_issue_a<SA ^ 1>(s, kt + 1, wave);
   dma_issue_b<(SB + 2) % 3>(s, kt + 2, wave);
   __builtin_amdgcn_sched_barrier(0);
   const uint16_t* sA = dma_stage_a<SA>() + (wm * 128 + lane % 16) * 64;
-  const uint16_t* sB = dma_stage_b<SB>() + (lane % 16) * 64;
+  const uint16_t* sB = dma_stage_b<SB>();
   const int c0 = ((lane / 16) ^ (lane & 7)) << 3, c1 = ((4 + lane / 16) ^ (lane & 7)) << 3;
-  mma_k64<8, 4, 1, 1>(
-      acc,
-      [&](int ks, int mb) {
-        return lds_read16(sA + mb * 16 * 64 + (ks ? c1 : c0));
-      },
-      [&](int ks, int nb) { return lds_read16(sB + P::brow(wn, nb) * 64 + (ks ? c1 : c0)); });
+  auto fa = [&](int ks, int mb) { return lds_read16(sA + mb * 16 * 64 + (ks ? c1 : c0)); };
+  if constexpr (D::kBKmajor) {
+    mma_k64<8, 4, 1, 2>(acc, fa, [&](int ks, int nb) {
+      return kmajor_frag_dma(sB, wn * 64 + nb * 16, ks * 32, lane);
+    });
+  } else {
+    const uint16_t* sBl = sB + (lane % 16) * 64;
+    mma_k64<8, 4, 1, 1>(acc, fa, [&](int ks, int nb) {
+      return lds_read16(sBl + D::brow(wn, nb) * 64 + (ks ? c1 : c0));
+    });
+  }
 }
 
 template <class D>
-__global__ void __launch_bounds__(512, 2) dma_kernel(const typename D::P::Args a) {
-  using P = typename D::P;
-  static_assert(P::G::BM == 256 && P::G::BN == 256 && P::G::BK == 64 && P::G::THREADS == 512,
-                "256 x 256 tiles, K steps of 64, eight waves");
+__global__ void __launch_bounds__(512, 2) dma_kernel(const typename D::Args a) {
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wm = wave / 4, wn = wave % 4;
-  const int ntiles = P::ntiles(a);
+  const int ntiles = D::ntiles(a);
   const int R = (ntiles + kXcds - 1) / kXcds;
   const int step = gridDim.x / kXcds;
   for (int sidx = blockIdx.x / kXcds; sidx < R; sidx += step) {
     const int lt = (blockIdx.x % kXcds) * R + sidx;  // XCD x takes tiles [x R, (x+1) R)
     if (lt >= ntiles) break;
-    const typename P::Tile t = P::decode(a, lt);
+    const typename D::Tile t = D::decode(a, lt);
     f32x4 acc[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     DmaSrc s;
-    s.nk = P::num_k(a, t);
+    D::src(a, t, wave, lane, s);
     if (s.nk > 0) {
-      s.k0 = P::k_first(t, s.nk);
-      s.ra = raw_rsrc(D::abase(a, t));
-      s.rb = raw_rsrc(D::bbase(a, t));
-      const int ld = D::ld(a), r8 = lane / 8, c = (lane % 8) ^ r8;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 32 * wave + 8 * j + r8;
-        // rows past the expert's count (none, on full blocks) would repeat its last row
-        s.ao[j] = 2u * ((uint32_t)min(row, t.m.mcount - 1) * ld + c * 8);
-        s.bo[j] = 2u * ((uint32_t)D::brow(a, t, row) * ld + c * 8);
-      }
       dma_issue_a<0>(s, 0, wave);
       dma_issue_b<0>(s, 0, wave);
       dma_issue_b<1>(s, 1, wave);
@@ -1705,19 +1675,19 @@ __global__ void __launch_bounds__(512, 2) dma_kernel(const typename D::P::Args a
         dma_step<D, 1, 2>(acc, s, kt + 5, wave, wm, wn, lane);
         if (kt + 6 >= s.nk) break;
       }
-      // the trailing reloads have landed and no wave still reads a stage: the next tile's
-      // first loads may go out as soon as its epilogue is done
+      // the trailing reloads have landed and no wave still reads a stage: the epilogue may use
+      // LDS, and the next tile's first loads may go out once it is done
       __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
       __builtin_amdgcn_s_barrier();
     }
-    P::epilogue(a, t, acc, nullptr);
+    D::epilogue(a, t, acc);
   }
 }
 
 // Grid as launch's: one-shot grids cover every tile, persistent grids are the resident
 // workgroup count (one per CU: the stages take all of its LDS); both multiples of 8.
 template <class D>
-static hipError_t launch_dma(const typename D::P::Args& a, int max_tiles, bool persistent,
+static hipError_t launch_dma(const typename D::Args& a, int max_tiles, bool persistent,
                              hipStream_t stream) {
   if (max_tiles <= 0) return hipSuccess;
   int grid = (max_tiles + kXcds - 1) / kXcds * kXcds;
@@ -1736,7 +1706,7 @@ static hipError_t launch_dma(const typename D::P::Args& a, int max_tiles, bool p
     if (resident > 0 && resident < grid) grid = resident;
   }
   {
-    TraceScope trace(D::P::kName, stream);
+    TraceScope trace(D::kName, stream);
     hipLaunchKernelGGL(dma_kernel<D>, dim3(grid), dim3(512), 0, stream, a);
   }
   return hipGetLastError();
@@ -1833,40 +1803,16 @@ hipError_t launch_fwd_down(const GemmFwdDownArgs& x, bool persistent, hipStream_
   return launch<FwdDown>(a, sched_max_rem(x.Tk, x.E) * (x.d / 128), persistent, s);
 }
 
-// Resident workgroup count of a 512-thread big-tile kernel (one per CU), a multiple of 8.
-template <class K>
-static hipError_t big_resident(K kernel, int* resident) {
-  if (*resident == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(kernel), kDgThreads, 0);
-    if (e != hipSuccess) return e;
-    *resident = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
-  }
-  return hipSuccess;
-}
-
-// With I a multiple of 256 the down dgrad runs the 256-row blocks with down_dgrad_big_kernel,
+// With I a multiple of 256 the down dgrad runs the 256-row blocks with dma_kernel<DmaDownDgrad>,
 // then the remainders; otherwise every 128-row block with the 128 x 128 kernel.
 hipError_t launch_bwd_down_dgrad(const GemmBwdDownDgradArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
   const bool big = x.I % kDgT == 0;
   const int max_big = big ? sched_max_big(x.Tk) * (x.I / kDgT) : 0;
   if (max_big > 0) {
-    static int resident = 0;  // every device of one process is an MI355X
-    hipError_t e = big_resident(down_dgrad_big_kernel, &resident);
-    if (e != hipSuccess) return e;
-    const int grid = std::min(resident, (max_big + kXcds - 1) / kXcds * kXcds);
     DownDgradBigArgs ab{x.dy, x.row_src, x.topk_w, x.w2, x.H, x.A, x.dH, x.dwpart,
                         x.offsets, st.big, x.d, x.I, x.k};
-    {
-      TraceScope trace("bwd_down_dgrad_big", s);
-      hipLaunchKernelGGL(down_dgrad_big_kernel, dim3(grid), dim3(kDgThreads), 0, s, ab);
-    }
-    e = hipGetLastError();
+    const hipError_t e = launch_dma<DmaDownDgrad>(ab, max_big, true, s);
     if (e != hipSuccess) return e;
   }
   BwdDownDgrad::Args a{x.dy, x.row_src, x.topk_w, x.w2, x.H, x.A, x.dH, x.dwpart,
@@ -1875,21 +1821,13 @@ hipError_t launch_bwd_down_dgrad(const GemmBwdDownDgradArgs& x, bool persistent,
   return launch<BwdDownDgrad>(a, max_small * (x.I / 128), persistent, s);
 }
 
-// The gate dgrad runs the 256-row blocks with gate_dgrad_big_kernel, then the remainders.
+// The gate dgrad runs the 256-row blocks with dma_kernel<DmaGateDgrad>, then the remainders.
 hipError_t launch_bwd_gate_dgrad(const GemmBwdGateDgradArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
   const int max_big = sched_max_big(x.Tk) * (x.d / kDgT);
   if (max_big > 0) {
-    static int resident = 0;  // every device of one process is an MI355X
-    hipError_t e0 = big_resident(gate_dgrad_big_kernel, &resident);
-    if (e0 != hipSuccess) return e0;
-    const int grid = std::min(resident, (max_big + kXcds - 1) / kXcds * kXcds);
     GateDgradBigArgs ab{x.dH, x.w1, x.dXp, x.offsets, st.big, x.d, x.I};
-    {
-      TraceScope trace("bwd_gate_dgrad_big", s);
-      hipLaunchKernelGGL(gate_dgrad_big_kernel, dim3(grid), dim3(kDgThreads), 0, s, ab);
-    }
-    hipError_t e = hipGetLastError();
+    const hipError_t e = launch_dma<DmaGateDgrad>(ab, max_big, true, s);
     if (e != hipSuccess) return e;
   }
   BwdGateDgrad::Args a{x.dH, x.w1, x.dXp, x.offsets, st.rem, x.d, x.I};

@@ -37,11 +37,10 @@ KERNELS = [
     (r"perm_place_kernel", "perm_place", "permute.hip"),
     (r"wgrad_sched_kernel", "wgrad_sched", "wgrad.hip"),
     (r"sched_build_kernel", "sched_build", "gemm.hip"),
-    (r"gg_kernel<moe::FwdGateUpT<moe::Geo<256", "fwd_gateup_big", "gemm.hip"),
-    (r"gg_kernel<moe::FwdDownT<moe::Geo<256", "fwd_down_big", "gemm.hip"),
-    (r"gg_kernel<moe::BwdGateDgradT<moe::Geo<256", "bwd_gate_dgrad_big", "gemm.hip"),
-    (r"gate_dgrad_big_kernel", "bwd_gate_dgrad_big", "gemm.hip"),
-    (r"down_dgrad_big_kernel", "bwd_down_dgrad_big", "gemm.hip"),
+    (r"dma_kernel<moe::DmaGateUp>", "fwd_gateup_big", "gemm.hip"),
+    (r"dma_kernel<moe::DmaDown>", "fwd_down_big", "gemm.hip"),
+    (r"dma_kernel<moe::DmaGateDgrad>", "bwd_gate_dgrad_big", "gemm.hip"),
+    (r"dma_kernel<moe::DmaDownDgrad>", "bwd_down_dgrad_big", "gemm.hip"),
     (r"gg_kernel<moe::FwdGateUp", "fwd_gateup", "gemm.hip"),
     (r"gg_kernel<moe::FwdDown", "fwd_down", "gemm.hip"),
     (r"gg_kernel<moe::BwdDownDgrad", "bwd_down_dgrad", "gemm.hip"),
