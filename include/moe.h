@@ -61,8 +61,8 @@ enum {
 enum { MOE_DEVICE_BAD_EXPERT_INDEX = 1 /* a topk_idx entry outside [0, E): that row is skipped */ };
 
 /* Layer shape and mode. Constraints checked on the host: T >= 1; 1 <= k <= E <= 1024; k <= 64;
- * d % 256 == 0; I % 128 == 0; T * k < 2^31; T * E < 2^31; T * d < 2^31; precision
- * MOE_PREC_BF16 or MOE_PREC_MXFP8.
+ * d % 256 == 0; I % 128 == 0; T * k < 2^31; T * E < 2^31; T * d < 2^31; T * 2I < 2^31;
+ * precision MOE_PREC_BF16 or MOE_PREC_MXFP8.
  *
  * MXFP8 mode (the pages name BF16 and MXFP8 modes: MarkTechPost, closing paragraph of "Three
  * design decisions that matter") follows the OCP MX v1.0 MXFP8 format. Elements are E4M3; every

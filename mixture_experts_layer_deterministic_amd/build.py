@@ -47,7 +47,7 @@ def _compile(src: str, obj: str) -> dict:
                 name = line.split("Function Name:")[1].split("[")[0].strip()
             elif "ScratchSize [bytes/lane]:" in line and name:
                 scratch[name] = int(line.split("ScratchSize [bytes/lane]:")[1].split("[")[0])
-        elif noise not in line:
+        elif noise not in line and not line.startswith("In file included from"):
             other.append(line)
     err = "\n".join(other)
     if r.returncode != 0:

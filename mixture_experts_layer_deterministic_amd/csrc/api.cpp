@@ -40,6 +40,8 @@ bool cfg_ok(const moe_cfg* c) {
   const long long Tk = (long long)c->T * c->k;
   if (Tk >= (1LL << 31) || (long long)c->T * c->E >= (1LL << 31)) return false;
   if ((long long)c->T * c->d >= (1LL << 31)) return false;  // 32-bit row offsets into X and dY
+  // 32-bit byte offsets into an expert's rows of dH and A (an expert has at most T rows)
+  if ((long long)c->T * 2 * c->I >= (1LL << 31)) return false;
   return true;
 }
 

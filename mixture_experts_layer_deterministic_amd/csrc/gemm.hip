@@ -8,18 +8,20 @@
 //   bwd  down dg : dA'[pos]     = dY[t]    . W2[e]        SwiGLU backward + router-weight grad
 //   bwd  gate dg : dXp[pos]     = dH[pos]  . W1[e]
 // The two weight gradients have their own kernel (wgrad.hip). One kernel template runs the
-// four, in BF16 and (further down) in MXFP8. A workgroup owns a BM x BN output tile: 128 x 128
-// with 4 waves, or 256 x 256 with 8 waves for the forward GEMMs' full 256-row expert blocks.
-// Tiles of BK stream through double-buffered LDS, stored K-contiguous in rows of 64 values whose
-// 16-byte chunks are permuted per row (rowswz), so every MFMA fragment is one 16-byte LDS read
-// and neither those reads nor the row stores conflict on banks. The weights in dgrad, whose K axis is not
-// contiguous in memory, are loaded as 8x8 blocks and transposed in registers on their way in.
+// four, in BF16 and (further down) in MXFP8. A workgroup owns a 128 x 128 output tile with 4
+// waves; the full 256-row expert blocks of all four run on 256 x 256 tiles with 8 waves and
+// direct global -> LDS loads (dma.h). Tiles of BK stream through double-buffered LDS, stored
+// K-contiguous in rows of 64 values whose 16-byte chunks are permuted per row (rowswz), so every
+// MFMA fragment is one 16-byte LDS read and neither those reads nor the row stores conflict on
+// banks. In the 128 x 128 dgrads the weights, whose K axis is not contiguous in memory, are
+// loaded as 8x8 blocks and transposed in registers on their way in.
 //
 // Determinism: every output element is produced by exactly one workgroup, which reduces K in a
 // fixed order. There are no atomics and no split-K.
 #include <algorithm>
 
 #include "common.h"
+#include "dma.h"
 #include "kernels.h"
 
 namespace moe {
@@ -1279,119 +1281,7 @@ static hipError_t launch(const typename P::Args& a, int max_tiles, bool persiste
 }
 
 // ------------------------------------------------------------------------------------------
-// Full 256-row blocks with direct global -> LDS loads: the forward products and the dgrads.
-//
-// In a register-staged K loop a step's loads are issued at the start of the step and written to
-// LDS at its end, so they have one step to arrive, and a second step in flight would need 32
-// more staging registers a lane does not have. Here each load writes LDS itself
-// (buffer_load_dwordx4 with the LDS bit: lane l's 16 bytes land at byte 16 l of a 1 KB block
-// whose base is M0), so no register holds a stage. The token-row operand moves through two
-// stages and the weights through three, 32 KB each, 160 KB in all: a step's token-row loads
-// have one step to arrive, its weight loads two.
-//
-// The stages hold the register-staged layouts, so the fragment reads and MFMAs are unchanged
-// and so are the results, bit for bit:
-//  * K-contiguous rows (the token rows; the forward weights) in rowswz's chunk-permuted rows.
-//    One load instruction covers 8 rows: lane l fetches chunk (l % 8) ^ (l / 8) of row l / 8,
-//    each row one whole 128-byte line.
-//  * K-major weights (the dgrads) as 64 K rows of 256 values with kmajor_swz-permuted column
-//    groups, read with the transposing LDS read. One instruction covers 2 K rows: lane l
-//    fetches 8 values of row l / 32, the ones that belong at position l % 32.
-//
-// The five stages are distinct LDS arrays and the K loop is unrolled by six (both stage
-// cycles), so the compiler can tell which stage each load writes and each read reads, and does
-// not wait for every load in flight before an LDS read. A wave's loads complete in issue order;
-// a step issues the token rows of step kt + 1 before the weights of step kt + 2, so at the top
-// of step kt only the four weight loads issued last may still be in flight. The step waits for
-// the rest, then meets the other waves at a bare barrier: a workgroup fence there would wait
-// for every load, since loads into LDS count as LDS writes. Loads past the last K chunk reload
-// the last chunk into a free stage, so every step issues the same eight loads and the count
-// holds.
-constexpr int kDmaStage = 256 * 64;  // uint16 per stage: 256 rows of 64 K values, or 64 x 256
-__shared__ __align__(1024) uint16_t dma_a0[kDmaStage];
-__shared__ __align__(1024) uint16_t dma_a1[kDmaStage];
-__shared__ __align__(1024) uint16_t dma_b0[kDmaStage];
-__shared__ __align__(1024) uint16_t dma_b1[kDmaStage];
-__shared__ __align__(1024) uint16_t dma_b2[kDmaStage];
-
-template <int S>
-MOE_DEV uint16_t* dma_stage_a() {
-  if constexpr (S == 0) return dma_a0;
-  else return dma_a1;
-}
-template <int S>
-MOE_DEV uint16_t* dma_stage_b() {
-  if constexpr (S == 0) return dma_b0;
-  else if constexpr (S == 1) return dma_b1;
-  else return dma_b2;
-}
-
-// Buffer resource over a whole tensor: raw (stride 0), no range limit, gfx9 data format word.
-MOE_DEV __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
-}
-
-// 16 bytes per lane from rsrc's base + soff + voff bytes to LDS at lds + 16 * lane bytes (rsrc,
-// soff and lds the same in every lane). The 32-bit lane offset lives in one register for the
-// whole tile; the K advance rides in soff.
-MOE_DEV void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint16_t* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds,
-                                           16, voff, soff, 0, 0);
-}
-
-// A 16-byte LDS read as one vector load. Read as a uint4 struct, the load is split into four
-// 32-bit loads and put back together late, and the rebuilt load loses the alias scope that
-// tells the stages apart: the compiler then waits for every load in flight before it.
-MOE_DEV uint4 lds_read16(const uint16_t* p) {
-  typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
-  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// kmajor_frag with each transposing read through a restrict pointer of its own: the inlined
-// intrinsic then carries an alias scope, and the compiler can tell it apart from the loads
-// still writing other stages.
-MOE_DEV s16x4 lds_read_tr16_scoped(const uint16_t* __restrict__ p) {
-  typedef __attribute__((address_space(3))) s16x4* lds_ptr;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p));
-}
-MOE_DEV uint4 kmajor_frag_dma(const uint16_t* s, int base, int kb, int lane) {
-  const int g = lane / 16, q = lane % 16, kr = 8 * g + q / 4;
-  const int n = (base ^ kmajor_swz(kr)) + 4 * (q % 4);
-  const s16x4 a = lds_read_tr16_scoped(s + (kb + kr) * 256 + n);
-  const s16x4 b = lds_read_tr16_scoped(s + (kb + kr + 4) * 256 + n);
-  uint4 v;
-  v.x = (uint32_t)(uint16_t)a[0] | ((uint32_t)(uint16_t)a[1] << 16);
-  v.y = (uint32_t)(uint16_t)a[2] | ((uint32_t)(uint16_t)a[3] << 16);
-  v.z = (uint32_t)(uint16_t)b[0] | ((uint32_t)(uint16_t)b[1] << 16);
-  v.w = (uint32_t)(uint16_t)b[2] | ((uint32_t)(uint16_t)b[3] << 16);
-  return v;
-}
-
-// gfx9 s_waitcnt immediates: vmcnt [3:0], expcnt [6:4], lgkmcnt [11:8]
-constexpr int kWaitVm4Lgkm0 = 0x0074;  // vmcnt(4) lgkmcnt(0)
-constexpr int kWaitVm0Lgkm0 = 0x0070;  // vmcnt(0) lgkmcnt(0)
-
-// A lane's loads for one tile: the two operands' buffer resources, the byte offsets of the
-// pieces its four token-row and four weight load instructions fetch, and the bytes one K chunk
-// advances each operand; K chunks run k0, k0 + 1, .., nk - 1, 0, .., k0 - 1.
-struct DmaSrc {
-  __amdgpu_buffer_rsrc_t ra, rb;
-  uint32_t ao[4], bo[4];
-  uint32_t astep, bstep;
-  int k0, nk;
-};
-
-// Row (of 256) that load j of a lane fetches in a K-contiguous tile, and the byte offset of its
-// 16-byte piece within the 64-value K chunk.
-MOE_DEV int dma_row(int wave, int j, int lane) { return 32 * wave + 8 * j + lane / 8; }
-MOE_DEV uint32_t dma_piece(int lane) { return 16u * ((lane % 8) ^ (lane / 8)); }
-// K row (of 64) that load j of a lane fetches in a K-major tile, and the byte offset of its
-// 8 values within the row's 256.
-MOE_DEV int dma_krow(int wave, int j, int lane) { return 8 * wave + 2 * j + lane / 32; }
-MOE_DEV uint32_t dma_kpiece(int kr, int lane) {
-  return 2u * (((lane % 32) * 8) ^ kmajor_swz(kr));
-}
+// Full 256-row blocks of the four products on dma_kernel (dma.h): one trait per product.
 
 // Problem 1's full blocks: rows of xp (pitch d) against W1[e]'s gate rows n0.. and up rows
 // I + n0.. (pitch d), in the LDS row order of Problem 1's B tile.
@@ -1400,7 +1290,8 @@ struct DmaGateUp {
   using Args = P::Args;
   using Tile = P::Tile;
   static constexpr const char* kName = "fwd_gateup_big";
-  static constexpr bool kBKmajor = false;
+  static constexpr bool kAKmajor = false, kBKmajor = false;
+  static constexpr bool kVoffStep = false, kRoundOrder = false;
   static MOE_DEV int ntiles(const Args& a) { return P::ntiles(a); }
   static MOE_DEV Tile decode(const Args& a, int lt) { return P::decode(a, lt); }
   static MOE_DEV int brow(int wn, int nb) { return P::brow(wn, nb); }
@@ -1432,7 +1323,8 @@ struct DmaDown {
   using Args = P::Args;
   using Tile = P::Tile;
   static constexpr const char* kName = "fwd_down_big";
-  static constexpr bool kBKmajor = false;
+  static constexpr bool kAKmajor = false, kBKmajor = false;
+  static constexpr bool kVoffStep = false, kRoundOrder = false;
   static MOE_DEV int ntiles(const Args& a) { return P::ntiles(a); }
   static MOE_DEV Tile decode(const Args& a, int lt) { return P::decode(a, lt); }
   static MOE_DEV int brow(int wn, int nb) { return P::brow(wn, nb); }
@@ -1466,7 +1358,8 @@ struct DmaGateDgrad {
   using Args = GateDgradBigArgs;
   using Tile = DgradTile;
   static constexpr const char* kName = "bwd_gate_dgrad_big";
-  static constexpr bool kBKmajor = true;
+  static constexpr bool kAKmajor = false, kBKmajor = true;
+  static constexpr bool kVoffStep = false, kRoundOrder = false;
   static MOE_DEV int ntiles(const Args& a) { return a.big[0].x * (a.d / 256); }
   static MOE_DEV Tile decode(const Args& a, int lt) {
     const int2 mn = tile_mn<true>(lt, a.big[0].x, a.d / 256);
@@ -1515,7 +1408,8 @@ struct DmaDownDgrad {
   using Args = DownDgradBigArgs;
   using Tile = DgradTile;
   static constexpr const char* kName = "bwd_down_dgrad_big";
-  static constexpr bool kBKmajor = true;
+  static constexpr bool kAKmajor = false, kBKmajor = true;
+  static constexpr bool kVoffStep = false, kRoundOrder = false;
   static MOE_DEV int ntiles(const Args& a) { return a.big[0].x * (a.I / 256); }
   static MOE_DEV Tile decode(const Args& a, int lt) {
     const int2 mn = tile_mn<true>(lt, a.big[0].x, a.I / 256);
@@ -1592,125 +1486,6 @@ struct DmaDownDgrad {
   }
 };
 
-// K chunk kt of the tile (clamped to the last) into token-row stage S, or weight stage S: the
-// wave's 1 KB quarter of the stage, four load instructions.
-template <int S>
-MOE_DEV void dma_issue_a(const DmaSrc& s, int kt, int wave) {
-  int kk = min(kt, s.nk - 1) + s.k0;
-  kk = kk >= s.nk ? kk - s.nk : kk;
-  uint16_t* st = dma_stage_a<S>() + wave * 2048;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) dma16(s.ra, s.ao[j], (uint32_t)kk * s.astep, st + j * 512);
-}
-template <int S>
-MOE_DEV void dma_issue_b(const DmaSrc& s, int kt, int wave) {
-  int kk = min(kt, s.nk - 1) + s.k0;
-  kk = kk >= s.nk ? kk - s.nk : kk;
-  uint16_t* st = dma_stage_b<S>() + wave * 2048;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) dma16(s.rb, s.bo[j], (uint32_t)kk * s.bstep, st + j * 512);
-}
-
-// K step kt on token-row stage SA and weight stage SB: wait for them, refill the stages the
-// previous step read (token rows of step kt + 1, weights of step kt + 2), then the 64-deep MFMA
-// step of a 128 x 64 wave tile.
-template <class D, int SA, int SB>
-MOE_DEV void dma_step(f32x4 (&acc)[8][4], const DmaSrc& s, int kt, int wave, int wm, int wn,
-                      int lane) {
-  __builtin_amdgcn_s_waitcnt(kWaitVm4Lgkm0);
-  __builtin_amdgcn_s_barrier();
-  dma_issue_a<SA ^ 1>(s, kt + 1, wave);
-  dma_issue_b<(SB + 2) % 3>(s, kt + 2, wave);
-  __builtin_amdgcn_sched_barrier(0);
-  const uint16_t* sA = dma_stage_a<SA>() + (wm * 128 + lane % 16) * 64;
-  const uint16_t* sB = dma_stage_b<SB>();
-  const int c0 = ((lane / 16) ^ (lane & 7)) << 3, c1 = ((4 + lane / 16) ^ (lane & 7)) << 3;
-  auto fa = [&](int ks, int mb) { return lds_read16(sA + mb * 16 * 64 + (ks ? c1 : c0)); };
-  if constexpr (D::kBKmajor) {
-    mma_k64<8, 4, 1, 2>(acc, fa, [&](int ks, int nb) {
-      return kmajor_frag_dma(sB, wn * 64 + nb * 16, ks * 32, lane);
-    });
-  } else {
-    const uint16_t* sBl = sB + (lane % 16) * 64;
-    mma_k64<8, 4, 1, 1>(acc, fa, [&](int ks, int nb) {
-      return lds_read16(sBl + D::brow(wn, nb) * 64 + (ks ? c1 : c0));
-    });
-  }
-}
-
-template <class D>
-__global__ void __launch_bounds__(512, 2) dma_kernel(const typename D::Args a) {
-  const int lane = threadIdx.x % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int wm = wave / 4, wn = wave % 4;
-  const int ntiles = D::ntiles(a);
-  const int R = (ntiles + kXcds - 1) / kXcds;
-  const int step = gridDim.x / kXcds;
-  for (int sidx = blockIdx.x / kXcds; sidx < R; sidx += step) {
-    const int lt = (blockIdx.x % kXcds) * R + sidx;  // XCD x takes tiles [x R, (x+1) R)
-    if (lt >= ntiles) break;
-    const typename D::Tile t = D::decode(a, lt);
-    f32x4 acc[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    DmaSrc s;
-    D::src(a, t, wave, lane, s);
-    if (s.nk > 0) {
-      dma_issue_a<0>(s, 0, wave);
-      dma_issue_b<0>(s, 0, wave);
-      dma_issue_b<1>(s, 1, wave);
-      for (int kt = 0;; kt += 6) {
-        dma_step<D, 0, 0>(acc, s, kt, wave, wm, wn, lane);
-        if (kt + 1 >= s.nk) break;
-        dma_step<D, 1, 1>(acc, s, kt + 1, wave, wm, wn, lane);
-        if (kt + 2 >= s.nk) break;
-        dma_step<D, 0, 2>(acc, s, kt + 2, wave, wm, wn, lane);
-        if (kt + 3 >= s.nk) break;
-        dma_step<D, 1, 0>(acc, s, kt + 3, wave, wm, wn, lane);
-        if (kt + 4 >= s.nk) break;
-        dma_step<D, 0, 1>(acc, s, kt + 4, wave, wm, wn, lane);
-        if (kt + 5 >= s.nk) break;
-        dma_step<D, 1, 2>(acc, s, kt + 5, wave, wm, wn, lane);
-        if (kt + 6 >= s.nk) break;
-      }
-      // the trailing reloads have landed and no wave still reads a stage: the epilogue may use
-      // LDS, and the next tile's first loads may go out once it is done
-      __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
-      __builtin_amdgcn_s_barrier();
-    }
-    D::epilogue(a, t, acc);
-  }
-}
-
-// Grid as launch's: one-shot grids cover every tile, persistent grids are the resident
-// workgroup count (one per CU: the stages take all of its LDS); both multiples of 8.
-template <class D>
-static hipError_t launch_dma(const typename D::Args& a, int max_tiles, bool persistent,
-                             hipStream_t stream) {
-  if (max_tiles <= 0) return hipSuccess;
-  int grid = (max_tiles + kXcds - 1) / kXcds * kXcds;
-  if (persistent) {
-    static int resident = 0;  // per kernel; every device of one process is an MI355X
-    if (resident == 0) {
-      int dev = 0, cus = 0, per_cu = 0;
-      hipError_t e = hipGetDevice(&dev);
-      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-      if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&dma_kernel<D>), 512, 0);
-      if (e != hipSuccess) return e;
-      resident = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
-    }
-    if (resident > 0 && resident < grid) grid = resident;
-  }
-  {
-    TraceScope trace(D::kName, stream);
-    hipLaunchKernelGGL(dma_kernel<D>, dim3(grid), dim3(512), 0, stream, a);
-  }
-  return hipGetLastError();
-}
 
 // ------------------------------------------------------------------------------------------
 // Schedule tables, built on the device from the offsets so the host never learns the counts.

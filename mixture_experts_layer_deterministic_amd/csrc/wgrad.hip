@@ -25,11 +25,12 @@
 //
 // Experts with many rows (at least kWgradBigRows) make the product MFMA-bound rather than
 // write-bound. They go to a second kernel with 256 x 256 output tiles and 64-position K steps,
-// twice the flops per loaded byte of the 256 x 128 tiles (see wgrad_big_kernel).
+// twice the flops per loaded byte of the 256 x 128 tiles (see DmaWgrad).
 //
 // Determinism: every dW element belongs to exactly one task, whose workgroup reduces K in
 // ascending position order. No atomics, no split-K.
 #include "common.h"
+#include "dma.h"
 #include "kernels.h"
 
 namespace moe {
@@ -37,7 +38,7 @@ namespace moe {
 namespace {
 
 constexpr int BM = kWgradBM, BN = kWgradBN, BK = 32;
-constexpr int kWgradBigRows = 512;  // experts with at least this many rows: wgrad_big_kernel
+constexpr int kWgradBigRows = 512;  // experts with at least this many rows: DmaWgrad
 constexpr int kEmptyRun = 4;        // tiles per task of an expert with no rows (zero fill)
 constexpr int KRES = 128;           // positions of L kept resident in LDS for a whole task
 constexpr int LDL = KRES + 8;       // row pitch of the L buffer [BM][LDL]
@@ -389,42 +390,25 @@ __global__ void __launch_bounds__(1024) wgrad_sched_kernel(const int32_t* __rest
 // Experts with many rows. With thousands of positions per expert the product is MFMA-bound,
 // and the kernel's rate follows the flops per byte its tiles load into LDS: 256 x 256 output
 // tiles with 64-position K steps carry 128 flop/B, against 85 for the 256 x 128 stripes with
-// 32-position steps above. Eight waves of 128 x 64 outputs (128 accumulators each), one
-// workgroup per CU, two LDS stages.
+// 32-position steps above. They run on dma_kernel (dma.h): eight waves of 128 x 64 outputs, one
+// workgroup per CU, operands loaded straight into LDS (L through two stages, R through three).
 //
-// Both operands are position-major, so a K step of either is 64 rows of 256 contiguous values.
-// They are copied into LDS as they are, [64][256] per operand in 16-byte vectors, with the
-// 32-byte column groups of row k permuted by XOR with kmajor_swz(k). The MFMA fragments (8
-// consecutive positions of one row or column per lane) are then read with gfx950's
-// transposing LDS read (kmajor_frag), so neither operand is transposed in registers.
-constexpr int kBigT = 256;                    // dW tile edge
-constexpr int kBigK = 64;                     // positions per K step
-constexpr int kBigThreads = 512;              // 8 waves: 2 along M x 4 along N
-constexpr int kBigWM = 128, kBigWN = 64;      // outputs per wave
-constexpr int kBigStage = 2 * kBigK * kBigT;  // uint16 elements per stage: L rows, then R rows
-
-// One K step of one operand: positions [p, p + 64) x 256 columns from `base` (row pitch ld),
-// rows at or past p1 as zeros. Four 16-byte vectors per thread; a wave instruction covers two
-// whole 512-byte rows.
-struct BigLoader {
-  const uint16_t* base;
-  int ld;
-  uint4 r[4];
-  MOE_DEV void load(int p, int p1) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int v = threadIdx.x + kBigThreads * j, row = v / 32, col = (v % 32) * 8;
-      r[j] = p + row < p1 ? *reinterpret_cast<const uint4*>(base + (size_t)(p + row) * ld + col)
-                          : make_uint4(0, 0, 0, 0);
-    }
-  }
-  MOE_DEV void store(uint16_t* s) const {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int v = threadIdx.x + kBigThreads * j, row = v / 32, col = (v % 32) * 8;
-      *reinterpret_cast<uint4*>(s + row * kBigT + (col ^ kmajor_swz(row))) = r[j];
-    }
-  }
+// Both operands are position-major, so a K step of either is 64 rows of 256 contiguous values,
+// and both sit in LDS as they are in memory, with the 32-byte column groups of row k permuted
+// by XOR with kmajor_swz(k); the MFMA fragments (8 consecutive positions of one row or column
+// per lane) come from gfx950's transposing LDS read, so neither operand is transposed in
+// registers. Each operand's buffer range ends at the expert's last position, so the rows of
+// the last K step past it load as zeros.
+struct WgBigArgs {
+  const uint16_t* L;       // [T*k, Mdim]
+  const uint16_t* R;       // [T*k, Ndim]
+  float* dw;               // [E, Mdim, Ndim]
+  const int4* big;         // count, then the listed experts (x = expert)
+  const int32_t* offsets;
+  int Mdim, Ndim;
+};
+struct WgBigTile {
+  int e, m0, n0, p0, p1;
 };
 
 // Tiles of the listed experts, expert by expert in list order (decreasing rows); inside an
@@ -432,76 +416,54 @@ struct BigLoader {
 // the tiles [r G + x G/8, r G + (x+1) G/8): neighbouring tiles share operand panels in its L2.
 // GATE only separates the two instances (dW1 and dW2) for profilers.
 template <bool ACC, bool GATE>
-__global__ void __launch_bounds__(kBigThreads, 1) wgrad_big_kernel(const Args a,
-                                                                   const int4* __restrict__ big,
-                                                                   const int32_t* __restrict__ offsets) {
-  __shared__ __align__(16) uint16_t sm[2 * kBigStage];
-  const int ntm = a.Mdim / kBigT, ntn = a.Ndim / kBigT, tpe = ntm * ntn;
-  const int ntiles = big[0].x * tpe;
-  const int lane = threadIdx.x % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int wm = wave / (kBigT / kBigWN), wn = wave % (kBigT / kBigWN);
-  const int G = gridDim.x, G8 = G / kXcds, xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  for (int round = 0;; ++round) {
-    const int ti = round * G + xcd * G8 + slot;
-    if (ti >= ntiles) break;
-    const int e = big[1 + ti / tpe].x;
+struct DmaWgrad {
+  using Args = WgBigArgs;
+  using Tile = WgBigTile;
+  static constexpr const char* kName = GATE ? "bwd_gate_wgrad_big" : "bwd_down_wgrad_big";
+  static constexpr bool kAKmajor = true, kBKmajor = true;
+  static constexpr bool kVoffStep = true, kRoundOrder = true;
+  static MOE_DEV int ntiles(const Args& a) { return a.big[0].x * (a.Mdim / 256) * (a.Ndim / 256); }
+  static MOE_DEV Tile decode(const Args& a, int ti) {
+    const int ntm = a.Mdim / 256, ntn = a.Ndim / 256, tpe = ntm * ntn;
+    Tile t;
+    t.e = a.big[1 + ti / tpe].x;
     const int lt = ti % tpe;
     const int group = lt / (4 * ntn), mfirst = group * 4, gm = min(4, ntm - mfirst);
     const int rr = lt - mfirst * ntn;
-    const int m0 = (mfirst + rr % gm) * kBigT, n0 = (rr / gm) * kBigT;
-    const int p0 = offsets[e], p1 = offsets[e + 1];
-    const int nk = (p1 - p0 + kBigK - 1) / kBigK;
-    BigLoader la, lb;
-    la.base = a.L + m0;
-    la.ld = a.Mdim;
-    lb.base = a.R + n0;
-    lb.ld = a.Ndim;
-    f32x4 acc[kBigWM / 16][kBigWN / 16];
+    t.m0 = (mfirst + rr % gm) * 256;
+    t.n0 = (rr / gm) * 256;
+    t.p0 = a.offsets[t.e];
+    t.p1 = a.offsets[t.e + 1];
+    return t;
+  }
+  static MOE_DEV int brow(int, int) { return 0; }
+  // byte offsets fit 32 bits: an expert has at most T positions, and T d, T 2I < 2^31 are API
+  // limits
+  static MOE_DEV void src(const Args& a, const Tile& t, int wave, int lane, DmaSrc& s) {
+    const int rows = t.p1 - t.p0;
+    s.nk = (rows + 63) / 64;
+    s.k0 = 0;
+    s.ra = raw_rsrc(a.L + (size_t)t.p0 * a.Mdim + t.m0, 2u * (uint32_t)rows * (uint32_t)a.Mdim);
+    s.rb = raw_rsrc(a.R + (size_t)t.p0 * a.Ndim + t.n0, 2u * (uint32_t)rows * (uint32_t)a.Ndim);
+    s.astep = 128u * (uint32_t)a.Mdim;
+    s.bstep = 128u * (uint32_t)a.Ndim;
 #pragma unroll
-    for (int i = 0; i < kBigWM / 16; ++i)
-#pragma unroll
-      for (int j = 0; j < kBigWN / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    la.load(p0, p1);
-    lb.load(p0, p1);
-    la.store(sm);
-    lb.store(sm + kBigK * kBigT);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint16_t* sl = sm + (kt & 1) * kBigStage;
-      const uint16_t* sr = sl + kBigK * kBigT;
-      if (kt + 1 < nk) {
-        la.load(p0 + (kt + 1) * kBigK, p1);
-        lb.load(p0 + (kt + 1) * kBigK, p1);
-      }
-#pragma unroll
-      for (int ks = 0; ks < kBigK / 32; ++ks) {
-        uint4 bf[kBigWN / 16], af[kBigWM / 16];
-#pragma unroll
-        for (int nb = 0; nb < kBigWN / 16; ++nb)
-          bf[nb] = kmajor_frag<kBigT>(sr, wn * kBigWN + nb * 16, ks * 32, lane);
-#pragma unroll
-        for (int mb = 0; mb < kBigWM / 16; ++mb)
-          af[mb] = kmajor_frag<kBigT>(sl, wm * kBigWM + mb * 16, ks * 32, lane);
-#pragma unroll
-        for (int mb = 0; mb < kBigWM / 16; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < kBigWN / 16; ++nb) acc[mb][nb] = mfma16(bf[nb], af[mb], acc[mb][nb]);
-      }
-      if (kt + 1 < nk) {
-        uint16_t* nx = sm + ((kt + 1) & 1) * kBigStage;
-        la.store(nx);
-        lb.store(nx + kBigK * kBigT);
-      }
-      __syncthreads();
+    for (int j = 0; j < 4; ++j) {
+      const int kr = dma_krow(wave, j, lane);
+      s.ao[j] = 2u * (uint32_t)kr * (uint32_t)a.Mdim + dma_kpiece(kr, lane);
+      s.bo[j] = 2u * (uint32_t)kr * (uint32_t)a.Ndim + dma_kpiece(kr, lane);
     }
-    float* out = a.dw + ((size_t)e * a.Mdim + m0) * a.Ndim + n0;
+  }
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[8][4]) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int wm = wave / 4, wn = wave % 4;
+    float* out = a.dw + ((size_t)t.e * a.Mdim + t.m0) * a.Ndim + t.n0;
 #pragma unroll
-    for (int mb = 0; mb < kBigWM / 16; ++mb) {
-      const int m = wm * kBigWM + mb * 16 + lane % 16;
+    for (int mb = 0; mb < 8; ++mb) {
+      const int m = wm * 128 + mb * 16 + lane % 16;
 #pragma unroll
-      for (int nb = 0; nb < kBigWN / 16; ++nb) {
-        const int n = wn * kBigWN + nb * 16 + 4 * (lane / 16);
+      for (int nb = 0; nb < 4; ++nb) {
+        const int n = wn * 64 + nb * 16 + 4 * (lane / 16);
         float4* dst = reinterpret_cast<float4*>(out + (size_t)m * a.Ndim + n);
         float4 v = make_float4(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]);
         if (ACC) {
@@ -515,7 +477,7 @@ __global__ void __launch_bounds__(kBigThreads, 1) wgrad_big_kernel(const Args a,
       }
     }
   }
-}
+};
 
 int resident_grid() {
   static int grid = 0;  // every device of one process is an MI355X
@@ -526,21 +488,6 @@ int resident_grid() {
       return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &per_cu, reinterpret_cast<const void*>(&wgrad_kernel<false, false, false>), kThreads, 0) != hipSuccess)
-      return 0;
-    grid = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
-  }
-  return grid;
-}
-
-int resident_grid_big() {
-  static int grid = 0;
-  if (grid == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&wgrad_big_kernel<false, false>), kBigThreads, 0) != hipSuccess)
       return 0;
     grid = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
   }
@@ -560,7 +507,7 @@ size_t wgrad_table_entries(int Tk, int E, int Mdim, int Ndim) {
 
 hipError_t launch_wgrad(const WgradArgs& x, hipStream_t s) {
   // the big-expert kernel takes bf16 operands whose dW dimensions are multiples of its tile
-  const bool big_ok = !x.R8 && x.Mdim % kBigT == 0 && x.Ndim % kBigT == 0;
+  const bool big_ok = !x.R8 && x.Mdim % 256 == 0 && x.Ndim % 256 == 0;
   const int big_rows = big_ok ? kWgradBigRows : 0x7fffffff;
   int4* big = x.table;
   int4* table = x.table + 1 + x.E;
@@ -584,15 +531,14 @@ hipError_t launch_wgrad(const WgradArgs& x, hipStream_t s) {
   }
   err = hipGetLastError();
   if (err != hipSuccess || !big_ok) return err;
-  const int gbig = resident_grid_big();
-  if (gbig <= 0) return hipErrorInvalidValue;
-  {
-    TraceScope trace(x.gate ? "bwd_gate_wgrad_big" : "bwd_down_wgrad_big", s);
-    auto kern = x.accumulate ? (x.gate ? wgrad_big_kernel<true, true> : wgrad_big_kernel<true, false>)
-                             : (x.gate ? wgrad_big_kernel<false, true> : wgrad_big_kernel<false, false>);
-    hipLaunchKernelGGL(kern, dim3(gbig), dim3(kBigThreads), 0, s, a, big, x.offsets);
-  }
-  return hipGetLastError();
+  // the big experts' tile count is known on the device only: a resident grid walks it
+  const WgBigArgs ab{x.L, x.R, x.dw, big, x.offsets, x.Mdim, x.Ndim};
+  constexpr int kAnyTiles = 1 << 30;
+  if (x.accumulate)
+    return x.gate ? launch_dma<DmaWgrad<true, true>>(ab, kAnyTiles, true, s)
+                  : launch_dma<DmaWgrad<true, false>>(ab, kAnyTiles, true, s);
+  return x.gate ? launch_dma<DmaWgrad<false, true>>(ab, kAnyTiles, true, s)
+                : launch_dma<DmaWgrad<false, false>>(ab, kAnyTiles, true, s);
 }
 
 }  // namespace moe

@@ -49,8 +49,8 @@ KERNELS = [
     (r"gg_kernel<moe::MxFwdDown", "fwd_down", "gemm.hip"),
     (r"gg_kernel<moe::MxBwdDownDgrad", "bwd_down_dgrad", "gemm.hip"),
     (r"gg_kernel<moe::MxBwdGateDgrad", "bwd_gate_dgrad", "gemm.hip"),
-    (r"wgrad_big_kernel<(true|false), false", "bwd_down_wgrad_big", "wgrad.hip"),
-    (r"wgrad_big_kernel<(true|false), true", "bwd_gate_wgrad_big", "wgrad.hip"),
+    (r"DmaWgrad<(true|false), false>", "bwd_down_wgrad_big", "wgrad.hip"),
+    (r"DmaWgrad<(true|false), true>", "bwd_gate_wgrad_big", "wgrad.hip"),
     (r"wgrad_kernel<(true|false), false", "bwd_down_wgrad", "wgrad.hip"),
     (r"wgrad_kernel<(true|false), true", "bwd_gate_wgrad", "wgrad.hip"),
     (r"moe::combine_kernel", "combine", "elementwise.hip"),

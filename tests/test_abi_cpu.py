@@ -42,6 +42,7 @@ def test_query_sizes_follow_the_shapes():
     (16, 256, 2000, 2, 128),  # E > 1024
     (16, 256, 128, 65, 128),  # k > 64
     (300000, 7168, 8, 1, 128),  # T * d >= 2^31 (32-bit row offsets)
+    (600000, 256, 8, 1, 2048),  # T * 2I >= 2^31 (32-bit byte offsets into an expert's dH)
 ])
 def test_query_rejects_bad_shapes(shape):
     with pytest.raises(m.MoeError) as ei:
