@@ -61,7 +61,7 @@ KERNELS = [
     (r"quant_rows_kernel", "quant_rows", "mx.hip"),
     (r"quant_weight_kernel", "quant_weight", "mx.hip"),
 ]
-COMMON_SOURCES = ("common.h", "kernels.h")
+COMMON_SOURCES = ("common.h", "dma.h", "kernels.h")
 
 
 def bench_name(raw: str):
