@@ -30,8 +30,9 @@
 //   Args, Tile; kName; ntiles(a); decode(a, lt) -> Tile;
 //   kAKmajor, kBKmajor: operand layouts (K-contiguous rows, or K-major);
 //   brow(wn, nb): LDS row of B's column block nb for wave column wn (K-contiguous B);
-//   kVoffStep: the K advance rides in the lane offset, where a buffer range limit zeroes the
-//     rows past the operand's end (the limit covers the lane offset, not the scalar one);
+//   kVoffStep: the K advance rides in the lane offset and the scalar offset stays zero, so a
+//     buffer range limit (checked against the lane offset) zeroes the rows past the operand's
+//     end;
 //   kRoundOrder: tiles dealt round by round (tile r G + x G/8 + s to workgroup s of XCD x)
 //     instead of one contiguous range per XCD;
 //   src(a, t, wave, lane, DmaSrc&): the lane's sources; epilogue(a, t, acc).
