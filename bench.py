@@ -271,6 +271,17 @@ def main():
                       "rows_per_s": round(cz["T"] * cz["k"] / (r["ms"] * 1e-3), 1),
                       "grouped_gemm": r["gemm"],
                       "gemm_us": {g: r["kernels"][g]["us"] for g in GEMMS if g in r["kernels"]}}
+        if not args.no_mxfp8:
+            # MXFP8 on the same slice: its GEMMs against the fp8 MFMA peak where they are
+            # MFMA-bound rather than weight-streaming
+            print("[bench] local expert slice in MXFP8 mode", file=sys.stderr, flush=True)
+            rz = run_layer(m, MoeLayer, iz, cz, stream, args, mx=True)
+            slice_line["mxfp8"] = {
+                "ms_per_step": round(rz["ms"], 4),
+                "weight_quantize_ms": round(rz["quant_ms"], 4),
+                "layer_ms_without_weight_quantize": round(rz["ms"] - rz["quant_ms"], 4),
+                "grouped_gemm": rz["gemm"],
+                "gemm_us": {g: rz["kernels"][g]["us"] for g in GEMMS if g in rz["kernels"]}}
         del iz
         torch.cuda.empty_cache()
 
