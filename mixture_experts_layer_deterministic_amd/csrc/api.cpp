@@ -396,15 +396,17 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
                       wg_count + 1, E, d, I, accumulate, false, "bwd_down_wgrad",
                       "wgrad_sched_down"},
                      s));
+    // the gate wgrad goes first: until the gate dgrad writes dXp, that buffer holds the bf16
+    // image of the big experts' fp8 Xp rows for the big-expert wgrad kernel
+    if (!L.err)
+      L(launch_wgrad({dH, nullptr, xp8, xps, dw1, offsets, at<int4>(workspace, Y.wg_table1),
+                      wg_count, E, 2 * I, d, accumulate, true, "bwd_gate_wgrad",
+                      "wgrad_sched_gate", dXp},
+                     s));
     if (!L.err)
       L(launch_bwd_gate_dgrad_mx({dhq, dhs, at<uint8_t>(wq, Y.w1b), at<uint8_t>(wq, Y.w1bs), dXp,
                                   offsets, sched, d, I, Tk, E},
                                  pers, s));
-    if (!L.err)
-      L(launch_wgrad({dH, nullptr, xp8, xps, dw1, offsets, at<int4>(workspace, Y.wg_table1),
-                      wg_count, E, 2 * I, d, accumulate, true, "bwd_gate_wgrad",
-                      "wgrad_sched_gate"},
-                     s));
   } else {
     if (!L.err) L(launch_scale_gather(dyp, tk_row, topk_w, cfg->T, k, d, dyw, s));
     if (!L.err)

@@ -166,6 +166,9 @@ struct WgradArgs {
   bool gate;  // dW1 (true) or dW2 (false)
   const char* name;
   const char* name_sched;
+  // with an fp8 R: bf16 scratch [T*k, Ndim] for the exact bf16 image of the big experts' R rows
+  // (they then run on the big-expert kernel), or null (every expert on the task kernel)
+  uint16_t* Rx = nullptr;
 };
 size_t wgrad_table_entries(int Tk, int E, int Mdim, int Ndim);
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);

@@ -479,6 +479,32 @@ struct DmaWgrad {
   }
 };
 
+// The exact bf16 image (codes times their scale, as Mover::expand_fp8 makes it) of the rows
+// of the listed big experts of an MXFP8 operand, at the same row positions. One thread per
+// 8-column piece, grid-stride over each expert's rows in turn.
+__global__ void __launch_bounds__(256) expand_big_rows_kernel(const uint8_t* __restrict__ r8,
+                                                              const uint8_t* __restrict__ r8s,
+                                                              uint16_t* __restrict__ out,
+                                                              const int4* __restrict__ big,
+                                                              const int32_t* __restrict__ offsets,
+                                                              int Ndim) {
+  const int per_row = Ndim / 8;
+  const int nbig = big[0].x;
+  for (int i = 0; i < nbig; ++i) {
+    const int e = big[1 + i].x;
+    const int p0 = offsets[e];
+    const long long n = (long long)(offsets[e + 1] - p0) * per_row;
+    for (long long c = (long long)blockIdx.x * blockDim.x + threadIdx.x; c < n;
+         c += (long long)gridDim.x * blockDim.x) {
+      const size_t p = (size_t)p0 + (size_t)(c / per_row);
+      const int col = (int)(c % per_row) * 8;
+      const uint2 q = *reinterpret_cast<const uint2*>(r8 + p * Ndim + col);
+      const uint4 raw = make_uint4(q.x, q.y, r8s[p * (Ndim / 32) + col / 32], 0);
+      *reinterpret_cast<uint4*>(out + p * Ndim + col) = Mover<1>::expand_fp8(raw);
+    }
+  }
+}
+
 int resident_grid() {
   static int grid = 0;  // every device of one process is an MI355X
   if (grid == 0) {
@@ -506,8 +532,9 @@ size_t wgrad_table_entries(int Tk, int E, int Mdim, int Ndim) {
 }
 
 hipError_t launch_wgrad(const WgradArgs& x, hipStream_t s) {
-  // the big-expert kernel takes bf16 operands whose dW dimensions are multiples of its tile
-  const bool big_ok = !x.R8 && x.Mdim % 256 == 0 && x.Ndim % 256 == 0;
+  // the big-expert kernel takes bf16 operands whose dW dimensions are multiples of its tile; an
+  // fp8 R needs the scratch for its bf16 image
+  const bool big_ok = (!x.R8 || x.Rx) && x.Mdim % 256 == 0 && x.Ndim % 256 == 0;
   const int big_rows = big_ok ? kWgradBigRows : 0x7fffffff;
   int4* big = x.table;
   int4* table = x.table + 1 + x.E;
@@ -531,8 +558,15 @@ hipError_t launch_wgrad(const WgradArgs& x, hipStream_t s) {
   }
   err = hipGetLastError();
   if (err != hipSuccess || !big_ok) return err;
+  if (x.R8) {
+    TraceScope trace("wgrad_expand", s);
+    hipLaunchKernelGGL(expand_big_rows_kernel, dim3(1024), dim3(256), 0, s, x.R8, x.R8s, x.Rx,
+                       big, x.offsets, x.Ndim);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   // the big experts' tile count is known on the device only: a resident grid walks it
-  const WgBigArgs ab{x.L, x.R, x.dw, big, x.offsets, x.Mdim, x.Ndim};
+  const WgBigArgs ab{x.L, x.R8 ? x.Rx : x.R, x.dw, big, x.offsets, x.Mdim, x.Ndim};
   constexpr int kAnyTiles = 1 << 30;
   if (x.accumulate)
     return x.gate ? launch_dma<DmaWgrad<true, true>>(ab, kAnyTiles, true, s)
