@@ -47,5 +47,10 @@ from .moe import (  # noqa: F401
     permute,
     forward,
     backward,
+    layer,
+    expert_forward,
+    expert_backward,
+    gather_sum,
+    router_backward,
     readings,
 )

@@ -149,6 +149,101 @@ def _sigmoid(z):
     return 1.0 / (1.0 + np.exp(-z))
 
 
+def _identity(a, axis=-1):
+    return a
+
+
+def _rounder(storage):
+    return bf16_round if storage == "bf16" else (lambda a: a)
+
+
+def expert_forward(x, w1, w2, *, rnd, mxq=_identity):
+    """One expert's forward over its rows x [c, d] (readings "expert", "storage_bf16", "mxfp8").
+
+    [g | u] = x W1_e^T, a = silu(g) * u, o = a W2_e^T. With bf16 storage H = [g | u] is stored
+    rounded, A is rounded once from the unrounded g and u, and the down projection reads the
+    stored A. ``mxq`` is the MXFP8 image taken of both operands of each GEMM (identity in BF16
+    mode). Returns (H [c, 2I], A [c, I], O_exact [c, d]); the caller rounds O where it is stored.
+    """
+    I = w1.shape[0] // 2
+    x = mxq(x)
+    w1 = mxq(np.asarray(w1, np.float64))
+    g = x @ w1[:I].T
+    u = x @ w1[I:].T
+    h = np.concatenate([rnd(g), rnd(u)], axis=1)
+    a = rnd(_silu(g) * u)
+    o = mxq(a) @ mxq(np.asarray(w2, np.float64)).T
+    return h, a, o
+
+
+def expert_backward(x, dy, wv, h, a, o_used, w1, w2, *, rnd, mxmode=False):
+    """One expert's backward over its rows (readings "router_grad", "storage_bf16", "mxfp8").
+
+    x and dy are the rows' tokens and upstream gradients, wv [c, 1] their routing weights, h and
+    a the stored forward H and A, o_used the stored O. Per row:
+    * dw = <dy, o>, the router-weight gradient; in MXFP8 mode the fused <dA', a> with dA' from
+      the quantised dgrad GEMM;
+    * dA = w * (dy W2_e); dg = dA * u * s * (1 + g (1 - s)) with s = sigmoid(g), du = dA * silu(g),
+      from the stored g and u; dH = [dg | du] is stored (rounded);
+    * dXp = dH W1_e, stored (rounded).
+    Over the expert's rows: dW2_e = sum (w dy) outer a, dW1_e = sum dH outer x. In MXFP8 mode both
+    dgrad GEMMs take MXFP8 images along their reduction axes and x enters dW1 as its MXFP8 image.
+    Returns (dw [c], dH [c, 2I], dXp [c, d], dW1_e [2I, d], dW2_e [d, I]).
+    """
+    I = h.shape[1] // 2
+    w1 = np.asarray(w1, np.float64)
+    w2 = np.asarray(w2, np.float64)
+    if mxmode:
+        dAp = mx.qdq(dy) @ mx.qdq(w2.T).T      # W2 [d, I] quantised along d
+        dw = np.sum(dAp * a, axis=1)
+    else:
+        dAp = dy @ w2
+        dw = np.sum(dy * o_used, axis=1)
+    dA = wv * dAp
+    g = h[:, :I]
+    u = h[:, I:]
+    s = _sigmoid(g)
+    dg = dA * u * s * (1.0 + g * (1.0 - s))
+    du = dA * (g * s)
+    dh = rnd(np.concatenate([dg, du], axis=1))
+    if mxmode:
+        dxp = rnd(mx.qdq(dh) @ mx.qdq(w1.T).T)  # W1 [2I, d] quantised along 2I
+    else:
+        dxp = rnd(dh @ w1)
+    dW2 = (wv * dy).T @ a
+    dW1 = dh.T @ (mx.qdq(x) if mxmode else x)
+    return dw, dh, dxp, dW1, dW2
+
+
+def gather_sum(R, w, tk_row, k):
+    """out_t = sum_j w_tj R[pos(t, j)], j ascending, unrounded; w = None sums without weights.
+    The combine (reading "combine") and the sum of a token's dXp rows in backward."""
+    T = len(tk_row) // k
+    out = np.zeros((T, R.shape[1]))
+    for j in range(k):
+        rows = R[tk_row[np.arange(T) * k + j]]
+        out += rows if w is None else w[:, j:j + 1] * rows
+    return out
+
+
+def router_backward(w, idx, dw, E):
+    """Top-k softmax backward: dlogit_j = w_j (dw_j - sum_{i in S} w_i dw_i) on the selected set
+    S, and exactly 0 off it (reading "router_grad": nothing is detached). Returns [T, E]."""
+    dl = w * (dw - np.sum(w * dw, axis=1, keepdims=True))
+    dlogits = np.zeros((w.shape[0], E))
+    np.put_along_axis(dlogits, idx, dl, axis=1)
+    return dlogits
+
+
+def _routing(X, Wr, k, topk_idx, topk_w, logits):
+    if topk_idx is None:
+        L = router_logits_fp32(X, Wr) if logits == "fp32" else router_logits_fp64(X, Wr)
+        idx, w = route_topk(L, k)
+        return idx, w, k, L
+    idx = np.asarray(topk_idx, np.int32)
+    return idx, np.asarray(topk_w, np.float64), idx.shape[1], None
+
+
 def forward(X, W1, W2, *, Wr=None, k=None, topk_idx=None, topk_w=None,
             storage="bf16", logits="fp32", experts=None, precision="bf16") -> dict:
     """Forward pass of the MoE layer.
@@ -156,26 +251,21 @@ def forward(X, W1, W2, *, Wr=None, k=None, topk_idx=None, topk_w=None,
     Routing comes from the router (Wr, k) or is given (topk_idx, topk_w). ``experts`` limits
     the expert math to a subset, for bounded CPU timings; rows of the other experts stay NaN.
 
-    Per expert e and each of its rows (readings "expert", "storage_bf16"):
-    [g | u] = x W1_e^T, a = silu(g) * u, o = a W2_e^T. Then y_t = sum_j w_tj o_tj, j ascending
-    (reading "combine"). With precision="mxfp8" the two GEMMs take MXFP8 images of their
-    operands (reading "mxfp8"). Returns a dict of every intermediate the GPU path also produces.
+    Per expert e and each of its rows (``expert_forward``): [g | u] = x W1_e^T,
+    a = silu(g) * u, o = a W2_e^T. Then y_t = sum_j w_tj o_tj, j ascending (reading
+    "combine"). With precision="mxfp8" the two GEMMs take MXFP8 images of their operands
+    (reading "mxfp8"). Returns a dict of every intermediate the GPU path also produces.
     """
-    mxq = mx.qdq if precision == "mxfp8" else (lambda a, axis=-1: a)
+    mxq = mx.qdq if precision == "mxfp8" else _identity
     X = np.asarray(X, np.float64)
     T, d = X.shape
     E, twoI, _ = W1.shape
     I = twoI // 2
-    rnd = bf16_round if storage == "bf16" else (lambda a: a)
+    rnd = _rounder(storage)
     out = {}
-    if topk_idx is None:
-        L = router_logits_fp32(X, Wr) if logits == "fp32" else router_logits_fp64(X, Wr)
-        idx, w = route_topk(L, k)
+    idx, w, k, L = _routing(X, Wr, k, topk_idx, topk_w, logits)
+    if L is not None:
         out["logits"] = L
-    else:
-        idx = np.asarray(topk_idx, np.int32)
-        w = np.asarray(topk_w, np.float64)
-        k = idx.shape[1]
     counts, offsets, row_src, tk_row = permute(idx, E)
     Tk = T * k
     H = np.full((Tk, twoI), np.nan)
@@ -188,20 +278,10 @@ def forward(X, W1, W2, *, Wr=None, k=None, topk_idx=None, topk_w=None,
         if p1 == p0:
             continue
         tok = row_src[p0:p1] // k
-        x = mxq(X[tok])
-        w1 = mxq(np.asarray(W1[e], np.float64))
-        g = x @ w1[:I].T
-        u = x @ w1[I:].T
-        H[p0:p1, :I] = rnd(g)
-        H[p0:p1, I:] = rnd(u)
-        a = rnd(_silu(g) * u)
-        A[p0:p1] = a
-        o = mxq(a) @ mxq(np.asarray(W2[e], np.float64)).T
-        O_exact[p0:p1] = o
-        O[p0:p1] = rnd(o)
-    Y = np.zeros((T, d))
-    for j in range(k):
-        Y += w[:, j:j + 1] * O[tk_row[np.arange(T) * k + j]]
+        H[p0:p1], A[p0:p1], O_exact[p0:p1] = expert_forward(X[tok], W1[e], W2[e], rnd=rnd,
+                                                            mxq=mxq)
+        O[p0:p1] = rnd(O_exact[p0:p1])
+    Y = gather_sum(O, w, tk_row, k)
     out.update(idx=idx, w=w, counts=counts, offsets=offsets, row_src=row_src, tk_row=tk_row,
                H=H, A=A, O=O, O_exact=O_exact, Y=rnd(Y), k=k, storage=storage,
                routed=topk_idx is None, precision=precision)
@@ -211,14 +291,14 @@ def forward(X, W1, W2, *, Wr=None, k=None, topk_idx=None, topk_w=None,
 def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None) -> dict:
     """Backward pass: gradients of L = <Y, dY> with respect to every input.
 
-    Per row at position pos (token t, slot j, expert e, weight w):
+    Per row at position pos (token t, slot j, expert e, weight w), by ``expert_backward``:
     * dw = <dY_t, o>, the router-weight gradient (reading "router_grad");
     * dA = w * (dY_t W2_e);
     * dg = dA * u * s * (1 + g (1 - s)) with s = sigmoid(g), and du = dA * silu(g);
     * dXp = [dg | du] W1_e;
     * dW2_e = sum over rows of (w dY_t) outer a;
     * dW1_e = sum over rows of [dg | du] outer x_t.
-    Per token, over its selected set S:
+    Per token, over its selected set S (``router_backward``):
     * dlogit_j = w_j (dw_j - sum_{i in S} w_i dw_i), and 0 off S;
     * dX_t = sum_j dXp_tj + sum_j dlogit_j Wr_{e_j};
     * dWr = dlogits^T X.
@@ -236,10 +316,9 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None) -> dict:
     E, twoI, _ = W1.shape
     I = twoI // 2
     k = fwd["k"]
-    rnd = bf16_round if fwd["storage"] == "bf16" else (lambda a: a)
+    rnd = _rounder(fwd["storage"])
     offsets, row_src, tk_row = fwd["offsets"], fwd["row_src"], fwd["tk_row"]
     w_flat = fwd["w"].reshape(-1)
-    O_used = fwd["O"]
     Tk = T * k
     dw_pos = np.full(Tk, np.nan)
     dH = np.full((Tk, twoI), np.nan)
@@ -253,43 +332,75 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None) -> dict:
             continue
         rows = row_src[p0:p1]
         tok = rows // k
-        wv = w_flat[rows][:, None]
-        dy = dY[tok]
-        w2 = np.asarray(W2[e], np.float64)
-        w1 = np.asarray(W1[e], np.float64)
-        if mxmode:
-            dAp = mx.qdq(dy) @ mx.qdq(w2.T).T      # W2 [d, I] quantised along d
-            dw_pos[p0:p1] = np.sum(dAp * fwd["A"][p0:p1], axis=1)
-        else:
-            dAp = dy @ w2
-            dw_pos[p0:p1] = np.sum(dy * O_used[p0:p1], axis=1)
-        dA = wv * dAp
-        g = fwd["H"][p0:p1, :I]
-        u = fwd["H"][p0:p1, I:]
-        s = _sigmoid(g)
-        dg = dA * u * s * (1.0 + g * (1.0 - s))
-        du = dA * (g * s)
-        dh = rnd(np.concatenate([dg, du], axis=1))
-        dH[p0:p1] = dh
-        if mxmode:
-            dXp[p0:p1] = rnd(mx.qdq(dh) @ mx.qdq(w1.T).T)  # W1 [2I, d] quantised along 2I
-        else:
-            dXp[p0:p1] = rnd(dh @ w1)
-        dW2[slot] = (wv * dy).T @ fwd["A"][p0:p1]
-        dW1[slot] = dh.T @ (mx.qdq(X[tok]) if mxmode else X[tok])
+        dw_pos[p0:p1], dH[p0:p1], dXp[p0:p1], dW1[slot], dW2[slot] = expert_backward(
+            X[tok], dY[tok], w_flat[rows][:, None], fwd["H"][p0:p1], fwd["A"][p0:p1],
+            fwd["O"][p0:p1], W1[e], W2[e], rnd=rnd, mxmode=mxmode)
     dw = dw_pos[tk_row].reshape(T, k)
-    dXsum = np.zeros((T, d))
-    for j in range(k):
-        dXsum += dXp[tk_row[np.arange(T) * k + j]]
+    dXsum = gather_sum(dXp, None, tk_row, k)
     out = dict(dw=dw, dH=dH, dXp=dXp, dW1=dW1, dW2=dW2, experts=ex)
     if fwd["routed"]:
-        w = fwd["w"]
-        idx = fwd["idx"]
-        dl = w * (dw - np.sum(w * dw, axis=1, keepdims=True))
-        dlogits = np.zeros((T, E))
-        np.put_along_axis(dlogits, idx, dl, axis=1)
-        Wr64 = np.asarray(Wr, np.float64)
-        dXsum = dXsum + dlogits @ Wr64
+        dlogits = router_backward(fwd["w"], fwd["idx"], dw, E)
+        dXsum = dXsum + dlogits @ np.asarray(Wr, np.float64)
+        out["dlogits"] = dlogits
+        out["dWr"] = dlogits.T @ (mx.qdq(X) if mxmode else X)
+    out["dX"] = rnd(dXsum)
+    return out
+
+
+def layer(X, W1, W2, dY, *, Wr=None, k=None, topk_idx=None, topk_w=None, storage="bf16",
+          precision="bf16", on_expert=None) -> dict:
+    """Forward and backward of the whole layer, one expert at a time.
+
+    The same steps as ``forward`` followed by ``backward``, in the same order and arithmetic,
+    but each expert's forward and backward run back to back and its weight gradients are handed
+    to ``on_expert(e, dW1_e, dW2_e)`` instead of being kept. Host memory thus stays at the
+    per-row intermediates plus one expert's dW, which lets the oracle cover every token of the
+    largest workloads. Returns the forward intermediates and the backward results of
+    ``forward``/``backward`` (without dW1 and dW2).
+    """
+    mxmode = precision == "mxfp8"
+    mxq = mx.qdq if mxmode else _identity
+    X = np.asarray(X, np.float64)
+    dY = np.asarray(dY, np.float64)
+    T, d = X.shape
+    E, twoI, _ = W1.shape
+    I = twoI // 2
+    rnd = _rounder(storage)
+    idx, w, k, L = _routing(X, Wr, k, topk_idx, topk_w, "fp32")
+    counts, offsets, row_src, tk_row = permute(idx, E)
+    Tk = T * k
+    w_flat = w.reshape(-1)
+    H = np.full((Tk, twoI), np.nan)
+    A = np.full((Tk, I), np.nan)
+    O = np.full((Tk, d), np.nan)
+    dw_pos = np.full(Tk, np.nan)
+    dH = np.full((Tk, twoI), np.nan)
+    dXp = np.full((Tk, d), np.nan)
+    for e in range(E):
+        p0, p1 = int(offsets[e]), int(offsets[e + 1])
+        if p1 == p0:
+            if on_expert is not None:
+                on_expert(e, np.zeros((twoI, d)), np.zeros((d, I)))
+            continue
+        rows = row_src[p0:p1]
+        tok = rows // k
+        w1, w2 = W1[e], W2[e]
+        H[p0:p1], A[p0:p1], o = expert_forward(X[tok], w1, w2, rnd=rnd, mxq=mxq)
+        O[p0:p1] = rnd(o)
+        dw_pos[p0:p1], dH[p0:p1], dXp[p0:p1], dW1, dW2 = expert_backward(
+            X[tok], dY[tok], w_flat[rows][:, None], H[p0:p1], A[p0:p1], O[p0:p1], w1, w2,
+            rnd=rnd, mxmode=mxmode)
+        if on_expert is not None:
+            on_expert(e, dW1, dW2)
+    out = dict(idx=idx, w=w, counts=counts, offsets=offsets, row_src=row_src, tk_row=tk_row,
+               H=H, A=A, O=O, Y=rnd(gather_sum(O, w, tk_row, k)), k=k)
+    dw = dw_pos[tk_row].reshape(T, k)
+    dXsum = gather_sum(dXp, None, tk_row, k)
+    out.update(dw=dw, dH=dH, dXp=dXp)
+    if L is not None:
+        out["logits"] = L
+        dlogits = router_backward(w, idx, dw, E)
+        dXsum = dXsum + dlogits @ np.asarray(Wr, np.float64)
         out["dlogits"] = dlogits
         out["dWr"] = dlogits.T @ (mx.qdq(X) if mxmode else X)
     out["dX"] = rnd(dXsum)
