@@ -6,11 +6,15 @@ the forward grouped GEMMs and combine, and the full backward. Inputs are residen
 before timing starts. The default workload is the DeepSeek-V3-shaped routed layer: T=2048
 tokens, d=7168, 256 experts, top-8, SwiGLU intermediate 2048, BF16.
 
-Prints one JSON line. `value` is tokens/s over the timed steps (hipEvents on the layer's
-stream). `roofline` is the dominant kernel's algorithmic bytes (or flops) per launch divided
-by its average launch time. Those times come from events the library records around each of
-its launches on that same stream, during the timed steps. `cpu_baseline` times the float64
-CPU oracle on a bounded sample of the same workload, extrapolated to the whole layer.
+Prints one JSON line. `value` is tokens/s over the timed steps (hipEvents between steps on the
+layer's stream, nothing between the launches). `roofline` is the dominant kernel's algorithmic
+bytes (or flops) per launch divided by its average launch time. Those times come from a second
+timed region of as many steps, in which the library records events around each of its launches
+on that same stream (`ms_per_step_traced` is that region's step time). `cpu_baseline` times the
+float64 CPU oracle on a bounded sample of the same workload, extrapolated to the whole layer,
+with per-workload samples beside it. Further lines: the other grid form (persistent), MXFP8
+mode, the local expert slice, the tiny layer (eager and as a HIP graph) and the streaming
+macrobatch (serial and overlapped).
 """
 from __future__ import annotations
 
@@ -131,41 +135,134 @@ def measured_traffic(workload, kernel):
     return rec["read_bytes"] + rec["write_bytes"]
 
 
-def cpu_baseline(inp, cfg, s_small=8, s_large=40):
-    """The CPU oracle on a bounded sample: the full router and bookkeeping plus the expert math
-    of the first `s` experts, for two values of s. Its time is linear in the expert count, so
-    the whole-layer time is extrapolated to all E experts."""
-    import numpy as np
+def _oracle_threads():
+    from threadpoolctl import threadpool_info
+    return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+
+
+def _oracle_step(inp, cfg, experts=None):
+    """One oracle forward + backward of the workload (expert math limited to `experts`)."""
     import oracle
     import workload
-    from threadpoolctl import threadpool_info
-
     X = workload.to_numpy(inp["X"])
     dY = workload.to_numpy(inp["dY"])
     W1 = workload.HostExperts(inp["W1"])
     W2 = workload.HostExperts(inp["W2"])
-    routed = "Wr" in inp
-    kw = dict(Wr=workload.to_numpy(inp["Wr"]), k=cfg["k"]) if routed else dict(
+    kw = dict(Wr=workload.to_numpy(inp["Wr"]), k=cfg["k"]) if "Wr" in inp else dict(
         topk_idx=workload.to_numpy(inp["topk_idx"]), topk_w=workload.to_numpy(inp["topk_w"]))
+    f = oracle.forward(X, W1, W2, experts=experts, **kw)
+    oracle.backward(f, X, W1, W2, dY, Wr=kw.get("Wr"), experts=experts)
+
+
+def cpu_baseline(inp, cfg, s_small=8, s_large=40):
+    """The CPU oracle on a bounded sample of the workload: the full router and bookkeeping plus
+    the expert math of the first `s` experts, for two values of s. Its time is linear in the
+    expert count (near-uniform load), so the whole-layer time is extrapolated to all E experts.
+    `cores` is the BLAS thread count the oracle's matrix products ran on (its element-wise
+    numpy steps run on one thread); `os_cpu_count` is what the host reports."""
     E = cfg["E"]
     times = {}
     for s in (s_small, s_large):
         ex = list(range(min(s, E)))
         t0 = time.perf_counter()
-        f = oracle.forward(X, W1, W2, experts=ex, **kw)
-        oracle.backward(f, X, W1, W2, dY, Wr=kw.get("Wr"), experts=ex)
+        _oracle_step(inp, cfg, experts=ex)
         times[len(ex)] = time.perf_counter() - t0
-        del f
     (sa, ta), (sb, tb) = sorted(times.items())
     slope = (tb - ta) / max(sb - sa, 1)
     full = ta + slope * (E - sa)
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": cfg["T"] / full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": cfg["T"] / full, "unit": "tokens/s", "cores": _oracle_threads(),
+            "os_cpu_count": os.cpu_count(), "kind": "oracle",
             "sample": (f"{cfg['name']} seed 0, full router and bookkeeping, expert math of "
                        f"experts 0..{sa - 1} ({ta:.2f} s) and 0..{sb - 1} ({tb:.2f} s) "
                        f"fwd+bwd; whole-layer time extrapolated linearly to {E} experts "
                        f"= {full:.1f} s"),
             "layer_seconds": full}
+
+
+def cpu_tiny(dev):
+    """The oracle on the whole tiny workload (no sampling), on all BLAS threads and on one."""
+    import workload
+    from threadpoolctl import threadpool_limits
+    cfg = workload.config("tiny")
+    inp = workload.make_inputs("tiny", seed=0, device=dev)
+    out = {}
+    for label, limit in (("all_threads", None), ("one_thread", 1)):
+        if limit is None:
+            t0 = time.perf_counter()
+            _oracle_step(inp, cfg)
+            dt = time.perf_counter() - t0
+            threads = _oracle_threads()
+        else:
+            with threadpool_limits(limits=limit):
+                t0 = time.perf_counter()
+                _oracle_step(inp, cfg)
+                dt = time.perf_counter() - t0
+            threads = 1
+        out[label] = {"seconds": round(dt, 3), "tokens_per_s": round(cfg["T"] / dt, 1),
+                      "threads": threads}
+    return out
+
+
+def cpu_expert_sample(inp, cfg, rows_total):
+    """The oracle on the lightest non-empty expert of a given-routing workload, scaled by rows:
+    the whole layer's expert math is linear in the rows (identical expert shapes)."""
+    import numpy as np
+    import workload
+    idx = workload.to_numpy(inp["topk_idx"]).reshape(-1)
+    counts = np.bincount(idx, minlength=cfg["E"])
+    nz = np.flatnonzero(counts)
+    e = int(nz[np.argmin(counts[nz])])
+    t0 = time.perf_counter()
+    _oracle_step(inp, cfg, experts=[e])
+    dt = time.perf_counter() - t0
+    full = dt * rows_total / counts[e]
+    return {"seconds_sample": round(dt, 3), "sample": f"expert {e} ({counts[e]} rows) fwd+bwd",
+            "layer_seconds": round(full, 2), "rows_per_s": round(rows_total / full, 1),
+            "threads": _oracle_threads()}
+
+
+def cpu_stream_sample(inp, cfg):
+    """The oracle on one microbatch of the streaming macrobatch, experts 0..15 of its 512,
+    scaled to 512 experts and 8 microbatches (near-uniform load)."""
+    import workload
+    one = dict(inp, X=inp["X"][0], dY=inp["dY"][0])
+    t0 = time.perf_counter()
+    _oracle_step(one, cfg, experts=list(range(16)))
+    dt = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    _oracle_step(one, cfg, experts=list(range(32)))
+    dt2 = time.perf_counter() - t1
+    per_mb = dt + (dt2 - dt) / 16 * (cfg["E"] - 16)
+    full = per_mb * cfg["microbatches"]
+    del workload
+    return {"sample": "microbatch 0, router and bookkeeping plus experts 0..15 and 0..31; "
+                      "extrapolated linearly to 512 experts and 8 microbatches",
+            "seconds_sample": round(dt + dt2, 2), "layer_seconds": round(full, 1),
+            "tokens_per_s": round(cfg["T"] * cfg["microbatches"] / full, 1),
+            "threads": _oracle_threads()}
+
+
+def time_steps(step, stream, steps, warmup):
+    """Mean, median and minimum ms per step over `steps` steps after `warmup` untimed ones.
+    Events sit only between steps, on the layer's stream."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t_host = time.perf_counter()
+    marks[0].record(stream)
+    for i in range(steps):
+        step()
+        marks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
+    per = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    h = len(per) // 2
+    median = per[h] if len(per) % 2 else 0.5 * (per[h - 1] + per[h])
+    return {"ms": marks[0].elapsed_time(marks[-1]) / steps, "ms_median": median,
+            "ms_min": per[0], "t_host": t_host}
 
 
 def main():
@@ -175,13 +272,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--persistent", action="store_true")
+    ap.add_argument("--persistent", action="store_true",
+                    help="time the persistent grids as the headline (default: one-shot grids)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-trace", action="store_true", help="skip per-kernel events")
+    ap.add_argument("--no-trace", action="store_true", help="skip the per-kernel traced pass")
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the MXFP8-mode run on the same inputs")
     ap.add_argument("--no-expert-slice", action="store_true",
                     help="skip the local expert-slice (local_zipf) run")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the persistent, tiny and streaming-macrobatch lines")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB, a known-size "
                          "reference for HBM byte counters")
@@ -206,7 +306,8 @@ def main():
     torch.cuda.set_device(dev)
     cfg = workload.config(args.workload)
     if cfg.get("microbatches"):
-        print("the streaming workload is a parity case, not a bench line", file=sys.stderr)
+        print("the streaming workload is reported as the `stream` line of the default run",
+              file=sys.stderr)
         sys.exit(2)
     print(f"[bench] generating {args.workload} inputs (seed {args.seed})", file=sys.stderr,
           flush=True)
@@ -225,9 +326,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    main_run = run_layer(m, MoeLayer, inp, cfg, stream, args, mx=mx)
+    main_run = run_layer(m, MoeLayer, inp, cfg, stream, args, mx=mx,
+                         persistent=args.persistent)
     ms, kernels = main_run["ms"], main_run["kernels"]
-    # in MXFP8 mode a step also re-quantises the weights (they change every optimizer step)
     tokens_per_s = T / (ms * 1e-3)
 
     dominant = max(kernels, key=lambda n: kernels[n]["us"]) if kernels else None
@@ -240,9 +341,21 @@ def main():
                 "alg_bytes": kd["alg_bytes"], "us_per_step": kd["us"],
                 "launches_per_step": kd["launches_per_step"]}
     pc = {}
-    for n in ("perm_place", "combine"):
+    for n in ("perm_place", "combine", "scale_gather", "uncombine"):
         if n in kernels:
             pc[n] = {"GB/s": kernels[n].get("achieved"), "frac_hbm": kernels[n].get("frac")}
+
+    extra = {}
+    if not args.no_extra and args.workload == "dsv3" and not mx:
+        # the same layer on the persistent grids (or on one-shot grids when those are headline)
+        print("[bench] the other grid form on the same inputs", file=sys.stderr, flush=True)
+        r = run_layer(m, MoeLayer, inp, cfg, stream, args, mx=False,
+                      persistent=not args.persistent, trace=False)
+        extra["other_grid"] = {"persistent": not args.persistent,
+                               "tokens_per_s": round(T / (r["ms"] * 1e-3), 1),
+                               "ms_per_step": round(r["ms"], 4),
+                               "ms_per_step_median": round(r["ms_median"], 4)}
+        torch.cuda.empty_cache()
 
     # The same layer in MXFP8 mode on the same inputs: the second precision the metric names.
     mx_line = None
@@ -257,12 +370,18 @@ def main():
                    "grouped_gemm": r["gemm"], "kernels": r["kernels"]}
         torch.cuda.empty_cache()
 
+    cpu = None
+    if not args.no_cpu_baseline and not mx:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp, cfg)
+    del inp
+    torch.cuda.empty_cache()
+
     # The local expert slice (16,384 received rows over 8 experts, Zipf-skewed): there the
     # grouped GEMMs are MFMA-bound, so it is where their fraction of the MFMA peak means something.
     slice_line = None
     if args.workload == "dsv3" and not args.no_expert_slice:
         print("[bench] local expert slice (local_zipf)", file=sys.stderr, flush=True)
-        torch.cuda.empty_cache()
         cz = workload.config("local_zipf")
         iz = workload.make_inputs("local_zipf", seed=args.seed, device=dev)
         r = run_layer(m, MoeLayer, iz, cz, stream, args, mx=False)
@@ -270,7 +389,8 @@ def main():
                       "ms_per_step": round(r["ms"], 4),
                       "rows_per_s": round(cz["T"] * cz["k"] / (r["ms"] * 1e-3), 1),
                       "grouped_gemm": r["gemm"],
-                      "gemm_us": {g: r["kernels"][g]["us"] for g in GEMMS if g in r["kernels"]}}
+                      "gemm_us": {g: r["kernels"][g]["us"] for g in GEMMS if g in r["kernels"]},
+                      "kernels": r["kernels"]}
         if not args.no_mxfp8:
             # MXFP8 on the same slice: its GEMMs against the fp8 MFMA peak where they are
             # MFMA-bound rather than weight-streaming
@@ -282,7 +402,22 @@ def main():
                 "layer_ms_without_weight_quantize": round(rz["ms"] - rz["quant_ms"], 4),
                 "grouped_gemm": rz["gemm"],
                 "gemm_us": {g: rz["kernels"][g]["us"] for g in GEMMS if g in rz["kernels"]}}
+        if cpu is not None:
+            cpu.setdefault("per_config", {})["local_zipf"] = cpu_expert_sample(
+                iz, cz, cz["T"] * cz["k"])
         del iz
+        torch.cuda.empty_cache()
+
+    if not args.no_extra and args.workload == "dsv3":
+        print("[bench] tiny layer", file=sys.stderr, flush=True)
+        extra["tiny"] = run_tiny(m, MoeLayer, workload, dev, stream, args)
+        print("[bench] streaming macrobatch", file=sys.stderr, flush=True)
+        extra["stream"], ist = run_stream(workload, dev, stream, args)
+        if cpu is not None:
+            cpu.setdefault("per_config", {})["stream"] = cpu_stream_sample(
+                ist, workload.config("stream"))
+            cpu["per_config"]["tiny"] = cpu_tiny(dev)
+        del ist
         torch.cuda.empty_cache()
 
     # practical HBM ceiling: one plain 2 GiB device copy (read + write), best of 3. Skipped in
@@ -304,11 +439,6 @@ def main():
         hbm_copy = round(2 * n / (best * 1e-3) / 1e9, 1)
         del src, dst
 
-    cpu = None
-    if not args.no_cpu_baseline and not mx:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(inp, cfg)
-
     line = {
         "metric": "MoE layer fwd+bwd tokens/s",
         "value": round(tokens_per_s, 1),
@@ -319,6 +449,8 @@ def main():
         "ms_per_step": round(ms, 4),
         "ms_per_step_median": round(main_run["ms_median"], 4),
         "ms_per_step_min": round(main_run["ms_min"], 4),
+        "ms_per_step_traced": (round(main_run["ms_traced"], 4)
+                               if main_run.get("ms_traced") else None),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -333,6 +465,7 @@ def main():
         "permute_combine": pc,
         "mxfp8": mx_line,
         "expert_slice": slice_line,
+        **extra,
         "hbm_copy": {"GB/s": hbm_copy, "bytes": 2 * n, "what": "one plain device copy, read + write"},
         "kernels": kernels,
         "host_seconds_timed": round(main_run["t_host"], 4),
@@ -340,15 +473,78 @@ def main():
     print(json.dumps(line))
 
 
-def run_layer(m, MoeLayer, inp, cfg, stream, args, mx):
-    """Warm up and time `args.steps` layer steps; per-kernel times from the library's own
-    events on the layer's stream. In MXFP8 mode each step first quantises the weights."""
+def run_tiny(m, MoeLayer, workload, dev, stream, args):
+    """The tiny layer (T=256, d=256, 8 experts, top-2): launch-bound. Eager steps, then the
+    same step captured once into a HIP graph and replayed (one host launch per step)."""
+    import torch
+    cfg = workload.config("tiny")
+    inp = workload.make_inputs("tiny", seed=args.seed, device=dev)
+    L = MoeLayer(cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"], device=dev)
+    X, Wr, W1, W2, dY = (inp[n] for n in ("X", "Wr", "W1", "W2", "dY"))
+    eager = time_steps(lambda: L.step(X, Wr, W1, W2, dY, stream=stream), stream,
+                       max(args.steps, 50), args.warmup)
+    out = {"T": cfg["T"], "eager": {"tokens_per_s": round(cfg["T"] / (eager["ms"] * 1e-3), 1),
+                                    "ms_per_step": round(eager["ms"], 4),
+                                    "ms_per_step_median": round(eager["ms_median"], 4),
+                                    "host_ms_per_step": round(eager["t_host"] * 1e3
+                                                              / max(args.steps, 50), 4)}}
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            L.step(X, Wr, W1, W2, dY)  # warm the side stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=side):
+                L.step(X, Wr, W1, W2, dY)
+        torch.cuda.synchronize()
+        graph = time_steps(g.replay, torch.cuda.current_stream(), max(args.steps, 50),
+                           args.warmup)
+        out["graph"] = {"tokens_per_s": round(cfg["T"] / (graph["ms"] * 1e-3), 1),
+                        "ms_per_step": round(graph["ms"], 4),
+                        "ms_per_step_median": round(graph["ms_median"], 4)}
+        del g
+    except RuntimeError as e:  # report, keep the rest of the bench line
+        out["graph"] = {"error": str(e)[:200]}
+    del L, inp
+    return out
+
+
+def run_stream(workload, dev, stream, args):
+    """The streaming macrobatch: 8 microbatches of 2368 tokens through one 512 MiB ring (2
+    slots), forward 0..7, backward 7..0 with the overwritten slots replayed. Tokens/s counts the
+    8 x 2368 tokens of a macrobatch, replay included; serial, then with the next microbatch's
+    routing and permutation on a second stream."""
+    from mixture_experts_layer_deterministic_amd.layer import Macrobatch
+    cfg = workload.config("stream")
+    inp = workload.make_inputs("stream", seed=args.seed, device=dev)
+    n = cfg["microbatches"]
+    tokens = n * cfg["T"]
+    out = {"microbatches": n, "T": cfg["T"], "tokens": tokens, "ring_bytes": cfg["ring_bytes"]}
+    for overlap in (False, True):
+        mb = Macrobatch(cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"], n, cfg["ring_bytes"],
+                        device=dev, overlap=overlap)
+        out["ring_slots"] = mb.S
+        r = time_steps(lambda: mb.run(inp["X"], inp["Wr"], inp["W1"], inp["W2"], inp["dY"],
+                                      stream), stream, max(3, args.steps // 4), 1)
+        out["overlap" if overlap else "serial"] = {
+            "tokens_per_s": round(tokens / (r["ms"] * 1e-3), 1),
+            "ms_per_macrobatch": round(r["ms"], 3),
+            "ms_per_macrobatch_median": round(r["ms_median"], 3)}
+        del mb
+    return out, inp
+
+
+def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=True):
+    """Warm up and time `args.steps` layer steps without any per-launch event, then (unless
+    `trace` is off) time as many again with the library's per-launch events on the layer's
+    stream, for the per-kernel times. In MXFP8 mode each step first quantises the weights."""
     import torch
     T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
     dev = inp["X"].device
     routed = "Wr" in inp
     prec = m.MOE_PREC_MXFP8 if mx else m.MOE_PREC_BF16
-    L = MoeLayer(T, d, E, k, I, device=dev, persistent=args.persistent, precision=prec)
+    L = MoeLayer(T, d, E, k, I, device=dev, persistent=persistent, precision=prec)
     wr = inp.get("Wr")
     if not routed:
         L.set_routing(inp["topk_idx"], inp["topk_w"])
@@ -359,10 +555,9 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx):
             L.quantize_weights(W1, W2, stream)
         L.step(X, wr, W1, W2, dY, stream=stream)
 
-    print(f"[bench] warmup ({'mxfp8' if mx else 'bf16'})", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    print(f"[bench] {'mxfp8' if mx else 'bf16'}{' persistent' if persistent else ''}: "
+          f"warmup and {args.steps} untraced steps", file=sys.stderr, flush=True)
+    res = time_steps(step, stream, args.steps, args.warmup)
 
     # launches per step (traced once, untimed)
     probe = [torch.cuda.Event(enable_timing=True) for _ in range(128)]
@@ -375,56 +570,41 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx):
     torch.cuda.synchronize()
     del keep
 
-    ev = []
-    names = None
-    keep = None
-    if not args.no_trace:
+    kernels = {}
+    alg = algorithmic(cfg, routed=routed, mx=mx)
+    if trace and not args.no_trace:
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * per_step * args.steps)]
         for e in ev:
             e.record(stream)
         torch.cuda.synchronize()
         names = (ctypes.c_char_p * (per_step * args.steps))()
-
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} steps ({per_step} launches each)", file=sys.stderr,
-          flush=True)
-    if ev:
+        print(f"[bench] {args.steps} traced steps ({per_step} launches each)", file=sys.stderr,
+              flush=True)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         keep = m.moe_trace_begin([e.cuda_event for e in ev], names)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    t_host = time.perf_counter()
-    start.record(stream)
-    marks[0].record(stream)
-    for i in range(args.steps):
-        step()
-        marks[i + 1].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    t_host = time.perf_counter() - t_host
-    if ev:
+        a.record(stream)
+        for _ in range(args.steps):
+            step()
+        b.record(stream)
+        torch.cuda.synchronize()
         m.moe_trace_end()
-    ms = start.elapsed_time(end) / args.steps
-    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
-    h = len(step_ms) // 2
-    ms_median = step_ms[h] if len(step_ms) % 2 else 0.5 * (step_ms[h - 1] + step_ms[h])
-    ms_min = step_ms[0]
-
-    alg = algorithmic(cfg, routed=routed, mx=mx)
-    kernels = {}
-    if ev:
+        res["ms_traced"] = a.elapsed_time(b) / args.steps
         tot = {}
         cnt = {}
         for i in range(per_step * args.steps):
             n = names[i].decode()
             tot[n] = tot.get(n, 0.0) + ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3
             cnt[n] = cnt.get(n, 0) + 1
-        # A step's work of one kind may take several launches (the forward GEMMs run their
-        # 256-row blocks and their remainders as two, "<name>_big" and "<name>"): a kernel's
-        # `us` is its time per step, summed over them, and `parts` splits it.
+        # A step's work of one kind may take several launches (the GEMMs run their 256-row
+        # blocks and their remainders as two, "<name>_big" and "<name>"; the MXFP8 gate wgrad
+        # also expands the big experts' fp8 rows, "<name>_expand"): a kernel's `us` is its time
+        # per step, summed over them, and `parts` splits it.
         parts = {}
         for n in list(tot):
-            base = n[:-4] if n.endswith("_big") else n
+            base = n
+            for suffix in ("_big", "_expand"):
+                if n.endswith(suffix):
+                    base = n[:-len(suffix)]
             parts.setdefault(base, {})[n] = tot[n] / args.steps
         for n, pt in parts.items():
             us = sum(pt.values())
@@ -437,6 +617,7 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx):
                              for kk, v in r.items()}}
             if len(pt) > 1:
                 kernels[n]["parts_us"] = {p: round(v, 2) for p, v in pt.items()}
+        del keep
     quant_ms = sum(kernels[n]["us"] for n in kernels if n.startswith("quant_w")) / 1e3
     gemm = None
     gemm_us = sum(kernels[g]["us"] for g in GEMMS if g in kernels)
@@ -454,10 +635,9 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx):
                 "attainable_tflops": round(attainable, 2),
                 "frac_attainable": round(tf / attainable, 4),
                 "alg_bytes": nbytes, "hbm_gbps": round(nbytes / (gemm_us * 1e-6) / 1e9, 1),
-                "share_of_step": round(gemm_us / 1e3 / ms, 4)}
+                "share_of_step": round(gemm_us / 1e3 / res.get("ms_traced", res["ms"]), 4)}
     del L
-    return {"ms": ms, "ms_median": ms_median, "ms_min": ms_min, "kernels": kernels, "gemm": gemm,
-            "quant_ms": quant_ms, "t_host": t_host}
+    return dict(res, kernels=kernels, gemm=gemm, quant_ms=quant_ms)
 
 
 if __name__ == "__main__":

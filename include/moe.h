@@ -61,8 +61,13 @@ enum {
 enum { MOE_DEVICE_BAD_EXPERT_INDEX = 1 /* a topk_idx entry outside [0, E): that row is skipped */ };
 
 /* Layer shape and mode. Constraints checked on the host: T >= 1; 1 <= k <= E <= 1024; k <= 64;
- * d % 256 == 0; I % 128 == 0; T * k < 2^31; T * E < 2^31; T * d < 2^31; T * 2I < 2^31;
+ * d % 256 == 0 (the GEMMs have no masked K tail: K steps of 64 and 256-wide tiles along d);
+ * I % 128 == 0 (128-wide tiles along I); T * k < 2^31; T * E < 2^31; and, because the kernels
+ * address rows with 32-bit offsets: T * d < 2^31, T * k * d < 2^31, T * k * 2I < 2^31 (an
+ * expert may receive all T * k rows) and 4 * I * d < 2^31 (the bytes of one expert's W1).
  * precision MOE_PREC_BF16 or MOE_PREC_MXFP8.
+ * Every entry point that enqueues work also checks that the current HIP device is a gfx950
+ * (MOE_ERR_UNSUPPORTED otherwise, MOE_ERR_HIP when no device can be queried).
  *
  * MXFP8 mode (the pages name BF16 and MXFP8 modes: MarkTechPost, closing paragraph of "Three
  * design decisions that matter") follows the OCP MX v1.0 MXFP8 format. Elements are E4M3; every
@@ -95,7 +100,9 @@ typedef struct moe_sizes {
     size_t wq;             /* MXFP8: bytes of the quantised-weight buffer (0 in BF16 mode) */
 } moe_sizes;
 
-/* Sizes of every caller buffer for `cfg`. Host only; enqueues nothing.
+/* Sizes of every caller buffer for `cfg`. Host only; enqueues nothing. (Plumbing of this
+ * library, defined by no passage of the pages. The schedule and task tables live inside the
+ * workspace, so they have no size of their own here.)
  * In MXFP8 mode a ring slot holds the E4M3 codes of Xp [T*k, d] followed (at the next 256-byte
  * boundary) by their scales [T*k, d/32]. */
 int moe_query(const moe_cfg* cfg, moe_sizes* out);
@@ -149,7 +156,9 @@ int moe_route(const moe_cfg* cfg, const void* x, const void* w_router, float* lo
  * goes to position pos = offsets[e] + (number of rows r' < r with the same expert e), so inside
  * an expert segment rows ascend by r.
  *
- *   topk_idx int32 [T, k]          in   (from moe_route, or given by the caller)
+ *   topk_idx int32 [T, k]          in   (from moe_route, or given by the caller; a caller's row
+ *                                       may name one expert twice: every row is its own
+ *                                       position either way)
  *   x        bf16 [T, d]           in
  *   ring     bytes [ring_bytes]    out: slot `slot` (at slot * ring_slot bytes) receives
  *                                       Xp[pos] = x[row_src[pos] / k], bf16 [T*k, d]; in MXFP8
@@ -165,6 +174,28 @@ int moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, void
                 size_t ring_bytes, int32_t slot, int32_t* counts, int32_t* offsets,
                 int32_t* row_src, int32_t* tk_row, void* workspace, size_t ws_bytes,
                 moe_stream_t stream);
+
+/*
+ * moe_permute_static - moe_permute for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same operation, arguments and
+ * results as moe_permute, except that:
+ *  - there is no workspace argument: the permutation's scratch (per-256-row-block expert counts,
+ *    per-row ranks, per-block flags) lives in a fixed array of MOE_STATIC_SCRATCH_BYTES inside
+ *    the library, one per GPU, held until the process ends;
+ *  - the device status word is written to `device_status` (int32, caller device memory) instead
+ *    of the workspace's first word.
+ * The call allocates nothing and frees nothing. Its scratch needs 4 * (nb * E + nb + T * k)
+ * bytes with nb = ceil(T * k / 256), each part 256-byte aligned; beyond MOE_STATIC_SCRATCH_BYTES
+ * it returns MOE_ERR_WORKSPACE_TOO_SMALL and enqueues nothing. Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (concurrent streams, or threads) race and give
+ * undefined results. Calls in one stream order are safe; the array keeps the last call's
+ * contents, and every word is written before it is read.
+ */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)4 << 20)
+int moe_permute_static(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, void* ring,
+                       size_t ring_bytes, int32_t slot, int32_t* counts, int32_t* offsets,
+                       int32_t* row_src, int32_t* tk_row, int32_t* device_status,
+                       moe_stream_t stream);
 
 /*
  * moe_forward - grouped SwiGLU expert MLPs over the ring slot, then the weighted combine.
@@ -254,7 +285,8 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
 int moe_trace_begin(void* const* events, int capacity, const char** names);
 int moe_trace_end(void);
 
-/* A static string for a moe_status value. */
+/* A static string for a moe_status value (plumbing of this library, defined by no passage of
+ * the pages). */
 const char* moe_status_string(int status);
 
 #ifdef __cplusplus

@@ -61,7 +61,11 @@ _SIGS = {
     "moe_backward": [ctypes.POINTER(MoeCfg), _P, _SZ, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                      _SZ, _P, _SZ, _P, _P, _P, _P, _P, _P, _I32, _P, _SZ, _P],
     "moe_quantize_weights": [ctypes.POINTER(MoeCfg), _P, _P, _P, _SZ, _P],
+    "moe_permute_static": [ctypes.POINTER(MoeCfg), _P, _P, _P, _SZ, _I32, _P, _P, _P, _P, _P,
+                           _P],
 }
+
+MOE_STATIC_SCRATCH_BYTES = 4 << 20
 
 
 def lib() -> ctypes.CDLL:
@@ -153,6 +157,14 @@ def moe_permute(cfg, topk_idx, x, ring, slot, counts, offsets, row_src, tk_row, 
                              _nbytes(ring), slot, _ptr(counts), _ptr(offsets), _ptr(row_src),
                              _ptr(tk_row), _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "moe_permute")
+
+
+def moe_permute_static(cfg, topk_idx, x, ring, slot, counts, offsets, row_src, tk_row,
+                       device_status, stream=None):
+    _check(lib().moe_permute_static(ctypes.byref(cfg), _ptr(topk_idx), _ptr(x), _ptr(ring),
+                                    _nbytes(ring), slot, _ptr(counts), _ptr(offsets),
+                                    _ptr(row_src), _ptr(tk_row), _ptr(device_status),
+                                    _stream(stream)), "moe_permute_static")
 
 
 def _wq_bytes(wq):

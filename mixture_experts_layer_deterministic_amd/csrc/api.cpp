@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstring>
 #include <mutex>
 
 #include "moe.h"
@@ -12,6 +13,7 @@
 namespace {
 
 using namespace moe;
+static_assert(MOE_STATIC_SCRATCH_BYTES == kStaticPermScratchBytes, "one size in both places");
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -37,12 +39,41 @@ bool cfg_ok(const moe_cfg* c) {
   if (!c) return false;
   if (c->T < 1 || c->d < 256 || c->d % 256 != 0 || c->I < 128 || c->I % 128 != 0) return false;
   if (c->E < 1 || c->E > 1024 || c->k < 1 || c->k > c->E || c->k > kMaxTopK) return false;
-  const long long Tk = (long long)c->T * c->k;
-  if (Tk >= (1LL << 31) || (long long)c->T * c->E >= (1LL << 31)) return false;
-  if ((long long)c->T * c->d >= (1LL << 31)) return false;  // 32-bit row offsets into X and dY
-  // 32-bit byte offsets into an expert's rows of dH and A (an expert has at most T rows)
-  if ((long long)c->T * 2 * c->I >= (1LL << 31)) return false;
+  const long long T = c->T, d = c->d, I = c->I, Tk = T * c->k;
+  if (Tk >= (1LL << 31) || T * c->E >= (1LL << 31)) return false;
+  // The kernels address rows with 32-bit offsets. Element offsets into X and dY, and byte
+  // offsets into one expert's rows of Xp, dXp, dYw, H, A and dH: a caller's routing may send
+  // every row to one expert (a token may even repeat an expert), so an expert has up to T*k
+  // rows. Byte offsets into one expert's weights: W1[e] is 2I x d bf16.
+  if (T * d >= (1LL << 31)) return false;
+  if (Tk * d >= (1LL << 31) || Tk * 2 * I >= (1LL << 31)) return false;
+  if (4 * I * d >= (1LL << 31)) return false;
   return true;
+}
+
+// The kernels are built for gfx950 only. The current device's architecture is read once per
+// device and kept.
+int check_device() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> verdict[kMaxDev];  // 0 unknown, 1 gfx950, 2 another device
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return MOE_ERR_HIP;
+  }
+  if (dev < kMaxDev) {
+    const int v = verdict[dev].load(std::memory_order_relaxed);
+    if (v) return v == 1 ? MOE_OK : MOE_ERR_UNSUPPORTED;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ERR_HIP;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                  (prop.gcnArchName[6] == 0 || prop.gcnArchName[6] == ':');
+  if (dev < kMaxDev) verdict[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? MOE_OK : MOE_ERR_UNSUPPORTED;
 }
 
 Layout layout(const moe_cfg* c) {
@@ -223,6 +254,7 @@ int moe_quantize_weights(const moe_cfg* cfg, const void* w1, const void* w2, voi
   if (!aligned16(w1) || !aligned16(w2) || !aligned16(wq)) return MOE_ERR_INVALID_ARG;
   const Layout Y = layout(cfg);
   if (wq_bytes < Y.wq_total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if ((st = check_device())) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int E = cfg->E, d = cfg->d, I = cfg->I;
   const uint16_t* a1 = static_cast<const uint16_t*>(w1);
@@ -246,6 +278,7 @@ int moe_route(const moe_cfg* cfg, const void* x, const void* w_router, float* lo
     return MOE_ERR_INVALID_ARG;
   const Layout Y = layout(cfg);
   if (ws_bytes < Y.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if ((st = check_device())) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Launches L;
   L(launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
@@ -267,6 +300,7 @@ int moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, void
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ring(Y, ring, ring_bytes, slot))) return st;
   if (ws_bytes < Y.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if ((st = check_device())) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int Tk = cfg->T * cfg->k;
   int32_t* blk = at<int32_t>(workspace, Y.blk_cnt);
@@ -287,6 +321,48 @@ int moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, void
   return L.status();
 }
 
+int moe_permute_static(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, void* ring,
+                       size_t ring_bytes, int32_t slot, int32_t* counts, int32_t* offsets,
+                       int32_t* row_src, int32_t* tk_row, int32_t* device_status,
+                       moe_stream_t stream) {
+  int st = check_mode(cfg);
+  if (st) return st;
+  const Layout Y = layout(cfg);
+  if (!aligned4(topk_idx) || !aligned16(x) || !aligned4(counts) || !aligned4(offsets) ||
+      !aligned4(row_src) || !aligned4(tk_row) || !aligned4(device_status))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ring(Y, ring, ring_bytes, slot))) return st;
+  // the permutation's scratch, packed from offset 0 of the fixed array
+  const size_t Tk = (size_t)cfg->T * cfg->k;
+  const size_t o_flag = align_up(sizeof(int32_t) * (size_t)Y.nb * cfg->E);
+  const size_t o_rank = o_flag + align_up(sizeof(int32_t) * (size_t)Y.nb);
+  if (o_rank + sizeof(int32_t) * Tk > MOE_STATIC_SCRATCH_BYTES)
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if ((st = check_device())) return st;
+  void* base = nullptr;
+  if (static_perm_scratch(&base) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ERR_HIP;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* slot_base = at<uint8_t>(ring, (size_t)slot * Y.slot);
+  uint16_t* xp = Y.mx ? nullptr : reinterpret_cast<uint16_t*>(slot_base);
+  uint8_t* xp8 = Y.mx ? slot_base : nullptr;
+  uint8_t* xps = Y.mx ? slot_base + Y.slot_sc : nullptr;
+  int32_t* blk = at<int32_t>(base, 0);
+  int32_t* flag = at<int32_t>(base, o_flag);
+  int32_t* rank = at<int32_t>(base, o_rank);
+  // every scratch word is written before it is read: nothing needs clearing
+  Launches L;
+  L(launch_perm_hist(topk_idx, (int)Tk, cfg->E, blk, rank, flag, s));
+  if (!L.err)
+    L(launch_perm_scan(blk, Y.nb, cfg->E, flag, counts, offsets, device_status, s));
+  if (!L.err)
+    L(launch_perm_place(topk_idx, rank, blk, (int)Tk, cfg->E, cfg->k, row_src, tk_row,
+                        static_cast<const uint16_t*>(x), xp, xp8, xps, cfg->d, s));
+  return L.status();
+}
+
 int moe_forward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t slot,
                 const int32_t* offsets, const int32_t* tk_row, const float* topk_w,
                 const void* w1, const void* w2, const void* wq, size_t wq_bytes, void* y,
@@ -301,6 +377,7 @@ int moe_forward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t
   if ((st = check_ring(Y, ring, ring_bytes, slot))) return st;
   if ((st = check_wq(Y, wq, wq_bytes))) return st;
   if (saved_bytes < Y.saved_total || ws_bytes < Y.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if ((st = check_device())) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool pers = cfg->flags & MOE_FLAG_PERSISTENT;
   const int Tk = cfg->T * cfg->k, d = cfg->d, I = cfg->I, E = cfg->E;
@@ -356,6 +433,7 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
   if ((st = check_ring(Y, ring, ring_bytes, slot))) return st;
   if ((st = check_wq(Y, wq, wq_bytes))) return st;
   if (saved_bytes < Y.saved_total || ws_bytes < Y.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if ((st = check_device())) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool pers = cfg->flags & MOE_FLAG_PERSISTENT;
   const int Tk = cfg->T * cfg->k, d = cfg->d, I = cfg->I, E = cfg->E, k = cfg->k;

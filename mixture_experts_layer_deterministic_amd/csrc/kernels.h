@@ -32,6 +32,10 @@ hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t*
                               hipStream_t s);
 
 // permute.hip
+// Bytes of the fixed per-device scratch behind moe_permute_static, and its device address on
+// the current device (fetched once per device).
+constexpr size_t kStaticPermScratchBytes = size_t(4) << 20;
+hipError_t static_perm_scratch(void** ptr);
 hipError_t launch_perm_hist(const int32_t* idx, int Tk, int E, int32_t* blk_cnt, int32_t* rank,
                             int32_t* blk_flag, hipStream_t s);
 hipError_t launch_perm_scan(int32_t* blk_cnt, int nb, int E, const int32_t* blk_flag,

@@ -6,10 +6,37 @@
 // the worst case, so no expert imbalance can overflow it. The counts stay on the device.
 // Row r = t*k + j of expert e lands at offsets[e] + (rows r' < r of expert e), so segments
 // ascend by r.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
+
+// Fixed scratch of the permutation for callers that cannot allocate (moe_permute_static): one
+// copy per GPU, held until the process ends. Host code never passes this name to a kernel (on
+// the host it is only a stand-in); it passes the device address that static_perm_scratch()
+// fetched with hipGetSymbolAddress on that device.
+static __device__ __align__(256) unsigned char scratch[kStaticPermScratchBytes];
+
+hipError_t static_perm_scratch(void** ptr) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDev] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 // Block b owns rows [256 b, 256 b + 256): per-expert counts of the block, and each row's rank
 // among the block's earlier rows of the same expert (a direct count, so it is stable).

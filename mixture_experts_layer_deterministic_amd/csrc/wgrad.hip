@@ -559,7 +559,7 @@ hipError_t launch_wgrad(const WgradArgs& x, hipStream_t s) {
   err = hipGetLastError();
   if (err != hipSuccess || !big_ok) return err;
   if (x.R8) {
-    TraceScope trace("wgrad_expand", s);
+    TraceScope trace("bwd_gate_wgrad_expand", s);
     hipLaunchKernelGGL(expand_big_rows_kernel, dim3(1024), dim3(256), 0, s, x.R8, x.R8s, x.Rx,
                        big, x.offsets, x.Ndim);
     err = hipGetLastError();

@@ -115,3 +115,124 @@ class MoeLayer:
         self.permute(x, slot, stream)
         self.forward(w1, w2, slot, stream=stream)
         self.backward(w_router, w1, w2, dy, slot, stream=stream)
+
+
+class Macrobatch:
+    """The streaming macrobatch: ``n`` microbatches through one fixed ring of ``ring_bytes``.
+
+    Forward runs microbatches 0..n-1, microbatch i in slot i mod S with S = ring slots that fit;
+    backward walks n-1..0 and re-permutes (replays) a microbatch whose slot a later one
+    overwrote, accumulating the weight gradients in that fixed order (MarkTechPost, "Three
+    design decisions that matter": the ring is walked in reverse in backward). Each microbatch
+    keeps its own routing, saved activations and outputs.
+
+    With ``overlap`` the router and permutation of the next microbatch (and, in backward, the
+    replay of the next one down) run on a second stream while the current microbatch's grouped
+    GEMMs run on the first, with their own workspace; events order the two. Every kernel still
+    sees exactly the same inputs, so results are bitwise those of the serial walk.
+    """
+
+    def __init__(self, T, d, E, k, I, n, ring_bytes, device="cuda", overlap=False):
+        self.T, self.d, self.E, self.k, self.I, self.n = T, d, E, k, I, n
+        self.main = MoeLayer(T, d, E, k, I, device=device, ring_slots=1)
+        s = self.main.sizes
+        self.S = ring_bytes // s.ring_slot
+        if self.S < 1:
+            raise ValueError("ring_bytes holds no ring slot")
+        self.main.ring = torch.empty(self.S * s.ring_slot, dtype=torch.uint8, device=device)
+        self.overlap = overlap
+        dev = torch.device(device)
+        i32, f32, bf = torch.int32, torch.float32, torch.bfloat16
+        Tk = T * k
+        self.route_ws = torch.empty(s.workspace, dtype=torch.uint8, device=dev) if overlap else None
+        self.side = torch.cuda.Stream(device=dev) if overlap else None
+        self.mb = []
+        for _ in range(n):
+            self.mb.append(dict(
+                logits=torch.empty(T, E, dtype=f32, device=dev),
+                topk_idx=torch.empty(T, k, dtype=i32, device=dev),
+                topk_w=torch.empty(T, k, dtype=f32, device=dev),
+                counts=torch.empty(E, dtype=i32, device=dev),
+                offsets=torch.empty(E + 1, dtype=i32, device=dev),
+                row_src=torch.empty(Tk, dtype=i32, device=dev),
+                tk_row=torch.empty(Tk, dtype=i32, device=dev),
+                saved=torch.empty(s.saved, dtype=torch.uint8, device=dev),
+                y=torch.empty(T, d, dtype=bf, device=dev),
+                dx=torch.empty(T, d, dtype=bf, device=dev),
+                d_topk_w=torch.empty(T, k, dtype=f32, device=dev)))
+
+    @property
+    def dw1(self):
+        return self.main.dw1
+
+    @property
+    def dw2(self):
+        return self.main.dw2
+
+    @property
+    def dwr(self):
+        return self.main.dwr
+
+    def _route_permute(self, i, x, w_router, ws, stream, route=True):
+        b, L = self.mb[i], self.main
+        if route:
+            moe_route(L.cfg, x, w_router, b["logits"], b["topk_idx"], b["topk_w"], ws, stream)
+        moe_permute(L.cfg, b["topk_idx"], x, L.ring, i % self.S, b["counts"], b["offsets"],
+                    b["row_src"], b["tk_row"], ws, stream)
+
+    def _forward(self, i, w1, w2, stream):
+        b, L = self.mb[i], self.main
+        moe_forward(L.cfg, L.ring, i % self.S, b["offsets"], b["tk_row"], b["topk_w"], w1, w2,
+                    None, b["y"], b["saved"], L.workspace, stream)
+
+    def _backward(self, i, w_router, w1, w2, dy, stream):
+        b, L = self.mb[i], self.main
+        moe_backward(L.cfg, L.ring, i % self.S, b["offsets"], b["row_src"], b["tk_row"],
+                     b["topk_idx"], b["topk_w"], w_router, w1, w2, None, b["saved"], dy, b["dx"],
+                     L.dw1, L.dw2, L.dwr, b["d_topk_w"], int(i != self.n - 1), L.workspace,
+                     stream)
+
+    def run(self, X, w_router, w1, w2, dY, stream=None):
+        """X and dY: [n, T, d] bf16. One macrobatch: forward 0..n-1, backward n-1..0."""
+        main = torch.cuda.current_stream() if stream is None else stream
+        n, S = self.n, self.S
+        replay = lambda i: i < n - S  # its slot was overwritten by microbatch i + S
+        if not self.overlap or S < 2:  # one slot: each microbatch waits for the previous one
+            for i in range(n):
+                self._route_permute(i, X[i], w_router, self.main.workspace, main)
+                self._forward(i, w1, w2, main)
+            for i in reversed(range(n)):
+                if replay(i):
+                    self._route_permute(i, X[i], w_router, self.main.workspace, main, False)
+                self._backward(i, w_router, w1, w2, dY[i], main)
+            return
+        side = self.side
+        ready = [torch.cuda.Event() for _ in range(n)]   # microbatch i routed and permuted
+        slot_free = [torch.cuda.Event() for _ in range(n)]  # microbatch i done with its slot
+        side.wait_stream(main)
+        self._route_permute(0, X[0], w_router, self.route_ws, side)
+        ready[0].record(side)
+        for i in range(n):
+            if i + 1 < n:
+                if i + 1 >= S:  # slot (i+1) mod S last held microbatch i+1-S
+                    side.wait_event(slot_free[i + 1 - S])
+                self._route_permute(i + 1, X[i + 1], w_router, self.route_ws, side)
+                ready[i + 1].record(side)
+            main.wait_event(ready[i])
+            self._forward(i, w1, w2, main)
+            slot_free[i].record(main)
+        # backward: the replay of microbatch i-1 overlaps the backward of microbatch i
+        done = [torch.cuda.Event() for _ in range(n)]  # backward of microbatch i finished
+        for i in reversed(range(n)):
+            j = i - 1
+            if j >= 0 and replay(j):
+                # slot j mod S holds microbatch j+S (> i, walked already): its backward must be
+                # done with the slot before the replay overwrites it
+                side.wait_event(done[j + S])
+                self._route_permute(j, X[j], w_router, self.route_ws, side, False)
+                ready[j].record(side)
+            if replay(i):
+                main.wait_event(ready[i])
+            self._backward(i, w_router, w1, w2, dY[i], main)
+            done[i].record(main)
+        main.wait_stream(side)

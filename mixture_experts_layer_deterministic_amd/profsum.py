@@ -36,7 +36,7 @@ KERNELS = [
     (r"perm_scan_kernel", "perm_scan", "permute.hip"),
     (r"perm_place_kernel", "perm_place", "permute.hip"),
     (r"wgrad_sched_kernel", "wgrad_sched", "wgrad.hip"),
-    (r"expand_big_rows_kernel", "wgrad_expand", "wgrad.hip"),
+    (r"expand_big_rows_kernel", "bwd_gate_wgrad_expand", "wgrad.hip"),
     (r"sched_build_kernel", "sched_build", "gemm.hip"),
     (r"dma_kernel<moe::DmaGateUp>", "fwd_gateup_big", "gemm.hip"),
     (r"dma_kernel<moe::DmaDown>", "fwd_down_big", "gemm.hip"),

@@ -43,11 +43,21 @@ def test_query_sizes_follow_the_shapes():
     (16, 256, 128, 65, 128),  # k > 64
     (300000, 7168, 8, 1, 128),  # T * d >= 2^31 (32-bit row offsets)
     (600000, 256, 8, 1, 2048),  # T * 2I >= 2^31 (32-bit byte offsets into an expert's dH)
+    (16, 65536, 8, 2, 65536),   # one expert's W1 bytes (4 I d) >= 2^31
+    (16, 32768, 8, 2, 16384),   # 4 I d = 2^31 exactly
+    (150000, 7168, 8, 2, 128),  # T*k*d >= 2^31 (all rows may go to one expert)
+    (300000, 256, 8, 2, 2048),  # T*k*2I >= 2^31
 ])
 def test_query_rejects_bad_shapes(shape):
     with pytest.raises(m.MoeError) as ei:
         m.moe_query(m.make_cfg(*shape))
     assert ei.value.status == -1
+
+
+def test_query_accepts_the_largest_expert_weights_below_the_limit():
+    # 4 I d = 2^31 - 2^22 < 2^31: accepted (host only; nothing is allocated or launched)
+    s = m.moe_query(m.make_cfg(16, 32768 - 256, 8, 2, 16384 + 128))
+    assert s.ring_slot > 0
 
 
 def _fake(addr=1 << 20):
@@ -98,6 +108,24 @@ def test_entry_points_reject_bad_arguments_before_launching():
                           p, s.saved, p, p, p, p, null, p, 0, p, s.workspace, None) == -1
 
 
+def test_static_permute_checks_its_fixed_scratch_before_launching():
+    L = m.lib()
+    p = _fake()
+    # 4 (nb E + nb + T k) bytes beyond the 4 MiB fixed scratch: refused on the host
+    big = m.make_cfg(300000, 256, 1024, 4, 128)
+    sb = m.moe_query(big)
+    assert L.moe_permute_static(ctypes.byref(big), p, p, p, sb.ring_slot, 0, p, p, p, p, p,
+                                None) == -5
+    cfg = m.make_cfg(64, 256, 8, 2, 128)
+    s = m.moe_query(cfg)
+    # a null status word, and a ring too small for the slot
+    assert L.moe_permute_static(ctypes.byref(cfg), p, p, p, s.ring_slot, 0, p, p, p, p, None,
+                                None) == -1
+    assert L.moe_permute_static(ctypes.byref(cfg), p, p, p, s.ring_slot, 1, p, p, p, p, p,
+                                None) == -2
+    assert m.MOE_STATIC_SCRATCH_BYTES == 4 << 20
+
+
 def test_mxfp8_sizes():
     T, d, E, k, I = 2048, 7168, 256, 8, 2048
     s = m.moe_query(m.make_cfg(T, d, E, k, I, m.MOE_PREC_MXFP8))
@@ -113,3 +141,17 @@ def test_status_strings():
     assert m.status_string(0) == "ok"
     assert "ring" in m.status_string(-2)
     assert m.status_string(-99) == "unknown status"
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() != 0,
+                    reason="checks the no-device path; on a GPU host the call would launch")
+def test_entry_points_report_a_missing_device_instead_of_launching():
+    """With valid arguments an entry point reaches its device check; with no HIP device it
+    returns MOE_ERR_HIP and enqueues nothing (on a non-gfx950 device: MOE_ERR_UNSUPPORTED)."""
+    L = m.lib()
+    cfg = m.make_cfg(64, 256, 8, 2, 128)
+    s = m.moe_query(cfg)
+    p = _fake()
+    assert L.moe_route(ctypes.byref(cfg), p, p, p, p, p, p, s.workspace, None) == -4
+    assert L.moe_permute(ctypes.byref(cfg), p, p, p, s.ring_slot, 0, p, p, p, p, p,
+                         s.workspace, None) == -4

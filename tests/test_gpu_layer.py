@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import workload
+from mixture_experts_layer_deterministic_amd.layer import Macrobatch
 from tests._gpu import (DEV, MoeLayer, _announce, _np, assert_bitwise_equal, check_parity, m,
                         outputs, run_gpu, run_oracle)
 from tests._util import assert_act, assert_grad
@@ -132,6 +133,22 @@ def test_large_experts_on_the_256_tile_kernels_and_accumulation():
         assert torch.equal(g, 2 * g0)
 
 
+def test_caller_routing_may_repeat_an_expert_within_a_token():
+    """Given routing whose rows name one expert twice for a third of the tokens: each row is its
+    own position, so the expert receives both rows, and the layer still matches the oracle."""
+    T, d, E, k, I = 300, 256, 6, 2, 128
+    _announce(f"[repeat] T={T} d={d} E={E} k={k} I={I}, a third of the tokens repeat an expert")
+    inp = workload.make_inputs("local_zipf", seed=12, device=DEV, T=T, d=d, E=E, k=k, I=I)
+    rng = np.random.default_rng(12)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    idx[::3, 1] = idx[::3, 0]
+    inp["topk_idx"] = torch.from_numpy(idx).to(DEV)
+    inp["topk_w"] = torch.from_numpy(rng.random((T, k)).astype(np.float32)).to(DEV)
+    L = run_gpu(inp)
+    f, b = run_oracle(inp)
+    check_parity(L, inp, f, b)
+
+
 def test_zero_router_and_duplicate_router_rows():
     _announce("[ties] zero router, duplicate rows")
     inp = workload.make_inputs("tiny", seed=5, device=DEV)
@@ -212,3 +229,44 @@ def test_streaming_microbatches_with_ring_replay():
     assert_grad("dW1 (sum)", _np(L.dw1), dW1)
     assert_grad("dW2 (sum)", _np(L.dw2), dW2)
     assert_grad("dWr (sum)", _np(L.dwr), dWr)
+
+
+def _macro_outputs(mb):
+    outs = []
+    for b in mb.mb:
+        outs += [b[n].clone() for n in ("topk_idx", "topk_w", "counts", "offsets", "row_src",
+                                         "tk_row", "y", "dx", "d_topk_w")]
+    return outs + [mb.dw1.clone(), mb.dw2.clone(), mb.dwr.clone()]
+
+
+def test_macrobatch_overlap_matches_the_serial_walk_and_the_oracle():
+    """The macrobatch runner with the next microbatch's routing and permutation (and, in
+    backward, the next replay) on a second stream: bitwise equal to the serial ring walk, and
+    equal to the oracle per microbatch (Y, dX) and summed (dW1, dW2, dWr)."""
+    nmb = 5
+    _announce(f"[macrobatch] {nmb} microbatches, 2-slot ring, serial vs two streams")
+    inp = workload.make_inputs("stream", seed=14, device=DEV, T=96, d=256, E=16, k=4, I=128,
+                               microbatches=nmb)
+    c = inp["cfg"]
+    T, d, E, k, I = c["T"], c["d"], c["E"], c["k"], c["I"]
+    slot = m.moe_query(m.make_cfg(T, d, E, k, I)).ring_slot
+    runs = []
+    for overlap in (False, True, True):
+        mb = Macrobatch(T, d, E, k, I, nmb, 2 * slot, device=DEV, overlap=overlap)
+        assert mb.S == 2
+        mb.run(inp["X"], inp["Wr"], inp["W1"], inp["W2"], inp["dY"])
+        torch.cuda.synchronize()
+        runs.append(_macro_outputs(mb))
+    assert_bitwise_equal(runs[0], runs[1])
+    assert_bitwise_equal(runs[0], runs[2])
+    X, W1, W2, dY, Wr = (_np(inp[n]) for n in ("X", "W1", "W2", "dY", "Wr"))
+    dW1 = dW2 = dWr = 0
+    for i in range(nmb):
+        f = oracle.forward(X[i], W1, W2, Wr=Wr, k=k)
+        b = oracle.backward(f, X[i], W1, W2, dY[i], Wr=Wr)
+        assert_act(f"Y[{i}]", _np(mb.mb[i]["y"]), f["Y"])
+        assert_act(f"dX[{i}]", _np(mb.mb[i]["dx"]), b["dX"])
+        dW1, dW2, dWr = dW1 + b["dW1"], dW2 + b["dW2"], dWr + b["dWr"]
+    assert_grad("dW1 (sum)", _np(mb.dw1), dW1)
+    assert_grad("dW2 (sum)", _np(mb.dw2), dW2)
+    assert_grad("dWr (sum)", _np(mb.dwr), dWr)

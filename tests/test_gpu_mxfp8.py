@@ -200,3 +200,79 @@ def test_mxfp8_quantiser_edge_values_are_bit_exact():
     q, sc = oracle.mx.quantize(Xn[row_src // k])
     np.testing.assert_array_equal(_np(scales), sc)
     np.testing.assert_array_equal(_np(codes), q)
+
+
+def test_mxfp8_big_expert_wgrad_with_accumulation():
+    """One expert of 700 rows (the gate wgrad's big-expert kernel, fed the exact bf16 image of
+    the ring's fp8 rows through the dXp buffer), beside small and empty experts, in MXFP8 mode:
+    parity with the MXFP8 oracle, then a second backward with accumulate=1 must double every
+    weight gradient exactly."""
+    counts = [700, 300, 0, 24]
+    _announce(f"[mxfp8] big expert {counts}, d=512 I=256 k=1, accumulate")
+    E, d, I = len(counts), 512, 256
+    T = sum(counts)
+    inp = workload.make_inputs("local_zipf", seed=13, device=DEV, T=T, d=d, E=E, I=I,
+                               precision="mxfp8")
+    idx = np.repeat(np.arange(E, dtype=np.int32), counts)
+    np.random.default_rng(13).shuffle(idx)
+    inp["topk_idx"] = torch.from_numpy(idx.reshape(T, 1)).to(DEV)
+    L = run_gpu(inp)
+    f, b = run_oracle(inp)
+    assert list(f["counts"]) == counts
+    check_parity(L, inp, f, b, tol_act=TOL_MX, tol_grad=TOL_MX)
+    first = [g.clone() for g in (L.dw1, L.dw2)]
+    L.backward(None, inp["W1"], inp["W2"], inp["dY"], accumulate=True)
+    torch.cuda.synchronize()
+    for g0, g in zip(first, (L.dw1, L.dw2)):
+        assert torch.equal(g, 2 * g0)
+
+
+def test_mxfp8_local_zipf_full_size_sampled_parity():
+    """The full local expert slice in MXFP8 mode (16,384 rows, d=7168, I=2048, one expert over
+    40%): the ring's codes and scales bit-exact on sampled positions, the heaviest and the
+    lightest expert's dW1 and dW2, and sampled tokens of those two experts, against the MXFP8
+    oracle; then a second run bitwise equal to the first."""
+    _announce("[mxfp8] local_zipf 16384 rows d=7168 E=8 k=1 I=2048 seed 0, MXFP8")
+    inp = workload.make_inputs("local_zipf", seed=0, device=DEV, precision="mxfp8")
+    L = run_gpu(inp)
+    X, dY = _np(inp["X"]), _np(inp["dY"])
+    idx, w = _np(inp["topk_idx"]), _np(inp["topk_w"])
+    counts, offsets, row_src, tk_row = oracle.permute(idx, 8)
+    for n, want in (("counts", counts), ("offsets", offsets), ("row_src", row_src),
+                    ("tk_row", tk_row)):
+        np.testing.assert_array_equal(_np(getattr(L, n)), want, err_msg=n)
+    pos = np.unique(np.concatenate([[0, len(row_src) - 1],
+                                    np.random.default_rng(7).choice(len(row_src), 256)]))
+    codes, scales = L.xp()
+    q, sc = oracle.mx.quantize(X[row_src[pos]])
+    p_dev = torch.from_numpy(pos).to(DEV)
+    np.testing.assert_array_equal(_np(codes[p_dev]), q)
+    np.testing.assert_array_equal(_np(scales[p_dev]), sc)
+    _announce("  permutation and sampled ring codes bit-exact")
+    nonempty = np.flatnonzero(counts)
+    heavy = int(np.argmax(counts))
+    light = int(nonempty[np.argmin(counts[nonempty])])
+    W1h, W2h = workload.HostExperts(inp["W1"]), workload.HostExperts(inp["W2"])
+    fe = oracle.forward(X, W1h, W2h, topk_idx=idx, topk_w=w, experts=[heavy, light],
+                        precision="mxfp8")
+    be = oracle.backward(fe, X, W1h, W2h, dY, experts=[heavy, light])
+    for i, e in enumerate((heavy, light)):
+        assert_grad(f"dW1[{e}] ({counts[e]} rows)", _np(L.dw1[e]), be["dW1"][i], TOL_MX)
+        assert_grad(f"dW2[{e}] ({counts[e]} rows)", _np(L.dw2[e]), be["dW2"][i], TOL_MX)
+    _announce("  heaviest and lightest experts' weight gradients done")
+    rng = np.random.default_rng(8)
+    tok = np.unique(np.concatenate([rng.choice(np.flatnonzero(idx[:, 0] == e), 8, replace=False)
+                                    for e in (heavy, light)]))
+    t_dev = torch.from_numpy(tok).to(DEV)
+    rows = tk_row[tok]
+    assert_act("Y[tokens]", _np(L.y[t_dev]), fe["Y"][tok], TOL_MX)
+    assert_act("dX[tokens]", _np(L.dx[t_dev]), be["dX"][tok], TOL_MX)
+    assert_grad("d_topk_w[tokens]", _np(L.d_topk_w[t_dev]), be["dw"][tok], TOL_MX)
+    r_dev = torch.from_numpy(rows).to(DEV)
+    assert_act("H[rows]", _np(L.H()[r_dev]), fe["H"][rows], TOL_MX)
+    assert_act("dH[rows]", _np(L.dH()[r_dev]), be["dH"][rows], TOL_MX)
+    ref = outputs(L, False)
+    del L
+    torch.cuda.empty_cache()
+    assert_bitwise_equal(ref, outputs(run_gpu(inp), False, clone=False))
+    _announce("  two full-size MXFP8 runs bitwise identical")

@@ -1,17 +1,15 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py times.
 
-At these sizes the oracle cannot redo the whole layer in seconds, so each output is checked
-where the oracle can compute it piece by piece:
-* Routing (fp32 logits in the stated order, top-k, weights) and the permutation maps are
-  recomputed for every token and compared bit for bit (weights within 1e-6). So is the permuted
-  token copy.
-* Y, dX, d_topk_w and the saved H and A rows are checked on sampled tokens. Each depends only on
-  its own token, so the oracle runs on those tokens alone.
-* dW1 and dW2 are checked on sampled experts. The oracle routes every token but does the
-  expert math of those experts only.
-* dWr is checked against dlogits^T X, formed in float64 from the layer's own d_topk_w, whose
-  sampled rows are oracle-checked, and from its routing weights.
-Two runs, and the persistent grid, must agree bitwise at the DeepSeek-V3 shape.
+The oracle walks the experts one at a time (``oracle.layer``): it keeps every per-row
+intermediate and hands over one expert's weight gradients at a time, so it covers every token
+of the full workloads in host memory:
+* routing (fp32 logits in the stated order, top-k, weights) and the permutation maps, bit for
+  bit (weights within 1e-6), and the permuted token copy;
+* every token's Y, dX and d_topk_w, and every row's H, A, O, dH and dXp;
+* dWr against the oracle's own dlogits^T X;
+* dW1 and dW2 of sampled experts (all experts of the local slice).
+Two runs, and the persistent grid, must agree bitwise at the DeepSeek-V3 shape; two runs must
+agree bitwise on the local slice and on the streaming macrobatch as well.
 """
 import numpy as np
 import pytest
@@ -32,96 +30,61 @@ def _sample(n_total, n, seed):
     return np.unique(np.concatenate([[0, n_total - 1], pick])).astype(np.int64)
 
 
-def _check_routing_and_permutation(L, inp, X):
-    cfg = inp["cfg"]
-    E, k = cfg["E"], cfg["k"]
-    if "Wr" in inp:
-        logits = oracle.router_logits_fp32(X, _np(inp["Wr"]))
-        np.testing.assert_array_equal(_np(L.logits), logits)
-        idx, w = oracle.route_topk(logits, k)
-        np.testing.assert_array_equal(_np(L.topk_idx), idx)
-        np.testing.assert_allclose(_np(L.topk_w), w, rtol=0, atol=1e-6)
-    else:
-        idx = _np(inp["topk_idx"])
-    counts, offsets, row_src, tk_row = oracle.permute(idx, E)
-    np.testing.assert_array_equal(_np(L.counts), counts)
-    np.testing.assert_array_equal(_np(L.offsets), offsets)
-    np.testing.assert_array_equal(_np(L.row_src), row_src)
-    np.testing.assert_array_equal(_np(L.tk_row), tk_row)
-    return counts
-
-
 def _check_xp(L, X_dev, k, slot=0):
     src = L.row_src.long() // k
     assert torch.equal(L.xp(slot).view(torch.int16), X_dev[src].view(torch.int16))
 
 
-def _check_tokens(L, inp, X, dY, tok, W1h, W2h):
-    """Per-token outputs on the sampled tokens against the oracle run on those tokens alone."""
-    k = inp["cfg"]["k"]
+def _whole_layer(L, inp, check_experts, tol_act=None, tol_grad=None):
+    """Every output of one GPU step against oracle.layer on the same inputs."""
+    cfg = inp["cfg"]
+    k = cfg["k"]
+    X, dY = _np(inp["X"]), _np(inp["dY"])
+    W1h, W2h = workload.HostExperts(inp["W1"]), workload.HostExperts(inp["W2"])
+    kw = dict(Wr=_np(inp["Wr"]), k=k) if "Wr" in inp else dict(
+        topk_idx=_np(inp["topk_idx"]), topk_w=_np(inp["topk_w"]))
+    prec = "mxfp8" if cfg.get("precision") == "mxfp8" else "bf16"
+    ta = {} if tol_act is None else {"tol": tol_act}
+    tg = {} if tol_grad is None else {"tol": tol_grad}
+    checked = []
+
+    def on_expert(e, dW1, dW2):
+        if e in check_experts:
+            assert_grad(f"dW1[{e}]", _np(L.dw1[e]), dW1, **tg)
+            assert_grad(f"dW2[{e}]", _np(L.dw2[e]), dW2, **tg)
+            checked.append(e)
+        if e % 32 == 31:
+            _announce(f"  oracle: experts 0..{e} done")
+
+    lay = oracle.layer(X, W1h, W2h, dY, precision=prec, on_expert=on_expert, **kw)
+    assert sorted(checked) == sorted(check_experts)
     if "Wr" in inp:
-        Wr = _np(inp["Wr"])
-        f = oracle.forward(X[tok], W1h, W2h, Wr=Wr, k=k)
-        b = oracle.backward(f, X[tok], W1h, W2h, dY[tok], Wr=Wr)
-    else:
-        f = oracle.forward(X[tok], W1h, W2h, topk_idx=_np(inp["topk_idx"])[tok],
-                           topk_w=_np(inp["topk_w"])[tok])
-        b = oracle.backward(f, X[tok], W1h, W2h, dY[tok])
-    t_dev = torch.from_numpy(tok).to(DEV)
-    assert_act("Y[tokens]", _np(L.y[t_dev]), f["Y"])
-    assert_act("dX[tokens]", _np(L.dx[t_dev]), b["dX"])
-    assert_grad("d_topk_w[tokens]", _np(L.d_topk_w[t_dev]), b["dw"])
-    rows = (tok[:, None] * k + np.arange(k)).reshape(-1)
-    pos = L.tk_row[torch.from_numpy(rows).to(DEV)].long()
-    sub = f["tk_row"][np.arange(len(tok) * k)]
-    assert_act("H[rows]", _np(L.H()[pos]), f["H"][sub])
-    assert_act("A[rows]", _np(L.A()[pos]), f["A"][sub])
-
-
-def _check_experts(L, inp, X, dY, experts, W1h, W2h):
-    """dW1 and dW2 of the listed experts against the oracle (all tokens routed, expert math of
-    those experts only)."""
-    k = inp["cfg"]["k"]
+        np.testing.assert_array_equal(_np(L.logits), lay["logits"])
+        np.testing.assert_array_equal(_np(L.topk_idx), lay["idx"])
+        np.testing.assert_allclose(_np(L.topk_w), lay["w"], rtol=0, atol=1e-6)
+    for n in ("counts", "offsets", "row_src", "tk_row"):
+        np.testing.assert_array_equal(_np(getattr(L, n)), lay[n], err_msg=n)
+    _announce("  routing and permutation bit-exact over every token")
+    for n, got in (("H", L.H()), ("A", L.A()), ("O", L.O()), ("dH", L.dH()), ("dXp", L.dXp())):
+        assert_act(f"{n} (every row)", _np(got), lay[n], **ta)
+    assert_act("Y (every token)", _np(L.y), lay["Y"], **ta)
+    assert_act("dX (every token)", _np(L.dx), lay["dX"], **ta)
+    assert_grad("d_topk_w (every token)", _np(L.d_topk_w), lay["dw"], **tg)
     if "Wr" in inp:
-        Wr = _np(inp["Wr"])
-        f = oracle.forward(X, W1h, W2h, Wr=Wr, k=k, experts=experts)
-        b = oracle.backward(f, X, W1h, W2h, dY, Wr=Wr, experts=experts)
-    else:
-        f = oracle.forward(X, W1h, W2h, topk_idx=_np(inp["topk_idx"]),
-                           topk_w=_np(inp["topk_w"]), experts=experts)
-        b = oracle.backward(f, X, W1h, W2h, dY, experts=experts)
-    for i, e in enumerate(experts):
-        assert_grad(f"dW1[{e}]", _np(L.dw1[e]), b["dW1"][i])
-        assert_grad(f"dW2[{e}]", _np(L.dw2[e]), b["dW2"][i])
-    return b
+        assert_grad("dWr (oracle dlogits)", _np(L.dwr), lay["dWr"], **tg)
+    return lay
 
 
-def _check_dwr(L, X):
-    """dWr = dlogits^T X, with dlogit_j = w_j (dw_j - sum_i w_i dw_i) from the layer's own
-    (sample-checked) d_topk_w and routing weights, in float64."""
-    w = _np(L.topk_w).astype(np.float64)
-    dw = _np(L.d_topk_w).astype(np.float64)
-    idx = _np(L.topk_idx)
-    dl = w * (dw - np.sum(w * dw, axis=1, keepdims=True))
-    E = L.E
-    dlogits = np.zeros((X.shape[0], E))
-    np.put_along_axis(dlogits, idx, dl, axis=1)
-    assert_grad("dWr", _np(L.dwr), dlogits.T @ X.astype(np.float64))
-
-
-def test_dsv3_full_size_parity():
-    _announce("[full] dsv3 T=2048 d=7168 E=256 k=8 I=2048 seed 0, one-shot grids")
+def test_dsv3_every_token_against_the_oracle():
+    _announce("[full] dsv3 T=2048 d=7168 E=256 k=8 I=2048 seed 0, one-shot grids, every token")
     inp = workload.make_inputs("dsv3", seed=0, device=DEV)
     L = run_gpu(inp)
-    X, dY = _np(inp["X"]), _np(inp["dY"])
-    counts = _check_routing_and_permutation(L, inp, X)
     _check_xp(L, inp["X"], inp["cfg"]["k"])
-    W1h, W2h = workload.HostExperts(inp["W1"]), workload.HostExperts(inp["W2"])
-    _check_tokens(L, inp, X, dY, _sample(X.shape[0], 10, seed=1), W1h, W2h)
+    counts = _np(L.counts)
     heavy = int(np.argmax(counts))
     light = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
-    _check_experts(L, inp, X, dY, sorted({heavy, light, 0}), W1h, W2h)
-    _check_dwr(L, X)
+    experts = sorted({heavy, light} | set(range(0, 256, 16)))
+    _whole_layer(L, inp, experts)
 
 
 def test_dsv3_two_runs_and_persistent_grid_are_bitwise_identical():
@@ -139,29 +102,31 @@ def test_dsv3_two_runs_and_persistent_grid_are_bitwise_identical():
     assert_bitwise_equal(ref, outputs(L, True, clone=False))
 
 
-def test_local_zipf_full_size_parity():
-    _announce("[full] local_zipf 16384 rows d=7168 E=8 k=1 I=2048 seed 0")
+def test_local_zipf_every_row_against_the_oracle():
+    _announce("[full] local_zipf 16384 rows d=7168 E=8 k=1 I=2048 seed 0, every row")
     inp = workload.make_inputs("local_zipf", seed=0, device=DEV)
     L = run_gpu(inp)
-    X, dY = _np(inp["X"]), _np(inp["dY"])
-    counts = _check_routing_and_permutation(L, inp, X)
-    assert counts.sum() == X.shape[0] and np.count_nonzero(counts == 0) == 3
+    counts = _np(L.counts)
+    assert counts.sum() == inp["cfg"]["T"] and np.count_nonzero(counts == 0) == 3
+    assert counts.max() > 0.4 * inp["cfg"]["T"]
     _check_xp(L, inp["X"], 1)
-    W1h, W2h = workload.HostExperts(inp["W1"]), workload.HostExperts(inp["W2"])
-    _check_tokens(L, inp, X, dY, _sample(X.shape[0], 12, seed=2), W1h, W2h)
-    nonempty = np.flatnonzero(counts)
-    light = int(nonempty[np.argmin(counts[nonempty])])
-    empty = int(np.flatnonzero(counts == 0)[0])
-    _check_experts(L, inp, X, dY, sorted({light, empty}), W1h, W2h)
-    assert torch.count_nonzero(L.dw1[empty]) == 0 and torch.count_nonzero(L.dw2[empty]) == 0
+    _whole_layer(L, inp, list(range(8)))
+    for e in np.flatnonzero(counts == 0):
+        assert torch.count_nonzero(L.dw1[e]) == 0 and torch.count_nonzero(L.dw2[e]) == 0
 
 
-def test_stream_full_size_ring_walk():
-    """8 microbatches of 2368 tokens through a 512 MiB ring (2 slots). Forward runs 0..7;
-    backward runs 7..0, re-permuting microbatches whose slot was overwritten, and accumulates
-    the weight gradients."""
-    _announce("[full] stream 8 x T=2368 d=4096 E=512 k=10 I=1024, 512 MiB ring, seed 0")
-    inp = workload.make_inputs("stream", seed=0, device=DEV)
+def test_local_zipf_two_runs_are_bitwise_identical():
+    _announce("[full] local_zipf determinism: two runs")
+    inp = workload.make_inputs("local_zipf", seed=4, device=DEV)
+    ref = outputs(run_gpu(inp), False)
+    torch.cuda.empty_cache()
+    assert_bitwise_equal(ref, outputs(run_gpu(inp), False, clone=False))
+
+
+def _stream_run(inp):
+    """8 microbatches through a 2-slot ring: forward 0..7, then backward 7..0, re-permuting the
+    microbatches whose slot was overwritten (replay), with the weight gradients accumulated.
+    Returns the layer, the per-microbatch routing, Y, dX and d_topk_w."""
     cfg = inp["cfg"]
     T, d, E, k, I, nmb = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"], cfg["microbatches"]
     S = cfg["ring_bytes"] // m.moe_query(m.make_cfg(T, d, E, k, I)).ring_slot
@@ -189,10 +154,21 @@ def test_stream_full_size_ring_walk():
         dxs[i] = L.dx.clone()
         dtws[i] = L.d_topk_w.clone()
     torch.cuda.synchronize()
+    return L, routing, ys, dxs, dtws
+
+
+def test_stream_full_size_ring_walk():
+    """8 microbatches of 2368 tokens through a 512 MiB ring (2 slots), backward in reverse with
+    replay and accumulated weight gradients, against the oracle on sampled tokens and experts."""
+    _announce("[full] stream 8 x T=2368 d=4096 E=512 k=10 I=1024, 512 MiB ring, seed 0")
+    inp = workload.make_inputs("stream", seed=0, device=DEV)
+    cfg = inp["cfg"]
+    T, k, nmb = cfg["T"], cfg["k"], cfg["microbatches"]
+    L, routing, ys, dxs, dtws = _stream_run(inp)
     Wr = _np(inp["Wr"])
     W1h, W2h = workload.HostExperts(inp["W1"]), workload.HostExperts(inp["W2"])
     experts = None
-    dW1 = dW2 = None
+    dW1 = dW2 = dWr = None
     for i in range(nmb):
         X, dY = _np(inp["X"][i]), _np(inp["dY"][i])
         tok = _sample(T, 4, seed=10 + i)
@@ -211,6 +187,28 @@ def test_stream_full_size_ring_walk():
         be = oracle.backward(fe, X, W1h, W2h, dY, Wr=Wr, experts=experts)
         dW1 = be["dW1"] if dW1 is None else dW1 + be["dW1"]
         dW2 = be["dW2"] if dW2 is None else dW2 + be["dW2"]
+        # dWr sums every microbatch's dlogits^T X: the oracle's dlogits need every row's dw, so
+        # this uses the GPU's d_topk_w, which the sampled tokens above pin to the oracle's
+        w = _np(routing[i][1]).astype(np.float64)
+        dl = oracle.router_backward(w, _np(routing[i][0]), _np(dtws[i]).astype(np.float64),
+                                    cfg["E"])
+        dWr = dl.T @ X if dWr is None else dWr + dl.T @ X
+        _announce(f"  microbatch {i} checked")
     for j, e in enumerate(experts):
         assert_grad(f"dW1[{e}] (sum of 8)", _np(L.dw1[e]), dW1[j])
         assert_grad(f"dW2[{e}] (sum of 8)", _np(L.dw2[e]), dW2[j])
+    assert_grad("dWr (sum of 8)", _np(L.dwr), dWr)
+
+
+def test_stream_two_macrobatch_runs_are_bitwise_identical():
+    _announce("[full] stream determinism: the whole 8-microbatch ring walk twice")
+    inp = workload.make_inputs("stream", seed=1, device=DEV)
+    runs = []
+    for _ in range(2):
+        L, routing, ys, dxs, dtws = _stream_run(inp)
+        flat = [t for r in routing for t in r] + ys + dxs + dtws
+        flat += [L.dw1.clone(), L.dw2.clone(), L.dwr.clone()]
+        runs.append(flat)
+        del L
+        torch.cuda.empty_cache()
+    assert_bitwise_equal(runs[0], runs[1])
