@@ -31,7 +31,10 @@ def _static_call(L, x, slot):
 
 
 def _compare(L, x, slot=0):
-    L.ring.fill_(0xA5)  # bytes neither call writes (padding, a skipped row) then match too
+    # bytes neither call writes (padding, a skipped row's position) then match too
+    L.ring.fill_(0xA5)
+    for n in ("counts", "offsets", "row_src", "tk_row"):
+        getattr(L, n).fill_(-7)
     L.permute(x, slot=slot)
     torch.cuda.synchronize()
     got = _static_call(L, x, slot)
