@@ -488,6 +488,13 @@ def run_tiny(m, MoeLayer, workload, dev, stream, args):
                                     "ms_per_step_median": round(eager["ms_median"], 4),
                                     "host_ms_per_step": round(eager["t_host"] * 1e3
                                                               / max(args.steps, 50), 4)}}
+    # the forward as one launch (moe_forward_fused), then the same backward
+    fused = time_steps(lambda: L.step(X, Wr, W1, W2, dY, stream=stream, fused=True), stream,
+                       max(args.steps, 50), args.warmup)
+    out["fused_forward"] = {"tokens_per_s": round(cfg["T"] / (fused["ms"] * 1e-3), 1),
+                            "ms_per_step": round(fused["ms"], 4),
+                            "ms_per_step_median": round(fused["ms_median"], 4)}
+    out["forward_only_ms"] = forward_only(L, X, Wr, W1, W2, stream, args)
     try:
         side = torch.cuda.Stream()
         side.wait_stream(stream)
@@ -510,24 +517,41 @@ def run_tiny(m, MoeLayer, workload, dev, stream, args):
     return out
 
 
+def forward_only(L, X, Wr, W1, W2, stream, args):
+    """The forward alone: route + permute + forward as separate launches, and as one."""
+    sep = time_steps(lambda: (L.route(X, Wr, stream), L.permute(X, 0, stream),
+                              L.forward(W1, W2, 0, stream=stream)), stream,
+                     max(args.steps, 50), args.warmup)
+    one = time_steps(lambda: L.forward_fused(X, Wr, W1, W2, 0, stream=stream), stream,
+                     max(args.steps, 50), args.warmup)
+    return {"separate": round(sep["ms"], 4), "fused": round(one["ms"], 4)}
+
+
 def run_stream(workload, dev, stream, args):
     """The streaming macrobatch: 8 microbatches of 2368 tokens through one 512 MiB ring (2
     slots), forward 0..7, backward 7..0 with the overwritten slots replayed. Tokens/s counts the
     8 x 2368 tokens of a macrobatch, replay included; serial, then with the next microbatch's
-    routing and permutation on a second stream."""
+    routing and permutation on a second stream, and with each microbatch's forward as one
+    launch."""
     from mixture_experts_layer_deterministic_amd.layer import Macrobatch
     cfg = workload.config("stream")
     inp = workload.make_inputs("stream", seed=args.seed, device=dev)
     n = cfg["microbatches"]
     tokens = n * cfg["T"]
     out = {"microbatches": n, "T": cfg["T"], "tokens": tokens, "ring_bytes": cfg["ring_bytes"]}
-    for overlap in (False, True):
+    # one microbatch's forward alone, as separate launches and as one
+    from mixture_experts_layer_deterministic_amd.layer import MoeLayer
+    Lm = MoeLayer(cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"], device=dev)
+    out["microbatch_forward_only_ms"] = forward_only(Lm, inp["X"][0], inp["Wr"], inp["W1"],
+                                                     inp["W2"], stream, args)
+    del Lm
+    for mode in ("serial", "overlap", "fused_forward"):
         mb = Macrobatch(cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"], n, cfg["ring_bytes"],
-                        device=dev, overlap=overlap)
+                        device=dev, overlap=mode == "overlap", fused=mode == "fused_forward")
         out["ring_slots"] = mb.S
         r = time_steps(lambda: mb.run(inp["X"], inp["Wr"], inp["W1"], inp["W2"], inp["dY"],
                                       stream), stream, max(3, args.steps // 4), 1)
-        out["overlap" if overlap else "serial"] = {
+        out[mode] = {
             "tokens_per_s": round(tokens / (r["ms"] * 1e-3), 1),
             "ms_per_macrobatch": round(r["ms"], 3),
             "ms_per_macrobatch_median": round(r["ms_median"], 3)}

@@ -58,7 +58,11 @@ enum {
 
 /* Device status word (first 4 bytes of the workspace). moe_permute clears it and ORs bits into
  * it; the caller may read it after its own synchronisation. */
-enum { MOE_DEVICE_BAD_EXPERT_INDEX = 1 /* a topk_idx entry outside [0, E): that row is skipped */ };
+enum {
+    MOE_DEVICE_BAD_EXPERT_INDEX = 1, /* a topk_idx entry outside [0, E): that row is skipped */
+    MOE_DEVICE_BARRIER_TIMEOUT = 2   /* moe_forward_fused: a grid barrier waited ~2 s and gave up
+                                        (the results of that call are not valid) */
+};
 
 /* Layer shape and mode. Constraints checked on the host: T >= 1; 1 <= k <= E <= 1024; k <= 64;
  * d % 256 == 0 (the GEMMs have no masked K tail: K steps of 64 and 256-wide tiles along d);
@@ -224,6 +228,29 @@ int moe_forward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t
                 const void* w1, const void* w2, const void* wq, size_t wq_bytes, void* y,
                 void* saved, size_t saved_bytes, void* workspace, size_t ws_bytes,
                 moe_stream_t stream);
+
+/*
+ * moe_forward_fused - moe_route, moe_permute and moe_forward in ONE kernel launch (BF16 mode).
+ *
+ * The pages' layer is one persistent kernel that fuses all of its steps (MarkTechPost, "Cursor
+ * Open-Sources Mixture-of-Kittens (MoK)": introduction, and the closing paragraph of "Three
+ * design decisions that matter"). This call runs the router, the permutation into ring slot
+ * `slot`, both grouped GEMMs and the combine as phases of one cooperatively launched grid
+ * (every workgroup resident) that meet at grid-wide barriers, so a small layer pays one launch
+ * instead of about a dozen. It writes everything the three calls write (logits, topk_idx,
+ * topk_w, counts, offsets, row_src, tk_row, the ring slot, H and A in `saved`, O in the
+ * workspace, y, the device status word), with the same values: bit for bit when no expert
+ * receives 256 rows or more; otherwise the down projection of those experts' rows sums its K
+ * chunks from another start (the separate path gives such blocks a 256 x 256 tile), which
+ * changes their O and y in the last bits only. Arguments and errors are those of the three
+ * calls; MXFP8 mode returns MOE_ERR_UNSUPPORTED. The grid barriers keep their state in a
+ * device variable of the library, one per GPU: fused calls that overlap on one GPU race.
+ */
+int moe_forward_fused(const moe_cfg* cfg, const void* x, const void* w_router, float* logits,
+                      int32_t* topk_idx, float* topk_w, void* ring, size_t ring_bytes,
+                      int32_t slot, int32_t* counts, int32_t* offsets, int32_t* row_src,
+                      int32_t* tk_row, const void* w1, const void* w2, void* y, void* saved,
+                      size_t saved_bytes, void* workspace, size_t ws_bytes, moe_stream_t stream);
 
 /*
  * moe_backward - gradients of L = <y, dy> with respect to x, the router weight, w1, w2 and the

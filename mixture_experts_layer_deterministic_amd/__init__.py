@@ -26,6 +26,7 @@ MOE_PREC_BF16 = 0
 MOE_PREC_MXFP8 = 1
 MOE_FLAG_PERSISTENT = 1
 MOE_DEVICE_BAD_EXPERT_INDEX = 1
+MOE_DEVICE_BARRIER_TIMEOUT = 2
 
 
 class MoeError(RuntimeError):
@@ -61,6 +62,8 @@ _SIGS = {
     "moe_backward": [ctypes.POINTER(MoeCfg), _P, _SZ, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                      _SZ, _P, _SZ, _P, _P, _P, _P, _P, _P, _I32, _P, _SZ, _P],
     "moe_quantize_weights": [ctypes.POINTER(MoeCfg), _P, _P, _P, _SZ, _P],
+    "moe_forward_fused": [ctypes.POINTER(MoeCfg), _P, _P, _P, _P, _P, _P, _SZ, _I32, _P, _P, _P,
+                          _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P],
     "moe_permute_static": [ctypes.POINTER(MoeCfg), _P, _P, _P, _SZ, _I32, _P, _P, _P, _P, _P,
                            _P],
 }
@@ -182,6 +185,16 @@ def moe_forward(cfg, ring, slot, offsets, tk_row, topk_w, w1, w2, wq, y, saved, 
                              _ptr(tk_row), _ptr(topk_w), _ptr(w1), _ptr(w2), _ptr(wq),
                              _wq_bytes(wq), _ptr(y), _ptr(saved), _nbytes(saved),
                              _ptr(workspace), _nbytes(workspace), _stream(stream)), "moe_forward")
+
+
+def moe_forward_fused(cfg, x, w_router, logits, topk_idx, topk_w, ring, slot, counts, offsets,
+                      row_src, tk_row, w1, w2, y, saved, workspace, stream=None):
+    _check(lib().moe_forward_fused(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(logits),
+                                   _ptr(topk_idx), _ptr(topk_w), _ptr(ring), _nbytes(ring), slot,
+                                   _ptr(counts), _ptr(offsets), _ptr(row_src), _ptr(tk_row),
+                                   _ptr(w1), _ptr(w2), _ptr(y), _ptr(saved), _nbytes(saved),
+                                   _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "moe_forward_fused")
 
 
 def moe_backward(cfg, ring, slot, offsets, row_src, tk_row, topk_idx, topk_w, w_router, w1, w2,

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
 SOURCES = ["api.cpp", "router.hip", "permute.hip", "gemm.hip", "wgrad.hip", "mx.hip",
-           "elementwise.hip"]
+           "elementwise.hip", "fused.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 ops are disabled for the device code; the host pass warns that it does not know

@@ -413,6 +413,64 @@ int moe_forward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t
   return L.status();
 }
 
+int moe_forward_fused(const moe_cfg* cfg, const void* x, const void* w_router, float* logits,
+                      int32_t* topk_idx, float* topk_w, void* ring, size_t ring_bytes,
+                      int32_t slot, int32_t* counts, int32_t* offsets, int32_t* row_src,
+                      int32_t* tk_row, const void* w1, const void* w2, void* y, void* saved,
+                      size_t saved_bytes, void* workspace, size_t ws_bytes, moe_stream_t stream) {
+  int st = check_mode(cfg);
+  if (st) return st;
+  if (cfg->precision != MOE_PREC_BF16) return MOE_ERR_UNSUPPORTED;
+  const Layout Y = layout(cfg);
+  if (!aligned16(x) || !aligned16(w_router) || !aligned4(logits) || !aligned4(topk_idx) ||
+      !aligned4(topk_w) || !aligned4(counts) || !aligned4(offsets) || !aligned4(row_src) ||
+      !aligned4(tk_row) || !aligned16(w1) || !aligned16(w2) || !aligned16(y) ||
+      !aligned16(saved) || !aligned16(workspace))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ring(Y, ring, ring_bytes, slot))) return st;
+  if (saved_bytes < Y.saved_total || ws_bytes < Y.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if ((st = check_device())) return st;
+  const int Tk = cfg->T * cfg->k;
+  FusedFwdParams p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.wr = static_cast<const uint16_t*>(w_router);
+  p.w32 = at<float>(workspace, Y.wr32);
+  p.logits = logits;
+  p.topk_idx = topk_idx;
+  p.topk_w = topk_w;
+  p.blk_cnt = at<int32_t>(workspace, Y.blk_cnt);
+  p.rank = at<int32_t>(workspace, Y.rank);
+  p.blk_flag = at<int32_t>(workspace, Y.blk_flag);
+  p.counts = counts;
+  p.offsets = offsets;
+  p.status = at<int32_t>(workspace, Y.status);
+  p.row_src = row_src;
+  p.tk_row = tk_row;
+  p.xp = at<uint16_t>(ring, (size_t)slot * Y.slot);
+  p.sched = at<int2>(workspace, Y.sched);  // the 128-row block table opens the region
+  p.w1 = static_cast<const uint16_t*>(w1);
+  p.w2 = static_cast<const uint16_t*>(w2);
+  p.H = at<uint16_t>(saved, Y.H);
+  p.A = at<uint16_t>(saved, Y.A);
+  p.O = at<uint16_t>(workspace, Y.O);
+  p.y = static_cast<uint16_t*>(y);
+  p.T = cfg->T;
+  p.d = cfg->d;
+  p.E = cfg->E;
+  p.k = cfg->k;
+  p.I = cfg->I;
+  p.nb = Y.nb;
+  // tokens per placement block, as moe_permute's launch chooses them
+  int tpb = 1024 / (cfg->d / 8);
+  if (tpb < 1) tpb = 1;
+  if (tpb > 256 / cfg->k) tpb = 256 / cfg->k;
+  p.tpb = tpb;
+  (void)Tk;
+  Launches L;
+  L(launch_fused_forward(p, static_cast<hipStream_t>(stream)));
+  return L.status();
+}
+
 int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t slot,
                  const int32_t* offsets, const int32_t* row_src, const int32_t* tk_row,
                  const int32_t* topk_idx, const float* topk_w, const void* w_router,

@@ -153,6 +153,34 @@ hipError_t launch_fwd_down(const GemmFwdDownArgs& a, bool persistent, hipStream_
 hipError_t launch_bwd_down_dgrad(const GemmBwdDownDgradArgs& a, bool persistent, hipStream_t s);
 hipError_t launch_bwd_gate_dgrad(const GemmBwdGateDgradArgs& a, bool persistent, hipStream_t s);
 
+// fused.hip: route, permute and forward in one cooperative launch (BF16)
+struct FusedFwdParams {
+  const uint16_t* x;
+  const uint16_t* wr;
+  float* w32;
+  float* logits;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* blk_cnt;
+  int32_t* rank;
+  int32_t* blk_flag;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* status;
+  int32_t* row_src;
+  int32_t* tk_row;
+  uint16_t* xp;
+  int2* sched;  // the 128-row block table: count, then (expert, first row)
+  const uint16_t* w1;
+  const uint16_t* w2;
+  uint16_t* H;
+  uint16_t* A;
+  uint16_t* O;
+  uint16_t* y;
+  int T, d, E, k, I, nb, tpb;
+};
+hipError_t launch_fused_forward(const FusedFwdParams& p, hipStream_t s);
+
 // wgrad.hip
 constexpr int kWgradBM = 256;         // dW rows per task stripe
 constexpr int kWgradBN = 128;         // dW columns per tile

@@ -10,6 +10,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "permute.h"
 
 namespace moe {
 
@@ -38,8 +39,6 @@ hipError_t static_perm_scratch(void** ptr) {
   return hipSuccess;
 }
 
-// Block b owns rows [256 b, 256 b + 256): per-expert counts of the block, and each row's rank
-// among the block's earlier rows of the same expert (a direct count, so it is stable).
 __global__ void __launch_bounds__(kPermRows) perm_hist_kernel(const int32_t* __restrict__ idx,
                                                               int Tk, int E,
                                                               int32_t* __restrict__ blk_cnt,
@@ -47,27 +46,7 @@ __global__ void __launch_bounds__(kPermRows) perm_hist_kernel(const int32_t* __r
                                                               int32_t* __restrict__ blk_flag) {
   __shared__ int sh_e[kPermRows];
   __shared__ int sh_cnt[1024];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int r = b * kPermRows + tid;
-  for (int i = tid; i < E; i += kPermRows) sh_cnt[i] = 0;
-  int e = -1;
-  int bad = 0;
-  if (r < Tk) {
-    e = idx[r];
-    if (e < 0 || e >= E) {
-      bad = 1;
-      e = -1;
-    }
-  }
-  sh_e[tid] = e;
-  __syncthreads();
-  if (e >= 0) atomicAdd(&sh_cnt[e], 1);  // integer counts: the result is order independent
-  int rk = 0;
-  for (int j = 0; j < tid; ++j) rk += (sh_e[j] == e);
-  const int any_bad = __syncthreads_or(bad);
-  if (r < Tk) rank[r] = e >= 0 ? rk : -1;
-  for (int i = tid; i < E; i += kPermRows) blk_cnt[(size_t)b * E + i] = sh_cnt[i];
-  if (tid == 0) blk_flag[b] = any_bad;
+  perm_hist_block(blockIdx.x, idx, Tk, E, blk_cnt, rank, blk_flag, sh_e, sh_cnt);
 }
 
 // One workgroup: column-wise exclusive scan of the block counts (block order), expert totals,
@@ -121,12 +100,6 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ b
   if (e == 0) status[0] = f ? 1 : 0;
 }
 
-// Block b owns tokens [tpb b, tpb b + tpb) and their rows r = t*k + j (tpb*k <= 256). It
-// places every row, then copies each token slice ONCE from x and stores it to the token's k
-// positions: Xp[pos(t*k+j)] = x[t]. With MX the stored image is the token's MXFP8 form: E4M3
-// codes xp8 [T*k, d] and one scale per 32 along d in xps [T*k, d/32]. Four consecutive lanes
-// own one 32-block (d is a multiple of 32, so blocks never straddle rows), and every lane runs
-// the shuffles.
 template <bool MX>
 __global__ void __launch_bounds__(256) perm_place_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ rank,
@@ -134,84 +107,8 @@ __global__ void __launch_bounds__(256) perm_place_kernel(
     int32_t* __restrict__ tk_row, const uint16_t* __restrict__ x, uint16_t* __restrict__ xp,
     uint8_t* __restrict__ xp8, uint8_t* __restrict__ xps, int d, int tpb) {
   __shared__ int sh_pos[256];
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * tpb;
-  const int Tk = T * k;
-  const int nr = tpb * k;
-  if (tid < nr) {
-    const int r = t0 * k + tid;
-    int pos = -1;
-    if (r < Tk) {
-      const int rk = rank[r];
-      if (rk >= 0) {
-        pos = blk_base[(size_t)(r / kPermRows) * E + idx[r]] + rk;
-        row_src[pos] = r;
-      }
-      tk_row[r] = pos;
-    }
-    sh_pos[tid] = pos;
-  }
-  __syncthreads();
-  const int vpr = d / 8;
-  const int n = tpb * vpr;
-  if constexpr (!MX) {
-    // U token slices loaded together, then each stored to its k positions
-    constexpr int U = 4;
-    for (int i0 = 0; i0 < n; i0 += 256 * U) {
-      uint4 val[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + 256 * u + tid;
-        const int t = t0 + i / vpr;
-        val[u] = i < n && t < T
-                     ? *reinterpret_cast<const uint4*>(x + (size_t)t * d + (i % vpr) * 8)
-                     : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + 256 * u + tid;
-        const int tt = i / vpr, v = i % vpr;
-        if (i >= n || t0 + tt >= T) continue;
-        for (int j = 0; j < k; ++j) {
-          const int pos = sh_pos[tt * k + j];
-          if (pos >= 0) *reinterpret_cast<uint4*>(xp + (size_t)pos * d + v * 8) = val[u];
-        }
-      }
-    }
-    return;
-  }
-  for (int i0 = 0; i0 < n; i0 += 256) {
-    const int i = i0 + tid;
-    const int tt = i / vpr, v = i % vpr;
-    const int t = t0 + tt;
-    const bool live = i < n && t < T;
-    const uint4 val =
-        live ? *reinterpret_cast<const uint4*>(x + (size_t)t * d + v * 8) : make_uint4(0, 0, 0, 0);
-    const uint32_t xw[4] = {val.x, val.y, val.z, val.w};
-    float f[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f[2 * q] = bf2f_lo(xw[q]);
-      f[2 * q + 1] = bf2f_hi(xw[q]);
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    const uint32_t code = mx_scale_code(amax);
-    const float inv = mx_inv_scale(code);
-    uint2 o;
-    o.x = e4m3x2(f[0] * inv, f[1] * inv) | (e4m3x2(f[2] * inv, f[3] * inv) << 16);
-    o.y = e4m3x2(f[4] * inv, f[5] * inv) | (e4m3x2(f[6] * inv, f[7] * inv) << 16);
-    if (!live) continue;
-    for (int j = 0; j < k; ++j) {
-      const int pos = sh_pos[tt * k + j];
-      if (pos < 0) continue;
-      *reinterpret_cast<uint2*>(xp8 + (size_t)pos * d + v * 8) = o;
-      if ((v & 3) == 0) xps[(size_t)pos * (d / 32) + v / 4] = static_cast<uint8_t>(code);
-    }
-  }
+  perm_place_block<MX>(blockIdx.x, idx, rank, blk_base, T, E, k, row_src, tk_row, x, xp, xp8,
+                       xps, d, tpb, sh_pos);
 }
 
 hipError_t launch_perm_hist(const int32_t* idx, int Tk, int E, int32_t* blk_cnt, int32_t* rank,

@@ -7,7 +7,8 @@ from __future__ import annotations
 import torch
 
 from . import (MOE_FLAG_PERSISTENT, MOE_PREC_BF16, MOE_PREC_MXFP8, make_cfg, moe_backward,
-               moe_forward, moe_permute, moe_query, moe_quantize_weights, moe_route)
+               moe_forward, moe_forward_fused, moe_permute, moe_query, moe_quantize_weights,
+               moe_route)
 
 
 class MoeLayer:
@@ -101,6 +102,13 @@ class MoeLayer:
                     self.wq, self.y, self.saved if saved is None else saved, self.workspace,
                     stream)
 
+    def forward_fused(self, x, w_router, w1, w2, slot=0, saved=None, stream=None):
+        """route + permute + forward in one kernel launch (moe_forward_fused)."""
+        moe_forward_fused(self.cfg, x, w_router, self.logits, self.topk_idx, self.topk_w,
+                          self.ring, slot, self.counts, self.offsets, self.row_src, self.tk_row,
+                          w1, w2, self.y, self.saved if saved is None else saved, self.workspace,
+                          stream)
+
     def backward(self, w_router, w1, w2, dy, slot=0, accumulate=False, saved=None, stream=None):
         moe_backward(self.cfg, self.ring, slot, self.offsets, self.row_src, self.tk_row,
                      self.topk_idx, self.topk_w, w_router, w1, w2, self.wq,
@@ -108,8 +116,13 @@ class MoeLayer:
                      self.dwr if w_router is not None else None, self.d_topk_w, accumulate,
                      self.workspace, stream)
 
-    def step(self, x, w_router, w1, w2, dy, slot=0, stream=None):
-        """One fwd+bwd pass: route (when w_router is given), permute, forward, backward."""
+    def step(self, x, w_router, w1, w2, dy, slot=0, stream=None, fused=False):
+        """One fwd+bwd pass: route (when w_router is given), permute, forward, backward. With
+        ``fused`` the first three run as one launch (moe_forward_fused)."""
+        if fused:
+            self.forward_fused(x, w_router, w1, w2, slot, stream=stream)
+            self.backward(w_router, w1, w2, dy, slot, stream=stream)
+            return
         if w_router is not None:
             self.route(x, w_router, stream)
         self.permute(x, slot, stream)
@@ -132,7 +145,7 @@ class Macrobatch:
     sees exactly the same inputs, so results are bitwise those of the serial walk.
     """
 
-    def __init__(self, T, d, E, k, I, n, ring_bytes, device="cuda", overlap=False):
+    def __init__(self, T, d, E, k, I, n, ring_bytes, device="cuda", overlap=False, fused=False):
         self.T, self.d, self.E, self.k, self.I, self.n = T, d, E, k, I, n
         self.main = MoeLayer(T, d, E, k, I, device=device, ring_slots=1)
         s = self.main.sizes
@@ -141,6 +154,7 @@ class Macrobatch:
             raise ValueError("ring_bytes holds no ring slot")
         self.main.ring = torch.empty(self.S * s.ring_slot, dtype=torch.uint8, device=device)
         self.overlap = overlap
+        self.fused = fused  # each microbatch's route + permute + forward as one launch
         dev = torch.device(device)
         i32, f32, bf = torch.int32, torch.float32, torch.bfloat16
         Tk = T * k
@@ -197,6 +211,18 @@ class Macrobatch:
         main = torch.cuda.current_stream() if stream is None else stream
         n, S = self.n, self.S
         replay = lambda i: i < n - S  # its slot was overwritten by microbatch i + S
+        if self.fused:
+            for i in range(n):
+                b, L = self.mb[i], self.main
+                moe_forward_fused(L.cfg, X[i], w_router, b["logits"], b["topk_idx"],
+                                  b["topk_w"], L.ring, i % S, b["counts"], b["offsets"],
+                                  b["row_src"], b["tk_row"], w1, w2, b["y"], b["saved"],
+                                  L.workspace, main)
+            for i in reversed(range(n)):
+                if replay(i):
+                    self._route_permute(i, X[i], w_router, self.main.workspace, main, False)
+                self._backward(i, w_router, w1, w2, dY[i], main)
+            return
         if not self.overlap or S < 2:  # one slot: each microbatch waits for the previous one
             for i in range(n):
                 self._route_permute(i, X[i], w_router, self.main.workspace, main)

@@ -155,3 +155,22 @@ def test_entry_points_report_a_missing_device_instead_of_launching():
     assert L.moe_route(ctypes.byref(cfg), p, p, p, p, p, p, s.workspace, None) == -4
     assert L.moe_permute(ctypes.byref(cfg), p, p, p, s.ring_slot, 0, p, p, p, p, p,
                          s.workspace, None) == -4
+
+
+def test_fused_forward_checks_arguments_before_launching():
+    L = m.lib()
+    cfg = m.make_cfg(64, 256, 8, 2, 128)
+    s = m.moe_query(cfg)
+    p = _fake()
+    args = lambda c, ring_bytes, slot, saved, ws: (ctypes.byref(c), p, p, p, p, p, p, ring_bytes,
+                                                   slot, p, p, p, p, p, p, p, p, saved, p, ws, None)
+    # MXFP8 mode is not provided by the single-launch forward
+    cfg8 = m.make_cfg(64, 256, 8, 2, 128, m.MOE_PREC_MXFP8)
+    s8 = m.moe_query(cfg8)
+    assert L.moe_forward_fused(*args(cfg8, s8.ring_slot, 0, s8.saved, s8.workspace)) == -3
+    assert L.moe_forward_fused(*args(cfg, s.ring_slot - 1, 0, s.saved, s.workspace)) == -2
+    assert L.moe_forward_fused(*args(cfg, s.ring_slot, 0, s.saved - 1, s.workspace)) == -5
+    assert L.moe_forward_fused(*args(cfg, s.ring_slot, 0, s.saved, s.workspace - 1)) == -5
+    bad = list(args(cfg, s.ring_slot, 0, s.saved, s.workspace))
+    bad[2] = None  # no router weight
+    assert L.moe_forward_fused(*bad) == -1
