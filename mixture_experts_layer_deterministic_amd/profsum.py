@@ -27,40 +27,49 @@ import re
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
-# rocprofv3 kernel-name pattern -> (bench name, source file)
+# rocprofv3 kernel-name pattern -> (bench name, the sources it is built from besides the
+# common headers)
+R = ("router.hip", "router.h")
+P = ("permute.hip", "permute.h")
+G = ("gemm.hip", "gemm_tiles.h")
+W = ("wgrad.hip",)
+M = ("mx.hip",)
+C = ("elementwise.hip", "combine.h")
 KERNELS = [
-    (r"widen_router_kernel", "widen_router", "router.hip"),
-    (r"router_logits_kernel", "router_logits", "router.hip"),
-    (r"router_topk_kernel", "router_topk", "router.hip"),
-    (r"perm_hist_kernel", "perm_hist", "permute.hip"),
-    (r"perm_scan_kernel", "perm_scan", "permute.hip"),
-    (r"perm_place_kernel", "perm_place", "permute.hip"),
-    (r"wgrad_sched_kernel", "wgrad_sched", "wgrad.hip"),
-    (r"expand_big_rows_kernel", "bwd_gate_wgrad_expand", "wgrad.hip"),
-    (r"sched_build_kernel", "sched_build", "gemm.hip"),
-    (r"dma_kernel<moe::DmaGateUp>", "fwd_gateup_big", "gemm.hip"),
-    (r"dma_kernel<moe::DmaDown>", "fwd_down_big", "gemm.hip"),
-    (r"dma_kernel<moe::DmaGateDgrad>", "bwd_gate_dgrad_big", "gemm.hip"),
-    (r"dma_kernel<moe::DmaDownDgrad>", "bwd_down_dgrad_big", "gemm.hip"),
-    (r"gg_kernel<moe::FwdGateUp", "fwd_gateup", "gemm.hip"),
-    (r"gg_kernel<moe::FwdDown", "fwd_down", "gemm.hip"),
-    (r"gg_kernel<moe::BwdDownDgrad", "bwd_down_dgrad", "gemm.hip"),
-    (r"gg_kernel<moe::BwdGateDgrad", "bwd_gate_dgrad", "gemm.hip"),
-    (r"gg_kernel<moe::MxFwdGateUp", "fwd_gateup", "gemm.hip"),
-    (r"gg_kernel<moe::MxFwdDown", "fwd_down", "gemm.hip"),
-    (r"gg_kernel<moe::MxBwdDownDgrad", "bwd_down_dgrad", "gemm.hip"),
-    (r"gg_kernel<moe::MxBwdGateDgrad", "bwd_gate_dgrad", "gemm.hip"),
-    (r"DmaWgrad<(true|false), false>", "bwd_down_wgrad_big", "wgrad.hip"),
-    (r"DmaWgrad<(true|false), true>", "bwd_gate_wgrad_big", "wgrad.hip"),
-    (r"wgrad_kernel<(true|false), false", "bwd_down_wgrad", "wgrad.hip"),
-    (r"wgrad_kernel<(true|false), true", "bwd_gate_wgrad", "wgrad.hip"),
-    (r"moe::combine_kernel", "combine", "elementwise.hip"),
-    (r"dw_router_kernel", "dw_router", "elementwise.hip"),
-    (r"uncombine_kernel", "uncombine", "elementwise.hip"),
-    (r"dwr_kernel", "dwr", "elementwise.hip"),
-    (r"scale_gather_kernel", "scale_gather", "mx.hip"),
-    (r"quant_rows_kernel", "quant_rows", "mx.hip"),
-    (r"quant_weight_kernel", "quant_weight", "mx.hip"),
+    (r"widen_router_kernel", "widen_router", R),
+    (r"router_logits_kernel", "router_logits", R),
+    (r"router_topk_kernel", "router_topk", R),
+    (r"perm_hist_kernel", "perm_hist", P),
+    (r"perm_scan_kernel", "perm_scan", P),
+    (r"perm_place_kernel", "perm_place", P),
+    (r"wgrad_sched_kernel", "wgrad_sched", W),
+    (r"expand_big_rows_kernel", "bwd_gate_wgrad_expand", W),
+    (r"sched_build_kernel", "sched_build", G),
+    (r"dma_kernel<moe::DmaGateUp>", "fwd_gateup_big", G),
+    (r"dma_kernel<moe::DmaDown>", "fwd_down_big", G),
+    (r"dma_kernel<moe::DmaGateDgrad>", "bwd_gate_dgrad_big", G),
+    (r"dma_kernel<moe::DmaDownDgrad>", "bwd_down_dgrad_big", G),
+    (r"gg_kernel<moe::FwdGateUp", "fwd_gateup", G),
+    (r"gg_kernel<moe::FwdDown", "fwd_down", G),
+    (r"gg_kernel<moe::BwdDownDgrad", "bwd_down_dgrad", G),
+    (r"gg_kernel<moe::BwdGateDgrad", "bwd_gate_dgrad", G),
+    (r"gg_kernel<moe::MxFwdGateUp", "fwd_gateup", G),
+    (r"gg_kernel<moe::MxFwdDown", "fwd_down", G),
+    (r"gg_kernel<moe::MxBwdDownDgrad", "bwd_down_dgrad", G),
+    (r"gg_kernel<moe::MxBwdGateDgrad", "bwd_gate_dgrad", G),
+    (r"DmaWgrad<(true|false), false>", "bwd_down_wgrad_big", W),
+    (r"DmaWgrad<(true|false), true>", "bwd_gate_wgrad_big", W),
+    (r"wgrad_kernel<(true|false), false", "bwd_down_wgrad", W),
+    (r"wgrad_kernel<(true|false), true", "bwd_gate_wgrad", W),
+    (r"moe::combine_kernel", "combine", C),
+    (r"dw_router_kernel", "dw_router", C),
+    (r"uncombine_kernel", "uncombine", C),
+    (r"dwr_kernel", "dwr", C),
+    (r"scale_gather_kernel", "scale_gather", M),
+    (r"quant_rows_kernel", "quant_rows", M),
+    (r"quant_weight_kernel", "quant_weight", M),
+    (r"fused_forward_kernel", "fused_forward",
+     ("fused.hip", "router.h", "permute.h", "gemm_tiles.h", "combine.h")),
 ]
 COMMON_SOURCES = ("common.h", "dma.h", "kernels.h")
 
@@ -75,9 +84,9 @@ def bench_name(raw: str):
     return None
 
 
-def source_hash(src: str) -> str:
+def source_hash(srcs) -> str:
     h = hashlib.sha256()
-    for f in (src, *COMMON_SOURCES):
+    for f in (*srcs, *COMMON_SOURCES):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -110,6 +119,8 @@ def main():
     ap.add_argument("--command", required=True)
     ap.add_argument("--out", required=True)
     ap.add_argument("--traffic")
+    ap.add_argument("--bench-log", help="bench.py output of the profiled run: its JSON line's "
+                                        "roofline kernel is quoted next to the trace")
     args = ap.parse_args()
 
     stats = {}
@@ -131,6 +142,17 @@ def main():
 
     lines = [f"# rocprofv3 kernel summary: {args.workload}", "",
              f"Command: `{args.command}`", ""]
+    if args.bench_log:
+        import json as _json
+        line = [ln for ln in open(args.bench_log) if ln.startswith("{")][-1]
+        b = _json.loads(line)
+        r = b["roofline"]
+        per = r["us_per_step"] / max(r["launches_per_step"], 1)
+        lines += [f"The bench line of the same run: roofline kernel `{r['kernel']}`, "
+                  f"{r['us_per_step']:.1f} us per step over {r['launches_per_step']} launch(es) "
+                  f"(HIP events on the layer's stream), {b['ms_per_step']:.2f} ms per step under "
+                  f"the profiler; the trace's average for `{r['kernel']}` is below.", ""]
+        del per
     if fetch is not None:
         lines += [f"HBM bytes: FETCH_SIZE x {fs:.3f} and WRITE_SIZE x {ws:.3f}, the factors that "
                   f"map a plain {args.calib_mib} MiB device copy onto its true size.", ""]

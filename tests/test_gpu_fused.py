@@ -93,3 +93,32 @@ def test_fused_forward_with_large_experts_matches_the_oracle():
     torch.cuda.synchronize()
     f, bk = run_oracle(inp)
     check_parity(L, inp, f, bk)
+
+
+def test_fused_step_in_a_captured_graph_replays_exactly():
+    """The fused forward and the backward captured once into a HIP graph: three replays, with
+    eager work and synchronisations between them, each equal to the eager step bit for bit."""
+    _announce("[fused] tiny step captured in a HIP graph, three replays")
+    inp = workload.make_inputs("tiny", seed=2, device=DEV)
+    X, Wr, W1, W2, dY = (inp[n] for n in ("X", "Wr", "W1", "W2", "dY"))
+    L = _layer(inp)
+    L.step(X, Wr, W1, W2, dY, fused=True)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (L.y, L.dx, L.dw1, L.dw2, L.dwr, L.d_topk_w)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        L.step(X, Wr, W1, W2, dY, fused=True)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            L.step(X, Wr, W1, W2, dY, fused=True)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for t in (L.y, L.dx, L.dw1, L.dw2, L.dwr, L.d_topk_w):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert L.device_status() == 0
+        assert_bitwise_equal(want, [L.y, L.dx, L.dw1, L.dw2, L.dwr, L.d_topk_w])
