@@ -35,6 +35,12 @@ readings = {
                    "SwiGLU backward), flowing on to the logits, the router weight and the input",
     "storage_bf16": "H = [g|u], A, O, Y, dH, dXp, dX stored as bf16; A is rounded once from "
                     "the unrounded g, u; every later step reads the stored value",
+    "mxfp8_wgrad": "MXFP8 weight gradients (an option of MXFP8 mode): both operands of each "
+                   "weight-gradient product are MXFP8 images quantised along its reduction "
+                   "axis, the positions of one expert segment, in blocks of 32 consecutive "
+                   "positions from the segment's first (the last block holds the rest): dW2 "
+                   "from (w dY) and A, dW1 from dH and the MXFP8 image of Xp the ring holds "
+                   "(quantised again, along the positions)",
     "mxfp8": "MXFP8 mode (MarkTechPost, closing paragraph of 'Three design decisions that "
              "matter': BF16 and MXFP8 modes): every expert GEMM of forward and dgrad takes both "
              "operands as MXFP8 images quantised along that GEMM's reduction axis - Xp and W1 "
@@ -176,7 +182,7 @@ def expert_forward(x, w1, w2, *, rnd, mxq=_identity):
     return h, a, o
 
 
-def expert_backward(x, dy, wv, h, a, o_used, w1, w2, *, rnd, mxmode=False):
+def expert_backward(x, dy, wv, h, a, o_used, w1, w2, *, rnd, mxmode=False, mx_wgrad=False):
     """One expert's backward over its rows (readings "router_grad", "storage_bf16", "mxfp8").
 
     x and dy are the rows' tokens and upstream gradients, wv [c, 1] their routing weights, h and
@@ -188,6 +194,8 @@ def expert_backward(x, dy, wv, h, a, o_used, w1, w2, *, rnd, mxmode=False):
     * dXp = dH W1_e, stored (rounded).
     Over the expert's rows: dW2_e = sum (w dy) outer a, dW1_e = sum dH outer x. In MXFP8 mode both
     dgrad GEMMs take MXFP8 images along their reduction axes and x enters dW1 as its MXFP8 image.
+    With mx_wgrad (reading "mxfp8_wgrad") both weight-gradient products take MXFP8 images of
+    their operands along the expert's positions.
     Returns (dw [c], dH [c, 2I], dXp [c, d], dW1_e [2I, d], dW2_e [d, I]).
     """
     I = h.shape[1] // 2
@@ -210,8 +218,13 @@ def expert_backward(x, dy, wv, h, a, o_used, w1, w2, *, rnd, mxmode=False):
         dxp = rnd(mx.qdq(dh) @ mx.qdq(w1.T).T)  # W1 [2I, d] quantised along 2I
     else:
         dxp = rnd(dh @ w1)
-    dW2 = (wv * dy).T @ a
-    dW1 = dh.T @ (mx.qdq(x) if mxmode else x)
+    xr = mx.qdq(x) if mxmode else x
+    if mx_wgrad:
+        dW2 = mx.qdq_segment(wv * dy).T @ mx.qdq_segment(a)
+        dW1 = mx.qdq_segment(dh).T @ mx.qdq_segment(xr)
+    else:
+        dW2 = (wv * dy).T @ a
+        dW1 = dh.T @ xr
     return dw, dh, dxp, dW1, dW2
 
 
@@ -288,7 +301,7 @@ def forward(X, W1, W2, *, Wr=None, k=None, topk_idx=None, topk_w=None,
     return out
 
 
-def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None) -> dict:
+def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None, wgrad="bf16") -> dict:
     """Backward pass: gradients of L = <Y, dY> with respect to every input.
 
     Per row at position pos (token t, slot j, expert e, weight w), by ``expert_backward``:
@@ -307,9 +320,12 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None) -> dict:
     ``experts`` limits the expert math to a subset (rows of other experts stay NaN). dW1 and dW2
     then hold one block per listed expert, in the order listed in out["experts"].
     In MXFP8 mode (reading "mxfp8") both dgrad GEMMs take MXFP8 images of their operands, dw is
-    <dA', A>, and Xp enters dW1 and dWr as its MXFP8 image.
+    <dA', A>, and Xp enters dW1 and dWr as its MXFP8 image. wgrad="mxfp8" (MXFP8 mode only,
+    reading "mxfp8_wgrad") quantises both operands of both weight-gradient products along the
+    expert's positions.
     """
     mxmode = fwd.get("precision", "bf16") == "mxfp8"
+    assert wgrad in ("bf16", "mxfp8") and (wgrad == "bf16" or mxmode), "MXFP8 wgrad needs MXFP8"
     X = np.asarray(X, np.float64)
     dY = np.asarray(dY, np.float64)
     T, d = X.shape
@@ -334,7 +350,7 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None) -> dict:
         tok = rows // k
         dw_pos[p0:p1], dH[p0:p1], dXp[p0:p1], dW1[slot], dW2[slot] = expert_backward(
             X[tok], dY[tok], w_flat[rows][:, None], fwd["H"][p0:p1], fwd["A"][p0:p1],
-            fwd["O"][p0:p1], W1[e], W2[e], rnd=rnd, mxmode=mxmode)
+            fwd["O"][p0:p1], W1[e], W2[e], rnd=rnd, mxmode=mxmode, mx_wgrad=wgrad == "mxfp8")
     dw = dw_pos[tk_row].reshape(T, k)
     dXsum = gather_sum(dXp, None, tk_row, k)
     out = dict(dw=dw, dH=dH, dXp=dXp, dW1=dW1, dW2=dW2, experts=ex)
@@ -348,7 +364,7 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None) -> dict:
 
 
 def layer(X, W1, W2, dY, *, Wr=None, k=None, topk_idx=None, topk_w=None, storage="bf16",
-          precision="bf16", on_expert=None) -> dict:
+          precision="bf16", on_expert=None, wgrad="bf16") -> dict:
     """Forward and backward of the whole layer, one expert at a time.
 
     The same steps as ``forward`` followed by ``backward``, in the same order and arithmetic,
@@ -389,7 +405,7 @@ def layer(X, W1, W2, dY, *, Wr=None, k=None, topk_idx=None, topk_w=None, storage
         O[p0:p1] = rnd(o)
         dw_pos[p0:p1], dH[p0:p1], dXp[p0:p1], dW1, dW2 = expert_backward(
             X[tok], dY[tok], w_flat[rows][:, None], H[p0:p1], A[p0:p1], O[p0:p1], w1, w2,
-            rnd=rnd, mxmode=mxmode)
+            rnd=rnd, mxmode=mxmode, mx_wgrad=wgrad == "mxfp8")
         if on_expert is not None:
             on_expert(e, dW1, dW2)
     out = dict(idx=idx, w=w, counts=counts, offsets=offsets, row_src=row_src, tk_row=tk_row,

@@ -100,3 +100,16 @@ def qdq(x, axis=-1) -> np.ndarray:
     """The float64 image of x after MXFP8 quantisation along `axis`."""
     q, sc = quantize(x, axis)
     return dequantize(q, sc, axis)
+
+
+def qdq_segment(x) -> np.ndarray:
+    """The float64 image of x [rows, cols] after MXFP8 quantisation along its ROWS in blocks of
+    32 consecutive rows starting at row 0, the last block holding what is left (fewer than 32
+    rows when rows is not a multiple of 32). Rows are the positions of one expert segment, the
+    reduction axis of a weight-gradient product. The short last block is quantised as if padded
+    with zero rows: zeros change neither its largest magnitude nor any product."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[0]
+    pad = (-n) % BLOCK
+    xp = np.concatenate([x, np.zeros((pad,) + x.shape[1:])], axis=0) if pad else x
+    return qdq(xp, axis=0)[:n]

@@ -214,3 +214,99 @@ def test_mxfp8_layer_stays_within_its_error_bound_of_the_exact_layer(seed):
                        ("dWr", bm["dWr"], be["dWr"])):
         r = rel(a, b)
         assert 1e-3 < r < 0.12, (name, r)
+
+
+# --- MXFP8 weight gradients: quantisation along the positions of each expert segment ----------
+
+def test_segment_quantisation_matches_a_block_by_block_brute_force():
+    """qdq_segment: blocks of 32 rows from row 0, the last one short (45 = 32 + 13 rows). Each
+    block and column: scale from the block's largest magnitude (frexp), elements by brute-force
+    nearest E4M3 value (ties to the even code), saturated to 448."""
+    import math
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((45, 6)) * 2.0 ** rng.integers(-5, 5, (45, 6))
+    got = mx.qdq_segment(x)
+    pos = mx.e4m3_value(np.arange(127))  # non-negative finite E4M3 values, ascending
+    want = np.zeros_like(x)
+    for r0 in range(0, 45, 32):
+        blk = x[r0:r0 + 32]
+        for c in range(6):
+            amax = max(abs(v) for v in blk[:, c])
+            e = math.frexp(amax)[1] - 1 if amax > 0 else None
+            code = 0 if e is None else min(max(e - 8 + 127, 0), 254)
+            scale = 2.0 ** (code - 127)
+            for i, v in enumerate(blk[:, c]):
+                a = min(abs(v) / scale, 448.0)
+                dist = np.abs(pos - a)
+                best = np.flatnonzero(dist == dist.min())
+                q = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+                want[r0 + i, c] = math.copysign(pos[q] * scale, v)
+    np.testing.assert_array_equal(got, want)
+
+
+def _segment_exact(counts, cols, rng):
+    """Rows exact in MXFP8 along the rows within each segment of `counts` rows (blocks of 32
+    from each segment's first row), and the same rows made exact along the columns instead."""
+    parts_r, parts_c = [], []
+    for c in counts:
+        n32 = (c + 31) // 32 * 32
+        codes = rng.integers(0, 127, size=(n32, cols)).astype(np.uint8)
+        codes[::32] = 0x7A
+        sc = rng.integers(115, 125, size=(n32 // 32, cols)).astype(np.uint8)
+        parts_r.append(mx.dequantize(codes, sc, axis=0)[:c])
+        parts_c.append(mx.qdq(rng.standard_normal((c, cols)) * 0.5, axis=1) if cols % 32 == 0
+                       else None)
+    return parts_r, parts_c
+
+
+def test_mxfp8_wgrad_quantises_along_each_expert_segment():
+    """Given routing with segments of 45, 20 and 40 positions (none a multiple of 32, so blocks
+    of later experts start off the 32-row grid of the whole position axis). With w = 1, dY rows
+    and the saved A made exact in MXFP8 along each segment's positions, the MXFP8 dW2 equals the
+    BF16 dW2 bit for bit; made exact along the columns instead, it differs."""
+    rng = np.random.default_rng(10)
+    counts = [45, 20, 40]
+    E, d, I = 3, 64, 32
+    T = sum(counts)
+    idx = np.repeat(np.arange(E, dtype=np.int32), counts)
+    rng.shuffle(idx)
+    idx = idx.reshape(T, 1)
+    w = np.ones((T, 1))
+    X = oracle.bf16_round(rng.standard_normal((T, d)))
+    W1 = oracle.bf16_round(rng.standard_normal((E, 2 * I, d)) * 0.1)
+    W2 = oracle.bf16_round(rng.standard_normal((E, d, I)) * 0.1)
+    f = oracle.forward(X, W1, W2, topk_idx=idx, topk_w=w, precision="mxfp8")
+    rows_dy, _ = _segment_exact(counts, d, rng)
+    rows_a, cols_a = _segment_exact(counts, I, rng)
+    dY = np.zeros((T, d))
+    dY[f["row_src"]] = np.concatenate(rows_dy)  # position p holds token row_src[p] (k = 1)
+    fa = dict(f, A=np.concatenate(rows_a))
+    bb = oracle.backward(fa, X, W1, W2, dY)
+    bm = oracle.backward(fa, X, W1, W2, dY, wgrad="mxfp8")
+    np.testing.assert_array_equal(bm["dW2"], bb["dW2"])
+    assert not np.array_equal(bm["dW1"], bb["dW1"])  # dH and Xp are not exact: dW1 quantises
+    fc = dict(f, A=np.concatenate(cols_a))
+    assert not np.array_equal(oracle.backward(fc, X, W1, W2, dY, wgrad="mxfp8")["dW2"],
+                              oracle.backward(fc, X, W1, W2, dY)["dW2"])
+
+
+@pytest.mark.parametrize("seed", [11, 12])
+def test_mxfp8_wgrad_stays_within_its_error_bound(seed):
+    """Two more quantised operands per weight gradient than the MXFP8 layer's: dW1 and dW2 stay
+    within the same 0.12 relative error of the exact layer (and above 1e-3: they quantise)."""
+    rng = np.random.default_rng(seed)
+    T, d, E, k, I = 80, 128, 5, 2, 64
+    X = oracle.bf16_round(rng.standard_normal((T, d)))
+    W1 = oracle.bf16_round(rng.standard_normal((E, 2 * I, d)) * 0.05)
+    W2 = oracle.bf16_round(rng.standard_normal((E, d, I)) * 0.05)
+    Wr = oracle.bf16_round(rng.standard_normal((E, d)) * 0.05)
+    dY = oracle.bf16_round(rng.standard_normal((T, d)))
+    fe = oracle.forward(X, W1, W2, Wr=Wr, k=k, storage="exact")
+    be = oracle.backward(fe, X, W1, W2, dY, Wr=Wr)
+    fm = oracle.forward(X, W1, W2, Wr=Wr, k=k, precision="mxfp8")
+    bm = oracle.backward(fm, X, W1, W2, dY, Wr=Wr, wgrad="mxfp8")
+    for name in ("dW1", "dW2"):
+        r = np.linalg.norm(bm[name] - be[name]) / np.linalg.norm(be[name])
+        assert 1e-3 < r < 0.12, (name, r)
+    with pytest.raises(AssertionError):
+        oracle.backward(fe, X, W1, W2, dY, Wr=Wr, wgrad="mxfp8")  # MXFP8 mode only
