@@ -36,7 +36,7 @@ MFMA_FP8_TFLOPS = 5000.0   # dense fp8 MFMA (the MXFP8 scaled MFMA), TFLOP/s
 VALU_FP32_TFLOPS = 78.6
 
 
-def algorithmic(cfg, routed=True, accumulate=False, mx=False):
+def algorithmic(cfg, routed=True, accumulate=False, mx=False, mx_wgrad=False):
     """Algorithmic bytes and flops per launch of each kernel: what the method must move and
     compute (each tensor read or written once, no padding, no re-reads). M = T*k rows.
     In MXFP8 mode (`mx`) a quantised tensor of n elements is n code bytes plus n/32 scale
@@ -87,6 +87,13 @@ def algorithmic(cfg, routed=True, accumulate=False, mx=False):
                                2 * M * 2 * I * d)
         if routed:
             b["dwr"] = (q(M * d) + acc * E * d * 4 + M * 4, 2 * M * d)
+        if mx_wgrad:
+            # each operand read once in bf16 (Xp as its MXFP8 image) and quantised along the
+            # positions; the GEMM reads the quantised copies and writes fp32 dW
+            b["bwd_down_wgrad"] = (acc * E * d * I * 4 + T * d * 2 + M * I * 2 + q(M * d)
+                                   + q(M * I), 2 * M * d * I)
+            b["bwd_gate_wgrad"] = (acc * E * 2 * I * d * 4 + M * 2 * I * 2 + q(M * d)
+                                   + q(M * 2 * I) + q(M * d), 2 * M * 2 * I * d)
     return b
 
 
@@ -97,20 +104,20 @@ GEMMS = ("fwd_gateup", "fwd_down", "bwd_down_dgrad", "bwd_down_wgrad", "bwd_gate
 MX_GEMMS = ("fwd_gateup", "fwd_down", "bwd_down_dgrad", "bwd_gate_dgrad")  # scaled fp8 MFMA
 
 
-def mfma_peak(name, mx):
+def mfma_peak(name, mx, mx_wgrad=False):
     """Dense MFMA peak of a GEMM kernel: fp8 for the MXFP8 scaled-MFMA GEMMs, else bf16 (the
-    weight-gradient GEMMs run bf16 MFMA in both modes)."""
-    return MFMA_FP8_TFLOPS if mx and name in MX_GEMMS else MFMA_BF16_TFLOPS
+    weight-gradient GEMMs run bf16 MFMA unless the MXFP8 weight gradients are on)."""
+    return MFMA_FP8_TFLOPS if mx and (name in MX_GEMMS or mx_wgrad) else MFMA_BF16_TFLOPS
 
 
-def kernel_roofline(name, nbytes, flops, us, mx=False):
+def kernel_roofline(name, nbytes, flops, us, mx=False, mx_wgrad=False):
     """Achieved rate against the roofline that bounds the kernel."""
     s = us * 1e-6
     if name == "router_logits":
         ach = flops / s / 1e12
         return {"bound": "alu", "achieved": ach, "peak": VALU_FP32_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / VALU_FP32_TFLOPS}
-    peak = mfma_peak(name, mx)
+    peak = mfma_peak(name, mx, mx_wgrad)
     if flops and name in GEMMS and flops / nbytes > peak * 1e12 / (HBM_GBPS * 1e9):
         ach = flops / s / 1e12
         return {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
@@ -402,6 +409,18 @@ def main():
                 "layer_ms_without_weight_quantize": round(rz["ms"] - rz["quant_ms"], 4),
                 "grouped_gemm": rz["gemm"],
                 "gemm_us": {g: rz["kernels"][g]["us"] for g in GEMMS if g in rz["kernels"]}}
+            # and with the weight gradients in MXFP8 too
+            print("[bench] local expert slice, MXFP8 with MXFP8 weight gradients",
+                  file=sys.stderr, flush=True)
+            rw = run_layer(m, MoeLayer, iz, cz, stream, args, mx=True, mx_wgrad=True)
+            slice_line["mxfp8_wgrad"] = {
+                "ms_per_step": round(rw["ms"], 4),
+                "layer_ms_without_weight_quantize": round(rw["ms"] - rw["quant_ms"], 4),
+                "grouped_gemm": rw["gemm"],
+                "gemm_us": {g: rw["kernels"][g]["us"] for g in GEMMS if g in rw["kernels"]},
+                "wgrad_parts_us": {g: rw["kernels"][g].get("parts_us")
+                                   for g in ("bwd_down_wgrad", "bwd_gate_wgrad")
+                                   if g in rw["kernels"]}}
         if cpu is not None:
             cpu.setdefault("per_config", {})["local_zipf"] = cpu_expert_sample(
                 iz, cz, cz["T"] * cz["k"])
@@ -559,7 +578,8 @@ def run_stream(workload, dev, stream, args):
     return out, inp
 
 
-def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=True):
+def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=True,
+              mx_wgrad=False):
     """Warm up and time `args.steps` layer steps without any per-launch event, then (unless
     `trace` is off) time as many again with the library's per-launch events on the layer's
     stream, for the per-kernel times. In MXFP8 mode each step first quantises the weights."""
@@ -568,7 +588,8 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=T
     dev = inp["X"].device
     routed = "Wr" in inp
     prec = m.MOE_PREC_MXFP8 if mx else m.MOE_PREC_BF16
-    L = MoeLayer(T, d, E, k, I, device=dev, persistent=persistent, precision=prec)
+    L = MoeLayer(T, d, E, k, I, device=dev, persistent=persistent, precision=prec,
+                 mx_wgrad=mx_wgrad)
     wr = inp.get("Wr")
     if not routed:
         L.set_routing(inp["topk_idx"], inp["topk_w"])
@@ -595,7 +616,7 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=T
     del keep
 
     kernels = {}
-    alg = algorithmic(cfg, routed=routed, mx=mx)
+    alg = algorithmic(cfg, routed=routed, mx=mx, mx_wgrad=mx_wgrad)
     if trace and not args.no_trace:
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * per_step * args.steps)]
         for e in ev:
@@ -626,7 +647,7 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=T
         parts = {}
         for n in list(tot):
             base = n
-            for suffix in ("_big", "_expand"):
+            for suffix in ("_big", "_expand", "_qL", "_qR"):
                 if n.endswith(suffix):
                     base = n[:-len(suffix)]
             parts.setdefault(base, {})[n] = tot[n] / args.steps
@@ -634,7 +655,7 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=T
             us = sum(pt.values())
             launches = sum(cnt[p] for p in pt) // args.steps
             nbytes, flops = alg.get(n, (0, 0))
-            r = kernel_roofline(n, nbytes, flops, us, mx) if nbytes else {}
+            r = kernel_roofline(n, nbytes, flops, us, mx, mx_wgrad) if nbytes else {}
             kernels[n] = {"us": round(us, 2), "launches_per_step": launches,
                           "alg_bytes": nbytes, "alg_flops": flops,
                           **{kk: (round(v, 4) if isinstance(v, float) else v)
@@ -649,10 +670,12 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=T
         flops = sum(alg[g][1] for g in GEMMS)
         nbytes = sum(alg[g][0] for g in GEMMS)
         # the time-weighted MFMA peak of the six GEMMs at their own dtypes
-        peak = sum(kernels[g]["us"] * mfma_peak(g, mx) for g in GEMMS if g in kernels) / gemm_us
+        peak = sum(kernels[g]["us"] * mfma_peak(g, mx, mx_wgrad) for g in GEMMS
+                   if g in kernels) / gemm_us
         tf = flops / (gemm_us * 1e-6) / 1e12
         attainable = sum(
-            kernels[g]["us"] * min(mfma_peak(g, mx), HBM_GBPS * 1e9 * alg[g][1] / alg[g][0] / 1e12)
+            kernels[g]["us"] * min(mfma_peak(g, mx, mx_wgrad),
+                                   HBM_GBPS * 1e9 * alg[g][1] / alg[g][0] / 1e12)
             for g in GEMMS if g in kernels) / gemm_us
         gemm = {"tflops": round(tf, 2), "mfma_peak_tflops": round(peak, 1),
                 "frac_mfma_peak": round(tf / peak, 4),

@@ -53,7 +53,8 @@ enum { MOE_PREC_BF16 = 0, MOE_PREC_MXFP8 = 1 };
 
 /* cfg.flags bits */
 enum {
-    MOE_FLAG_PERSISTENT = 1 /* grouped GEMMs as persistent grids walking the schedule table */
+    MOE_FLAG_PERSISTENT = 1, /* grouped GEMMs as persistent grids walking the schedule table */
+    MOE_FLAG_MXFP8_WGRAD = 2 /* MXFP8 mode only: the weight gradients in MXFP8 too (below) */
 };
 
 /* Device status word (first 4 bytes of the workspace). moe_permute clears it and ORs bits into
@@ -80,7 +81,12 @@ enum {
  * to nearest even and saturate to +-448. The forward GEMMs read Xp and W1 quantised along d,
  * and A and W2 along I. The dgrad GEMMs read dY and W2 along d, and dH and W1 along 2I. The
  * weight gradients and dWr read bf16 operands, with Xp taken as the MXFP8 image the ring
- * holds. All accumulation is fp32; outputs are bf16 as in BF16 mode. */
+ * holds. All accumulation is fp32; outputs are bf16 as in BF16 mode.
+ * With MOE_FLAG_MXFP8_WGRAD the two weight gradients take MXFP8 operands as well, quantised
+ * along their reduction axis, the positions of each expert: blocks of 32 consecutive positions
+ * from the expert's first one, the last block holding what is left. dW2 reads w dY (the fp32
+ * product, quantised directly) and A, dW1 reads dH and the ring's MXFP8 image of Xp, each
+ * quantised so. dWr is unchanged. */
 typedef struct moe_cfg {
     int32_t T;         /* tokens entering the layer */
     int32_t d;         /* hidden size */

@@ -3,6 +3,7 @@
 // stream. It never allocates, synchronises or prints.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <mutex>
@@ -25,6 +26,10 @@ struct Layout {
       wg_table1, wg_table2, wr32, total;
   // workspace, MXFP8 only: dY, A and dH quantised along their GEMM's K (codes, scales)
   size_t dyq, dys, aq, aqs, dhq, dhs;
+  // workspace, MXFP8 weight gradients only: padded segment offsets [E + 1], and the two
+  // operands of one weight gradient quantised along the positions, [rows][P] with scales
+  size_t poff, lq, lqs, rq, rqs;
+  int P;
   // saved
   size_t H, A, saved_total;
   // ring slot: bf16 Xp, or MXFP8 Xp codes at 0 and scales at slot_sc
@@ -111,6 +116,14 @@ Layout layout(const moe_cfg* c) {
   L.aqs = take(mxs * Tk * I / 32);
   L.dhq = take(mxs * Tk * 2 * I);
   L.dhs = take(mxs * Tk * 2 * I / 32);
+  const size_t mxw = L.mx && (c->flags & MOE_FLAG_MXFP8_WGRAD) ? 1 : 0;
+  L.P = mxw ? seg_capacity((int)Tk, c->E) : 0;
+  const size_t P = L.P, lrows = std::max(2 * I, d), rrows = std::max(d, I);
+  L.poff = take(mxw * sizeof(int32_t) * (E + 1));
+  L.lq = take(lrows * P);
+  L.lqs = take(lrows * P / 32);
+  L.rq = take(rrows * P);
+  L.rqs = take(rrows * P / 32);
   L.total = o;
   o = 0;
   L.H = take(2 * Tk * 2 * I);
@@ -162,7 +175,9 @@ struct Launches {
 int check_mode(const moe_cfg* c) {
   if (!cfg_ok(c)) return MOE_ERR_INVALID_ARG;
   if (c->precision != MOE_PREC_BF16 && c->precision != MOE_PREC_MXFP8) return MOE_ERR_UNSUPPORTED;
-  if (c->flags & ~MOE_FLAG_PERSISTENT) return MOE_ERR_INVALID_ARG;
+  if (c->flags & ~(MOE_FLAG_PERSISTENT | MOE_FLAG_MXFP8_WGRAD)) return MOE_ERR_INVALID_ARG;
+  if ((c->flags & MOE_FLAG_MXFP8_WGRAD) && c->precision != MOE_PREC_MXFP8)
+    return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -232,7 +247,8 @@ int moe_trace_end(void) {
 }
 
 int moe_query(const moe_cfg* cfg, moe_sizes* out) {
-  if (!out || !cfg_ok(cfg)) return MOE_ERR_INVALID_ARG;
+  if (!out) return MOE_ERR_INVALID_ARG;
+  if (const int st = check_mode(cfg)) return st;
   const Layout L = layout(cfg);
   out->ring_slot = L.slot;
   out->saved = L.saved_total;
@@ -527,18 +543,53 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
                                  pers, s));
     if (!L.err)
       L(launch_dw_router(dwpart, Y.nIt, tk_row, topk_w, cfg->T, k, d_topk_w, dl_pos, routed, s));
-    if (!L.err)
-      L(launch_wgrad({dyw, A, nullptr, nullptr, dw2, offsets, at<int4>(workspace, Y.wg_table2),
-                      wg_count + 1, E, d, I, accumulate, false, "bwd_down_wgrad",
-                      "wgrad_sched_down"},
-                     s));
-    // the gate wgrad goes first: until the gate dgrad writes dXp, that buffer holds the bf16
-    // image of the big experts' fp8 Xp rows for the big-expert wgrad kernel
-    if (!L.err)
-      L(launch_wgrad({dH, nullptr, xp8, xps, dw1, offsets, at<int4>(workspace, Y.wg_table1),
-                      wg_count, E, 2 * I, d, accumulate, true, "bwd_gate_wgrad",
-                      "wgrad_sched_gate", dXp},
-                     s));
+    if (cfg->flags & MOE_FLAG_MXFP8_WGRAD) {
+      // both weight gradients in MXFP8, their operands quantised along each expert's positions
+      int32_t* poff = at<int32_t>(workspace, Y.poff);
+      uint8_t* lq = at<uint8_t>(workspace, Y.lq);
+      uint8_t* lqs = at<uint8_t>(workspace, Y.lqs);
+      uint8_t* rq = at<uint8_t>(workspace, Y.rq);
+      uint8_t* rqs = at<uint8_t>(workspace, Y.rqs);
+      if (!L.err) L(launch_seg_offsets(offsets, E, poff, s));
+      SegOperand wdy, sa, sdh, sxp;
+      wdy.src = dyp;  // w * dY, formed in fp32 and quantised from that
+      wdy.row_src = row_src;
+      wdy.topk_w = topk_w;
+      wdy.k = k;
+      sa.src = A;
+      sdh.src = dH;
+      sxp.src8 = xp8;
+      sxp.src8s = xps;
+      if (!L.err)
+        L(launch_quant_seg(wdy, offsets, poff, E, d, Y.P, lq, lqs, "bwd_down_wgrad_qL", s));
+      if (!L.err)
+        L(launch_quant_seg(sa, offsets, poff, E, I, Y.P, rq, rqs, "bwd_down_wgrad_qR", s));
+      if (!L.err)
+        L(launch_mx_wgrad({lq, lqs, rq, rqs, dw2, poff, E, d, I, Y.P, accumulate,
+                           "bwd_down_wgrad"},
+                          pers, s));
+      if (!L.err)
+        L(launch_quant_seg(sdh, offsets, poff, E, 2 * I, Y.P, lq, lqs, "bwd_gate_wgrad_qL", s));
+      if (!L.err)
+        L(launch_quant_seg(sxp, offsets, poff, E, d, Y.P, rq, rqs, "bwd_gate_wgrad_qR", s));
+      if (!L.err)
+        L(launch_mx_wgrad({lq, lqs, rq, rqs, dw1, poff, E, 2 * I, d, Y.P, accumulate,
+                           "bwd_gate_wgrad"},
+                          pers, s));
+    } else {
+      if (!L.err)
+        L(launch_wgrad({dyw, A, nullptr, nullptr, dw2, offsets, at<int4>(workspace, Y.wg_table2),
+                        wg_count + 1, E, d, I, accumulate, false, "bwd_down_wgrad",
+                        "wgrad_sched_down"},
+                       s));
+      // the gate wgrad goes first: until the gate dgrad writes dXp, that buffer holds the bf16
+      // image of the big experts' fp8 Xp rows for the big-expert wgrad kernel
+      if (!L.err)
+        L(launch_wgrad({dH, nullptr, xp8, xps, dw1, offsets, at<int4>(workspace, Y.wg_table1),
+                        wg_count, E, 2 * I, d, accumulate, true, "bwd_gate_wgrad",
+                        "wgrad_sched_gate", dXp},
+                       s));
+    }
     if (!L.err)
       L(launch_bwd_gate_dgrad_mx({dhq, dhs, at<uint8_t>(wq, Y.w1b), at<uint8_t>(wq, Y.w1bs), dXp,
                                   offsets, sched, d, I, Tk, E},

@@ -833,6 +833,97 @@ struct MxBwdGateDgrad {
   }
 };
 
+// MXFP8 weight gradients: dW[e][m][n] = sum over the expert's padded positions p of
+// lq[m][poff[e] + p] rq[n][poff[e] + p], both operands quantised along the positions (mx.hip,
+// quant_seg_kernel; codes past the count are zero). A 128 x 128 tile of one expert's dW per
+// workgroup; its K loop walks the expert's 128-position chunks in order. An expert with no
+// rows has no chunks: its tile is written as zeros (overwrite) or left as it is (accumulate).
+template <bool ACC>
+struct MxWgrad {
+  static constexpr const char* kName = "bwd_wgrad_mx";
+  using G = GeoMx<128, 128, 1, 4>;
+  struct Args {
+    const uint8_t* lq;
+    const uint8_t* lqs;
+    const uint8_t* rq;
+    const uint8_t* rqs;
+    float* dw;
+    const int32_t* poff;
+    int E, Mdim, Ndim, P;
+  };
+  struct Tile {
+    int e, m0, n0;
+  };
+  // gg_kernel gives XCD x the tile range [x R, (x + 1) R), R = ntiles / 8. Expert by expert,
+  // one XCD would hold one expert's tiles, and an expert with most of the rows would run on an
+  // eighth of the GPU. So tile lt is the (lt % R)-th tile of slot lt / R in an order that deals
+  // every expert's tiles round robin over the eight XCDs. The count is rounded up to a multiple
+  // of 8; the surplus tiles have no expert (e = -1) and do nothing.
+  static MOE_DEV int real_tiles(const Args& a) { return a.E * (a.Mdim / G::BM) * (a.Ndim / G::BN); }
+  static MOE_DEV int ntiles(const Args& a) { return (real_tiles(a) + kXcds - 1) / kXcds * kXcds; }
+  static MOE_DEV Tile decode(const Args& a, int lt) {
+    const int R = ntiles(a) / kXcds;
+    const int v = (lt % R) * kXcds + lt / R;
+    if (v >= real_tiles(a)) return Tile{-1, 0, 0};
+    const int nm = a.Mdim / G::BM, nn = a.Ndim / G::BN;
+    const int2 mn = tile_mn<true>(v % (nm * nn), nm, nn);
+    return Tile{v / (nm * nn), mn.x * G::BM, mn.y * G::BN};
+  }
+  static MOE_DEV int num_k(const Args& a, const Tile& t) {
+    return t.e < 0 ? 0 : (a.poff[t.e + 1] - a.poff[t.e]) / G::BK;
+  }
+  static MOE_DEV int k_first(const Tile&, int) { return 0; }
+  static MOE_DEV bool m_active(const Tile&, int) { return true; }
+  static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
+  struct Loader {
+    LoadK8<G::BM, G::LDK> la;
+    LoadK8<G::BN, G::LDK> lb;
+    MOE_DEV void init(const Args& a, const Tile& t) {
+      const size_t P = a.P, p0 = a.poff[t.e];
+      const uint8_t* lq = a.lq;
+      const uint8_t* lqs = a.lqs;
+      const uint8_t* rq = a.rq;
+      const uint8_t* rqs = a.rqs;
+      const int m0 = t.m0, n0 = t.n0;
+      // kdim 128: the scale words load one step at a time (4-byte aligned: P and p0 are
+      // multiples of 128)
+      la.init([&](int m) { return lq + (m0 + m) * P + p0; },
+              [&](int m) { return lqs + (m0 + m) * (P / 32) + p0 / 32; }, G::BK);
+      lb.init([&](int n) { return rq + (n0 + n) * P + p0; },
+              [&](int n) { return rqs + (n0 + n) * (P / 32) + p0 / 32; }, G::BK);
+    }
+    MOE_DEV void load(int kt) {
+      la.load(kt);
+      lb.load(kt);
+    }
+  };
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
+                               uint8_t*) {
+    if (t.e < 0 || (ACC && a.poff[t.e + 1] == a.poff[t.e])) return;  // nothing to write / add
+    const int lane = threadIdx.x % kWave, wn = (threadIdx.x / kWave) % G::WAVES_N;
+    // lane's first element; row block mb adds 16 rows, column block nb 16 columns
+    float* out = a.dw + ((size_t)t.e * a.Mdim + t.m0 + lane % 16) * a.Ndim + t.n0 + wn * G::WN +
+                 4 * (lane / 16);
+    const size_t rstep = (size_t)16 * a.Ndim;
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) {
+        float4* dst = reinterpret_cast<float4*>(out + mb * rstep + nb * 16);
+        float4 v = make_float4(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]);
+        if (ACC) {
+          const float4 o = *dst;
+          v.x += o.x;
+          v.y += o.y;
+          v.z += o.z;
+          v.w += o.w;
+        }
+        *dst = v;
+      }
+    }
+  }
+};
+
 // ------------------------------------------------------------------------------------------
 // The kernel: walks logical tiles. Each XCD owns one contiguous range of them (so the
 // workgroups sharing an expert's activations share that XCD's L2), striding by the grid within
@@ -865,8 +956,16 @@ static size_t smem_bytes() {
 // Grid: one-shot grids cover `max_tiles` (rounded up to a multiple of 8); persistent grids
 // are the resident workgroup count, also a multiple of 8.
 template <class P>
+static hipError_t launch_named(const typename P::Args& a, int max_tiles, bool persistent,
+                               const char* name, hipStream_t stream);
+template <class P>
 static hipError_t launch(const typename P::Args& a, int max_tiles, bool persistent,
                          hipStream_t stream) {
+  return launch_named<P>(a, max_tiles, persistent, P::kName, stream);
+}
+template <class P>
+static hipError_t launch_named(const typename P::Args& a, int max_tiles, bool persistent,
+                               const char* name, hipStream_t stream) {
   if (max_tiles <= 0) return hipSuccess;
   const size_t sm = smem_bytes<P>();
   static bool attr_set = false;  // benign race: every caller sets the same value
@@ -892,7 +991,7 @@ static hipError_t launch(const typename P::Args& a, int max_tiles, bool persiste
     if (resident > 0 && resident < grid) grid = resident;
   }
   {
-    TraceScope trace(P::kName, stream);
+    TraceScope trace(name, stream);
     hipLaunchKernelGGL(gg_kernel<P>, dim3(grid), dim3(P::G::THREADS), sm, stream, a);
   }
   return hipGetLastError();
@@ -1246,6 +1345,16 @@ hipError_t launch_bwd_down_dgrad_mx(const GemmMxDownDgradArgs& x, bool persisten
 hipError_t launch_bwd_gate_dgrad_mx(const GemmMxGateDgradArgs& x, bool persistent, hipStream_t s) {
   MxBwdGateDgrad::Args a{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, x.sched, x.d, x.I};
   return launch<MxBwdGateDgrad>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
+}
+
+hipError_t launch_mx_wgrad(const GemmMxWgradArgs& x, bool persistent, hipStream_t s) {
+  const int max_tiles = (x.E * (x.Mdim / 128) * (x.Ndim / 128) + kXcds - 1) / kXcds * kXcds;
+  if (x.accumulate) {
+    MxWgrad<true>::Args a{x.lq, x.lqs, x.rq, x.rqs, x.dw, x.poff, x.E, x.Mdim, x.Ndim, x.P};
+    return launch_named<MxWgrad<true>>(a, max_tiles, persistent, x.name, s);
+  }
+  MxWgrad<false>::Args a{x.lq, x.lqs, x.rq, x.rqs, x.dw, x.poff, x.E, x.Mdim, x.Ndim, x.P};
+  return launch_named<MxWgrad<false>>(a, max_tiles, persistent, x.name, s);
 }
 
 }  // namespace moe

@@ -212,6 +212,40 @@ hipError_t launch_quant_rows(const uint16_t* src, long long rows, int cols, uint
 hipError_t launch_quant_weight(const uint16_t* src, int B, int R, int C, uint8_t* dq,
                                uint8_t* dqs, uint8_t* tq, uint8_t* tqs, const char* name,
                                hipStream_t s);
+// MXFP8 weight gradients: expert segments padded to kSegK positions (segment offsets poff
+// [E + 1], the padded total in poff[E] <= seg_capacity), and an operand S [T*k, C] quantised
+// along each segment's positions into q [C][P] codes and qs [C][P / 32] scales.
+constexpr int kSegK = 128;
+inline int seg_capacity(int Tk, int E) {
+  return (Tk + E * (kSegK - 1) + kSegK - 1) / kSegK * kSegK;
+}
+hipError_t launch_seg_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t s);
+// The operand: bf16 rows (src), or the MXFP8 image along C (src8 codes, src8s scales), or
+// w * dY gathered in fp32 (src = dY [T, C], row_src, topk_w, k).
+struct SegOperand {
+  const uint16_t* src = nullptr;
+  const uint8_t* src8 = nullptr;
+  const uint8_t* src8s = nullptr;
+  const int32_t* row_src = nullptr;
+  const float* topk_w = nullptr;
+  int k = 1;
+};
+hipError_t launch_quant_seg(const SegOperand& x, const int32_t* offsets, const int32_t* poff,
+                            int E, int C, int P, uint8_t* q, uint8_t* qs, const char* name,
+                            hipStream_t s);
+// dW [E, Mdim, Ndim] (fp32, overwritten or accumulated) = per expert, lq^T rq over its padded
+// positions: lq [Mdim][P] and rq [Ndim][P] with scales [.][P / 32], from launch_quant_seg.
+struct GemmMxWgradArgs {
+  const uint8_t* lq;
+  const uint8_t* lqs;
+  const uint8_t* rq;
+  const uint8_t* rqs;
+  float* dw;
+  const int32_t* poff;
+  int E, Mdim, Ndim, P, accumulate;
+  const char* name;
+};
+hipError_t launch_mx_wgrad(const GemmMxWgradArgs& a, bool persistent, hipStream_t s);
 hipError_t launch_scale_gather(const uint16_t* dy, const int32_t* tk_row, const float* topk_w,
                                int T, int k, int d, uint16_t* dyw, hipStream_t s);
 

@@ -198,6 +198,155 @@ __global__ void __launch_bounds__(256) scale_gather_kernel(const uint16_t* __res
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// MXFP8 weight gradients: both operands quantised along the positions of each expert segment.
+//
+// Segment layout: expert e's positions are stored from poff[e] on, padded to npad_e = the count
+// rounded up to 128 (one scaled-MFMA K step), so poff is the exclusive scan of npad. One
+// workgroup of 1024 threads (E <= 1024).
+__global__ void __launch_bounds__(1024) seg_offsets_kernel(const int32_t* __restrict__ offsets,
+                                                           int E, int32_t* __restrict__ poff) {
+  __shared__ int scan[1024];
+  const int e = threadIdx.x;
+  const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+  const int np = (c + kSegK - 1) / kSegK * kSegK;
+  scan[e] = np;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int u = e >= off ? scan[e - off] : 0;
+    __syncthreads();
+    scan[e] += u;
+    __syncthreads();
+  }
+  if (e < E) poff[e] = scan[e] - np;
+  if (e == 1023) poff[E] = scan[1023];
+}
+
+// Q [C][P]: column c of an operand S [T*k, C] (position-major), expert by expert, quantised
+// along the positions in blocks of 32 from each segment's first position; codes past a
+// segment's count are zero (an all-padding block gets scale code 0). QS [C][P / 32] holds the
+// scale codes. S is read as
+//  * SRC_BF16: bf16 rows src [T*k, C];
+//  * SRC_FP8: the MXFP8 image (codes src8, per-32 scales src8s along C), expanded exactly;
+//  * SRC_WDY: w * dY[t] in fp32 for the row r = row_src[pos] of position pos, w = topk_w[r]
+//    and t = r / k (dY bf16 [T, C]): the down weight gradient's left operand, quantised from
+//    its fp32 value (no bf16 rounding in between).
+// Block (q, y): padded positions [128 q, 128 q + 128) (one expert, found by binary search over
+// poff) x columns [64 y, 64 y + 64). The 128 x 64 tile goes through LDS as fp32, then thread t
+// quantises column t / 4, rows [32 (t % 4), +32), and writes the block's 32 codes as two
+// 16-byte stores.
+enum SegSrc { SRC_BF16, SRC_FP8, SRC_WDY };
+template <int SRC>
+__global__ void __launch_bounds__(256) quant_seg_kernel(const uint16_t* __restrict__ src,
+                                                        const uint8_t* __restrict__ src8,
+                                                        const uint8_t* __restrict__ src8s,
+                                                        const int32_t* __restrict__ row_src,
+                                                        const float* __restrict__ topk_w, int k,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ poff, int E,
+                                                        int C, int P, uint8_t* __restrict__ q,
+                                                        uint8_t* __restrict__ qs) {
+  constexpr int LD = 64 + 1;  // fp32 LDS row pitch: column reads of 32 rows spread over banks
+  __shared__ float tile[kSegK * LD];
+  const int pstart = blockIdx.x * kSegK;
+  if (pstart >= poff[E]) return;  // whole workgroup
+  int lo = 0, hi = E;  // largest e with poff[e] <= pstart
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (poff[mid] <= pstart) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int rel = pstart - poff[e];
+  const int nvalid = min(kSegK, offsets[e + 1] - offsets[e] - rel);
+  const size_t row0 = (size_t)offsets[e] + rel;
+  const int c0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = tid + 256 * j, r = i / 8, pc = i % 8;  // row r, 8-column piece pc
+    float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (r < nvalid) {
+      const size_t row = row0 + r;
+      if constexpr (SRC == SRC_FP8) {
+        const uint2 c8 = *reinterpret_cast<const uint2*>(src8 + row * C + c0 + pc * 8);
+        const float sc = mx_scale(src8s[row * (C / 32) + (c0 + pc * 8) / 32]);
+        float a[4], b[4];
+        e4m3x4_to_f32(c8.x, a);
+        e4m3x4_to_f32(c8.y, b);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          f[h] = a[h] * sc;
+          f[4 + h] = b[h] * sc;
+        }
+      } else {
+        float w = 1.f;
+        size_t srow = row;
+        if constexpr (SRC == SRC_WDY) {
+          const int rr = row_src[row];
+          w = topk_w[rr];
+          srow = (size_t)(rr / k);
+        }
+        const uint4 v = *reinterpret_cast<const uint4*>(src + srow * C + c0 + pc * 8);
+        const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          f[2 * h] = w * bf2f_lo(vw[h]);
+          f[2 * h + 1] = w * bf2f_hi(vw[h]);
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 8; ++h) tile[r * LD + pc * 8 + h] = f[h];
+  }
+  __syncthreads();
+  const int c = tid / 4, b = tid % 4;
+  float f[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    f[i] = tile[(32 * b + i) * LD + c];
+    amax = fmaxf(amax, fabsf(f[i]));
+  }
+  const uint32_t code = mx_scale_code(amax);
+  const float inv = mx_inv_scale(code);
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    o[i] = e4m3x2(f[4 * i] * inv, f[4 * i + 1] * inv) |
+           (e4m3x2(f[4 * i + 2] * inv, f[4 * i + 3] * inv) << 16);
+  uint8_t* dst = q + (size_t)(c0 + c) * P + pstart + 32 * b;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+  *reinterpret_cast<uint4*>(dst + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+  qs[(size_t)(c0 + c) * (P / 32) + pstart / 32 + b] = static_cast<uint8_t>(code);
+}
+
+hipError_t launch_seg_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t s) {
+  {
+    TraceScope trace("seg_offsets", s);
+    hipLaunchKernelGGL(seg_offsets_kernel, dim3(1), dim3(1024), 0, s, offsets, E, poff);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_seg(const SegOperand& x, const int32_t* offsets, const int32_t* poff,
+                            int E, int C, int P, uint8_t* q, uint8_t* qs, const char* name,
+                            hipStream_t s) {
+  const dim3 grid(P / kSegK, C / 64);
+  {
+    TraceScope trace(name, s);
+    if (x.src8)
+      hipLaunchKernelGGL(quant_seg_kernel<SRC_FP8>, grid, dim3(256), 0, s, x.src, x.src8,
+                         x.src8s, x.row_src, x.topk_w, x.k, offsets, poff, E, C, P, q, qs);
+    else if (x.row_src)
+      hipLaunchKernelGGL(quant_seg_kernel<SRC_WDY>, grid, dim3(256), 0, s, x.src, x.src8,
+                         x.src8s, x.row_src, x.topk_w, x.k, offsets, poff, E, C, P, q, qs);
+    else
+      hipLaunchKernelGGL(quant_seg_kernel<SRC_BF16>, grid, dim3(256), 0, s, x.src, x.src8,
+                         x.src8s, x.row_src, x.topk_w, x.k, offsets, poff, E, C, P, q, qs);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_rows(const uint16_t* src, long long rows, int cols, uint8_t* dst,
                              uint8_t* sc, const char* name, hipStream_t s) {
   const long long nvec = rows * cols / 8;

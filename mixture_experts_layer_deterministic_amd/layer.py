@@ -6,7 +6,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (MOE_FLAG_PERSISTENT, MOE_PREC_BF16, MOE_PREC_MXFP8, make_cfg, moe_backward,
+from . import (MOE_FLAG_MXFP8_WGRAD, MOE_FLAG_PERSISTENT, MOE_PREC_BF16, MOE_PREC_MXFP8, make_cfg, moe_backward,
                moe_forward, moe_forward_fused, moe_permute, moe_query, moe_quantize_weights,
                moe_route)
 
@@ -16,13 +16,16 @@ class MoeLayer:
 
     ``ring_slots`` slots of T*k permuted rows make up the ring. Forward writes slot ``slot``,
     and backward reads the slot its batch was permuted into. With ``precision=MOE_PREC_MXFP8``
-    the layer also owns the quantised-weight buffer ``wq``; ``quantize_weights`` fills it.
+    the layer also owns the quantised-weight buffer ``wq``; ``quantize_weights`` fills it, and
+    ``mx_wgrad`` makes the weight gradients MXFP8 too.
     """
 
     def __init__(self, T, d, E, k, I, device="cuda", ring_slots=1, persistent=False,
-                 precision=MOE_PREC_BF16):
+                 precision=MOE_PREC_BF16, mx_wgrad=False):
         self.T, self.d, self.E, self.k, self.I = T, d, E, k, I
-        self.cfg = make_cfg(T, d, E, k, I, precision, MOE_FLAG_PERSISTENT if persistent else 0)
+        flags = (MOE_FLAG_PERSISTENT if persistent else 0) | (MOE_FLAG_MXFP8_WGRAD if mx_wgrad
+                                                               else 0)
+        self.cfg = make_cfg(T, d, E, k, I, precision, flags)
         s = moe_query(self.cfg)
         self.sizes = s
         dev = torch.device(device)

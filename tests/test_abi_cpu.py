@@ -174,3 +174,18 @@ def test_fused_forward_checks_arguments_before_launching():
     bad = list(args(cfg, s.ring_slot, 0, s.saved, s.workspace))
     bad[2] = None  # no router weight
     assert L.moe_forward_fused(*bad) == -1
+
+
+def test_mxfp8_wgrad_flag_needs_mxfp8_mode_and_sizes_its_workspace():
+    L = m.lib()
+    p = _fake()
+    bad = m.make_cfg(64, 256, 8, 2, 128, m.MOE_PREC_BF16, m.MOE_FLAG_MXFP8_WGRAD)
+    with pytest.raises(m.MoeError) as ei:
+        m.moe_query(bad)
+    assert ei.value.status == -1
+    assert L.moe_route(ctypes.byref(bad), p, p, p, p, p, p, 1 << 30, None) == -1
+    plain = m.moe_query(m.make_cfg(2048, 7168, 256, 8, 2048, m.MOE_PREC_MXFP8))
+    mxw = m.moe_query(m.make_cfg(2048, 7168, 256, 8, 2048, m.MOE_PREC_MXFP8,
+                                 m.MOE_FLAG_MXFP8_WGRAD))
+    P = (2048 * 8 + 256 * 127 + 127) // 128 * 128  # padded positions of all expert segments
+    assert mxw.workspace - plain.workspace >= (2 * 4096 * P + 2 * 4096 * P // 32) // 2

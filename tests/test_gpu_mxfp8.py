@@ -276,3 +276,52 @@ def test_mxfp8_local_zipf_full_size_sampled_parity():
     torch.cuda.empty_cache()
     assert_bitwise_equal(ref, outputs(run_gpu(inp), False, clone=False))
     _announce("  two full-size MXFP8 runs bitwise identical")
+
+
+# --- MXFP8 weight gradients (MOE_FLAG_MXFP8_WGRAD) ---------------------------------------------
+
+MXW_CASES = {
+    "tiny": dict(name="tiny"),
+    "ragged": dict(name="tiny", T=300, E=16, k=3, d=512, I=256),
+    "zipf_local": dict(name="local_zipf", T=2048, d=256, I=256),
+}
+
+
+@pytest.mark.parametrize("case", list(MXW_CASES))
+def test_mxfp8_weight_gradients_match_the_oracle(case):
+    """Both weight gradients in MXFP8, their operands quantised along each expert's positions
+    (blocks of 32 from the segment start): within 6e-2 of the oracle doing the same, with the
+    rest of the layer as in MXFP8 mode; then two runs bitwise equal, and accumulate doubling."""
+    spec = dict(MXW_CASES[case])
+    name = spec.pop("name")
+    _announce(f"[mxfp8 wgrad] case={case} shape={spec} seed=0")
+    inp = _mx_inputs(name, seed=0, mx_wgrad=True, **spec)
+    L = run_gpu(inp)
+    f, b = run_oracle(inp)
+    check_parity(L, inp, f, b, tol_act=TOL_MX, tol_grad=TOL_MX)
+    routed = "Wr" in inp
+    a = outputs(L, routed)
+    assert_bitwise_equal(a, outputs(run_gpu(inp), routed, clone=False))
+    first = [L.dw1.clone(), L.dw2.clone()]
+    L.backward(inp.get("Wr"), inp["W1"], inp["W2"], inp["dY"], accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(L.dw1, 2 * first[0]) and torch.equal(L.dw2, 2 * first[1])
+
+
+def test_mxfp8_weight_gradients_with_large_and_empty_experts():
+    """Experts of 700, 300, 0 and 24 rows at d=512, I=256: several 128-position K chunks, an
+    empty expert (zero blocks) and segments starting off the 32-row grid."""
+    counts = [700, 300, 0, 24]
+    _announce(f"[mxfp8 wgrad] expert sizes {counts}, d=512 I=256 k=1")
+    E, d, I = len(counts), 512, 256
+    T = sum(counts)
+    inp = workload.make_inputs("local_zipf", seed=15, device=DEV, T=T, d=d, E=E, I=I,
+                               precision="mxfp8", mx_wgrad=True)
+    idx = np.repeat(np.arange(E, dtype=np.int32), counts)
+    np.random.default_rng(15).shuffle(idx)
+    inp["topk_idx"] = torch.from_numpy(idx.reshape(T, 1)).to(DEV)
+    L = run_gpu(inp)
+    f, b = run_oracle(inp)
+    assert list(f["counts"]) == counts
+    check_parity(L, inp, f, b, tol_act=TOL_MX, tol_grad=TOL_MX)
+    assert torch.count_nonzero(L.dw1[2]) == 0 and torch.count_nonzero(L.dw2[2]) == 0
