@@ -33,40 +33,62 @@ constexpr int kFusedThreads = 256;
 constexpr int kRouterWaves = kFusedThreads / kWave;  // experts per router block
 constexpr unsigned kBarrierSpins = 1u << 21;         // about two seconds of waiting
 
-// Barrier state, one per GPU (zero when the code object loads; every completed barrier leaves
-// count at zero again): arrivals of the current barrier, and its generation.
+// Barrier state, one per GPU, zero when the code object loads; every completed barrier leaves
+// the counters at zero again. The workgroups arrive in kBarrierGroups groups (workgroup b in
+// group b % kBarrierGroups), each on a counter of its own, and the last of each group arrives
+// on the top counter: no counter takes more than n / kBarrierGroups arrivals, so the atomics,
+// which one memory channel serialises per address, spread over kBarrierGroups + 1 addresses.
+// Every field sits in its own 256-byte line, and the generation that the waiting workgroups
+// poll in yet another, so the polls do not queue behind the arrivals.
+constexpr int kBarrierGroups = 8;
+struct alignas(256) BarrierWord {
+  unsigned v;
+};
 struct GridBarrier {
-  unsigned count;
-  unsigned gen;
+  BarrierWord group[kBarrierGroups];
+  BarrierWord top;
+  BarrierWord gen;
 };
 static __device__ GridBarrier fused_barrier;
+static_assert(kXcds % kBarrierGroups == 0, "the grid is a multiple of kXcds workgroups");
 
-// All `n` workgroups of the grid meet here. The release fence before arriving and the acquire
-// fence after leaving make every write of every workgroup before the barrier visible to every
-// read after it, across the XCDs' L2 caches. The last workgroup to arrive resets the count and
-// starts the next generation. A workgroup that waits longer than kBarrierSpins polls gives up,
-// marks *status and goes on, so the kernel always ends.
+// All `n` workgroups of the grid meet here (n a multiple of kBarrierGroups). Each arrival is
+// an acquire-release atomic: thread 0 of a workgroup releases its workgroup's writes (they
+// leave the XCD's L2 for memory), and the last arrival of a group acquires the group's writes
+// before it releases them again on the top counter. The last arrival there starts the next
+// generation; the others poll the generation with relaxed loads and leave with one acquire
+// fence (an acquire on every poll would invalidate the L2 each time, under the feet of the
+// workgroups still working). So every write before the barrier is visible to every read after
+// it, across the XCDs' L2 caches. A workgroup that waits longer than kBarrierSpins polls gives
+// up, marks *status and goes on, so the kernel always ends.
 MOE_DEV void grid_sync(GridBarrier* b, unsigned n, int32_t* status) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
-    const unsigned g = __hip_atomic_load(&b->gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned arrived =
-        __hip_atomic_fetch_add(&b->count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) + 1;
-    if (arrived == n) {
-      __hip_atomic_store(&b->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&b->gen, g + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
+    // gen cannot move before this workgroup arrives, and this thread saw its last change
+    const unsigned g = __hip_atomic_load(&b->gen.v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    BarrierWord* grp = &b->group[blockIdx.x % kBarrierGroups];
+    bool done = false;
+    if (__hip_atomic_fetch_add(&grp->v, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
+        n / kBarrierGroups) {
+      __hip_atomic_store(&grp->v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__hip_atomic_fetch_add(&b->top.v, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
+          (unsigned)kBarrierGroups) {
+        __hip_atomic_store(&b->top.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&b->gen.v, g + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        done = true;
+      }
+    }
+    if (!done) {
       unsigned spins = 0;
-      while (__hip_atomic_load(&b->gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == g) {
+      while (__hip_atomic_load(&b->gen.v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g) {
         __builtin_amdgcn_s_sleep(2);
         if (++spins == kBarrierSpins) {
           atomicOr(status, MOE_DEVICE_BARRIER_TIMEOUT);
           break;
         }
       }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
-    __threadfence();
   }
   __syncthreads();
 }
