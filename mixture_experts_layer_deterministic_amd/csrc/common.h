@@ -81,25 +81,6 @@ MOE_DEV uint4 nt_load16(const void* p) {
 MOE_DEV float silu(float g) { return g / (1.0f + __expf(-g)); }
 MOE_DEV float sigmoid(float g) { return 1.0f / (1.0f + __expf(-g)); }
 
-// Transpose an 8x8 block of 16-bit values held as 8 rows of 8 (uint4 each): out[c] holds column
-// c of the input, i.e. out[c] element p = in[p] element c.
-MOE_DEV void transpose8x8_b16(const uint4 (&in)[8], uint4 (&out)[8]) {
-  const uint32_t* iw[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) iw[r] = reinterpret_cast<const uint32_t*>(&in[r]);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    uint32_t o[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t a = iw[2 * p][c >> 1];
-      const uint32_t b = iw[2 * p + 1][c >> 1];
-      o[p] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-    out[c] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-}
-
 // LDS tiles of 64 bf16 per row (128 bytes, no padding) whose 16-byte chunks are permuted per
 // row: chunk c of row r sits at chunk c ^ (r & 7). Element offset of (row, chunk). An MFMA
 // fragment read (16 rows, one chunk each, per 16 lanes) and a row store (8 chunks of a row per

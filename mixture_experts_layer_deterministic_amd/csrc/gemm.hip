@@ -13,8 +13,8 @@
 // direct global -> LDS loads (dma.h). Tiles of BK stream through double-buffered LDS, stored
 // K-contiguous in rows of 64 values whose 16-byte chunks are permuted per row (rowswz), so every
 // MFMA fragment is one 16-byte LDS read and neither those reads nor the row stores conflict on
-// banks. In the 128 x 128 dgrads the weights, whose K axis is not contiguous in memory, are
-// loaded as 8x8 blocks and transposed in registers on their way in.
+// banks. In the 128 x 128 dgrads the weights, whose K axis is not contiguous in memory, sit in
+// LDS as they are in memory and reach the MFMAs through gfx950's transposing LDS read.
 //
 // Determinism: every output element is produced by exactly one workgroup, which reduces K in a
 // fixed order. There are no atomics and no split-K.
@@ -36,6 +36,7 @@ namespace moe {
 struct BwdDownDgrad {
   static constexpr const char* kName = "bwd_down_dgrad";
   using G = Geo<128, 128, 64, 1, 4>;
+  static constexpr bool kBKMajor = true;  // W2[e] tiles are K-major (LoadKM)
   struct Args {
     const uint16_t* dy;      // [T, d]
     const int32_t* row_src;  // [T*k]
@@ -68,7 +69,7 @@ struct BwdDownDgrad {
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
     LoadK<G::BM, G::BK, G::LDK, kThreads, false> la;
-    LoadMN<G::BN, G::BK, G::LDK> lb;
+    LoadKM<G::BN, G::BK> lb;
     const uint16_t* wb;
     int ldw;
     MOE_DEV void init(const Args& a, const Tile& t) {
@@ -151,6 +152,7 @@ struct BwdDownDgrad {
 struct BwdGateDgrad {
   static constexpr const char* kName = "bwd_gate_dgrad";
   using G = Geo<128, 128, 64, 1, 4>;
+  static constexpr bool kBKMajor = true;  // W1[e] tiles are K-major (LoadKM)
   struct Args {
     const uint16_t* dH;  // [T*k, 2I]
     const uint16_t* w1;  // [E, 2I, d]
@@ -178,7 +180,7 @@ struct BwdGateDgrad {
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
     LoadK<G::BM, G::BK, G::LDK, kThreads, false> la;
-    LoadMN<G::BN, G::BK, G::LDK> lb;
+    LoadKM<G::BN, G::BK> lb;
     const uint16_t* wb;
     int ldw;
     MOE_DEV void init(const Args& a, const Tile& t) {

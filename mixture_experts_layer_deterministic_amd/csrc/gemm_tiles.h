@@ -8,6 +8,8 @@
 // section "Three design decisions that matter".
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -59,48 +61,45 @@ struct LoadK {
   }
 };
 
-// BK x MN tile stored MN-contiguous in memory (K is the slow axis). Loaded as 8x8 blocks whose
-// k-block index runs fastest across lanes (each wave instruction reads 8 rows x 128 contiguous
-// bytes), then transposed so LDS holds [MN][K] in rowswz's chunk-permuted rows. Only the first
-// NB threads hold a block.
-template <int MN, int BK, int LDK>
-struct LoadMN {
-  static constexpr int BKB = BK / 8;
-  static constexpr int NB = (MN / 8) * BKB;
-  static constexpr int PT = (NB + kThreads - 1) / kThreads;
-  uint4 r[PT][8];
+// BK x MN tile stored MN-contiguous in memory (K is the slow axis), copied into LDS as it sits
+// in memory: K row k of the stage holds the tile's MN values, with its 32-byte column groups
+// permuted by kmajor_swz(k). The MFMA fragments come from gfx950's transposing LDS read
+// (kmajor_frag), so no value is transposed in registers. Each thread moves BK * MN / 8 /
+// kThreads 16-byte pieces; MN / 8 consecutive threads cover one K row.
+template <int MN, int BK>
+struct LoadKM {
+  static constexpr int CPR = MN / 8;
+  static constexpr int NV = BK * CPR;
+  static constexpr int PT = NV / kThreads;
+  static_assert(NV % kThreads == 0 && MN <= 128, "whole pieces per thread, swizzle in a row");
+  uint4 r[PT];
 
-  // w: the tile's first column in its first K row of this step (the same in every lane); ld:
-  // the row pitch. A lane's eight rows are one 32-bit offset plus workgroup-uniform strides.
+  // w: the tile's first column in its first K row of this step; ld: the row pitch
   MOE_DEV void load(const uint16_t* w, int ld) {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
-      const int b = threadIdx.x + kThreads * j;
-      if (b < NB) {
-        const int kb = b % BKB, mb = b / BKB;
-        const uint16_t* p = w + (uint32_t)(kb * 8 * ld + mb * 8);
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr)
-          r[j][rr] = *reinterpret_cast<const uint4*>(p + (size_t)rr * ld);
-      }
+      const int v = threadIdx.x + kThreads * j;
+      r[j] = *reinterpret_cast<const uint4*>(w + (uint32_t)((v / CPR) * ld + (v % CPR) * 8));
     }
   }
   MOE_DEV void store(uint16_t* s) const {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
-      const int b = threadIdx.x + kThreads * j;
-      if (b < NB) {
-        const int kb = b % BKB, mb = b / BKB;
-        uint4 t[8];
-        transpose8x8_b16(r[j], t);
-        // rowswz(mb * 8 + c, kb) = mb * 512 + 64 c + 8 (kb ^ c), which is x ^ (72 c) for
-        // x = mb * 512 + 8 kb: one address and a constant per row
-        const int x = rowswz(mb * 8, kb);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(s + (x ^ (72 * c))) = t[c];
-      }
+      const int v = threadIdx.x + kThreads * j, k = v / CPR;
+      *reinterpret_cast<uint4*>(s + k * MN + (((v % CPR) * 8) ^ kmajor_swz(k))) = r[j];
     }
   }
+};
+
+// Whether problem P keeps its B operand K-major in LDS (P::kBKMajor, LoadKM) rather than in
+// rowswz rows; false where P does not say.
+template <class P, class = void>
+struct BKMajor {
+  static constexpr bool value = false;
+};
+template <class P>
+struct BKMajor<P, std::void_t<decltype(P::kBKMajor)>> {
+  static constexpr bool value = P::kBKMajor;
 };
 
 // ------------------------------------------------------------------------------------------
@@ -380,8 +379,12 @@ MOE_DEV void run_tile(const typename P::Args& a, const typename P::Tile& t, uint
         // once per step rather than once per 16-row block.
         uint4 bf[G::NB], af[G::MB];
 #pragma unroll
-        for (int nb = 0; nb < G::NB; ++nb)
-          bf[nb] = *reinterpret_cast<const uint4*>(sB + P::brow(wn, nb) * G::LDK + co);
+        for (int nb = 0; nb < G::NB; ++nb) {
+          if constexpr (BKMajor<P>::value)
+            bf[nb] = kmajor_frag<G::BN>(cur + G::BM * G::LDK, P::brow(wn, nb), 32 * ks, lane);
+          else
+            bf[nb] = *reinterpret_cast<const uint4*>(sB + P::brow(wn, nb) * G::LDK + co);
+        }
 #pragma unroll
         for (int mb = 0; mb < G::MB; ++mb)
           af[mb] = *reinterpret_cast<const uint4*>(sA + mb * 16 * G::LDK + co);
