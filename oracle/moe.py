@@ -41,6 +41,9 @@ readings = {
                    "positions from the segment's first (the last block holds the rest): dW2 "
                    "from (w dY) and A, dW1 from dH and the MXFP8 image of Xp the ring holds "
                    "(quantised again, along the positions)",
+    "dw_bf16": "weight gradients stored as bf16, an option (the default stores dW1 and dW2 in "
+               "fp32, the caller's main gradient): each element of dW1 and dW2 is its sum "
+               "rounded once to bf16 where it is stored; dWr stays fp32",
     "mxfp8": "MXFP8 mode (MarkTechPost, closing paragraph of 'Three design decisions that "
              "matter': BF16 and MXFP8 modes): every expert GEMM of forward and dgrad takes both "
              "operands as MXFP8 images quantised along that GEMM's reduction axis - Xp and W1 "
@@ -301,7 +304,8 @@ def forward(X, W1, W2, *, Wr=None, k=None, topk_idx=None, topk_w=None,
     return out
 
 
-def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None, wgrad="bf16") -> dict:
+def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None, wgrad="bf16",
+             dw_dtype="fp32") -> dict:
     """Backward pass: gradients of L = <Y, dY> with respect to every input.
 
     Per row at position pos (token t, slot j, expert e, weight w), by ``expert_backward``:
@@ -322,10 +326,12 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None, wgrad="bf16") -
     In MXFP8 mode (reading "mxfp8") both dgrad GEMMs take MXFP8 images of their operands, dw is
     <dA', A>, and Xp enters dW1 and dWr as its MXFP8 image. wgrad="mxfp8" (MXFP8 mode only,
     reading "mxfp8_wgrad") quantises both operands of both weight-gradient products along the
-    expert's positions.
+    expert's positions. dw_dtype="bf16" (reading "dw_bf16") rounds each dW1 and dW2 element once
+    to bf16.
     """
     mxmode = fwd.get("precision", "bf16") == "mxfp8"
     assert wgrad in ("bf16", "mxfp8") and (wgrad == "bf16" or mxmode), "MXFP8 wgrad needs MXFP8"
+    assert dw_dtype in ("fp32", "bf16")
     X = np.asarray(X, np.float64)
     dY = np.asarray(dY, np.float64)
     T, d = X.shape
@@ -351,6 +357,8 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None, wgrad="bf16") -
         dw_pos[p0:p1], dH[p0:p1], dXp[p0:p1], dW1[slot], dW2[slot] = expert_backward(
             X[tok], dY[tok], w_flat[rows][:, None], fwd["H"][p0:p1], fwd["A"][p0:p1],
             fwd["O"][p0:p1], W1[e], W2[e], rnd=rnd, mxmode=mxmode, mx_wgrad=wgrad == "mxfp8")
+    if dw_dtype == "bf16":
+        dW1, dW2 = bf16_round(dW1), bf16_round(dW2)
     dw = dw_pos[tk_row].reshape(T, k)
     dXsum = gather_sum(dXp, None, tk_row, k)
     out = dict(dw=dw, dH=dH, dXp=dXp, dW1=dW1, dW2=dW2, experts=ex)
@@ -364,7 +372,7 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None, wgrad="bf16") -
 
 
 def layer(X, W1, W2, dY, *, Wr=None, k=None, topk_idx=None, topk_w=None, storage="bf16",
-          precision="bf16", on_expert=None, wgrad="bf16") -> dict:
+          precision="bf16", on_expert=None, wgrad="bf16", dw_dtype="fp32") -> dict:
     """Forward and backward of the whole layer, one expert at a time.
 
     The same steps as ``forward`` followed by ``backward``, in the same order and arithmetic,
@@ -374,6 +382,8 @@ def layer(X, W1, W2, dY, *, Wr=None, k=None, topk_idx=None, topk_w=None, storage
     largest workloads. Returns the forward intermediates and the backward results of
     ``forward``/``backward`` (without dW1 and dW2).
     """
+    assert dw_dtype in ("fp32", "bf16")
+    dwr = bf16_round if dw_dtype == "bf16" else _identity
     mxmode = precision == "mxfp8"
     mxq = mx.qdq if mxmode else _identity
     X = np.asarray(X, np.float64)
@@ -407,7 +417,7 @@ def layer(X, W1, W2, dY, *, Wr=None, k=None, topk_idx=None, topk_w=None, storage
             X[tok], dY[tok], w_flat[rows][:, None], H[p0:p1], A[p0:p1], O[p0:p1], w1, w2,
             rnd=rnd, mxmode=mxmode, mx_wgrad=wgrad == "mxfp8")
         if on_expert is not None:
-            on_expert(e, dW1, dW2)
+            on_expert(e, dwr(dW1), dwr(dW2))
     out = dict(idx=idx, w=w, counts=counts, offsets=offsets, row_src=row_src, tk_row=tk_row,
                H=H, A=A, O=O, Y=rnd(gather_sum(O, w, tk_row, k)), k=k)
     dw = dw_pos[tk_row].reshape(T, k)

@@ -13,6 +13,9 @@ backward) that casts at those points and nowhere else:
   before the combine, the SwiGLU backward reading the unrounded g and u, dXp left unrounded
   before the token sum, dH not rounded) changes some stored value, so the bitwise comparison
   would catch it.
+With dw_dtype="bf16" the weight gradients are stored as bf16 too: the formulation's dW1 and
+dW2 cast once with torch's cast must equal the oracle's bit for bit, and leaving them unrounded
+must not.
 ``oracle.layer`` (forward and backward one expert at a time) must equal ``oracle.forward``
 followed by ``oracle.backward`` bit for bit: it is the same arithmetic in the same order.
 """
@@ -122,6 +125,13 @@ def test_bf16_storage_points_match_an_independent_torch_formulation(T, d, E, k, 
     for n in ("dw", "dW1", "dW2", "dWr"):
         np.testing.assert_allclose(b[n], ref[n], rtol=1e-12, atol=1e-12 * np.abs(ref[n]).max(),
                                    err_msg=n)
+    b16 = oracle.backward(f, X, W1, W2, dY, Wr=Wr, dw_dtype="bf16")
+    for n in ("dW1", "dW2"):
+        want = _bf(torch.from_numpy(ref[n])).numpy()
+        np.testing.assert_array_equal(b16[n], want, err_msg=n)
+        assert not np.array_equal(b16[n], ref[n])  # the unrounded sums differ from the stored
+    for n in ("dw", "dH", "dXp", "dX", "dWr"):
+        np.testing.assert_array_equal(b16[n], b[n], err_msg=n)  # nothing else changes
 
 
 @pytest.mark.parametrize("mutant,affected", [
@@ -152,16 +162,17 @@ def _layer_cases():
 
 
 @pytest.mark.parametrize("case", range(3))
-def test_layer_driver_equals_forward_then_backward_bitwise(case):
+@pytest.mark.parametrize("dw_dtype", ["fp32", "bf16"])
+def test_layer_driver_equals_forward_then_backward_bitwise(case, dw_dtype):
     cases, (T, d, E, I) = _layer_cases()
     mode, kw, prec = cases[case]
     X, Wr, W1, W2, dY = _inputs(T, d, E, kw.get("k", 1), I, 40 + case)
     if mode == "routed":
         kw = dict(kw, Wr=Wr)
     f = oracle.forward(X, W1, W2, precision=prec, **kw)
-    b = oracle.backward(f, X, W1, W2, dY, Wr=kw.get("Wr"))
+    b = oracle.backward(f, X, W1, W2, dY, Wr=kw.get("Wr"), dw_dtype=dw_dtype)
     seen = {}
-    lay = oracle.layer(X, W1, W2, dY, precision=prec,
+    lay = oracle.layer(X, W1, W2, dY, precision=prec, dw_dtype=dw_dtype,
                        on_expert=lambda e, a, c: seen.__setitem__(e, (a, c)), **kw)
     assert sorted(seen) == list(range(E))
     for n in ("idx", "w", "counts", "offsets", "row_src", "tk_row", "H", "A", "O", "Y"):
