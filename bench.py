@@ -36,15 +36,17 @@ MFMA_FP8_TFLOPS = 5000.0   # dense fp8 MFMA (the MXFP8 scaled MFMA), TFLOP/s
 VALU_FP32_TFLOPS = 78.6
 
 
-def algorithmic(cfg, routed=True, accumulate=False, mx=False, mx_wgrad=False):
+def algorithmic(cfg, routed=True, accumulate=False, mx=False, mx_wgrad=False, bf16_dw=False):
     """Algorithmic bytes and flops per launch of each kernel: what the method must move and
     compute (each tensor read or written once, no padding, no re-reads). M = T*k rows.
     In MXFP8 mode (`mx`) a quantised tensor of n elements is n code bytes plus n/32 scale
-    bytes, and the weights are read in the quantised copies."""
+    bytes, and the weights are read in the quantised copies. dW1 and dW2 elements are 4 bytes,
+    2 with `bf16_dw`."""
     T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
     M = T * k
     nb = (M + 255) // 256
     acc = 2 if accumulate else 1
+    wb = 2 if bf16_dw else 4  # bytes per dW1 / dW2 element
     q = lambda n: n + n // 32  # bytes of n MXFP8 elements with their scales
     b = {}
     if routed:
@@ -57,7 +59,7 @@ def algorithmic(cfg, routed=True, accumulate=False, mx=False, mx_wgrad=False):
     b["combine"] = (M * d * 2 + T * d * 2 + M * 8, 2 * M * d)
     b["dw_router"] = (M * (I // 128) * 4 + M * 12, 0)
     b["scale_gather"] = (T * d * 2 + M * d * 2 + M * 8, M * d)
-    b["bwd_down_wgrad"] = (acc * E * d * I * 4 + T * d * 2 + M * I * 2, 2 * M * d * I)
+    b["bwd_down_wgrad"] = (acc * E * d * I * wb + T * d * 2 + M * I * 2, 2 * M * d * I)
     b["uncombine"] = (M * d * 2 + T * d * 2 + (E * d * 2 if routed else 0) + M * 8, M * d)
     if not mx:
         b["perm_place"] = (T * d * 2 + M * d * 2 + M * 16, 0)
@@ -67,7 +69,7 @@ def algorithmic(cfg, routed=True, accumulate=False, mx=False, mx_wgrad=False):
         b["bwd_down_dgrad"] = (E * d * I * 2 + T * d * 2 + M * 2 * I * 2 * 2 + M * I * 2
                                + M * (I // 128) * 4, 2 * M * d * I)
         b["bwd_gate_dgrad"] = (E * 2 * I * d * 2 + M * 2 * I * 2 + M * d * 2, 2 * M * 2 * I * d)
-        b["bwd_gate_wgrad"] = (acc * E * 2 * I * d * 4 + M * 2 * I * 2 + M * d * 2,
+        b["bwd_gate_wgrad"] = (acc * E * 2 * I * d * wb + M * 2 * I * 2 + M * d * 2,
                                2 * M * 2 * I * d)
         if routed:
             b["dwr"] = (M * d * 2 + acc * E * d * 4 + M * 4, 2 * M * d)
@@ -83,16 +85,16 @@ def algorithmic(cfg, routed=True, accumulate=False, mx=False, mx_wgrad=False):
         b["bwd_down_dgrad"] = (q(E * d * I) + q(T * d) + M * 2 * I * 2 + M * I * 2
                                + M * 2 * I * 2 + q(M * 2 * I) + M * (I // 128) * 4, 2 * M * d * I)
         b["bwd_gate_dgrad"] = (q(E * 2 * I * d) + q(M * 2 * I) + M * d * 2, 2 * M * 2 * I * d)
-        b["bwd_gate_wgrad"] = (acc * E * 2 * I * d * 4 + M * 2 * I * 2 + q(M * d),
+        b["bwd_gate_wgrad"] = (acc * E * 2 * I * d * wb + M * 2 * I * 2 + q(M * d),
                                2 * M * 2 * I * d)
         if routed:
             b["dwr"] = (q(M * d) + acc * E * d * 4 + M * 4, 2 * M * d)
         if mx_wgrad:
             # each operand read once in bf16 (Xp as its MXFP8 image) and quantised along the
             # positions; the GEMM reads the quantised copies and writes fp32 dW
-            b["bwd_down_wgrad"] = (acc * E * d * I * 4 + T * d * 2 + M * I * 2 + q(M * d)
+            b["bwd_down_wgrad"] = (acc * E * d * I * wb + T * d * 2 + M * I * 2 + q(M * d)
                                    + q(M * I), 2 * M * d * I)
-            b["bwd_gate_wgrad"] = (acc * E * 2 * I * d * 4 + M * 2 * I * 2 + q(M * d)
+            b["bwd_gate_wgrad"] = (acc * E * 2 * I * d * wb + M * 2 * I * 2 + q(M * d)
                                    + q(M * 2 * I) + q(M * d), 2 * M * 2 * I * d)
     return b
 
@@ -281,6 +283,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--persistent", action="store_true",
                     help="time the persistent grids as the headline (default: one-shot grids)")
+    ap.add_argument("--bf16-dw", action="store_true",
+                    help="store dW1 and dW2 as bf16 in the headline run (default: fp32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="skip the per-kernel traced pass")
     ap.add_argument("--no-mxfp8", action="store_true",
@@ -334,7 +338,7 @@ def main():
         del src, dst
 
     main_run = run_layer(m, MoeLayer, inp, cfg, stream, args, mx=mx,
-                         persistent=args.persistent)
+                         persistent=args.persistent, bf16_dw=args.bf16_dw)
     ms, kernels = main_run["ms"], main_run["kernels"]
     tokens_per_s = T / (ms * 1e-3)
 
@@ -344,7 +348,8 @@ def main():
         kd = kernels[dominant]
         roof = {"kernel": dominant, "bound": kd["bound"], "achieved": kd["achieved"],
                 "peak": kd["peak"], "unit": kd["unit"], "frac": kd["frac"],
-                "traffic": measured_traffic(args.workload, dominant),
+                # the committed counter records are of the fp32-dW layer
+                "traffic": None if args.bf16_dw else measured_traffic(args.workload, dominant),
                 "alg_bytes": kd["alg_bytes"], "us_per_step": kd["us"],
                 "launches_per_step": kd["launches_per_step"]}
     pc = {}
@@ -375,6 +380,28 @@ def main():
                    "weight_quantize_ms": round(r["quant_ms"], 4),
                    "layer_ms_without_weight_quantize": round(r["ms"] - r["quant_ms"], 4),
                    "grouped_gemm": r["gemm"], "kernels": r["kernels"]}
+        torch.cuda.empty_cache()
+
+    # The weight gradients stored as bf16 (the alternative to fp32 main gradients): the same
+    # sums rounded once, with half the dW bytes, in both precisions.
+    bf16_dw_line = None
+    if not args.no_extra and args.workload == "dsv3" and not mx:
+        print("[bench] bf16 weight gradients on the same inputs", file=sys.stderr, flush=True)
+        bf16_dw_line = {}
+        for tag, is_mx in (("bf16", False), ("mxfp8", True)):
+            if is_mx and (args.no_mxfp8 or not routed):
+                continue
+            torch.cuda.empty_cache()
+            r = run_layer(m, MoeLayer, inp, cfg, stream, args, mx=is_mx, bf16_dw=True)
+            bf16_dw_line[tag] = {
+                "tokens_per_s": round(T / (r["ms"] * 1e-3), 1), "ms_per_step": round(r["ms"], 4),
+                "ms_per_step_median": round(r["ms_median"], 4),
+                "grouped_gemm": r["gemm"],
+                "kernels": {g: r["kernels"][g] for g in GEMMS if g in r["kernels"]}}
+            if is_mx:
+                bf16_dw_line[tag]["weight_quantize_ms"] = round(r["quant_ms"], 4)
+                bf16_dw_line[tag]["layer_ms_without_weight_quantize"] = round(
+                    r["ms"] - r["quant_ms"], 4)
         torch.cuda.empty_cache()
 
     cpu = None
@@ -476,13 +503,14 @@ def main():
         "dtype": "mxfp8-e4m3/bf16" if mx else "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "d": d, "E": E, "k": k, "I": I,
-                   "precision": cfg["precision"], "weight_grad_dtype": "fp32",
+                   "precision": cfg["precision"], "weight_grad_dtype": "bf16" if args.bf16_dw else "fp32",
                    "persistent": bool(args.persistent), "seed": args.seed},
         "roofline": roof,
         "cpu_baseline": cpu,
         "grouped_gemm": main_run["gemm"],
         "permute_combine": pc,
         "mxfp8": mx_line,
+        "bf16_dw": bf16_dw_line,
         "expert_slice": slice_line,
         **extra,
         "hbm_copy": {"GB/s": hbm_copy, "bytes": 2 * n, "what": "one plain device copy, read + write"},
@@ -579,7 +607,7 @@ def run_stream(workload, dev, stream, args):
 
 
 def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=True,
-              mx_wgrad=False):
+              mx_wgrad=False, bf16_dw=False):
     """Warm up and time `args.steps` layer steps without any per-launch event, then (unless
     `trace` is off) time as many again with the library's per-launch events on the layer's
     stream, for the per-kernel times. In MXFP8 mode each step first quantises the weights."""
@@ -589,7 +617,7 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=T
     routed = "Wr" in inp
     prec = m.MOE_PREC_MXFP8 if mx else m.MOE_PREC_BF16
     L = MoeLayer(T, d, E, k, I, device=dev, persistent=persistent, precision=prec,
-                 mx_wgrad=mx_wgrad)
+                 mx_wgrad=mx_wgrad, bf16_dw=bf16_dw)
     wr = inp.get("Wr")
     if not routed:
         L.set_routing(inp["topk_idx"], inp["topk_w"])
@@ -600,7 +628,8 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=T
             L.quantize_weights(W1, W2, stream)
         L.step(X, wr, W1, W2, dY, stream=stream)
 
-    print(f"[bench] {'mxfp8' if mx else 'bf16'}{' persistent' if persistent else ''}: "
+    print(f"[bench] {'mxfp8' if mx else 'bf16'}{' persistent' if persistent else ''}"
+          f"{' bf16-dW' if bf16_dw else ''}: "
           f"warmup and {args.steps} untraced steps", file=sys.stderr, flush=True)
     res = time_steps(step, stream, args.steps, args.warmup)
 
@@ -616,7 +645,7 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=T
     del keep
 
     kernels = {}
-    alg = algorithmic(cfg, routed=routed, mx=mx, mx_wgrad=mx_wgrad)
+    alg = algorithmic(cfg, routed=routed, mx=mx, mx_wgrad=mx_wgrad, bf16_dw=bf16_dw)
     if trace and not args.no_trace:
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * per_step * args.steps)]
         for e in ev:

@@ -53,8 +53,9 @@ enum { MOE_PREC_BF16 = 0, MOE_PREC_MXFP8 = 1 };
 
 /* cfg.flags bits */
 enum {
-    MOE_FLAG_PERSISTENT = 1, /* grouped GEMMs as persistent grids walking the schedule table */
-    MOE_FLAG_MXFP8_WGRAD = 2 /* MXFP8 mode only: the weight gradients in MXFP8 too (below) */
+    MOE_FLAG_PERSISTENT = 1,  /* grouped GEMMs as persistent grids walking the schedule table */
+    MOE_FLAG_MXFP8_WGRAD = 2, /* MXFP8 mode only: the weight gradients in MXFP8 too (below) */
+    MOE_FLAG_BF16_DW = 4      /* dw1 and dw2 are bf16 buffers instead of fp32 (below) */
 };
 
 /* Device status word (first 4 bytes of the workspace). moe_permute clears it and ORs bits into
@@ -86,7 +87,13 @@ enum {
  * along their reduction axis, the positions of each expert: blocks of 32 consecutive positions
  * from the expert's first one, the last block holding what is left. dW2 reads w dY (the fp32
  * product, quantised directly) and A, dW1 reads dH and the ring's MXFP8 image of Xp, each
- * quantised so. dWr is unchanged. */
+ * quantised so. dWr is unchanged.
+ *
+ * Weight-gradient precision. The pages do not say in which precision the weight gradients are
+ * kept. By default dw1 and dw2 are fp32 (the caller's main gradient, which microbatches
+ * accumulate into). With MOE_FLAG_BF16_DW (either precision) they are bf16: each element is
+ * the same fp32 sum rounded once to nearest even where it is stored; with accumulate the fp32
+ * sum of the stored bf16 value and the new result is rounded once. dwr stays fp32. */
 typedef struct moe_cfg {
     int32_t T;         /* tokens entering the layer */
     int32_t d;         /* hidden size */
@@ -271,15 +278,15 @@ int moe_forward_fused(const moe_cfg* cfg, const void* x, const void* w_router, f
  *   dA       = w * dA'
  *   dg, du   = dA * u * s * (1 + g (1 - s)),  dA * silu(g)   (s = sigmoid(g); g, u from H)
  *   dH[pos]  = bf16([dg | du]);  dXp[pos] = bf16(dH[pos] W1[e])
- *   dW2[e]   = sum over pos in e, ascending, of bf16(w dy[t]) (x) A[pos]       (fp32)
- *   dW1[e]   = sum over pos in e, ascending, of dH[pos] (x) Xp[pos]           (fp32)
+ *   dW2[e]   = sum over pos in e, ascending, of bf16(w dy[t]) (x) A[pos]   (fp32 sums)
+ *   dW1[e]   = sum over pos in e, ascending, of dH[pos] (x) Xp[pos]       (fp32 sums)
  * Per token: d_topk_w[t,j] = dw of its row. When w_router is given (the layer routed itself):
  *   dlogit_j = w_j (dw_j - sum_i w_i dw_i), and 0 off the selected set;
  *   dx[t]    = bf16( sum_j dXp[tk_row[t*k+j]] + sum_j dlogit_j Wr[e_j] ), j ascending, fp32;
  *   dWr[e]   = sum over pos in e, ascending, of dlogit(pos) * Xp[pos]          (fp32).
  * When w_router is NULL (routing given), dx[t] = bf16(sum_j dXp[tk_row[t*k+j]]), and dwr is not
  * touched. Experts with no rows get zero dW1/dW2 blocks. With accumulate != 0, dw1, dw2 and dwr
- * are added to (fp32 read-modify-write) instead of overwritten.
+ * are added to (read-modify-write, the sum in fp32) instead of overwritten.
  *
  *   ring, ring_bytes, slot        in: the slot holding this batch's Xp (written by moe_permute)
  *   offsets, row_src, tk_row      in: from moe_permute
@@ -289,8 +296,8 @@ int moe_forward_fused(const moe_cfg* cfg, const void* x, const void* w_router, f
  *   saved                         in: from moe_forward of the same batch
  *   dy       bf16 [T, d]          in
  *   dx       bf16 [T, d]          out
- *   dw1      fp32 [E, 2I, d]      out (or accumulated)
- *   dw2      fp32 [E, d, I]       out (or accumulated)
+ *   dw1      fp32 [E, 2I, d]      out (or accumulated); bf16 with MOE_FLAG_BF16_DW
+ *   dw2      fp32 [E, d, I]       out (or accumulated); bf16 with MOE_FLAG_BF16_DW
  *   dwr      fp32 [E, d]          out (or accumulated); ignored when w_router is NULL
  *   d_topk_w fp32 [T, k]          out
  *   workspace bytes [ws_bytes]    scratch (dH and dXp at the offsets moe_query reports)
@@ -299,8 +306,8 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
                  const int32_t* offsets, const int32_t* row_src, const int32_t* tk_row,
                  const int32_t* topk_idx, const float* topk_w, const void* w_router,
                  const void* w1, const void* w2, const void* wq, size_t wq_bytes,
-                 const void* saved, size_t saved_bytes, const void* dy, void* dx, float* dw1,
-                 float* dw2, float* dwr, float* d_topk_w, int32_t accumulate, void* workspace,
+                 const void* saved, size_t saved_bytes, const void* dy, void* dx, void* dw1,
+                 void* dw2, float* dwr, float* d_topk_w, int32_t accumulate, void* workspace,
                  size_t ws_bytes, moe_stream_t stream);
 
 /*

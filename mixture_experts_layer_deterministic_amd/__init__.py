@@ -26,6 +26,7 @@ MOE_PREC_BF16 = 0
 MOE_PREC_MXFP8 = 1
 MOE_FLAG_PERSISTENT = 1
 MOE_FLAG_MXFP8_WGRAD = 2
+MOE_FLAG_BF16_DW = 4
 MOE_DEVICE_BAD_EXPERT_INDEX = 1
 MOE_DEVICE_BARRIER_TIMEOUT = 2
 

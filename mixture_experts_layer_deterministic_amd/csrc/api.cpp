@@ -175,7 +175,8 @@ struct Launches {
 int check_mode(const moe_cfg* c) {
   if (!cfg_ok(c)) return MOE_ERR_INVALID_ARG;
   if (c->precision != MOE_PREC_BF16 && c->precision != MOE_PREC_MXFP8) return MOE_ERR_UNSUPPORTED;
-  if (c->flags & ~(MOE_FLAG_PERSISTENT | MOE_FLAG_MXFP8_WGRAD)) return MOE_ERR_INVALID_ARG;
+  if (c->flags & ~(MOE_FLAG_PERSISTENT | MOE_FLAG_MXFP8_WGRAD | MOE_FLAG_BF16_DW))
+    return MOE_ERR_INVALID_ARG;
   if ((c->flags & MOE_FLAG_MXFP8_WGRAD) && c->precision != MOE_PREC_MXFP8)
     return MOE_ERR_INVALID_ARG;
   return MOE_OK;
@@ -491,8 +492,8 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
                  const int32_t* offsets, const int32_t* row_src, const int32_t* tk_row,
                  const int32_t* topk_idx, const float* topk_w, const void* w_router,
                  const void* w1, const void* w2, const void* wq, size_t wq_bytes,
-                 const void* saved, size_t saved_bytes, const void* dy, void* dx, float* dw1,
-                 float* dw2, float* dwr, float* d_topk_w, int32_t accumulate, void* workspace,
+                 const void* saved, size_t saved_bytes, const void* dy, void* dx, void* dw1,
+                 void* dw2, float* dwr, float* d_topk_w, int32_t accumulate, void* workspace,
                  size_t ws_bytes, moe_stream_t stream) {
   int st = check_mode(cfg);
   if (st) return st;
@@ -510,6 +511,7 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
   if ((st = check_device())) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool pers = cfg->flags & MOE_FLAG_PERSISTENT;
+  const int bdw = (cfg->flags & MOE_FLAG_BF16_DW) ? 1 : 0;  // dW stored as bf16
   const int Tk = cfg->T * cfg->k, d = cfg->d, I = cfg->I, E = cfg->E, k = cfg->k;
   const uint8_t* slot_base = at<uint8_t>(ring, (size_t)slot * Y.slot);
   const uint16_t* xp = Y.mx ? nullptr : reinterpret_cast<const uint16_t*>(slot_base);
@@ -565,7 +567,7 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
       if (!L.err)
         L(launch_quant_seg(sa, offsets, poff, E, I, Y.P, rq, rqs, "bwd_down_wgrad_qR", s));
       if (!L.err)
-        L(launch_mx_wgrad({lq, lqs, rq, rqs, dw2, poff, E, d, I, Y.P, accumulate,
+        L(launch_mx_wgrad({lq, lqs, rq, rqs, dw2, poff, E, d, I, Y.P, accumulate, bdw,
                            "bwd_down_wgrad"},
                           pers, s));
       if (!L.err)
@@ -573,20 +575,20 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
       if (!L.err)
         L(launch_quant_seg(sxp, offsets, poff, E, d, Y.P, rq, rqs, "bwd_gate_wgrad_qR", s));
       if (!L.err)
-        L(launch_mx_wgrad({lq, lqs, rq, rqs, dw1, poff, E, 2 * I, d, Y.P, accumulate,
+        L(launch_mx_wgrad({lq, lqs, rq, rqs, dw1, poff, E, 2 * I, d, Y.P, accumulate, bdw,
                            "bwd_gate_wgrad"},
                           pers, s));
     } else {
       if (!L.err)
         L(launch_wgrad({dyw, A, nullptr, nullptr, dw2, offsets, at<int4>(workspace, Y.wg_table2),
-                        wg_count + 1, E, d, I, accumulate, false, "bwd_down_wgrad",
+                        wg_count + 1, E, d, I, accumulate, bdw, false, "bwd_down_wgrad",
                         "wgrad_sched_down"},
                        s));
       // the gate wgrad goes first: until the gate dgrad writes dXp, that buffer holds the bf16
       // image of the big experts' fp8 Xp rows for the big-expert wgrad kernel
       if (!L.err)
         L(launch_wgrad({dH, nullptr, xp8, xps, dw1, offsets, at<int4>(workspace, Y.wg_table1),
-                        wg_count, E, 2 * I, d, accumulate, true, "bwd_gate_wgrad",
+                        wg_count, E, 2 * I, d, accumulate, bdw, true, "bwd_gate_wgrad",
                         "wgrad_sched_gate", dXp},
                        s));
     }
@@ -604,13 +606,13 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
       L(launch_dw_router(dwpart, Y.nIt, tk_row, topk_w, cfg->T, k, d_topk_w, dl_pos, routed, s));
     if (!L.err)
       L(launch_wgrad({dyw, A, nullptr, nullptr, dw2, offsets, at<int4>(workspace, Y.wg_table2),
-                      wg_count + 1, E, d, I, accumulate, false, "bwd_down_wgrad",
+                      wg_count + 1, E, d, I, accumulate, bdw, false, "bwd_down_wgrad",
                       "wgrad_sched_down"},
                      s));
     if (!L.err) L(launch_bwd_gate_dgrad({dH, w1p, dXp, offsets, sched, d, I, Tk, E}, pers, s));
     if (!L.err)
       L(launch_wgrad({dH, xp, nullptr, nullptr, dw1, offsets, at<int4>(workspace, Y.wg_table1),
-                      wg_count, E, 2 * I, d, accumulate, true, "bwd_gate_wgrad",
+                      wg_count, E, 2 * I, d, accumulate, bdw, true, "bwd_gate_wgrad",
                       "wgrad_sched_gate"},
                      s));
   }

@@ -78,6 +78,57 @@ MOE_DEV uint4 nt_load16(const void* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Four consecutive fp32 weight-gradient values stored at p; with ACC added to what p holds.
+template <bool ACC>
+MOE_DEV void store_dw4(float* p, const f32x4& v) {
+  float4 o = make_float4(v[0], v[1], v[2], v[3]);
+  if (ACC) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    o.x += q.x;
+    o.y += q.y;
+    o.z += q.z;
+    o.w += q.w;
+  }
+  *reinterpret_cast<float4*>(p) = o;
+}
+
+// Two side-by-side 16 x 16 MFMA output blocks (columns c0 .. c0 + 31) stored as bf16, with ACC
+// added in fp32 to what is stored. Lane l holds row l % 16, columns c0 + 4 (l / 16) .. + 3 of
+// lo and c0 + 16 + 4 (l / 16) .. + 3 of hi. Lanes l and l ^ 16 swap one block's values so that
+// each lane holds 8 consecutive columns and the four lanes of a row cover its 64 contiguous
+// bytes: the memory system then takes one 64-byte write per row, where the blocks' own 8-byte
+// pieces made two of 32 bytes (write requests, not bytes, set the rate of a bf16 dW store).
+// row: this lane's row at column c0 (64-byte aligned).
+template <bool ACC>
+MOE_DEV void store_dw8_bf16(uint16_t* row, const f32x4& lo, const f32x4& hi, int lane) {
+  const int g = lane / 16;
+  const bool even = (g & 1) == 0;
+  float send[4], recv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) send[q] = even ? hi[q] : lo[q];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) recv[q] = __shfl_xor(send[q], 16);
+  float o[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    o[q] = even ? lo[q] : recv[q];
+    o[4 + q] = even ? recv[q] : hi[q];
+  }
+  // even g: columns 4 g .. 4 g + 7; odd g: 16 + 4 (g - 1) .. + 7
+  uint4* p = reinterpret_cast<uint4*>(row + (even ? 4 * g : 12 + 4 * g));
+  if (ACC) {
+    const uint4 v = *p;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[2 * q] += bf2f_lo(w[q]);
+      o[2 * q + 1] += bf2f_hi(w[q]);
+    }
+  }
+  *p = make_uint4(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]), pack_bf2(o[4], o[5]),
+                  pack_bf2(o[6], o[7]));
+}
+
 MOE_DEV float silu(float g) { return g / (1.0f + __expf(-g)); }
 MOE_DEV float sigmoid(float g) { return 1.0f / (1.0f + __expf(-g)); }
 

@@ -19,6 +19,7 @@
 // Determinism: every output element is produced by exactly one workgroup, which reduces K in a
 // fixed order. There are no atomics and no split-K.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "dma.h"
@@ -840,7 +841,8 @@ struct MxBwdGateDgrad {
 // quant_seg_kernel; codes past the count are zero). A 128 x 128 tile of one expert's dW per
 // workgroup; its K loop walks the expert's 128-position chunks in order. An expert with no
 // rows has no chunks: its tile is written as zeros (overwrite) or left as it is (accumulate).
-template <bool ACC>
+// BF: dW is stored as bf16.
+template <bool ACC, bool BF>
 struct MxWgrad {
   static constexpr const char* kName = "bwd_wgrad_mx";
   using G = GeoMx<128, 128, 1, 4>;
@@ -849,7 +851,7 @@ struct MxWgrad {
     const uint8_t* lqs;
     const uint8_t* rq;
     const uint8_t* rqs;
-    float* dw;
+    void* dw;
     const int32_t* poff;
     int E, Mdim, Ndim, P;
   };
@@ -903,24 +905,27 @@ struct MxWgrad {
                                uint8_t*) {
     if (t.e < 0 || (ACC && a.poff[t.e + 1] == a.poff[t.e])) return;  // nothing to write / add
     const int lane = threadIdx.x % kWave, wn = (threadIdx.x / kWave) % G::WAVES_N;
-    // lane's first element; row block mb adds 16 rows, column block nb 16 columns
-    float* out = a.dw + ((size_t)t.e * a.Mdim + t.m0 + lane % 16) * a.Ndim + t.n0 + wn * G::WN +
-                 4 * (lane / 16);
     const size_t rstep = (size_t)16 * a.Ndim;
+    if constexpr (BF) {
+      // lane's row at the wave's first column; pairs of column blocks share 64-byte row pieces
+      uint16_t* row = static_cast<uint16_t*>(a.dw) +
+                      ((size_t)t.e * a.Mdim + t.m0 + lane % 16) * a.Ndim + t.n0 + wn * G::WN;
 #pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb) {
+      for (int mb = 0; mb < G::MB; ++mb) {
 #pragma unroll
-      for (int nb = 0; nb < G::NB; ++nb) {
-        float4* dst = reinterpret_cast<float4*>(out + mb * rstep + nb * 16);
-        float4 v = make_float4(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]);
-        if (ACC) {
-          const float4 o = *dst;
-          v.x += o.x;
-          v.y += o.y;
-          v.z += o.z;
-          v.w += o.w;
-        }
-        *dst = v;
+        for (int nb = 0; nb < G::NB; nb += 2)
+          store_dw8_bf16<ACC>(row + mb * rstep + nb * 16, acc[mb][nb], acc[mb][nb + 1], lane);
+      }
+    } else {
+      // lane's first element; row block mb adds 16 rows, column block nb 16 columns
+      float* out = static_cast<float*>(a.dw) +
+                   ((size_t)t.e * a.Mdim + t.m0 + lane % 16) * a.Ndim + t.n0 + wn * G::WN +
+                   4 * (lane / 16);
+#pragma unroll
+      for (int mb = 0; mb < G::MB; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb)
+          store_dw4<ACC>(out + mb * rstep + nb * 16, acc[mb][nb]);
       }
     }
   }
@@ -1349,14 +1354,21 @@ hipError_t launch_bwd_gate_dgrad_mx(const GemmMxGateDgradArgs& x, bool persisten
   return launch<MxBwdGateDgrad>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
 }
 
+template <bool ACC, bool BF>
+hipError_t launch_mx_wgrad_as(const GemmMxWgradArgs& x, int max_tiles, bool persistent,
+                              hipStream_t s) {
+  typename MxWgrad<ACC, BF>::Args a{x.lq, x.lqs, x.rq, x.rqs, x.dw, x.poff, x.E, x.Mdim, x.Ndim,
+                                    x.P};
+  return launch_named<MxWgrad<ACC, BF>>(a, max_tiles, persistent, x.name, s);
+}
+
 hipError_t launch_mx_wgrad(const GemmMxWgradArgs& x, bool persistent, hipStream_t s) {
   const int max_tiles = (x.E * (x.Mdim / 128) * (x.Ndim / 128) + kXcds - 1) / kXcds * kXcds;
-  if (x.accumulate) {
-    MxWgrad<true>::Args a{x.lq, x.lqs, x.rq, x.rqs, x.dw, x.poff, x.E, x.Mdim, x.Ndim, x.P};
-    return launch_named<MxWgrad<true>>(a, max_tiles, persistent, x.name, s);
-  }
-  MxWgrad<false>::Args a{x.lq, x.lqs, x.rq, x.rqs, x.dw, x.poff, x.E, x.Mdim, x.Ndim, x.P};
-  return launch_named<MxWgrad<false>>(a, max_tiles, persistent, x.name, s);
+  if (x.bf16_dw)
+    return x.accumulate ? launch_mx_wgrad_as<true, true>(x, max_tiles, persistent, s)
+                        : launch_mx_wgrad_as<false, true>(x, max_tiles, persistent, s);
+  return x.accumulate ? launch_mx_wgrad_as<true, false>(x, max_tiles, persistent, s)
+                      : launch_mx_wgrad_as<false, false>(x, max_tiles, persistent, s);
 }
 
 }  // namespace moe

@@ -190,11 +190,11 @@ struct WgradArgs {
   const uint16_t* R;  // [T*k, Ndim], position-major (bf16), or null when R8 is given
   const uint8_t* R8;  // MXFP8 R: codes [T*k, Ndim] (gate wgrad only), or null
   const uint8_t* R8s; // its scales [T*k, Ndim/32]
-  float* dw;          // [E, Mdim, Ndim]
+  void* dw;           // [E, Mdim, Ndim], fp32 or (bf16_dw) bf16
   const int32_t* offsets;
   int4* table;        // task table, wgrad_table_entries(...) entries
   int32_t* count;     // task count (device)
-  int E, Mdim, Ndim, accumulate;
+  int E, Mdim, Ndim, accumulate, bf16_dw;
   bool gate;  // dW1 (true) or dW2 (false)
   const char* name;
   const char* name_sched;
@@ -240,9 +240,9 @@ struct GemmMxWgradArgs {
   const uint8_t* lqs;
   const uint8_t* rq;
   const uint8_t* rqs;
-  float* dw;
+  void* dw;  // fp32 or (bf16_dw) bf16
   const int32_t* poff;
-  int E, Mdim, Ndim, P, accumulate;
+  int E, Mdim, Ndim, P, accumulate, bf16_dw;
   const char* name;
 };
 hipError_t launch_mx_wgrad(const GemmMxWgradArgs& a, bool persistent, hipStream_t s);

@@ -29,6 +29,8 @@
 //
 // Determinism: every dW element belongs to exactly one task, whose workgroup reduces K in
 // ascending position order. No atomics, no split-K.
+#include <type_traits>
+
 #include "common.h"
 #include "dma.h"
 #include "kernels.h"
@@ -55,7 +57,7 @@ struct Args {
   const uint16_t* R;  // [T*k, Ndim] bf16, or (R8) fp8 codes R8 [T*k, Ndim] with scales R8s
   const uint8_t* R8;
   const uint8_t* R8s; // [T*k, Ndim/32]
-  float* dw;          // [E, Mdim, Ndim]
+  void* dw;           // [E, Mdim, Ndim], fp32 or (BF kernels) bf16
   const int32_t* offsets;
   const int4* table;  // (expert, first row, first n-tile, n-tile count)
   const int32_t* count;
@@ -147,26 +149,30 @@ struct Mover {
 constexpr int WMR = 64;        // dW rows per consumer wave (BM / 64 x BN / 64 waves)
 constexpr int MBW = WMR / 16;  // 16-row MFMA blocks per consumer wave
 
-template <bool ACC>
-MOE_DEV void store_tile(const Args& a, float* out, int n0, const f32x4 (&acc)[MBW][4]) {
+// dW element type: fp32, or bf16 in the BF kernels
+template <bool BF>
+using DwT = std::conditional_t<BF, uint16_t, float>;
+
+// out: the element offset of the task's first dW row (column 0)
+template <bool ACC, bool BF>
+MOE_DEV void store_tile(const Args& a, size_t out, int n0, const f32x4 (&acc)[MBW][4]) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int wm = wave / (BN / 64), wn = wave % (BN / 64);
+  DwT<BF>* base = static_cast<DwT<BF>*>(a.dw) + out;
 #pragma unroll
   for (int mb = 0; mb < MBW; ++mb) {
     const int m = wm * WMR + mb * 16 + lane % 16;
+    if constexpr (BF) {
+      uint16_t* row = base + (size_t)m * a.Ndim + n0 + wn * 64;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int n = n0 + wn * 64 + nb * 16 + 4 * (lane / 16);
-      float4* dst = reinterpret_cast<float4*>(out + (size_t)m * a.Ndim + n);
-      float4 v = make_float4(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]);
-      if (ACC) {
-        const float4 o = *dst;
-        v.x += o.x;
-        v.y += o.y;
-        v.z += o.z;
-        v.w += o.w;
+      for (int nb = 0; nb < 4; nb += 2)
+        store_dw8_bf16<ACC>(row + nb * 16, acc[mb][nb], acc[mb][nb + 1], lane);
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int n = n0 + wn * 64 + nb * 16 + 4 * (lane / 16);
+        store_dw4<ACC>(base + (size_t)m * a.Ndim + n, acc[mb][nb]);
       }
-      *dst = v;
     }
   }
 }
@@ -184,8 +190,9 @@ MOE_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::
 // c - 1, so every load has kProducers - 1 iterations to arrive. Producers and consumers run
 // separate loops with the same number of barriers per task (1 + nt * nk); the role is a
 // wave-uniform scalar, so each wave branches over the other role's code.
-// GATE only separates the two instances (dW1 and dW2) for profilers. R8: R is MXFP8.
-template <bool ACC, bool GATE, bool R8>
+// GATE only separates the two instances (dW1 and dW2) for profilers. R8: R is MXFP8. BF: dW is
+// stored as bf16.
+template <bool ACC, bool GATE, bool R8, bool BF>
 __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Args a,
                                                            const int4* __restrict__ table,
                                                            const int32_t* __restrict__ offsets,
@@ -288,7 +295,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
       const TaskInfo t = task_at(ti);
       const int nk = t.nk, total = t.total;
       const bool resident = t.resident;
-      float* out = a.dw + ((size_t)t.e * a.Mdim + t.m0) * a.Ndim;
+      const size_t out = ((size_t)t.e * a.Mdim + t.m0) * a.Ndim;
       f32x4 acc[MBW][4];
 #pragma unroll
       for (int i = 0; i < MBW; ++i)
@@ -296,7 +303,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
         for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (nk == 0) {  // an expert with no rows: its dW block is zero
         if (!ACC)
-          for (int j = 0; j < t.nt; ++j) store_tile<false>(a, out, t.col(j, ntn), acc);
+          for (int j = 0; j < t.nt; ++j) store_tile<false, BF>(a, out, t.col(j, ntn), acc);
         continue;
       }
       lds_barrier();
@@ -316,7 +323,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
           for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(bf[nb], af, acc[mb][nb]);
         }
         if (kt == nk - 1) {
-          store_tile<ACC>(a, out, t.col(j, ntn), acc);
+          store_tile<ACC, BF>(a, out, t.col(j, ntn), acc);
 #pragma unroll
           for (int i = 0; i < MBW; ++i)
 #pragma unroll
@@ -402,7 +409,7 @@ __global__ void __launch_bounds__(1024) wgrad_sched_kernel(const int32_t* __rest
 struct WgBigArgs {
   const uint16_t* L;       // [T*k, Mdim]
   const uint16_t* R;       // [T*k, Ndim]
-  float* dw;               // [E, Mdim, Ndim]
+  void* dw;                // [E, Mdim, Ndim], fp32 or (BF) bf16
   const int4* big;         // count, then the listed experts (x = expert)
   const int32_t* offsets;
   int Mdim, Ndim;
@@ -414,8 +421,8 @@ struct WgBigTile {
 // Tiles of the listed experts, expert by expert in list order (decreasing rows); inside an
 // expert, groups of four 256-row blocks take each 256-column block in turn. Round r gives XCD x
 // the tiles [r G + x G/8, r G + (x+1) G/8): neighbouring tiles share operand panels in its L2.
-// GATE only separates the two instances (dW1 and dW2) for profilers.
-template <bool ACC, bool GATE>
+// GATE only separates the two instances (dW1 and dW2) for profilers; BF stores dW as bf16.
+template <bool ACC, bool GATE, bool BF>
 struct DmaWgrad {
   using Args = WgBigArgs;
   using Tile = WgBigTile;
@@ -457,23 +464,22 @@ struct DmaWgrad {
   static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[8][4]) {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int wm = wave / 4, wn = wave % 4;
-    float* out = a.dw + ((size_t)t.e * a.Mdim + t.m0) * a.Ndim + t.n0;
+    DwT<BF>* out =
+        static_cast<DwT<BF>*>(a.dw) + ((size_t)t.e * a.Mdim + t.m0) * a.Ndim + t.n0;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       const int m = wm * 128 + mb * 16 + lane % 16;
+      if constexpr (BF) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int n = wn * 64 + nb * 16 + 4 * (lane / 16);
-        float4* dst = reinterpret_cast<float4*>(out + (size_t)m * a.Ndim + n);
-        float4 v = make_float4(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]);
-        if (ACC) {
-          const float4 o = *dst;
-          v.x += o.x;
-          v.y += o.y;
-          v.z += o.z;
-          v.w += o.w;
+        for (int nb = 0; nb < 4; nb += 2)
+          store_dw8_bf16<ACC>(out + (size_t)m * a.Ndim + wn * 64 + nb * 16, acc[mb][nb],
+                              acc[mb][nb + 1], lane);
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int n = wn * 64 + nb * 16 + 4 * (lane / 16);
+          store_dw4<ACC>(out + (size_t)m * a.Ndim + n, acc[mb][nb]);
         }
-        *dst = v;
       }
     }
   }
@@ -513,7 +519,8 @@ int resident_grid() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&wgrad_kernel<false, false, false>), kThreads, 0) != hipSuccess)
+            &per_cu, reinterpret_cast<const void*>(&wgrad_kernel<false, false, false, false>),
+            kThreads, 0) != hipSuccess)
       return 0;
     grid = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
   }
@@ -550,10 +557,19 @@ hipError_t launch_wgrad(const WgradArgs& x, hipStream_t s) {
   Args a{x.L, x.R, x.R8, x.R8s, x.dw, x.offsets, table, x.count, x.Mdim, x.Ndim, x.accumulate};
   {
     TraceScope trace(x.name, s);
-    auto kern = x.R8 ? (x.accumulate ? wgrad_kernel<true, true, true> : wgrad_kernel<false, true, true>)
-                     : x.accumulate
-                         ? (x.gate ? wgrad_kernel<true, true, false> : wgrad_kernel<true, false, false>)
-                         : (x.gate ? wgrad_kernel<false, true, false> : wgrad_kernel<false, false, false>);
+    using K = void (*)(const Args, const int4*, const int32_t*, const int32_t*);
+    // [accumulate][gate][fp8 R][bf16 dW]; an fp8 R comes with the gate wgrad only
+    static const K kernels[2][2][2][2] = {
+        {{{wgrad_kernel<false, false, false, false>, wgrad_kernel<false, false, false, true>},
+          {nullptr, nullptr}},
+         {{wgrad_kernel<false, true, false, false>, wgrad_kernel<false, true, false, true>},
+          {wgrad_kernel<false, true, true, false>, wgrad_kernel<false, true, true, true>}}},
+        {{{wgrad_kernel<true, false, false, false>, wgrad_kernel<true, false, false, true>},
+          {nullptr, nullptr}},
+         {{wgrad_kernel<true, true, false, false>, wgrad_kernel<true, true, false, true>},
+          {wgrad_kernel<true, true, true, false>, wgrad_kernel<true, true, true, true>}}}};
+    const K kern = kernels[x.accumulate ? 1 : 0][x.gate ? 1 : 0][x.R8 ? 1 : 0][x.bf16_dw ? 1 : 0];
+    if (!kern) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, s, a, table, x.offsets, x.count);
   }
   err = hipGetLastError();
@@ -568,11 +584,18 @@ hipError_t launch_wgrad(const WgradArgs& x, hipStream_t s) {
   // the big experts' tile count is known on the device only: a resident grid walks it
   const WgBigArgs ab{x.L, x.R8 ? x.Rx : x.R, x.dw, big, x.offsets, x.Mdim, x.Ndim};
   constexpr int kAnyTiles = 1 << 30;
+  if (x.bf16_dw) {
+    if (x.accumulate)
+      return x.gate ? launch_dma<DmaWgrad<true, true, true>>(ab, kAnyTiles, true, s)
+                    : launch_dma<DmaWgrad<true, false, true>>(ab, kAnyTiles, true, s);
+    return x.gate ? launch_dma<DmaWgrad<false, true, true>>(ab, kAnyTiles, true, s)
+                  : launch_dma<DmaWgrad<false, false, true>>(ab, kAnyTiles, true, s);
+  }
   if (x.accumulate)
-    return x.gate ? launch_dma<DmaWgrad<true, true>>(ab, kAnyTiles, true, s)
-                  : launch_dma<DmaWgrad<true, false>>(ab, kAnyTiles, true, s);
-  return x.gate ? launch_dma<DmaWgrad<false, true>>(ab, kAnyTiles, true, s)
-                : launch_dma<DmaWgrad<false, false>>(ab, kAnyTiles, true, s);
+    return x.gate ? launch_dma<DmaWgrad<true, true, false>>(ab, kAnyTiles, true, s)
+                  : launch_dma<DmaWgrad<true, false, false>>(ab, kAnyTiles, true, s);
+  return x.gate ? launch_dma<DmaWgrad<false, true, false>>(ab, kAnyTiles, true, s)
+                : launch_dma<DmaWgrad<false, false, false>>(ab, kAnyTiles, true, s);
 }
 
 }  // namespace moe

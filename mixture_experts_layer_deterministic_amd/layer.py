@@ -6,9 +6,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (MOE_FLAG_MXFP8_WGRAD, MOE_FLAG_PERSISTENT, MOE_PREC_BF16, MOE_PREC_MXFP8, make_cfg, moe_backward,
-               moe_forward, moe_forward_fused, moe_permute, moe_query, moe_quantize_weights,
-               moe_route)
+from . import (MOE_FLAG_BF16_DW, MOE_FLAG_MXFP8_WGRAD, MOE_FLAG_PERSISTENT, MOE_PREC_BF16,
+               MOE_PREC_MXFP8, make_cfg, moe_backward, moe_forward, moe_forward_fused, moe_permute,
+               moe_query, moe_quantize_weights, moe_route)
 
 
 class MoeLayer:
@@ -17,14 +17,14 @@ class MoeLayer:
     ``ring_slots`` slots of T*k permuted rows make up the ring. Forward writes slot ``slot``,
     and backward reads the slot its batch was permuted into. With ``precision=MOE_PREC_MXFP8``
     the layer also owns the quantised-weight buffer ``wq``; ``quantize_weights`` fills it, and
-    ``mx_wgrad`` makes the weight gradients MXFP8 too.
+    ``mx_wgrad`` makes the weight gradients MXFP8 too. ``bf16_dw`` keeps dw1 and dw2 in bf16.
     """
 
     def __init__(self, T, d, E, k, I, device="cuda", ring_slots=1, persistent=False,
-                 precision=MOE_PREC_BF16, mx_wgrad=False):
+                 precision=MOE_PREC_BF16, mx_wgrad=False, bf16_dw=False):
         self.T, self.d, self.E, self.k, self.I = T, d, E, k, I
-        flags = (MOE_FLAG_PERSISTENT if persistent else 0) | (MOE_FLAG_MXFP8_WGRAD if mx_wgrad
-                                                               else 0)
+        flags = ((MOE_FLAG_PERSISTENT if persistent else 0) |
+                 (MOE_FLAG_MXFP8_WGRAD if mx_wgrad else 0) | (MOE_FLAG_BF16_DW if bf16_dw else 0))
         self.cfg = make_cfg(T, d, E, k, I, precision, flags)
         s = moe_query(self.cfg)
         self.sizes = s
@@ -44,8 +44,9 @@ class MoeLayer:
         self.y = torch.empty(T, d, dtype=bf, device=dev)
         self.dx = torch.empty(T, d, dtype=bf, device=dev)
         self.d_topk_w = torch.empty(T, k, dtype=f32, device=dev)
-        self.dw1 = torch.zeros(E, 2 * I, d, dtype=f32, device=dev)
-        self.dw2 = torch.zeros(E, d, I, dtype=f32, device=dev)
+        dwt = bf if bf16_dw else f32
+        self.dw1 = torch.zeros(E, 2 * I, d, dtype=dwt, device=dev)
+        self.dw2 = torch.zeros(E, d, I, dtype=dwt, device=dev)
         self.dwr = torch.zeros(E, d, dtype=f32, device=dev)
         self.mx = precision == MOE_PREC_MXFP8
         self.wq = torch.empty(s.wq, dtype=u8, device=dev) if self.mx else None

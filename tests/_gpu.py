@@ -28,12 +28,12 @@ def is_mx(inp):
     return inp["cfg"].get("precision") == "mxfp8"
 
 
-def run_gpu(inp, persistent=False, slot=0, ring_slots=1):
+def run_gpu(inp, persistent=False, slot=0, ring_slots=1, bf16_dw=False):
     cfg = inp["cfg"]
     T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
     prec = m.MOE_PREC_MXFP8 if is_mx(inp) else m.MOE_PREC_BF16
     L = MoeLayer(T, d, E, k, I, device=DEV, ring_slots=ring_slots, persistent=persistent,
-                 precision=prec, mx_wgrad=bool(cfg.get("mx_wgrad")))
+                 precision=prec, mx_wgrad=bool(cfg.get("mx_wgrad")), bf16_dw=bf16_dw)
     if is_mx(inp):
         L.quantize_weights(inp["W1"], inp["W2"])
     wr = inp.get("Wr")
@@ -44,18 +44,18 @@ def run_gpu(inp, persistent=False, slot=0, ring_slots=1):
     return L
 
 
-def run_oracle(inp):
+def run_oracle(inp, dw_dtype="fp32"):
     X, W1, W2, dY = (_np(inp[n]) for n in ("X", "W1", "W2", "dY"))
     prec = "mxfp8" if is_mx(inp) else "bf16"
     wg = "mxfp8" if inp["cfg"].get("mx_wgrad") else "bf16"
     if "Wr" in inp:
         Wr = _np(inp["Wr"])
         f = oracle.forward(X, W1, W2, Wr=Wr, k=inp["cfg"]["k"], precision=prec)
-        b = oracle.backward(f, X, W1, W2, dY, Wr=Wr, wgrad=wg)
+        b = oracle.backward(f, X, W1, W2, dY, Wr=Wr, wgrad=wg, dw_dtype=dw_dtype)
     else:
         f = oracle.forward(X, W1, W2, topk_idx=_np(inp["topk_idx"]), topk_w=_np(inp["topk_w"]),
                            precision=prec)
-        b = oracle.backward(f, X, W1, W2, dY, wgrad=wg)
+        b = oracle.backward(f, X, W1, W2, dY, wgrad=wg, dw_dtype=dw_dtype)
     return f, b
 
 

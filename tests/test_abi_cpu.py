@@ -189,3 +189,15 @@ def test_mxfp8_wgrad_flag_needs_mxfp8_mode_and_sizes_its_workspace():
                                  m.MOE_FLAG_MXFP8_WGRAD))
     P = (2048 * 8 + 256 * 127 + 127) // 128 * 128  # padded positions of all expert segments
     assert mxw.workspace - plain.workspace >= (2 * 4096 * P + 2 * 4096 * P // 32) // 2
+
+
+def test_bf16_dw_flag_is_accepted_in_both_precisions_and_changes_no_size():
+    for prec, extra in ((m.MOE_PREC_BF16, 0), (m.MOE_PREC_MXFP8, 0),
+                        (m.MOE_PREC_MXFP8, m.MOE_FLAG_MXFP8_WGRAD)):
+        base = m.moe_query(m.make_cfg(300, 512, 16, 3, 256, prec, extra))
+        got = m.moe_query(m.make_cfg(300, 512, 16, 3, 256, prec, extra | m.MOE_FLAG_BF16_DW))
+        for f in ("ring_slot", "saved", "workspace", "wq"):
+            assert getattr(got, f) == getattr(base, f), (prec, extra, f)
+    with pytest.raises(m.MoeError) as ei:
+        m.moe_query(m.make_cfg(64, 256, 8, 2, 128, m.MOE_PREC_BF16, 8))  # an unknown flag bit
+    assert ei.value.status == -1
