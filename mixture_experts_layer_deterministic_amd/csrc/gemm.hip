@@ -276,10 +276,12 @@ struct GeoMx {
   static constexpr int STAGE = SC_OFF + (BM + BN) * 4;
   static constexpr int kSmem = 2 * STAGE;
   static constexpr bool kMx = true;
-  static constexpr int THREADS = kThreads;
+  static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
   static constexpr int kWavesPerEU = 2;
-  static_assert(WAVES_M * WAVES_N == 4, "4 waves per workgroup");
+  static_assert(WAVES_M * WAVES_N == 4 || WAVES_M * WAVES_N == 8, "4 or 8 waves per workgroup");
 };
+// Full 256-row blocks on the direct-to-LDS kernel (dmx_kernel): eight waves of 128 x 64.
+using GeoMxBig = GeoMx<256, 256, 2, 4>;
 
 // Byte offset of 16-byte chunk `chunk` of row `row` in an fp8 code tile of 128-byte rows, with
 // the chunks permuted per row as in rowswz (chunk c of row r at c ^ (r & 7)): fragment reads
@@ -443,13 +445,17 @@ MOE_DEV uint32_t mx_pack4(const float* v, float inv) {
   return e4m3x2(v[0] * inv, v[1] * inv) | (e4m3x2(v[2] * inv, v[3] * inv) << 16);
 }
 
-// Problem 1 (MXFP8): forward gate/up with SwiGLU. Waves form 2 x 2: wave (wm, wn) owns rows
-// [64 wm, +64) and gate columns [32 wn, +32) of the tile's 64 with the matching up columns, so
-// one row's 32 consecutive A columns sit in four lanes of one wave and A is quantised (along I,
-// for the down GEMM) in registers.
-struct MxFwdGateUp {
+// Problem 1 (MXFP8): forward gate/up with SwiGLU. A tile covers BN / 2 gate columns and the
+// matching up columns. Wave (wm, wn) owns rows [WM wm, +WM) and gate columns [32 wn, +32) of the
+// tile's with the matching up columns, so one row's 32 consecutive A columns sit in four lanes
+// of one wave and A is quantised (along I, for the down GEMM) in registers. G is the 128-row
+// tile (2 x 2 waves) or the 256-row one of dmx_kernel (2 x 4 waves).
+template <class G_>
+struct MxFwdGateUpT {
   static constexpr const char* kName = "fwd_gateup";
-  using G = GeoMx<128, 128, 2, 2>;
+  using G = G_;
+  static constexpr int kA = G::BN / 2;  // A columns per tile
+  static_assert(G::WN == 64, "each wave holds 32 gate and 32 up columns");
   struct Args {
     const uint8_t* xp8;  // [T*k, d] codes (ring slot)
     const uint8_t* xps;  // [T*k, d/32]
@@ -467,19 +473,25 @@ struct MxFwdGateUp {
     MTile m;
     int n0;
   };
-  static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.I / 64); }
+  static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.I / kA); }
   static MOE_DEV Tile decode(const Args& a, int lt) {
-    const int ntc = a.I / 64;
+    const int ntc = a.I / kA;
     Tile t;
-    t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
-    t.n0 = (lt % ntc) * 64;
+    if constexpr (G::BM > 128) {  // grouped order: row blocks of one expert share weight panels
+      const int2 mn = tile_mn<true>(lt, a.sched[0].x, ntc);
+      t.m = decode_mtile(a.sched, a.offsets, mn.x, G::BM);
+      t.n0 = mn.y * kA;
+    } else {
+      t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
+      t.n0 = (lt % ntc) * kA;
+    }
     return t;
   }
   static MOE_DEV int num_k(const Args& a, const Tile&) { return a.d / G::BK; }
   static MOE_DEV int k_first(const Tile&, int) { return 0; }
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) {
-    return nb < 2 ? wn * 32 + nb * 16 : 64 + wn * 32 + (nb - 2) * 16;
+    return nb < 2 ? wn * 32 + nb * 16 : kA + wn * 32 + (nb - 2) * 16;
   }
   struct Loader {
     LoadK8<G::BM, G::LDK> la;
@@ -493,7 +505,7 @@ struct MxFwdGateUp {
       const size_t wrow0 = (size_t)t.m.e * 2 * I;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
-      auto wrow = [=](int n) { return wrow0 + (n < 64 ? n0 + n : I + n0 + n - 64); };
+      auto wrow = [=](int n) { return wrow0 + (n < kA ? n0 + n : I + n0 + n - kA); };
       lb.init([&](int n) { return w8 + wrow(n) * d; },
               [&](int n) { return ws + wrow(n) * (d / 32); }, d);
     }
@@ -547,10 +559,14 @@ struct MxFwdGateUp {
   }
 };
 
+using MxFwdGateUp = MxFwdGateUpT<GeoMx<128, 128, 2, 2>>;
+using MxFwdGateUpBig = MxFwdGateUpT<GeoMxBig>;
+
 // Problem 2 (MXFP8): forward down. O[pos] = A[pos] . W2[e]^T, with A and W2 quantised along I.
-struct MxFwdDown {
+template <class G_>
+struct MxFwdDownT {
   static constexpr const char* kName = "fwd_down";
-  using G = GeoMx<128, 128, 1, 4>;
+  using G = G_;
   struct Args {
     const uint8_t* aq;   // [T*k, I]
     const uint8_t* aqs;  // [T*k, I/32]
@@ -602,10 +618,11 @@ struct MxFwdDown {
   };
   static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
                                uint8_t*) {
-    const int lane = threadIdx.x % kWave, wn = (threadIdx.x / kWave) % G::WAVES_N;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
 #pragma unroll
     for (int mb = 0; mb < G::MB; ++mb) {
-      const int m = mb * 16 + lane % 16;
+      const int m = wm * G::WM + mb * 16 + lane % 16;
       if (m >= t.m.mcount) continue;
       const size_t pos = t.m.row0 + m;
 #pragma unroll
@@ -619,6 +636,8 @@ struct MxFwdDown {
     }
   }
 };
+using MxFwdDown = MxFwdDownT<GeoMx<128, 128, 1, 4>>;
+using MxFwdDownBig = MxFwdDownT<GeoMxBig>;
 
 // Problem 3 (MXFP8): down dgrad, dA'[pos] = dY[t] . W2[e] with dY and W2 quantised along d
 // (W2 stored transposed, [E, I, d]). The epilogue is the BF16 one (router-weight-gradient
@@ -767,9 +786,10 @@ struct MxBwdDownDgrad {
 
 // Problem 4 (MXFP8): gate/up dgrad, dXp[pos] = dH[pos] . W1[e] with dH and W1 quantised along
 // 2I (W1 stored transposed, [E, d, 2I]).
-struct MxBwdGateDgrad {
+template <class G_>
+struct MxBwdGateDgradT {
   static constexpr const char* kName = "bwd_gate_dgrad";
-  using G = GeoMx<128, 128, 1, 4>;
+  using G = G_;
   struct Args {
     const uint8_t* dhq;  // [T*k, 2I]
     const uint8_t* dhs;  // [T*k, 2I/32]
@@ -787,9 +807,10 @@ struct MxBwdGateDgrad {
   static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.d / G::BN); }
   static MOE_DEV Tile decode(const Args& a, int lt) {
     const int ntc = a.d / G::BN;
+    const int2 mn = tile_mn<(G::BM > 128)>(lt, a.sched[0].x, ntc);
     Tile t;
-    t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
-    t.n0 = (lt % ntc) * G::BN;
+    t.m = decode_mtile(a.sched, a.offsets, mn.x, G::BM);
+    t.n0 = mn.y * G::BN;
     return t;
   }
   static MOE_DEV int num_k(const Args& a, const Tile&) { return 2 * a.I / G::BK; }
@@ -818,10 +839,11 @@ struct MxBwdGateDgrad {
   };
   static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[G::MB][G::NB],
                                uint8_t*) {
-    const int lane = threadIdx.x % kWave, wn = (threadIdx.x / kWave) % G::WAVES_N;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
 #pragma unroll
     for (int mb = 0; mb < G::MB; ++mb) {
-      const int m = mb * 16 + lane % 16;
+      const int m = wm * G::WM + mb * 16 + lane % 16;
       if (m >= t.m.mcount) continue;
       const size_t pos = t.m.row0 + m;
 #pragma unroll
@@ -835,6 +857,8 @@ struct MxBwdGateDgrad {
     }
   }
 };
+using MxBwdGateDgrad = MxBwdGateDgradT<GeoMx<128, 128, 1, 4>>;
+using MxBwdGateDgradBig = MxBwdGateDgradT<GeoMxBig>;
 
 // MXFP8 weight gradients: dW[e][m][n] = sum over the expert's padded positions p of
 // lq[m][poff[e] + p] rq[n][poff[e] + p], both operands quantised along the positions (mx.hip,
@@ -1212,6 +1236,397 @@ struct DmaDownDgrad {
 
 
 // ------------------------------------------------------------------------------------------
+// MXFP8 products on full 256-row blocks: 256 x 256 tiles of eight 128 x 64 wave tiles fed by
+// direct global -> LDS loads, as dma_kernel does for BF16. A 128-deep K step of fp8 codes is
+// one 128-byte line per row, the bytes of a 64-deep bf16 step, so the code stages keep
+// dma_kernel's row layout (mxswz is rowswz in bytes) and load mapping, and the fragments and
+// scaled MFMAs are run_tile_mx's. Each stage also holds the step's scale word of every row (4
+// bytes a row, 1 KB an operand), moved by one 4-byte load per lane: waves 0-3 load A's, waves
+// 4-7 B's. Two stages of 66 KB fit: each step waits for its own loads, then refills the other
+// stage for the next step, so loads have one step of MFMAs to arrive. The two stages are
+// distinct LDS arrays and the loop is unrolled over both, so the compiler can tell the stage a
+// load writes from the one the fragment reads read.
+constexpr int kDmxCodes = 256 * 128;                   // bytes of one operand's codes
+constexpr int kDmxStage = 2 * kDmxCodes + 2 * 256 * 4;  // A, B codes, then A, B scale words
+__shared__ __align__(1024) uint8_t dmx_s0[kDmxStage];
+__shared__ __align__(1024) uint8_t dmx_s1[kDmxStage];
+template <int S>
+MOE_DEV uint8_t* dmx_stage() {
+  if constexpr (S == 0) return dmx_s0;
+  else return dmx_s1;
+}
+
+// A lane's sources for one tile: code resources, the byte offsets of its four A pieces (rows
+// may be gathered) and of its first B piece (its load j fetches B rows 8 j further on, bst bytes
+// on, the same in every lane), and the resource and offset of the scale word it moves (its
+// wave's operand, row 64 (wave % 4) + lane). K chunks run k0, k0 + 1, .., nk - 1, 0, .., k0 - 1.
+struct DmxSrc {
+  __amdgpu_buffer_rsrc_t ra, rb, rs;
+  uint32_t ao[4], bo, so, bst;
+  int k0, nk;
+};
+
+MOE_DEV void dmx16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
+MOE_DEV void dmx4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
+                                           voff, soff, 0, 0);
+}
+
+// K chunk kt of the tile (clamped to the last) into stage S: nine load instructions a wave.
+template <int S>
+MOE_DEV void dmx_issue(const DmxSrc& s, int kt, int wave) {
+  int kk = min(kt, s.nk - 1) + s.k0;
+  kk = kk >= s.nk ? kk - s.nk : kk;
+  uint8_t* st = dmx_stage<S>();
+  const uint32_t step = (uint32_t)kk * 128;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dmx16(s.ra, s.ao[j], step, st + wave * 4096 + j * 1024);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    dmx16(s.rb, s.bo, step + j * s.bst, st + kDmxCodes + wave * 4096 + j * 1024);
+  dmx4(s.rs, s.so, (uint32_t)kk * 4, st + 2 * kDmxCodes + wave * 256);
+}
+
+template <class D, int S>
+MOE_DEV void dmx_step(f32x4 (&acc)[8][4], const DmxSrc& s, int kt, int wave, int wm, int wn,
+                      int lane) {
+  __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+  __builtin_amdgcn_s_barrier();
+  dmx_issue<S ^ 1>(s, kt + 1, wave);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint8_t* st = dmx_stage<S>();
+  const uint8_t* sA = st;
+  const uint8_t* sB = st + kDmxCodes;
+  const uint32_t* scA = reinterpret_cast<const uint32_t*>(st + 2 * kDmxCodes);
+  const uint32_t* scB = scA + 256;
+  // the lane's fragment addresses are recomputed in every step (a few adds) rather than held
+  // across the loop, where the accumulators and fragments leave no register for them
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int r16 = ln % 16, g = ln / 16;
+  i32x8 bf[4];
+  int bs[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int row = D::brow(wn, nb) + r16;
+    bf[nb] = mx_frag(sB, row, g);
+    bs[nb] = static_cast<int>((scB[row] >> (8 * g)) & 0xffu);
+  }
+  // row block mb + 1's A fragment is read while row block mb's MFMAs run
+  const int row0 = wm * 128 + r16;
+  i32x8 af = mx_frag(sA, row0, g);
+  int as = static_cast<int>((scA[row0] >> (8 * g)) & 0xffu);
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    i32x8 an = af;
+    int asn = as;
+    if (mb + 1 < 8) {
+      const int row = row0 + (mb + 1) * 16;
+      an = mx_frag(sA, row, g);
+      asn = static_cast<int>((scA[row] >> (8 * g)) & 0xffu);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nb], af, acc[mb][nb], 0,
+                                                                      0, 0, bs[nb], 0, as);
+    af = an;
+    as = asn;
+  }
+}
+
+// The tile walk of dma_kernel (XCD x takes the contiguous tile range [x R, (x + 1) R)).
+template <class D>
+__global__ void __launch_bounds__(512, 2) dmx_kernel(const typename D::Args a) {
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = wave / 4, wn = wave % 4;
+  const int ntiles = D::ntiles(a);
+  const int R = (ntiles + kXcds - 1) / kXcds;
+  const int G8 = gridDim.x / kXcds, xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  for (int it = 0;; ++it) {
+    const int sidx = slot + it * G8;
+    if (sidx >= R) break;
+    const int lt = xcd * R + sidx;
+    if (lt >= ntiles) break;
+    const typename D::Tile t = D::decode(a, lt);
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    DmxSrc s;
+    D::src(a, t, wave, lane, s);
+    if (s.nk > 0) {
+      dmx_issue<0>(s, 0, wave);
+      for (int kt = 0;; kt += 2) {
+        dmx_step<D, 0>(acc, s, kt, wave, wm, wn, lane);
+        if (kt + 1 >= s.nk) break;
+        dmx_step<D, 1>(acc, s, kt + 1, wave, wm, wn, lane);
+        if (kt + 2 >= s.nk) break;
+      }
+      // the trailing reload has landed and no wave still reads a stage
+      __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+      __builtin_amdgcn_s_barrier();
+    }
+    // The tile as the epilogue sees it, passed through an empty asm statement: the compiler
+    // cannot compute the epilogue's addresses before the K loop and hold them across it, where
+    // the accumulators and fragments already fill the register file.
+    typename D::Tile te = t;  // wave-uniform fields
+    te.m.e = __builtin_amdgcn_readfirstlane(te.m.e);
+    te.m.row0 = __builtin_amdgcn_readfirstlane(te.m.row0);
+    te.m.mcount = __builtin_amdgcn_readfirstlane(te.m.mcount);
+    te.n0 = __builtin_amdgcn_readfirstlane(te.n0);
+    asm volatile("" : "+s"(te.m.e), "+s"(te.m.row0), "+s"(te.m.mcount), "+s"(te.n0));
+    D::epilogue(a, te, acc);
+  }
+}
+
+template <class D>
+hipError_t launch_dmx(const typename D::Args& a, int max_tiles, bool persistent,
+                      hipStream_t stream) {
+  if (max_tiles <= 0) return hipSuccess;
+  int grid = (max_tiles + kXcds - 1) / kXcds * kXcds;
+  if (persistent) {
+    static int resident = 0;  // per kernel; every device of one process is an MI355X
+    if (resident == 0) {
+      int dev = 0, cus = 0, per_cu = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&dmx_kernel<D>), 512, 0);
+      if (e != hipSuccess) return e;
+      resident = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
+    }
+    if (resident > 0 && resident < grid) grid = resident;
+  }
+  {
+    TraceScope trace(D::kName, stream);
+    hipLaunchKernelGGL(dmx_kernel<D>, dim3(grid), dim3(512), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+// Problem 1 (MXFP8) on full 256-row blocks: 256 token rows (Xp codes, pitch d) against 128 gate
+// rows and the 128 matching up rows of W1[e]'s codes (pitch d). Byte offsets fit 32 bits: an
+// expert's W1 codes are below 2^31 bytes (4 I d < 2^31 is an API limit).
+struct DmxGateUp {
+  using P = MxFwdGateUpBig;
+  using Args = P::Args;
+  using Tile = P::Tile;
+  static constexpr const char* kName = "fwd_gateup_big";
+  static MOE_DEV int ntiles(const Args& a) { return P::ntiles(a); }
+  static MOE_DEV Tile decode(const Args& a, int lt) { return P::decode(a, lt); }
+  static MOE_DEV int brow(int wn, int nb) { return P::brow(wn, nb); }
+  static MOE_DEV void src(const Args& a, const Tile& t, int wave, int lane, DmxSrc& s) {
+    const int d = a.d, I = a.I, kA = P::kA;
+    auto wrow = [&](int r) { return r < kA ? t.n0 + r : I + t.n0 + r - kA; };
+    s.nk = d / 128;
+    s.k0 = 0;
+    s.ra = raw_rsrc(a.xp8 + (size_t)t.m.row0 * d);
+    s.rb = raw_rsrc(a.w8 + (size_t)t.m.e * 2 * I * d);
+    // load j's rows are 8 j further on, in the same half of the B tile (gate or up)
+    const int row = dma_row(wave, 0, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s.ao[j] = (uint32_t)(row + 8 * j) * d + dma_piece(lane);
+    s.bo = (uint32_t)wrow(row) * d + dma_piece(lane);
+    s.bst = 8u * (uint32_t)d;
+    const int r = 64 * (wave % 4) + lane;
+    if (wave < 4) {
+      s.rs = raw_rsrc(a.xps + (size_t)t.m.row0 * (d / 32));
+      s.so = (uint32_t)r * (d / 32);
+    } else {
+      s.rs = raw_rsrc(a.ws + (size_t)t.m.e * 2 * I * (d / 32));
+      s.so = (uint32_t)wrow(r) * (d / 32);
+    }
+  }
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[8][4]) {
+    P::epilogue(a, t, acc, nullptr);
+  }
+};
+
+// Problem 2 (MXFP8) on full 256-row blocks: A codes (pitch I) against W2[e]'s codes, rows n0..
+// (pitch I); each n-tile starts at its own K chunk, as in the 128-row kernel.
+struct DmxDown {
+  using P = MxFwdDownBig;
+  using Args = P::Args;
+  using Tile = P::Tile;
+  static constexpr const char* kName = "fwd_down_big";
+  static MOE_DEV int ntiles(const Args& a) { return P::ntiles(a); }
+  static MOE_DEV Tile decode(const Args& a, int lt) { return P::decode(a, lt); }
+  static MOE_DEV int brow(int wn, int nb) { return P::brow(wn, nb); }
+  static MOE_DEV void src(const Args& a, const Tile& t, int wave, int lane, DmxSrc& s) {
+    const int I = a.I;
+    s.nk = I / 128;
+    s.k0 = P::k_first(t, s.nk);
+    s.ra = raw_rsrc(a.aq + (size_t)t.m.row0 * I);
+    s.rb = raw_rsrc(a.w8 + ((size_t)t.m.e * a.d + t.n0) * I);
+    const int row = dma_row(wave, 0, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s.ao[j] = (uint32_t)(row + 8 * j) * I + dma_piece(lane);
+    s.bo = (uint32_t)row * I + dma_piece(lane);
+    s.bst = 8u * (uint32_t)I;
+    const int r = 64 * (wave % 4) + lane;
+    s.rs = wave < 4 ? raw_rsrc(a.aqs + (size_t)t.m.row0 * (I / 32))
+                    : raw_rsrc(a.ws + ((size_t)t.m.e * a.d + t.n0) * (I / 32));
+    s.so = (uint32_t)r * (I / 32);
+  }
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[8][4]) {
+    P::epilogue(a, t, acc, nullptr);
+  }
+};
+
+// Problem 4 (MXFP8) on full 256-row blocks: dH codes (pitch 2I) against W1[e]'s transposed
+// codes ([d, 2I], rows n0..).
+struct DmxGateDgrad {
+  using P = MxBwdGateDgradBig;
+  using Args = P::Args;
+  using Tile = P::Tile;
+  static constexpr const char* kName = "bwd_gate_dgrad_big";
+  static MOE_DEV int ntiles(const Args& a) { return P::ntiles(a); }
+  static MOE_DEV Tile decode(const Args& a, int lt) { return P::decode(a, lt); }
+  static MOE_DEV int brow(int wn, int nb) { return P::brow(wn, nb); }
+  static MOE_DEV void src(const Args& a, const Tile& t, int wave, int lane, DmxSrc& s) {
+    const int twoI = 2 * a.I;
+    s.nk = twoI / 128;
+    s.k0 = 0;
+    s.ra = raw_rsrc(a.dhq + (size_t)t.m.row0 * twoI);
+    s.rb = raw_rsrc(a.w8 + ((size_t)t.m.e * a.d + t.n0) * twoI);
+    const int row = dma_row(wave, 0, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s.ao[j] = (uint32_t)(row + 8 * j) * twoI + dma_piece(lane);
+    s.bo = (uint32_t)row * twoI + dma_piece(lane);
+    s.bst = 8u * (uint32_t)twoI;
+    const int r = 64 * (wave % 4) + lane;
+    s.rs = wave < 4 ? raw_rsrc(a.dhs + (size_t)t.m.row0 * (twoI / 32))
+                    : raw_rsrc(a.ws + ((size_t)t.m.e * a.d + t.n0) * (twoI / 32));
+    s.so = (uint32_t)r * (twoI / 32);
+  }
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[8][4]) {
+    P::epilogue(a, t, acc, nullptr);
+  }
+};
+
+// Problem 3 (MXFP8) on full 256-row blocks: the gathered dY codes (token rows, pitch d) against
+// W2[e]'s transposed codes ([I, d], rows n0..). The epilogue is the 128-row kernel's per 32-block
+// of I columns (a wave's 64 columns are two), and the router-weight partials of each 128-column
+// half are the sums of its two waves' row sums, as in the BF16 256 x 256 kernel.
+struct DmxDownDgrad {
+  using Args = MxBwdDownDgrad::Args;
+  using Tile = DgradTile;
+  static constexpr const char* kName = "bwd_down_dgrad_big";
+  static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.I / 256); }
+  static MOE_DEV Tile decode(const Args& a, int lt) {
+    const int2 mn = tile_mn<true>(lt, a.sched[0].x, a.I / 256);
+    return Tile{decode_mtile(a.sched, a.offsets, mn.x, 256), mn.y * 256};
+  }
+  static MOE_DEV int brow(int wn, int nb) { return wn * 64 + nb * 16; }
+  // byte offsets into dY's codes fit 32 bits: T d < 2^31 is an API limit
+  static MOE_DEV void src(const Args& a, const Tile& t, int wave, int lane, DmxSrc& s) {
+    const int d = a.d;
+    s.nk = d / 128;
+    s.k0 = 0;
+    s.ra = raw_rsrc(a.dyq);
+    s.rb = raw_rsrc(a.w8 + ((size_t)t.m.e * a.I + t.n0) * d);
+    const int row = dma_row(wave, 0, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      s.ao[j] = (uint32_t)(a.row_src[t.m.row0 + row + 8 * j] / a.k) * d + dma_piece(lane);
+    s.bo = (uint32_t)row * d + dma_piece(lane);
+    s.bst = 8u * (uint32_t)d;
+    const int r = 64 * (wave % 4) + lane;
+    if (wave < 4) {
+      s.rs = raw_rsrc(a.dys);
+      s.so = (uint32_t)(a.row_src[t.m.row0 + r] / a.k) * (d / 32);
+    } else {
+      s.rs = raw_rsrc(a.ws + ((size_t)t.m.e * a.I + t.n0) * (d / 32));
+      s.so = (uint32_t)r * (d / 32);
+    }
+  }
+  static MOE_DEV void epilogue(const Args& a, const Tile& t, f32x4 (&acc)[8][4]) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int wm = wave / 4, wn = wave % 4;
+    const int I = a.I;
+    float* red = reinterpret_cast<float*>(dmx_s0);  // [4][256] row sums per wave column
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const int m = wm * 128 + mb * 16 + lane % 16;
+      const size_t pos = t.m.row0 + m;
+      const float w = a.topk_w[a.row_src[pos]];
+      float part = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {  // the wave's two 32-blocks of I columns
+        const int c0 = t.n0 + wn * 64 + hb * 32;
+        float dgv[8], duv[8];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int nb = 2 * hb + q;
+          const int i = c0 + q * 16 + 4 * (lane / 16);
+          const uint2 av = *reinterpret_cast<const uint2*>(a.A + pos * I + i);
+          const uint2 gv = *reinterpret_cast<const uint2*>(a.H + pos * 2 * I + i);
+          const uint2 uv = *reinterpret_cast<const uint2*>(a.H + pos * 2 * I + I + i);
+          const float av4[4] = {bf2f_lo(av.x), bf2f_hi(av.x), bf2f_lo(av.y), bf2f_hi(av.y)};
+          const float g4[4] = {bf2f_lo(gv.x), bf2f_hi(gv.x), bf2f_lo(gv.y), bf2f_hi(gv.y)};
+          const float u4[4] = {bf2f_lo(uv.x), bf2f_hi(uv.x), bf2f_lo(uv.y), bf2f_hi(uv.y)};
+          float dg[4], du[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float dap = acc[mb][nb][r];
+            part = __builtin_fmaf(dap, av4[r], part);
+            const float dA = w * dap;
+            const float sg = sigmoid(g4[r]);
+            dg[r] = dA * u4[r] * sg * (1.0f + g4[r] * (1.0f - sg));
+            du[r] = dA * (g4[r] * sg);
+          }
+          uint2 og, ou;
+          og.x = pack_bf2(dg[0], dg[1]);
+          og.y = pack_bf2(dg[2], dg[3]);
+          ou.x = pack_bf2(du[0], du[1]);
+          ou.y = pack_bf2(du[2], du[3]);
+          dgv[4 * q + 0] = bf2f_lo(og.x);
+          dgv[4 * q + 1] = bf2f_hi(og.x);
+          dgv[4 * q + 2] = bf2f_lo(og.y);
+          dgv[4 * q + 3] = bf2f_hi(og.y);
+          duv[4 * q + 0] = bf2f_lo(ou.x);
+          duv[4 * q + 1] = bf2f_hi(ou.x);
+          duv[4 * q + 2] = bf2f_lo(ou.y);
+          duv[4 * q + 3] = bf2f_hi(ou.y);
+          *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + i) = og;
+          *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + I + i) = ou;
+        }
+        const uint32_t cg = mx_block_code(dgv), cu = mx_block_code(duv);
+        const float ig = mx_inv_scale(cg), iu = mx_inv_scale(cu);
+        uint8_t* qp = a.dhq + pos * 2 * I;
+        const int o = 4 * (lane / 16);
+        *reinterpret_cast<uint32_t*>(qp + c0 + o) = mx_pack4(dgv, ig);
+        *reinterpret_cast<uint32_t*>(qp + c0 + 16 + o) = mx_pack4(dgv + 4, ig);
+        *reinterpret_cast<uint32_t*>(qp + I + c0 + o) = mx_pack4(duv, iu);
+        *reinterpret_cast<uint32_t*>(qp + I + c0 + 16 + o) = mx_pack4(duv + 4, iu);
+        if (lane < 16) {
+          a.dhs[pos * (2 * I / 32) + c0 / 32] = static_cast<uint8_t>(cg);
+          a.dhs[pos * (2 * I / 32) + (I + c0) / 32] = static_cast<uint8_t>(cu);
+        }
+      }
+      // lanes l, l^16, l^32, l^48 share row m: butterfly in a fixed pattern
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      if (lane < 16) red[wn * 256 + m] = part;
+    }
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      const size_t pos = t.m.row0 + threadIdx.x;
+      float* dst = a.dwpart + pos * (I / 128) + t.n0 / 128;
+      dst[0] = red[0 * 256 + threadIdx.x] + red[1 * 256 + threadIdx.x];  // [n0, n0 + 128)
+      dst[1] = red[2 * 256 + threadIdx.x] + red[3 * 256 + threadIdx.x];  // [n0 + 128, n0 + 256)
+    }
+    __syncthreads();  // red is the next tile's first stage
+  }
+};
+
+// ------------------------------------------------------------------------------------------
 // Schedule tables, built on the device from the offsets so the host never learns the counts.
 // Entry 0 of each holds its count; entry i >= 1 is (expert, first row within the expert).
 //  * full: every 128-row block of every expert;
@@ -1333,25 +1748,55 @@ hipError_t launch_bwd_gate_dgrad(const GemmBwdGateDgradArgs& x, bool persistent,
   return launch<BwdGateDgrad>(a, sched_max_rem(x.Tk, x.E) * (x.d / 128), persistent, s);
 }
 
+// The MXFP8 forward GEMMs and gate dgrad run the 256-row blocks with dmx_kernel, then the
+// remainders on the 128-row kernels.
 hipError_t launch_fwd_gateup_mx(const GemmMxGateUpArgs& x, bool persistent, hipStream_t s) {
-  MxFwdGateUp::Args a{x.xp8, x.xps, x.w8, x.ws, x.H, x.A, x.aq, x.aqs, x.offsets, x.sched, x.d, x.I};
-  return launch<MxFwdGateUp>(a, sched_max_mtiles(x.Tk, x.E) * (x.I / 64), persistent, s);
+  const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
+  MxFwdGateUpBig::Args ab{x.xp8, x.xps, x.w8, x.ws, x.H,     x.A,
+                          x.aq,  x.aqs, x.offsets, st.big, x.d, x.I};
+  hipError_t e = launch_dmx<DmxGateUp>(ab, sched_max_big(x.Tk) * (x.I / MxFwdGateUpBig::kA),
+                                       true, s);
+  if (e != hipSuccess) return e;
+  MxFwdGateUp::Args a{x.xp8, x.xps, x.w8, x.ws, x.H, x.A, x.aq, x.aqs, x.offsets, st.rem, x.d, x.I};
+  return launch<MxFwdGateUp>(a, sched_max_rem(x.Tk, x.E) * (x.I / MxFwdGateUp::kA), persistent,
+                             s);
 }
 
 hipError_t launch_fwd_down_mx(const GemmMxDownArgs& x, bool persistent, hipStream_t s) {
-  MxFwdDown::Args a{x.aq, x.aqs, x.w8, x.ws, x.O, x.offsets, x.sched, x.d, x.I};
-  return launch<MxFwdDown>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
+  const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
+  MxFwdDownBig::Args ab{x.aq, x.aqs, x.w8, x.ws, x.O, x.offsets, st.big, x.d, x.I};
+  hipError_t e = launch_dmx<DmxDown>(ab, sched_max_big(x.Tk) * (x.d / 256), true, s);
+  if (e != hipSuccess) return e;
+  MxFwdDown::Args a{x.aq, x.aqs, x.w8, x.ws, x.O, x.offsets, st.rem, x.d, x.I};
+  return launch<MxFwdDown>(a, sched_max_rem(x.Tk, x.E) * (x.d / 128), persistent, s);
 }
 
+// With I a multiple of 256 the MXFP8 down dgrad runs the 256-row blocks with dmx_kernel, then
+// the remainders; otherwise every 128-row block on the 128-row kernel.
 hipError_t launch_bwd_down_dgrad_mx(const GemmMxDownDgradArgs& x, bool persistent, hipStream_t s) {
-  MxBwdDownDgrad::Args a{x.dyq, x.dys, x.row_src, x.topk_w, x.w8,     x.ws,    x.H,     x.A, x.dH,
-                         x.dwpart, x.dhq, x.dhs,  x.offsets, x.sched, x.d, x.I, x.k};
-  return launch<MxBwdDownDgrad>(a, sched_max_mtiles(x.Tk, x.E) * (x.I / 128), persistent, s);
+  const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
+  const bool big = x.I % 256 == 0;
+  const int max_big = big ? sched_max_big(x.Tk) * (x.I / 256) : 0;
+  if (max_big > 0) {
+    MxBwdDownDgrad::Args ab{x.dyq, x.dys, x.row_src, x.topk_w, x.w8, x.ws, x.H, x.A, x.dH,
+                            x.dwpart, x.dhq, x.dhs, x.offsets, st.big, x.d, x.I, x.k};
+    const hipError_t e = launch_dmx<DmxDownDgrad>(ab, max_big, true, s);
+    if (e != hipSuccess) return e;
+  }
+  MxBwdDownDgrad::Args a{x.dyq, x.dys, x.row_src, x.topk_w, x.w8,  x.ws, x.H,
+                         x.A,   x.dH,  x.dwpart,  x.dhq,    x.dhs, x.offsets,
+                         big ? st.rem : st.full, x.d, x.I, x.k};
+  const int max_small = big ? sched_max_rem(x.Tk, x.E) : sched_max_mtiles(x.Tk, x.E);
+  return launch<MxBwdDownDgrad>(a, max_small * (x.I / 128), persistent, s);
 }
 
 hipError_t launch_bwd_gate_dgrad_mx(const GemmMxGateDgradArgs& x, bool persistent, hipStream_t s) {
-  MxBwdGateDgrad::Args a{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, x.sched, x.d, x.I};
-  return launch<MxBwdGateDgrad>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
+  const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
+  MxBwdGateDgradBig::Args ab{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, st.big, x.d, x.I};
+  hipError_t e = launch_dmx<DmxGateDgrad>(ab, sched_max_big(x.Tk) * (x.d / 256), true, s);
+  if (e != hipSuccess) return e;
+  MxBwdGateDgrad::Args a{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, st.rem, x.d, x.I};
+  return launch<MxBwdGateDgrad>(a, sched_max_rem(x.Tk, x.E) * (x.d / 128), persistent, s);
 }
 
 template <bool ACC, bool BF>

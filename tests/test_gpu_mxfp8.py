@@ -227,6 +227,29 @@ def test_mxfp8_big_expert_wgrad_with_accumulation():
         assert torch.equal(g, 2 * g0)
 
 
+def test_mxfp8_expert_sizes_at_the_256_row_block_boundaries():
+    """Experts of 0, 1, 128, 255, 256, 257, 384, 511, 512 and 513 rows in MXFP8 mode: each of the
+    four MXFP8 GEMMs splits an expert into full 256-row blocks (the direct-to-LDS 256 x 256
+    kernels) and 128-row remainder tiles. Parity against the MXFP8 oracle, with d = 512 (four K
+    steps of the gate/up GEMM, two column tiles of the down GEMM and the gate dgrad) and
+    I = 512 (two column tiles of the down dgrad); persistent grids bitwise equal to one-shot
+    grids."""
+    counts = [255, 256, 257, 0, 511, 512, 513, 1, 128, 384]
+    _announce(f"[mxfp8] expert sizes {counts}, d=512 I=512 k=1")
+    E, d, I = len(counts), 512, 512
+    T = sum(counts)
+    inp = workload.make_inputs("local_zipf", seed=9, device=DEV, T=T, d=d, E=E, I=I,
+                               precision="mxfp8")
+    idx = np.repeat(np.arange(E, dtype=np.int32), counts)
+    np.random.default_rng(9).shuffle(idx)
+    inp["topk_idx"] = torch.from_numpy(idx.reshape(T, 1)).to(DEV)
+    L = run_gpu(inp)
+    f, b = run_oracle(inp)
+    assert list(f["counts"]) == counts
+    check_parity(L, inp, f, b, tol_act=TOL_MX, tol_grad=TOL_MX)
+    assert_bitwise_equal(outputs(L, False), outputs(run_gpu(inp, persistent=True), False))
+
+
 def test_mxfp8_local_zipf_full_size_sampled_parity():
     """The full local expert slice in MXFP8 mode (16,384 rows, d=7168, I=2048, one expert over
     40%): the ring's codes and scales bit-exact on sampled positions, the heaviest and the
