@@ -57,8 +57,12 @@ KERNELS = [
     (r"gg_kernel<moe::MxFwdDown", "fwd_down", G),
     (r"gg_kernel<moe::MxBwdDownDgrad", "bwd_down_dgrad", G),
     (r"gg_kernel<moe::MxBwdGateDgrad", "bwd_gate_dgrad", G),
-    (r"DmaWgrad<(true|false), false>", "bwd_down_wgrad_big", W),
-    (r"DmaWgrad<(true|false), true>", "bwd_gate_wgrad_big", W),
+    (r"dmx_kernel<moe::DmxGateUp>", "fwd_gateup_big", G),
+    (r"dmx_kernel<moe::DmxDown>", "fwd_down_big", G),
+    (r"dmx_kernel<moe::DmxGateDgrad>", "bwd_gate_dgrad_big", G),
+    (r"dmx_kernel<moe::DmxDownDgrad>", "bwd_down_dgrad_big", G),
+    (r"DmaWgrad<(true|false), false, (true|false)>", "bwd_down_wgrad_big", W),
+    (r"DmaWgrad<(true|false), true, (true|false)>", "bwd_gate_wgrad_big", W),
     (r"wgrad_kernel<(true|false), false", "bwd_down_wgrad", W),
     (r"wgrad_kernel<(true|false), true", "bwd_gate_wgrad", W),
     (r"moe::combine_kernel", "combine", C),
