@@ -44,6 +44,12 @@ readings = {
     "dw_bf16": "weight gradients stored as bf16, an option (the default stores dW1 and dW2 in "
                "fp32, the caller's main gradient): each element of dW1 and dW2 is its sum "
                "rounded once to bf16 where it is stored; dWr stays fp32",
+    "mxfp4": "MXFP4 mode, the 4-bit analogue of MXFP8 mode (MarkTechPost, 'MoE layer as the "
+             "bottleneck': the pages' NVFP4 training kernels; OCP MX v1.0 MXFP4): E2M1 elements "
+             "with one E8M0 scale per 32, the scale exponent floor(log2 amax) - 2, round to "
+             "nearest even, saturate to 6; every expert GEMM of forward and dgrad takes both "
+             "operands as MXFP4 images along the same axes as in MXFP8 mode, and the weight "
+             "gradients and dWr take Xp as its MXFP4 image",
     "mxfp8": "MXFP8 mode (MarkTechPost, closing paragraph of 'Three design decisions that "
              "matter': BF16 and MXFP8 modes): every expert GEMM of forward and dgrad takes both "
              "operands as MXFP8 images quantised along that GEMM's reduction axis - Xp and W1 "
@@ -185,8 +191,15 @@ def expert_forward(x, w1, w2, *, rnd, mxq=_identity):
     return h, a, o
 
 
-def expert_backward(x, dy, wv, h, a, o_used, w1, w2, *, rnd, mxmode=False, mx_wgrad=False):
-    """One expert's backward over its rows (readings "router_grad", "storage_bf16", "mxfp8").
+def _mx_images(precision):
+    """The MX image taken of the GEMM operands in a precision mode (reading "mxfp8" or "mxfp4"),
+    or None in BF16 mode."""
+    return {"bf16": None, "mxfp8": mx.qdq, "mxfp4": mx.qdq4}[precision]
+
+
+def expert_backward(x, dy, wv, h, a, o_used, w1, w2, *, rnd, mxq=None, mx_wgrad=False):
+    """One expert's backward over its rows (readings "router_grad", "storage_bf16", "mxfp8",
+    "mxfp4").
 
     x and dy are the rows' tokens and upstream gradients, wv [c, 1] their routing weights, h and
     a the stored forward H and A, o_used the stored O. Per row:
@@ -195,17 +208,17 @@ def expert_backward(x, dy, wv, h, a, o_used, w1, w2, *, rnd, mxmode=False, mx_wg
     * dA = w * (dy W2_e); dg = dA * u * s * (1 + g (1 - s)) with s = sigmoid(g), du = dA * silu(g),
       from the stored g and u; dH = [dg | du] is stored (rounded);
     * dXp = dH W1_e, stored (rounded).
-    Over the expert's rows: dW2_e = sum (w dy) outer a, dW1_e = sum dH outer x. In MXFP8 mode both
-    dgrad GEMMs take MXFP8 images along their reduction axes and x enters dW1 as its MXFP8 image.
-    With mx_wgrad (reading "mxfp8_wgrad") both weight-gradient products take MXFP8 images of
-    their operands along the expert's positions.
+    Over the expert's rows: dW2_e = sum (w dy) outer a, dW1_e = sum dH outer x. In an MX mode
+    (mxq the MXFP8 or MXFP4 image) both dgrad GEMMs take MX images along their reduction axes and
+    x enters dW1 as its MX image. With mx_wgrad (reading "mxfp8_wgrad") both weight-gradient
+    products take MXFP8 images of their operands along the expert's positions.
     Returns (dw [c], dH [c, 2I], dXp [c, d], dW1_e [2I, d], dW2_e [d, I]).
     """
     I = h.shape[1] // 2
     w1 = np.asarray(w1, np.float64)
     w2 = np.asarray(w2, np.float64)
-    if mxmode:
-        dAp = mx.qdq(dy) @ mx.qdq(w2.T).T      # W2 [d, I] quantised along d
+    if mxq is not None:
+        dAp = mxq(dy) @ mxq(w2.T).T            # W2 [d, I] quantised along d
         dw = np.sum(dAp * a, axis=1)
     else:
         dAp = dy @ w2
@@ -217,11 +230,11 @@ def expert_backward(x, dy, wv, h, a, o_used, w1, w2, *, rnd, mxmode=False, mx_wg
     dg = dA * u * s * (1.0 + g * (1.0 - s))
     du = dA * (g * s)
     dh = rnd(np.concatenate([dg, du], axis=1))
-    if mxmode:
-        dxp = rnd(mx.qdq(dh) @ mx.qdq(w1.T).T)  # W1 [2I, d] quantised along 2I
+    if mxq is not None:
+        dxp = rnd(mxq(dh) @ mxq(w1.T).T)        # W1 [2I, d] quantised along 2I
     else:
         dxp = rnd(dh @ w1)
-    xr = mx.qdq(x) if mxmode else x
+    xr = mxq(x) if mxq is not None else x
     if mx_wgrad:
         dW2 = mx.qdq_segment(wv * dy).T @ mx.qdq_segment(a)
         dW1 = mx.qdq_segment(dh).T @ mx.qdq_segment(xr)
@@ -269,10 +282,11 @@ def forward(X, W1, W2, *, Wr=None, k=None, topk_idx=None, topk_w=None,
 
     Per expert e and each of its rows (``expert_forward``): [g | u] = x W1_e^T,
     a = silu(g) * u, o = a W2_e^T. Then y_t = sum_j w_tj o_tj, j ascending (reading
-    "combine"). With precision="mxfp8" the two GEMMs take MXFP8 images of their operands
-    (reading "mxfp8"). Returns a dict of every intermediate the GPU path also produces.
+    "combine"). With precision="mxfp8" (or "mxfp4") the two GEMMs take MXFP8 (MXFP4) images of
+    their operands (readings "mxfp8", "mxfp4"). Returns a dict of every intermediate the GPU path
+    also produces.
     """
-    mxq = mx.qdq if precision == "mxfp8" else _identity
+    mxq = _mx_images(precision) or _identity
     X = np.asarray(X, np.float64)
     T, d = X.shape
     E, twoI, _ = W1.shape
@@ -323,14 +337,16 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None, wgrad="bf16",
     A and dH feed the later steps. Empty experts get all-zero dW1_e and dW2_e blocks.
     ``experts`` limits the expert math to a subset (rows of other experts stay NaN). dW1 and dW2
     then hold one block per listed expert, in the order listed in out["experts"].
-    In MXFP8 mode (reading "mxfp8") both dgrad GEMMs take MXFP8 images of their operands, dw is
-    <dA', A>, and Xp enters dW1 and dWr as its MXFP8 image. wgrad="mxfp8" (MXFP8 mode only,
+    In MXFP8 (MXFP4) mode (readings "mxfp8", "mxfp4") both dgrad GEMMs take MXFP8 (MXFP4)
+    images of their operands, dw is
+    <dA', A>, and Xp enters dW1 and dWr as its MX image. wgrad="mxfp8" (MXFP8 mode only,
     reading "mxfp8_wgrad") quantises both operands of both weight-gradient products along the
     expert's positions. dw_dtype="bf16" (reading "dw_bf16") rounds each dW1 and dW2 element once
     to bf16.
     """
-    mxmode = fwd.get("precision", "bf16") == "mxfp8"
-    assert wgrad in ("bf16", "mxfp8") and (wgrad == "bf16" or mxmode), "MXFP8 wgrad needs MXFP8"
+    mxq = _mx_images(fwd.get("precision", "bf16"))
+    assert wgrad in ("bf16", "mxfp8") and (wgrad == "bf16" or fwd.get("precision") == "mxfp8"), \
+        "MXFP8 wgrad needs MXFP8 mode"
     assert dw_dtype in ("fp32", "bf16")
     X = np.asarray(X, np.float64)
     dY = np.asarray(dY, np.float64)
@@ -356,7 +372,7 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None, wgrad="bf16",
         tok = rows // k
         dw_pos[p0:p1], dH[p0:p1], dXp[p0:p1], dW1[slot], dW2[slot] = expert_backward(
             X[tok], dY[tok], w_flat[rows][:, None], fwd["H"][p0:p1], fwd["A"][p0:p1],
-            fwd["O"][p0:p1], W1[e], W2[e], rnd=rnd, mxmode=mxmode, mx_wgrad=wgrad == "mxfp8")
+            fwd["O"][p0:p1], W1[e], W2[e], rnd=rnd, mxq=mxq, mx_wgrad=wgrad == "mxfp8")
     if dw_dtype == "bf16":
         dW1, dW2 = bf16_round(dW1), bf16_round(dW2)
     dw = dw_pos[tk_row].reshape(T, k)
@@ -366,7 +382,7 @@ def backward(fwd: dict, X, W1, W2, dY, *, Wr=None, experts=None, wgrad="bf16",
         dlogits = router_backward(fwd["w"], fwd["idx"], dw, E)
         dXsum = dXsum + dlogits @ np.asarray(Wr, np.float64)
         out["dlogits"] = dlogits
-        out["dWr"] = dlogits.T @ (mx.qdq(X) if mxmode else X)
+        out["dWr"] = dlogits.T @ (mxq(X) if mxq is not None else X)
     out["dX"] = rnd(dXsum)
     return out
 
@@ -384,8 +400,8 @@ def layer(X, W1, W2, dY, *, Wr=None, k=None, topk_idx=None, topk_w=None, storage
     """
     assert dw_dtype in ("fp32", "bf16")
     dwr = bf16_round if dw_dtype == "bf16" else _identity
-    mxmode = precision == "mxfp8"
-    mxq = mx.qdq if mxmode else _identity
+    mxb = _mx_images(precision)
+    mxq = mxb or _identity
     X = np.asarray(X, np.float64)
     dY = np.asarray(dY, np.float64)
     T, d = X.shape
@@ -415,7 +431,7 @@ def layer(X, W1, W2, dY, *, Wr=None, k=None, topk_idx=None, topk_w=None, storage
         O[p0:p1] = rnd(o)
         dw_pos[p0:p1], dH[p0:p1], dXp[p0:p1], dW1, dW2 = expert_backward(
             X[tok], dY[tok], w_flat[rows][:, None], H[p0:p1], A[p0:p1], O[p0:p1], w1, w2,
-            rnd=rnd, mxmode=mxmode, mx_wgrad=wgrad == "mxfp8")
+            rnd=rnd, mxq=mxb, mx_wgrad=wgrad == "mxfp8")
         if on_expert is not None:
             on_expert(e, dwr(dW1), dwr(dW2))
     out = dict(idx=idx, w=w, counts=counts, offsets=offsets, row_src=row_src, tk_row=tk_row,
@@ -428,6 +444,6 @@ def layer(X, W1, W2, dY, *, Wr=None, k=None, topk_idx=None, topk_w=None, storage
         dlogits = router_backward(w, idx, dw, E)
         dXsum = dXsum + dlogits @ np.asarray(Wr, np.float64)
         out["dlogits"] = dlogits
-        out["dWr"] = dlogits.T @ (mx.qdq(X) if mxmode else X)
+        out["dWr"] = dlogits.T @ (mxb(X) if mxb is not None else X)
     out["dX"] = rnd(dXsum)
     return out
