@@ -13,7 +13,7 @@ timed region of as many steps, in which the library records events around each o
 on that same stream (`ms_per_step_traced` is that region's step time). `cpu_baseline` times the
 float64 CPU oracle on a bounded sample of the same workload, extrapolated to the whole layer,
 with per-workload samples beside it. Further lines: the other grid form (persistent), MXFP8
-mode, the local expert slice, the tiny layer (eager and as a HIP graph) and the streaming
+and MXFP4 modes, the local expert slice, the tiny layer (eager and as a HIP graph) and the streaming
 macrobatch (serial and overlapped).
 """
 from __future__ import annotations
@@ -31,23 +31,25 @@ sys.path.insert(0, ROOT)
 HBM_GBPS = 8000.0         # MI355X HBM3E, GB/s
 MFMA_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, TFLOP/s
 MFMA_FP8_TFLOPS = 5000.0   # dense fp8 MFMA (the MXFP8 scaled MFMA), TFLOP/s
+MFMA_FP4_TFLOPS = 10100.0  # dense fp4 MFMA (the MXFP4 scaled MFMA), TFLOP/s
 # fp32 FMA on the vector ALUs without packed-fp32 instructions (the library is built without
 # them): 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz. Packed fp32 would double it (157.3).
 VALU_FP32_TFLOPS = 78.6
 
 
-def algorithmic(cfg, routed=True, accumulate=False, mx=False, mx_wgrad=False, bf16_dw=False):
+def algorithmic(cfg, routed=True, accumulate=False, mx=False, mx_wgrad=False, bf16_dw=False,
+                fbits=8):
     """Algorithmic bytes and flops per launch of each kernel: what the method must move and
     compute (each tensor read or written once, no padding, no re-reads). M = T*k rows.
-    In MXFP8 mode (`mx`) a quantised tensor of n elements is n code bytes plus n/32 scale
-    bytes, and the weights are read in the quantised copies. dW1 and dW2 elements are 4 bytes,
-    2 with `bf16_dw`."""
+    In the MX modes (`mx`) a quantised tensor of n elements is n * fbits / 8 code bytes (fbits
+    8 for MXFP8, 4 for MXFP4) plus n/32 scale bytes, and the weights are read in the quantised
+    copies. dW1 and dW2 elements are 4 bytes, 2 with `bf16_dw`."""
     T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
     M = T * k
     nb = (M + 255) // 256
     acc = 2 if accumulate else 1
     wb = 2 if bf16_dw else 4  # bytes per dW1 / dW2 element
-    q = lambda n: n + n // 32  # bytes of n MXFP8 elements with their scales
+    q = lambda n: n * fbits // 8 + n // 32  # bytes of n MX elements with their scales
     b = {}
     if routed:
         b["widen_router"] = (E * d * 2 + E * d * 4, 0)
@@ -103,23 +105,26 @@ GEMMS = ("fwd_gateup", "fwd_down", "bwd_down_dgrad", "bwd_down_wgrad", "bwd_gate
          "bwd_gate_wgrad")
 
 
-MX_GEMMS = ("fwd_gateup", "fwd_down", "bwd_down_dgrad", "bwd_gate_dgrad")  # scaled fp8 MFMA
+MX_GEMMS = ("fwd_gateup", "fwd_down", "bwd_down_dgrad", "bwd_gate_dgrad")  # scaled MFMA
 
 
-def mfma_peak(name, mx, mx_wgrad=False):
-    """Dense MFMA peak of a GEMM kernel: fp8 for the MXFP8 scaled-MFMA GEMMs, else bf16 (the
-    weight-gradient GEMMs run bf16 MFMA unless the MXFP8 weight gradients are on)."""
-    return MFMA_FP8_TFLOPS if mx and (name in MX_GEMMS or mx_wgrad) else MFMA_BF16_TFLOPS
+def mfma_peak(name, mx, mx_wgrad=False, fbits=8):
+    """Dense MFMA peak of a GEMM kernel: fp8 (MXFP8) or fp4 (MXFP4) for the scaled-MFMA GEMMs,
+    else bf16 (the weight-gradient GEMMs run bf16 MFMA unless the MXFP8 weight gradients are
+    on)."""
+    if mx and (name in MX_GEMMS or mx_wgrad):
+        return MFMA_FP4_TFLOPS if fbits == 4 else MFMA_FP8_TFLOPS
+    return MFMA_BF16_TFLOPS
 
 
-def kernel_roofline(name, nbytes, flops, us, mx=False, mx_wgrad=False):
+def kernel_roofline(name, nbytes, flops, us, mx=False, mx_wgrad=False, fbits=8):
     """Achieved rate against the roofline that bounds the kernel."""
     s = us * 1e-6
     if name == "router_logits":
         ach = flops / s / 1e12
         return {"bound": "alu", "achieved": ach, "peak": VALU_FP32_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / VALU_FP32_TFLOPS}
-    peak = mfma_peak(name, mx, mx_wgrad)
+    peak = mfma_peak(name, mx, mx_wgrad, fbits)
     if flops and name in GEMMS and flops / nbytes > peak * 1e12 / (HBM_GBPS * 1e9):
         ach = flops / s / 1e12
         return {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
@@ -289,6 +294,8 @@ def main():
     ap.add_argument("--no-trace", action="store_true", help="skip the per-kernel traced pass")
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the MXFP8-mode run on the same inputs")
+    ap.add_argument("--no-mxfp4", action="store_true",
+                    help="skip the MXFP4-mode run on the same inputs")
     ap.add_argument("--no-expert-slice", action="store_true",
                     help="skip the local expert-slice (local_zipf) run")
     ap.add_argument("--no-extra", action="store_true",
@@ -325,7 +332,8 @@ def main():
     inp = workload.make_inputs(args.workload, seed=args.seed, device=dev)
     T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
     routed = "Wr" in inp
-    mx = cfg["precision"] == "mxfp8"
+    mx = cfg["precision"] in ("mxfp8", "mxfp4")
+    fbits = 4 if cfg["precision"] == "mxfp4" else 8
     stream = torch.cuda.current_stream()
 
     if args.calib_copy_mib:
@@ -338,7 +346,7 @@ def main():
         del src, dst
 
     main_run = run_layer(m, MoeLayer, inp, cfg, stream, args, mx=mx,
-                         persistent=args.persistent, bf16_dw=args.bf16_dw)
+                         persistent=args.persistent, bf16_dw=args.bf16_dw, fbits=fbits)
     ms, kernels = main_run["ms"], main_run["kernels"]
     tokens_per_s = T / (ms * 1e-3)
 
@@ -380,6 +388,18 @@ def main():
                    "weight_quantize_ms": round(r["quant_ms"], 4),
                    "layer_ms_without_weight_quantize": round(r["ms"] - r["quant_ms"], 4),
                    "grouped_gemm": r["gemm"], "kernels": r["kernels"]}
+        torch.cuda.empty_cache()
+
+    # and in MXFP4 mode (E2M1 elements, the same scales and axes)
+    mx4_line = None
+    if not mx and not args.no_mxfp4 and routed and I % 256 == 0:
+        print("[bench] MXFP4 mode on the same inputs", file=sys.stderr, flush=True)
+        r = run_layer(m, MoeLayer, inp, cfg, stream, args, mx=True, fbits=4)
+        mx4_line = {"tokens_per_s": round(T / (r["ms"] * 1e-3), 1),
+                    "ms_per_step": round(r["ms"], 4),
+                    "weight_quantize_ms": round(r["quant_ms"], 4),
+                    "layer_ms_without_weight_quantize": round(r["ms"] - r["quant_ms"], 4),
+                    "grouped_gemm": r["gemm"], "kernels": r["kernels"]}
         torch.cuda.empty_cache()
 
     # The weight gradients stored as bf16 (the alternative to fp32 main gradients): the same
@@ -448,6 +468,15 @@ def main():
                 "wgrad_parts_us": {g: rw["kernels"][g].get("parts_us")
                                    for g in ("bwd_down_wgrad", "bwd_gate_wgrad")
                                    if g in rw["kernels"]}}
+        if not args.no_mxfp4 and cz["I"] % 256 == 0:
+            print("[bench] local expert slice in MXFP4 mode", file=sys.stderr, flush=True)
+            r4 = run_layer(m, MoeLayer, iz, cz, stream, args, mx=True, fbits=4)
+            slice_line["mxfp4"] = {
+                "ms_per_step": round(r4["ms"], 4),
+                "weight_quantize_ms": round(r4["quant_ms"], 4),
+                "layer_ms_without_weight_quantize": round(r4["ms"] - r4["quant_ms"], 4),
+                "grouped_gemm": r4["gemm"],
+                "gemm_us": {g: r4["kernels"][g]["us"] for g in GEMMS if g in r4["kernels"]}}
         if cpu is not None:
             cpu.setdefault("per_config", {})["local_zipf"] = cpu_expert_sample(
                 iz, cz, cz["T"] * cz["k"])
@@ -500,7 +529,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8-e4m3/bf16" if mx else "bf16",
+        "dtype": ("mxfp4-e2m1/bf16" if fbits == 4 else "mxfp8-e4m3/bf16") if mx else "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "d": d, "E": E, "k": k, "I": I,
                    "precision": cfg["precision"], "weight_grad_dtype": "bf16" if args.bf16_dw else "fp32",
@@ -510,6 +539,7 @@ def main():
         "grouped_gemm": main_run["gemm"],
         "permute_combine": pc,
         "mxfp8": mx_line,
+        "mxfp4": mx4_line,
         "bf16_dw": bf16_dw_line,
         "expert_slice": slice_line,
         **extra,
@@ -607,15 +637,16 @@ def run_stream(workload, dev, stream, args):
 
 
 def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=True,
-              mx_wgrad=False, bf16_dw=False):
+              mx_wgrad=False, bf16_dw=False, fbits=8):
     """Warm up and time `args.steps` layer steps without any per-launch event, then (unless
     `trace` is off) time as many again with the library's per-launch events on the layer's
-    stream, for the per-kernel times. In MXFP8 mode each step first quantises the weights."""
+    stream, for the per-kernel times. In the MX modes (`mx`; fbits 8 MXFP8, 4 MXFP4) each step
+    first quantises the weights."""
     import torch
     T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
     dev = inp["X"].device
     routed = "Wr" in inp
-    prec = m.MOE_PREC_MXFP8 if mx else m.MOE_PREC_BF16
+    prec = (m.MOE_PREC_MXFP4 if fbits == 4 else m.MOE_PREC_MXFP8) if mx else m.MOE_PREC_BF16
     L = MoeLayer(T, d, E, k, I, device=dev, persistent=persistent, precision=prec,
                  mx_wgrad=mx_wgrad, bf16_dw=bf16_dw)
     wr = inp.get("Wr")
@@ -628,7 +659,8 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=T
             L.quantize_weights(W1, W2, stream)
         L.step(X, wr, W1, W2, dY, stream=stream)
 
-    print(f"[bench] {'mxfp8' if mx else 'bf16'}{' persistent' if persistent else ''}"
+    tag = ("mxfp4" if fbits == 4 else "mxfp8") if mx else "bf16"
+    print(f"[bench] {tag}{' persistent' if persistent else ''}"
           f"{' bf16-dW' if bf16_dw else ''}: "
           f"warmup and {args.steps} untraced steps", file=sys.stderr, flush=True)
     res = time_steps(step, stream, args.steps, args.warmup)
@@ -645,7 +677,7 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=T
     del keep
 
     kernels = {}
-    alg = algorithmic(cfg, routed=routed, mx=mx, mx_wgrad=mx_wgrad, bf16_dw=bf16_dw)
+    alg = algorithmic(cfg, routed=routed, mx=mx, mx_wgrad=mx_wgrad, bf16_dw=bf16_dw, fbits=fbits)
     if trace and not args.no_trace:
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * per_step * args.steps)]
         for e in ev:
@@ -671,8 +703,9 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=T
             cnt[n] = cnt.get(n, 0) + 1
         # A step's work of one kind may take several launches (the GEMMs run their 256-row
         # blocks and their remainders as two, "<name>_big" and "<name>"; the MXFP8 gate wgrad
-        # also expands the big experts' fp8 rows, "<name>_expand"): a kernel's `us` is its time
-        # per step, summed over them, and `parts` splits it.
+        # also expands the big experts' fp8 rows, and the MXFP4 one every Xp row,
+        # "<name>_expand"): a kernel's `us` is its time per step, summed over them, and `parts`
+        # splits it.
         parts = {}
         for n in list(tot):
             base = n
@@ -684,7 +717,7 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=T
             us = sum(pt.values())
             launches = sum(cnt[p] for p in pt) // args.steps
             nbytes, flops = alg.get(n, (0, 0))
-            r = kernel_roofline(n, nbytes, flops, us, mx, mx_wgrad) if nbytes else {}
+            r = kernel_roofline(n, nbytes, flops, us, mx, mx_wgrad, fbits) if nbytes else {}
             kernels[n] = {"us": round(us, 2), "launches_per_step": launches,
                           "alg_bytes": nbytes, "alg_flops": flops,
                           **{kk: (round(v, 4) if isinstance(v, float) else v)
@@ -699,11 +732,11 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=T
         flops = sum(alg[g][1] for g in GEMMS)
         nbytes = sum(alg[g][0] for g in GEMMS)
         # the time-weighted MFMA peak of the six GEMMs at their own dtypes
-        peak = sum(kernels[g]["us"] * mfma_peak(g, mx, mx_wgrad) for g in GEMMS
+        peak = sum(kernels[g]["us"] * mfma_peak(g, mx, mx_wgrad, fbits) for g in GEMMS
                    if g in kernels) / gemm_us
         tf = flops / (gemm_us * 1e-6) / 1e12
         attainable = sum(
-            kernels[g]["us"] * min(mfma_peak(g, mx, mx_wgrad),
+            kernels[g]["us"] * min(mfma_peak(g, mx, mx_wgrad, fbits),
                                    HBM_GBPS * 1e9 * alg[g][1] / alg[g][0] / 1e12)
             for g in GEMMS if g in kernels) / gemm_us
         gemm = {"tflops": round(tf, 2), "mfma_peak_tflops": round(peak, 1),

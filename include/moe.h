@@ -49,7 +49,7 @@ typedef enum moe_status {
     MOE_ERR_WORKSPACE_TOO_SMALL = -5
 } moe_status;
 
-enum { MOE_PREC_BF16 = 0, MOE_PREC_MXFP8 = 1 };
+enum { MOE_PREC_BF16 = 0, MOE_PREC_MXFP8 = 1, MOE_PREC_MXFP4 = 2 };
 
 /* cfg.flags bits */
 enum {
@@ -71,7 +71,8 @@ enum {
  * I % 128 == 0 (128-wide tiles along I); T * k < 2^31; T * E < 2^31; and, because the kernels
  * address rows with 32-bit offsets: T * d < 2^31, T * k * d < 2^31, T * k * 2I < 2^31 (an
  * expert may receive all T * k rows) and 4 * I * d < 2^31 (the bytes of one expert's W1).
- * precision MOE_PREC_BF16 or MOE_PREC_MXFP8.
+ * precision MOE_PREC_BF16, MOE_PREC_MXFP8 or MOE_PREC_MXFP4 (MXFP4 also needs I % 256 == 0: its
+ * K steps along I are 256 deep).
  * Every entry point that enqueues work also checks that the current HIP device is a gfx950
  * (MOE_ERR_UNSUPPORTED otherwise, MOE_ERR_HIP when no device can be queried).
  *
@@ -89,9 +90,19 @@ enum {
  * product, quantised directly) and A, dW1 reads dH and the ring's MXFP8 image of Xp, each
  * quantised so. dWr is unchanged.
  *
+ * MXFP4 mode (the MarkTechPost page, section "MoE layer as the bottleneck", names the team's
+ * earlier 4-bit NVFP4 training kernels; this mode takes the OCP MX 4-bit format instead, which
+ * gfx950's scaled MFMA reads) follows the OCP MX v1.0 MXFP4 format on the same axes as MXFP8
+ * mode: elements are E2M1 (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), stored two to a byte
+ * with element 2i in the low nibble; the scale code is floor(log2 amax) - 2 + 127 clamped to
+ * 0..254; elements round to nearest even and saturate to +-6. The weight gradients and dWr read
+ * bf16 operands, Xp taken as the exact bf16 image of the MXFP4 codes the ring holds.
+ * MOE_FLAG_MXFP8_WGRAD is not accepted. Buffers: a ring slot holds Xp's codes [T*k, d/2 bytes]
+ * then its scales; moe_quantize_weights writes the four weight copies in E2M1.
+ *
  * Weight-gradient precision. The pages do not say in which precision the weight gradients are
  * kept. By default dw1 and dw2 are fp32 (the caller's main gradient, which microbatches
- * accumulate into). With MOE_FLAG_BF16_DW (either precision) they are bf16: each element is
+ * accumulate into). With MOE_FLAG_BF16_DW (any precision) they are bf16: each element is
  * the same fp32 sum rounded once to nearest even where it is stored; with accumulate the fp32
  * sum of the stored bf16 value and the new result is rounded once. dwr stays fp32. */
 typedef struct moe_cfg {
@@ -114,26 +125,27 @@ typedef struct moe_sizes {
     size_t ws_O;           /* offset of the expert outputs O, bf16 [T*k, d], valid after forward */
     size_t ws_dH;          /* offset of dH, bf16 [T*k, 2I], valid after backward */
     size_t ws_dXp;         /* offset of dXp, bf16 [T*k, d], valid after backward */
-    size_t wq;             /* MXFP8: bytes of the quantised-weight buffer (0 in BF16 mode) */
+    size_t wq;             /* MX modes: bytes of the quantised-weight buffer (0 in BF16 mode) */
 } moe_sizes;
 
 /* Sizes of every caller buffer for `cfg`. Host only; enqueues nothing. (Plumbing of this
  * library, defined by no passage of the pages. The schedule and task tables live inside the
  * workspace, so they have no size of their own here.)
  * In MXFP8 mode a ring slot holds the E4M3 codes of Xp [T*k, d] followed (at the next 256-byte
- * boundary) by their scales [T*k, d/32]. */
+ * boundary) by their scales [T*k, d/32]; in MXFP4 mode the E2M1 codes [T*k, d/2 bytes] followed
+ * by the scales. */
 int moe_query(const moe_cfg* cfg, moe_sizes* out);
 
 /*
- * moe_quantize_weights - MXFP8 mode only: the quantised expert weights every MXFP8 forward and
- * backward reads. Call it once per weight update; the result serves any number of batches.
+ * moe_quantize_weights - MX modes only: the quantised expert weights every MXFP8 or MXFP4 forward
+ * and backward reads. Call it once per weight update; the result serves any number of batches.
  *
  *   w1  bf16 [E, 2I, d]   in
  *   w2  bf16 [E, d, I]    in
- *   wq  bytes [wq_bytes]  out, wq_bytes >= moe_sizes.wq. It receives four MXFP8 tensors, each
+ *   wq  bytes [wq_bytes]  out, wq_bytes >= moe_sizes.wq. It receives four quantised tensors, each
  *       with its per-32 scales: W1 along d [E, 2I, d] and W2 along I [E, d, I] (forward), and W2
  *       along d stored transposed [E, I, d] and W1 along 2I stored transposed [E, d, 2I]
- *       (dgrad). The layout inside wq is private to the library.
+ *       (dgrad), in the mode's element format. The layout inside wq is private to the library.
  * Errors: MOE_ERR_INVALID_ARG in BF16 mode; MOE_ERR_WORKSPACE_TOO_SMALL for a short wq.
  */
 int moe_quantize_weights(const moe_cfg* cfg, const void* w1, const void* w2, void* wq,
@@ -178,8 +190,8 @@ int moe_route(const moe_cfg* cfg, const void* x, const void* w_router, float* lo
  *                                       position either way)
  *   x        bf16 [T, d]           in
  *   ring     bytes [ring_bytes]    out: slot `slot` (at slot * ring_slot bytes) receives
- *                                       Xp[pos] = x[row_src[pos] / k], bf16 [T*k, d]; in MXFP8
- *                                       mode its MXFP8 image (codes, then scales)
+ *                                       Xp[pos] = x[row_src[pos] / k], bf16 [T*k, d]; in an MX
+ *                                       mode its MX image (codes, then scales)
  *   counts   int32 [E]             out: rows per expert
  *   offsets  int32 [E+1]           out: exclusive scan of counts, offsets[E] = T*k
  *   row_src  int32 [T*k]           out: pos -> r
@@ -230,7 +242,7 @@ int moe_permute_static(const moe_cfg* cfg, const int32_t* topk_idx, const void* 
  *   topk_w   fp32 [T, k]     in
  *   w1       bf16 [E, 2I, d] in
  *   w2       bf16 [E, d, I]  in
- *   wq, wq_bytes             in: MXFP8 mode, the buffer moe_quantize_weights filled (ignored in
+ *   wq, wq_bytes             in: MX modes, the buffer moe_quantize_weights filled (ignored in
  *                                BF16 mode, may be NULL)
  *   y        bf16 [T, d]     out
  *   saved    bytes [saved_bytes]   out: H and A at the offsets moe_query reports
@@ -256,7 +268,7 @@ int moe_forward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t
  * receives 256 rows or more; otherwise the down projection of those experts' rows sums its K
  * chunks from another start (the separate path gives such blocks a 256 x 256 tile), which
  * changes their O and y in the last bits only. Arguments and errors are those of the three
- * calls; MXFP8 mode returns MOE_ERR_UNSUPPORTED. The grid barriers keep their state in a
+ * calls; the MX modes return MOE_ERR_UNSUPPORTED. The grid barriers keep their state in a
  * device variable of the library, one per GPU: fused calls that overlap on one GPU race.
  */
 int moe_forward_fused(const moe_cfg* cfg, const void* x, const void* w_router, float* logits,

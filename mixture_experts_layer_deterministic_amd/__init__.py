@@ -24,6 +24,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 MOE_OK = 0
 MOE_PREC_BF16 = 0
 MOE_PREC_MXFP8 = 1
+MOE_PREC_MXFP4 = 2
 MOE_FLAG_PERSISTENT = 1
 MOE_FLAG_MXFP8_WGRAD = 2
 MOE_FLAG_BF16_DW = 4

@@ -21,10 +21,11 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   bool mx;
+  int fb;  // MX code bits: 8 (MXFP8) or 4 (MXFP4); 0 in BF16 mode
   // workspace
   size_t status, sched, blk_cnt, blk_flag, rank, O, dH, dXp, dyw, dwpart, dl_pos, wg_count,
       wg_table1, wg_table2, wr32, total;
-  // workspace, MXFP8 only: dY, A and dH quantised along their GEMM's K (codes, scales)
+  // workspace, MX modes only: dY, A and dH quantised along their GEMM's K (codes, scales)
   size_t dyq, dys, aq, aqs, dhq, dhs;
   // workspace, MXFP8 weight gradients only: padded segment offsets [E + 1], and the two
   // operands of one weight gradient quantised along the positions, [rows][P] with scales
@@ -32,9 +33,9 @@ struct Layout {
   int P;
   // saved
   size_t H, A, saved_total;
-  // ring slot: bf16 Xp, or MXFP8 Xp codes at 0 and scales at slot_sc
+  // ring slot: bf16 Xp, or MX Xp codes at 0 and scales at slot_sc
   size_t slot, slot_sc;
-  // quantised weights (MXFP8): W1 and W2 along their forward K, and transposed along their
+  // quantised weights (MX): W1 and W2 along their forward K, and transposed along their
   // dgrad K: W1f [E,2I,d], W2f [E,d,I], W2b [E,I,d], W1b [E,d,2I], each with per-32 scales
   size_t w1f, w1fs, w2f, w2fs, w2b, w2bs, w1b, w1bs, wq_total;
   int nb, nIt, max_mtiles;
@@ -108,13 +109,16 @@ Layout layout(const moe_cfg* c) {
   L.dwpart = take(sizeof(float) * Tk * L.nIt);
   L.dl_pos = take(sizeof(float) * Tk);
   L.wr32 = take(sizeof(float) * E * d);
-  L.mx = c->precision == MOE_PREC_MXFP8;
+  L.mx = c->precision == MOE_PREC_MXFP8 || c->precision == MOE_PREC_MXFP4;
+  L.fb = c->precision == MOE_PREC_MXFP8 ? 8 : c->precision == MOE_PREC_MXFP4 ? 4 : 0;
   const size_t T = c->T, mxs = L.mx ? 1 : 0;
-  L.dyq = take(mxs * T * d);
+  // bytes of n codes
+  auto cb = [&](size_t n) { return n * L.fb / 8; };
+  L.dyq = take(mxs * cb(T * d));
   L.dys = take(mxs * T * d / 32);
-  L.aq = take(mxs * Tk * I);
+  L.aq = take(mxs * cb(Tk * I));
   L.aqs = take(mxs * Tk * I / 32);
-  L.dhq = take(mxs * Tk * 2 * I);
+  L.dhq = take(mxs * cb(Tk * 2 * I));
   L.dhs = take(mxs * Tk * 2 * I / 32);
   const size_t mxw = L.mx && (c->flags & MOE_FLAG_MXFP8_WGRAD) ? 1 : 0;
   L.P = mxw ? seg_capacity((int)Tk, c->E) : 0;
@@ -131,18 +135,18 @@ Layout layout(const moe_cfg* c) {
   L.saved_total = o;
   if (L.mx) {
     o = 0;
-    take(Tk * d);
+    take(cb(Tk * d));
     L.slot_sc = o;
     take(Tk * d / 32);
     L.slot = o;
     o = 0;
-    L.w1f = take(E * 2 * I * d);
+    L.w1f = take(cb(E * 2 * I * d));
     L.w1fs = take(E * 2 * I * d / 32);
-    L.w2f = take(E * d * I);
+    L.w2f = take(cb(E * d * I));
     L.w2fs = take(E * d * I / 32);
-    L.w2b = take(E * I * d);
+    L.w2b = take(cb(E * I * d));
     L.w2bs = take(E * I * d / 32);
-    L.w1b = take(E * d * 2 * I);
+    L.w1b = take(cb(E * d * 2 * I));
     L.w1bs = take(E * d * 2 * I / 32);
     L.wq_total = o;
   } else {
@@ -174,7 +178,10 @@ struct Launches {
 
 int check_mode(const moe_cfg* c) {
   if (!cfg_ok(c)) return MOE_ERR_INVALID_ARG;
-  if (c->precision != MOE_PREC_BF16 && c->precision != MOE_PREC_MXFP8) return MOE_ERR_UNSUPPORTED;
+  if (c->precision != MOE_PREC_BF16 && c->precision != MOE_PREC_MXFP8 &&
+      c->precision != MOE_PREC_MXFP4)
+    return MOE_ERR_UNSUPPORTED;
+  if (c->precision == MOE_PREC_MXFP4 && c->I % 256 != 0) return MOE_ERR_INVALID_ARG;
   if (c->flags & ~(MOE_FLAG_PERSISTENT | MOE_FLAG_MXFP8_WGRAD | MOE_FLAG_BF16_DW))
     return MOE_ERR_INVALID_ARG;
   if ((c->flags & MOE_FLAG_MXFP8_WGRAD) && c->precision != MOE_PREC_MXFP8)
@@ -188,7 +195,7 @@ int check_ring(const Layout& L, const void* ring, size_t ring_bytes, int32_t slo
   return MOE_OK;
 }
 
-// The quantised weights of MXFP8 mode, or an error code when they are missing.
+// The quantised weights of the MX modes, or an error code when they are missing.
 int check_wq(const Layout& Y, const void* wq, size_t wq_bytes) {
   if (!Y.mx) return MOE_OK;
   if (!aligned16(wq)) return MOE_ERR_INVALID_ARG;
@@ -267,9 +274,9 @@ int moe_quantize_weights(const moe_cfg* cfg, const void* w1, const void* w2, voi
                          size_t wq_bytes, moe_stream_t stream) {
   int st = check_mode(cfg);
   if (st) return st;
-  if (cfg->precision != MOE_PREC_MXFP8) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(w1) || !aligned16(w2) || !aligned16(wq)) return MOE_ERR_INVALID_ARG;
   const Layout Y = layout(cfg);
+  if (!Y.mx) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w1) || !aligned16(w2) || !aligned16(wq)) return MOE_ERR_INVALID_ARG;
   if (wq_bytes < Y.wq_total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if ((st = check_device())) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -278,10 +285,10 @@ int moe_quantize_weights(const moe_cfg* cfg, const void* w1, const void* w2, voi
   const uint16_t* a2 = static_cast<const uint16_t*>(w2);
   Launches L;
   L(launch_quant_weight(a1, E, 2 * I, d, at<uint8_t>(wq, Y.w1f), at<uint8_t>(wq, Y.w1fs),
-                        at<uint8_t>(wq, Y.w1b), at<uint8_t>(wq, Y.w1bs), "quant_w1", s));
+                        at<uint8_t>(wq, Y.w1b), at<uint8_t>(wq, Y.w1bs), Y.fb, "quant_w1", s));
   if (!L.err)
     L(launch_quant_weight(a2, E, d, I, at<uint8_t>(wq, Y.w2f), at<uint8_t>(wq, Y.w2fs),
-                          at<uint8_t>(wq, Y.w2b), at<uint8_t>(wq, Y.w2bs), "quant_w2", s));
+                          at<uint8_t>(wq, Y.w2b), at<uint8_t>(wq, Y.w2bs), Y.fb, "quant_w2", s));
   return L.status();
 }
 
@@ -334,7 +341,7 @@ int moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, void
                        s));
   if (!L.err)
     L(launch_perm_place(topk_idx, rank, blk, Tk, cfg->E, cfg->k, row_src, tk_row,
-                        static_cast<const uint16_t*>(x), xp, xp8, xps, cfg->d, s));
+                        static_cast<const uint16_t*>(x), xp, xp8, xps, cfg->d, Y.fb, s));
   return L.status();
 }
 
@@ -376,7 +383,7 @@ int moe_permute_static(const moe_cfg* cfg, const int32_t* topk_idx, const void* 
     L(launch_perm_scan(blk, Y.nb, cfg->E, flag, counts, offsets, device_status, s));
   if (!L.err)
     L(launch_perm_place(topk_idx, rank, blk, (int)Tk, cfg->E, cfg->k, row_src, tk_row,
-                        static_cast<const uint16_t*>(x), xp, xp8, xps, cfg->d, s));
+                        static_cast<const uint16_t*>(x), xp, xp8, xps, cfg->d, Y.fb, s));
   return L.status();
 }
 
@@ -410,11 +417,12 @@ int moe_forward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_t
     uint8_t* aqs = at<uint8_t>(workspace, Y.aqs);
     if (!L.err)
       L(launch_fwd_gateup_mx({slot_base, slot_base + Y.slot_sc, at<uint8_t>(wq, Y.w1f),
-                              at<uint8_t>(wq, Y.w1fs), H, A, aq, aqs, offsets, sched, d, I, Tk, E},
+                              at<uint8_t>(wq, Y.w1fs), H, A, aq, aqs, offsets, sched, d, I, Tk, E,
+                              Y.fb},
                              pers, s));
     if (!L.err)
       L(launch_fwd_down_mx({aq, aqs, at<uint8_t>(wq, Y.w2f), at<uint8_t>(wq, Y.w2fs), O, offsets,
-                            sched, d, I, Tk, E},
+                            sched, d, I, Tk, E, Y.fb},
                            pers, s));
   } else {
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(slot_base);
@@ -536,12 +544,12 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
     uint8_t* dys = at<uint8_t>(workspace, Y.dys);
     uint8_t* dhq = at<uint8_t>(workspace, Y.dhq);
     uint8_t* dhs = at<uint8_t>(workspace, Y.dhs);
-    if (!L.err) L(launch_quant_rows(dyp, cfg->T, d, dyq, dys, "quant_dy", s));
+    if (!L.err) L(launch_quant_rows(dyp, cfg->T, d, dyq, dys, Y.fb, "quant_dy", s));
     if (!L.err) L(launch_scale_gather(dyp, tk_row, topk_w, cfg->T, k, d, dyw, s));
     if (!L.err)
       L(launch_bwd_down_dgrad_mx({dyq, dys, row_src, topk_w, at<uint8_t>(wq, Y.w2b),
                                   at<uint8_t>(wq, Y.w2bs), H, A, dH, dwpart, dhq, dhs, offsets,
-                                  sched, d, I, k, Tk, E},
+                                  sched, d, I, k, Tk, E, Y.fb},
                                  pers, s));
     if (!L.err)
       L(launch_dw_router(dwpart, Y.nIt, tk_row, topk_w, cfg->T, k, d_topk_w, dl_pos, routed, s));
@@ -584,17 +592,30 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
                         wg_count + 1, E, d, I, accumulate, bdw, false, "bwd_down_wgrad",
                         "wgrad_sched_down"},
                        s));
-      // the gate wgrad goes first: until the gate dgrad writes dXp, that buffer holds the bf16
-      // image of the big experts' fp8 Xp rows for the big-expert wgrad kernel
-      if (!L.err)
-        L(launch_wgrad({dH, nullptr, xp8, xps, dw1, offsets, at<int4>(workspace, Y.wg_table1),
-                        wg_count, E, 2 * I, d, accumulate, bdw, true, "bwd_gate_wgrad",
-                        "wgrad_sched_gate", dXp},
-                       s));
+      if (Y.fb == 4) {
+        // MXFP4: the dXp buffer first holds the bf16 image of every Xp row, which the gate
+        // wgrad and dWr read, before the gate dgrad writes dXp into it
+        if (!L.err) L(launch_expand_fp4(xp8, xps, Tk, d, dXp, "bwd_gate_wgrad_expand", s));
+        if (!L.err)
+          L(launch_wgrad({dH, dXp, nullptr, nullptr, dw1, offsets,
+                          at<int4>(workspace, Y.wg_table1), wg_count, E, 2 * I, d, accumulate,
+                          bdw, true, "bwd_gate_wgrad", "wgrad_sched_gate"},
+                         s));
+        if (!L.err && routed)
+          L(launch_dwr(dl_pos, dXp, nullptr, nullptr, offsets, E, d, dwr, accumulate, s));
+      } else {
+        // the gate wgrad goes first: until the gate dgrad writes dXp, that buffer holds the
+        // bf16 image of the big experts' fp8 Xp rows for the big-expert wgrad kernel
+        if (!L.err)
+          L(launch_wgrad({dH, nullptr, xp8, xps, dw1, offsets, at<int4>(workspace, Y.wg_table1),
+                          wg_count, E, 2 * I, d, accumulate, bdw, true, "bwd_gate_wgrad",
+                          "wgrad_sched_gate", dXp},
+                         s));
+      }
     }
     if (!L.err)
       L(launch_bwd_gate_dgrad_mx({dhq, dhs, at<uint8_t>(wq, Y.w1b), at<uint8_t>(wq, Y.w1bs), dXp,
-                                  offsets, sched, d, I, Tk, E},
+                                  offsets, sched, d, I, Tk, E, Y.fb},
                                  pers, s));
   } else {
     if (!L.err) L(launch_scale_gather(dyp, tk_row, topk_w, cfg->T, k, d, dyw, s));
@@ -620,7 +641,8 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
     L(launch_uncombine(dXp, tk_row, topk_idx, dl_pos,
                        routed ? static_cast<const uint16_t*>(w_router) : nullptr, cfg->T, k, d,
                        static_cast<uint16_t*>(dx), s));
-  if (!L.err && routed) L(launch_dwr(dl_pos, xp, xp8, xps, offsets, E, d, dwr, accumulate, s));
+  if (!L.err && routed && Y.fb != 4)
+    L(launch_dwr(dl_pos, xp, xp8, xps, offsets, E, d, dwr, accumulate, s));
   return L.status();
 }
 

@@ -69,6 +69,34 @@ MOE_DEV void e4m3x4_to_f32(uint32_t w, float (&f)[4]) {
   f[3] = hi[1];
 }
 
+// MXFP4 (OCP MX): E2M1 elements (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) sharing one E8M0 scale
+// per 32, packed two to a byte with element 2i in the low nibble. The scale code is
+// floor(log2 amax) - 2 + 127 (2 being E2M1's largest exponent), clamped to 0..254, 0 for an
+// all-zero block; mx_inv_scale and mx_scale read it as for MXFP8.
+MOE_DEV uint32_t mx4_scale_code(float amax) {
+  const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu);
+  return static_cast<uint32_t>(min(max(e - 2, 0), 254));
+}
+// The E2M1 code of a scaled fp32 value: the nearest magnitude, a tie going to the even code, and
+// magnitudes past 6 saturating to 6; the sign bit (8) is the value's sign bit. The comparisons
+// are exact, so this is round-to-nearest-even on the value itself.
+MOE_DEV uint32_t e2m1_code(float x) {
+  const float a = fabsf(x);
+  const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.f ? 6u : 7u;
+  return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+// Four scaled values to four E2M1 codes in the low 16 bits (value i in bits 4 i .. 4 i + 3).
+MOE_DEV uint32_t e2m1x4(float a, float b, float c, float d) {
+  return e2m1_code(a) | (e2m1_code(b) << 4) | (e2m1_code(c) << 8) | (e2m1_code(d) << 12);
+}
+// The value of an E2M1 code (exact in fp32).
+MOE_DEV float e2m1_value(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const float mag = e == 0 ? 0.5f * (float)m : __builtin_ldexpf(1.0f + 0.5f * (float)m, (int)e - 1);
+  return (c & 8u) ? -mag : mag;
+}
+
 // 16 bytes read once: a non-temporal load, so a single-use stream does not push reused data
 // (router rows, index arrays) out of the caches. Measured on the un-permute at the DeepSeek-V3
 // shape: 89-103 -> 58 us.

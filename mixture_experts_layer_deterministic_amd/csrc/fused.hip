@@ -230,7 +230,7 @@ __global__ void __launch_bounds__(kFusedThreads, 2) fused_forward_kernel(const F
   grid_sync(bar, nwg, p.status);
   // 6. placement of every row and the copy of its token into the ring slot
   for (int vb = b0; vb * p.tpb < T; vb += G) {
-    perm_place_block<false>(vb, p.topk_idx, p.rank, p.blk_cnt, T, E, k, p.row_src, p.tk_row, p.x,
+    perm_place_block<0>(vb, p.topk_idx, p.rank, p.blk_cnt, T, E, k, p.row_src, p.tk_row, p.x,
                             p.xp, nullptr, nullptr, d, p.tpb, ish);
     __syncthreads();
   }

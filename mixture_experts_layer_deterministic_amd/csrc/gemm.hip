@@ -257,23 +257,29 @@ struct DownDgradBigArgs {
 
 
 // ------------------------------------------------------------------------------------------
-// MXFP8 mode. Both operands are E4M3 codes, K-contiguous, with one E8M0 scale per 32 along K;
-// one v_mfma_scale_f32_16x16x128_f8f6f4 covers 16 x 16 outputs and 128 K. Operand layout of
-// that instruction on gfx950 (lane l, row or column l % 16, group g = l / 16): bytes 0..15 hold
-// K [16 g, 16 g + 16) and bytes 16..31 hold K [64 + 16 g, 64 + 16 g + 16); the scale of K
-// block b = [32 b, 32 b + 32) comes from byte 0 of lane (row + 16 b). LDS holds each stage as
-// [BM][LDK] A codes, [BN][LDK] B codes (chunk-permuted rows, mxswz), then one 32-bit word of
-// four block scales per row.
+// MX modes. Both operands are K-contiguous codes with one E8M0 scale per 32 along K: E4M3, one
+// a byte (MXFP8, F = 8), or E2M1, two a byte with element 2i in the low nibble (MXFP4, F = 4).
+// One v_mfma_scale_f32_16x16x128_f8f6f4 covers 16 x 16 outputs and 128 K. Its operand layout on
+// gfx950 (lane l, row or column l % 16, group g = l / 16): for E4M3, bytes 0..15 hold K
+// [16 g, 16 g + 16) and bytes 16..31 hold K [64 + 16 g, 64 + 16 g + 16); for E2M1, bytes 0..15
+// hold K [32 g, 32 g + 32) and the upper half of the operand is not read. The scale of K block
+// b = [32 b, 32 b + 32) comes from byte 0 of lane (row + 16 b) in both. A K step moves 128
+// bytes of every row: 128 K of E4M3 (one MFMA) or 256 K of E2M1 (two MFMAs, on the row's
+// 16-byte chunks g and 4 + g). LDS holds each stage as [BM][128] A codes, [BN][128] B codes
+// (chunk-permuted rows, mxswz), then the step's block scales, 4 (E4M3) or 8 (E2M1) bytes a row.
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int F_ = 8>
 struct GeoMx {
-  static constexpr int BM = BM_, BN = BN_, BK = 128;
+  static constexpr int F = F_;                     // bits per code
+  static_assert(F == 8 || F == 4, "E4M3 or E2M1 codes");
+  static constexpr int BM = BM_, BN = BN_, BK = 1024 / F;  // K per step
+  static constexpr int SCW = BK / 128;             // 32-bit scale words per row and step
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int MB = WM / 16, NB = WN / 16;
-  static constexpr int LDK = BK;                   // bytes per LDS row (chunks permuted)
+  static constexpr int LDK = 128;                  // bytes per LDS row (chunks permuted)
   static constexpr int SC_OFF = (BM + BN) * LDK;   // byte offset of the scale words
-  static constexpr int STAGE = SC_OFF + (BM + BN) * 4;
+  static constexpr int STAGE = SC_OFF + (BM + BN) * 4 * SCW;
   static constexpr int kSmem = 2 * STAGE;
   static constexpr bool kMx = true;
   static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
@@ -288,21 +294,23 @@ using GeoMxBig = GeoMx<256, 256, 2, 4>;
 // and row stores then spread over all banks, where rows padded to 144 bytes conflicted.
 MOE_DEV int mxswz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
-// ROWS rows of fp8 codes, K-contiguous: 8 vectors of 16 bytes per 128-K step. Thread t < ROWS
-// also moves row t's scale word (four block scales of the step), loading the words of four
-// steps at once where the row length allows. Every row is real (a tile's rows past its expert's
-// count repeat the expert's last row; their outputs are never stored), so the code loads carry
-// no per-row condition, as in LoadK.
-template <int ROWS, int LDK>
+// ROWS rows of codes, K-contiguous: 8 vectors of 16 bytes per step. Thread t < ROWS also moves
+// row t's SCW scale words (the step's block scales), loading the words of 16 bytes of scales at
+// once where the row length allows. Every row is real (a tile's rows past its expert's count
+// repeat the expert's last row; their outputs are never stored), so the code loads carry no
+// per-row condition, as in LoadK.
+template <int ROWS, int LDK, int SCW = 1>
 struct LoadK8 {
   static constexpr int VPR = 8;
   static constexpr int NV = ROWS * VPR;
   static constexpr int PT = (NV + kThreads - 1) / kThreads;
+  static constexpr int SPG = 4 / SCW;  // steps per 16 bytes of scales
+  static_assert(SCW == 1 || SCW == 2, "4 or 8 scale bytes per step");
   const uint8_t* rp[PT];
   uint4 r[PT];
   const uint8_t* sp;
-  uint4 s4;     // the scale words of four consecutive steps (or of one, in s4.x)
-  int sg, sidx; // group held in s4 and this step's word in it
+  uint4 s4;     // the scale words of SPG consecutive steps (or of one, from s4.x)
+  int sg, sidx; // group held in s4 and this step's index in it
   bool grouped; // rows hold a multiple of 16 scale bytes: load them 16 bytes at a time
 
   // kdim: the K extent of a row (elements), so a row holds kdim / 32 scale bytes. The scale
@@ -320,7 +328,7 @@ struct LoadK8 {
     s4 = make_uint4(0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu);
     sidx = 0;
   }
-  // The scale word is picked in store(), so no load result is waited for here.
+  // The scale words are picked in store(), so no load result is waited for here.
   MOE_DEV void load(int kt) {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
@@ -329,13 +337,18 @@ struct LoadK8 {
     }
     if (!sp) return;
     if (grouped) {
-      if ((kt >> 2) != sg) {
-        sg = kt >> 2;
+      if (kt / SPG != sg) {
+        sg = kt / SPG;
         s4 = *reinterpret_cast<const uint4*>(sp + (size_t)sg * 16);
       }
-      sidx = kt & 3;
-    } else {
+      sidx = kt % SPG;
+    } else if constexpr (SCW == 1) {
       s4.x = *reinterpret_cast<const uint32_t*>(sp + (size_t)kt * 4);
+      sidx = 0;
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2*>(sp + (size_t)kt * 8);
+      s4.x = w.x;
+      s4.y = w.y;
       sidx = 0;
     }
   }
@@ -347,18 +360,29 @@ struct LoadK8 {
     }
     if (threadIdx.x < ROWS) {
       // masks rather than a selected vector element, which the compiler would index in scratch
-      const uint32_t m0 = 0u - (sidx == 0), m1 = 0u - (sidx == 1), m2 = 0u - (sidx == 2),
-                     m3 = 0u - (sidx == 3);
-      scales[threadIdx.x] = (s4.x & m0) | (s4.y & m1) | (s4.z & m2) | (s4.w & m3);
+      if constexpr (SCW == 1) {
+        const uint32_t m0 = 0u - (sidx == 0), m1 = 0u - (sidx == 1), m2 = 0u - (sidx == 2),
+                       m3 = 0u - (sidx == 3);
+        scales[threadIdx.x] = (s4.x & m0) | (s4.y & m1) | (s4.z & m2) | (s4.w & m3);
+      } else {
+        const uint32_t m0 = 0u - (sidx == 0), m1 = ~m0;
+        *reinterpret_cast<uint2*>(scales + 2 * threadIdx.x) =
+            make_uint2((s4.x & m0) | (s4.z & m1), (s4.y & m0) | (s4.w & m1));
+      }
     }
   }
 };
 
 template <class G>
-MOE_DEV void mx_store_stage(const LoadK8<G::BM, G::LDK>& la, const LoadK8<G::BN, G::LDK>& lb,
-                            uint8_t* stage) {
+using LoadA8 = LoadK8<G::BM, G::LDK, G::SCW>;
+template <class G>
+using LoadB8 = LoadK8<G::BN, G::LDK, G::SCW>;
+
+template <class G>
+MOE_DEV void mx_store_stage(const LoadA8<G>& la, const LoadB8<G>& lb, uint8_t* stage) {
   la.store(stage, reinterpret_cast<uint32_t*>(stage + G::SC_OFF));
-  lb.store(stage + G::BM * G::LDK, reinterpret_cast<uint32_t*>(stage + G::SC_OFF) + G::BM);
+  lb.store(stage + G::BM * G::LDK,
+           reinterpret_cast<uint32_t*>(stage + G::SC_OFF) + G::BM * G::SCW);
 }
 
 MOE_DEV i32x8 mx_frag(const uint8_t* tile, int row, int g) {
@@ -374,6 +398,45 @@ MOE_DEV i32x8 mx_frag(const uint8_t* tile, int row, int g) {
   v[6] = static_cast<int>(hi.z);
   v[7] = static_cast<int>(hi.w);
   return v;
+}
+
+// Half H of an operand read by mx_frag (chunk g for H = 0, chunk 4 + g for H = 1) as the
+// operand of an E2M1 MFMA, which reads the lower four registers only.
+template <int H>
+MOE_DEV i32x8 mx_half(const i32x8& v) {
+  i32x8 h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = v[4 * H + i];
+    h[4 + i] = v[4 * H + i];
+  }
+  return h;
+}
+
+// The scale bytes a lane of group g passes for one row: byte g of the step's word 0 (E4M3, and
+// the first 128 K of E2M1) and of word 1 (the second 128 K of E2M1).
+template <int SCW>
+MOE_DEV int2 mx_scales(const uint32_t* sc, int row, int g) {
+  if constexpr (SCW == 1) {
+    return make_int2(static_cast<int>((sc[row] >> (8 * g)) & 0xffu), 0);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(sc + 2 * row);
+    return make_int2(static_cast<int>((w.x >> (8 * g)) & 0xffu),
+                     static_cast<int>((w.y >> (8 * g)) & 0xffu));
+  }
+}
+
+// acc += the step's product of one row block and one column block
+template <int F>
+MOE_DEV f32x4 mx_mfma(const i32x8& b, const i32x8& a, f32x4 acc, int2 bs, int2 as) {
+  if constexpr (F == 8) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, acc, 0, 0, 0, bs.x, 0, as.x);
+  } else {
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mx_half<0>(b), mx_half<0>(a), acc, 4,
+                                                           4, 0, bs.x, 0, as.x);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(mx_half<1>(b), mx_half<1>(a), acc, 4,
+                                                            4, 0, bs.y, 0, as.y);
+  }
 }
 
 template <class P>
@@ -402,25 +465,24 @@ MOE_DEV void run_tile_mx(const typename P::Args& a, const typename P::Tile& t, u
       const uint8_t* sA = cur;
       const uint8_t* sB = cur + G::BM * G::LDK;
       const uint32_t* scA = reinterpret_cast<const uint32_t*>(cur + G::SC_OFF);
-      const uint32_t* scB = scA + G::BM;
+      const uint32_t* scB = scA + G::BM * G::SCW;
       i32x8 bf[G::NB];
-      int bs[G::NB];
+      int2 bs[G::NB];
 #pragma unroll
       for (int nb = 0; nb < G::NB; ++nb) {
         const int row = P::brow(wn, nb) + r16;
         bf[nb] = mx_frag(sB, row, g);
-        bs[nb] = static_cast<int>((scB[row] >> (8 * g)) & 0xffu);
+        bs[nb] = mx_scales<G::SCW>(scB, row, g);
       }
 #pragma unroll
       for (int mb = 0; mb < G::MB; ++mb) {
         if (!P::m_active(t, wm * G::WM + mb * 16)) continue;
         const int row = wm * G::WM + mb * 16 + r16;
         const i32x8 af = mx_frag(sA, row, g);
-        const int as = static_cast<int>((scA[row] >> (8 * g)) & 0xffu);
+        const int2 as = mx_scales<G::SCW>(scA, row, g);
 #pragma unroll
         for (int nb = 0; nb < G::NB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              bf[nb], af, acc[mb][nb], 0, 0, 0, bs[nb], 0, as);
+          acc[mb][nb] = mx_mfma<G::F>(bf[nb], af, acc[mb][nb], bs[nb], as);
       }
       if (kt + 1 < nk) mx_store_stage<G>(ld.la, ld.lb, smem + ((kt + 1) & 1) * G::STAGE);
       __syncthreads();
@@ -430,19 +492,33 @@ MOE_DEV void run_tile_mx(const typename P::Args& a, const typename P::Tile& t, u
   __syncthreads();
 }
 
-// MXFP8 image of 8 values held by one lane, as 2 dwords of E4M3 codes, with the block scale
-// shared by the four lanes l, l^16, l^32, l^48 (one row's 32 consecutive columns). Every lane
-// must call it.
+// MX image of 8 values held by one lane, with the block scale shared by the four lanes l, l^16,
+// l^32, l^48 (one row's 32 consecutive columns): the scale code for F-bit codes. Every lane must
+// call it.
+template <int F>
 MOE_DEV uint32_t mx_block_code(const float (&v)[8]) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   amax = fmaxf(amax, __shfl_xor(amax, 16));
   amax = fmaxf(amax, __shfl_xor(amax, 32));
-  return mx_scale_code(amax);
+  return F == 8 ? mx_scale_code(amax) : mx4_scale_code(amax);
 }
+// The codes of four values times inv: four E4M3 bytes, or four E2M1 nibbles in the low 16 bits.
+template <int F>
 MOE_DEV uint32_t mx_pack4(const float* v, float inv) {
-  return e4m3x2(v[0] * inv, v[1] * inv) | (e4m3x2(v[2] * inv, v[3] * inv) << 16);
+  if constexpr (F == 8)
+    return e4m3x2(v[0] * inv, v[1] * inv) | (e4m3x2(v[2] * inv, v[3] * inv) << 16);
+  else
+    return e2m1x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+}
+// Stores four codes of mx_pack4 at elements [c, c + 4) of a row of codes (c a multiple of 4).
+template <int F>
+MOE_DEV void mx_put4(uint8_t* row, int c, uint32_t codes) {
+  if constexpr (F == 8)
+    *reinterpret_cast<uint32_t*>(row + c) = codes;
+  else
+    *reinterpret_cast<uint16_t*>(row + c / 2) = static_cast<uint16_t>(codes);
 }
 
 // Problem 1 (MXFP8): forward gate/up with SwiGLU. A tile covers BN / 2 gate columns and the
@@ -494,19 +570,20 @@ struct MxFwdGateUpT {
     return nb < 2 ? wn * 32 + nb * 16 : kA + wn * 32 + (nb - 2) * 16;
   }
   struct Loader {
-    LoadK8<G::BM, G::LDK> la;
-    LoadK8<G::BN, G::LDK> lb;
+    LoadA8<G> la;
+    LoadB8<G> lb;
     MOE_DEV void init(const Args& a, const Tile& t) {
       const int d = a.d, I = a.I, mc = t.m.mcount, row0 = t.m.row0, n0 = t.n0;
       const uint8_t* xp8 = a.xp8;
       const uint8_t* xps = a.xps;
-      la.init([&](int m) { return xp8 + (size_t)(row0 + min(m, mc - 1)) * d; },
+      const size_t pb = (size_t)d * G::F / 8;  // bytes of codes per row
+      la.init([&](int m) { return xp8 + (size_t)(row0 + min(m, mc - 1)) * pb; },
               [&](int m) { return xps + (size_t)(row0 + min(m, mc - 1)) * (d / 32); }, d);
       const size_t wrow0 = (size_t)t.m.e * 2 * I;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
       auto wrow = [=](int n) { return wrow0 + (n < kA ? n0 + n : I + n0 + n - kA); };
-      lb.init([&](int n) { return w8 + wrow(n) * d; },
+      lb.init([&](int n) { return w8 + wrow(n) * pb; },
               [&](int n) { return ws + wrow(n) * (d / 32); }, d);
     }
     MOE_DEV void load(int kt) {  // weights first: they are the HBM stream
@@ -547,12 +624,12 @@ struct MxFwdGateUpT {
           *reinterpret_cast<uint2*>(a.A + pos * I + j) = aw;
         }
       }
-      const uint32_t code = mx_block_code(av);
+      const uint32_t code = mx_block_code<G::F>(av);
       const float inv = mx_inv_scale(code);
       if (live) {
-        *reinterpret_cast<uint32_t*>(a.aq + pos * I + c0 + 4 * (lane / 16)) = mx_pack4(av, inv);
-        *reinterpret_cast<uint32_t*>(a.aq + pos * I + c0 + 16 + 4 * (lane / 16)) =
-            mx_pack4(av + 4, inv);
+        uint8_t* q = a.aq + pos * (I * G::F / 8);
+        mx_put4<G::F>(q, c0 + 4 * (lane / 16), mx_pack4<G::F>(av, inv));
+        mx_put4<G::F>(q, c0 + 16 + 4 * (lane / 16), mx_pack4<G::F>(av + 4, inv));
         if (lane < 16) a.aqs[pos * (I / 32) + c0 / 32] = static_cast<uint8_t>(code);
       }
     }
@@ -597,18 +674,19 @@ struct MxFwdDownT {
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
-    LoadK8<G::BM, G::LDK> la;
-    LoadK8<G::BN, G::LDK> lb;
+    LoadA8<G> la;
+    LoadB8<G> lb;
     MOE_DEV void init(const Args& a, const Tile& t) {
       const int I = a.I, mc = t.m.mcount, row0 = t.m.row0;
       const uint8_t* aq = a.aq;
       const uint8_t* aqs = a.aqs;
-      la.init([&](int m) { return aq + (size_t)(row0 + min(m, mc - 1)) * I; },
+      const size_t pb = (size_t)I * G::F / 8;  // bytes of codes per row
+      la.init([&](int m) { return aq + (size_t)(row0 + min(m, mc - 1)) * pb; },
               [&](int m) { return aqs + (size_t)(row0 + min(m, mc - 1)) * (I / 32); }, I);
       const size_t wrow0 = (size_t)t.m.e * a.d + t.n0;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
-      lb.init([&](int n) { return w8 + (wrow0 + n) * I; },
+      lb.init([&](int n) { return w8 + (wrow0 + n) * pb; },
               [&](int n) { return ws + (wrow0 + n) * (I / 32); }, I);
     }
     MOE_DEV void load(int kt) {  // weights first: they are the HBM stream
@@ -643,9 +721,10 @@ using MxFwdDownBig = MxFwdDownT<GeoMxBig>;
 // (W2 stored transposed, [E, I, d]). The epilogue is the BF16 one (router-weight-gradient
 // partials, SwiGLU backward, dH in bf16) plus dH quantised along 2I: the wave's 32 consecutive
 // I columns make one 32-block of the gate half and one of the up half.
-struct MxBwdDownDgrad {
+template <class G_>
+struct MxBwdDownDgradT {
   static constexpr const char* kName = "bwd_down_dgrad";
-  using G = GeoMx<128, 128, 1, 4>;
+  using G = G_;
   struct Args {
     const uint8_t* dyq;      // [T, d]
     const uint8_t* dys;      // [T, d/32]
@@ -680,19 +759,20 @@ struct MxBwdDownDgrad {
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
-    LoadK8<G::BM, G::LDK> la;
-    LoadK8<G::BN, G::LDK> lb;
+    LoadA8<G> la;
+    LoadB8<G> lb;
     MOE_DEV void init(const Args& a, const Tile& t) {
       const int d = a.d, k = a.k, mc = t.m.mcount, row0 = t.m.row0;
       const uint8_t* dyq = a.dyq;
       const uint8_t* dys = a.dys;
       const int32_t* rs = a.row_src;
-      la.init([&](int m) { return dyq + (size_t)(rs[row0 + min(m, mc - 1)] / k) * d; },
+      const size_t pb = (size_t)d * G::F / 8;  // bytes of codes per row
+      la.init([&](int m) { return dyq + (size_t)(rs[row0 + min(m, mc - 1)] / k) * pb; },
               [&](int m) { return dys + (size_t)(rs[row0 + min(m, mc - 1)] / k) * (d / 32); }, d);
       const size_t wrow0 = (size_t)t.m.e * a.I + t.n0;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
-      lb.init([&](int n) { return w8 + (wrow0 + n) * d; },
+      lb.init([&](int n) { return w8 + (wrow0 + n) * pb; },
               [&](int n) { return ws + (wrow0 + n) * (d / 32); }, d);
     }
     MOE_DEV void load(int kt) {  // weights first: they are the HBM stream
@@ -754,15 +834,15 @@ struct MxBwdDownDgrad {
           *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + I + i) = ou;
         }
       }
-      const uint32_t cg = mx_block_code(dgv), cu = mx_block_code(duv);
+      const uint32_t cg = mx_block_code<G::F>(dgv), cu = mx_block_code<G::F>(duv);
       const float ig = mx_inv_scale(cg), iu = mx_inv_scale(cu);
       if (live) {
-        uint8_t* q = a.dhq + pos * 2 * I;
+        uint8_t* q = a.dhq + pos * (2 * I * G::F / 8);
         const int o = 4 * (lane / 16);
-        *reinterpret_cast<uint32_t*>(q + c0 + o) = mx_pack4(dgv, ig);
-        *reinterpret_cast<uint32_t*>(q + c0 + 16 + o) = mx_pack4(dgv + 4, ig);
-        *reinterpret_cast<uint32_t*>(q + I + c0 + o) = mx_pack4(duv, iu);
-        *reinterpret_cast<uint32_t*>(q + I + c0 + 16 + o) = mx_pack4(duv + 4, iu);
+        mx_put4<G::F>(q, c0 + o, mx_pack4<G::F>(dgv, ig));
+        mx_put4<G::F>(q, c0 + 16 + o, mx_pack4<G::F>(dgv + 4, ig));
+        mx_put4<G::F>(q, I + c0 + o, mx_pack4<G::F>(duv, iu));
+        mx_put4<G::F>(q, I + c0 + 16 + o, mx_pack4<G::F>(duv + 4, iu));
         if (lane < 16) {
           a.dhs[pos * (2 * I / 32) + c0 / 32] = static_cast<uint8_t>(cg);
           a.dhs[pos * (2 * I / 32) + (I + c0) / 32] = static_cast<uint8_t>(cu);
@@ -783,6 +863,8 @@ struct MxBwdDownDgrad {
     }
   }
 };
+
+using MxBwdDownDgrad = MxBwdDownDgradT<GeoMx<128, 128, 1, 4>>;
 
 // Problem 4 (MXFP8): gate/up dgrad, dXp[pos] = dH[pos] . W1[e] with dH and W1 quantised along
 // 2I (W1 stored transposed, [E, d, 2I]).
@@ -818,18 +900,19 @@ struct MxBwdGateDgradT {
   static MOE_DEV bool m_active(const Tile& t, int m) { return m < t.m.mcount; }
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
-    LoadK8<G::BM, G::LDK> la;
-    LoadK8<G::BN, G::LDK> lb;
+    LoadA8<G> la;
+    LoadB8<G> lb;
     MOE_DEV void init(const Args& a, const Tile& t) {
       const int twoI = 2 * a.I, mc = t.m.mcount, row0 = t.m.row0;
       const uint8_t* dhq = a.dhq;
       const uint8_t* dhs = a.dhs;
-      la.init([&](int m) { return dhq + (size_t)(row0 + min(m, mc - 1)) * twoI; },
+      const size_t pb = (size_t)twoI * G::F / 8;  // bytes of codes per row
+      la.init([&](int m) { return dhq + (size_t)(row0 + min(m, mc - 1)) * pb; },
               [&](int m) { return dhs + (size_t)(row0 + min(m, mc - 1)) * (twoI / 32); }, twoI);
       const size_t wrow0 = (size_t)t.m.e * a.d + t.n0;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
-      lb.init([&](int n) { return w8 + (wrow0 + n) * twoI; },
+      lb.init([&](int n) { return w8 + (wrow0 + n) * pb; },
               [&](int n) { return ws + (wrow0 + n) * (twoI / 32); }, twoI);
     }
     MOE_DEV void load(int kt) {  // weights first: they are the HBM stream
@@ -904,8 +987,8 @@ struct MxWgrad {
   static MOE_DEV bool m_active(const Tile&, int) { return true; }
   static MOE_DEV int brow(int wn, int nb) { return wn * G::WN + nb * 16; }
   struct Loader {
-    LoadK8<G::BM, G::LDK> la;
-    LoadK8<G::BN, G::LDK> lb;
+    LoadA8<G> la;
+    LoadB8<G> lb;
     MOE_DEV void init(const Args& a, const Tile& t) {
       const size_t P = a.P, p0 = a.poff[t.e];
       const uint8_t* lq = a.lq;
@@ -1597,14 +1680,14 @@ struct DmxDownDgrad {
           *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + i) = og;
           *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + I + i) = ou;
         }
-        const uint32_t cg = mx_block_code(dgv), cu = mx_block_code(duv);
+        const uint32_t cg = mx_block_code<8>(dgv), cu = mx_block_code<8>(duv);
         const float ig = mx_inv_scale(cg), iu = mx_inv_scale(cu);
         uint8_t* qp = a.dhq + pos * 2 * I;
         const int o = 4 * (lane / 16);
-        *reinterpret_cast<uint32_t*>(qp + c0 + o) = mx_pack4(dgv, ig);
-        *reinterpret_cast<uint32_t*>(qp + c0 + 16 + o) = mx_pack4(dgv + 4, ig);
-        *reinterpret_cast<uint32_t*>(qp + I + c0 + o) = mx_pack4(duv, iu);
-        *reinterpret_cast<uint32_t*>(qp + I + c0 + 16 + o) = mx_pack4(duv + 4, iu);
+        mx_put4<8>(qp, c0 + o, mx_pack4<8>(dgv, ig));
+        mx_put4<8>(qp, c0 + 16 + o, mx_pack4<8>(dgv + 4, ig));
+        mx_put4<8>(qp, I + c0 + o, mx_pack4<8>(duv, iu));
+        mx_put4<8>(qp, I + c0 + 16 + o, mx_pack4<8>(duv + 4, iu));
         if (lane < 16) {
           a.dhs[pos * (2 * I / 32) + c0 / 32] = static_cast<uint8_t>(cg);
           a.dhs[pos * (2 * I / 32) + (I + c0) / 32] = static_cast<uint8_t>(cu);
@@ -1748,10 +1831,23 @@ hipError_t launch_bwd_gate_dgrad(const GemmBwdGateDgradArgs& x, bool persistent,
   return launch<BwdGateDgrad>(a, sched_max_rem(x.Tk, x.E) * (x.d / 128), persistent, s);
 }
 
+// MXFP4: every 128-row block on the 128-row kernels.
+using GeoMx4 = GeoMx<128, 128, 1, 4, 4>;
+using MxFwdGateUp4 = MxFwdGateUpT<GeoMx<128, 128, 2, 2, 4>>;
+using MxFwdDown4 = MxFwdDownT<GeoMx4>;
+using MxBwdDownDgrad4 = MxBwdDownDgradT<GeoMx4>;
+using MxBwdGateDgrad4 = MxBwdGateDgradT<GeoMx4>;
+
 // The MXFP8 forward GEMMs and gate dgrad run the 256-row blocks with dmx_kernel, then the
 // remainders on the 128-row kernels.
 hipError_t launch_fwd_gateup_mx(const GemmMxGateUpArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
+  if (x.fbits == 4) {
+    MxFwdGateUp4::Args a{x.xp8, x.xps, x.w8, x.ws, x.H, x.A, x.aq, x.aqs, x.offsets, st.full,
+                         x.d, x.I};
+    return launch<MxFwdGateUp4>(a, sched_max_mtiles(x.Tk, x.E) * (x.I / MxFwdGateUp4::kA),
+                                persistent, s);
+  }
   MxFwdGateUpBig::Args ab{x.xp8, x.xps, x.w8, x.ws, x.H,     x.A,
                           x.aq,  x.aqs, x.offsets, st.big, x.d, x.I};
   hipError_t e = launch_dmx<DmxGateUp>(ab, sched_max_big(x.Tk) * (x.I / MxFwdGateUpBig::kA),
@@ -1764,6 +1860,10 @@ hipError_t launch_fwd_gateup_mx(const GemmMxGateUpArgs& x, bool persistent, hipS
 
 hipError_t launch_fwd_down_mx(const GemmMxDownArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
+  if (x.fbits == 4) {
+    MxFwdDown4::Args a{x.aq, x.aqs, x.w8, x.ws, x.O, x.offsets, st.full, x.d, x.I};
+    return launch<MxFwdDown4>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
+  }
   MxFwdDownBig::Args ab{x.aq, x.aqs, x.w8, x.ws, x.O, x.offsets, st.big, x.d, x.I};
   hipError_t e = launch_dmx<DmxDown>(ab, sched_max_big(x.Tk) * (x.d / 256), true, s);
   if (e != hipSuccess) return e;
@@ -1775,6 +1875,12 @@ hipError_t launch_fwd_down_mx(const GemmMxDownArgs& x, bool persistent, hipStrea
 // the remainders; otherwise every 128-row block on the 128-row kernel.
 hipError_t launch_bwd_down_dgrad_mx(const GemmMxDownDgradArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
+  if (x.fbits == 4) {
+    MxBwdDownDgrad4::Args a{x.dyq, x.dys, x.row_src, x.topk_w, x.w8,  x.ws,   x.H,
+                            x.A,   x.dH,  x.dwpart,  x.dhq,    x.dhs, x.offsets, st.full,
+                            x.d,   x.I,   x.k};
+    return launch<MxBwdDownDgrad4>(a, sched_max_mtiles(x.Tk, x.E) * (x.I / 128), persistent, s);
+  }
   const bool big = x.I % 256 == 0;
   const int max_big = big ? sched_max_big(x.Tk) * (x.I / 256) : 0;
   if (max_big > 0) {
@@ -1792,6 +1898,10 @@ hipError_t launch_bwd_down_dgrad_mx(const GemmMxDownDgradArgs& x, bool persisten
 
 hipError_t launch_bwd_gate_dgrad_mx(const GemmMxGateDgradArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
+  if (x.fbits == 4) {
+    MxBwdGateDgrad4::Args a{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, st.full, x.d, x.I};
+    return launch<MxBwdGateDgrad4>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
+  }
   MxBwdGateDgradBig::Args ab{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, st.big, x.d, x.I};
   hipError_t e = launch_dmx<DmxGateDgrad>(ab, sched_max_big(x.Tk) * (x.d / 256), true, s);
   if (e != hipSuccess) return e;

@@ -40,12 +40,12 @@ hipError_t launch_perm_hist(const int32_t* idx, int Tk, int E, int32_t* blk_cnt,
                             int32_t* blk_flag, hipStream_t s);
 hipError_t launch_perm_scan(int32_t* blk_cnt, int nb, int E, const int32_t* blk_flag,
                             int32_t* counts, int32_t* offsets, int32_t* status, hipStream_t s);
-// With xp8 non-null the slot receives the MXFP8 image of each token (xp8 codes, xps scales)
-// instead of the bf16 copy xp.
+// With xp8 non-null the slot receives the MX image of each token (xp8 codes of fbits bits, xps
+// scales) instead of the bf16 copy xp.
 hipError_t launch_perm_place(const int32_t* idx, const int32_t* rank, const int32_t* blk_base,
                              int Tk, int E, int k, int32_t* row_src, int32_t* tk_row,
                              const uint16_t* x, uint16_t* xp, uint8_t* xp8, uint8_t* xps, int d,
-                             hipStream_t s);
+                             int fbits, hipStream_t s);
 
 // gemm.hip
 int sched_max_mtiles(int Tk, int E);
@@ -93,7 +93,9 @@ struct GemmBwdGateDgradArgs {
   const int2* sched;
   int d, I, Tk, E;
 };
-// MXFP8 mode: E4M3 codes (uint8) with one E8M0 scale (uint8) per 32 along each GEMM's K.
+// MX modes: codes with one E8M0 scale (uint8) per 32 along each GEMM's K. fbits 8: E4M3 codes,
+// one a byte (MXFP8); fbits 4: E2M1 codes, two a byte, element 2i in the low nibble (MXFP4), so
+// a row of n codes takes n * fbits / 8 bytes. The shapes below count codes.
 struct GemmMxGateUpArgs {
   const uint8_t* xp8;  // [T*k, d], scales xps [T*k, d/32]
   const uint8_t* xps;
@@ -105,7 +107,7 @@ struct GemmMxGateUpArgs {
   uint8_t* aqs;
   const int32_t* offsets;
   const int2* sched;
-  int d, I, Tk, E;
+  int d, I, Tk, E, fbits;
 };
 struct GemmMxDownArgs {
   const uint8_t* aq;
@@ -115,7 +117,7 @@ struct GemmMxDownArgs {
   uint16_t* O;
   const int32_t* offsets;
   const int2* sched;
-  int d, I, Tk, E;
+  int d, I, Tk, E, fbits;
 };
 struct GemmMxDownDgradArgs {
   const uint8_t* dyq;  // [T, d], scales [T, d/32]
@@ -132,7 +134,7 @@ struct GemmMxDownDgradArgs {
   uint8_t* dhs;
   const int32_t* offsets;
   const int2* sched;
-  int d, I, k, Tk, E;
+  int d, I, k, Tk, E, fbits;
 };
 struct GemmMxGateDgradArgs {
   const uint8_t* dhq;
@@ -142,7 +144,7 @@ struct GemmMxGateDgradArgs {
   uint16_t* dXp;
   const int32_t* offsets;
   const int2* sched;
-  int d, I, Tk, E;
+  int d, I, Tk, E, fbits;
 };
 hipError_t launch_fwd_gateup_mx(const GemmMxGateUpArgs& a, bool persistent, hipStream_t s);
 hipError_t launch_fwd_down_mx(const GemmMxDownArgs& a, bool persistent, hipStream_t s);
@@ -206,12 +208,16 @@ size_t wgrad_table_entries(int Tk, int E, int Mdim, int Ndim);
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
 
 // mx.hip
+// fbits: 8 for MXFP8 (E4M3 codes, one a byte), 4 for MXFP4 (E2M1 codes, two a byte)
 hipError_t launch_quant_rows(const uint16_t* src, long long rows, int cols, uint8_t* dst,
-                             uint8_t* sc, const char* name, hipStream_t s);
+                             uint8_t* sc, int fbits, const char* name, hipStream_t s);
 // Both MXFP8 copies of src [B][R][C]: along C into (dq, dqs), along R transposed into (tq, tqs).
 hipError_t launch_quant_weight(const uint16_t* src, int B, int R, int C, uint8_t* dq,
-                               uint8_t* dqs, uint8_t* tq, uint8_t* tqs, const char* name,
-                               hipStream_t s);
+                               uint8_t* dqs, uint8_t* tq, uint8_t* tqs, int fbits,
+                               const char* name, hipStream_t s);
+// The exact bf16 image of MXFP4 rows: codes q [rows, cols / 2], scales qs [rows, cols / 32].
+hipError_t launch_expand_fp4(const uint8_t* q, const uint8_t* qs, long long rows, int cols,
+                             uint16_t* out, const char* name, hipStream_t s);
 // MXFP8 weight gradients: expert segments padded to kSegK positions (segment offsets poff
 // [E + 1], the padded total in poff[E] <= seg_capacity), and an operand S [T*k, C] quantised
 // along each segment's positions into q [C][P] codes and qs [C][P / 32] scales.

@@ -1,18 +1,47 @@
-// MXFP8 (OCP Microscaling) quantisation kernels for the layer's MXFP8 mode: E4M3 elements with
-// one E8M0 scale per 32 consecutive elements along the reduction axis of the GEMM that reads them.
+// MX (OCP Microscaling) quantisation kernels for the layer's MXFP8 and MXFP4 modes: E4M3 (F = 8)
+// or E2M1 (F = 4, two codes a byte) elements with one E8M0 scale per 32 consecutive elements
+// along the reduction axis of the GEMM that reads them.
 //
 // The MarkTechPost page on Mixture-of-Kittens (MoK), closing paragraph of "Three design
-// decisions that matter", names BF16 and MXFP8 precision modes. Scale code of a block:
-// floor(log2 amax) - 8 + 127, clamped to 0..254 (0 for an all-zero block). Elements:
-// round to nearest even of v / 2^(code - 127), saturated to +-448.
+// decisions that matter", names BF16 and MXFP8 precision modes, and its section "MoE layer as the
+// bottleneck" names 4-bit (NVFP4) training kernels. Scale code of a block: floor(log2 amax) -
+// emax + 127 with emax 8 (E4M3) or 2 (E2M1), clamped to 0..254 (0 for an all-zero block).
+// Elements: round to nearest even of v / 2^(code - 127), saturated to +-448 or +-6.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
+// The scale code of a block with max magnitude amax, and the codes of eight scaled values: 8
+// bytes (E4M3) or 4 bytes (E2M1) in element order.
+template <int F>
+MOE_DEV uint32_t mxf_scale_code(float amax) {
+  return F == 8 ? mx_scale_code(amax) : mx4_scale_code(amax);
+}
+template <int F>
+MOE_DEV uint2 mxf_encode8(const float (&f)[8], float inv) {
+  if constexpr (F == 8) {
+    return make_uint2(e4m3x2(f[0] * inv, f[1] * inv) | (e4m3x2(f[2] * inv, f[3] * inv) << 16),
+                      e4m3x2(f[4] * inv, f[5] * inv) | (e4m3x2(f[6] * inv, f[7] * inv) << 16));
+  } else {
+    return make_uint2(e2m1x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv) |
+                          (e2m1x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv) << 16),
+                      0u);
+  }
+}
+// Stores the codes of eight elements (element offset `e`, a multiple of 8) into a code array.
+template <int F>
+MOE_DEV void mxf_store8(uint8_t* base, size_t e, uint2 codes) {
+  if constexpr (F == 8)
+    *reinterpret_cast<uint2*>(base + e) = codes;
+  else
+    *reinterpret_cast<uint32_t*>(base + e / 2) = codes.x;
+}
+
 // Rows of bf16 quantised along the row: thread v handles elements [8 v, 8 v + 8) of the
 // flattened array; four consecutive threads (lanes 4q..4q+3 of a wave) make one 32-block.
 // Requires the row length to be a multiple of 32.
+template <int F>
 __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restrict__ src,
                                                          uint8_t* __restrict__ dst,
                                                          uint8_t* __restrict__ sc,
@@ -32,34 +61,35 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restr
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
   amax = fmaxf(amax, __shfl_xor(amax, 1));
   amax = fmaxf(amax, __shfl_xor(amax, 2));
-  const uint32_t code = mx_scale_code(amax);
-  const float inv = mx_inv_scale(code);
-  uint2 o;
-  o.x = e4m3x2(f[0] * inv, f[1] * inv) | (e4m3x2(f[2] * inv, f[3] * inv) << 16);
-  o.y = e4m3x2(f[4] * inv, f[5] * inv) | (e4m3x2(f[6] * inv, f[7] * inv) << 16);
+  const uint32_t code = mxf_scale_code<F>(amax);
+  const uint2 o = mxf_encode8<F>(f, mx_inv_scale(code));
   if (live) {
-    reinterpret_cast<uint2*>(dst)[v] = o;
+    mxf_store8<F>(dst, (size_t)v * 8, o);
     if ((v & 3) == 0) sc[v >> 2] = static_cast<uint8_t>(code);
   }
 }
 
-// Both MXFP8 copies of a weight src [B][R][C] bf16 in one pass over it:
+// Both MX copies of a weight src [B][R][C] bf16 in one pass over it:
 //  * along C (the forward GEMM's reduction axis): dq [B][R][C] codes, dqs [B][R][C/32] scales;
 //  * along R, transposed (the dgrad's reduction axis): tq [B][C][R] codes, tqs [B][C][R/32].
 // One workgroup of 256 threads per 128 x 128 tile (R and C are multiples of 128). The tile is
 // read once: each row's 32-blocks are quantised from registers as they arrive, and the tile goes
 // to LDS, where wave w quantises rows [32 w, 32 w + 32) of every column. The column codes are
 // then staged in the same LDS (about 33 KB per workgroup in all, so four fit on a CU) and each
-// column's 128 codes leave as 128 contiguous bytes. Scale codes leave four bytes at a time.
+// column's 128 codes leave as 128 (E2M1: 64) contiguous bytes. Scale codes leave four bytes at
+// a time.
 constexpr int kQT = 128;
+template <int F>
 __global__ void __launch_bounds__(256) quant_weight_kernel(const uint16_t* __restrict__ src,
                                                            uint8_t* __restrict__ dq,
                                                            uint8_t* __restrict__ dqs,
                                                            uint8_t* __restrict__ tq,
                                                            uint8_t* __restrict__ tqs, int R,
                                                            int C) {
-  constexpr int TP = kQT / 2 + 1;  // tile pitch in words (bf16 pairs)
-  constexpr int OP = kQT / 4 + 1;  // pitch of the staged column codes in words
+  constexpr int TP = kQT / 2 + 1;        // tile pitch in words (bf16 pairs)
+  constexpr int WPC = kQT * F / 32;      // code words of one column's 128 elements
+  constexpr int WPB = 32 * F / 32;       // code words of one column's 32-row block
+  constexpr int OP = WPC + 1;            // pitch of the staged column codes in words
   static_assert(kQT * OP <= kQT * TP, "column codes fit in the tile's LDS");
   __shared__ uint32_t tile[kQT * TP];
   __shared__ uint32_t scT[kQT];  // the column's four scale codes, one per byte
@@ -97,13 +127,10 @@ __global__ void __launch_bounds__(256) quant_weight_kernel(const uint16_t* __res
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
     amax = fmaxf(amax, __shfl_xor(amax, 1));
     amax = fmaxf(amax, __shfl_xor(amax, 2));
-    const uint32_t code = mx_scale_code(amax);
-    const float inv = mx_inv_scale(code);
-    uint2 o;
-    o.x = e4m3x2(f[0] * inv, f[1] * inv) | (e4m3x2(f[2] * inv, f[3] * inv) << 16);
-    o.y = e4m3x2(f[4] * inv, f[5] * inv) | (e4m3x2(f[6] * inv, f[7] * inv) << 16);
+    const uint32_t code = mxf_scale_code<F>(amax);
+    const uint2 o = mxf_encode8<F>(f, mx_inv_scale(code));
     const size_t row = (size_t)b * R + r0 + r;
-    *reinterpret_cast<uint2*>(dq + row * C + c0 + cv * 8) = o;
+    mxf_store8<F>(dq, row * C + c0 + cv * 8, o);
     // the row's four block scales (lanes cv = 0, 4, 8, 12 of its group) as one word
     const int g0 = (t % kWave) & ~15;
     const uint32_t w4 = __shfl(code, g0) | (__shfl(code, g0 + 4) << 8) |
@@ -113,7 +140,7 @@ __global__ void __launch_bounds__(256) quant_weight_kernel(const uint16_t* __res
   __syncthreads();
   // Phase 2: wave w takes rows [32 w, 32 w + 32); lane l the column pair (2 l, 2 l + 1).
   const int w = t / kWave, l = t % kWave;
-  uint32_t clo[8], chi[8];
+  uint32_t clo[WPB], chi[WPB];
   {
     float lo[32], hi[32];
     float alo = 0.f, ahi = 0.f;
@@ -125,14 +152,24 @@ __global__ void __launch_bounds__(256) quant_weight_kernel(const uint16_t* __res
       alo = fmaxf(alo, fabsf(lo[i]));
       ahi = fmaxf(ahi, fabsf(hi[i]));
     }
-    const uint32_t slo = mx_scale_code(alo), shi = mx_scale_code(ahi);
+    const uint32_t slo = mxf_scale_code<F>(alo), shi = mxf_scale_code<F>(ahi);
     const float ilo = mx_inv_scale(slo), ihi = mx_inv_scale(shi);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      clo[q] = e4m3x2(lo[4 * q] * ilo, lo[4 * q + 1] * ilo) |
-               (e4m3x2(lo[4 * q + 2] * ilo, lo[4 * q + 3] * ilo) << 16);
-      chi[q] = e4m3x2(hi[4 * q] * ihi, hi[4 * q + 1] * ihi) |
-               (e4m3x2(hi[4 * q + 2] * ihi, hi[4 * q + 3] * ihi) << 16);
+    for (int q = 0; q < 4; ++q) {  // 8 rows each
+      const float vl[8] = {lo[8 * q], lo[8 * q + 1], lo[8 * q + 2], lo[8 * q + 3],
+                           lo[8 * q + 4], lo[8 * q + 5], lo[8 * q + 6], lo[8 * q + 7]};
+      const float vh[8] = {hi[8 * q], hi[8 * q + 1], hi[8 * q + 2], hi[8 * q + 3],
+                           hi[8 * q + 4], hi[8 * q + 5], hi[8 * q + 6], hi[8 * q + 7]};
+      const uint2 cl = mxf_encode8<F>(vl, ilo), ch = mxf_encode8<F>(vh, ihi);
+      if constexpr (F == 8) {
+        clo[2 * q] = cl.x;
+        clo[2 * q + 1] = cl.y;
+        chi[2 * q] = ch.x;
+        chi[2 * q + 1] = ch.y;
+      } else {
+        clo[q] = cl.x;
+        chi[q] = ch.x;
+      }
     }
     reinterpret_cast<uint8_t*>(scT)[(2 * l) * 4 + w] = static_cast<uint8_t>(slo);
     reinterpret_cast<uint8_t*>(scT)[(2 * l + 1) * 4 + w] = static_cast<uint8_t>(shi);
@@ -140,18 +177,20 @@ __global__ void __launch_bounds__(256) quant_weight_kernel(const uint16_t* __res
   __syncthreads();  // every wave has read the tile: its LDS now holds the column codes
   uint32_t* outT = tile;  // [kQT][OP]
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    outT[(2 * l) * OP + w * 8 + q] = clo[q];
-    outT[(2 * l + 1) * OP + w * 8 + q] = chi[q];
+  for (int q = 0; q < WPB; ++q) {
+    outT[(2 * l) * OP + w * WPB + q] = clo[q];
+    outT[(2 * l + 1) * OP + w * WPB + q] = chi[q];
   }
   __syncthreads();
-  // Phase 3: each column's 128 codes as eight 16-byte stores, and its four scales as one word.
+  // Phase 3: each column's 128 codes as 16-byte stores (eight, or four for E2M1), and its four
+  // scales as one word.
+  constexpr int PPC = WPC / 4;  // 16-byte pieces per column
 #pragma unroll
-  for (int j = 0; j < kQT * 8 / 256; ++j) {
-    const int idx = t + 256 * j, c = idx / 8, part = idx % 8;
+  for (int j = 0; j < kQT * PPC / 256; ++j) {
+    const int idx = t + 256 * j, c = idx / PPC, part = idx % PPC;
     const uint4 v = make_uint4(outT[c * OP + part * 4], outT[c * OP + part * 4 + 1],
                                outT[c * OP + part * 4 + 2], outT[c * OP + part * 4 + 3]);
-    *reinterpret_cast<uint4*>(tq + ((size_t)b * C + c0 + c) * R + r0 + part * 16) = v;
+    *reinterpret_cast<uint4*>(tq + (((size_t)b * C + c0 + c) * R + r0) * F / 8 + part * 16) = v;
   }
   if (t < kQT)
     *reinterpret_cast<uint32_t*>(tqs + ((size_t)b * C + c0 + t) * (R / 32) + r0 / 32) = scT[t];
@@ -348,26 +387,63 @@ hipError_t launch_quant_seg(const SegOperand& x, const int32_t* offsets, const i
 }
 
 hipError_t launch_quant_rows(const uint16_t* src, long long rows, int cols, uint8_t* dst,
-                             uint8_t* sc, const char* name, hipStream_t s) {
+                             uint8_t* sc, int fbits, const char* name, hipStream_t s) {
   const long long nvec = rows * cols / 8;
   if (nvec == 0) return hipSuccess;
   {
     TraceScope trace(name, s);
-    hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0, s,
-                       src, dst, sc, nvec);
+    const dim3 grid((unsigned)((nvec + 255) / 256));
+    if (fbits == 4)
+      hipLaunchKernelGGL(quant_rows_kernel<4>, grid, dim3(256), 0, s, src, dst, sc, nvec);
+    else
+      hipLaunchKernelGGL(quant_rows_kernel<8>, grid, dim3(256), 0, s, src, dst, sc, nvec);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_quant_weight(const uint16_t* src, int B, int R, int C, uint8_t* dq,
-                               uint8_t* dqs, uint8_t* tq, uint8_t* tqs, const char* name,
-                               hipStream_t s) {
+                               uint8_t* dqs, uint8_t* tq, uint8_t* tqs, int fbits,
+                               const char* name, hipStream_t s) {
   if (R % kQT != 0 || C % kQT != 0) return hipErrorInvalidValue;
   if (B == 0) return hipSuccess;
   {
     TraceScope trace(name, s);
-    hipLaunchKernelGGL(quant_weight_kernel, dim3(C / kQT, R / kQT, B), dim3(256), 0, s, src, dq,
-                       dqs, tq, tqs, R, C);
+    const dim3 grid(C / kQT, R / kQT, B);
+    if (fbits == 4)
+      hipLaunchKernelGGL(quant_weight_kernel<4>, grid, dim3(256), 0, s, src, dq, dqs, tq, tqs, R,
+                         C);
+    else
+      hipLaunchKernelGGL(quant_weight_kernel<8>, grid, dim3(256), 0, s, src, dq, dqs, tq, tqs, R,
+                         C);
+  }
+  return hipGetLastError();
+}
+
+// The exact bf16 image of MXFP4 rows (E2M1 codes times their block's scale): thread v expands
+// elements [8 v, 8 v + 8) of the flattened array, 4 bytes of codes, into one 16-byte store.
+__global__ void __launch_bounds__(256) expand_fp4_kernel(const uint8_t* __restrict__ q,
+                                                         const uint8_t* __restrict__ qs,
+                                                         uint16_t* __restrict__ out,
+                                                         long long nvec) {
+  const long long v = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (v >= nvec) return;
+  const uint32_t c = reinterpret_cast<const uint32_t*>(q)[v];
+  const float s = mx_scale(qs[v / 4]);
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = e2m1_value((c >> (4 * i)) & 0xfu) * s;
+  reinterpret_cast<uint4*>(out)[v] = make_uint4(pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3]),
+                                                pack_bf2(f[4], f[5]), pack_bf2(f[6], f[7]));
+}
+
+hipError_t launch_expand_fp4(const uint8_t* q, const uint8_t* qs, long long rows, int cols,
+                             uint16_t* out, const char* name, hipStream_t s) {
+  const long long nvec = rows * cols / 8;
+  if (nvec == 0) return hipSuccess;
+  {
+    TraceScope trace(name, s);
+    hipLaunchKernelGGL(expand_fp4_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0, s,
+                       q, qs, out, nvec);
   }
   return hipGetLastError();
 }

@@ -43,12 +43,12 @@ MOE_DEV void perm_hist_block(int b, const int32_t* __restrict__ idx, int Tk, int
 
 // Block b owns tokens [tpb b, tpb b + tpb) and their rows r = t*k + j (tpb*k <= 256). It
 // places every row, then copies each token slice ONCE from x and stores it to the token's k
-// positions: Xp[pos(t*k+j)] = x[t]. With MX the stored image is the token's MXFP8 form: E4M3
-// codes xp8 [T*k, d] and one scale per 32 along d in xps [T*k, d/32]. Four consecutive lanes
-// own one 32-block (d is a multiple of 32, so blocks never straddle rows), and every lane runs
-// the shuffles.
+// positions: Xp[pos(t*k+j)] = x[t]. With MX (Q = 8 or 4) the stored image is the token's MX
+// form: codes xp8 [T*k, d] (E4M3 bytes, Q = 8, or E2M1 nibbles two a byte, Q = 4) and one scale
+// per 32 along d in xps [T*k, d/32]. Four consecutive lanes own one 32-block (d is a multiple
+// of 32, so blocks never straddle rows), and every lane runs the shuffles.
 // Run by 256 threads; sh_pos [256] is the block's LDS.
-template <bool MX>
+template <int Q>
 MOE_DEV void perm_place_block(int blk, const int32_t* __restrict__ idx,
                               const int32_t* __restrict__ rank,
                               const int32_t* __restrict__ blk_base, int T, int E, int k,
@@ -76,7 +76,7 @@ MOE_DEV void perm_place_block(int blk, const int32_t* __restrict__ idx,
   __syncthreads();
   const int vpr = d / 8;
   const int n = tpb * vpr;
-  if constexpr (!MX) {
+  if constexpr (Q == 0) {
     // U token slices loaded together, then each stored to its k positions
     constexpr int U = 4;
     for (int i0 = 0; i0 < n; i0 += 256 * U) {
@@ -121,16 +121,24 @@ MOE_DEV void perm_place_block(int blk, const int32_t* __restrict__ idx,
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
     amax = fmaxf(amax, __shfl_xor(amax, 1));
     amax = fmaxf(amax, __shfl_xor(amax, 2));
-    const uint32_t code = mx_scale_code(amax);
+    const uint32_t code = Q == 8 ? mx_scale_code(amax) : mx4_scale_code(amax);
     const float inv = mx_inv_scale(code);
     uint2 o;
-    o.x = e4m3x2(f[0] * inv, f[1] * inv) | (e4m3x2(f[2] * inv, f[3] * inv) << 16);
-    o.y = e4m3x2(f[4] * inv, f[5] * inv) | (e4m3x2(f[6] * inv, f[7] * inv) << 16);
+    if constexpr (Q == 8) {
+      o.x = e4m3x2(f[0] * inv, f[1] * inv) | (e4m3x2(f[2] * inv, f[3] * inv) << 16);
+      o.y = e4m3x2(f[4] * inv, f[5] * inv) | (e4m3x2(f[6] * inv, f[7] * inv) << 16);
+    } else {
+      o.x = e2m1x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv) |
+            (e2m1x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv) << 16);
+    }
     if (!live) continue;
     for (int j = 0; j < k; ++j) {
       const int pos = sh_pos[tt * k + j];
       if (pos < 0) continue;
-      *reinterpret_cast<uint2*>(xp8 + (size_t)pos * d + v * 8) = o;
+      if constexpr (Q == 8)
+        *reinterpret_cast<uint2*>(xp8 + (size_t)pos * d + v * 8) = o;
+      else
+        *reinterpret_cast<uint32_t*>(xp8 + (size_t)pos * (d / 2) + v * 4) = o.x;
       if ((v & 3) == 0) xps[(size_t)pos * (d / 32) + v / 4] = static_cast<uint8_t>(code);
     }
   }

@@ -100,14 +100,14 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ b
   if (e == 0) status[0] = f ? 1 : 0;
 }
 
-template <bool MX>
+template <int Q>
 __global__ void __launch_bounds__(256) perm_place_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ rank,
     const int32_t* __restrict__ blk_base, int T, int E, int k, int32_t* __restrict__ row_src,
     int32_t* __restrict__ tk_row, const uint16_t* __restrict__ x, uint16_t* __restrict__ xp,
     uint8_t* __restrict__ xp8, uint8_t* __restrict__ xps, int d, int tpb) {
   __shared__ int sh_pos[256];
-  perm_place_block<MX>(blockIdx.x, idx, rank, blk_base, T, E, k, row_src, tk_row, x, xp, xp8,
+  perm_place_block<Q>(blockIdx.x, idx, rank, blk_base, T, E, k, row_src, tk_row, x, xp, xp8,
                        xps, d, tpb, sh_pos);
 }
 
@@ -135,7 +135,7 @@ hipError_t launch_perm_scan(int32_t* blk_cnt, int nb, int E, const int32_t* blk_
 hipError_t launch_perm_place(const int32_t* idx, const int32_t* rank, const int32_t* blk_base,
                              int Tk, int E, int k, int32_t* row_src, int32_t* tk_row,
                              const uint16_t* x, uint16_t* xp, uint8_t* xp8, uint8_t* xps, int d,
-                             hipStream_t s) {
+                             int fbits, hipStream_t s) {
   const int T = Tk / k;
   // about 1024 slices of 16 bytes per block, and at most 256 rows
   int tpb = 1024 / (d / 8);
@@ -144,11 +144,14 @@ hipError_t launch_perm_place(const int32_t* idx, const int32_t* rank, const int3
   const int grid = (T + tpb - 1) / tpb;
   {
     TraceScope trace("perm_place", s);
-    if (xp8)
-      hipLaunchKernelGGL(perm_place_kernel<true>, dim3(grid), dim3(256), 0, s, idx, rank, blk_base,
+    if (xp8 && fbits == 4)
+      hipLaunchKernelGGL(perm_place_kernel<4>, dim3(grid), dim3(256), 0, s, idx, rank, blk_base,
+                         T, E, k, row_src, tk_row, x, xp, xp8, xps, d, tpb);
+    else if (xp8)
+      hipLaunchKernelGGL(perm_place_kernel<8>, dim3(grid), dim3(256), 0, s, idx, rank, blk_base,
                          T, E, k, row_src, tk_row, x, xp, xp8, xps, d, tpb);
     else
-      hipLaunchKernelGGL(perm_place_kernel<false>, dim3(grid), dim3(256), 0, s, idx, rank,
+      hipLaunchKernelGGL(perm_place_kernel<0>, dim3(grid), dim3(256), 0, s, idx, rank,
                          blk_base, T, E, k, row_src, tk_row, x, xp, xp8, xps, d, tpb);
   }
   return hipGetLastError();

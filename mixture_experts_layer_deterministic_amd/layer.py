@@ -7,7 +7,7 @@ from __future__ import annotations
 import torch
 
 from . import (MOE_FLAG_BF16_DW, MOE_FLAG_MXFP8_WGRAD, MOE_FLAG_PERSISTENT, MOE_PREC_BF16,
-               MOE_PREC_MXFP8, make_cfg, moe_backward, moe_forward, moe_forward_fused, moe_permute,
+               MOE_PREC_MXFP4, MOE_PREC_MXFP8, make_cfg, moe_backward, moe_forward, moe_forward_fused, moe_permute,
                moe_query, moe_quantize_weights, moe_route)
 
 
@@ -16,8 +16,9 @@ class MoeLayer:
 
     ``ring_slots`` slots of T*k permuted rows make up the ring. Forward writes slot ``slot``,
     and backward reads the slot its batch was permuted into. With ``precision=MOE_PREC_MXFP8``
-    the layer also owns the quantised-weight buffer ``wq``; ``quantize_weights`` fills it, and
-    ``mx_wgrad`` makes the weight gradients MXFP8 too. ``bf16_dw`` keeps dw1 and dw2 in bf16.
+    or ``MOE_PREC_MXFP4`` the layer also owns the quantised-weight buffer ``wq``;
+    ``quantize_weights`` fills it, and ``mx_wgrad`` (MXFP8 only) makes the weight gradients
+    MXFP8 too. ``bf16_dw`` keeps dw1 and dw2 in bf16.
     """
 
     def __init__(self, T, d, E, k, I, device="cuda", ring_slots=1, persistent=False,
@@ -48,7 +49,8 @@ class MoeLayer:
         self.dw1 = torch.zeros(E, 2 * I, d, dtype=dwt, device=dev)
         self.dw2 = torch.zeros(E, d, I, dtype=dwt, device=dev)
         self.dwr = torch.zeros(E, d, dtype=f32, device=dev)
-        self.mx = precision == MOE_PREC_MXFP8
+        self.mx = precision in (MOE_PREC_MXFP8, MOE_PREC_MXFP4)
+        self.fbits = 8 if precision == MOE_PREC_MXFP8 else 4 if precision == MOE_PREC_MXFP4 else 16
         self.wq = torch.empty(s.wq, dtype=u8, device=dev) if self.mx else None
 
     # views of intermediates -----------------------------------------------------------------
@@ -57,14 +59,16 @@ class MoeLayer:
         return buf[off:off + n].view(torch.bfloat16).view(rows, cols)
 
     def xp(self, slot=0):
-        """The slot's bf16 Xp (BF16 mode), or (E4M3 codes [T*k, d], scale codes [T*k, d/32]) as
-        uint8 tensors (MXFP8 mode)."""
+        """The slot's bf16 Xp (BF16 mode), or (codes, scale codes [T*k, d/32]) as uint8 tensors:
+        E4M3 codes [T*k, d] (MXFP8 mode) or E2M1 codes two a byte [T*k, d/2], element 2i in the
+        low nibble (MXFP4 mode)."""
         base = slot * self.sizes.ring_slot
         if not self.mx:
             return self._view(self.ring, base, self.T * self.k, self.d)
         Tk, d = self.T * self.k, self.d
-        codes = self.ring[base:base + Tk * d].view(Tk, d)
-        sc0 = base + (Tk * d + 255) // 256 * 256
+        nb = d * self.fbits // 8
+        codes = self.ring[base:base + Tk * nb].view(Tk, nb)
+        sc0 = base + (Tk * nb + 255) // 256 * 256
         return codes, self.ring[sc0:sc0 + Tk * d // 32].view(Tk, d // 32)
 
     def H(self):

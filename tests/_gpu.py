@@ -25,13 +25,20 @@ def _announce(msg):
 
 
 def is_mx(inp):
-    return inp["cfg"].get("precision") == "mxfp8"
+    return inp["cfg"].get("precision") in ("mxfp8", "mxfp4")
+
+
+PRECISIONS = {"bf16": m.MOE_PREC_BF16, "mxfp8": m.MOE_PREC_MXFP8, "mxfp4": m.MOE_PREC_MXFP4}
+
+
+def precision(inp):
+    return inp["cfg"].get("precision", "bf16")
 
 
 def run_gpu(inp, persistent=False, slot=0, ring_slots=1, bf16_dw=False):
     cfg = inp["cfg"]
     T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
-    prec = m.MOE_PREC_MXFP8 if is_mx(inp) else m.MOE_PREC_BF16
+    prec = PRECISIONS[precision(inp)]
     L = MoeLayer(T, d, E, k, I, device=DEV, ring_slots=ring_slots, persistent=persistent,
                  precision=prec, mx_wgrad=bool(cfg.get("mx_wgrad")), bf16_dw=bf16_dw)
     if is_mx(inp):
@@ -46,7 +53,7 @@ def run_gpu(inp, persistent=False, slot=0, ring_slots=1, bf16_dw=False):
 
 def run_oracle(inp, dw_dtype="fp32"):
     X, W1, W2, dY = (_np(inp[n]) for n in ("X", "W1", "W2", "dY"))
-    prec = "mxfp8" if is_mx(inp) else "bf16"
+    prec = precision(inp)
     wg = "mxfp8" if inp["cfg"].get("mx_wgrad") else "bf16"
     if "Wr" in inp:
         Wr = _np(inp["Wr"])
@@ -60,17 +67,30 @@ def run_oracle(inp, dw_dtype="fp32"):
 
 
 def check_xp(L, inp, f, slot=0):
-    """The slot's permuted tokens: a bit-exact copy of X (BF16 mode), or the MXFP8 codes and
-    scales of X, bit-exact against the oracle's quantiser (MXFP8 mode)."""
+    """The slot's permuted tokens: a bit-exact copy of X (BF16 mode), or the MX codes and scales
+    of X, bit-exact against the oracle's quantiser (MX modes; E2M1 codes unpacked from their
+    nibbles)."""
     k = inp["cfg"]["k"]
     src = _np(inp["X"])[f["row_src"] // k]
     if not is_mx(inp):
         np.testing.assert_array_equal(_np(L.xp(slot)), src)
         return
     codes, scales = L.xp(slot)
-    q, sc = oracle.mx.quantize(src)
+    fmt = "e2m1" if precision(inp) == "mxfp4" else "e4m3"
+    q, sc = oracle.mx.quantize(src, fmt=fmt)
     np.testing.assert_array_equal(_np(scales), sc)
-    np.testing.assert_array_equal(_np(codes), q)
+    np.testing.assert_array_equal(codes_of(_np(codes), fmt), q)
+
+
+def codes_of(raw, fmt):
+    """Element codes of a stored code array: bytes as they are (E4M3), or each byte's two E2M1
+    nibbles, the low one first."""
+    if fmt == "e4m3":
+        return raw
+    out = np.empty(raw.shape[:-1] + (2 * raw.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = raw & 0xF
+    out[..., 1::2] = raw >> 4
+    return out
 
 
 def check_parity(L, inp, f, b, slot=0, tol_act=None, tol_grad=None):

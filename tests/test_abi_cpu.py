@@ -89,7 +89,7 @@ def test_entry_points_reject_bad_arguments_before_launching():
     assert L.moe_forward(ctypes.byref(cfg), p, s.ring_slot, 0, p, p, p, p, p, None, 0, p, p,
                          s.saved - 1, p, s.workspace, None) == -5
     # an unknown precision is not provided by this build
-    cfgx = m.make_cfg(64, 256, 8, 2, 128, 2)
+    cfgx = m.make_cfg(64, 256, 8, 2, 128, 3)
     assert L.moe_route(ctypes.byref(cfgx), p, p, p, p, p, p, s.workspace, None) == -3
     # MXFP8: the quantised weights are required, and sized
     cfg8 = m.make_cfg(64, 256, 8, 2, 128, m.MOE_PREC_MXFP8)
@@ -135,6 +135,39 @@ def test_mxfp8_sizes():
     wq = 2 * (up(E * 2 * I * d) + up(E * 2 * I * d // 32)) + 2 * (up(E * d * I) + up(E * d * I // 32))
     assert s.wq == wq
     assert m.moe_query(m.make_cfg(T, d, E, k, I)).wq == 0
+
+
+def test_mxfp4_sizes_and_mode_checks():
+    """MXFP4 codes take half a byte: the ring slot, the quantised weights and the quantised
+    activations shrink accordingly; I must be a multiple of 256 and the MXFP8 wgrad flag is
+    refused; the fused forward does not provide the mode."""
+    T, d, E, k, I = 2048, 7168, 256, 8, 2048
+    s4 = m.moe_query(m.make_cfg(T, d, E, k, I, m.MOE_PREC_MXFP4))
+    s8 = m.moe_query(m.make_cfg(T, d, E, k, I, m.MOE_PREC_MXFP8))
+    Tk = T * k
+    up = lambda v: (v + 255) // 256 * 256
+    assert s4.ring_slot == up(Tk * d // 2) + up(Tk * d // 32)
+    wq = (2 * (up(E * 2 * I * d // 2) + up(E * 2 * I * d // 32)) +
+          2 * (up(E * d * I // 2) + up(E * d * I // 32)))
+    assert s4.wq == wq
+    # dY, A and dH codes: half of MXFP8's
+    assert s8.workspace - s4.workspace == up(T * d) - up(T * d // 2) + up(Tk * I) - \
+        up(Tk * I // 2) + up(Tk * 2 * I) - up(Tk * 2 * I // 2)
+    assert s4.saved == s8.saved
+    for cfg in (m.make_cfg(64, 256, 8, 2, 128, m.MOE_PREC_MXFP4),
+                m.make_cfg(64, 256, 8, 2, 256, m.MOE_PREC_MXFP4, m.MOE_FLAG_MXFP8_WGRAD)):
+        with pytest.raises(m.MoeError) as ei:
+            m.moe_query(cfg)
+        assert ei.value.status == -1
+    got = m.moe_query(m.make_cfg(300, 512, 16, 3, 256, m.MOE_PREC_MXFP4, m.MOE_FLAG_BF16_DW))
+    base = m.moe_query(m.make_cfg(300, 512, 16, 3, 256, m.MOE_PREC_MXFP4))
+    assert (got.ring_slot, got.workspace, got.wq) == (base.ring_slot, base.workspace, base.wq)
+    L = m.lib()
+    p = _fake()
+    cfg4 = m.make_cfg(64, 256, 8, 2, 256, m.MOE_PREC_MXFP4)
+    q = m.moe_query(cfg4)
+    assert L.moe_forward_fused(ctypes.byref(cfg4), p, p, p, p, p, p, q.ring_slot, 0, p, p, p, p,
+                               p, p, p, p, q.saved, p, q.workspace, None) == -3
 
 
 def test_status_strings():

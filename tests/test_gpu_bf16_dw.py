@@ -7,7 +7,7 @@ stored. So, on the same inputs:
 * with accumulate, they equal the stored bf16 value plus the new fp32 sums, rounded once;
 * dW1, dW2 are within the layer's gradient tolerance of the oracle's bf16-stored gradients.
 The cases cover the task-table wgrad kernel (bf16 and MXFP8 right operands), the 256 x 256
-big-expert kernel, the MXFP8 wgrad kernel and empty experts (zero blocks).
+big-expert kernel, the MXFP8 wgrad kernel, MXFP4 mode and empty experts (zero blocks).
 """
 import numpy as np
 import pytest
@@ -38,13 +38,17 @@ def _inputs(case):
     if case == "mxfp8_zipf_local":
         return workload.make_inputs("local_zipf", seed=0, device=DEV, T=2048, d=256, I=256,
                                     precision="mxfp8")
+    if case == "mxfp4_zipf_local":
+        return workload.make_inputs("local_zipf", seed=0, device=DEV, T=2048, d=256, I=256,
+                                    precision="mxfp4")
     if case == "mxfp8_wgrad_zipf_local":
         return workload.make_inputs("local_zipf", seed=0, device=DEV, T=2048, d=256, I=256,
                                     precision="mxfp8", mx_wgrad=True)
     raise KeyError(case)
 
 
-CASES = ["tiny", "zipf_local", "large", "mxfp8_tiny", "mxfp8_zipf_local", "mxfp8_wgrad_zipf_local"]
+CASES = ["tiny", "zipf_local", "large", "mxfp8_tiny", "mxfp8_zipf_local", "mxfp8_wgrad_zipf_local",
+         "mxfp4_zipf_local"]
 
 
 def _backward_again(L, inp, dy, accumulate):
@@ -81,12 +85,13 @@ def test_bf16_dw_is_the_fp32_sum_rounded_once(case):
         assert torch.equal(want.view(torch.int16), g.view(torch.int16))
 
 
-@pytest.mark.parametrize("case", ["tiny", "zipf_local", "mxfp8_wgrad_zipf_local"])
+@pytest.mark.parametrize("case", ["tiny", "zipf_local", "mxfp8_wgrad_zipf_local",
+                                  "mxfp4_zipf_local"])
 def test_bf16_dw_matches_the_oracle(case):
     _announce(f"[bf16 dW] case={case}: against the oracle with bf16-stored weight gradients")
     inp = _inputs(case)
     L = run_gpu(inp, bf16_dw=True)
     f, b = run_oracle(inp, dw_dtype="bf16")
-    # MXFP8 mode is held to the MXFP8 bar, 6e-2 against the quantisation-emulating oracle
-    tol = dict(tol_act=6e-2, tol_grad=6e-2) if inp["cfg"].get("precision") == "mxfp8" else {}
+    # the MX modes are held to their bar, 6e-2 against the quantisation-emulating oracle
+    tol = dict(tol_act=6e-2, tol_grad=6e-2) if inp["cfg"].get("precision") != "bf16" else {}
     check_parity(L, inp, f, b, **tol)

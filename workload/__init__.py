@@ -4,7 +4,7 @@ This module only draws numbers and fixes shapes. It holds none of the layer's ar
 no routing, no permutation and no expert math. The GPU path and the CPU oracle both consume
 what it returns, and neither imports the other.
 
-Five workloads are defined, named for what they are:
+Six workloads are defined, named for what they are:
 
 * ``tiny``: T=256 tokens, d=256, E=8 experts, top-2, SwiGLU intermediate 512.
 * ``dsv3``: a DeepSeek-V3-shaped routed layer on one GPU. T=2048, d=7168, E=256, top-8,
@@ -13,6 +13,7 @@ Five workloads are defined, named for what they are:
   experts, d=7168, intermediate 2048, one expert per row. Rows follow a Zipf(1.2) expert
   popularity with three experts left empty, and each row carries a given gate weight.
 * ``dsv3_mxfp8``: the ``dsv3`` shapes in MXFP8 mode.
+* ``dsv3_mxfp4``: the ``dsv3`` shapes in MXFP4 mode.
 * ``stream``: 8 microbatches of 2368 tokens through d=4096, E=512, top-10, intermediate 1024,
   sharing one 512 MiB ring buffer.
 
@@ -37,6 +38,7 @@ CONFIGS = {
     "dsv3": dict(T=2048, d=7168, E=256, k=8, I=2048, precision="bf16", routing="router"),
     "local_zipf": dict(T=16384, d=7168, E=8, k=1, I=2048, precision="bf16", routing="zipf"),
     "dsv3_mxfp8": dict(T=2048, d=7168, E=256, k=8, I=2048, precision="mxfp8", routing="router"),
+    "dsv3_mxfp4": dict(T=2048, d=7168, E=256, k=8, I=2048, precision="mxfp4", routing="router"),
     "stream": dict(T=2368, d=4096, E=512, k=10, I=1024, precision="bf16", routing="router",
                    microbatches=8, ring_bytes=512 * 1024 * 1024),
 }
