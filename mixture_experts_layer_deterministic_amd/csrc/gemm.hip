@@ -268,9 +268,11 @@ struct DownDgradBigArgs {
 // 16-byte chunks g and 4 + g). LDS holds each stage as [BM][128] A codes, [BN][128] B codes
 // (chunk-permuted rows, mxswz), then the step's block scales, 4 (E4M3) or 8 (E2M1) bytes a row.
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int F_ = 8>
+// GS: the K extent is a multiple of 512, so each row's scales load 16 bytes at a time (LoadK8).
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int F_ = 8, bool GS_ = true>
 struct GeoMx {
   static constexpr int F = F_;                     // bits per code
+  static constexpr bool GS = GS_;
   static_assert(F == 8 || F == 4, "E4M3 or E2M1 codes");
   static constexpr int BM = BM_, BN = BN_, BK = 1024 / F;  // K per step
   static constexpr int SCW = BK / 128;             // 32-bit scale words per row and step
@@ -295,11 +297,14 @@ using GeoMxBig = GeoMx<256, 256, 2, 4>;
 MOE_DEV int mxswz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
 // ROWS rows of codes, K-contiguous: 8 vectors of 16 bytes per step. Thread t < ROWS also moves
-// row t's SCW scale words (the step's block scales), loading the words of 16 bytes of scales at
-// once where the row length allows. Every row is real (a tile's rows past its expert's count
-// repeat the expert's last row; their outputs are never stored), so the code loads carry no
-// per-row condition, as in LoadK.
-template <int ROWS, int LDK, int SCW = 1>
+// row t's SCW scale words (the step's block scales). With GS (rows of a multiple of 16 scale
+// bytes: K a multiple of 512) they come 16 bytes at a time, one load per 16 / (4 SCW) steps;
+// otherwise one 4- or 8-byte load per step, a cache line per lane each time. The two forms are
+// separate instantiations: one scale path that merged words loaded on different branches made
+// the compiler wait for every load right after issuing it. Every row is real (a tile's rows
+// past its expert's count repeat the expert's last row; their outputs are never stored), so
+// the code loads carry no per-row condition, as in LoadK.
+template <int ROWS, int LDK, int SCW, bool GS>
 struct LoadK8 {
   static constexpr int VPR = 8;
   static constexpr int NV = ROWS * VPR;
@@ -309,24 +314,21 @@ struct LoadK8 {
   const uint8_t* rp[PT];
   uint4 r[PT];
   const uint8_t* sp;
-  uint4 s4;     // the scale words of SPG consecutive steps (or of one, from s4.x)
-  int sg, sidx; // group held in s4 and this step's index in it
-  bool grouped; // rows hold a multiple of 16 scale bytes: load them 16 bytes at a time
+  uint4 s4;      // GS: the scale words of SPG consecutive steps; else this step's in s4.x (.y)
+  int sg, sidx;  // GS: the group held in s4 and this step's place in it
 
-  // kdim: the K extent of a row (elements), so a row holds kdim / 32 scale bytes. The scale
-  // arrays start 16-byte aligned.
+  // The scale arrays start 16-byte aligned.
   template <class RowPtr, class ScalePtr>
-  MOE_DEV void init(RowPtr rowptr, ScalePtr scaleptr, int kdim) {
+  MOE_DEV void init(RowPtr rowptr, ScalePtr scaleptr) {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const int v = threadIdx.x + kThreads * j;
       rp[j] = rowptr(min(v / VPR, ROWS - 1));
     }
     sp = threadIdx.x < ROWS ? scaleptr(threadIdx.x) : nullptr;
-    grouped = kdim % 512 == 0;
     sg = -1;
-    s4 = make_uint4(0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu);
     sidx = 0;
+    s4 = make_uint4(0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu);
   }
   // The scale words are picked in store(), so no load result is waited for here.
   MOE_DEV void load(int kt) {
@@ -336,7 +338,7 @@ struct LoadK8 {
       r[j] = *reinterpret_cast<const uint4*>(rp[j] + (size_t)kt * 128 + (v % VPR) * 16);
     }
     if (!sp) return;
-    if (grouped) {
+    if constexpr (GS) {
       if (kt / SPG != sg) {
         sg = kt / SPG;
         s4 = *reinterpret_cast<const uint4*>(sp + (size_t)sg * 16);
@@ -344,12 +346,10 @@ struct LoadK8 {
       sidx = kt % SPG;
     } else if constexpr (SCW == 1) {
       s4.x = *reinterpret_cast<const uint32_t*>(sp + (size_t)kt * 4);
-      sidx = 0;
     } else {
       const uint2 w = *reinterpret_cast<const uint2*>(sp + (size_t)kt * 8);
       s4.x = w.x;
       s4.y = w.y;
-      sidx = 0;
     }
   }
   MOE_DEV void store(uint8_t* rows, uint32_t* scales) const {
@@ -358,25 +358,29 @@ struct LoadK8 {
       const int v = threadIdx.x + kThreads * j;
       if (v < NV) *reinterpret_cast<uint4*>(rows + mxswz(v / VPR, v % VPR)) = r[j];
     }
-    if (threadIdx.x < ROWS) {
-      // masks rather than a selected vector element, which the compiler would index in scratch
-      if constexpr (SCW == 1) {
-        const uint32_t m0 = 0u - (sidx == 0), m1 = 0u - (sidx == 1), m2 = 0u - (sidx == 2),
-                       m3 = 0u - (sidx == 3);
-        scales[threadIdx.x] = (s4.x & m0) | (s4.y & m1) | (s4.z & m2) | (s4.w & m3);
-      } else {
-        const uint32_t m0 = 0u - (sidx == 0), m1 = ~m0;
-        *reinterpret_cast<uint2*>(scales + 2 * threadIdx.x) =
-            make_uint2((s4.x & m0) | (s4.z & m1), (s4.y & m0) | (s4.w & m1));
-      }
+    if (threadIdx.x >= ROWS) return;
+    // masks rather than a selected vector element, which the compiler would index in scratch
+    if constexpr (!GS) {
+      if constexpr (SCW == 1)
+        scales[threadIdx.x] = s4.x;
+      else
+        *reinterpret_cast<uint2*>(scales + 2 * threadIdx.x) = make_uint2(s4.x, s4.y);
+    } else if constexpr (SCW == 1) {
+      const uint32_t m0 = 0u - (sidx == 0), m1 = 0u - (sidx == 1), m2 = 0u - (sidx == 2),
+                     m3 = 0u - (sidx == 3);
+      scales[threadIdx.x] = (s4.x & m0) | (s4.y & m1) | (s4.z & m2) | (s4.w & m3);
+    } else {
+      const uint32_t m0 = 0u - (sidx == 0), m1 = ~m0;
+      *reinterpret_cast<uint2*>(scales + 2 * threadIdx.x) =
+          make_uint2((s4.x & m0) | (s4.z & m1), (s4.y & m0) | (s4.w & m1));
     }
   }
 };
 
 template <class G>
-using LoadA8 = LoadK8<G::BM, G::LDK, G::SCW>;
+using LoadA8 = LoadK8<G::BM, G::LDK, G::SCW, G::GS>;
 template <class G>
-using LoadB8 = LoadK8<G::BN, G::LDK, G::SCW>;
+using LoadB8 = LoadK8<G::BN, G::LDK, G::SCW, G::GS>;
 
 template <class G>
 MOE_DEV void mx_store_stage(const LoadA8<G>& la, const LoadB8<G>& lb, uint8_t* stage) {
@@ -578,13 +582,13 @@ struct MxFwdGateUpT {
       const uint8_t* xps = a.xps;
       const size_t pb = (size_t)d * G::F / 8;  // bytes of codes per row
       la.init([&](int m) { return xp8 + (size_t)(row0 + min(m, mc - 1)) * pb; },
-              [&](int m) { return xps + (size_t)(row0 + min(m, mc - 1)) * (d / 32); }, d);
+              [&](int m) { return xps + (size_t)(row0 + min(m, mc - 1)) * (d / 32); });
       const size_t wrow0 = (size_t)t.m.e * 2 * I;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
       auto wrow = [=](int n) { return wrow0 + (n < kA ? n0 + n : I + n0 + n - kA); };
       lb.init([&](int n) { return w8 + wrow(n) * pb; },
-              [&](int n) { return ws + wrow(n) * (d / 32); }, d);
+              [&](int n) { return ws + wrow(n) * (d / 32); });
     }
     MOE_DEV void load(int kt) {  // weights first: they are the HBM stream
       lb.load(kt);
@@ -636,7 +640,8 @@ struct MxFwdGateUpT {
   }
 };
 
-using MxFwdGateUp = MxFwdGateUpT<GeoMx<128, 128, 2, 2>>;
+template <int F, bool GS>
+using MxFwdGateUpS = MxFwdGateUpT<GeoMx<128, 128, 2, 2, F, GS>>;
 using MxFwdGateUpBig = MxFwdGateUpT<GeoMxBig>;
 
 // Problem 2 (MXFP8): forward down. O[pos] = A[pos] . W2[e]^T, with A and W2 quantised along I.
@@ -682,12 +687,12 @@ struct MxFwdDownT {
       const uint8_t* aqs = a.aqs;
       const size_t pb = (size_t)I * G::F / 8;  // bytes of codes per row
       la.init([&](int m) { return aq + (size_t)(row0 + min(m, mc - 1)) * pb; },
-              [&](int m) { return aqs + (size_t)(row0 + min(m, mc - 1)) * (I / 32); }, I);
+              [&](int m) { return aqs + (size_t)(row0 + min(m, mc - 1)) * (I / 32); });
       const size_t wrow0 = (size_t)t.m.e * a.d + t.n0;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
       lb.init([&](int n) { return w8 + (wrow0 + n) * pb; },
-              [&](int n) { return ws + (wrow0 + n) * (I / 32); }, I);
+              [&](int n) { return ws + (wrow0 + n) * (I / 32); });
     }
     MOE_DEV void load(int kt) {  // weights first: they are the HBM stream
       lb.load(kt);
@@ -714,7 +719,8 @@ struct MxFwdDownT {
     }
   }
 };
-using MxFwdDown = MxFwdDownT<GeoMx<128, 128, 1, 4>>;
+template <int F, bool GS>
+using MxFwdDownS = MxFwdDownT<GeoMx<128, 128, 1, 4, F, GS>>;
 using MxFwdDownBig = MxFwdDownT<GeoMxBig>;
 
 // Problem 3 (MXFP8): down dgrad, dA'[pos] = dY[t] . W2[e] with dY and W2 quantised along d
@@ -768,12 +774,12 @@ struct MxBwdDownDgradT {
       const int32_t* rs = a.row_src;
       const size_t pb = (size_t)d * G::F / 8;  // bytes of codes per row
       la.init([&](int m) { return dyq + (size_t)(rs[row0 + min(m, mc - 1)] / k) * pb; },
-              [&](int m) { return dys + (size_t)(rs[row0 + min(m, mc - 1)] / k) * (d / 32); }, d);
+              [&](int m) { return dys + (size_t)(rs[row0 + min(m, mc - 1)] / k) * (d / 32); });
       const size_t wrow0 = (size_t)t.m.e * a.I + t.n0;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
       lb.init([&](int n) { return w8 + (wrow0 + n) * pb; },
-              [&](int n) { return ws + (wrow0 + n) * (d / 32); }, d);
+              [&](int n) { return ws + (wrow0 + n) * (d / 32); });
     }
     MOE_DEV void load(int kt) {  // weights first: they are the HBM stream
       lb.load(kt);
@@ -864,7 +870,8 @@ struct MxBwdDownDgradT {
   }
 };
 
-using MxBwdDownDgrad = MxBwdDownDgradT<GeoMx<128, 128, 1, 4>>;
+template <int F, bool GS>
+using MxBwdDownDgradS = MxBwdDownDgradT<GeoMx<128, 128, 1, 4, F, GS>>;
 
 // Problem 4 (MXFP8): gate/up dgrad, dXp[pos] = dH[pos] . W1[e] with dH and W1 quantised along
 // 2I (W1 stored transposed, [E, d, 2I]).
@@ -908,12 +915,12 @@ struct MxBwdGateDgradT {
       const uint8_t* dhs = a.dhs;
       const size_t pb = (size_t)twoI * G::F / 8;  // bytes of codes per row
       la.init([&](int m) { return dhq + (size_t)(row0 + min(m, mc - 1)) * pb; },
-              [&](int m) { return dhs + (size_t)(row0 + min(m, mc - 1)) * (twoI / 32); }, twoI);
+              [&](int m) { return dhs + (size_t)(row0 + min(m, mc - 1)) * (twoI / 32); });
       const size_t wrow0 = (size_t)t.m.e * a.d + t.n0;
       const uint8_t* w8 = a.w8;
       const uint8_t* ws = a.ws;
       lb.init([&](int n) { return w8 + (wrow0 + n) * pb; },
-              [&](int n) { return ws + (wrow0 + n) * (twoI / 32); }, twoI);
+              [&](int n) { return ws + (wrow0 + n) * (twoI / 32); });
     }
     MOE_DEV void load(int kt) {  // weights first: they are the HBM stream
       lb.load(kt);
@@ -940,7 +947,8 @@ struct MxBwdGateDgradT {
     }
   }
 };
-using MxBwdGateDgrad = MxBwdGateDgradT<GeoMx<128, 128, 1, 4>>;
+template <int F, bool GS>
+using MxBwdGateDgradS = MxBwdGateDgradT<GeoMx<128, 128, 1, 4, F, GS>>;
 using MxBwdGateDgradBig = MxBwdGateDgradT<GeoMxBig>;
 
 // MXFP8 weight gradients: dW[e][m][n] = sum over the expert's padded positions p of
@@ -952,7 +960,7 @@ using MxBwdGateDgradBig = MxBwdGateDgradT<GeoMxBig>;
 template <bool ACC, bool BF>
 struct MxWgrad {
   static constexpr const char* kName = "bwd_wgrad_mx";
-  using G = GeoMx<128, 128, 1, 4>;
+  using G = GeoMx<128, 128, 1, 4, 8, false>;  // a K step's scale words load one step at a time
   struct Args {
     const uint8_t* lq;
     const uint8_t* lqs;
@@ -996,12 +1004,11 @@ struct MxWgrad {
       const uint8_t* rq = a.rq;
       const uint8_t* rqs = a.rqs;
       const int m0 = t.m0, n0 = t.n0;
-      // kdim 128: the scale words load one step at a time (4-byte aligned: P and p0 are
-      // multiples of 128)
+      // the scale words are 4-byte aligned: P and p0 are multiples of 128
       la.init([&](int m) { return lq + (m0 + m) * P + p0; },
-              [&](int m) { return lqs + (m0 + m) * (P / 32) + p0 / 32; }, G::BK);
+              [&](int m) { return lqs + (m0 + m) * (P / 32) + p0 / 32; });
       lb.init([&](int n) { return rq + (n0 + n) * P + p0; },
-              [&](int n) { return rqs + (n0 + n) * (P / 32) + p0 / 32; }, G::BK);
+              [&](int n) { return rqs + (n0 + n) * (P / 32) + p0 / 32; });
     }
     MOE_DEV void load(int kt) {
       la.load(kt);
@@ -1598,7 +1605,7 @@ struct DmxGateDgrad {
 // of I columns (a wave's 64 columns are two), and the router-weight partials of each 128-column
 // half are the sums of its two waves' row sums, as in the BF16 256 x 256 kernel.
 struct DmxDownDgrad {
-  using Args = MxBwdDownDgrad::Args;
+  using Args = MxBwdDownDgradS<8, true>::Args;
   using Tile = DgradTile;
   static constexpr const char* kName = "bwd_down_dgrad_big";
   static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.I / 256); }
@@ -1831,82 +1838,96 @@ hipError_t launch_bwd_gate_dgrad(const GemmBwdGateDgradArgs& x, bool persistent,
   return launch<BwdGateDgrad>(a, sched_max_rem(x.Tk, x.E) * (x.d / 128), persistent, s);
 }
 
-// MXFP4: every 128-row block on the 128-row kernels.
-using GeoMx4 = GeoMx<128, 128, 1, 4, 4>;
-using MxFwdGateUp4 = MxFwdGateUpT<GeoMx<128, 128, 2, 2, 4>>;
-using MxFwdDown4 = MxFwdDownT<GeoMx4>;
-using MxBwdDownDgrad4 = MxBwdDownDgradT<GeoMx4>;
-using MxBwdGateDgrad4 = MxBwdGateDgradT<GeoMx4>;
+// The 128-row MX kernels, instantiated for both scale-load forms (GeoMx::GS) and picked by the
+// GEMM's K extent; MXFP4 runs every 128-row block on them.
+template <class T>
+struct Tag {
+  using type = T;
+};
+// f(Tag<P<F, K % 512 == 0>>) for the code width fbits
+template <template <int, bool> class P, class Fn>
+hipError_t with_mx(int fbits, int K, Fn&& f) {
+  const bool gs = K % 512 == 0;
+  if (fbits == 4) return gs ? f(Tag<P<4, true>>{}) : f(Tag<P<4, false>>{});
+  return gs ? f(Tag<P<8, true>>{}) : f(Tag<P<8, false>>{});
+}
 
 // The MXFP8 forward GEMMs and gate dgrad run the 256-row blocks with dmx_kernel, then the
 // remainders on the 128-row kernels.
 hipError_t launch_fwd_gateup_mx(const GemmMxGateUpArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
-  if (x.fbits == 4) {
-    MxFwdGateUp4::Args a{x.xp8, x.xps, x.w8, x.ws, x.H, x.A, x.aq, x.aqs, x.offsets, st.full,
-                         x.d, x.I};
-    return launch<MxFwdGateUp4>(a, sched_max_mtiles(x.Tk, x.E) * (x.I / MxFwdGateUp4::kA),
-                                persistent, s);
+  const bool fp4 = x.fbits == 4;
+  if (!fp4) {
+    MxFwdGateUpBig::Args ab{x.xp8, x.xps, x.w8, x.ws, x.H,     x.A,
+                            x.aq,  x.aqs, x.offsets, st.big, x.d, x.I};
+    const hipError_t e = launch_dmx<DmxGateUp>(
+        ab, sched_max_big(x.Tk) * (x.I / MxFwdGateUpBig::kA), true, s);
+    if (e != hipSuccess) return e;
   }
-  MxFwdGateUpBig::Args ab{x.xp8, x.xps, x.w8, x.ws, x.H,     x.A,
-                          x.aq,  x.aqs, x.offsets, st.big, x.d, x.I};
-  hipError_t e = launch_dmx<DmxGateUp>(ab, sched_max_big(x.Tk) * (x.I / MxFwdGateUpBig::kA),
-                                       true, s);
-  if (e != hipSuccess) return e;
-  MxFwdGateUp::Args a{x.xp8, x.xps, x.w8, x.ws, x.H, x.A, x.aq, x.aqs, x.offsets, st.rem, x.d, x.I};
-  return launch<MxFwdGateUp>(a, sched_max_rem(x.Tk, x.E) * (x.I / MxFwdGateUp::kA), persistent,
-                             s);
+  const int mt = fp4 ? sched_max_mtiles(x.Tk, x.E) : sched_max_rem(x.Tk, x.E);
+  return with_mx<MxFwdGateUpS>(x.fbits, x.d, [&](auto tag) {
+    using P = typename decltype(tag)::type;
+    typename P::Args a{x.xp8, x.xps, x.w8, x.ws, x.H, x.A, x.aq, x.aqs, x.offsets,
+                       fp4 ? st.full : st.rem, x.d, x.I};
+    return launch<P>(a, mt * (x.I / P::kA), persistent, s);
+  });
 }
 
 hipError_t launch_fwd_down_mx(const GemmMxDownArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
-  if (x.fbits == 4) {
-    MxFwdDown4::Args a{x.aq, x.aqs, x.w8, x.ws, x.O, x.offsets, st.full, x.d, x.I};
-    return launch<MxFwdDown4>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
+  const bool fp4 = x.fbits == 4;
+  if (!fp4) {
+    MxFwdDownBig::Args ab{x.aq, x.aqs, x.w8, x.ws, x.O, x.offsets, st.big, x.d, x.I};
+    const hipError_t e = launch_dmx<DmxDown>(ab, sched_max_big(x.Tk) * (x.d / 256), true, s);
+    if (e != hipSuccess) return e;
   }
-  MxFwdDownBig::Args ab{x.aq, x.aqs, x.w8, x.ws, x.O, x.offsets, st.big, x.d, x.I};
-  hipError_t e = launch_dmx<DmxDown>(ab, sched_max_big(x.Tk) * (x.d / 256), true, s);
-  if (e != hipSuccess) return e;
-  MxFwdDown::Args a{x.aq, x.aqs, x.w8, x.ws, x.O, x.offsets, st.rem, x.d, x.I};
-  return launch<MxFwdDown>(a, sched_max_rem(x.Tk, x.E) * (x.d / 128), persistent, s);
+  const int mt = fp4 ? sched_max_mtiles(x.Tk, x.E) : sched_max_rem(x.Tk, x.E);
+  return with_mx<MxFwdDownS>(x.fbits, x.I, [&](auto tag) {
+    using P = typename decltype(tag)::type;
+    typename P::Args a{x.aq, x.aqs, x.w8, x.ws, x.O, x.offsets, fp4 ? st.full : st.rem, x.d, x.I};
+    return launch<P>(a, mt * (x.d / 128), persistent, s);
+  });
 }
 
 // With I a multiple of 256 the MXFP8 down dgrad runs the 256-row blocks with dmx_kernel, then
 // the remainders; otherwise every 128-row block on the 128-row kernel.
 hipError_t launch_bwd_down_dgrad_mx(const GemmMxDownDgradArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
-  if (x.fbits == 4) {
-    MxBwdDownDgrad4::Args a{x.dyq, x.dys, x.row_src, x.topk_w, x.w8,  x.ws,   x.H,
-                            x.A,   x.dH,  x.dwpart,  x.dhq,    x.dhs, x.offsets, st.full,
-                            x.d,   x.I,   x.k};
-    return launch<MxBwdDownDgrad4>(a, sched_max_mtiles(x.Tk, x.E) * (x.I / 128), persistent, s);
-  }
-  const bool big = x.I % 256 == 0;
+  const bool big = x.fbits == 8 && x.I % 256 == 0;
   const int max_big = big ? sched_max_big(x.Tk) * (x.I / 256) : 0;
   if (max_big > 0) {
-    MxBwdDownDgrad::Args ab{x.dyq, x.dys, x.row_src, x.topk_w, x.w8, x.ws, x.H, x.A, x.dH,
-                            x.dwpart, x.dhq, x.dhs, x.offsets, st.big, x.d, x.I, x.k};
+    MxBwdDownDgradS<8, true>::Args ab{x.dyq, x.dys,    x.row_src, x.topk_w, x.w8,    x.ws,
+                                      x.H,   x.A,      x.dH,      x.dwpart, x.dhq,   x.dhs,
+                                      x.offsets, st.big, x.d,     x.I,      x.k};
     const hipError_t e = launch_dmx<DmxDownDgrad>(ab, max_big, true, s);
     if (e != hipSuccess) return e;
   }
-  MxBwdDownDgrad::Args a{x.dyq, x.dys, x.row_src, x.topk_w, x.w8,  x.ws, x.H,
-                         x.A,   x.dH,  x.dwpart,  x.dhq,    x.dhs, x.offsets,
-                         big ? st.rem : st.full, x.d, x.I, x.k};
-  const int max_small = big ? sched_max_rem(x.Tk, x.E) : sched_max_mtiles(x.Tk, x.E);
-  return launch<MxBwdDownDgrad>(a, max_small * (x.I / 128), persistent, s);
+  const int mt = big ? sched_max_rem(x.Tk, x.E) : sched_max_mtiles(x.Tk, x.E);
+  return with_mx<MxBwdDownDgradS>(x.fbits, x.d, [&](auto tag) {
+    using P = typename decltype(tag)::type;
+    typename P::Args a{x.dyq, x.dys, x.row_src, x.topk_w, x.w8,  x.ws, x.H,
+                       x.A,   x.dH,  x.dwpart,  x.dhq,    x.dhs, x.offsets,
+                       big ? st.rem : st.full, x.d, x.I, x.k};
+    return launch<P>(a, mt * (x.I / 128), persistent, s);
+  });
 }
 
 hipError_t launch_bwd_gate_dgrad_mx(const GemmMxGateDgradArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
-  if (x.fbits == 4) {
-    MxBwdGateDgrad4::Args a{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, st.full, x.d, x.I};
-    return launch<MxBwdGateDgrad4>(a, sched_max_mtiles(x.Tk, x.E) * (x.d / 128), persistent, s);
+  const bool fp4 = x.fbits == 4;
+  if (!fp4) {
+    MxBwdGateDgradBig::Args ab{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, st.big, x.d, x.I};
+    const hipError_t e =
+        launch_dmx<DmxGateDgrad>(ab, sched_max_big(x.Tk) * (x.d / 256), true, s);
+    if (e != hipSuccess) return e;
   }
-  MxBwdGateDgradBig::Args ab{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, st.big, x.d, x.I};
-  hipError_t e = launch_dmx<DmxGateDgrad>(ab, sched_max_big(x.Tk) * (x.d / 256), true, s);
-  if (e != hipSuccess) return e;
-  MxBwdGateDgrad::Args a{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, st.rem, x.d, x.I};
-  return launch<MxBwdGateDgrad>(a, sched_max_rem(x.Tk, x.E) * (x.d / 128), persistent, s);
+  const int mt = fp4 ? sched_max_mtiles(x.Tk, x.E) : sched_max_rem(x.Tk, x.E);
+  return with_mx<MxBwdGateDgradS>(x.fbits, 2 * x.I, [&](auto tag) {
+    using P = typename decltype(tag)::type;
+    typename P::Args a{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, fp4 ? st.full : st.rem, x.d,
+                       x.I};
+    return launch<P>(a, mt * (x.d / 128), persistent, s);
+  });
 }
 
 template <bool ACC, bool BF>

@@ -429,11 +429,11 @@ __global__ void __launch_bounds__(256) expand_fp4_kernel(const uint8_t* __restri
   if (v >= nvec) return;
   const uint32_t c = reinterpret_cast<const uint32_t*>(q)[v];
   const float s = mx_scale(qs[v / 4]);
-  float f[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = e2m1_value((c >> (4 * i)) & 0xfu) * s;
-  reinterpret_cast<uint4*>(out)[v] = make_uint4(pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3]),
-                                                pack_bf2(f[4], f[5]), pack_bf2(f[6], f[7]));
+  const float2 f0 = e2m1x2_to_f32<0>(c), f1 = e2m1x2_to_f32<1>(c), f2 = e2m1x2_to_f32<2>(c),
+               f3 = e2m1x2_to_f32<3>(c);
+  reinterpret_cast<uint4*>(out)[v] =
+      make_uint4(pack_bf2(f0.x * s, f0.y * s), pack_bf2(f1.x * s, f1.y * s),
+                 pack_bf2(f2.x * s, f2.y * s), pack_bf2(f3.x * s, f3.y * s));
 }
 
 hipError_t launch_expand_fp4(const uint8_t* q, const uint8_t* qs, long long rows, int cols,
