@@ -289,7 +289,8 @@ struct GeoMx {
   static_assert(WAVES_M * WAVES_N == 4 || WAVES_M * WAVES_N == 8, "4 or 8 waves per workgroup");
 };
 // Full 256-row blocks on the direct-to-LDS kernel (dmx_kernel): eight waves of 128 x 64.
-using GeoMxBig = GeoMx<256, 256, 2, 4>;
+template <int F>
+using GeoMxBig = GeoMx<256, 256, 2, 4, F>;
 
 // Byte offset of 16-byte chunk `chunk` of row `row` in an fp8 code tile of 128-byte rows, with
 // the chunks permuted per row as in rowswz (chunk c of row r at c ^ (r & 7)): fragment reads
@@ -642,7 +643,8 @@ struct MxFwdGateUpT {
 
 template <int F, bool GS>
 using MxFwdGateUpS = MxFwdGateUpT<GeoMx<128, 128, 2, 2, F, GS>>;
-using MxFwdGateUpBig = MxFwdGateUpT<GeoMxBig>;
+template <int F>
+using MxFwdGateUpBig = MxFwdGateUpT<GeoMxBig<F>>;
 
 // Problem 2 (MXFP8): forward down. O[pos] = A[pos] . W2[e]^T, with A and W2 quantised along I.
 template <class G_>
@@ -721,7 +723,8 @@ struct MxFwdDownT {
 };
 template <int F, bool GS>
 using MxFwdDownS = MxFwdDownT<GeoMx<128, 128, 1, 4, F, GS>>;
-using MxFwdDownBig = MxFwdDownT<GeoMxBig>;
+template <int F>
+using MxFwdDownBig = MxFwdDownT<GeoMxBig<F>>;
 
 // Problem 3 (MXFP8): down dgrad, dA'[pos] = dY[t] . W2[e] with dY and W2 quantised along d
 // (W2 stored transposed, [E, I, d]). The epilogue is the BF16 one (router-weight-gradient
@@ -949,7 +952,8 @@ struct MxBwdGateDgradT {
 };
 template <int F, bool GS>
 using MxBwdGateDgradS = MxBwdGateDgradT<GeoMx<128, 128, 1, 4, F, GS>>;
-using MxBwdGateDgradBig = MxBwdGateDgradT<GeoMxBig>;
+template <int F>
+using MxBwdGateDgradBig = MxBwdGateDgradT<GeoMxBig<F>>;
 
 // MXFP8 weight gradients: dW[e][m][n] = sum over the expert's padded positions p of
 // lq[m][poff[e] + p] rq[n][poff[e] + p], both operands quantised along the positions (mx.hip,
@@ -1336,8 +1340,11 @@ struct DmaDownDgrad {
 // stage for the next step, so loads have one step of MFMAs to arrive. The two stages are
 // distinct LDS arrays and the loop is unrolled over both, so the compiler can tell the stage a
 // load writes from the one the fragment reads read.
-constexpr int kDmxCodes = 256 * 128;                   // bytes of one operand's codes
-constexpr int kDmxStage = 2 * kDmxCodes + 2 * 256 * 4;  // A, B codes, then A, B scale words
+// E2M1 steps (256 K in the same 128 bytes a row) carry two scale words a row: word 0 of every A
+// and B row, then word 1 of every row, each moved by one 4-byte load per lane.
+constexpr int kDmxCodes = 256 * 128;   // bytes of one operand's codes
+constexpr int kDmxWords = 2 * 256 * 4;  // one scale word of every A and B row
+constexpr int kDmxStage = 2 * kDmxCodes + 2 * kDmxWords;  // A, B codes, then the scale words
 __shared__ __align__(1024) uint8_t dmx_s0[kDmxStage];
 __shared__ __align__(1024) uint8_t dmx_s1[kDmxStage];
 template <int S>
@@ -1365,8 +1372,9 @@ MOE_DEV void dmx4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_
                                            voff, soff, 0, 0);
 }
 
-// K chunk kt of the tile (clamped to the last) into stage S: nine load instructions a wave.
-template <int S>
+// K chunk kt of the tile (clamped to the last) into stage S: nine load instructions a wave (ten
+// for E2M1 codes, F = 4).
+template <int S, int F>
 MOE_DEV void dmx_issue(const DmxSrc& s, int kt, int wave) {
   int kk = min(kt, s.nk - 1) + s.k0;
   kk = kk >= s.nk ? kk - s.nk : kk;
@@ -1377,51 +1385,61 @@ MOE_DEV void dmx_issue(const DmxSrc& s, int kt, int wave) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     dmx16(s.rb, s.bo, step + j * s.bst, st + kDmxCodes + wave * 4096 + j * 1024);
-  dmx4(s.rs, s.so, (uint32_t)kk * 4, st + 2 * kDmxCodes + wave * 256);
+  constexpr uint32_t SB = F == 8 ? 4 : 8;  // scale bytes a row per step
+  dmx4(s.rs, s.so, (uint32_t)kk * SB, st + 2 * kDmxCodes + wave * 256);
+  if constexpr (F == 4)
+    dmx4(s.rs, s.so, (uint32_t)kk * SB + 4, st + 2 * kDmxCodes + kDmxWords + wave * 256);
+}
+
+// The scale bytes lane group g passes for LDS scale row q (A rows 0..255, B rows 256..511):
+// byte g of word 0 and (E2M1) of word 1.
+template <int F>
+MOE_DEV int2 dmx_scales(const uint32_t* sc, int q, int g) {
+  const int x = static_cast<int>((sc[q] >> (8 * g)) & 0xffu);
+  if constexpr (F == 8) return make_int2(x, 0);
+  else return make_int2(x, static_cast<int>((sc[512 + q] >> (8 * g)) & 0xffu));
 }
 
 template <class D, int S>
 MOE_DEV void dmx_step(f32x4 (&acc)[8][4], const DmxSrc& s, int kt, int wave, int wm, int wn,
                       int lane) {
+  constexpr int F = D::F;
   __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
   __builtin_amdgcn_s_barrier();
-  dmx_issue<S ^ 1>(s, kt + 1, wave);
+  dmx_issue<S ^ 1, F>(s, kt + 1, wave);
   __builtin_amdgcn_sched_barrier(0);
   const uint8_t* st = dmx_stage<S>();
   const uint8_t* sA = st;
   const uint8_t* sB = st + kDmxCodes;
-  const uint32_t* scA = reinterpret_cast<const uint32_t*>(st + 2 * kDmxCodes);
-  const uint32_t* scB = scA + 256;
+  const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + 2 * kDmxCodes);
   // the lane's fragment addresses are recomputed in every step (a few adds) rather than held
   // across the loop, where the accumulators and fragments leave no register for them
   int ln = lane;
   asm volatile("" : "+v"(ln));
   const int r16 = ln % 16, g = ln / 16;
   i32x8 bf[4];
-  int bs[4];
+  int2 bs[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int row = D::brow(wn, nb) + r16;
     bf[nb] = mx_frag(sB, row, g);
-    bs[nb] = static_cast<int>((scB[row] >> (8 * g)) & 0xffu);
+    bs[nb] = dmx_scales<F>(sc, 256 + row, g);
   }
   // row block mb + 1's A fragment is read while row block mb's MFMAs run
   const int row0 = wm * 128 + r16;
   i32x8 af = mx_frag(sA, row0, g);
-  int as = static_cast<int>((scA[row0] >> (8 * g)) & 0xffu);
+  int2 as = dmx_scales<F>(sc, row0, g);
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
     i32x8 an = af;
-    int asn = as;
+    int2 asn = as;
     if (mb + 1 < 8) {
       const int row = row0 + (mb + 1) * 16;
       an = mx_frag(sA, row, g);
-      asn = static_cast<int>((scA[row] >> (8 * g)) & 0xffu);
+      asn = dmx_scales<F>(sc, row, g);
     }
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nb], af, acc[mb][nb], 0,
-                                                                      0, 0, bs[nb], 0, as);
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mx_mfma<F>(bf[nb], af, acc[mb][nb], bs[nb], as);
     af = an;
     as = asn;
   }
@@ -1450,7 +1468,7 @@ __global__ void __launch_bounds__(512, 2) dmx_kernel(const typename D::Args a) {
     DmxSrc s;
     D::src(a, t, wave, lane, s);
     if (s.nk > 0) {
-      dmx_issue<0>(s, 0, wave);
+      dmx_issue<0, D::F>(s, 0, wave);
       for (int kt = 0;; kt += 2) {
         dmx_step<D, 0>(acc, s, kt, wave, wm, wn, lane);
         if (kt + 1 >= s.nk) break;
@@ -1500,30 +1518,33 @@ hipError_t launch_dmx(const typename D::Args& a, int max_tiles, bool persistent,
   return hipGetLastError();
 }
 
-// Problem 1 (MXFP8) on full 256-row blocks: 256 token rows (Xp codes, pitch d) against 128 gate
-// rows and the 128 matching up rows of W1[e]'s codes (pitch d). Byte offsets fit 32 bits: an
-// expert's W1 codes are below 2^31 bytes (4 I d < 2^31 is an API limit).
+// Problem 1 (MX) on full 256-row blocks: 256 token rows (Xp codes, pitch d F / 8 bytes) against
+// 128 gate rows and the 128 matching up rows of W1[e]'s codes (same pitch). Byte offsets fit 32
+// bits: an expert's W1 codes are below 2^31 bytes (4 I d < 2^31 is an API limit).
+template <int F_>
 struct DmxGateUp {
-  using P = MxFwdGateUpBig;
-  using Args = P::Args;
-  using Tile = P::Tile;
+  static constexpr int F = F_;
+  using P = MxFwdGateUpBig<F>;
+  using Args = typename P::Args;
+  using Tile = typename P::Tile;
   static constexpr const char* kName = "fwd_gateup_big";
   static MOE_DEV int ntiles(const Args& a) { return P::ntiles(a); }
   static MOE_DEV Tile decode(const Args& a, int lt) { return P::decode(a, lt); }
   static MOE_DEV int brow(int wn, int nb) { return P::brow(wn, nb); }
   static MOE_DEV void src(const Args& a, const Tile& t, int wave, int lane, DmxSrc& s) {
     const int d = a.d, I = a.I, kA = P::kA;
+    const int pb = d * F / 8;  // bytes of codes per row
     auto wrow = [&](int r) { return r < kA ? t.n0 + r : I + t.n0 + r - kA; };
-    s.nk = d / 128;
+    s.nk = d / P::G::BK;
     s.k0 = 0;
-    s.ra = raw_rsrc(a.xp8 + (size_t)t.m.row0 * d);
-    s.rb = raw_rsrc(a.w8 + (size_t)t.m.e * 2 * I * d);
+    s.ra = raw_rsrc(a.xp8 + (size_t)t.m.row0 * pb);
+    s.rb = raw_rsrc(a.w8 + (size_t)t.m.e * 2 * I * pb);
     // load j's rows are 8 j further on, in the same half of the B tile (gate or up)
     const int row = dma_row(wave, 0, lane);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s.ao[j] = (uint32_t)(row + 8 * j) * d + dma_piece(lane);
-    s.bo = (uint32_t)wrow(row) * d + dma_piece(lane);
-    s.bst = 8u * (uint32_t)d;
+    for (int j = 0; j < 4; ++j) s.ao[j] = (uint32_t)(row + 8 * j) * pb + dma_piece(lane);
+    s.bo = (uint32_t)wrow(row) * pb + dma_piece(lane);
+    s.bst = 8u * (uint32_t)pb;
     const int r = 64 * (wave % 4) + lane;
     if (wave < 4) {
       s.rs = raw_rsrc(a.xps + (size_t)t.m.row0 * (d / 32));
@@ -1538,27 +1559,29 @@ struct DmxGateUp {
   }
 };
 
-// Problem 2 (MXFP8) on full 256-row blocks: A codes (pitch I) against W2[e]'s codes, rows n0..
-// (pitch I); each n-tile starts at its own K chunk, as in the 128-row kernel.
+// Problem 2 (MX) on full 256-row blocks: A codes (pitch I F / 8 bytes) against W2[e]'s codes,
+// rows n0.. (same pitch); each n-tile starts at its own K chunk, as in the 128-row kernel.
+template <int F_>
 struct DmxDown {
-  using P = MxFwdDownBig;
-  using Args = P::Args;
-  using Tile = P::Tile;
+  static constexpr int F = F_;
+  using P = MxFwdDownBig<F>;
+  using Args = typename P::Args;
+  using Tile = typename P::Tile;
   static constexpr const char* kName = "fwd_down_big";
   static MOE_DEV int ntiles(const Args& a) { return P::ntiles(a); }
   static MOE_DEV Tile decode(const Args& a, int lt) { return P::decode(a, lt); }
   static MOE_DEV int brow(int wn, int nb) { return P::brow(wn, nb); }
   static MOE_DEV void src(const Args& a, const Tile& t, int wave, int lane, DmxSrc& s) {
-    const int I = a.I;
-    s.nk = I / 128;
+    const int I = a.I, pb = I * F / 8;
+    s.nk = I / P::G::BK;
     s.k0 = P::k_first(t, s.nk);
-    s.ra = raw_rsrc(a.aq + (size_t)t.m.row0 * I);
-    s.rb = raw_rsrc(a.w8 + ((size_t)t.m.e * a.d + t.n0) * I);
+    s.ra = raw_rsrc(a.aq + (size_t)t.m.row0 * pb);
+    s.rb = raw_rsrc(a.w8 + ((size_t)t.m.e * a.d + t.n0) * pb);
     const int row = dma_row(wave, 0, lane);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s.ao[j] = (uint32_t)(row + 8 * j) * I + dma_piece(lane);
-    s.bo = (uint32_t)row * I + dma_piece(lane);
-    s.bst = 8u * (uint32_t)I;
+    for (int j = 0; j < 4; ++j) s.ao[j] = (uint32_t)(row + 8 * j) * pb + dma_piece(lane);
+    s.bo = (uint32_t)row * pb + dma_piece(lane);
+    s.bst = 8u * (uint32_t)pb;
     const int r = 64 * (wave % 4) + lane;
     s.rs = wave < 4 ? raw_rsrc(a.aqs + (size_t)t.m.row0 * (I / 32))
                     : raw_rsrc(a.ws + ((size_t)t.m.e * a.d + t.n0) * (I / 32));
@@ -1569,27 +1592,29 @@ struct DmxDown {
   }
 };
 
-// Problem 4 (MXFP8) on full 256-row blocks: dH codes (pitch 2I) against W1[e]'s transposed
-// codes ([d, 2I], rows n0..).
+// Problem 4 (MX) on full 256-row blocks: dH codes (pitch 2I F / 8 bytes) against W1[e]'s
+// transposed codes ([d, 2I], rows n0..).
+template <int F_>
 struct DmxGateDgrad {
-  using P = MxBwdGateDgradBig;
-  using Args = P::Args;
-  using Tile = P::Tile;
+  static constexpr int F = F_;
+  using P = MxBwdGateDgradBig<F>;
+  using Args = typename P::Args;
+  using Tile = typename P::Tile;
   static constexpr const char* kName = "bwd_gate_dgrad_big";
   static MOE_DEV int ntiles(const Args& a) { return P::ntiles(a); }
   static MOE_DEV Tile decode(const Args& a, int lt) { return P::decode(a, lt); }
   static MOE_DEV int brow(int wn, int nb) { return P::brow(wn, nb); }
   static MOE_DEV void src(const Args& a, const Tile& t, int wave, int lane, DmxSrc& s) {
-    const int twoI = 2 * a.I;
-    s.nk = twoI / 128;
+    const int twoI = 2 * a.I, pb = twoI * F / 8;
+    s.nk = twoI / P::G::BK;
     s.k0 = 0;
-    s.ra = raw_rsrc(a.dhq + (size_t)t.m.row0 * twoI);
-    s.rb = raw_rsrc(a.w8 + ((size_t)t.m.e * a.d + t.n0) * twoI);
+    s.ra = raw_rsrc(a.dhq + (size_t)t.m.row0 * pb);
+    s.rb = raw_rsrc(a.w8 + ((size_t)t.m.e * a.d + t.n0) * pb);
     const int row = dma_row(wave, 0, lane);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s.ao[j] = (uint32_t)(row + 8 * j) * twoI + dma_piece(lane);
-    s.bo = (uint32_t)row * twoI + dma_piece(lane);
-    s.bst = 8u * (uint32_t)twoI;
+    for (int j = 0; j < 4; ++j) s.ao[j] = (uint32_t)(row + 8 * j) * pb + dma_piece(lane);
+    s.bo = (uint32_t)row * pb + dma_piece(lane);
+    s.bst = 8u * (uint32_t)pb;
     const int r = 64 * (wave % 4) + lane;
     s.rs = wave < 4 ? raw_rsrc(a.dhs + (size_t)t.m.row0 * (twoI / 32))
                     : raw_rsrc(a.ws + ((size_t)t.m.e * a.d + t.n0) * (twoI / 32));
@@ -1604,8 +1629,10 @@ struct DmxGateDgrad {
 // W2[e]'s transposed codes ([I, d], rows n0..). The epilogue is the 128-row kernel's per 32-block
 // of I columns (a wave's 64 columns are two), and the router-weight partials of each 128-column
 // half are the sums of its two waves' row sums, as in the BF16 256 x 256 kernel.
+template <int F_>
 struct DmxDownDgrad {
-  using Args = MxBwdDownDgradS<8, true>::Args;
+  static constexpr int F = F_;
+  using Args = typename MxBwdDownDgradS<F, true>::Args;
   using Tile = DgradTile;
   static constexpr const char* kName = "bwd_down_dgrad_big";
   static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.I / 256); }
@@ -1616,17 +1643,17 @@ struct DmxDownDgrad {
   static MOE_DEV int brow(int wn, int nb) { return wn * 64 + nb * 16; }
   // byte offsets into dY's codes fit 32 bits: T d < 2^31 is an API limit
   static MOE_DEV void src(const Args& a, const Tile& t, int wave, int lane, DmxSrc& s) {
-    const int d = a.d;
-    s.nk = d / 128;
+    const int d = a.d, pb = d * F / 8;
+    s.nk = d / (1024 / F);
     s.k0 = 0;
     s.ra = raw_rsrc(a.dyq);
-    s.rb = raw_rsrc(a.w8 + ((size_t)t.m.e * a.I + t.n0) * d);
+    s.rb = raw_rsrc(a.w8 + ((size_t)t.m.e * a.I + t.n0) * pb);
     const int row = dma_row(wave, 0, lane);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      s.ao[j] = (uint32_t)(a.row_src[t.m.row0 + row + 8 * j] / a.k) * d + dma_piece(lane);
-    s.bo = (uint32_t)row * d + dma_piece(lane);
-    s.bst = 8u * (uint32_t)d;
+      s.ao[j] = (uint32_t)(a.row_src[t.m.row0 + row + 8 * j] / a.k) * pb + dma_piece(lane);
+    s.bo = (uint32_t)row * pb + dma_piece(lane);
+    s.bst = 8u * (uint32_t)pb;
     const int r = 64 * (wave % 4) + lane;
     if (wave < 4) {
       s.rs = raw_rsrc(a.dys);
@@ -1687,14 +1714,14 @@ struct DmxDownDgrad {
           *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + i) = og;
           *reinterpret_cast<uint2*>(a.dH + pos * 2 * I + I + i) = ou;
         }
-        const uint32_t cg = mx_block_code<8>(dgv), cu = mx_block_code<8>(duv);
+        const uint32_t cg = mx_block_code<F>(dgv), cu = mx_block_code<F>(duv);
         const float ig = mx_inv_scale(cg), iu = mx_inv_scale(cu);
-        uint8_t* qp = a.dhq + pos * 2 * I;
+        uint8_t* qp = a.dhq + pos * (2 * I * F / 8);
         const int o = 4 * (lane / 16);
-        mx_put4<8>(qp, c0 + o, mx_pack4<8>(dgv, ig));
-        mx_put4<8>(qp, c0 + 16 + o, mx_pack4<8>(dgv + 4, ig));
-        mx_put4<8>(qp, I + c0 + o, mx_pack4<8>(duv, iu));
-        mx_put4<8>(qp, I + c0 + 16 + o, mx_pack4<8>(duv + 4, iu));
+        mx_put4<F>(qp, c0 + o, mx_pack4<F>(dgv, ig));
+        mx_put4<F>(qp, c0 + 16 + o, mx_pack4<F>(dgv + 4, ig));
+        mx_put4<F>(qp, I + c0 + o, mx_pack4<F>(duv, iu));
+        mx_put4<F>(qp, I + c0 + 16 + o, mx_pack4<F>(duv + 4, iu));
         if (lane < 16) {
           a.dhs[pos * (2 * I / 32) + c0 / 32] = static_cast<uint8_t>(cg);
           a.dhs[pos * (2 * I / 32) + (I + c0) / 32] = static_cast<uint8_t>(cu);
@@ -1839,7 +1866,7 @@ hipError_t launch_bwd_gate_dgrad(const GemmBwdGateDgradArgs& x, bool persistent,
 }
 
 // The 128-row MX kernels, instantiated for both scale-load forms (GeoMx::GS) and picked by the
-// GEMM's K extent; MXFP4 runs every 128-row block on them.
+// GEMM's K extent, and the 256-row ones, each for both code widths.
 template <class T>
 struct Tag {
   using type = T;
@@ -1851,55 +1878,60 @@ hipError_t with_mx(int fbits, int K, Fn&& f) {
   if (fbits == 4) return gs ? f(Tag<P<4, true>>{}) : f(Tag<P<4, false>>{});
   return gs ? f(Tag<P<8, true>>{}) : f(Tag<P<8, false>>{});
 }
+// f(Tag<D<F>>) for the code width fbits
+template <template <int> class D, class Fn>
+hipError_t with_big(int fbits, Fn&& f) {
+  return fbits == 4 ? f(Tag<D<4>>{}) : f(Tag<D<8>>{});
+}
 
-// The MXFP8 forward GEMMs and gate dgrad run the 256-row blocks with dmx_kernel, then the
-// remainders on the 128-row kernels.
+// The MX GEMMs run the 256-row blocks with dmx_kernel, then the remainders on the 128-row
+// kernels.
 hipError_t launch_fwd_gateup_mx(const GemmMxGateUpArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
-  const bool fp4 = x.fbits == 4;
-  if (!fp4) {
-    MxFwdGateUpBig::Args ab{x.xp8, x.xps, x.w8, x.ws, x.H,     x.A,
-                            x.aq,  x.aqs, x.offsets, st.big, x.d, x.I};
-    const hipError_t e = launch_dmx<DmxGateUp>(
-        ab, sched_max_big(x.Tk) * (x.I / MxFwdGateUpBig::kA), true, s);
-    if (e != hipSuccess) return e;
-  }
-  const int mt = fp4 ? sched_max_mtiles(x.Tk, x.E) : sched_max_rem(x.Tk, x.E);
+  hipError_t e = with_big<DmxGateUp>(x.fbits, [&](auto tag) {
+    using D = typename decltype(tag)::type;
+    typename D::Args ab{x.xp8, x.xps, x.w8, x.ws, x.H, x.A, x.aq, x.aqs, x.offsets, st.big,
+                        x.d, x.I};
+    return launch_dmx<D>(ab, sched_max_big(x.Tk) * (x.I / D::P::kA), true, s);
+  });
+  if (e != hipSuccess) return e;
   return with_mx<MxFwdGateUpS>(x.fbits, x.d, [&](auto tag) {
     using P = typename decltype(tag)::type;
-    typename P::Args a{x.xp8, x.xps, x.w8, x.ws, x.H, x.A, x.aq, x.aqs, x.offsets,
-                       fp4 ? st.full : st.rem, x.d, x.I};
-    return launch<P>(a, mt * (x.I / P::kA), persistent, s);
+    typename P::Args a{x.xp8, x.xps, x.w8, x.ws, x.H, x.A, x.aq, x.aqs, x.offsets, st.rem,
+                       x.d, x.I};
+    return launch<P>(a, sched_max_rem(x.Tk, x.E) * (x.I / P::kA), persistent, s);
   });
 }
 
 hipError_t launch_fwd_down_mx(const GemmMxDownArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
-  const bool fp4 = x.fbits == 4;
-  if (!fp4) {
-    MxFwdDownBig::Args ab{x.aq, x.aqs, x.w8, x.ws, x.O, x.offsets, st.big, x.d, x.I};
-    const hipError_t e = launch_dmx<DmxDown>(ab, sched_max_big(x.Tk) * (x.d / 256), true, s);
-    if (e != hipSuccess) return e;
-  }
-  const int mt = fp4 ? sched_max_mtiles(x.Tk, x.E) : sched_max_rem(x.Tk, x.E);
+  hipError_t e = with_big<DmxDown>(x.fbits, [&](auto tag) {
+    using D = typename decltype(tag)::type;
+    typename D::Args ab{x.aq, x.aqs, x.w8, x.ws, x.O, x.offsets, st.big, x.d, x.I};
+    return launch_dmx<D>(ab, sched_max_big(x.Tk) * (x.d / 256), true, s);
+  });
+  if (e != hipSuccess) return e;
   return with_mx<MxFwdDownS>(x.fbits, x.I, [&](auto tag) {
     using P = typename decltype(tag)::type;
-    typename P::Args a{x.aq, x.aqs, x.w8, x.ws, x.O, x.offsets, fp4 ? st.full : st.rem, x.d, x.I};
-    return launch<P>(a, mt * (x.d / 128), persistent, s);
+    typename P::Args a{x.aq, x.aqs, x.w8, x.ws, x.O, x.offsets, st.rem, x.d, x.I};
+    return launch<P>(a, sched_max_rem(x.Tk, x.E) * (x.d / 128), persistent, s);
   });
 }
 
-// With I a multiple of 256 the MXFP8 down dgrad runs the 256-row blocks with dmx_kernel, then
-// the remainders; otherwise every 128-row block on the 128-row kernel.
+// With I a multiple of 256 (always so in MXFP4) the MX down dgrad runs the 256-row blocks with
+// dmx_kernel, then the remainders; otherwise every 128-row block on the 128-row kernel.
 hipError_t launch_bwd_down_dgrad_mx(const GemmMxDownDgradArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
-  const bool big = x.fbits == 8 && x.I % 256 == 0;
+  const bool big = x.I % 256 == 0;
   const int max_big = big ? sched_max_big(x.Tk) * (x.I / 256) : 0;
   if (max_big > 0) {
-    MxBwdDownDgradS<8, true>::Args ab{x.dyq, x.dys,    x.row_src, x.topk_w, x.w8,    x.ws,
-                                      x.H,   x.A,      x.dH,      x.dwpart, x.dhq,   x.dhs,
-                                      x.offsets, st.big, x.d,     x.I,      x.k};
-    const hipError_t e = launch_dmx<DmxDownDgrad>(ab, max_big, true, s);
+    const hipError_t e = with_big<DmxDownDgrad>(x.fbits, [&](auto tag) {
+      using D = typename decltype(tag)::type;
+      typename D::Args ab{x.dyq,    x.dys, x.row_src, x.topk_w, x.w8, x.ws,
+                          x.H,      x.A,   x.dH,      x.dwpart, x.dhq, x.dhs,
+                          x.offsets, st.big, x.d,     x.I,      x.k};
+      return launch_dmx<D>(ab, max_big, true, s);
+    });
     if (e != hipSuccess) return e;
   }
   const int mt = big ? sched_max_rem(x.Tk, x.E) : sched_max_mtiles(x.Tk, x.E);
@@ -1914,19 +1946,16 @@ hipError_t launch_bwd_down_dgrad_mx(const GemmMxDownDgradArgs& x, bool persisten
 
 hipError_t launch_bwd_gate_dgrad_mx(const GemmMxGateDgradArgs& x, bool persistent, hipStream_t s) {
   const SchedTables st = sched_tables(x.sched, x.Tk, x.E);
-  const bool fp4 = x.fbits == 4;
-  if (!fp4) {
-    MxBwdGateDgradBig::Args ab{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, st.big, x.d, x.I};
-    const hipError_t e =
-        launch_dmx<DmxGateDgrad>(ab, sched_max_big(x.Tk) * (x.d / 256), true, s);
-    if (e != hipSuccess) return e;
-  }
-  const int mt = fp4 ? sched_max_mtiles(x.Tk, x.E) : sched_max_rem(x.Tk, x.E);
+  hipError_t e = with_big<DmxGateDgrad>(x.fbits, [&](auto tag) {
+    using D = typename decltype(tag)::type;
+    typename D::Args ab{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, st.big, x.d, x.I};
+    return launch_dmx<D>(ab, sched_max_big(x.Tk) * (x.d / 256), true, s);
+  });
+  if (e != hipSuccess) return e;
   return with_mx<MxBwdGateDgradS>(x.fbits, 2 * x.I, [&](auto tag) {
     using P = typename decltype(tag)::type;
-    typename P::Args a{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, fp4 ? st.full : st.rem, x.d,
-                       x.I};
-    return launch<P>(a, mt * (x.d / 128), persistent, s);
+    typename P::Args a{x.dhq, x.dhs, x.w8, x.ws, x.dXp, x.offsets, st.rem, x.d, x.I};
+    return launch<P>(a, sched_max_rem(x.Tk, x.E) * (x.d / 128), persistent, s);
   });
 }
 

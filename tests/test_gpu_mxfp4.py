@@ -154,10 +154,11 @@ def test_mxfp4_layer_parity(case):
 
 
 def test_mxfp4_expert_sizes_at_tile_boundaries_and_determinism():
-    """Experts of 0, 1, 127, 128, 129, 255, 256, 257 and 384 rows (the 128-row tiles and their
-    ragged last tile), d = 512 and I = 512 (two K steps of 256 along I, several column tiles):
-    parity against the MXFP4 oracle, persistent grids bitwise equal to one-shot grids, and a
-    second backward with accumulate doubling both weight gradients exactly."""
+    """Experts of 0, 1, 127, 128, 129, 255, 256, 257 and 384 rows (full 256-row blocks on the
+    direct-to-LDS kernels, 128-row remainder tiles and their ragged last tile), d = 512 and
+    I = 512 (two K steps of 256 along d and I, several column tiles): parity against the MXFP4
+    oracle, persistent grids bitwise equal to one-shot grids, and a second backward with
+    accumulate doubling both weight gradients exactly."""
     counts = [255, 256, 257, 0, 127, 128, 129, 1, 384]
     _announce(f"[mxfp4] expert sizes {counts}, d=512 I=512 k=1")
     E, d, I = len(counts), 512, 512
