@@ -164,3 +164,29 @@ def test_mxfp4_layer_stays_within_its_error_bound_of_the_exact_layer(seed):
                        ("dWr", bm["dWr"], be["dWr"])):
         r = rel(a, b)
         assert 0.05 < r < 0.5, (name, r)
+
+
+@pytest.mark.parametrize("precision, qdq, bound", [("mxfp8", mx.qdq, 0.05), ("mxfp4", mx.qdq4, 0.2)])
+def test_mx_dwr_reads_the_ring_image_of_x_and_its_distance_from_the_exact_product(precision, qdq,
+                                                                                   bound):
+    """In the MX modes dWr = dlogits^T Xq, Xq being the MX image of X that the ring holds (the
+    readings "mxfp8", "mxfp4"), not dlogits^T X. This pins that it is exactly that product (on
+    the oracle's own dlogits) and states how far it is from the exact one: the relative
+    Frobenius distance is the MX quantisation error of X carried through one product, about
+    0.02 (E4M3) and 0.11 (E2M1) on Gaussian tokens."""
+    rng = np.random.default_rng(11)
+    T, d, E, k, I = 64, 256, 8, 2, 64
+    X = oracle.bf16_round(rng.standard_normal((T, d)))
+    W1 = oracle.bf16_round(rng.standard_normal((E, 2 * I, d)) * 0.05)
+    W2 = oracle.bf16_round(rng.standard_normal((E, d, I)) * 0.05)
+    Wr = oracle.bf16_round(rng.standard_normal((E, d)) * 0.05)
+    dY = oracle.bf16_round(rng.standard_normal((T, d)))
+    f = oracle.forward(X, W1, W2, Wr=Wr, k=k, precision=precision)
+    b = oracle.backward(f, X, W1, W2, dY, Wr=Wr)
+    dl = b["dlogits"]
+    np.testing.assert_allclose(b["dWr"], dl.T @ qdq(X), rtol=1e-12, atol=1e-15)
+    exact = dl.T @ X
+    dist = np.linalg.norm(b["dWr"] - exact) / np.linalg.norm(exact)
+    eps_x = np.linalg.norm(qdq(X) - X) / np.linalg.norm(X)
+    print(f"  {precision}: dWr vs dlogits^T X: rel fro {dist:.3e} (X's MX error {eps_x:.3e})")
+    assert 0.3 * eps_x < dist < bound, (dist, eps_x)
