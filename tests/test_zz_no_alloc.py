@@ -1,9 +1,9 @@
 """moe_permute_static (no workspace, no allocation) against moe_permute, through the C ABI.
 
 Two calls in a row share the library's fixed scratch: the second one is smaller and must not
-see anything the first one left there. Then an MXFP8 call. Every output is compared bit for bit
-with moe_permute's on the same inputs: counts, offsets, both permutation maps, the ring slot's
-contents and the device status word.
+see anything the first one left there. Then an MXFP8 and an MXFP4 call. Every output is
+compared bit for bit with moe_permute's on the same inputs: counts, offsets, both permutation
+maps, the ring slot's contents and the device status word.
 """
 import numpy as np
 import pytest
@@ -63,10 +63,13 @@ def test_static_permute_matches_moe_permute_on_two_calls_in_a_row():
     _compare(L2, x2, slot=1)
 
 
-def test_static_permute_mxfp8_and_bad_index():
-    _announce("[no-alloc] MXFP8 T=300 E=8 k=2 d=256; then a bad expert index")
+def test_static_permute_mx_modes_and_bad_index():
+    _announce("[no-alloc] MXFP8 T=300 E=8 k=2 d=256; MXFP4 T=200 E=8 k=2 d=512; then a bad "
+              "expert index")
     L, x = _layer(300, 256, 8, 2, 128, seed=3, precision=m.MOE_PREC_MXFP8)
     _compare(L, x)
+    L4, x4 = _layer(200, 512, 8, 2, 256, seed=5, precision=m.MOE_PREC_MXFP4)
+    _compare(L4, x4)
     L2, x2 = _layer(64, 256, 4, 1, 128, seed=4)
     idx = L2.topk_idx.clone()
     idx[10, 0] = 9
