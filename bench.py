@@ -702,10 +702,9 @@ def run_layer(m, MoeLayer, inp, cfg, stream, args, mx, persistent=False, trace=T
             tot[n] = tot.get(n, 0.0) + ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3
             cnt[n] = cnt.get(n, 0) + 1
         # A step's work of one kind may take several launches (the GEMMs run their 256-row
-        # blocks and their remainders as two, "<name>_big" and "<name>"; the MXFP8 gate wgrad
-        # also expands the big experts' fp8 rows, and the MXFP4 one every Xp row,
-        # "<name>_expand"): a kernel's `us` is its time per step, summed over them, and `parts`
-        # splits it.
+        # blocks and their remainders as two, "<name>_big" and "<name>"; in the MX modes the
+        # gate wgrad also expands the big experts' Xp rows, "<name>_expand"): a kernel's `us`
+        # is its time per step, summed over them, and `parts` splits it.
         parts = {}
         for n in list(tot):
             base = n

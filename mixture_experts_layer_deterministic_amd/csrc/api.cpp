@@ -592,26 +592,13 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
                         wg_count + 1, E, d, I, accumulate, bdw, false, "bwd_down_wgrad",
                         "wgrad_sched_down"},
                        s));
-      if (Y.fb == 4) {
-        // MXFP4: the dXp buffer first holds the bf16 image of every Xp row, which the gate
-        // wgrad and dWr read, before the gate dgrad writes dXp into it
-        if (!L.err) L(launch_expand_fp4(xp8, xps, Tk, d, dXp, "bwd_gate_wgrad_expand", s));
-        if (!L.err)
-          L(launch_wgrad({dH, dXp, nullptr, nullptr, dw1, offsets,
-                          at<int4>(workspace, Y.wg_table1), wg_count, E, 2 * I, d, accumulate,
-                          bdw, true, "bwd_gate_wgrad", "wgrad_sched_gate"},
-                         s));
-        if (!L.err && routed)
-          L(launch_dwr(dl_pos, dXp, nullptr, nullptr, offsets, E, d, dwr, accumulate, s));
-      } else {
-        // the gate wgrad goes first: until the gate dgrad writes dXp, that buffer holds the
-        // bf16 image of the big experts' fp8 Xp rows for the big-expert wgrad kernel
-        if (!L.err)
-          L(launch_wgrad({dH, nullptr, xp8, xps, dw1, offsets, at<int4>(workspace, Y.wg_table1),
-                          wg_count, E, 2 * I, d, accumulate, bdw, true, "bwd_gate_wgrad",
-                          "wgrad_sched_gate", dXp},
-                         s));
-      }
+      // the gate wgrad goes first: until the gate dgrad writes dXp, that buffer holds the bf16
+      // image of the big experts' MX Xp rows for the big-expert wgrad kernel
+      if (!L.err)
+        L(launch_wgrad({dH, nullptr, xp8, xps, dw1, offsets, at<int4>(workspace, Y.wg_table1),
+                        wg_count, E, 2 * I, d, accumulate, bdw, true, "bwd_gate_wgrad",
+                        "wgrad_sched_gate", dXp, Y.fb},
+                       s));
     }
     if (!L.err)
       L(launch_bwd_gate_dgrad_mx({dhq, dhs, at<uint8_t>(wq, Y.w1b), at<uint8_t>(wq, Y.w1bs), dXp,
@@ -641,8 +628,7 @@ int moe_backward(const moe_cfg* cfg, const void* ring, size_t ring_bytes, int32_
     L(launch_uncombine(dXp, tk_row, topk_idx, dl_pos,
                        routed ? static_cast<const uint16_t*>(w_router) : nullptr, cfg->T, k, d,
                        static_cast<uint16_t*>(dx), s));
-  if (!L.err && routed && Y.fb != 4)
-    L(launch_dwr(dl_pos, xp, xp8, xps, offsets, E, d, dwr, accumulate, s));
+  if (!L.err && routed) L(launch_dwr(dl_pos, xp, xp8, xps, Y.fb, offsets, E, d, dwr, accumulate, s));
   return L.status();
 }
 

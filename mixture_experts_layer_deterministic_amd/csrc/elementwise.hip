@@ -163,9 +163,10 @@ __global__ void __launch_bounds__(256) uncombine_kernel(
 // dWr[e, c] = sum over positions p of expert e of dl_pos[p] * Xp[p, c] (fp32). Block (cx, e)
 // covers columns [512 cx, 512 cx + 512); each lane owns 8 columns. The expert's positions are
 // split into four contiguous quarters, one per wave, each summed in ascending p; the quarters
-// are then added in order ((q0 + q1) + q2) + q3, so the result is the same on every run. MX
-// reads Xp as its MXFP8 image (codes xp8, one scale per 32 columns in xps).
-template <bool MX>
+// are then added in order ((q0 + q1) + q2) + q3, so the result is the same on every run. F = 8
+// reads Xp as its MXFP8 image (E4M3 codes xp8, one scale per 32 columns in xps), F = 4 as its
+// MXFP4 image (E2M1 codes, two a byte), F = 0 as bf16 rows xp.
+template <int F>
 __global__ void __launch_bounds__(256) dwr_kernel(const float* __restrict__ dl_pos,
                                                   const uint16_t* __restrict__ xp,
                                                   const uint8_t* __restrict__ xp8,
@@ -192,13 +193,19 @@ __global__ void __launch_bounds__(256) dwr_kernel(const float* __restrict__ dl_p
       const int p = pg + u;
       const bool live = col && p < q1;
       dl[u] = live ? dl_pos[p] : 0.f;
-      if constexpr (MX) {
+      if constexpr (F == 8) {
         typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
         const u32x2 q2 = live ? __builtin_nontemporal_load(
                                     reinterpret_cast<const u32x2*>(xp8 + (size_t)p * d + c0))
                               : u32x2{0u, 0u};
         const uint2 q = make_uint2(q2[0], q2[1]);
         raw[u] = make_uint4(q.x, q.y, 0, 0);
+        sc[u] = live ? xps[(size_t)p * (d / 32) + c0 / 32] : 0u;
+      } else if constexpr (F == 4) {
+        const uint32_t q = live ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(
+                                      xp8 + (size_t)p * (d / 2) + c0 / 2))
+                                : 0u;
+        raw[u] = make_uint4(q, 0, 0, 0);
         sc[u] = live ? xps[(size_t)p * (d / 32) + c0 / 32] : 0u;
       } else {
         raw[u] = live ? nt_load16(xp + (size_t)p * d + c0) : make_uint4(0, 0, 0, 0);
@@ -209,7 +216,7 @@ __global__ void __launch_bounds__(256) dwr_kernel(const float* __restrict__ dl_p
     for (int u = 0; u < U; ++u) {
       if (pg + u >= q1) break;
       float xv[8];
-      if constexpr (MX) {
+      if constexpr (F == 8) {
         const float s = mx_scale(sc[u]);
         float f[4], g[4];
         e4m3x4_to_f32(raw[u].x, f);
@@ -219,6 +226,12 @@ __global__ void __launch_bounds__(256) dwr_kernel(const float* __restrict__ dl_p
           xv[q4] = f[q4] * s;
           xv[4 + q4] = g[q4] * s;
         }
+      } else if constexpr (F == 4) {
+        const float s = mx_scale(sc[u]);
+        const float2 f0 = e2m1x2_to_f32<0>(raw[u].x), f1 = e2m1x2_to_f32<1>(raw[u].x),
+                     f2 = e2m1x2_to_f32<2>(raw[u].x), f3 = e2m1x2_to_f32<3>(raw[u].x);
+        xv[0] = f0.x * s, xv[1] = f0.y * s, xv[2] = f1.x * s, xv[3] = f1.y * s;
+        xv[4] = f2.x * s, xv[5] = f2.y * s, xv[6] = f3.x * s, xv[7] = f3.y * s;
       } else {
         const uint32_t gw[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
@@ -304,16 +317,20 @@ hipError_t launch_uncombine(const uint16_t* dXp, const int32_t* tk_row, const in
 }
 
 hipError_t launch_dwr(const float* dl_pos, const uint16_t* xp, const uint8_t* xp8,
-                      const uint8_t* xps, const int32_t* offsets, int E, int d, float* dwr,
-                      int accumulate, hipStream_t s) {
+                      const uint8_t* xps, int fbits, const int32_t* offsets, int E, int d,
+                      float* dwr, int accumulate, hipStream_t s) {
   {
     TraceScope trace("dwr", s);
-    if (xp8)
-      hipLaunchKernelGGL(dwr_kernel<true>, dim3((d + 511) / 512, E), dim3(256), 0, s, dl_pos, xp,
-                         xp8, xps, offsets, d, dwr, accumulate);
+    const dim3 grid((d + 511) / 512, E);
+    if (xp8 && fbits == 4)
+      hipLaunchKernelGGL(dwr_kernel<4>, grid, dim3(256), 0, s, dl_pos, xp, xp8, xps, offsets, d,
+                         dwr, accumulate);
+    else if (xp8)
+      hipLaunchKernelGGL(dwr_kernel<8>, grid, dim3(256), 0, s, dl_pos, xp, xp8, xps, offsets, d,
+                         dwr, accumulate);
     else
-      hipLaunchKernelGGL(dwr_kernel<false>, dim3((d + 511) / 512, E), dim3(256), 0, s, dl_pos, xp,
-                         xp8, xps, offsets, d, dwr, accumulate);
+      hipLaunchKernelGGL(dwr_kernel<0>, grid, dim3(256), 0, s, dl_pos, xp, xp8, xps, offsets, d,
+                         dwr, accumulate);
   }
   return hipGetLastError();
 }

@@ -190,7 +190,7 @@ constexpr int kWgradTaskSteps = 64;   // K-steps of 32 positions per task (targe
 struct WgradArgs {
   const uint16_t* L;  // [T*k, Mdim], position-major
   const uint16_t* R;  // [T*k, Ndim], position-major (bf16), or null when R8 is given
-  const uint8_t* R8;  // MXFP8 R: codes [T*k, Ndim] (gate wgrad only), or null
+  const uint8_t* R8;  // MX R (gate wgrad only): codes [T*k, Ndim * rbits / 8], or null
   const uint8_t* R8s; // its scales [T*k, Ndim/32]
   void* dw;           // [E, Mdim, Ndim], fp32 or (bf16_dw) bf16
   const int32_t* offsets;
@@ -200,9 +200,10 @@ struct WgradArgs {
   bool gate;  // dW1 (true) or dW2 (false)
   const char* name;
   const char* name_sched;
-  // with an fp8 R: bf16 scratch [T*k, Ndim] for the exact bf16 image of the big experts' R rows
+  // with an MX R: bf16 scratch [T*k, Ndim] for the exact bf16 image of the big experts' R rows
   // (they then run on the big-expert kernel), or null (every expert on the task kernel)
   uint16_t* Rx = nullptr;
+  int rbits = 8;  // an MX R's codes: 8 (E4M3) or 4 (E2M1)
 };
 size_t wgrad_table_entries(int Tk, int E, int Mdim, int Ndim);
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
@@ -215,9 +216,6 @@ hipError_t launch_quant_rows(const uint16_t* src, long long rows, int cols, uint
 hipError_t launch_quant_weight(const uint16_t* src, int B, int R, int C, uint8_t* dq,
                                uint8_t* dqs, uint8_t* tq, uint8_t* tqs, int fbits,
                                const char* name, hipStream_t s);
-// The exact bf16 image of MXFP4 rows: codes q [rows, cols / 2], scales qs [rows, cols / 32].
-hipError_t launch_expand_fp4(const uint8_t* q, const uint8_t* qs, long long rows, int cols,
-                             uint16_t* out, const char* name, hipStream_t s);
 // MXFP8 weight gradients: expert segments padded to kSegK positions (segment offsets poff
 // [E + 1], the padded total in poff[E] <= seg_capacity), and an operand S [T*k, C] quantised
 // along each segment's positions into q [C][P] codes and qs [C][P / 32] scales.
@@ -265,8 +263,9 @@ hipError_t launch_uncombine(const uint16_t* dXp, const int32_t* tk_row, const in
                             const float* dl_pos, const uint16_t* wr, int T, int k, int d,
                             uint16_t* dx, hipStream_t s);
 // With xp8 non-null, Xp is read as MXFP8 (codes xp8, scales xps) instead of bf16 xp.
+// Xp as bf16 rows xp, or (xp8 given) as MX codes xp8 with scales xps: fbits 8 E4M3, 4 E2M1.
 hipError_t launch_dwr(const float* dl_pos, const uint16_t* xp, const uint8_t* xp8,
-                      const uint8_t* xps, const int32_t* offsets, int E, int d, float* dwr,
-                      int accumulate, hipStream_t s);
+                      const uint8_t* xps, int fbits, const int32_t* offsets, int E, int d,
+                      float* dwr, int accumulate, hipStream_t s);
 
 }  // namespace moe

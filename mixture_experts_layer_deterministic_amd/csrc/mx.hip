@@ -419,35 +419,6 @@ hipError_t launch_quant_weight(const uint16_t* src, int B, int R, int C, uint8_t
   return hipGetLastError();
 }
 
-// The exact bf16 image of MXFP4 rows (E2M1 codes times their block's scale): thread v expands
-// elements [8 v, 8 v + 8) of the flattened array, 4 bytes of codes, into one 16-byte store.
-__global__ void __launch_bounds__(256) expand_fp4_kernel(const uint8_t* __restrict__ q,
-                                                         const uint8_t* __restrict__ qs,
-                                                         uint16_t* __restrict__ out,
-                                                         long long nvec) {
-  const long long v = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (v >= nvec) return;
-  const uint32_t c = reinterpret_cast<const uint32_t*>(q)[v];
-  const float s = mx_scale(qs[v / 4]);
-  const float2 f0 = e2m1x2_to_f32<0>(c), f1 = e2m1x2_to_f32<1>(c), f2 = e2m1x2_to_f32<2>(c),
-               f3 = e2m1x2_to_f32<3>(c);
-  reinterpret_cast<uint4*>(out)[v] =
-      make_uint4(pack_bf2(f0.x * s, f0.y * s), pack_bf2(f1.x * s, f1.y * s),
-                 pack_bf2(f2.x * s, f2.y * s), pack_bf2(f3.x * s, f3.y * s));
-}
-
-hipError_t launch_expand_fp4(const uint8_t* q, const uint8_t* qs, long long rows, int cols,
-                             uint16_t* out, const char* name, hipStream_t s) {
-  const long long nvec = rows * cols / 8;
-  if (nvec == 0) return hipSuccess;
-  {
-    TraceScope trace(name, s);
-    hipLaunchKernelGGL(expand_fp4_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0, s,
-                       q, qs, out, nvec);
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_scale_gather(const uint16_t* dy, const int32_t* tk_row, const float* topk_w,
                                int T, int k, int d, uint16_t* dyw, hipStream_t s) {
   const long long nvec = (long long)T * d / 8;

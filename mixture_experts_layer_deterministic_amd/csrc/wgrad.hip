@@ -54,8 +54,8 @@ constexpr int R_STAGE = BN * LDR;   // uint16 elements per R stage
 
 struct Args {
   const uint16_t* L;  // [T*k, Mdim]
-  const uint16_t* R;  // [T*k, Ndim] bf16, or (R8) fp8 codes R8 [T*k, Ndim] with scales R8s
-  const uint8_t* R8;
+  const uint16_t* R;  // [T*k, Ndim] bf16, or null when R is MX: codes R8, scales R8s
+  const uint8_t* R8;  // [T*k, Ndim * F / 8]: E4M3 (F = 8) or packed E2M1 (F = 4) codes
   const uint8_t* R8s; // [T*k, Ndim/32]
   void* dw;           // [E, Mdim, Ndim], fp32 or (BF kernels) bf16
   const int32_t* offsets;
@@ -71,15 +71,16 @@ struct Args {
 template <int NH>
 struct Mover {
   const uint16_t* base;  // operand base, already offset to the task's first column
-  const uint8_t* base8;  // fp8 operand: codes and per-32 scales (FP8 loads only)
+  const uint8_t* base8;  // MX operand: codes and per-32 scales (MX loads only)
   const uint8_t* sc8;
   int ld;                // row pitch of the operand (elements)
   uint4 r[NH][4];
 
-  // FP8: the operand is MXFP8 (E4M3 codes with one scale per 32 along the row). The load keeps
-  // the raw codes (x, y) and the scale code (z) of each 8-column piece; `store` expands them to
-  // their exact bf16 values, so the conversion waits for data only when the chunk is written.
-  template <bool FP8 = false>
+  // RF = 8: the operand is MXFP8 (E4M3 codes with one scale per 32 along the row); RF = 4:
+  // MXFP4 (E2M1 codes, two a byte). The load keeps the raw codes (x, and y for E4M3) and the
+  // scale code (z) of each 8-column piece; `store` expands them to their exact bf16 values, so
+  // the conversion waits for data only when the chunk is written. RF = 0: bf16.
+  template <int RF = 0>
   MOE_DEV void load(int pbase, int p1, int col0, int lane) {
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -87,16 +88,20 @@ struct Mover {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int p = pbase + kq * 4 + rr;
-        if constexpr (!FP8) {
+        if constexpr (RF == 0) {
           r[h][rr] = p < p1 ? *reinterpret_cast<const uint4*>(base + (size_t)p * ld + col0 + mb * 8)
                             : make_uint4(0, 0, 0, 0);
         } else {
           uint4 v = make_uint4(0, 0, 0, 0);
           if (p < p1) {
             const int c = col0 + mb * 8;
-            const uint2 q = *reinterpret_cast<const uint2*>(base8 + (size_t)p * ld + c);
-            v.x = q.x;
-            v.y = q.y;
+            if constexpr (RF == 8) {
+              const uint2 q = *reinterpret_cast<const uint2*>(base8 + (size_t)p * ld + c);
+              v.x = q.x;
+              v.y = q.y;
+            } else {
+              v.x = *reinterpret_cast<const uint32_t*>(base8 + (size_t)p * (ld / 2) + c / 2);
+            }
             v.z = sc8[(size_t)p * (ld / 32) + c / 32];
           }
           r[h][rr] = v;
@@ -116,15 +121,32 @@ struct Mover {
     v.w = pack_bf2(g[2] * s, g[3] * s);
     return v;
   }
+  static MOE_DEV uint4 expand_fp4(const uint4 raw) {
+    const float s = mx_scale(raw.z);
+    const float2 f0 = e2m1x2_to_f32<0>(raw.x), f1 = e2m1x2_to_f32<1>(raw.x),
+                 f2 = e2m1x2_to_f32<2>(raw.x), f3 = e2m1x2_to_f32<3>(raw.x);
+    uint4 v;
+    v.x = pack_bf2(f0.x * s, f0.y * s);
+    v.y = pack_bf2(f1.x * s, f1.y * s);
+    v.z = pack_bf2(f2.x * s, f2.y * s);
+    v.w = pack_bf2(f3.x * s, f3.y * s);
+    return v;
+  }
+  template <int RF>
+  static MOE_DEV uint4 expand(const uint4 raw) {
+    if constexpr (RF == 8) return expand_fp8(raw);
+    else if constexpr (RF == 4) return expand_fp4(raw);
+    else return raw;
+  }
   // Writes the transposed blocks into an LDS buffer [MN][ldk] at K column kcol.
-  template <bool FP8 = false>
+  template <int RF = 0>
   MOE_DEV void store(uint16_t* s, int ldk, int kcol, int lane) const {
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const int b = lane + kWave * h, kq = b % 8, mb = b / 8;
       uint4 e[4];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) e[rr] = FP8 ? expand_fp8(r[h][rr]) : r[h][rr];
+      for (int rr = 0; rr < 4; ++rr) e[rr] = expand<RF>(r[h][rr]);
       const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&e[0]);
       const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&e[1]);
       const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&e[2]);
@@ -190,9 +212,9 @@ MOE_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::
 // c - 1, so every load has kProducers - 1 iterations to arrive. Producers and consumers run
 // separate loops with the same number of barriers per task (1 + nt * nk); the role is a
 // wave-uniform scalar, so each wave branches over the other role's code.
-// GATE only separates the two instances (dW1 and dW2) for profilers. R8: R is MXFP8. BF: dW is
-// stored as bf16.
-template <bool ACC, bool GATE, bool R8, bool BF>
+// GATE only separates the two instances (dW1 and dW2) for profilers. RF: R is bf16 (0), MXFP8
+// (8) or MXFP4 (4). BF: dW is stored as bf16.
+template <bool ACC, bool GATE, int RF, bool BF>
 __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Args a,
                                                            const int4* __restrict__ table,
                                                            const int32_t* __restrict__ offsets,
@@ -264,10 +286,10 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
       // chunk pq: loads now; chunk 0 is written before the first barrier
       if (pq < total) {
         const int pb = p0 + (pq % nk) * BK;
-        mr.load<R8>(pb, p1, t.col(pq / nk, ntn), lane);
+        mr.load<RF>(pb, p1, t.col(pq / nk, ntn), lane);
         if (!resident) ml.load(pb, p1, 0, lane);
         if (pq == 0) {
-          mr.store<R8>(rbuf, LDR, 0, lane);
+          mr.store<RF>(rbuf, LDR, 0, lane);
           if (!resident) ml.store(lbuf, LDL, 0, lane);
         }
       }
@@ -275,13 +297,13 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) wgrad_kernel(const Ar
       for (int it = 0; it < total; ++it) {
         const int c = it + 1;
         if (c < total && c % kProducers == pq) {  // its loads were issued kProducers - 1 ago
-          mr.store<R8>(rbuf + (c & 1) * R_STAGE, LDR, 0, lane);
+          mr.store<RF>(rbuf + (c & 1) * R_STAGE, LDR, 0, lane);
           if (!resident) ml.store(lbuf, LDL, (c & 1) * BK, lane);
         }
         const int cn = it + kProducers;
         if (it % kProducers == pq && cn < total) {
           const int pb = p0 + (cn % nk) * BK;
-          mr.load<R8>(pb, p1, t.col(cn / nk, ntn), lane);
+          mr.load<RF>(pb, p1, t.col(cn / nk, ntn), lane);
           if (!resident) ml.load(pb, p1, 0, lane);
         }
         lds_barrier();
@@ -485,9 +507,11 @@ struct DmaWgrad {
   }
 };
 
-// The exact bf16 image (codes times their scale, as Mover::expand_fp8 makes it) of the rows
-// of the listed big experts of an MXFP8 operand, at the same row positions. One thread per
-// 8-column piece, grid-stride over each expert's rows in turn.
+// The exact bf16 image (codes times their scale, as Mover::expand makes it) of the rows of the
+// listed big experts of an MX operand (F = 8: E4M3 codes; F = 4: E2M1 codes, two a byte), at
+// the same row positions. One thread per 8-column piece, grid-stride over each expert's rows in
+// turn.
+template <int F>
 __global__ void __launch_bounds__(256) expand_big_rows_kernel(const uint8_t* __restrict__ r8,
                                                               const uint8_t* __restrict__ r8s,
                                                               uint16_t* __restrict__ out,
@@ -504,9 +528,15 @@ __global__ void __launch_bounds__(256) expand_big_rows_kernel(const uint8_t* __r
          c += (long long)gridDim.x * blockDim.x) {
       const size_t p = (size_t)p0 + (size_t)(c / per_row);
       const int col = (int)(c % per_row) * 8;
-      const uint2 q = *reinterpret_cast<const uint2*>(r8 + p * Ndim + col);
-      const uint4 raw = make_uint4(q.x, q.y, r8s[p * (Ndim / 32) + col / 32], 0);
-      *reinterpret_cast<uint4*>(out + p * Ndim + col) = Mover<1>::expand_fp8(raw);
+      uint4 raw = make_uint4(0, 0, r8s[p * (Ndim / 32) + col / 32], 0);
+      if constexpr (F == 8) {
+        const uint2 q = *reinterpret_cast<const uint2*>(r8 + p * Ndim + col);
+        raw.x = q.x;
+        raw.y = q.y;
+      } else {
+        raw.x = *reinterpret_cast<const uint32_t*>(r8 + p * (Ndim / 2) + col / 2);
+      }
+      *reinterpret_cast<uint4*>(out + p * Ndim + col) = Mover<1>::expand<F>(raw);
     }
   }
 }
@@ -519,7 +549,7 @@ int resident_grid() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&wgrad_kernel<false, false, false, false>),
+            &per_cu, reinterpret_cast<const void*>(&wgrad_kernel<false, false, 0, false>),
             kThreads, 0) != hipSuccess)
       return 0;
     grid = (cus * (per_cu > 0 ? per_cu : 1)) / kXcds * kXcds;
@@ -558,17 +588,23 @@ hipError_t launch_wgrad(const WgradArgs& x, hipStream_t s) {
   {
     TraceScope trace(x.name, s);
     using K = void (*)(const Args, const int4*, const int32_t*, const int32_t*);
-    // [accumulate][gate][fp8 R][bf16 dW]; an fp8 R comes with the gate wgrad only
-    static const K kernels[2][2][2][2] = {
-        {{{wgrad_kernel<false, false, false, false>, wgrad_kernel<false, false, false, true>},
+    // [accumulate][gate][R: bf16, E4M3, E2M1][bf16 dW]; an MX R comes with the gate wgrad only
+    static const K kernels[2][2][3][2] = {
+        {{{wgrad_kernel<false, false, 0, false>, wgrad_kernel<false, false, 0, true>},
+          {nullptr, nullptr},
           {nullptr, nullptr}},
-         {{wgrad_kernel<false, true, false, false>, wgrad_kernel<false, true, false, true>},
-          {wgrad_kernel<false, true, true, false>, wgrad_kernel<false, true, true, true>}}},
-        {{{wgrad_kernel<true, false, false, false>, wgrad_kernel<true, false, false, true>},
+         {{wgrad_kernel<false, true, 0, false>, wgrad_kernel<false, true, 0, true>},
+          {wgrad_kernel<false, true, 8, false>, wgrad_kernel<false, true, 8, true>},
+          {wgrad_kernel<false, true, 4, false>, wgrad_kernel<false, true, 4, true>}}},
+        {{{wgrad_kernel<true, false, 0, false>, wgrad_kernel<true, false, 0, true>},
+          {nullptr, nullptr},
           {nullptr, nullptr}},
-         {{wgrad_kernel<true, true, false, false>, wgrad_kernel<true, true, false, true>},
-          {wgrad_kernel<true, true, true, false>, wgrad_kernel<true, true, true, true>}}}};
-    const K kern = kernels[x.accumulate ? 1 : 0][x.gate ? 1 : 0][x.R8 ? 1 : 0][x.bf16_dw ? 1 : 0];
+         {{wgrad_kernel<true, true, 0, false>, wgrad_kernel<true, true, 0, true>},
+          {wgrad_kernel<true, true, 8, false>, wgrad_kernel<true, true, 8, true>},
+          {wgrad_kernel<true, true, 4, false>, wgrad_kernel<true, true, 4, true>}}}};
+    if (x.R8 && x.rbits != 8 && x.rbits != 4) return hipErrorInvalidValue;
+    const int rf = x.R8 ? (x.rbits == 8 ? 1 : 2) : 0;
+    const K kern = kernels[x.accumulate ? 1 : 0][x.gate ? 1 : 0][rf][x.bf16_dw ? 1 : 0];
     if (!kern) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, s, a, table, x.offsets, x.count);
   }
@@ -576,8 +612,12 @@ hipError_t launch_wgrad(const WgradArgs& x, hipStream_t s) {
   if (err != hipSuccess || !big_ok) return err;
   if (x.R8) {
     TraceScope trace("bwd_gate_wgrad_expand", s);
-    hipLaunchKernelGGL(expand_big_rows_kernel, dim3(1024), dim3(256), 0, s, x.R8, x.R8s, x.Rx,
-                       big, x.offsets, x.Ndim);
+    if (x.rbits == 4)
+      hipLaunchKernelGGL(expand_big_rows_kernel<4>, dim3(1024), dim3(256), 0, s, x.R8, x.R8s,
+                         x.Rx, big, x.offsets, x.Ndim);
+    else
+      hipLaunchKernelGGL(expand_big_rows_kernel<8>, dim3(1024), dim3(256), 0, s, x.R8, x.R8s,
+                         x.Rx, big, x.offsets, x.Ndim);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

@@ -72,7 +72,6 @@ KERNELS = [
     (r"scale_gather_kernel", "scale_gather", M),
     (r"quant_rows_kernel", "quant_rows", M),
     (r"quant_weight_kernel", "quant_weight", M),
-    (r"expand_fp4_kernel", "bwd_gate_wgrad_expand", M),
     (r"fused_forward_kernel", "fused_forward",
      ("fused.hip", "router.h", "permute.h", "gemm_tiles.h", "combine.h")),
 ]

@@ -182,7 +182,7 @@ def test_mxfp4_expert_sizes_at_tile_boundaries_and_determinism():
 
 
 def test_mxfp4_routed_layer_determinism_and_dwr_accumulation():
-    """The routed layer (router, dWr through the expanded Xp image) twice: bitwise equal, and
+    """The routed layer (router, dWr from the E2M1 Xp codes) twice: bitwise equal, and
     dWr doubles exactly under accumulate."""
     _announce("[mxfp4] determinism, routed multi-m-tile shape")
     inp = _mx4_inputs("tiny", seed=2, T=1024, E=8, k=2, d=512, I=256)
