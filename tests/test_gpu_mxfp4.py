@@ -154,12 +154,13 @@ def test_mxfp4_layer_parity(case):
 
 
 def test_mxfp4_expert_sizes_at_tile_boundaries_and_determinism():
-    """Experts of 0, 1, 127, 128, 129, 255, 256, 257 and 384 rows (full 256-row blocks on the
-    direct-to-LDS kernels, 128-row remainder tiles and their ragged last tile), d = 512 and
-    I = 512 (two K steps of 256 along d and I, several column tiles): parity against the MXFP4
-    oracle, persistent grids bitwise equal to one-shot grids, and a second backward with
-    accumulate doubling both weight gradients exactly."""
-    counts = [255, 256, 257, 0, 127, 128, 129, 1, 384]
+    """Experts of 0, 1, 127, 128, 129, 255, 256, 257, 384, 511, 512 and 513 rows (full 256-row
+    blocks on the direct-to-LDS kernels, 128-row remainder tiles and their ragged last tile; from
+    512 rows the weight gradients' big-expert kernel, which reads the expert's Xp rows expanded
+    from their E2M1 codes), d = 512 and I = 512 (two K steps of 256 along d and I, several
+    column tiles): parity against the MXFP4 oracle, persistent grids bitwise equal to one-shot
+    grids, and a second backward with accumulate doubling both weight gradients exactly."""
+    counts = [255, 256, 257, 0, 127, 128, 129, 1, 384, 511, 512, 513]
     _announce(f"[mxfp4] expert sizes {counts}, d=512 I=512 k=1")
     E, d, I = len(counts), 512, 512
     T = sum(counts)
@@ -179,6 +180,31 @@ def test_mxfp4_expert_sizes_at_tile_boundaries_and_determinism():
     for g0, g in zip(first, (L.dw1, L.dw2)):
         assert torch.equal(g, 2 * g0)
     assert torch.count_nonzero(L.dw1[3]) == 0 and torch.count_nonzero(L.dw2[3]) == 0
+
+
+def test_mxfp4_big_expert_wgrad_with_accumulation():
+    """One expert of 700 rows beside small and empty experts (the gate wgrad reads the big
+    expert's Xp rows expanded from their E2M1 codes into the dXp buffer, and the others' codes
+    directly): parity with the MXFP4 oracle, then a second backward with accumulate=1 doubles
+    dW1 and dW2 exactly."""
+    counts = [700, 300, 0, 24]
+    _announce(f"[mxfp4] big expert {counts}, d=512 I=256 k=1, accumulate")
+    E, d, I = len(counts), 512, 256
+    T = sum(counts)
+    inp = _mx4_inputs("local_zipf", seed=13, T=T, d=d, E=E, I=I)
+    idx = np.repeat(np.arange(E, dtype=np.int32), counts)
+    np.random.default_rng(13).shuffle(idx)
+    inp["topk_idx"] = torch.from_numpy(idx.reshape(T, 1)).to(DEV)
+    L = run_gpu(inp)
+    f, b = run_oracle(inp)
+    assert list(f["counts"]) == counts
+    check_parity(L, inp, f, b, tol_act=TOL_ACT, tol_grad=TOL_GRAD)
+    first = [g.clone() for g in (L.dw1, L.dw2)]
+    L.backward(None, inp["W1"], inp["W2"], inp["dY"], accumulate=True)
+    torch.cuda.synchronize()
+    for g0, g in zip(first, (L.dw1, L.dw2)):
+        assert torch.equal(g, 2 * g0)
+    assert torch.count_nonzero(L.dw1[2]) == 0 and torch.count_nonzero(L.dw2[2]) == 0
 
 
 def test_mxfp4_routed_layer_determinism_and_dwr_accumulation():
