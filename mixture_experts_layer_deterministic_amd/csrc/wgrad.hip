@@ -570,7 +570,7 @@ size_t wgrad_table_entries(int Tk, int E, int Mdim, int Ndim) {
 
 hipError_t launch_wgrad(const WgradArgs& x, hipStream_t s) {
   // the big-expert kernel takes bf16 operands whose dW dimensions are multiples of its tile; an
-  // fp8 R needs the scratch for its bf16 image
+  // MX R needs the scratch for its bf16 image
   const bool big_ok = (!x.R8 || x.Rx) && x.Mdim % 256 == 0 && x.Ndim % 256 == 0;
   const int big_rows = big_ok ? kWgradBigRows : 0x7fffffff;
   int4* big = x.table;

@@ -88,11 +88,19 @@ def bench_name(raw: str):
     return None
 
 
+def _code_only(text: str) -> str:
+    """The source without its comments and with whitespace runs collapsed: a change to a
+    comment does not change the code the counters were taken on."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(srcs) -> str:
     h = hashlib.sha256()
     for f in (*srcs, *COMMON_SOURCES):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
