@@ -125,13 +125,22 @@ def kernel_roofline(name, nbytes, flops, us, mx=False, mx_wgrad=False, fbits=8):
         return {"bound": "alu", "achieved": ach, "peak": VALU_FP32_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / VALU_FP32_TFLOPS}
     peak = mfma_peak(name, mx, mx_wgrad, fbits)
-    if flops and name in GEMMS and flops / nbytes > peak * 1e12 / (HBM_GBPS * 1e9):
-        ach = flops / s / 1e12
-        return {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
-                "frac": ach / peak}
-    ach = nbytes / s / 1e9
-    return {"bound": "hbm", "achieved": ach, "peak": HBM_GBPS, "unit": "GB/s",
-            "frac": ach / HBM_GBPS}
+    gbps = nbytes / s / 1e9
+    if flops and name in GEMMS:
+        # a GEMM also carries all three views: % of its MFMA peak, % of HBM peak, and % of the
+        # attainable rate min(MFMA peak, HBM peak x flop/B)
+        tflops = flops / s / 1e12
+        attainable = min(peak, HBM_GBPS * 1e9 * flops / nbytes / 1e12)
+        views = {"tflops": tflops, "frac_mfma_peak": tflops / peak, "hbm_gbps": gbps,
+                 "frac_hbm": gbps / HBM_GBPS, "attainable_tflops": attainable,
+                 "frac_attainable": tflops / attainable}
+        if flops / nbytes > peak * 1e12 / (HBM_GBPS * 1e9):
+            return {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                    "frac": tflops / peak, **views}
+        return {"bound": "hbm", "achieved": gbps, "peak": HBM_GBPS, "unit": "GB/s",
+                "frac": gbps / HBM_GBPS, **views}
+    return {"bound": "hbm", "achieved": gbps, "peak": HBM_GBPS, "unit": "GB/s",
+            "frac": gbps / HBM_GBPS}
 
 
 def measured_traffic(workload, kernel):
