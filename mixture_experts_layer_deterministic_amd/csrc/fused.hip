@@ -224,7 +224,8 @@ __global__ void __launch_bounds__(kFusedThreads, 2) fused_forward_kernel(const F
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       for (int i = 0; i < nfull[q]; ++i)
-        p.sched[1 + first[q] + i] = make_int2(4 * tid + q, i * kSchedBM);
+        p.sched[1 + first[q] + i] = mtile_entry(4 * tid + q, excl[q] + i * kSchedBM,
+                                                min(kSchedBM, tot[q] - i * kSchedBM));
     if (tid == 0) p.sched[0] = make_int2(ntot, 0);
   }
   grid_sync(bar, nwg, p.status);

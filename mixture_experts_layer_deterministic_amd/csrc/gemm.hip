@@ -60,7 +60,7 @@ struct BwdDownDgrad {
     const int ntc = a.I / G::BN;
     const int2 mn = tile_mn<true>(lt, a.sched[0].x, ntc);
     Tile t;
-    t.m = decode_mtile(a.sched, a.offsets, mn.x, G::BM);
+    t.m = decode_mtile(a.sched, mn.x);
     t.n0 = mn.y * G::BN;
     return t;
   }
@@ -171,7 +171,7 @@ struct BwdGateDgrad {
     const int ntc = a.d / G::BN;
     const int2 mn = tile_mn<true>(lt, a.sched[0].x, ntc);
     Tile t;
-    t.m = decode_mtile(a.sched, a.offsets, mn.x, G::BM);
+    t.m = decode_mtile(a.sched, mn.x);
     t.n0 = mn.y * G::BN;
     return t;
   }
@@ -560,10 +560,10 @@ struct MxFwdGateUpT {
     Tile t;
     if constexpr (G::BM > 128) {  // grouped order: row blocks of one expert share weight panels
       const int2 mn = tile_mn<true>(lt, a.sched[0].x, ntc);
-      t.m = decode_mtile(a.sched, a.offsets, mn.x, G::BM);
+      t.m = decode_mtile(a.sched, mn.x);
       t.n0 = mn.y * kA;
     } else {
-      t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
+      t.m = decode_mtile(a.sched, lt / ntc);
       t.n0 = (lt % ntc) * kA;
     }
     return t;
@@ -670,7 +670,7 @@ struct MxFwdDownT {
     const int ntc = a.d / G::BN;
     const int2 mn = tile_mn<(G::BM > 128)>(lt, a.sched[0].x, ntc);
     Tile t;
-    t.m = decode_mtile(a.sched, a.offsets, mn.x, G::BM);
+    t.m = decode_mtile(a.sched, mn.x);
     t.n0 = mn.y * G::BN;
     return t;
   }
@@ -759,7 +759,7 @@ struct MxBwdDownDgradT {
   static MOE_DEV Tile decode(const Args& a, int lt) {
     const int ntc = a.I / G::BN;
     Tile t;
-    t.m = decode_mtile(a.sched, a.offsets, lt / ntc, G::BM);
+    t.m = decode_mtile(a.sched, lt / ntc);
     t.n0 = (lt % ntc) * G::BN;
     return t;
   }
@@ -901,7 +901,7 @@ struct MxBwdGateDgradT {
     const int ntc = a.d / G::BN;
     const int2 mn = tile_mn<(G::BM > 128)>(lt, a.sched[0].x, ntc);
     Tile t;
-    t.m = decode_mtile(a.sched, a.offsets, mn.x, G::BM);
+    t.m = decode_mtile(a.sched, mn.x);
     t.n0 = mn.y * G::BN;
     return t;
   }
@@ -1205,7 +1205,7 @@ struct DmaGateDgrad {
   static MOE_DEV int ntiles(const Args& a) { return a.big[0].x * (a.d / 256); }
   static MOE_DEV Tile decode(const Args& a, int lt) {
     const int2 mn = tile_mn<true>(lt, a.big[0].x, a.d / 256);
-    return Tile{decode_mtile(a.big, a.offsets, mn.x, 256), mn.y * 256};
+    return Tile{decode_mtile(a.big, mn.x), mn.y * 256};
   }
   static MOE_DEV int brow(int, int) { return 0; }
   static MOE_DEV void src(const Args& a, const Tile& t, int wave, int lane, DmaSrc& s) {
@@ -1255,7 +1255,7 @@ struct DmaDownDgrad {
   static MOE_DEV int ntiles(const Args& a) { return a.big[0].x * (a.I / 256); }
   static MOE_DEV Tile decode(const Args& a, int lt) {
     const int2 mn = tile_mn<true>(lt, a.big[0].x, a.I / 256);
-    return Tile{decode_mtile(a.big, a.offsets, mn.x, 256), mn.y * 256};
+    return Tile{decode_mtile(a.big, mn.x), mn.y * 256};
   }
   static MOE_DEV int brow(int, int) { return 0; }
   static MOE_DEV void src(const Args& a, const Tile& t, int wave, int lane, DmaSrc& s) {
@@ -1638,7 +1638,7 @@ struct DmxDownDgrad {
   static MOE_DEV int ntiles(const Args& a) { return a.sched[0].x * (a.I / 256); }
   static MOE_DEV Tile decode(const Args& a, int lt) {
     const int2 mn = tile_mn<true>(lt, a.sched[0].x, a.I / 256);
-    return Tile{decode_mtile(a.sched, a.offsets, mn.x, 256), mn.y * 256};
+    return Tile{decode_mtile(a.sched, mn.x), mn.y * 256};
   }
   static MOE_DEV int brow(int wn, int nb) { return wn * 64 + nb * 16; }
   // byte offsets into dY's codes fit 32 bits: T d < 2^31 is an API limit
@@ -1770,17 +1770,23 @@ __global__ void __launch_bounds__(1024) sched_build_kernel(const int32_t* offset
                                                            int2* full, int2* big, int2* rem) {
   __shared__ int scan[1024];
   const int e = threadIdx.x;
-  const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+  const int p0 = e < E ? offsets[e] : 0;
+  const int c = e < E ? offsets[e + 1] - p0 : 0;
   const int nfull = (c + kSchedBM - 1) / kSchedBM;
   const int nbig = c / kSchedBigBM;
   const int nrem = (c - nbig * kSchedBigBM + kSchedBM - 1) / kSchedBM;
   const int efull = block_scan_1024(nfull, scan);
   const int ebig = block_scan_1024(nbig, scan);
   const int erem = block_scan_1024(nrem, scan);
-  for (int i = 0; i < nfull; ++i) full[1 + efull - nfull + i] = make_int2(e, i * kSchedBM);
-  for (int i = 0; i < nbig; ++i) big[1 + ebig - nbig + i] = make_int2(e, i * kSchedBigBM);
-  for (int i = 0; i < nrem; ++i)
-    rem[1 + erem - nrem + i] = make_int2(e, nbig * kSchedBigBM + i * kSchedBM);
+  for (int i = 0; i < nfull; ++i)
+    full[1 + efull - nfull + i] =
+        mtile_entry(e, p0 + i * kSchedBM, min(kSchedBM, c - i * kSchedBM));
+  for (int i = 0; i < nbig; ++i)
+    big[1 + ebig - nbig + i] = mtile_entry(e, p0 + i * kSchedBigBM, kSchedBigBM);
+  for (int i = 0; i < nrem; ++i) {
+    const int r = nbig * kSchedBigBM + i * kSchedBM;
+    rem[1 + erem - nrem + i] = mtile_entry(e, p0 + r, min(kSchedBM, c - r));
+  }
   if (e == 1023) {
     full[0] = make_int2(efull, 0);
     big[0] = make_int2(ebig, 0);

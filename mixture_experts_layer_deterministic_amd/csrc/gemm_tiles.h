@@ -132,16 +132,21 @@ using GeoSmall = Geo<128, 128, 64, 1, 4>;
 // line (steps of 32 fetched half lines and ran 16% slower).
 using GeoBig = Geo<256, 256, 64, 2, 4>;
 
-// Row segment of one expert for dynamic-M problems: table entry -> (expert, first row).
+// Row segment of one expert for dynamic-M problems. A tile table entry holds the expert and
+// the segment's row count (x = e | mcount << 16) and its first row position (y), so a tile
+// finds its rows with one read.
 struct MTile {
   int e, row0, mcount;
 };
-MOE_DEV MTile decode_mtile(const int2* sched, const int32_t* offsets, int mt, int BM) {
+MOE_DEV int2 mtile_entry(int e, int row0, int mcount) {
+  return make_int2(e | (mcount << 16), row0);
+}
+MOE_DEV MTile decode_mtile(const int2* sched, int mt) {
   const int2 ent = sched[1 + mt];
   MTile t;
-  t.e = ent.x;
-  t.row0 = offsets[ent.x] + ent.y;
-  t.mcount = min(BM, offsets[ent.x + 1] - t.row0);
+  t.e = ent.x & 0xffff;
+  t.mcount = ent.x >> 16;
+  t.row0 = ent.y;
   return t;
 }
 
@@ -191,7 +196,7 @@ struct FwdGateUpT {
     const int nt_count = a.I / (G::BN / 2);
     const int2 mn = tile_mn<(G::BM > 128)>(lt, a.sched[0].x, nt_count);
     Tile t;
-    t.m = decode_mtile(a.sched, a.offsets, mn.x, G::BM);
+    t.m = decode_mtile(a.sched, mn.x);
     t.n0 = mn.y * (G::BN / 2);
     return t;
   }
@@ -281,7 +286,7 @@ struct FwdDownT {
     const int ntc = a.d / G::BN;
     const int2 mn = tile_mn<(G::BM > 128)>(lt, a.sched[0].x, ntc);
     Tile t;
-    t.m = decode_mtile(a.sched, a.offsets, mn.x, G::BM);
+    t.m = decode_mtile(a.sched, mn.x);
     t.n0 = mn.y * G::BN;
     return t;
   }
