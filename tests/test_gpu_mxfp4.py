@@ -271,3 +271,55 @@ def test_mxfp4_full_size_sampled_parity_and_determinism():
     torch.cuda.empty_cache()
     assert_bitwise_equal(ref, outputs(run_gpu(inp), True, clone=False))
     _announce("  two full-size MXFP4 runs bitwise identical")
+
+
+def test_mxfp4_local_zipf_full_size_sampled_parity():
+    """The full local expert slice in MXFP4 mode (16,384 rows, d=7168, I=2048, one expert over
+    40%: the 256-row MXFP4 kernels and the weight gradients' big-expert kernel on expanded E2M1
+    rows): the ring's codes and scales bit-exact on sampled positions, the heaviest and the
+    lightest expert's dW1 and dW2, and sampled tokens of those two experts, against the MXFP4
+    oracle at the BF16 bar; then a second run bitwise equal to the first."""
+    _announce("[mxfp4] local_zipf 16384 rows d=7168 E=8 k=1 I=2048 seed 0, MXFP4")
+    inp = _mx4_inputs("local_zipf")
+    L = run_gpu(inp)
+    X, dY = _np(inp["X"]), _np(inp["dY"])
+    idx, w = _np(inp["topk_idx"]), _np(inp["topk_w"])
+    counts, offsets, row_src, tk_row = oracle.permute(idx, 8)
+    for n, want in (("counts", counts), ("offsets", offsets), ("row_src", row_src),
+                    ("tk_row", tk_row)):
+        np.testing.assert_array_equal(_np(getattr(L, n)), want, err_msg=n)
+    pos = np.unique(np.concatenate([[0, len(row_src) - 1],
+                                    np.random.default_rng(7).choice(len(row_src), 256)]))
+    codes, scales = L.xp()
+    q, sc = oracle.mx.quantize(X[row_src[pos]], fmt="e2m1")
+    p_dev = torch.from_numpy(pos).to(DEV)
+    np.testing.assert_array_equal(codes_of(_np(codes[p_dev]), "e2m1"), q)
+    np.testing.assert_array_equal(_np(scales[p_dev]), sc)
+    _announce("  permutation and sampled ring codes bit-exact")
+    nonempty = np.flatnonzero(counts)
+    heavy = int(np.argmax(counts))
+    light = int(nonempty[np.argmin(counts[nonempty])])
+    W1h, W2h = workload.HostExperts(inp["W1"]), workload.HostExperts(inp["W2"])
+    fe = oracle.forward(X, W1h, W2h, topk_idx=idx, topk_w=w, experts=[heavy, light],
+                        precision="mxfp4")
+    be = oracle.backward(fe, X, W1h, W2h, dY, experts=[heavy, light])
+    for i, e in enumerate((heavy, light)):
+        assert_grad(f"dW1[{e}] ({counts[e]} rows)", _np(L.dw1[e]), be["dW1"][i], TOL_GRAD)
+        assert_grad(f"dW2[{e}] ({counts[e]} rows)", _np(L.dw2[e]), be["dW2"][i], TOL_GRAD)
+    _announce("  heaviest and lightest experts' weight gradients done")
+    rng = np.random.default_rng(8)
+    tok = np.unique(np.concatenate([rng.choice(np.flatnonzero(idx[:, 0] == e), 8, replace=False)
+                                    for e in (heavy, light)]))
+    t_dev = torch.from_numpy(tok).to(DEV)
+    rows = tk_row[tok]
+    assert_act("Y[tokens]", _np(L.y[t_dev]), fe["Y"][tok], TOL_ACT)
+    assert_act("dX[tokens]", _np(L.dx[t_dev]), be["dX"][tok], TOL_ACT)
+    assert_grad("d_topk_w[tokens]", _np(L.d_topk_w[t_dev]), be["dw"][tok], TOL_GRAD)
+    r_dev = torch.from_numpy(rows).to(DEV)
+    assert_act("H[rows]", _np(L.H()[r_dev]), fe["H"][rows], TOL_ACT)
+    assert_act("dH[rows]", _np(L.dH()[r_dev]), be["dH"][rows], TOL_ACT)
+    ref = outputs(L, False)
+    del L
+    torch.cuda.empty_cache()
+    assert_bitwise_equal(ref, outputs(run_gpu(inp), False, clone=False))
+    _announce("  two full-size MXFP4 runs bitwise identical")
