@@ -331,6 +331,34 @@ def test_mxfp8_weight_gradients_match_the_oracle(case):
     assert torch.equal(L.dw1, 2 * first[0]) and torch.equal(L.dw2, 2 * first[1])
 
 
+def test_mxfp8_weight_gradients_full_size_local_zipf():
+    """MXFP8 weight gradients on the full local expert slice (16,384 rows, d=7168, I=2048, one
+    expert of over 8,000 rows): the heaviest and the lightest expert's dW1 and dW2 within 6e-2
+    of the oracle quantising the same operands along each expert's positions, then a second
+    run bitwise equal to the first."""
+    _announce("[mxfp8 wgrad] local_zipf 16384 rows d=7168 E=8 k=1 I=2048 seed 0")
+    inp = _mx_inputs("local_zipf", seed=0, mx_wgrad=True)
+    L = run_gpu(inp)
+    X, dY = _np(inp["X"]), _np(inp["dY"])
+    idx, w = _np(inp["topk_idx"]), _np(inp["topk_w"])
+    counts = np.bincount(idx[:, 0], minlength=8)
+    nonempty = np.flatnonzero(counts)
+    heavy = int(np.argmax(counts))
+    light = int(nonempty[np.argmin(counts[nonempty])])
+    W1h, W2h = workload.HostExperts(inp["W1"]), workload.HostExperts(inp["W2"])
+    fe = oracle.forward(X, W1h, W2h, topk_idx=idx, topk_w=w, experts=[heavy, light],
+                        precision="mxfp8")
+    be = oracle.backward(fe, X, W1h, W2h, dY, experts=[heavy, light], wgrad="mxfp8")
+    for i, e in enumerate((heavy, light)):
+        assert_grad(f"dW1[{e}] ({counts[e]} rows)", _np(L.dw1[e]), be["dW1"][i], TOL_MX)
+        assert_grad(f"dW2[{e}] ({counts[e]} rows)", _np(L.dw2[e]), be["dW2"][i], TOL_MX)
+    ref = outputs(L, False)
+    del L
+    torch.cuda.empty_cache()
+    assert_bitwise_equal(ref, outputs(run_gpu(inp), False, clone=False))
+    _announce("  two full-size runs with MXFP8 weight gradients bitwise identical")
+
+
 def test_mxfp8_weight_gradients_with_large_and_empty_experts():
     """Experts of 700, 300, 0 and 24 rows at d=512, I=256: several 128-position K chunks, an
     empty expert (zero blocks) and segments starting off the 32-row grid."""
