@@ -315,7 +315,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one MI355X: this build has no multi-GPU path "
+        print("bench.py measures one MI355X: the library has no multi-GPU path "
               "(no collectives, no sharding); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

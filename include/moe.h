@@ -44,7 +44,7 @@ typedef enum moe_status {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = -1,     /* null pointer, bad shape, misaligned pointer */
     MOE_ERR_RING_TOO_SMALL = -2,  /* ring_bytes < (slot + 1) * ring slot bytes */
-    MOE_ERR_UNSUPPORTED = -3,     /* a mode this build does not provide */
+    MOE_ERR_UNSUPPORTED = -3,     /* a mode the library does not provide */
     MOE_ERR_HIP = -4,             /* a HIP runtime error while enqueuing */
     MOE_ERR_WORKSPACE_TOO_SMALL = -5
 } moe_status;

@@ -61,14 +61,14 @@ bool cfg_ok(const moe_cfg* c) {
 // device and kept.
 int check_device() {
   constexpr int kMaxDev = 64;
-  static std::atomic<int> verdict[kMaxDev];  // 0 unknown, 1 gfx950, 2 another device
+  static std::atomic<int> arch_seen[kMaxDev];  // 0 unknown, 1 gfx950, 2 another device
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
     (void)hipGetLastError();
     return MOE_ERR_HIP;
   }
   if (dev < kMaxDev) {
-    const int v = verdict[dev].load(std::memory_order_relaxed);
+    const int v = arch_seen[dev].load(std::memory_order_relaxed);
     if (v) return v == 1 ? MOE_OK : MOE_ERR_UNSUPPORTED;
   }
   hipDeviceProp_t prop;
@@ -78,7 +78,7 @@ int check_device() {
   }
   const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
                   (prop.gcnArchName[6] == 0 || prop.gcnArchName[6] == ':');
-  if (dev < kMaxDev) verdict[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  if (dev < kMaxDev) arch_seen[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
   return ok ? MOE_OK : MOE_ERR_UNSUPPORTED;
 }
 

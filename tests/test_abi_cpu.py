@@ -88,7 +88,7 @@ def test_entry_points_reject_bad_arguments_before_launching():
                          s.workspace - 1, None) == -5
     assert L.moe_forward(ctypes.byref(cfg), p, s.ring_slot, 0, p, p, p, p, p, None, 0, p, p,
                          s.saved - 1, p, s.workspace, None) == -5
-    # an unknown precision is not provided by this build
+    # an unknown precision is not provided by the library
     cfgx = m.make_cfg(64, 256, 8, 2, 128, 3)
     assert L.moe_route(ctypes.byref(cfgx), p, p, p, p, p, p, s.workspace, None) == -3
     # MXFP8: the quantised weights are required, and sized
