@@ -231,6 +231,60 @@ def test_streaming_microbatches_with_ring_replay():
     assert_grad("dWr (sum)", _np(L.dwr), dWr)
 
 
+@pytest.mark.parametrize("prec", ["mxfp8", "mxfp4"])
+def test_streaming_microbatches_with_ring_replay_in_mx_modes(prec):
+    """The reverse ring walk with replay in the MX modes, where a ring slot holds the
+    microbatch's MX codes and scales: weights quantised once, 4 microbatches through 2 slots,
+    the overwritten slots re-permuted before their backward, the weight gradients accumulated.
+    Against the oracle emulating the same quantisation (6e-2 for MXFP8; the BF16 bar for
+    MXFP4, which its emulation meets)."""
+    _announce(f"[stream {prec}] 4 microbatches, 2 slots, reverse walk with replay")
+    nmb, S = 4, 2
+    inp = workload.make_inputs("stream", seed=9, device=DEV, T=64, d=256, E=16, k=4, I=256,
+                               microbatches=nmb)
+    cfg = inp["cfg"]
+    T, d, E, k, I = cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["I"]
+    code = m.MOE_PREC_MXFP8 if prec == "mxfp8" else m.MOE_PREC_MXFP4
+    tol_a, tol_g = (6e-2, 6e-2) if prec == "mxfp8" else (1e-2, 2e-2)
+    L = MoeLayer(T, d, E, k, I, device=DEV, ring_slots=S, precision=code)
+    L.quantize_weights(inp["W1"], inp["W2"])
+    saved = [torch.empty_like(L.saved) for _ in range(nmb)]
+    routing, ys = [], []
+    for i in range(nmb):
+        L.route(inp["X"][i], inp["Wr"])
+        L.permute(inp["X"][i], slot=i % S)
+        L.forward(inp["W1"], inp["W2"], slot=i % S, saved=saved[i])
+        ys.append(L.y.clone())
+        routing.append((L.topk_idx.clone(), L.topk_w.clone(), L.counts.clone(),
+                        L.offsets.clone(), L.row_src.clone(), L.tk_row.clone()))
+    dxs = [None] * nmb
+    for i in reversed(range(nmb)):
+        for dst, src in zip((L.topk_idx, L.topk_w, L.counts, L.offsets, L.row_src, L.tk_row),
+                            routing[i]):
+            dst.copy_(src)
+        if i < nmb - S:
+            L.permute(inp["X"][i], slot=i % S)   # replay: the slot was overwritten
+        L.backward(inp["Wr"], inp["W1"], inp["W2"], inp["dY"][i], slot=i % S,
+                   accumulate=(i != nmb - 1), saved=saved[i])
+        dxs[i] = L.dx.clone()
+    torch.cuda.synchronize()
+    X, W1, W2, dY, Wr = (_np(inp[n]) for n in ("X", "W1", "W2", "dY", "Wr"))
+    dW1 = np.zeros_like(W1, dtype=np.float64)
+    dW2 = np.zeros_like(W2, dtype=np.float64)
+    dWr = np.zeros_like(Wr, dtype=np.float64)
+    for i in range(nmb):
+        f = oracle.forward(X[i], W1, W2, Wr=Wr, k=k, precision=prec)
+        b = oracle.backward(f, X[i], W1, W2, dY[i], Wr=Wr)
+        assert_act(f"Y[{i}]", _np(ys[i]), f["Y"], tol_a)
+        assert_act(f"dX[{i}]", _np(dxs[i]), b["dX"], tol_a)
+        dW1 += b["dW1"]
+        dW2 += b["dW2"]
+        dWr += b["dWr"]
+    assert_grad("dW1 (sum)", _np(L.dw1), dW1, tol_g)
+    assert_grad("dW2 (sum)", _np(L.dw2), dW2, tol_g)
+    assert_grad("dWr (sum)", _np(L.dwr), dWr, tol_g)
+
+
 def _macro_outputs(mb):
     outs = []
     for b in mb.mb:
