@@ -1,7 +1,7 @@
 """Bitwise determinism across processes: a fresh process, whose buffers sit elsewhere in device
 memory (it first takes a 3 GiB spacer allocation), must produce every output of one layer step
 bit for bit as this process does, in BF16, MXFP8 and MXFP4, on one-shot and persistent grids,
-and at the full DeepSeek-V3 shape.
+and at the full sizes: the DeepSeek-V3-shaped layer in all three precisions and the expert slice.
 
 Every output element has one producer and a fixed summation order, so neither buffer placement
 nor launch timing may change a bit. The comparison is between two runs of the same library; no
@@ -34,6 +34,10 @@ CASES = [
     ("multi_mtile_bf16_dw", "tiny", dict(T=1024, E=4, k=2, d=512, I=256), dict(bf16_dw=True)),
     # the DeepSeek-V3-shaped layer: 2048 tokens, d 7168, 256 experts, top-8, I 2048
     ("dsv3_bf16", "dsv3", {}, {}),
+    ("dsv3_mxfp8", "dsv3_mxfp8", {}, {}),
+    ("dsv3_mxfp4", "dsv3_mxfp4", {}, {}),
+    # one device's expert slice: 16384 rows over 8 experts of d 7168, I 2048, Zipf-skewed
+    ("local_zipf_bf16", "local_zipf", {}, {}),
 ]
 
 
