@@ -1,7 +1,8 @@
 """Bitwise determinism across processes: a fresh process, whose buffers sit elsewhere in device
 memory (it first takes a 3 GiB spacer allocation), must produce every output of one layer step
 bit for bit as this process does, in BF16, MXFP8 and MXFP4, on one-shot and persistent grids,
-and at the full sizes: the DeepSeek-V3-shaped layer in all three precisions and the expert slice.
+and at the full sizes: the DeepSeek-V3-shaped layer in all three precisions, the expert slice
+and the streaming macrobatch's whole ring walk.
 
 Every output element has one producer and a fixed summation order, so neither buffer placement
 nor launch timing may change a bit. The comparison is between two runs of the same library; no
@@ -18,6 +19,7 @@ import torch
 
 import workload
 from tests._gpu import DEV, _announce, outputs, run_gpu
+from tests.test_gpu_sizes_full import _stream_run
 
 pytestmark = pytest.mark.gpu
 
@@ -77,6 +79,14 @@ def digests():
         out[label] = _digest(outputs(L, "Wr" in inp, clone=False))
         del L, inp
         torch.cuda.empty_cache()
+    # the streaming macrobatch: 8 microbatches of 2368 tokens through a 2-slot ring, forward
+    # 0..7, then backward 7..0 with replays and the weight gradients accumulated
+    inp = workload.make_inputs("stream", seed=7, device=DEV)
+    L, routing, ys, dxs, dtws = _stream_run(inp)
+    flat = [t for r in routing for t in r] + ys + dxs + dtws + [L.dw1, L.dw2, L.dwr]
+    out["stream_ring_walk"] = _digest(flat)
+    del L, inp, routing, ys, dxs, dtws, flat
+    torch.cuda.empty_cache()
     return out
 
 
@@ -89,9 +99,9 @@ def child_main():
 
 
 def test_outputs_are_bitwise_identical_across_processes():
-    _announce("[processes] " + ", ".join(c[0] for c in CASES))
+    _announce("[processes] " + ", ".join(c[0] for c in CASES) + ", stream_ring_walk")
     here = digests()
-    assert len(set(here.values())) == len(CASES)
+    assert len(set(here.values())) == len(CASES) + 1
     code = "import tests.test_gpu_processes as t; t.child_main()"
     r = subprocess.run([sys.executable, "-u", "-c", code], cwd=ROOT, capture_output=True,
                        text=True, timeout=300)
